@@ -1,0 +1,12 @@
+"""MI355X (gfx950) Gated Delta Rule token mixer.
+
+The compute lives in libgdn.so (HIP kernels behind the C ABI declared in
+include/gdn.h); this package holds its ctypes binding, the build script and
+the seeded synthetic input recipes. Importing the package does not load the
+library; the first call does, and fails loudly if it has not been built.
+"""
+from ._binding import (GDNError, gdn_decode_step, gdn_mixer_epilogue,  # noqa: F401
+                       gdn_mixer_prologue, gdn_prefill, gdn_prefill_recurrent, load)
+
+__all__ = ["GDNError", "gdn_prefill", "gdn_prefill_recurrent", "gdn_decode_step",
+           "gdn_mixer_prologue", "gdn_mixer_epilogue", "load"]

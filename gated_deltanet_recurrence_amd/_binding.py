@@ -1,0 +1,189 @@
+"""ctypes binding of libgdn.so: argument marshalling only.
+
+Each wrapper checks that the torch tensors it is given are on the GPU,
+contiguous, of the expected dtype and shape, passes their device pointers and
+the current HIP stream to the C entry point of the same name, and raises on a
+non-zero status. No arithmetic of the method runs here; torch only supplies
+device memory and streams. If libgdn.so is missing the first call raises
+(build it with ``python -m gated_deltanet_recurrence_amd.build``): there is
+no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_DTYPE_F32 = 0
+GDN_DTYPE_BF16 = 1
+_DTYPES = {torch.float32: GDN_DTYPE_F32, torch.bfloat16: GDN_DTYPE_BF16}
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+
+# name -> argtypes (restype int for all)
+_SIGS = {
+    "gdn_version": [],
+    "gdn_status_string": [_i],
+    "gdn_check_cu_seqlens": [_vp, _i, _i],
+    "gdn_prefill": [_vp] * 9 + [_i] * 6 + [_f, _i, _vp],
+    "gdn_prefill_recurrent": [_vp] * 9 + [_i] * 6 + [_f, _i, _vp],
+    "gdn_decode_step": [_vp] * 7 + [_i] * 4 + [_f, _i, _vp],
+    "gdn_mixer_prologue": [_vp] * 14 + [_i] * 7 + [_vp],
+    "gdn_mixer_epilogue": [_vp] * 4 + [_i] * 3 + [_f, _i, _vp],
+}
+EXPORTED = tuple(_SIGS)
+
+_lib = None
+
+
+class GDNError(RuntimeError):
+    pass
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libgdn.so (once) and declare the entry points' signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise GDNError(f"{p} is missing: build it with "
+                       "`python -m gated_deltanet_recurrence_amd.build`")
+    lib = ctypes.CDLL(p)
+    for name, args in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_char_p if name == "gdn_status_string" else ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = load().gdn_status_string(status).decode()
+        raise GDNError(f"libgdn status {status}: {msg}")
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None, shape=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise GDNError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise GDNError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise GDNError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise GDNError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise GDNError(f"unsupported dtype {t.dtype}")
+    return _DTYPES[t.dtype]
+
+
+def _prefill(entry, q, k, v, g, beta, initial_state=None, final_state=None, o=None,
+             cu_seqlens=None, scale=None):
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    dt = q.dtype
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=q.device)
+    if scale is None:
+        scale = dk ** -0.5
+    args = [
+        _dev(q, "q", dt), _dev(k, "k", dt, q.shape), _dev(v, "v", dt, (B, T, H, dv)),
+        _dev(g, "g", torch.float32, (B, T, H)), _dev(beta, "beta", torch.float32, (B, T, H)),
+        _dev(initial_state, "initial_state", torch.float32, (N, H, dv, dk)),
+        _dev(final_state, "final_state", torch.float32, (N, H, dv, dk)),
+        _dev(o, "o", dt, (B, T, H, dv)),
+        _dev(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,)),
+    ]
+    _check(getattr(load(), entry)(*args, B, T, H, dk, dv, N, float(scale), _dtype_code(q),
+                                  _stream(q.device)))
+    return o, final_state
+
+
+def gdn_prefill(q, k, v, g, beta, initial_state=None, final_state=None, o=None,
+                cu_seqlens=None, scale=None):
+    """Chunkwise forward (see include/gdn.h). Returns (o, final_state)."""
+    return _prefill("gdn_prefill", q, k, v, g, beta, initial_state, final_state, o,
+                    cu_seqlens, scale)
+
+
+def gdn_prefill_recurrent(q, k, v, g, beta, initial_state=None, final_state=None, o=None,
+                          cu_seqlens=None, scale=None):
+    """Token-serial fp32 forward (see include/gdn.h). Returns (o, final_state)."""
+    return _prefill("gdn_prefill_recurrent", q, k, v, g, beta, initial_state, final_state, o,
+                    cu_seqlens, scale)
+
+
+def gdn_decode_step(q, k, v, g, beta, state, o=None, scale=None):
+    """One in-place recurrent step. q,k: [B,H,d_k]; v: [B,H,d_v]; g,beta: [B,H];
+    state: [B,H,d_v,d_k] fp32 (updated). Returns o [B,H,d_v]."""
+    B, H, dk = q.shape
+    dv = v.shape[2]
+    dt = q.dtype
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=dt, device=q.device)
+    if scale is None:
+        scale = dk ** -0.5
+    _check(load().gdn_decode_step(
+        _dev(q, "q", dt), _dev(k, "k", dt, q.shape), _dev(v, "v", dt, (B, H, dv)),
+        _dev(g, "g", torch.float32, (B, H)), _dev(beta, "beta", torch.float32, (B, H)),
+        _dev(state, "state", torch.float32, (B, H, dv, dk)), _dev(o, "o", dt, (B, H, dv)),
+        B, H, dk, dv, float(scale), _dtype_code(q), _stream(q.device)))
+    return o
+
+
+def gdn_mixer_prologue(q_raw, k_raw, v_raw, conv_w, a, b, A, dt_bias=None, cu_seqlens=None,
+                       out=None):
+    """Conv+SiLU, L2-norm of q,k, gates. Returns (q, k, v, g, beta)."""
+    B, T, H, dk = q_raw.shape
+    dv = v_raw.shape[3]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    dt = q_raw.dtype
+    if out is None:
+        out = (torch.empty_like(q_raw), torch.empty_like(k_raw), torch.empty_like(v_raw),
+               torch.empty((B, T, H), dtype=torch.float32, device=q_raw.device),
+               torch.empty((B, T, H), dtype=torch.float32, device=q_raw.device))
+    q, k, v, g, beta = out
+    _check(load().gdn_mixer_prologue(
+        _dev(q_raw, "q_raw", dt), _dev(k_raw, "k_raw", dt, q_raw.shape),
+        _dev(v_raw, "v_raw", dt, (B, T, H, dv)),
+        _dev(conv_w, "conv_w", dt, (H * (2 * dk + dv), 4)),
+        _dev(a, "a", dt, (B, T, H)), _dev(b, "b", dt, (B, T, H)),
+        _dev(A, "A", torch.float32, (H,)), _dev(dt_bias, "dt_bias", torch.float32, (H,)),
+        _dev(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,)),
+        _dev(q, "q", dt, q_raw.shape), _dev(k, "k", dt, q_raw.shape),
+        _dev(v, "v", dt, (B, T, H, dv)), _dev(g, "g", torch.float32, (B, T, H)),
+        _dev(beta, "beta", torch.float32, (B, T, H)),
+        B, T, H, dk, dv, N, _dtype_code(q_raw), _stream(q_raw.device)))
+    return q, k, v, g, beta
+
+
+def gdn_mixer_epilogue(y, z, norm_w=None, out=None, eps=1e-6):
+    """Gated RMSNorm over the last axis of y [B,T,H,d_v] with gate z."""
+    B, T, H, dv = y.shape
+    dt = y.dtype
+    if out is None:
+        out = torch.empty_like(y)
+    _check(load().gdn_mixer_epilogue(
+        _dev(y, "y", dt), _dev(z, "z", dt, y.shape), _dev(norm_w, "norm_w", torch.float32, (dv,)),
+        _dev(out, "out", dt, y.shape), B * T, H, dv, float(eps), _dtype_code(y),
+        _stream(y.device)))
+    return out

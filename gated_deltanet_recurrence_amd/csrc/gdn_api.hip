@@ -1,0 +1,168 @@
+// gdn_api.hip - the extern "C" entry points of libgdn: argument validation,
+// choice of kernel, launch on the caller's stream. No device memory is
+// allocated and no state is kept between calls.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn.h"
+#include "common.h"
+
+namespace gdn {
+template <typename TIO>
+hipError_t launch_decode(const void *, const void *, const void *, const float *, const float *,
+                         float *, void *, int, int, int, int, float, hipStream_t);
+template <typename TIO>
+hipError_t launch_prefill_recurrent(const void *, const void *, const void *, const float *,
+                                    const float *, const float *, float *, void *,
+                                    const int32_t *, int, int, int, int, int, float, hipStream_t);
+hipError_t launch_prefill_chunk(const void *, const void *, const void *, const float *,
+                                const float *, const float *, float *, void *, const int32_t *,
+                                int, int, int, float, hipStream_t);
+template <typename TIO>
+hipError_t launch_prologue(const void *, const void *, const void *, const void *, const void *,
+                           const void *, const float *, const float *, const int32_t *, void *,
+                           void *, void *, float *, float *, int, int, int, int, int, int,
+                           hipStream_t);
+template <typename TIO>
+hipError_t launch_epilogue(const void *, const void *, const float *, void *, long, int, float,
+                           hipStream_t);
+}  // namespace gdn
+
+namespace {
+
+bool head_dim_pow2(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool mixer_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128 || d == 256; }
+bool valid_dtype(int dt) { return dt == GDN_DTYPE_F32 || dt == GDN_DTYPE_BF16; }
+int status_of(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
+
+// Shared validation of the prefill arguments.
+int check_prefill(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                  const void *o, const int32_t *cu, int B, int T, int H, int d_k, int d_v, int N,
+                  int dtype)
+{
+    // with no tokens at all the activation pointers are never dereferenced
+    const bool no_tokens = (int64_t)B * T == 0;
+    if (!no_tokens && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
+    if (!valid_dtype(dtype)) return GDN_ERR_DTYPE;
+    if (B < 1 || T < 0 || H < 1 || N < 1 || d_k < 1 || d_v < 1) return GDN_ERR_SHAPE;
+    if (cu ? B != 1 : N != B) return GDN_ERR_SHAPE;
+    if ((int64_t)B * T > (int64_t)INT32_MAX) return GDN_ERR_SHAPE;   // token index fits int32
+    if (H > 65535 || N > 65535) return GDN_ERR_UNSUPPORTED;           // launch grid y / z
+    if (!head_dim_pow2(d_k) || d_v > 128) return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_version(void) { return GDN_VERSION; }
+
+const char *gdn_status_string(int status)
+{
+    switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_NULL: return "a required pointer is NULL";
+    case GDN_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case GDN_ERR_DTYPE: return "unknown dtype";
+    case GDN_ERR_UNSUPPORTED: return "valid arguments, but this size or mode is not implemented";
+    case GDN_ERR_HIP: return "the HIP runtime reported an error at launch";
+    default: return "unknown status";
+    }
+}
+
+int gdn_check_cu_seqlens(const int32_t *cu, int N, int T)
+{
+    if (!cu) return GDN_ERR_NULL;
+    if (N < 1 || T < 0 || cu[0] != 0 || cu[N] != T) return GDN_ERR_SHAPE;
+    for (int n = 0; n < N; ++n)
+        if (cu[n + 1] < cu[n]) return GDN_ERR_SHAPE;
+    return GDN_OK;
+}
+
+int gdn_prefill_recurrent(const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const float *initial_state, float *final_state,
+                          void *o, const int32_t *cu_seqlens, int B, int T, int H, int d_k,
+                          int d_v, int N, float scale, int dtype, void *stream)
+{
+    int st = check_prefill(q, k, v, g, beta, o, cu_seqlens, B, T, H, d_k, d_v, N, dtype);
+    if (st != GDN_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = dtype == GDN_DTYPE_BF16
+        ? gdn::launch_prefill_recurrent<gdn::bf16>(q, k, v, g, beta, initial_state, final_state, o,
+                                                   cu_seqlens, T, H, d_k, d_v, N, scale, s)
+        : gdn::launch_prefill_recurrent<float>(q, k, v, g, beta, initial_state, final_state, o,
+                                               cu_seqlens, T, H, d_k, d_v, N, scale, s);
+    return status_of(e);
+}
+
+int gdn_prefill(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                const float *initial_state, float *final_state, void *o,
+                const int32_t *cu_seqlens, int B, int T, int H, int d_k, int d_v, int N,
+                float scale, int dtype, void *stream)
+{
+    int st = check_prefill(q, k, v, g, beta, o, cu_seqlens, B, T, H, d_k, d_v, N, dtype);
+    if (st != GDN_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype == GDN_DTYPE_BF16 && d_k == 128 && d_v == 128) {
+        return status_of(gdn::launch_prefill_chunk(q, k, v, g, beta, initial_state, final_state,
+                                                   o, cu_seqlens, T, H, N, scale, s));
+    }
+    return gdn_prefill_recurrent(q, k, v, g, beta, initial_state, final_state, o, cu_seqlens, B,
+                                 T, H, d_k, d_v, N, scale, dtype, stream);
+}
+
+int gdn_decode_step(const void *q, const void *k, const void *v, const float *g,
+                    const float *beta, float *state, void *o, int B, int H, int d_k, int d_v,
+                    float scale, int dtype, void *stream)
+{
+    if (!q || !k || !v || !g || !beta || !state || !o) return GDN_ERR_NULL;
+    if (!valid_dtype(dtype)) return GDN_ERR_DTYPE;
+    if (B < 1 || H < 1 || d_k < 1 || d_v < 1) return GDN_ERR_SHAPE;
+    if ((int64_t)B * H > (int64_t)INT32_MAX) return GDN_ERR_SHAPE;
+    if (!head_dim_pow2(d_k) || d_v > 4096) return GDN_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = dtype == GDN_DTYPE_BF16
+        ? gdn::launch_decode<gdn::bf16>(q, k, v, g, beta, state, o, B, H, d_k, d_v, scale, s)
+        : gdn::launch_decode<float>(q, k, v, g, beta, state, o, B, H, d_k, d_v, scale, s);
+    return status_of(e);
+}
+
+int gdn_mixer_prologue(const void *q_raw, const void *k_raw, const void *v_raw,
+                       const void *conv_w, const void *a, const void *b, const float *A,
+                       const float *dt_bias, const int32_t *cu_seqlens, void *q, void *k,
+                       void *v, float *g, float *beta, int B, int T, int H, int d_k, int d_v,
+                       int N, int dtype, void *stream)
+{
+    if (!q_raw || !k_raw || !v_raw || !conv_w || !a || !b || !A || !q || !k || !v || !g || !beta)
+        return GDN_ERR_NULL;
+    if (!valid_dtype(dtype)) return GDN_ERR_DTYPE;
+    if (B < 1 || T < 0 || H < 1 || N < 1 || d_k < 1 || d_v < 1) return GDN_ERR_SHAPE;
+    if (cu_seqlens ? B != 1 : N != B) return GDN_ERR_SHAPE;
+    if ((int64_t)B * T > (int64_t)INT32_MAX) return GDN_ERR_SHAPE;
+    if (!mixer_dim(d_k) || !mixer_dim(d_v)) return GDN_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = dtype == GDN_DTYPE_BF16
+        ? gdn::launch_prologue<gdn::bf16>(q_raw, k_raw, v_raw, conv_w, a, b, A, dt_bias, cu_seqlens,
+                                          q, k, v, g, beta, B, T, H, d_k, d_v, N, s)
+        : gdn::launch_prologue<float>(q_raw, k_raw, v_raw, conv_w, a, b, A, dt_bias, cu_seqlens, q,
+                                      k, v, g, beta, B, T, H, d_k, d_v, N, s);
+    return status_of(e);
+}
+
+int gdn_mixer_epilogue(const void *y, const void *z, const float *norm_w, void *out, int rows,
+                       int H, int d_v, float eps, int dtype, void *stream)
+{
+    if (!y || !z || !out) return GDN_ERR_NULL;
+    if (!valid_dtype(dtype)) return GDN_ERR_DTYPE;
+    if (rows < 0 || H < 1 || d_v < 1 || !(eps >= 0.0f)) return GDN_ERR_SHAPE;
+    if (!mixer_dim(d_v)) return GDN_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    const long r = (long)rows * H;
+    hipError_t e = dtype == GDN_DTYPE_BF16
+        ? gdn::launch_epilogue<gdn::bf16>(y, z, norm_w, out, r, d_v, eps, s)
+        : gdn::launch_epilogue<float>(y, z, norm_w, out, r, d_v, eps, s);
+    return status_of(e);
+}
+
+}  // extern "C"

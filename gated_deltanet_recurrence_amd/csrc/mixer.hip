@@ -1,0 +1,246 @@
+// mixer.hip - the elementwise stages around the recurrence: the prologue
+// (causal conv1d + SiLU, L2-norm of q and k, gates) and the epilogue (gated
+// RMSNorm). Both are HBM-bound streaming kernels.
+//
+// Sources:
+//  "5. Linear Attention" (LinkQwen ch. 5): section "Causal Conv1d"
+//   (depthwise, 4 taps, left zero padding, no bias, followed by SiLU);
+//   section "Gated RMSNorm" (weight * x * rsqrt(mean(x^2) + eps) * silu(z));
+//   the layer body (conv -> split q/k/v -> gates -> core -> gated norm).
+//  "6.6 Gated DeltaNet (linear attention)", LLM full-stack book: section
+//   6.6.3 (alpha = exp(-A * softplus(.)), beta = sigmoid(.)) and the l2norm
+//   of section 6.6.4 (eps 1e-6 added to the sum of squares).
+//
+// Work mapping (both kernels): one (token, head) row of D channels is owned
+// by G = D/8 lanes, 8 channels (16 B of bf16) per lane, so row reductions are
+// DPP sums inside the group. In the prologue each group walks a tile of TT
+// consecutive tokens of one head of one tensor and keeps the three previous
+// inputs of its channels in registers (the convolution window), so every
+// input element is read from HBM once.
+#include "common.h"
+
+namespace gdn {
+
+constexpr int PRO_TT = 16;          // tokens per lane group in the prologue
+
+// Sequence of global token t: [start, end). cu == nullptr: rows of T tokens.
+__device__ __forceinline__ void seq_bounds(const int32_t *cu, int N, long T, long t, long &start,
+                                           long &end, int &n)
+{
+    if (!cu) {
+        n = (int)(t / T);
+        start = (long)n * T;
+        end = start + T;
+        return;
+    }
+    // largest n with cu[n] <= t (offsets clamped into [0, T], non-decreasing)
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        long c = cu[mid];
+        if (c <= t) lo = mid; else hi = mid - 1;
+    }
+    n = lo;
+    start = cu[lo];
+    end = cu[lo + 1];
+    if (start < 0) start = 0;
+    if (end > T) end = T;
+}
+
+template <int D, typename TIO>
+__global__ void __launch_bounds__(256)
+prologue_conv_kernel(const TIO *__restrict__ x_q, const TIO *__restrict__ x_k,
+                     const TIO *__restrict__ x_v, const TIO *__restrict__ conv_w,
+                     TIO *__restrict__ y_q, TIO *__restrict__ y_k, TIO *__restrict__ y_v,
+                     const TIO *__restrict__ a, const TIO *__restrict__ b,
+                     const float *__restrict__ A, const float *__restrict__ dt_bias,
+                     float *__restrict__ g, float *__restrict__ beta,
+                     const int32_t *__restrict__ cu, long total, long T, int N, int H,
+                     int d_k, int which0)
+{
+    constexpr int G = D / 8;
+    constexpr int GPB = 256 / G;                  // lane groups per block
+    const int which = which0 + (int)blockIdx.z;   // 0 = q, 1 = k, 2 = v
+    const int h = blockIdx.y;
+    const int lr = threadIdx.x % G;
+    const long t0 = ((long)blockIdx.x * GPB + threadIdx.x / G) * PRO_TT;
+    if (t0 >= total) return;
+    const long t1 = t0 + PRO_TT < total ? t0 + PRO_TT : total;
+
+    const TIO *x = which == 0 ? x_q : (which == 1 ? x_k : x_v);
+    TIO *y = which == 0 ? y_q : (which == 1 ? y_k : y_v);
+    const int c = 8 * lr;
+    // conv channel of (tensor, head, c): q channels, then k, then v
+    const long ch = (long)which * H * d_k + (long)h * D + c;
+    float w[8][4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[e][j] = to_f32(conv_w[(ch + e) * 4 + j]);
+
+    long start, end;
+    int n;
+    seq_bounds(cu, N, T, t0, start, end, n);
+
+    auto row = [&](long t) { return ((size_t)t * H + h) * D + c; };
+    float x1[8], x2[8], x3[8];                    // inputs at t-1, t-2, t-3
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { x1[e] = 0.f; x2[e] = 0.f; x3[e] = 0.f; }
+    if (t0 - 1 >= start) load8(x + row(t0 - 1), x1);
+    if (t0 - 2 >= start) load8(x + row(t0 - 2), x2);
+    if (t0 - 3 >= start) load8(x + row(t0 - 3), x3);
+
+    for (long t = t0; t < t1; ++t) {
+        while (t >= end && n < N - 1) {           // crossed into the next sequence
+            ++n;
+            start = end;
+            end = cu ? (long)cu[n + 1] : start + T;
+            if (end > T && cu) end = T;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { x1[e] = 0.f; x2[e] = 0.f; x3[e] = 0.f; }
+        }
+        float xt[8], out[8];
+        load8(x + row(t), xt);
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float pre = w[e][3] * xt[e] + w[e][2] * x1[e] + w[e][1] * x2[e]
+                            + w[e][0] * x3[e];
+            out[e] = silu_f32(pre);
+            ss += out[e] * out[e];
+        }
+        if (which < 2) {                          // L2-norm of q and k rows
+            ss = group_sum<G>(ss);
+            const float inv = 1.0f / sqrtf(ss + 1e-6f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) out[e] *= inv;
+        }
+        store8(y + row(t), out);
+        if (which == 0 && lr == 0) {              // gates, once per (token, head)
+            const size_t i = (size_t)t * H + h;
+            const float bias = dt_bias ? dt_bias[h] : 0.f;
+            g[i] = -A[h] * softplus_f32(to_f32(a[i]) + bias);
+            beta[i] = 1.0f / (1.0f + expf(-to_f32(b[i])));
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { x3[e] = x2[e]; x2[e] = x1[e]; x1[e] = xt[e]; }
+    }
+}
+
+template <int D, typename TIO>
+__global__ void __launch_bounds__(256)
+epilogue_kernel(const TIO *y, const TIO *__restrict__ z, const float *__restrict__ w,
+                TIO *out, long rows, float eps)
+{
+    constexpr int G = D / 8;
+    constexpr int GPB = 256 / G;
+    const int lr = threadIdx.x % G;
+    const int c = 8 * lr;
+    float wv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wv[e] = w ? w[c + e] : 1.0f;
+    for (long r = (long)blockIdx.x * GPB + threadIdx.x / G; r < rows;
+         r += (long)gridDim.x * GPB) {
+        float yv[8], zv[8], ov[8];
+        load8(y + (size_t)r * D + c, yv);
+        load8(z + (size_t)r * D + c, zv);
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += yv[e] * yv[e];
+        ss = group_sum<G>(ss);
+        const float inv = 1.0f / sqrtf(ss * (1.0f / D) + eps);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ov[e] = wv[e] * (yv[e] * inv) * silu_f32(zv[e]);
+        store8(out + (size_t)r * D + c, ov);
+    }
+}
+
+template <int D, typename TIO>
+static hipError_t launch_conv(const void *xq, const void *xk, const void *xv, const void *w,
+                              void *yq, void *yk, void *yv, const void *a, const void *b,
+                              const float *A, const float *dtb, float *g, float *beta,
+                              const int32_t *cu, long total, long T, int N, int H, int d_k,
+                              int which0, int nwhich, hipStream_t stream)
+{
+    constexpr int GPB = 256 / (D / 8);
+    const long tiles = (total + PRO_TT - 1) / PRO_TT;
+    dim3 grid((unsigned)((tiles + GPB - 1) / GPB), (unsigned)H, (unsigned)nwhich), block(256);
+    hipLaunchKernelGGL((prologue_conv_kernel<D, TIO>), grid, block, 0, stream,
+                       (const TIO *)xq, (const TIO *)xk, (const TIO *)xv, (const TIO *)w,
+                       (TIO *)yq, (TIO *)yk, (TIO *)yv, (const TIO *)a, (const TIO *)b, A, dtb,
+                       g, beta, cu, total, T, N, H, d_k, which0);
+    return hipGetLastError();
+}
+
+template <typename TIO>
+static hipError_t conv_dispatch(int D, const void *xq, const void *xk, const void *xv,
+                                const void *w, void *yq, void *yk, void *yv, const void *a,
+                                const void *b, const float *A, const float *dtb, float *g,
+                                float *beta, const int32_t *cu, long total, long T, int N, int H,
+                                int d_k, int which0, int nwhich, hipStream_t s)
+{
+    switch (D) {
+    case 16: return launch_conv<16, TIO>(xq, xk, xv, w, yq, yk, yv, a, b, A, dtb, g, beta, cu, total, T, N, H, d_k, which0, nwhich, s);
+    case 32: return launch_conv<32, TIO>(xq, xk, xv, w, yq, yk, yv, a, b, A, dtb, g, beta, cu, total, T, N, H, d_k, which0, nwhich, s);
+    case 64: return launch_conv<64, TIO>(xq, xk, xv, w, yq, yk, yv, a, b, A, dtb, g, beta, cu, total, T, N, H, d_k, which0, nwhich, s);
+    case 128: return launch_conv<128, TIO>(xq, xk, xv, w, yq, yk, yv, a, b, A, dtb, g, beta, cu, total, T, N, H, d_k, which0, nwhich, s);
+    case 256: return launch_conv<256, TIO>(xq, xk, xv, w, yq, yk, yv, a, b, A, dtb, g, beta, cu, total, T, N, H, d_k, which0, nwhich, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename TIO>
+hipError_t launch_prologue(const void *q_raw, const void *k_raw, const void *v_raw,
+                           const void *conv_w, const void *a, const void *b, const float *A,
+                           const float *dt_bias, const int32_t *cu, void *q, void *k, void *v,
+                           float *g, float *beta, int B, int T, int H, int d_k, int d_v, int N,
+                           hipStream_t stream)
+{
+    const long total = (long)B * T;
+    if (total == 0) return hipSuccess;
+    // q and k share a launch (same head size); v has its own.
+    hipError_t e = conv_dispatch<TIO>(d_k, q_raw, k_raw, v_raw, conv_w, q, k, v, a, b, A, dt_bias,
+                                      g, beta, cu, total, (long)T, N, H, d_k, 0, 2, stream);
+    if (e != hipSuccess) return e;
+    return conv_dispatch<TIO>(d_v, q_raw, k_raw, v_raw, conv_w, q, k, v, a, b, A, dt_bias, g,
+                              beta, cu, total, (long)T, N, H, d_k, 2, 1, stream);
+}
+
+template <typename TIO>
+hipError_t launch_epilogue(const void *y, const void *z, const float *w, void *out, long rows,
+                           int d_v, float eps, hipStream_t stream)
+{
+    if (rows == 0) return hipSuccess;
+    auto go = [&](auto kern, int gpb) {
+        long blocks = (rows + gpb - 1) / gpb;
+        if (blocks > 65536) blocks = 65536;
+        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, stream, (const TIO *)y,
+                           (const TIO *)z, w, (TIO *)out, rows, eps);
+        return hipGetLastError();
+    };
+    switch (d_v) {
+    case 16: return go(epilogue_kernel<16, TIO>, 128);
+    case 32: return go(epilogue_kernel<32, TIO>, 64);
+    case 64: return go(epilogue_kernel<64, TIO>, 32);
+    case 128: return go(epilogue_kernel<128, TIO>, 16);
+    case 256: return go(epilogue_kernel<256, TIO>, 8);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template hipError_t launch_prologue<float>(const void *, const void *, const void *, const void *,
+                                           const void *, const void *, const float *,
+                                           const float *, const int32_t *, void *, void *, void *,
+                                           float *, float *, int, int, int, int, int, int,
+                                           hipStream_t);
+template hipError_t launch_prologue<bf16>(const void *, const void *, const void *, const void *,
+                                          const void *, const void *, const float *,
+                                          const float *, const int32_t *, void *, void *, void *,
+                                          float *, float *, int, int, int, int, int, int,
+                                          hipStream_t);
+template hipError_t launch_epilogue<float>(const void *, const void *, const float *, void *,
+                                           long, int, float, hipStream_t);
+template hipError_t launch_epilogue<bf16>(const void *, const void *, const float *, void *, long,
+                                          int, float, hipStream_t);
+
+}  // namespace gdn

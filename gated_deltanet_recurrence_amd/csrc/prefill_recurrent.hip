@@ -1,0 +1,142 @@
+// prefill_recurrent.hip - token-serial form of the gated delta rule over whole
+// sequences, fp32 arithmetic throughout.
+//
+// This is the recurrent execution path of "[LLM Algorithms-2] Gated DeltaNet:
+// Teaching Linear Attention to Overwrite and Forget" (section 5 pseudo-code,
+// section 7 table: recurrent vs chunkwise): for each token, decay the state,
+// retrieve at k, write the gated error along k, read the updated state with q.
+// It serves fp32 inputs (where a bf16 matrix-core path would not meet fp32
+// accuracy), head sizes other than 128, and is the on-GPU cross-check of the
+// chunkwise kernel.
+//
+// Work mapping: grid (row blocks, H, N). A state row (d_k floats) lives in
+// the registers of G = d_k/8 lanes for the whole sequence; rows never
+// exchange data, so there is no barrier anywhere. Per token each lane group
+// needs three length-d_k dot products (S.k, S.q, k.q), reduced with DPP.
+// The next token's q, k, v, g, beta are fetched while the current token is
+// being processed.
+#include "common.h"
+
+namespace gdn {
+
+template <int DK, typename TIO>
+__global__ void __launch_bounds__(256)
+prefill_recurrent_kernel(const TIO *__restrict__ q, const TIO *__restrict__ k,
+                         const TIO *__restrict__ v, const float *__restrict__ g,
+                         const float *__restrict__ beta, const float *s_init,
+                         float *s_final, TIO *__restrict__ o,
+                         const int32_t *__restrict__ cu_seqlens, int T, int H, int d_v,
+                         float scale)
+{
+    constexpr int G = DK / 8;
+    constexpr int RPB = 256 / G;              // state rows per workgroup
+    const int h = blockIdx.y, n = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int lr = tid % G;
+    const int row = blockIdx.x * RPB + tid / G;
+    const bool active = row < d_v;            // uniform inside a row group
+    const int c0 = 4 * lr, c1 = DK / 2 + 4 * lr;
+
+    long bos, eos;
+    if (cu_seqlens) {
+        long a = cu_seqlens[n], b = cu_seqlens[n + 1];
+        a = a < 0 ? 0 : (a > T ? T : a);
+        b = b < a ? a : (b > T ? T : b);
+        bos = a;
+        eos = b;
+    } else {
+        bos = (long)n * T;
+        eos = bos + T;
+    }
+
+    const size_t sbase = (((size_t)n * H + h) * d_v + (active ? row : 0)) * DK;
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    if (s_init && active) {
+        s0 = load4(s_init + sbase + c0);
+        s1 = load4(s_init + sbase + c1);
+    }
+
+    const int vrow = active ? row : 0;
+    auto fetch = [&](long t, f32x4 &k0, f32x4 &k1, f32x4 &q0, f32x4 &q1, float &vv, float &gg,
+                     float &bb) {
+        const size_t tk = ((size_t)t * H + h) * DK;
+        k0 = load4(k + tk + c0);
+        k1 = load4(k + tk + c1);
+        q0 = load4(q + tk + c0);
+        q1 = load4(q + tk + c1);
+        vv = to_f32(v[((size_t)t * H + h) * d_v + vrow]);
+        gg = g[(size_t)t * H + h];
+        bb = beta[(size_t)t * H + h];
+    };
+
+    f32x4 k0, k1, q0, q1;
+    float vv = 0.f, gg = 0.f, bb = 0.f;
+    if (bos < eos)
+        fetch(bos, k0, k1, q0, q1, vv, gg, bb);
+    for (long t = bos; t < eos; ++t) {
+        f32x4 nk0 = k0, nk1 = k1, nq0 = q0, nq1 = q1;
+        float nvv = vv, ngg = gg, nbb = bb;
+        if (t + 1 < eos)
+            fetch(t + 1, nk0, nk1, nq0, nq1, nvv, ngg, nbb);
+
+        const float alpha = __expf(gg);
+        float sk = 0.f, sq = 0.f, kq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sk += s0[e] * k0[e] + s1[e] * k1[e];
+            sq += s0[e] * q0[e] + s1[e] * q1[e];
+            kq += k0[e] * q0[e] + k1[e] * q1[e];
+        }
+        sk = group_sum<G>(sk);
+        sq = group_sum<G>(sq);
+        kq = group_sum<G>(kq);
+        const float delta = bb * (vv - alpha * sk);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            s0[e] = alpha * s0[e] + delta * k0[e];
+            s1[e] = alpha * s1[e] + delta * k1[e];
+        }
+        if (active && lr == 0)
+            o[((size_t)t * H + h) * d_v + row] = from_f32<TIO>(scale * (alpha * sq + delta * kq));
+
+        k0 = nk0; k1 = nk1; q0 = nq0; q1 = nq1;
+        vv = nvv; gg = ngg; bb = nbb;
+    }
+    if (s_final && active) {
+        store4(s_final + sbase + c0, s0);
+        store4(s_final + sbase + c1, s1);
+    }
+}
+
+template <typename TIO>
+hipError_t launch_prefill_recurrent(const void *q, const void *k, const void *v, const float *g,
+                                    const float *beta, const float *s_init, float *s_final,
+                                    void *o, const int32_t *cu_seqlens, int T, int H, int d_k,
+                                    int d_v, int N, float scale, hipStream_t stream)
+{
+    auto go = [&](auto kern, int rpb) {
+        dim3 grid((unsigned)((d_v + rpb - 1) / rpb), (unsigned)H, (unsigned)N), block(256);
+        hipLaunchKernelGGL(kern, grid, block, 0, stream, (const TIO *)q, (const TIO *)k,
+                           (const TIO *)v, g, beta, s_init, s_final, (TIO *)o, cu_seqlens, T,
+                           H, d_v, scale);
+        return hipGetLastError();
+    };
+    switch (d_k) {
+    case 16: return go(prefill_recurrent_kernel<16, TIO>, 256 / 2);
+    case 32: return go(prefill_recurrent_kernel<32, TIO>, 256 / 4);
+    case 64: return go(prefill_recurrent_kernel<64, TIO>, 256 / 8);
+    case 128: return go(prefill_recurrent_kernel<128, TIO>, 256 / 16);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template hipError_t launch_prefill_recurrent<float>(const void *, const void *, const void *,
+                                                    const float *, const float *, const float *,
+                                                    float *, void *, const int32_t *, int, int,
+                                                    int, int, int, float, hipStream_t);
+template hipError_t launch_prefill_recurrent<bf16>(const void *, const void *, const void *,
+                                                   const float *, const float *, const float *,
+                                                   float *, void *, const int32_t *, int, int,
+                                                   int, int, int, float, hipStream_t);
+
+}  // namespace gdn

@@ -1,0 +1,212 @@
+/*
+ * gdn.h - C ABI of the MI355X (gfx950) Gated Delta Rule token-mixer library
+ * (libgdn.so).
+ *
+ * The library computes the gated delta rule of
+ *   "[LLM Algorithms-2] Gated DeltaNet: Teaching Linear Attention to
+ *    Overwrite and Forget", section 4 (boxed update) and section 5:
+ *
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = scale * S_t q_t
+ *
+ * with one state S of shape d_v x d_k per (sequence, head). The decay is
+ * applied before the retrieval (section 4.3 of the same page) and the readout
+ * uses the updated state.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer (memory from hipMalloc or a
+ *    device allocator on the device current when the call is made). The
+ *    caller owns and allocates every buffer; the library keeps no pointer
+ *    after a call returns and allocates no device memory.
+ *  - Activations are token-major and C-contiguous: q, k are [B][T][H][d_k];
+ *    v, o are [B][T][H][d_v]; per-token scalars are [B][T][H].
+ *  - States are fp32, [N][H][d_v][d_k] with d_k contiguous.
+ *  - The decay gate is passed in log space: g = log(alpha), fp32 (alpha =
+ *    exp(g) <= 1 for g <= 0). beta is fp32, one scalar per (token, head).
+ *  - dtype (gdn_dtype_t) selects the storage type of q, k, v and of the
+ *    output o: GDN_DTYPE_F32 or GDN_DTYPE_BF16. All arithmetic accumulates in
+ *    fp32; bf16 tensors are rounded to nearest-even on store.
+ *  - stream is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls only enqueue work and return; results are valid once the stream
+ *    has reached that point. Launch errors are reported by the call itself;
+ *    faults during execution surface at the caller's next synchronisation.
+ *  - Arguments are validated before anything is enqueued. On error nothing is
+ *    enqueued and a negative gdn_status_t is returned; gdn_status_string()
+ *    describes it. No call aborts the process or throws.
+ *  - Calls on different streams may run concurrently when their output
+ *    buffers are disjoint.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_VERSION 1
+
+typedef enum {
+    GDN_DTYPE_F32 = 0,
+    GDN_DTYPE_BF16 = 1
+} gdn_dtype_t;
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL = -1,        /* a required pointer is NULL                        */
+    GDN_ERR_SHAPE = -2,       /* a size is negative, zero where not allowed, or
+                                 inconsistent with another argument                 */
+    GDN_ERR_DTYPE = -3,       /* dtype is not a gdn_dtype_t value                   */
+    GDN_ERR_UNSUPPORTED = -4, /* valid but not implemented (e.g. head dim > 128)    */
+    GDN_ERR_HIP = -5          /* the HIP runtime reported an error at launch        */
+} gdn_status_t;
+
+/* Library version (GDN_VERSION). */
+int gdn_version(void);
+
+/* Static description of a status code (never NULL). */
+const char *gdn_status_string(int status);
+
+/*
+ * gdn_prefill - forward pass of the gated delta rule over whole sequences,
+ * computed chunkwise ("5. Linear Attention" chapter, section "Chunk
+ * implementation of the Delta Rule", stages 1-3; "Overwrite and Forget",
+ * section 7): per chunk of 64 tokens the intra-chunk key Gram system is
+ * solved as a unit-lower-triangular inverse and the chunk is applied to the
+ * state as one update; the state is carried in fp32 from chunk to chunk.
+ * The result equals the token-by-token recurrence up to rounding.
+ *
+ *   q, k          [B][T][H][d_k], dtype
+ *   v             [B][T][H][d_v], dtype
+ *   g, beta       [B][T][H] fp32 (g = log alpha)
+ *   initial_state [N][H][d_v][d_k] fp32, or NULL for a zero initial state
+ *   final_state   [N][H][d_v][d_k] fp32, or NULL to skip; may alias
+ *                 initial_state (in-place continuation)
+ *   o             [B][T][H][d_v], dtype; must not alias any input
+ *   cu_seqlens    NULL: N must equal B and each batch row is one sequence of
+ *                 T tokens. Otherwise a DEVICE int32 array of N+1 offsets
+ *                 that packs N sequences along the T axis of a single batch
+ *                 row: B must be 1, cu_seqlens[0] = 0, non-decreasing,
+ *                 cu_seqlens[N] = T. Sequence n is tokens [cu[n], cu[n+1]);
+ *                 empty sequences are allowed (their final state equals their
+ *                 initial state). The offsets are read only on the device;
+ *                 kernels clamp them into [0, T] and treat a decreasing pair
+ *                 as an empty sequence, so malformed offsets give wrong
+ *                 results but never out-of-range accesses. Check offsets on
+ *                 the host with gdn_check_cu_seqlens() when in doubt.
+ *   B, T, H, N    B >= 1, T >= 0, 1 <= H <= 65535, 1 <= N <= 65535,
+ *                 B*T < 2^31. When B*T = 0 the activation
+ *                 pointers (q, k, v, g, beta, o) are not read and may be NULL.
+ *   d_k, d_v      d_k in {16, 32, 64, 128}; 1 <= d_v <= 128 (else
+ *                 GDN_ERR_UNSUPPORTED). bf16 with d_k = d_v = 128 runs the
+ *                 MFMA chunk kernel; every other case runs the fp32
+ *                 token-serial kernel (same result up to rounding).
+ *   scale         multiplies every output (d_k^-1/2 in the usual layer)
+ */
+int gdn_prefill(const void *q, const void *k, const void *v,
+                const float *g, const float *beta,
+                const float *initial_state, float *final_state,
+                void *o, const int32_t *cu_seqlens,
+                int B, int T, int H, int d_k, int d_v, int N,
+                float scale, int dtype, void *stream);
+
+/*
+ * gdn_prefill_recurrent - the same forward pass as gdn_prefill, computed by
+ * the token-serial recurrence in fp32 arithmetic (the "recurrent" execution
+ * path of "Overwrite and Forget", section 7). Same arguments, layouts and
+ * errors as gdn_prefill. gdn_prefill itself uses this path for fp32 tensors
+ * and for head sizes other than d_k = d_v = 128; calling it directly gives
+ * the chunkwise path an independent on-device cross-check.
+ */
+int gdn_prefill_recurrent(const void *q, const void *k, const void *v,
+                          const float *g, const float *beta,
+                          const float *initial_state, float *final_state,
+                          void *o, const int32_t *cu_seqlens,
+                          int B, int T, int H, int d_k, int d_v, int N,
+                          float scale, int dtype, void *stream);
+
+/*
+ * gdn_decode_step - one recurrent step for B independent sequences, updating
+ * an HBM-resident state in place ("Overwrite and Forget", section 5
+ * pseudo-code; "6.6 Gated DeltaNet" section 6.6.8, inference flow):
+ *
+ *   r = alpha S k;  delta = beta (v - r);  S <- alpha S + delta k^T;
+ *   o = scale S q
+ *
+ * Each state row is read once and written once.
+ *
+ *   q, k       [B][H][d_k], dtype
+ *   v          [B][H][d_v], dtype
+ *   g, beta    [B][H] fp32
+ *   state      [B][H][d_v][d_k] fp32, read and overwritten in place
+ *   o          [B][H][d_v], dtype
+ *   d_k, d_v   d_k in {16, 32, 64, 128}; 1 <= d_v <= 4096
+ */
+int gdn_decode_step(const void *q, const void *k, const void *v,
+                    const float *g, const float *beta,
+                    float *state, void *o,
+                    int B, int H, int d_k, int d_v,
+                    float scale, int dtype, void *stream);
+
+/*
+ * gdn_mixer_prologue - everything between the input projections and the
+ * recurrence ("5. Linear Attention" chapter, sections "Causal Conv1d" and
+ * "Gated DeltaNet body"; "6.6 Gated DeltaNet" sections 6.6.3-6.6.4):
+ *
+ *   1. depthwise causal convolution with 4 taps over every channel of q, k,
+ *      v (zero history before each sequence start, no bias), then SiLU;
+ *   2. L2 normalisation of q and k per (token, head):
+ *      x / sqrt(sum x^2 + 1e-6);
+ *   3. gates: g = -A[h] * softplus(a + dt_bias[h]),  beta = sigmoid(b).
+ *
+ *   q_raw, k_raw   [B][T][H][d_k], dtype        (projection outputs)
+ *   v_raw          [B][T][H][d_v], dtype
+ *   conv_w         [H*(2*d_k + d_v)][4], dtype; channel order: all q
+ *                  channels (head-major), then k, then v; tap 3 multiplies
+ *                  the current token, tap 0 the token three steps back
+ *   a, b           [B][T][H], dtype
+ *   A              [H] fp32 (positive decay rates)
+ *   dt_bias        [H] fp32, or NULL for zero
+ *   cu_seqlens     as for gdn_prefill (NULL: each batch row is a sequence)
+ *   q, k, v        outputs, same shapes and dtype as the raw inputs; must not
+ *                  alias them
+ *   g, beta        outputs [B][T][H] fp32
+ *   d_k, d_v       each in {16, 32, 64, 128, 256} (else GDN_ERR_UNSUPPORTED)
+ */
+int gdn_mixer_prologue(const void *q_raw, const void *k_raw, const void *v_raw,
+                       const void *conv_w, const void *a, const void *b,
+                       const float *A, const float *dt_bias,
+                       const int32_t *cu_seqlens,
+                       void *q, void *k, void *v, float *g, float *beta,
+                       int B, int T, int H, int d_k, int d_v, int N,
+                       int dtype, void *stream);
+
+/*
+ * gdn_mixer_epilogue - gated RMSNorm of the recurrence output ("5. Linear
+ * Attention" chapter, section "Gated RMSNorm"; "6.6 Gated DeltaNet" section
+ * 6.6.2, output gate), per (token, head) row of d_v values:
+ *
+ *   out = norm_w * y / sqrt(mean(y^2) + eps) * silu(z)
+ *
+ *   y, z, out   [rows][H][d_v], dtype (rows = B*T); out may alias y
+ *   norm_w      [d_v] fp32, or NULL for ones
+ *   d_v         in {16, 32, 64, 128, 256} (else GDN_ERR_UNSUPPORTED)
+ */
+int gdn_mixer_epilogue(const void *y, const void *z, const float *norm_w, void *out,
+                       int rows, int H, int d_v, float eps, int dtype, void *stream);
+
+/*
+ * gdn_check_cu_seqlens - host-side validation of packed-sequence offsets.
+ * cu is a HOST array of N+1 entries. Returns GDN_OK when cu[0] = 0, the
+ * offsets are non-decreasing and cu[N] = T; GDN_ERR_SHAPE otherwise;
+ * GDN_ERR_NULL for a NULL pointer.
+ */
+int gdn_check_cu_seqlens(const int32_t *cu, int N, int T);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

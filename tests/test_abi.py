@@ -1,0 +1,113 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/gdn.h, and rejects bad arguments with the documented status
+codes before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_UNSUPPORTED = 0, -1, -2, -3, -4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char \*)\s*(gdn_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from gated_deltanet_recurrence_amd import _binding
+    if not os.path.exists(_binding.LIB_PATH):
+        from gated_deltanet_recurrence_amd import build
+        build.build()
+    return _binding.load()
+
+
+def test_header_and_binding_agree(lib):
+    from gated_deltanet_recurrence_amd import _binding
+    decl = declared_functions()
+    assert len(decl) >= 8
+    assert sorted(_binding.EXPORTED) == decl
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.gdn_version() == 1
+    for st in (GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_UNSUPPORTED, -5, 99):
+        s = lib.gdn_status_string(st)
+        assert isinstance(s, bytes) and len(s) > 0
+
+
+P = ctypes.c_void_p(16)      # a non-null dummy pointer; never dereferenced on rejection
+
+
+def _prefill(lib, *, null=None, B=1, T=8, H=1, dk=128, dv=128, N=1, dtype=1, cu=None):
+    ptrs = [P] * 8
+    if null is not None:
+        ptrs[null] = None
+    q, k, v, g, beta, s0, s1, o = ptrs
+    return lib.gdn_prefill(q, k, v, g, beta, s0, s1, o, cu, B, T, H, dk, dv, N, 1.0, dtype, None)
+
+
+@pytest.mark.parametrize("which", [0, 1, 2, 3, 4, 7])
+def test_prefill_null_pointers(lib, which):
+    assert _prefill(lib, null=which) == GDN_ERR_NULL
+
+
+def test_prefill_null_allowed_without_tokens(lib):
+    # T = 0 with NULL activations passes validation (nothing is read); it is not
+    # launched here, so only a rejection for another reason would show up
+    assert _prefill(lib, null=0, T=0, dk=48) == GDN_ERR_UNSUPPORTED
+
+
+def test_prefill_validation(lib):
+    assert _prefill(lib, dtype=7) == GDN_ERR_DTYPE
+    assert _prefill(lib, B=0) == GDN_ERR_SHAPE
+    assert _prefill(lib, T=-1) == GDN_ERR_SHAPE
+    assert _prefill(lib, H=0) == GDN_ERR_SHAPE
+    assert _prefill(lib, B=2, N=1) == GDN_ERR_SHAPE          # N must equal B without offsets
+    assert _prefill(lib, B=2, N=2, cu=P) == GDN_ERR_SHAPE    # packed sequences need B == 1
+    assert _prefill(lib, dk=48) == GDN_ERR_UNSUPPORTED
+    assert _prefill(lib, dv=256) == GDN_ERR_UNSUPPORTED
+    assert _prefill(lib, B=1 << 16, N=1 << 16, T=1 << 16) == GDN_ERR_SHAPE
+
+
+def test_decode_validation(lib):
+    f = lib.gdn_decode_step
+    assert f(P, P, P, P, P, None, P, 1, 1, 128, 128, 1.0, 1, None) == GDN_ERR_NULL
+    assert f(P, P, P, P, P, P, P, 1, 1, 128, 128, 1.0, 2, None) == GDN_ERR_DTYPE
+    assert f(P, P, P, P, P, P, P, 0, 1, 128, 128, 1.0, 1, None) == GDN_ERR_SHAPE
+    assert f(P, P, P, P, P, P, P, 1, 1, 100, 128, 1.0, 1, None) == GDN_ERR_UNSUPPORTED
+
+
+def test_mixer_validation(lib):
+    pro = lib.gdn_mixer_prologue
+    args = [P] * 7 + [None, None] + [P] * 5
+    bad = list(args)
+    bad[0] = None
+    assert pro(*bad, 1, 4, 1, 128, 128, 1, 1, None) == GDN_ERR_NULL
+    assert pro(*args, 1, 4, 1, 128, 128, 1, 5, None) == GDN_ERR_DTYPE
+    assert pro(*args, 1, 4, 1, 96, 128, 1, 1, None) == GDN_ERR_UNSUPPORTED
+    assert pro(*args, 2, 4, 1, 128, 128, 1, 1, None) == GDN_ERR_SHAPE
+    epi = lib.gdn_mixer_epilogue
+    assert epi(None, P, None, P, 4, 1, 128, 1e-6, 1, None) == GDN_ERR_NULL
+    assert epi(P, P, None, P, 4, 1, 100, 1e-6, 1, None) == GDN_ERR_UNSUPPORTED
+    assert epi(P, P, None, P, -1, 1, 128, 1e-6, 1, None) == GDN_ERR_SHAPE
+
+
+def test_check_cu_seqlens(lib):
+    arr = lambda xs: (ctypes.c_int32 * len(xs))(*xs)
+    f = lib.gdn_check_cu_seqlens
+    assert f(arr([0, 5, 5, 12]), 3, 12) == GDN_OK
+    assert f(arr([0, 5, 4, 12]), 3, 12) == GDN_ERR_SHAPE
+    assert f(arr([1, 5, 12]), 2, 12) == GDN_ERR_SHAPE
+    assert f(arr([0, 5, 11]), 2, 12) == GDN_ERR_SHAPE
+    assert f(None, 2, 12) == GDN_ERR_NULL

@@ -1,0 +1,287 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every input is seeded and synthetic (gated_deltanet_recurrence_amd.inputs);
+the oracle receives exactly the values the GPU receives (bf16/fp32 upcast to
+fp64). Tolerances: max over (sequence, head) slices of the inf-norm relative
+error, 1e-4 for fp32 inputs and 2e-2 for bf16 inputs with an fp32 state, on
+outputs and final states separately.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import gated_deltanet_recurrence_amd as gdn
+from gated_deltanet_recurrence_amd import inputs
+from parity import (TOL_BF16, TOL_F32, dev, host64, o_err, o_err_packed, report, s_err)
+
+pytestmark = pytest.mark.gpu
+
+
+def _tol(case):
+    return TOL_F32 if case.dtype == "f32" else TOL_BF16
+
+
+def run_prefill(case, entry=None, with_final=True, init=True):
+    entry = entry or gdn.gdn_prefill
+    s0 = dev(case.s0) if (init and case.s0 is not None) else None
+    fin = torch.empty((case.N, case.H, case.d_v, case.d_k), dtype=torch.float32,
+                      device="cuda:0") if with_final else None
+    o, _ = entry(dev(case.q), dev(case.k), dev(case.v), dev(case.g), dev(case.beta), s0, fin,
+                 cu_seqlens=dev(case.cu_seqlens), scale=case.scale)
+    torch.cuda.synchronize()
+    return o, fin
+
+
+def oracle_prefill(case, init=True):
+    return oracle.gdn_recurrent(case.q, case.k, case.v, case.g, case.beta,
+                                case.s0 if init else None, case.cu_seqlens, case.scale)
+
+
+# --- the five workloads ------------------------------------------------------
+
+def test_tiny_fp32():
+    """B=1, H=1, T=64, d=16, fp32: the fp32 path meets 1e-4."""
+    c = inputs.make_tiny()
+    o, fin = run_prefill(c)
+    o_ref, s_ref = oracle_prefill(c)
+    eo, es = o_err(o, o_ref), s_err(fin, s_ref)
+    report("tiny fp32", o=eo, state=es)
+    assert eo <= TOL_F32 and es <= TOL_F32
+
+
+@pytest.fixture(scope="module")
+def prefill_full():
+    return inputs.make_prefill()
+
+
+def test_prefill_full_size(prefill_full):
+    """B=4, H=16, T=4096, d=128, bf16, zero initial state: all 64 chains."""
+    c = prefill_full
+    o, fin = run_prefill(c)
+    o_ref, s_ref = oracle_prefill(c)
+    eo, es = o_err(o, o_ref), s_err(fin, s_ref)
+    report("prefill B4 H16 T4096", o=eo, state=es)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_decode_full_size():
+    """B=256, H=32, d=128: one in-place step of the 512 MiB fp32 state."""
+    c = inputs.make_decode()
+    st = dev(c.s0)
+    o = gdn.gdn_decode_step(dev(c.q[:, 0]), dev(c.k[:, 0]), dev(c.v[:, 0]), dev(c.g[:, 0]),
+                            dev(c.beta[:, 0]), st, scale=c.scale)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_prefill(c)
+    eo, es = o_err(o[:, None], o_ref), s_err(st, s_ref)
+    report("decode B256 H32", o=eo, state=es)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_mixer_full_size_sampled():
+    """B=8, T=8192, H=16, d=128 bf16 raw inputs through prologue -> prefill ->
+    epilogue on the GPU; the oracle recomputes two batch rows x three heads
+    from the raw inputs (heads never mix, so a slice is exact)."""
+    c = inputs.make_mixer()
+    q, k, v, g, beta = gdn.gdn_mixer_prologue(dev(c.q_raw), dev(c.k_raw), dev(c.v_raw),
+                                              dev(c.conv_w), dev(c.a), dev(c.b), dev(c.A))
+    y, _ = gdn.gdn_prefill(q, k, v, g, beta, scale=c.scale)
+    out = gdn.gdn_mixer_epilogue(y, dev(c.z), eps=c.eps)
+    torch.cuda.synchronize()
+    rows, heads = [0, 7], [0, 9, 15]
+    ref, mid = oracle.mixer(c.q_raw, c.k_raw, c.v_raw, c.z, c.a, c.b, c.conv_w, c.A,
+                            scale=c.scale, eps=c.eps, heads=heads, rows=rows,
+                            return_intermediates=True)
+    sel = lambda t: t[rows][:, :, heads]
+    e_out = o_err(sel(out.cpu()), ref)
+    e_q = o_err(sel(q.cpu()), mid["q"])
+    e_v = o_err(sel(v.cpu()), mid["v"])
+    e_g = float(np.abs(host64(sel(g.cpu())) - mid["g"]).max() / np.abs(mid["g"]).max())
+    e_b = float(np.abs(host64(sel(beta.cpu())) - mid["beta"]).max())
+    e_y = o_err(sel(y.cpu()), mid["y"])
+    report("mixer B8 T8192 H16", out=e_out, q=e_q, v=e_v, g=e_g, beta=e_b, y=e_y)
+    assert max(e_q, e_v) <= TOL_BF16 and e_g <= 1e-5 and e_b <= 1e-6
+    assert e_y <= TOL_BF16 and e_out <= TOL_BF16
+
+
+def test_varlen_full_size_sampled():
+    """H=32, d=128, 8 packed sequences (lengths log-uniform in [512, 65536]),
+    non-zero initial states: every sequence, four heads."""
+    c = inputs.make_varlen()
+    o, fin = run_prefill(c)
+    heads = [0, 5, 17, 31]
+    cu = [int(x) for x in c.cu_seqlens.tolist()]
+    outs, s_ref = oracle.gdn_recurrent_heads(c.q, c.k, c.v, c.g, c.beta, heads, c.s0,
+                                             c.cu_seqlens, c.scale, nthreads=0)
+    o_h = o.cpu()[:, :, heads]
+    eo = max(o_err(o_h[:, a:b], r) for (a, b), r in zip(zip(cu[:-1], cu[1:]), outs) if b > a)
+    es = s_err(fin.cpu()[:, heads], s_ref)
+    report(f"varlen lengths={c.meta['lengths']}", o=eo, state=es)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+# --- smaller shapes: tiles, ragged tails, edge cases ------------------------
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 130, 257])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_prefill_ragged_bf16(T, with_state):
+    c = inputs.make_prefill(seed=1000 + T, B=2, T=T, H=3, d=128, with_state=with_state)
+    o, fin = run_prefill(c)
+    o_ref, s_ref = oracle_prefill(c)
+    eo, es = o_err(o, o_ref), s_err(fin, s_ref)
+    report(f"prefill bf16 T={T} state={with_state}", o=eo, state=es)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_head_dims(d, dtype):
+    c = inputs.make_prefill(seed=2000 + d, B=2, T=77, H=2, d=d, dtype=dtype, with_state=True)
+    o, fin = run_prefill(c)
+    o_ref, s_ref = oracle_prefill(c)
+    eo, es = o_err(o, o_ref), s_err(fin, s_ref)
+    report(f"prefill {dtype} d={d}", o=eo, state=es)
+    tol = _tol(c)
+    assert eo <= tol and es <= tol
+
+
+def test_prefill_fp32_d128():
+    """fp32 inputs at d=128 meet the fp32 tolerance."""
+    c = inputs.make_prefill(seed=7, B=1, T=300, H=2, d=128, dtype="f32", with_state=True)
+    o, fin = run_prefill(c)
+    o_ref, s_ref = oracle_prefill(c)
+    eo, es = o_err(o, o_ref), s_err(fin, s_ref)
+    report("prefill f32 d=128", o=eo, state=es)
+    assert eo <= TOL_F32 and es <= TOL_F32
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_small(dtype):
+    c = inputs.make_decode(seed=31, B=5, H=3, d=128, dtype=dtype)
+    st = dev(c.s0)
+    o = gdn.gdn_decode_step(dev(c.q[:, 0]), dev(c.k[:, 0]), dev(c.v[:, 0]), dev(c.g[:, 0]),
+                            dev(c.beta[:, 0]), st, scale=c.scale)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_prefill(c)
+    eo, es = o_err(o[:, None], o_ref), s_err(st, s_ref)
+    report(f"decode {dtype}", o=eo, state=es)
+    assert eo <= _tol(c) and es <= _tol(c)
+
+
+@pytest.mark.parametrize("d", [16, 32, 64])
+def test_decode_head_dims(d):
+    c = inputs.make_decode(seed=40 + d, B=3, H=2, d=d, dtype="f32")
+    st = dev(c.s0)
+    o = gdn.gdn_decode_step(dev(c.q[:, 0]), dev(c.k[:, 0]), dev(c.v[:, 0]), dev(c.g[:, 0]),
+                            dev(c.beta[:, 0]), st, scale=c.scale)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_prefill(c)
+    assert o_err(o[:, None], o_ref) <= TOL_F32 and s_err(st, s_ref) <= TOL_F32
+
+
+def test_packed_with_empty_and_tiny_sequences():
+    """Packed sequences including empty ones and ones shorter than a chunk; an
+    empty sequence returns its initial state."""
+    lengths = [0, 1, 64, 0, 3, 129, 70]
+    c = inputs.make_varlen(seed=55, H=2, d=128, lengths=lengths)
+    o, fin = run_prefill(c)
+    o_ref, s_ref = oracle_prefill(c)
+    cu = [int(x) for x in c.cu_seqlens.tolist()]
+    eo, es = o_err_packed(o, o_ref, cu), s_err(fin, s_ref)
+    report("packed with empties", o=eo, state=es)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+    for n, L in enumerate(lengths):
+        if L == 0:
+            assert torch.equal(fin[n].cpu(), c.s0[n])
+
+
+def test_zero_length_batch():
+    """T = 0: nothing to compute; the final state is the initial state."""
+    c = inputs.make_prefill(seed=3, B=2, T=0, H=2, d=128, with_state=True)
+    o, fin = run_prefill(c)
+    assert o.numel() == 0 and torch.equal(fin.cpu(), c.s0)
+
+
+def test_gate_special_cases():
+    """beta = 0, alpha = 1 leaves the state unchanged; beta = 0 alone scales it."""
+    c = inputs.make_prefill(seed=4, B=1, T=100, H=2, d=128, with_state=True)
+    c.beta.zero_()
+    c.g.zero_()
+    _, fin = run_prefill(c)
+    assert s_err(fin, host64(c.s0)) <= 1e-6
+    c = inputs.make_prefill(seed=5, B=1, T=100, H=2, d=128, with_state=True)
+    c.beta.zero_()
+    c.g.mul_(0.02)                     # keep the accumulated decay well above denormals
+    _, fin = run_prefill(c)
+    decay = np.exp(host64(c.g)[0].sum(axis=0))            # [H]
+    assert s_err(fin, host64(c.s0) * decay[None, :, None, None]) <= 1e-4
+
+
+# --- execution-path consistency ---------------------------------------------
+
+def test_split_resume():
+    """prefill(T1) -> state -> prefill(T2, state) equals prefill(T1 + T2), and
+    prefill followed by decode steps equals a longer prefill."""
+    c = inputs.make_prefill(seed=9, B=2, T=200, H=2, d=128, with_state=True)
+    o_all, f_all = run_prefill(c)
+    T1 = 77
+    fin1 = torch.empty_like(f_all)
+    o1, _ = gdn.gdn_prefill(dev(c.q[:, :T1]), dev(c.k[:, :T1]), dev(c.v[:, :T1]),
+                            dev(c.g[:, :T1]), dev(c.beta[:, :T1]), dev(c.s0), fin1, scale=c.scale)
+    fin2 = torch.empty_like(f_all)
+    o2, _ = gdn.gdn_prefill(dev(c.q[:, T1:196]), dev(c.k[:, T1:196]), dev(c.v[:, T1:196]),
+                            dev(c.g[:, T1:196]), dev(c.beta[:, T1:196]), fin1, fin2,
+                            scale=c.scale)
+    st = fin2.clone()
+    outs = []
+    for t in range(196, 200):
+        outs.append(gdn.gdn_decode_step(dev(c.q[:, t]), dev(c.k[:, t]), dev(c.v[:, t]),
+                                        dev(c.g[:, t]), dev(c.beta[:, t]), st, scale=c.scale))
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_prefill(c)
+    o_cat = torch.cat([o1, o2, torch.stack(outs, 1)], 1)
+    eo, es = o_err(o_cat, o_ref), s_err(st, s_ref)
+    report("split/resume", o=eo, state=es)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+    assert o_err(o_cat, host64(o_all)) <= TOL_BF16
+
+
+def test_in_place_state_continuation():
+    """initial_state and final_state may be the same buffer."""
+    c = inputs.make_prefill(seed=12, B=2, T=90, H=2, d=128, with_state=True)
+    st = dev(c.s0)
+    gdn.gdn_prefill(dev(c.q), dev(c.k), dev(c.v), dev(c.g), dev(c.beta), st, st, scale=c.scale)
+    torch.cuda.synchronize()
+    _, s_ref = oracle_prefill(c)
+    assert s_err(st, s_ref) <= TOL_BF16
+
+
+def test_chunk_matches_recurrent_on_gpu():
+    """The chunkwise path and the token-serial path agree ("parallel, chunkwise
+    and recurrent paths must agree" - Overwrite and Forget, section 7)."""
+    c = inputs.make_prefill(seed=13, B=2, T=333, H=4, d=128, with_state=True)
+    o_c, f_c = run_prefill(c)
+    o_r, f_r = run_prefill(c, entry=gdn.gdn_prefill_recurrent)
+    assert o_err(o_c, host64(o_r)) <= TOL_BF16 and s_err(f_c, host64(f_r)) <= TOL_BF16
+
+
+def test_deterministic():
+    c = inputs.make_prefill(seed=14, B=2, T=300, H=2, d=128, with_state=True)
+    o1, f1 = run_prefill(c)
+    o2, f2 = run_prefill(c)
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+def test_prologue_packed_sequences():
+    """The convolution history restarts at each packed sequence start."""
+    c = inputs.make_mixer(seed=21, B=1, T=300, H=2, d=128)
+    cu = torch.tensor([0, 5, 5, 130, 300], dtype=torch.int32)
+    q, k, v, g, beta = gdn.gdn_mixer_prologue(dev(c.q_raw), dev(c.k_raw), dev(c.v_raw),
+                                              dev(c.conv_w), dev(c.a), dev(c.b), dev(c.A),
+                                              cu_seqlens=dev(cu))
+    torch.cuda.synchronize()
+    _, mid = oracle.mixer(c.q_raw, c.k_raw, c.v_raw, c.z, c.a, c.b, c.conv_w, c.A,
+                          scale=c.scale, cu_seqlens=cu.tolist(), return_intermediates=True)
+    assert o_err(q.cpu(), mid["q"]) <= TOL_BF16
+    assert o_err(k.cpu(), mid["k"]) <= TOL_BF16
+    assert o_err(v.cpu(), mid["v"]) <= TOL_BF16
