@@ -1,0 +1,286 @@
+"""Benchmark of the Gated Delta Rule hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill,decode,...]
+
+A step is one gdn_prefill call over the chunked-prefill workload (B=4, H=16,
+T=4096, d_k=d_v=128, bf16 q/k/v, fp32 gates and state, zero initial state);
+``value`` is prefill tokens/s (B*T per step). The same JSON line carries:
+
+* ``roofline`` of the prefill chunk kernel: algorithmic HBM bytes per launch
+  (q, k, v, o in bf16 and g, beta in fp32 per token-head, plus the fp32 final
+  state) over its average launch time, against 8 TB/s; the algorithmic
+  matrix-core rate against the 2.5 PFLOP/s dense bf16 peak is given too;
+  ``traffic`` is the measured HBM bytes per launch from the committed counter
+  summary (profiles/), or null when the kernel source has changed since;
+* ``decode``: one in-place step of B=256, H=32, d=128 fp32 states (512 MiB),
+  GB/s of algorithmic traffic and its fraction of 8 TB/s;
+* ``mixer``: prologue -> prefill -> epilogue at B=8, T=8192, H=16, d=128;
+* ``varlen``: packed prefill, H=32, 8 sequences, lengths log-uniform in
+  [512, 65536], non-zero initial states;
+* ``cpu_baseline``: the fp64 CPU oracle timed on this host on the prefill
+  workload (a reported baseline, not a target).
+
+Timing: warm-up launches, then K launches bracketed by device
+synchronisation and timed with HIP events recorded on the stream the kernels
+run on (torch's current stream, which the binding launches on). Prefill
+inputs and outputs alternate between two copies so that successive launches
+read from HBM rather than from the 256 MB last-level cache.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, TFLOP/s
+METRIC = "prefill tokens/s (H=16,d=128,T=4096) + decode state GB/s vs HBM peak"
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "prefill_chunk_B4_H16_T4096_traffic.md")
+CHUNK_SRC = os.path.join(ROOT, "gated_deltanet_recurrence_amd", "csrc", "prefill_chunk.hip")
+
+
+def prefill_flops_per_token_head(dk=128, dv=128, C=64):
+    """Algorithmic flops of the chunk form per token and head: the three
+    state contractions W S^T, Q S^T and Delta~^T K (2 dk dv each), and the
+    triangular C x C products K K^T, Q K^T, T K (C dk each) and T V, P Delta
+    (C dv each), counted at half size: 6 dk dv + 3 C dk + 2 C dv."""
+    return 6 * dk * dv + 3 * C * dk + 2 * C * dv
+
+
+def prefill_bytes(B, T, H, dk=128, dv=128, n_states_out=None, n_states_in=0):
+    tok_head = B * T * H
+    per = 2 * (dk + dk + dv + dv) + 4 + 4          # q, k, v, o bf16; g, beta fp32
+    states = (n_states_out if n_states_out is not None else B) * H * dv * dk * 4
+    return tok_head * per + states + n_states_in * H * dv * dk * 4
+
+
+def decode_bytes(B, H, dk=128, dv=128):
+    return B * H * (2 * dv * dk * 4 + 2 * (dk + dk + dv + dv) + 4 + 4)
+
+
+def event_time(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(i)
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps        # ms per call
+
+
+def _src_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per prefill launch from the committed counter summary, if the
+    kernel source still matches the hash recorded there."""
+    if not os.path.exists(PROFILE_SUMMARY):
+        return None, "no counter summary"
+    text = open(PROFILE_SUMMARY).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]{16})", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes:
+        return None, "summary lacks fields"
+    if m_hash.group(1) != _src_hash(CHUNK_SRC):
+        return None, "kernel changed since the counters were taken"
+    return float(m_bytes.group(1)), "ok"
+
+
+def bench_prefill(gdn, inputs, steps, warmup):
+    import torch
+    c = inputs.make_prefill()
+    sets = []
+    for _ in range(2):
+        d = lambda t: t.cuda().contiguous()
+        sets.append(dict(q=d(c.q), k=d(c.k), v=d(c.v), g=d(c.g), beta=d(c.beta),
+                         o=torch.empty_like(d(c.v)),
+                         fin=torch.empty((c.B, c.H, 128, 128), dtype=torch.float32,
+                                         device="cuda")))
+
+    def step(i):
+        s = sets[i & 1]
+        gdn.gdn_prefill(s["q"], s["k"], s["v"], s["g"], s["beta"], None, s["fin"], s["o"],
+                        scale=c.scale)
+    ms = event_time(step, steps, warmup)
+    tokens = c.B * c.T
+    nbytes = prefill_bytes(c.B, c.T, c.H)
+    flops = prefill_flops_per_token_head() * c.B * c.T * c.H
+    return dict(ms=ms, tokens=tokens, bytes=nbytes, flops=flops, case=c)
+
+
+def bench_decode(gdn, inputs, steps, warmup):
+    import torch
+    c = inputs.make_decode()
+    st = c.s0.cuda()
+    q, k, v = (x[:, 0].cuda().contiguous() for x in (c.q, c.k, c.v))
+    g, beta = c.g[:, 0].cuda().contiguous(), c.beta[:, 0].cuda().contiguous()
+    o = torch.empty_like(v)
+
+    def step(i):
+        gdn.gdn_decode_step(q, k, v, g, beta, st, o, scale=c.scale)
+    ms = event_time(step, steps, warmup)
+    nbytes = decode_bytes(c.B, c.H)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return dict(workload="decode step B=256 H=32 d_k=d_v=128, fp32 state 512 MiB in place, bf16 q/k/v",
+                us_per_step=round(ms * 1e3, 2), bytes_per_step=nbytes, **{"GB/s": round(gbs, 1)},
+                frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
+
+
+def bench_mixer(gdn, inputs, steps, warmup):
+    import torch
+    c = inputs.make_mixer()
+    d = lambda t: t.cuda().contiguous()
+    raw = [d(x) for x in (c.q_raw, c.k_raw, c.v_raw, c.conv_w, c.a, c.b)]
+    A, z = d(c.A), d(c.z)
+    B, T, H, D = c.q_raw.shape
+    outs = (torch.empty_like(raw[0]), torch.empty_like(raw[1]), torch.empty_like(raw[2]),
+            torch.empty((B, T, H), dtype=torch.float32, device="cuda"),
+            torch.empty((B, T, H), dtype=torch.float32, device="cuda"))
+    y = torch.empty_like(raw[2])
+    out = torch.empty_like(y)
+
+    def pro(i):
+        gdn.gdn_mixer_prologue(*raw, A, out=outs)
+
+    def core(i):
+        gdn.gdn_prefill(*outs, o=y, scale=c.scale)
+
+    def epi(i):
+        gdn.gdn_mixer_epilogue(y, z, out=out, eps=c.eps)
+
+    def full(i):
+        pro(i); core(i); epi(i)
+    ms_full = event_time(full, max(1, steps // 4), 1)
+    ms_pro = event_time(pro, max(1, steps // 4), 1)
+    ms_core = event_time(core, max(1, steps // 4), 1)
+    ms_epi = event_time(epi, max(1, steps // 4), 1)
+    pro_bytes = B * T * H * (D * 2 * 3 * 2 + 2 * 2 + 4 * 2)   # q,k,v in+out, a,b in, g,beta out
+    epi_bytes = B * T * H * D * 2 * 3
+    return dict(workload="token mixer B=8 T=8192 H=16 d=128 bf16: conv+SiLU, L2-norm, gates -> "
+                         "chunked prefill -> gated RMSNorm",
+                tokens_per_s=round(B * T / (ms_full * 1e-3), 1), ms_per_step=round(ms_full, 4),
+                ms_prologue=round(ms_pro, 4), ms_prefill=round(ms_core, 4),
+                ms_epilogue=round(ms_epi, 4),
+                prologue_GBps=round(pro_bytes / (ms_pro * 1e-3) / 1e9, 1),
+                epilogue_GBps=round(epi_bytes / (ms_epi * 1e-3) / 1e9, 1))
+
+
+def bench_varlen(gdn, inputs, steps, warmup):
+    import torch
+    c = inputs.make_varlen()
+    d = lambda t: t.cuda().contiguous()
+    q, k, v, g, beta, s0, cu = (d(x) for x in (c.q, c.k, c.v, c.g, c.beta, c.s0, c.cu_seqlens))
+    fin = torch.empty_like(s0)
+    o = torch.empty_like(v)
+
+    def step(i):
+        gdn.gdn_prefill(q, k, v, g, beta, s0, fin, o, cu_seqlens=cu, scale=c.scale)
+    ms = event_time(step, max(1, steps // 4), 1)
+    total = int(c.cu_seqlens[-1])
+    return dict(workload="packed prefill H=32 d=128 bf16, 8 sequences log-uniform in [512, 65536], "
+                         "non-zero initial states",
+                lengths=c.meta["lengths"], tokens_per_s=round(total / (ms * 1e-3), 1),
+                ms_per_step=round(ms, 4),
+                longest_sequence_tokens_per_s=round(max(c.meta["lengths"]) / (ms * 1e-3), 1))
+
+
+def bench_copy(steps, warmup, nbytes=1 << 30):
+    """A plain device copy of known size: the calibration kernel for the
+    FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    ms = event_time(lambda i: dst.copy_(src), steps, warmup)
+    return dict(bytes_read=nbytes, bytes_written=nbytes, ms=round(ms, 4),
+                GBps=round(2 * nbytes / (ms * 1e-3) / 1e9, 1))
+
+
+def cpu_baseline():
+    """fp64 oracle on the prefill workload's host arrays (all 4 x 16 chains of
+    4096 tokens), timed once after a small warm-up run."""
+    import oracle
+    from gated_deltanet_recurrence_amd import inputs
+    c = inputs.make_prefill()
+    oracle.gdn_recurrent(c.q[:1, :64], c.k[:1, :64], c.v[:1, :64], c.g[:1, :64],
+                         c.beta[:1, :64], None, None, c.scale)
+    t = time.perf_counter()
+    oracle.gdn_recurrent(c.q, c.k, c.v, c.g, c.beta, None, None, c.scale)
+    dt = time.perf_counter() - t
+    return {"value": round(c.B * c.T / dt, 1), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "the whole prefill workload (B=4, T=4096, H=16, d=128) once, fp64 "
+                      f"token recurrence, {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default="prefill,decode,mixer,varlen,cpu",
+                    help="comma list of: prefill, decode, mixer, varlen, cpu, copy")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "heads and sequences shard across GPUs with no communication, so the per-GPU "
+              "figure is the one-GPU figure", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import gated_deltanet_recurrence_amd as gdn
+    from gated_deltanet_recurrence_amd import inputs
+    gdn.load()
+    which = set(args.only.split(","))
+    result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+              "data": "synthetic (seeded; q,k unit Gaussian, v N(0,1), "
+                      "log(alpha) = -A softplus(N(0,1)), beta = sigmoid(N(0,1)))"}
+    if "prefill" in which:
+        p = bench_prefill(gdn, inputs, args.steps, args.warmup)
+        sec = p["ms"] * 1e-3
+        achieved = p["bytes"] / sec / 1e9
+        traffic, why = measured_traffic()
+        result.update({
+            "value": round(p["tokens"] / sec, 1), "unit": "tokens/s",
+            "ms_per_step": round(p["ms"], 5),
+            "config": {"workload": "chunked prefill B=4 H=16 T=4096 d_k=d_v=128, bf16 q/k/v, "
+                                   "fp32 gates and state, zero initial state, 64-token chunks",
+                       "global_batch": 4, "seq_len": 4096, "heads": 16, "head_dim": 128,
+                       "parallelism": "single GPU"},
+            "roofline": {"kernel": "prefill_chunk_kernel", "bound": "hbm",
+                         "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                         "traffic_note": why, "algorithmic_bytes_per_launch": p["bytes"],
+                         "avg_launch_us": round(p["ms"] * 1e3, 2),
+                         "mfma_algorithmic_tflops": round(p["flops"] / sec / 1e12, 2),
+                         "mfma_frac_of_bf16_peak": round(p["flops"] / sec / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        })
+    else:
+        result.update({"value": None, "unit": "tokens/s", "ms_per_step": None,
+                       "config": {"workload": "partial run: " + args.only}})
+    if "decode" in which:
+        result["decode"] = bench_decode(gdn, inputs, args.steps, args.warmup)
+    if "mixer" in which:
+        result["mixer"] = bench_mixer(gdn, inputs, args.steps, args.warmup)
+    if "varlen" in which:
+        result["varlen"] = bench_varlen(gdn, inputs, args.steps, args.warmup)
+    if "copy" in which:
+        result["copy_calibration"] = bench_copy(args.steps, args.warmup)
+    if "cpu" in which:
+        result["cpu_baseline"] = cpu_baseline()
+    torch.cuda.synchronize()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -48,6 +48,7 @@ int check_prefill(const void *q, const void *k, const void *v, const float *g, c
     if (cu ? B != 1 : N != B) return GDN_ERR_SHAPE;
     if ((int64_t)B * T > (int64_t)INT32_MAX) return GDN_ERR_SHAPE;   // token index fits int32
     if (H > 65535 || N > 65535) return GDN_ERR_UNSUPPORTED;           // launch grid y / z
+    if ((int64_t)H * N * 4 > (int64_t)INT32_MAX) return GDN_ERR_UNSUPPORTED;  // 1-D grid
     if (!head_dim_pow2(d_k) || d_v > 128) return GDN_ERR_UNSUPPORTED;
     return GDN_OK;
 }
