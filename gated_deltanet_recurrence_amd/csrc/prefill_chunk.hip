@@ -69,7 +69,6 @@ constexpr int LD_QK = DK + 8;  // sQ, sK, sWn rows (bf16)
 constexpr int LD_T = C + 8;    // token-contiguous bf16 rows: sKt, sVt, sP, sTw, sTu, sDt, sDtw
 constexpr int LD_S = DK + 8;   // sS rows (bf16)
 constexpr int LD_A = C + 4;    // fp32 rows: sA, sT
-constexpr int LD_Y = 16 + 4;   // fp32 16x16 scratch blocks
 constexpr int LD_O = DVT + 8;  // output staging (bf16)
 
 // LDS regions (bytes)
@@ -98,7 +97,7 @@ constexpr int OFF_SC = OFF_S + SZ_S;
 constexpr int LDS_BYTES = OFF_SC + SZ_SC;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 static_assert(C * LD_QK * 2 <= SZ_A, "-W fits in the A region");
-static_assert(9 * 16 * LD_Y * 4 <= SZ_Y, "solve scratch fits");
+static_assert(4 * 256 * 4 <= SZ_Y, "solve scratch fits");
 static_assert(2 * DVT * LD_T * 2 + C * LD_O * 2 <= SZ_Y, "chain buffers fit");
 
 // per-token scalar slots in the SC region
@@ -165,17 +164,32 @@ __device__ __forceinline__ f32x4 mm16(f32x4 acc, const float *X, int ldx, const 
     for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[s], yb[s], acc, 0, 0, 0);
     return acc;
 }
-// 16 x 16 fp32 block <-> accumulator layout (element r of lane l is row
-// 4(l/16) + r, column l%16)
-__device__ __forceinline__ void st16(float *Z, int ldz, f32x4 acc, int lane) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) Z[(4 * (lane >> 4) + r) * ldz + (lane & 15)] = acc[r];
+// Accumulator layout -> B-operand layout of v_mfma_f32_16x16x4f32 without
+// LDS. Element r of lane (q, j) = 16q + j holds M[4q + r][j]; k-step s of a
+// B operand needs M[4s + q][j] at lane (q, j). Viewing the four registers as
+// a 4 x 4 grid of (register, 16-lane row) blocks, that is a block transpose:
+// swap rows 2,3 of registers 0,1 with rows 0,1 of registers 2,3
+// (v_permlane32_swap), then odd rows of registers 0,2 with even rows of
+// registers 1,3 (v_permlane16_swap).
+__device__ __forceinline__ f32x4 acc_to_bop(f32x4 c) {
+    auto u = [](float x) { return __builtin_bit_cast(unsigned, x); };
+    auto f = [](unsigned x) { return __builtin_bit_cast(float, x); };
+    const auto p02 = __builtin_amdgcn_permlane32_swap(u(c[0]), u(c[2]), false, false);
+    const auto p13 = __builtin_amdgcn_permlane32_swap(u(c[1]), u(c[3]), false, false);
+    const auto q01 = __builtin_amdgcn_permlane16_swap(p02[0], p13[0], false, false);
+    const auto q23 = __builtin_amdgcn_permlane16_swap(p02[1], p13[1], false, false);
+    return f32x4{f(q01[0]), f(q01[1]), f(q23[0]), f(q23[1])};
 }
-__device__ __forceinline__ f32x4 ld16(const float *Z, int ldz, int lane) {
-    f32x4 a;
+// acc += X Y with X a 16 x 16 fp32 block in LDS and Y given in B-operand
+// registers (acc_to_bop of a product computed by this wave)
+__device__ __forceinline__ f32x4 mm16_rb(f32x4 acc, const float *X, int ldx, f32x4 yb, int lane) {
+    const int r = lane & 15, kq = lane >> 4;
+    float xa[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) a[r] = Z[(4 * (lane >> 4) + r) * ldz + (lane & 15)];
-    return a;
+    for (int s = 0; s < 4; ++s) xa[s] = X[r * ldx + 4 * s + kq];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[s], yb[s], acc, 0, 0, 0);
+    return acc;
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8
@@ -301,7 +315,7 @@ prefill_chunk_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     // Q: 2 x 16 B per thread (token row id/16, 8 columns). One 8 x 8 block (8
     // tokens x 8 channels) per thread of threads 0..159: K for 0..127 (token
     // block jb, d_k block cb), V for 128..159 (token block jb, d_v block cb of
-    // this tile). g, beta: wave 0, one token per lane.
+    // this tile). g, beta: wave 3, one token per lane.
     const size_t tstride = (size_t)H * DK;     // elements between tokens (q, k, v)
     const bool blk_k = tid < 128, blk_v = tid >= 128 && tid < 160;
     const int blk_jb = blk_k ? (tid >> 4) : ((tid - 128) >> 2);
@@ -332,7 +346,7 @@ prefill_chunk_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                     rb[r] = *reinterpret_cast<const bf16x8 *>(bb0 + coff + (size_t)r * tstride);
             }
         }
-        if (wave == 0) {
+        if (wave == 3) {
             const bool ok = base + lane < len;
             const size_t t = (size_t)bos + base + lane;
             rg = ok ? g[t * H + h] : 0.f;
@@ -368,7 +382,7 @@ prefill_chunk_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                     *reinterpret_cast<bf16x8 *>(sVt + (8 * blk_cb + r) * LD_T + 8 * blk_jb) = tr[r];
             }
         }
-        if (wave == 0) {
+        if (wave == 3) {
             const float gam = wave_inclusive_scan(rg);
             const float glast = __builtin_bit_cast(
                 float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gam), 63));
@@ -382,23 +396,6 @@ prefill_chunk_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         }
         lds_barrier();
         if (ch + 1 < nchunks) fetch(ch + 1);   // in flight during this chunk
-
-        // ---------------- gram: A = -strict_lower(diag(beta) K K^T * Gamma) -------
-#pragma unroll
-        for (int item = 0; item < 10; ++item) {
-            if ((item & 7) != wave || item >= 10) continue;     // wave-uniform
-            const int ti = TI[item], tj = TJ[item];
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mma<4>(acc, sK, LD_QK, 16 * ti, sK, LD_QK, 16 * tj, lane);
-            const int i0 = 16 * ti + 4 * lq, j = 16 * tj + lr;
-            const f32x4 gi = *reinterpret_cast<const f32x4 *>(sGam + i0);
-            const f32x4 bi = *reinterpret_cast<const f32x4 *>(sBeta + i0);
-            const float gj = sGam[j];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sA[(i0 + r) * LD_A + j] = j < i0 + r ? -bi[r] * acc[r] * __expf(gi[r] - gj) : 0.f;
-        }
-        lds_barrier();
 
         // store a finished fp32 block of T, and its bf16 T diag(beta e^gamma),
         // T diag(beta) images
@@ -415,102 +412,144 @@ prefill_chunk_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         };
         auto blkA = [&](int I, int J) { return sA + (16 * I) * LD_A + 16 * J; };
         auto blkT = [&](int I, int J) { return sT + (16 * I) * LD_A + 16 * J; };
-        auto slot = [&](int s) { return sY + s * 16 * LD_Y; };
+        // one 16 x 16 tile of A = -strict_lower(diag(beta) K K^T * Gamma), in
+        // accumulator layout
+        auto gram_tile = [&](int ti, int tj) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mma<4>(acc, sK, LD_QK, 16 * ti, sK, LD_QK, 16 * tj, lane);
+            const int i0 = 16 * ti + 4 * lq, j = 16 * tj + lr;
+            const f32x4 gi = *reinterpret_cast<const f32x4 *>(sGam + i0);
+            const f32x4 bi = *reinterpret_cast<const f32x4 *>(sBeta + i0);
+            const float gj = sGam[j];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[r] = j < i0 + r ? -bi[r] * acc[r] * __expf(gi[r] - gj) : 0.f;
+            return acc;
+        };
+        // one 16 x 16 tile of P = lower_incl_diag(Q K^T * Gamma) -> sP
+        auto p_tile = [&](int item) {
+            const int ti = TI[item], tj = TJ[item];
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mma<4>(acc, sQ, LD_QK, 16 * ti, sK, LD_QK, 16 * tj, lane);
+            const int i0 = 16 * ti + 4 * lq, j = 16 * tj + lr;
+            const f32x4 gi = *reinterpret_cast<const f32x4 *>(sGam + i0);
+            const float gj = sGam[j];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sP[(i0 + r) * LD_T + j] = (bf16)(j <= i0 + r ? acc[r] * __expf(gi[r] - gj) : 0.f);
+        };
 
+        // ---------------- gram + diagonal blocks of T = (I - A)^-1 -----------------
         if (wave < 4) {
-            // ---- diagonal block D_b = (I - A_bb)^-1, b = wave: lane j < 16 owns
-            // column j; x_i = [i == j] + sum_{m<i} A_bb[i][m] x_m
-            if (lane < 16) {
-                const int b = wave, j = lane;
-                const float *ab = sA + (16 * b) * LD_A + 16 * b;
-                float x[16];
+            // Wave b forms the diagonal tile A_bb and inverts I - A_bb by forward
+            // substitution, D[i][j] = [i == j] + sum_{m<i} A_bb[i][m] D[m][j].
+            // Lane 4j + p owns column j and the terms m = p (mod 4); the four
+            // partial sums meet by DPP inside the quad. A_bb goes through a
+            // wave-private LDS copy laid out [p][i][m/4] so each lane reads its
+            // terms of row i as one float4.
+            const int b = wave;
+            const f32x4 ab = gram_tile(b, b);
+            float *ap = sY + b * 256;                   // [4][16][4] floats
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float row[16];
+            for (int r = 0; r < 4; ++r) {
+                const int i = 4 * lq + r, m = lr;
+                ap[(m & 3) * 64 + i * 4 + (m >> 2)] = ab[r];
+            }
+            wave_lds_order();
+            const int jc = lane >> 2, p = lane & 3;
+            const float *myp = ap + p * 64;
+            f32x4 arow[16];
 #pragma unroll
-                    for (int m4 = 0; m4 < 4; ++m4) {
-                        const f32x4 v4 = *reinterpret_cast<const f32x4 *>(ab + i * LD_A + 4 * m4);
-                        row[4 * m4] = v4[0]; row[4 * m4 + 1] = v4[1];
-                        row[4 * m4 + 2] = v4[2]; row[4 * m4 + 3] = v4[3];
-                    }
-                    float acc = (i == j) ? 1.f : 0.f;
+            for (int i = 0; i < 16; ++i) arow[i] = *reinterpret_cast<const f32x4 *>(myp + 4 * i);
+            float xs[4] = {0.f, 0.f, 0.f, 0.f};          // xs[t] = D[p + 4t][jc]
 #pragma unroll
-                    for (int m = 0; m < i; ++m) acc += row[m] * x[m];
-                    x[i] = acc;
-                }
-                const float bw = sBeg[16 * b + j], bu = sBeta[16 * b + j];
+            for (int i = 0; i < 16; ++i) {
+                float part = arow[i][0] * xs[0] + arow[i][1] * xs[1] + arow[i][2] * xs[2]
+                           + arow[i][3] * xs[3];
+                part += dpp_f32<DPP_QUAD_XOR1>(part);
+                part += dpp_f32<DPP_QUAD_XOR2>(part);
+                const float xi = part + (i == jc ? 1.f : 0.f);
+                if (p == (i & 3)) xs[i >> 2] = xi;
+            }
+            const int jj = 16 * b + jc;
+            const float bw = sBeg[jj], bu = sBeta[jj];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int ii = 16 * b + i, jj = 16 * b + j;
-                    sT[ii * LD_A + jj] = x[i];
-                    sTw[ii * LD_T + jj] = (bf16)(x[i] * bw);
-                    sTu[ii * LD_T + jj] = (bf16)(x[i] * bu);
-                }
+            for (int t = 0; t < 4; ++t) {
+                const int ii = 16 * b + p + 4 * t;
+                sT[ii * LD_A + jj] = xs[t];
+                sTw[ii * LD_T + jj] = (bf16)(xs[t] * bw);
+                sTu[ii * LD_T + jj] = (bf16)(xs[t] * bu);
             }
         } else {
-            // ---- waves 4..7: P = lower_incl_diag(Q K^T * Gamma) ---------------------
+            // waves 4..7: the six off-diagonal tiles of A
+            auto put = [&](int ti, int tj) {
+                const f32x4 a = gram_tile(ti, tj);
 #pragma unroll
-            for (int item = 0; item < 10; ++item) {
-                if ((item & 3) != wave - 4) continue;           // wave-uniform
-                const int ti = TI[item], tj = TJ[item];
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = mma<4>(acc, sQ, LD_QK, 16 * ti, sK, LD_QK, 16 * tj, lane);
-                const int i0 = 16 * ti + 4 * lq, j = 16 * tj + lr;
-                const f32x4 gi = *reinterpret_cast<const f32x4 *>(sGam + i0);
-                const float gj = sGam[j];
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sP[(i0 + r) * LD_T + j] = (bf16)(j <= i0 + r ? acc[r] * __expf(gi[r] - gj) : 0.f);
-            }
+                for (int r = 0; r < 4; ++r) sA[(16 * ti + 4 * lq + r) * LD_A + 16 * tj + lr] = a[r];
+            };
+            if (wave == 4) { put(1, 0); put(3, 0); }
+            else if (wave == 5) { put(2, 0); put(3, 1); }
+            else if (wave == 6) put(2, 1);
+            else put(3, 2);
         }
         lds_barrier();
 
-        // ---- off-diagonal blocks. With D_b the diagonal inverses:
+        // ---- off-diagonal blocks of T. With D_b the diagonal inverses:
         //   T10 = D1 A10 D0,  T32 = D3 A32 D2                      (16-level)
         //   Y = [A20 A21; A30 A31] [D0 0; T10 D1] = [Y00 P21; Y10 P31]
         //   [T20 T21; T30 T31] = [D2 0; T32 D3] Y                  (32-level)
-        // slots: 0, 1, 6, 7, 8 wave-private; 2 = P21 = A21 D1; 3 = R20 = A20 D0;
-        //        4 = P31 = A31 D1; 5 = Q30 = A30 D0
+        // Right factors produced by a wave stay in its registers (acc_to_bop);
+        // waves without a block product form tiles of P meanwhile.
         {
             const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-            f32x4 acc31 = z4;
+            f32x4 h0 = z4, h1 = z4;                     // products kept for the 32-level
             if (wave == 0) {
-                st16(slot(0), LD_Y, mm16(z4, blkA(1, 0), LD_A, blkT(0, 0), LD_A, lane), lane);
-                wave_lds_order();
-                store_T(1, 0, mm16(z4, blkT(1, 1), LD_A, slot(0), LD_Y, lane));
+                const f32x4 c = mm16(z4, blkA(1, 0), LD_A, blkT(0, 0), LD_A, lane);
+                store_T(1, 0, mm16_rb(z4, blkT(1, 1), LD_A, acc_to_bop(c), lane));
             } else if (wave == 1) {
-                st16(slot(1), LD_Y, mm16(z4, blkA(3, 2), LD_A, blkT(2, 2), LD_A, lane), lane);
-                wave_lds_order();
-                store_T(3, 2, mm16(z4, blkT(3, 3), LD_A, slot(1), LD_Y, lane));
+                const f32x4 c = mm16(z4, blkA(3, 2), LD_A, blkT(2, 2), LD_A, lane);
+                store_T(3, 2, mm16_rb(z4, blkT(3, 3), LD_A, acc_to_bop(c), lane));
             } else if (wave == 2) {
-                st16(slot(2), LD_Y, mm16(z4, blkA(2, 1), LD_A, blkT(1, 1), LD_A, lane), lane);
-                wave_lds_order();
-                store_T(2, 1, mm16(z4, blkT(2, 2), LD_A, slot(2), LD_Y, lane));
+                const f32x4 c = mm16(z4, blkA(2, 1), LD_A, blkT(1, 1), LD_A, lane);
+                store_T(2, 1, mm16_rb(z4, blkT(2, 2), LD_A, acc_to_bop(c), lane));
             } else if (wave == 3) {
-                st16(slot(3), LD_Y, mm16(z4, blkA(2, 0), LD_A, blkT(0, 0), LD_A, lane), lane);
+                h0 = mm16(z4, blkA(2, 0), LD_A, blkT(0, 0), LD_A, lane);            // R20
             } else if (wave == 4) {
-                st16(slot(4), LD_Y, mm16(z4, blkA(3, 1), LD_A, blkT(1, 1), LD_A, lane), lane);
-                wave_lds_order();
-                acc31 = mm16(z4, blkT(3, 3), LD_A, slot(4), LD_Y, lane);
+                h0 = mm16(z4, blkA(2, 1), LD_A, blkT(1, 1), LD_A, lane);            // P21
+                h1 = mm16(z4, blkA(3, 1), LD_A, blkT(1, 1), LD_A, lane);            // P31
             } else if (wave == 5) {
-                st16(slot(5), LD_Y, mm16(z4, blkA(3, 0), LD_A, blkT(0, 0), LD_A, lane), lane);
+                h0 = mm16(z4, blkA(2, 0), LD_A, blkT(0, 0), LD_A, lane);            // R20
+                h1 = mm16(z4, blkA(3, 0), LD_A, blkT(0, 0), LD_A, lane);            // Q30
+            } else if (wave == 6) {
+                p_tile(0); p_tile(2);
+            } else {
+                p_tile(1); p_tile(3);
             }
             lds_barrier();
-            if (wave == 0) {
+            if (wave == 3) {
                 // T20 = D2 (R20 + A21 T10)
-                st16(slot(6), LD_Y, mm16(ld16(slot(3), LD_Y, lane), blkA(2, 1), LD_A, blkT(1, 0), LD_A, lane), lane);
-                wave_lds_order();
-                store_T(2, 0, mm16(z4, blkT(2, 2), LD_A, slot(6), LD_Y, lane));
-            } else if (wave == 1) {
-                // T30 = T32 (R20 + A21 T10) + D3 (Q30 + A31 T10)
-                st16(slot(7), LD_Y, mm16(ld16(slot(3), LD_Y, lane), blkA(2, 1), LD_A, blkT(1, 0), LD_A, lane), lane);
-                st16(slot(8), LD_Y, mm16(ld16(slot(5), LD_Y, lane), blkA(3, 1), LD_A, blkT(1, 0), LD_A, lane), lane);
-                wave_lds_order();
-                const f32x4 t = mm16(z4, blkT(3, 2), LD_A, slot(7), LD_Y, lane);
-                store_T(3, 0, mm16(t, blkT(3, 3), LD_A, slot(8), LD_Y, lane));
+                const f32x4 y00 = mm16(h0, blkA(2, 1), LD_A, blkT(1, 0), LD_A, lane);
+                store_T(2, 0, mm16_rb(z4, blkT(2, 2), LD_A, acc_to_bop(y00), lane));
             } else if (wave == 4) {
                 // T31 = T32 P21 + D3 P31
-                store_T(3, 1, mm16(acc31, blkT(3, 2), LD_A, slot(2), LD_Y, lane));
+                const f32x4 t = mm16_rb(z4, blkT(3, 2), LD_A, acc_to_bop(h0), lane);
+                store_T(3, 1, mm16_rb(t, blkT(3, 3), LD_A, acc_to_bop(h1), lane));
+            } else if (wave == 5) {
+                // T30 = T32 (R20 + A21 T10) + D3 (Q30 + A31 T10)
+                const f32x4 y00 = mm16(h0, blkA(2, 1), LD_A, blkT(1, 0), LD_A, lane);
+                const f32x4 y10 = mm16(h1, blkA(3, 1), LD_A, blkT(1, 0), LD_A, lane);
+                const f32x4 t = mm16_rb(z4, blkT(3, 2), LD_A, acc_to_bop(y00), lane);
+                store_T(3, 0, mm16_rb(t, blkT(3, 3), LD_A, acc_to_bop(y10), lane));
+            } else if (wave == 0) {
+                p_tile(4);
+            } else if (wave == 1) {
+                p_tile(5);
+            } else if (wave == 2) {
+                p_tile(6);
+            } else if (wave == 6) {
+                p_tile(7); p_tile(9);
+            } else {
+                p_tile(8);
             }
             lds_barrier();
         }
