@@ -18,24 +18,29 @@
 // nilpotent, so the inverse is a finite series).
 //
 // Work mapping: one workgroup of 8 waves (two per SIMD) per (32-wide d_v
-// tile, head, sequence); the columns of S (rows of our d_v x d_k state) evolve
-// independently, so the four d_v tiles of a head never communicate. The
-// state tile (32 x 128 fp32) stays in MFMA accumulator registers for the
-// whole sequence; a bf16 copy in LDS is the operand of the next chunk.
-// The next chunk's q, k, v are loaded into registers while the current one
-// is computed. Inside a chunk:
-//   load   Q, K row-major and K^T, V^T (token-contiguous) into LDS
-//   gamma  inclusive prefix sum of g over the chunk (wave 0, DPP row shifts and
-//          row broadcasts)
-//   gram   K K^T lower tiles on MFMA, masked -> A (fp32)
-//   solve  T = (I - A)^-1 in fp32. Waves 0-3 invert the four 16 x 16 diagonal
-//          blocks by forward substitution while waves 4-7 form
-//          P = lower(Q K^T * Gamma) on MFMA; the off-diagonal blocks follow
-//          from two levels of 2 x 2 block inversion, (L^-1)_21 =
-//          L22^-1 A21 L11^-1, as 16 x 16 fp32 MFMA products. Every finished
-//          block is also written as bf16 T diag(beta e^gamma) and T diag(beta).
-//   W, U   bf16 MFMA
-//   chain  Delta = U - W S^T, O = e^gamma Q S^T + P Delta, S update (MFMA)
+// tile, head, sequence); the columns of S (rows of our d_v x d_k state)
+// evolve independently, so the four d_v tiles of a head never communicate.
+// Waves 0-3 keep the state tile (32 x 128 fp32) in MFMA accumulators for the
+// whole sequence, 32 x 32 each; a bf16 copy in LDS is the operand of the next
+// chunk. The next chunk's q, k, v are loaded into registers while the current
+// one is computed. Inside a chunk (one LDS barrier between phases):
+//   load   Q, K row-major and K^T, V^T (token-contiguous, column-swizzled)
+//          into LDS; gamma = inclusive prefix sum of g (wave 3, DPP scan)
+//   G      waves 0-3: a 32 x 32 tile of A = -strict_lower(diag(beta) K K^T *
+//          Gamma) and the inverse of one 16 x 16 diagonal block of I - A by
+//          forward substitution (lane 4j + p owns column j and the terms
+//          m = p mod 4; DPP quad sums); wave 4: the off-diagonal 32 x 32 tile
+//          of A; waves 5-7: tiles of P = lower_incl_diag(Q K^T * Gamma)
+//   L1/L2  the off-diagonal blocks of T = (I - A)^-1 by two levels of 2 x 2
+//          block inversion, (L^-1)_21 = L22^-1 A21 L11^-1, on fp32 MFMA with
+//          intermediate right factors kept in registers; meanwhile waves 6-7
+//          form the inter-chunk output term Q S^T. Each finished block of T
+//          is also written as bf16 T diag(beta e^gamma) and T diag(beta).
+//   WU     W = T diag(beta e^gamma) K (one 32 x 32 tile per wave) -> LDS as -W;
+//          U = T diag(beta) V (waves 0-1, kept in registers)
+//   C1     Delta = U - W S^T (waves 0-1, two split-K accumulators)
+//   C2     O = scale (e^gamma * Q S^T + P Delta) (waves 6-7);
+//          S <- e^{gamma_63} S + Delta~^T K (waves 0-3)
 // Tokens past the end of a sequence are identity steps (q = k = v = 0,
 // beta = 0, g = 0) and their outputs are not stored.
 //
@@ -47,10 +52,11 @@
 // Barriers wait for LDS traffic only (lgkmcnt), never for the global loads of
 // the next chunk that are in flight.
 //
-// MFMA used: v_mfma_f32_16x16x32_bf16 and, for the solve, v_mfma_f32_16x16x4f32. Lane l holds A[l%16][8(l/16)+e] and
-// B[8(l/16)+e][l%16] (e = 0..7), and accumulator element r is
-// C[4(l/16)+r][l%16]; so both operands are read as 16-byte rows of a
-// k-contiguous LDS matrix.
+// Matrix cores: v_mfma_f32_32x32x16_bf16 for every bf16 product (its operand
+// reads, 32 consecutive LDS rows per half-wave, are free of bank conflicts
+// with the row paddings used here) and v_mfma_f32_16x16x4f32 for the solve.
+// Lane l of the 32x32x16 form holds A[l%32][8(l/32)+e] and B[8(l/32)+e][l%32]
+// (e = 0..7); accumulator element r is C[8(r/4) + 4(l/32) + r%4][l%32].
 #include "common.h"
 
 namespace gdn {
@@ -97,42 +103,74 @@ constexpr int OFF_SC = OFF_S + SZ_S;
 constexpr int LDS_BYTES = OFF_SC + SZ_SC;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 static_assert(C * LD_QK * 2 <= SZ_A, "-W fits in the A region");
-static_assert(4 * 256 * 4 <= SZ_Y, "solve scratch fits");
+static_assert(4 * 4 * 4 * 68 * 4 <= SZ_Y, "solve scratch fits");
 static_assert(2 * DVT * LD_T * 2 + C * LD_O * 2 <= SZ_Y, "chain buffers fit");
 
 // per-token scalar slots in the SC region
 enum { SC_GAM = 0, SC_BETA, SC_BEG, SC_EG, SC_DEND };
 
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// 16 x 8 operand slice: row r0 + lane%16, columns k0 + 8*(lane/16) .. +8
-__device__ __forceinline__ bf16x8 frag(const bf16 *m, int ld, int r0, int k0, int lane) {
-    return *reinterpret_cast<const bf16x8 *>(m + (r0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
+// 32 x 8 operand slice of a row-major bf16 LDS matrix: row r0 + lane%32,
+// columns k0 + 8*(lane/32) .. +8
+__device__ __forceinline__ bf16x8 frag32(const bf16 *m, int ld, int r0, int k0, int lane) {
+    return *reinterpret_cast<const bf16x8 *>(m + (r0 + (lane & 31)) * ld + k0 + 8 * (lane >> 5));
 }
-
-// acc += A[i0.., 0..32*KS) B[0..32*KS, j0..]; A row-major (ld_a), B given as
-// Bt[j][k] (ld_b). All operand fragments are read before the first MFMA.
-template <int KS>
-__device__ __forceinline__ f32x4 mma(f32x4 acc, const bf16 *a, int ld_a, int i0, const bf16 *bt,
-                                     int ld_b, int j0, int lane) {
+// The token-contiguous copies of K and V (sKt, sVt) are written as 8 x 8
+// transposed blocks; to keep those writes free of LDS bank conflicts the
+// 8-token column block of row d is stored at block (k/8) ^ ((d >> 4) & 7).
+__device__ __forceinline__ bf16x8 frag32_sw(const bf16 *m, int ld, int r0, int k0, int lane) {
+    const int row = r0 + (lane & 31);
+    const int blk = ((k0 >> 3) + (lane >> 5)) ^ ((row >> 4) & 7);
+    return *reinterpret_cast<const bf16x8 *>(m + row * ld + 8 * blk);
+}
+// acc += A[i0..i0+32, kb..kb+16*KS) B[kb..kb+16*KS, j0..j0+32]; A row-major
+// (ld_a), B given as Bt[j][k] (ld_b), column-swizzled as above when SWB. All
+// operand fragments are read before the first MFMA.
+//
+// The compiler's scheduler would otherwise interleave each fragment load
+// with a wait right before its MFMA and expose the LDS latency once per
+// k-step; sched_barrier keeps the whole batch of loads ahead of the MFMAs.
+template <int KS, bool SWB = false>
+__device__ __forceinline__ f32x16 mma32(f32x16 acc, const bf16 *a, int ld_a, int i0,
+                                        const bf16 *bt, int ld_b, int j0, int lane, int kb = 0) {
     bf16x8 fa[KS], fb[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-        fa[s] = frag(a, ld_a, i0, 32 * s, lane);
-        fb[s] = frag(bt, ld_b, j0, 32 * s, lane);
+        fa[s] = frag32(a, ld_a, i0, kb + 16 * s, lane);
+        fb[s] = SWB ? frag32_sw(bt, ld_b, j0, kb + 16 * s, lane) : frag32(bt, ld_b, j0, kb + 16 * s, lane);
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) acc = mfma16(fa[s], fb[s], acc);
+    for (int s = 0; s < KS; ++s) acc = mfma32(fa[s], fb[s], acc);
     return acc;
 }
-// products with a lower-triangular 64 x 64 left factor, row tile ti: the
-// k range is [0, 32) for ti < 2 and [0, 64) otherwise
-__device__ __forceinline__ f32x4 mma_tri(f32x4 acc, int ti, const bf16 *a, int ld_a,
-                                         const bf16 *bt, int ld_b, int j0, int lane) {
-    return ti < 2 ? mma<1>(acc, a, ld_a, 16 * ti, bt, ld_b, j0, lane)
-                  : mma<2>(acc, a, ld_a, 16 * ti, bt, ld_b, j0, lane);
+// Same product over k in [0, 32*KS2) as two independent accumulator chains
+// (even / odd k-steps) interleaved, which halves the dependent MFMA latency;
+// returns the sum.
+template <int KS2, bool SWB = false>
+__device__ __forceinline__ f32x16 mma32_2(f32x16 acc, const bf16 *a, int ld_a, int i0,
+                                          const bf16 *bt, int ld_b, int j0, int lane) {
+    bf16x8 fa[2 * KS2], fb[2 * KS2];
+#pragma unroll
+    for (int s = 0; s < 2 * KS2; ++s) {
+        fa[s] = frag32(a, ld_a, i0, 16 * s, lane);
+        fb[s] = SWB ? frag32_sw(bt, ld_b, j0, 16 * s, lane) : frag32(bt, ld_b, j0, 16 * s, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 acc1 = {};
+#pragma unroll
+    for (int s = 0; s < KS2; ++s) {
+        acc = mfma32(fa[2 * s], fb[2 * s], acc);
+        acc1 = mfma32(fa[2 * s + 1], fb[2 * s + 1], acc1);
+    }
+    return acc + acc1;
+}
+// row of accumulator element r of a 32x32 tile (the column is lane % 32)
+__device__ __forceinline__ int acc_row(int r, int lane) {
+    return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
 // Workgroup barrier that orders LDS traffic only: global loads issued before
@@ -160,6 +198,7 @@ __device__ __forceinline__ f32x4 mm16(f32x4 acc, const float *X, int ldx, const 
         xa[s] = X[r * ldx + 4 * s + kq];
         yb[s] = Y[(4 * s + kq) * ldy + r];
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[s], yb[s], acc, 0, 0, 0);
     return acc;
@@ -187,6 +226,7 @@ __device__ __forceinline__ f32x4 mm16_rb(f32x4 acc, const float *X, int ldx, f32
     float xa[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) xa[s] = X[r * ldx + 4 * s + kq];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[s], yb[s], acc, 0, 0, 0);
     return acc;
@@ -217,10 +257,6 @@ __device__ __forceinline__ void transpose8x8(const bf16x8 (&in)[8], bf16x8 (&out
 #pragma unroll
         for (int r = 0; r < 8; ++r) out[e][r] = in[r][e];
 }
-
-// lower 16x16 tiles (ti, tj), tj <= ti, enumerated 0..9
-constexpr int TI[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-constexpr int TJ[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 
 }  // namespace chunk
 
@@ -283,67 +319,86 @@ prefill_chunk_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const int len = (int)(eos - bos);
     const int nchunks = (len + C - 1) / C;
 
-    // ---- state tile in accumulators: wave w owns state rows (d_v) cs0..cs0+15
-    //      and d_k tiles dt0, dt0 + 1 ---------------------------------------------
-    const int tid = tid0, lane = tid0 & 63, lr = lane & 15, lq = lane >> 4;
-    const int cs0 = 16 * (wave & 1);
-    const int dt0 = 2 * (wave >> 1);
-    f32x4 accS[2];
+    // ---- state tile: waves 0-3 own S[c][d], c = 0..31 (this d_v tile), d in
+    //      [32w, 32w + 32), as one 32x32 accumulator ---------------------------------
+    f32x16 accS = {};
     const size_t sbase = ((size_t)n * H + h) * DV * DK;
+    if (wave < 4) {
+        const int lane = tid0 & 63;
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int c = cs0 + 4 * lq + r, d = 16 * (dt0 + t2) + lr;
-            accS[t2][r] = s_init ? s_init[sbase + (size_t)(cbase + c) * DK + d] : 0.0f;
+        for (int r = 0; r < 16; ++r) {
+            const int c = acc_row(r, lane), d = 32 * wave + (lane & 31);
+            accS[r] = s_init ? s_init[sbase + (size_t)(cbase + c) * DK + d] : 0.0f;
         }
+    }
 
     // ---- one-time LDS initialisation: the blocks above the diagonal of P, T_w
     //      and T_u are never written again; the bf16 copy of the state ---------
-    for (int e = tid; e < C * LD_T; e += NT) {
+    for (int e = tid0; e < C * LD_T; e += NT) {
         sP[e] = (bf16)0.0f;
         sTw[e] = (bf16)0.0f;
         sTu[e] = (bf16)0.0f;
     }
+    if (wave < 4) {
+        const int lane = tid0 & 63;
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            sS[(cs0 + 4 * lq + r) * LD_S + 16 * (dt0 + t2) + lr] = (bf16)accS[t2][r];
+        for (int r = 0; r < 16; ++r)
+            sS[acc_row(r, lane) * LD_S + 32 * wave + (lane & 31)] = (bf16)accS[r];
+    }
 
     // ---- register prefetch of one chunk ---------------------------------------
     // Q: 2 x 16 B per thread (token row id/16, 8 columns). One 8 x 8 block (8
     // tokens x 8 channels) per thread of threads 0..159: K for 0..127 (token
     // block jb, d_k block cb), V for 128..159 (token block jb, d_v block cb of
     // this tile). g, beta: wave 3, one token per lane.
-    const size_t tstride = (size_t)H * DK;     // elements between tokens (q, k, v)
+    const int tid = tid0;
+    const int tstride = H * DK;                // elements between tokens (q, k, v)
     const bool blk_k = tid < 128, blk_v = tid >= 128 && tid < 160;
     const int blk_jb = blk_k ? (tid >> 4) : ((tid - 128) >> 2);
     const int blk_cb = blk_k ? (tid & 15) : ((tid - 128) & 3);
-    const bf16 *qb0 = q + (size_t)bos * tstride + (size_t)h * DK + 8 * (tid & 15);
     const int qrow0 = tid >> 4;                // rows qrow0 and qrow0 + 32
-    const bf16 *bb0 = (blk_k ? k + (size_t)h * DK : v + (size_t)h * DV + cbase) + 8 * blk_cb
-                      + ((size_t)bos + 8 * blk_jb) * tstride;
+    // uniform bases; per-lane offsets fit in 32 bits (row < 64, H * 128 < 2^23)
+    const bf16 *qbase = q + (size_t)bos * tstride + (size_t)h * DK;
+    const bf16 *kbase = k + (size_t)bos * tstride + (size_t)h * DK;
+    const bf16 *vbase = v + (size_t)bos * tstride + (size_t)h * DV + cbase;
+    const int qoff = qrow0 * tstride + 8 * (tid & 15);
+    const int boff = 8 * blk_jb * tstride + 8 * blk_cb;
     bf16x8 rq[2], rb[8];
     float rg = 0.f, rbeta = 0.f;
     auto fetch = [&](int ch) {
         const bf16x8 z8 = {};
-        const size_t coff = (size_t)ch * C * tstride;
+        const size_t coff = (size_t)ch * C * tstride;   // uniform
         const int base = ch * C;
-        const bool full = base + C <= len;     // uniform
+        const int lane = tid & 63;
+        const bf16 *qc = qbase + coff, *kc = kbase + coff, *vc = vbase + coff;
+        if (base + C <= len) {                 // whole chunk inside the sequence (uniform)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int row = qrow0 + 32 * u;
-            rq[u] = z8;
-            if (full || base + row < len)
-                rq[u] = *reinterpret_cast<const bf16x8 *>(qb0 + coff + (size_t)row * tstride);
-        }
-        if (blk_k || blk_v) {
+            for (int u = 0; u < 2; ++u)
+                rq[u] = *reinterpret_cast<const bf16x8 *>(qc + qoff + 32 * u * tstride);
+            if (blk_k) {
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                rb[r] = z8;
-                if (full || base + 8 * blk_jb + r < len)
-                    rb[r] = *reinterpret_cast<const bf16x8 *>(bb0 + coff + (size_t)r * tstride);
+                for (int r = 0; r < 8; ++r)
+                    rb[r] = *reinterpret_cast<const bf16x8 *>(kc + boff + r * tstride);
+            } else if (blk_v) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r)
+                    rb[r] = *reinterpret_cast<const bf16x8 *>(vc + boff + r * tstride);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                rq[u] = z8;
+                if (base + qrow0 + 32 * u < len)
+                    rq[u] = *reinterpret_cast<const bf16x8 *>(qc + qoff + 32 * u * tstride);
+            }
+            if (blk_k || blk_v) {
+                const bf16 *bc = blk_k ? kc : vc;
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    rb[r] = z8;
+                    if (base + 8 * blk_jb + r < len)
+                        rb[r] = *reinterpret_cast<const bf16x8 *>(bc + boff + r * tstride);
+                }
             }
         }
         if (wave == 3) {
@@ -360,13 +415,15 @@ prefill_chunk_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         // Lane-derived indices are recomputed every chunk (the empty asm hides
         // the thread id from loop-invariant hoisting, which would otherwise
         // keep hundreds of precomputed LDS addresses live across the loop).
-        int tid = tid0;
-        asm volatile("" : "+v"(tid));
-        const int lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+        int tidl = tid0;
+        asm volatile("" : "+v"(tidl));
+        const int lane = tidl & 63, lr = lane & 15, lq = lane >> 4;
+        const int l32 = lane & 31, lh = lane >> 5;   // 32x32x16 lane coordinates
+
         // ---------------- load: registers -> LDS; decay prefix sums ----------------
 #pragma unroll
         for (int u = 0; u < 2; ++u)
-            *reinterpret_cast<bf16x8 *>(sQ + (qrow0 + 32 * u) * LD_QK + 8 * (tid & 15)) = rq[u];
+            *reinterpret_cast<bf16x8 *>(sQ + (qrow0 + 32 * u) * LD_QK + 8 * (tidl & 15)) = rq[u];
         if (blk_k || blk_v) {
             bf16x8 tr[8];
             transpose8x8(rb, tr);
@@ -374,12 +431,12 @@ prefill_chunk_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
                 for (int r = 0; r < 8; ++r) {
                     *reinterpret_cast<bf16x8 *>(sK + (8 * blk_jb + r) * LD_QK + 8 * blk_cb) = rb[r];
-                    *reinterpret_cast<bf16x8 *>(sKt + (8 * blk_cb + r) * LD_T + 8 * blk_jb) = tr[r];
+                    *reinterpret_cast<bf16x8 *>(sKt + (8 * blk_cb + r) * LD_T + 8 * (blk_jb ^ ((blk_cb >> 1) & 7))) = tr[r];
                 }
             } else {
 #pragma unroll
                 for (int r = 0; r < 8; ++r)
-                    *reinterpret_cast<bf16x8 *>(sVt + (8 * blk_cb + r) * LD_T + 8 * blk_jb) = tr[r];
+                    *reinterpret_cast<bf16x8 *>(sVt + (8 * blk_cb + r) * LD_T + 8 * (blk_jb ^ (blk_cb >> 1))) = tr[r];
             }
         }
         if (wave == 3) {
@@ -397,8 +454,53 @@ prefill_chunk_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         lds_barrier();
         if (ch + 1 < nchunks) fetch(ch + 1);   // in flight during this chunk
 
-        // store a finished fp32 block of T, and its bf16 T diag(beta e^gamma),
-        // T diag(beta) images
+        // per-row scalars of accumulator elements r = 4q'..4q'+3 of a 32x32 tile
+        // whose first row is i0: rows i0 + 8q' + 4*lh + 0..3
+        auto rows4 = [&](const float *v, int i0, int qq) {
+            return *reinterpret_cast<const f32x4 *>(v + i0 + 8 * qq + 4 * lh);
+        };
+        // one 32x32 tile of A = -strict_lower(diag(beta) K K^T * Gamma)
+        auto gram32 = [&](int ti, int tj) {
+            const int j = 32 * tj + l32;
+            const float gj = sGam[j];
+            f32x4 gi[4], bi[4];
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                gi[qq] = rows4(sGam, 32 * ti, qq);
+                bi[qq] = rows4(sBeta, 32 * ti, qq);
+            }
+            f32x16 acc = {};
+            acc = mma32_2<4>(acc, sK, LD_QK, 32 * ti, sK, LD_QK, 32 * tj, lane);
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) {
+                    const int r = 4 * qq + s2, i = 32 * ti + acc_row(r, lane);
+                    acc[r] = j < i ? -bi[qq][s2] * acc[r] * __expf(gi[qq][s2] - gj) : 0.f;
+                }
+            }
+            return acc;
+        };
+        // one 32x32 tile of P = lower_incl_diag(Q K^T * Gamma) -> sP
+        auto p32 = [&](int ti, int tj) {
+            const int j = 32 * tj + l32;
+            const float gj = sGam[j];
+            f32x4 gi[4];
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) gi[qq] = rows4(sGam, 32 * ti, qq);
+            f32x16 acc = {};
+            acc = mma32_2<4>(acc, sQ, LD_QK, 32 * ti, sK, LD_QK, 32 * tj, lane);
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) {
+                    const int r = 4 * qq + s2, i = 32 * ti + acc_row(r, lane);
+                    sP[i * LD_T + j] = (bf16)(j <= i ? acc[r] * __expf(gi[qq][s2] - gj) : 0.f);
+                }
+            }
+        };
+        // store a finished 16x16 fp32 block of T, and its bf16 T diag(beta e^gamma),
+        // T diag(beta) images (16x16x4 accumulator layout)
         auto store_T = [&](int I, int J, f32x4 acc) {
             const int j = 16 * J + lr;
             const float bw = sBeg[j], bu = sBeta[j];
@@ -412,52 +514,34 @@ prefill_chunk_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         };
         auto blkA = [&](int I, int J) { return sA + (16 * I) * LD_A + 16 * J; };
         auto blkT = [&](int I, int J) { return sT + (16 * I) * LD_A + 16 * J; };
-        // one 16 x 16 tile of A = -strict_lower(diag(beta) K K^T * Gamma), in
-        // accumulator layout
-        auto gram_tile = [&](int ti, int tj) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mma<4>(acc, sK, LD_QK, 16 * ti, sK, LD_QK, 16 * tj, lane);
-            const int i0 = 16 * ti + 4 * lq, j = 16 * tj + lr;
-            const f32x4 gi = *reinterpret_cast<const f32x4 *>(sGam + i0);
-            const f32x4 bi = *reinterpret_cast<const f32x4 *>(sBeta + i0);
-            const float gj = sGam[j];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                acc[r] = j < i0 + r ? -bi[r] * acc[r] * __expf(gi[r] - gj) : 0.f;
-            return acc;
-        };
-        // one 16 x 16 tile of P = lower_incl_diag(Q K^T * Gamma) -> sP
-        auto p_tile = [&](int item) {
-            const int ti = TI[item], tj = TJ[item];
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mma<4>(acc, sQ, LD_QK, 16 * ti, sK, LD_QK, 16 * tj, lane);
-            const int i0 = 16 * ti + 4 * lq, j = 16 * tj + lr;
-            const f32x4 gi = *reinterpret_cast<const f32x4 *>(sGam + i0);
-            const float gj = sGam[j];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sP[(i0 + r) * LD_T + j] = (bf16)(j <= i0 + r ? acc[r] * __expf(gi[r] - gj) : 0.f);
-        };
 
-        // ---------------- gram + diagonal blocks of T = (I - A)^-1 -----------------
+        // ---------------- G: A tiles, diagonal blocks of T, P -----------------------
         if (wave < 4) {
-            // Wave b forms the diagonal tile A_bb and inverts I - A_bb by forward
-            // substitution, D[i][j] = [i == j] + sum_{m<i} A_bb[i][m] D[m][j].
-            // Lane 4j + p owns column j and the terms m = p (mod 4); the four
-            // partial sums meet by DPP inside the quad. A_bb goes through a
-            // wave-private LDS copy laid out [p][i][m/4] so each lane reads its
-            // terms of row i as one float4.
-            const int b = wave;
-            const f32x4 ab = gram_tile(b, b);
-            float *ap = sY + b * 256;                   // [4][16][4] floats
+            // wave w = 2 tt + bt: tile (tt, tt) of A; invert its diagonal block bt
+            // (global diagonal block w) by forward substitution,
+            // D[i][j] = [i == j] + sum_{m<i} A_ww[i][m] D[m][j]
+            const int tt = wave >> 1, bt = wave & 1;
+            const f32x16 at = gram32(tt, tt);
+            // whole 32x32 tile, unconditionally: into this wave's private copy laid
+            // out [16x16 block][p][i][t] (element (i, m) of a block at
+            // p = m % 4, t = m / 4; p stride 68 floats), and, by the even waves,
+            // into sA (only its lower off-diagonal block is read later)
+            float *ap = sY + wave * (4 * 4 * 68);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 4 * lq + r, m = lr;
-                ap[(m & 3) * 64 + i * 4 + (m >> 2)] = ab[r];
+            for (int r = 0; r < 16; ++r) {
+                const int it = acc_row(r, lane), jt = l32;
+                const int blk = 2 * (it >> 4) + (jt >> 4), i = it & 15, m = jt & 15;
+                ap[blk * (4 * 68) + (m & 3) * 68 + i * 4 + (m >> 2)] = at[r];
+            }
+            if (bt == 0) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    sA[(32 * tt + acc_row(r, lane)) * LD_A + 32 * tt + l32] = at[r];
             }
             wave_lds_order();
+            // lane 4 jc + p owns column jc and the terms m = p (mod 4)
             const int jc = lane >> 2, p = lane & 3;
-            const float *myp = ap + p * 64;
+            const float *myp = ap + (3 * bt) * (4 * 68) + p * 68;   // diagonal block bt
             f32x4 arow[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) arow[i] = *reinterpret_cast<const f32x4 *>(myp + 4 * i);
@@ -471,26 +555,22 @@ prefill_chunk_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                 const float xi = part + (i == jc ? 1.f : 0.f);
                 if (p == (i & 3)) xs[i >> 2] = xi;
             }
-            const int jj = 16 * b + jc;
+            const int jj = 16 * wave + jc;
             const float bw = sBeg[jj], bu = sBeta[jj];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const int ii = 16 * b + p + 4 * t;
+                const int ii = 16 * wave + p + 4 * t;
                 sT[ii * LD_A + jj] = xs[t];
                 sTw[ii * LD_T + jj] = (bf16)(xs[t] * bw);
                 sTu[ii * LD_T + jj] = (bf16)(xs[t] * bu);
             }
-        } else {
-            // waves 4..7: the six off-diagonal tiles of A
-            auto put = [&](int ti, int tj) {
-                const f32x4 a = gram_tile(ti, tj);
+        } else if (wave == 4) {
+            // the off-diagonal 32x32 tile of A (rows 32..63, columns 0..31)
+            const f32x16 at = gram32(1, 0);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sA[(16 * ti + 4 * lq + r) * LD_A + 16 * tj + lr] = a[r];
-            };
-            if (wave == 4) { put(1, 0); put(3, 0); }
-            else if (wave == 5) { put(2, 0); put(3, 1); }
-            else if (wave == 6) put(2, 1);
-            else put(3, 2);
+            for (int r = 0; r < 16; ++r) sA[(32 + acc_row(r, lane)) * LD_A + l32] = at[r];
+        } else {
+            p32(wave == 5 ? 0 : 1, wave == 7 ? 1 : 0);   // tiles (0,0), (1,0), (1,1)
         }
         lds_barrier();
 
@@ -498,8 +578,9 @@ prefill_chunk_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         //   T10 = D1 A10 D0,  T32 = D3 A32 D2                      (16-level)
         //   Y = [A20 A21; A30 A31] [D0 0; T10 D1] = [Y00 P21; Y10 P31]
         //   [T20 T21; T30 T31] = [D2 0; T32 D3] Y                  (32-level)
-        // Right factors produced by a wave stay in its registers (acc_to_bop);
-        // waves without a block product form tiles of P meanwhile.
+        // Right factors produced by a wave stay in its registers (acc_to_bop).
+        // Waves 6-7 form the inter-chunk output term Q S^T meanwhile.
+        f32x16 accOi = {};
         {
             const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
             f32x4 h0 = z4, h1 = z4;                     // products kept for the 32-level
@@ -520,10 +601,8 @@ prefill_chunk_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             } else if (wave == 5) {
                 h0 = mm16(z4, blkA(2, 0), LD_A, blkT(0, 0), LD_A, lane);            // R20
                 h1 = mm16(z4, blkA(3, 0), LD_A, blkT(0, 0), LD_A, lane);            // Q30
-            } else if (wave == 6) {
-                p_tile(0); p_tile(2);
             } else {
-                p_tile(1); p_tile(3);
+                accOi = mma32_2<4>(accOi, sQ, LD_QK, 32 * (wave - 6), sS, LD_S, 0, lane);
             }
             lds_barrier();
             if (wave == 3) {
@@ -540,95 +619,92 @@ prefill_chunk_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                 const f32x4 y10 = mm16(h1, blkA(3, 1), LD_A, blkT(1, 0), LD_A, lane);
                 const f32x4 t = mm16_rb(z4, blkT(3, 2), LD_A, acc_to_bop(y00), lane);
                 store_T(3, 0, mm16_rb(t, blkT(3, 3), LD_A, acc_to_bop(y10), lane));
-            } else if (wave == 0) {
-                p_tile(4);
-            } else if (wave == 1) {
-                p_tile(5);
-            } else if (wave == 2) {
-                p_tile(6);
-            } else if (wave == 6) {
-                p_tile(7); p_tile(9);
-            } else {
-                p_tile(8);
             }
             lds_barrier();
         }
 
-        // ---------------- W = T_w K -> sWn = -W ; U = T_u V (registers) ------------
+        // ---------------- WU: W = T_w K -> sWn = -W ; U = T_u V (waves 0, 1) ---------
+        f32x16 accD = {};
         {
-            // wave w: d_k column tile w over the four row tiles
-            const int d0 = 16 * wave;
+            // wave w: W rows 32 (w/4) .., d_k columns 32 (w%4) ..; T_w is lower
+            // triangular, so row tile 0 needs tokens 0..31 only
+            const int rt = wave >> 2, ct = wave & 3;
+            f32x16 acc = {};
+            acc = rt == 0 ? mma32<2, true>(acc, sTw, LD_T, 0, sKt, LD_T, 32 * ct, lane)
+                          : mma32<4, true>(acc, sTw, LD_T, 32, sKt, LD_T, 32 * ct, lane);
 #pragma unroll
-            for (int ti = 0; ti < 4; ++ti) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = mma_tri(acc, ti, sTw, LD_T, sKt, LD_T, d0, lane);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sWn[(16 * ti + 4 * lq + r) * LD_QK + d0 + lr] = (bf16)(-acc[r]);
-            }
-        }
-        // wave w owns row tile ti = w/2 and d_v column tile ct = w%2 of U, Delta, O
-        const int ti = wave >> 1, ct = wave & 1;
-        const int i0 = 16 * ti + 4 * lq;           // first of this lane's 4 rows
-        f32x4 accD = {0.f, 0.f, 0.f, 0.f};
-        accD = mma_tri(accD, ti, sTu, LD_T, sVt, LD_T, 16 * ct, lane);
-        lds_barrier();
-
-        // ---------------- chain 1: Delta = U - W S^T ; O = Q S^T ----------------------
-        accD = mma<4>(accD, sWn, LD_QK, 16 * ti, sS, LD_S, 16 * ct, lane);
-        f32x4 accO = {0.f, 0.f, 0.f, 0.f};
-        accO = mma<4>(accO, sQ, LD_QK, 16 * ti, sS, LD_S, 16 * ct, lane);
-        {
-            const f32x4 eg = *reinterpret_cast<const f32x4 *>(sEg + i0);
-            const f32x4 de = *reinterpret_cast<const f32x4 *>(sDend + i0);
-            const int c = 16 * ct + lr;
-            bf16x4 dv, dw;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                dv[r] = (bf16)accD[r];
-                dw[r] = (bf16)(accD[r] * de[r]);
-                accO[r] *= eg[r];
-            }
-            *reinterpret_cast<bf16x4 *>(sDt + c * LD_T + i0) = dv;
-            *reinterpret_cast<bf16x4 *>(sDtw + c * LD_T + i0) = dw;
+            for (int r = 0; r < 16; ++r)
+                sWn[(32 * rt + acc_row(r, lane)) * LD_QK + 32 * ct + l32] = (bf16)(-acc[r]);
+            if (wave == 0) accD = mma32<2, true>(accD, sTu, LD_T, 0, sVt, LD_T, 0, lane);
+            if (wave == 1) accD = mma32<4, true>(accD, sTu, LD_T, 32, sVt, LD_T, 0, lane);
         }
         lds_barrier();
 
-        // ---------------- chain 2: O += P Delta ; S <- e^{g63} S + Delta~^T K ----------
-        accO = mma_tri(accO, ti, sP, LD_T, sDt, LD_T, 16 * ct, lane);
+        // ---------------- C1: Delta = U - W S^T (waves 0, 1; rows 32 w ..) ----------
+        if (wave < 2) {
+            const int i0 = 32 * wave;
+            f32x4 de4[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sO[(i0 + r) * LD_O + 16 * ct + lr] = (bf16)(scale * accO[r]);
-        {
+            for (int qq = 0; qq < 4; ++qq) de4[qq] = rows4(sDend, i0, qq);
+            accD = mma32_2<4>(accD, sWn, LD_QK, i0, sS, LD_S, 0, lane);
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const f32x4 de = de4[qq];
+                bf16x4 dv, dw;
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) {
+                    const float d = accD[4 * qq + s2];
+                    dv[s2] = (bf16)d;
+                    dw[s2] = (bf16)(d * de[s2]);
+                }
+                const int i = i0 + 8 * qq + 4 * lh;
+                *reinterpret_cast<bf16x4 *>(sDt + l32 * LD_T + i) = dv;
+                *reinterpret_cast<bf16x4 *>(sDtw + l32 * LD_T + i) = dw;
+            }
+        }
+        lds_barrier();
+
+        // ---------------- C2: O = scale (e^g Q S^T + P Delta); state update -----------
+        if (wave >= 6) {
+            const int rt = wave - 6, i0 = 32 * rt;
+            f32x4 eg4[4];
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) eg4[qq] = rows4(sEg, i0, qq);
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) accOi[4 * qq + s2] *= eg4[qq][s2];
+            accOi = rt == 0 ? mma32<2>(accOi, sP, LD_T, 0, sDt, LD_T, 0, lane)
+                            : mma32<4>(accOi, sP, LD_T, 32, sDt, LD_T, 0, lane);
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                sO[(i0 + acc_row(r, lane)) * LD_O + l32] = (bf16)(scale * accOi[r]);
+        } else if (wave < 4) {
             const float eend = sEg[C - 1];
 #pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2) {
+            for (int r = 0; r < 16; ++r) accS[r] *= eend;
+            accS = mma32<4, true>(accS, sDtw, LD_T, 0, sKt, LD_T, 32 * wave, lane);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) accS[t2][r] *= eend;
-                accS[t2] = mma<2>(accS[t2], sDtw, LD_T, cs0, sKt, LD_T, 16 * (dt0 + t2), lane);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sS[(cs0 + 4 * lq + r) * LD_S + 16 * (dt0 + t2) + lr] = (bf16)accS[t2][r];
-            }
+            for (int r = 0; r < 16; ++r)
+                sS[acc_row(r, lane) * LD_S + 32 * wave + l32] = (bf16)accS[r];
         }
         lds_barrier();
         // output tile 64 x 32 bf16: one 16-byte store per thread of the first 256
-        if (tid < 256) {
-            const int row = tid >> 2, col = 8 * (tid & 3);
+        if (tidl < 256) {
+            const int row = tidl >> 2, col = 8 * (tidl & 3);
             if (base + row < len)
                 *reinterpret_cast<bf16x8 *>(o + ((size_t)bos + base + row) * H * DV + (size_t)h * DV + cbase + col) =
                     *reinterpret_cast<const bf16x8 *>(sO + row * LD_O + col);
         }
     }
 
-    if (s_final) {
-        const int lane = tid0 & 63, lr = lane & 15, lq = lane >> 4;
+    if (s_final && wave < 4) {
+        const int lane = tid0 & 63;
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int c = cs0 + 4 * lq + r, d = 16 * (dt0 + t2) + lr;
-                s_final[sbase + (size_t)(cbase + c) * DK + d] = accS[t2][r];
-            }
+        for (int r = 0; r < 16; ++r) {
+            const int c = acc_row(r, lane), d = 32 * wave + (lane & 31);
+            s_final[sbase + (size_t)(cbase + c) * DK + d] = accS[r];
+        }
     }
 }
 
