@@ -3,15 +3,25 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill,decode,...]
 
 A step is one gdn_prefill call over the chunked-prefill workload (B=4, H=16,
-T=4096, d_k=d_v=128, bf16 q/k/v, fp32 gates and state, zero initial state);
-``value`` is prefill tokens/s (B*T per step). The same JSON line carries:
+T=4096, d_k=d_v=128, bf16 q/k/v, fp32 gates and state, zero initial state),
+with a workspace, i.e. its two passes: chunk_prep (every chunk's triangular
+system, all chunks in parallel) and chunk_chain (the state recurrence over
+chunks). ``value`` is prefill tokens/s (B*T per step). The same JSON line
+carries:
 
-* ``roofline`` of the prefill chunk kernel: algorithmic HBM bytes per launch
-  (q, k, v, o in bf16 and g, beta in fp32 per token-head, plus the fp32 final
-  state) over its average launch time, against 8 TB/s; the algorithmic
-  matrix-core rate against the 2.5 PFLOP/s dense bf16 peak is given too;
-  ``traffic`` is the measured HBM bytes per launch from the committed counter
-  summary (profiles/), or null when the kernel source has changed since;
+* ``roofline`` of the dominant kernel (the pass with the longer average
+  duration, timed with HIP events around each pass): its algorithmic HBM
+  bytes per launch over that duration, against 8 TB/s. Per token-head,
+  chunk_chain moves q, k, v, o (bf16), g (fp32) and the 192 B of bf16
+  T diag(beta e^gamma), T diag(beta) that chunk_prep left in the workspace
+  (1220 B), plus the fp32 final states; chunk_prep moves k, g, beta and
+  writes those 192 B (456 B). ``traffic`` is the measured HBM bytes per
+  launch from the committed counter summary (profiles/), or null when the
+  kernel source has changed since. ``path`` gives the whole step against the
+  method's own 1032 B per token-head (q, k, v, o, g, beta) and the
+  matrix-core rate against the 2.5 PFLOP/s dense bf16 peak;
+* ``one_pass``: the same call without a workspace (one kernel that solves
+  each chunk's system on the sequential path);
 * ``decode``: one in-place step of B=256, H=32, d=128 fp32 states (512 MiB),
   GB/s of algorithmic traffic and its fraction of 8 TB/s;
 * ``mixer``: prologue -> prefill -> epilogue at B=8, T=8192, H=16, d=128;
@@ -40,8 +50,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, TFLOP/s
 METRIC = "prefill tokens/s (H=16,d=128,T=4096) + decode state GB/s vs HBM peak"
-PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "prefill_chunk_B4_H16_T4096_traffic.md")
-CHUNK_SRC = os.path.join(ROOT, "gated_deltanet_recurrence_amd", "csrc", "prefill_chunk.hip")
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "chunk_prefill_B4_H16_T4096_traffic.md")
+CHUNK_SRC = os.path.join(ROOT, "gated_deltanet_recurrence_amd", "csrc", "prefill_split.hip")
 
 
 def prefill_flops_per_token_head(dk=128, dv=128, C=64):
@@ -57,6 +67,20 @@ def prefill_bytes(B, T, H, dk=128, dv=128, n_states_out=None, n_states_in=0):
     per = 2 * (dk + dk + dv + dv) + 4 + 4          # q, k, v, o bf16; g, beta fp32
     states = (n_states_out if n_states_out is not None else B) * H * dv * dk * 4
     return tok_head * per + states + n_states_in * H * dv * dk * 4
+
+
+TWU_BYTES_PER_TOKEN_HEAD = 2 * 3 * 32 * 32 * 2 // 64   # 192: bf16 T_w, T_u blocks per token
+
+
+def chain_bytes(B, T, H, dk=128, dv=128):
+    """chunk_chain per launch: q, k, v, o bf16, g fp32, T_w/T_u read back, final states."""
+    per = 2 * (dk + dk + dv + dv) + 4 + TWU_BYTES_PER_TOKEN_HEAD
+    return B * T * H * per + B * H * dv * dk * 4
+
+
+def prep_bytes(B, T, H, dk=128):
+    """chunk_prep per launch: k bf16, g and beta fp32 read, T_w/T_u written."""
+    return B * T * H * (2 * dk + 4 + 4 + TWU_BYTES_PER_TOKEN_HEAD)
 
 
 def decode_bytes(B, H, dk=128, dv=128):
@@ -82,14 +106,14 @@ def _src_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per prefill launch from the committed counter summary, if the
-    kernel source still matches the hash recorded there."""
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if
+    the kernel source still matches the hash recorded there."""
     if not os.path.exists(PROFILE_SUMMARY):
         return None, "no counter summary"
     text = open(PROFILE_SUMMARY).read()
     m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]{16})", text)
-    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_bytes = re.search(kernel + r"_hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not m_hash or not m_bytes:
         return None, "summary lacks fields"
     if m_hash.group(1) != _src_hash(CHUNK_SRC):
@@ -108,15 +132,43 @@ def bench_prefill(gdn, inputs, steps, warmup):
                          fin=torch.empty((c.B, c.H, 128, 128), dtype=torch.float32,
                                          device="cuda")))
 
+    nws = gdn.gdn_prefill_workspace_size(c.B, c.T, c.H, 128, 128, c.B, False, torch.bfloat16)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+
     def step(i):
         s = sets[i & 1]
         gdn.gdn_prefill(s["q"], s["k"], s["v"], s["g"], s["beta"], None, s["fin"], s["o"],
-                        scale=c.scale)
+                        scale=c.scale, workspace=ws)
+
+    def step_one_pass(i):
+        s = sets[i & 1]
+        gdn.gdn_prefill(s["q"], s["k"], s["v"], s["g"], s["beta"], None, s["fin"], s["o"],
+                        scale=c.scale, workspace=None)
     ms = event_time(step, steps, warmup)
+    ms_one = event_time(step_one_pass, max(2, steps // 4), 2)
+
+    # each pass alone: events recorded between the launches, on the stream both run on
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        s = sets[i & 1]
+        ev[i][0].record(stream)
+        gdn.gdn_prefill_prepare(s["k"], s["g"], s["beta"], ws)
+        ev[i][1].record(stream)
+        gdn.gdn_prefill_apply(s["q"], s["k"], s["v"], s["g"], ws, None, s["fin"], s["o"],
+                              scale=c.scale)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    ms_prep = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    ms_chain = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
     tokens = c.B * c.T
-    nbytes = prefill_bytes(c.B, c.T, c.H)
-    flops = prefill_flops_per_token_head() * c.B * c.T * c.H
-    return dict(ms=ms, tokens=tokens, bytes=nbytes, flops=flops, case=c)
+    return dict(ms=ms, ms_one_pass=ms_one, ms_prep=ms_prep, ms_chain=ms_chain, tokens=tokens,
+                bytes=prefill_bytes(c.B, c.T, c.H), chain_bytes=chain_bytes(c.B, c.T, c.H),
+                prep_bytes=prep_bytes(c.B, c.T, c.H),
+                flops=prefill_flops_per_token_head() * c.B * c.T * c.H, case=c)
 
 
 def bench_decode(gdn, inputs, steps, warmup):
@@ -153,8 +205,11 @@ def bench_mixer(gdn, inputs, steps, warmup):
     def pro(i):
         gdn.gdn_mixer_prologue(*raw, A, out=outs)
 
+    ws = torch.empty(gdn.gdn_prefill_workspace_size(B, T, H, D, D, B, False, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+
     def core(i):
-        gdn.gdn_prefill(*outs, o=y, scale=c.scale)
+        gdn.gdn_prefill(*outs, o=y, scale=c.scale, workspace=ws)
 
     def epi(i):
         gdn.gdn_mixer_epilogue(y, z, out=out, eps=c.eps)
@@ -183,9 +238,13 @@ def bench_varlen(gdn, inputs, steps, warmup):
     q, k, v, g, beta, s0, cu = (d(x) for x in (c.q, c.k, c.v, c.g, c.beta, c.s0, c.cu_seqlens))
     fin = torch.empty_like(s0)
     o = torch.empty_like(v)
+    N = cu.numel() - 1
+    ws = torch.empty(gdn.gdn_prefill_workspace_size(1, q.shape[1], q.shape[2], 128, 128, N, True,
+                                                    torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
 
     def step(i):
-        gdn.gdn_prefill(q, k, v, g, beta, s0, fin, o, cu_seqlens=cu, scale=c.scale)
+        gdn.gdn_prefill(q, k, v, g, beta, s0, fin, o, cu_seqlens=cu, scale=c.scale, workspace=ws)
     ms = event_time(step, max(1, steps // 4), 1)
     total = int(c.cu_seqlens[-1])
     return dict(workload="packed prefill H=32 d=128 bf16, 8 sequences log-uniform in [512, 65536], "
@@ -248,8 +307,12 @@ def main():
     if "prefill" in which:
         p = bench_prefill(gdn, inputs, args.steps, args.warmup)
         sec = p["ms"] * 1e-3
-        achieved = p["bytes"] / sec / 1e9
-        traffic, why = measured_traffic()
+        chain_dominant = p["ms_chain"] >= p["ms_prep"]
+        kname = "chunk_chain_kernel" if chain_dominant else "chunk_prep_kernel"
+        k_ms = p["ms_chain"] if chain_dominant else p["ms_prep"]
+        k_bytes = p["chain_bytes"] if chain_dominant else p["prep_bytes"]
+        achieved = k_bytes / (k_ms * 1e-3) / 1e9
+        traffic, why = measured_traffic(kname)
         result.update({
             "value": round(p["tokens"] / sec, 1), "unit": "tokens/s",
             "ms_per_step": round(p["ms"], 5),
@@ -257,13 +320,20 @@ def main():
                                    "fp32 gates and state, zero initial state, 64-token chunks",
                        "global_batch": 4, "seq_len": 4096, "heads": 16, "head_dim": 128,
                        "parallelism": "single GPU"},
-            "roofline": {"kernel": "prefill_chunk_kernel", "bound": "hbm",
+            "roofline": {"kernel": kname, "bound": "hbm",
                          "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                         "traffic_note": why, "algorithmic_bytes_per_launch": p["bytes"],
-                         "avg_launch_us": round(p["ms"] * 1e3, 2),
-                         "mfma_algorithmic_tflops": round(p["flops"] / sec / 1e12, 2),
-                         "mfma_frac_of_bf16_peak": round(p["flops"] / sec / 1e12 / BF16_PEAK_TFLOPS, 4)},
+                         "traffic_note": why, "algorithmic_bytes_per_launch": k_bytes,
+                         "avg_launch_us": round(k_ms * 1e3, 2),
+                         "other_kernel_avg_launch_us": round((p["ms_prep"] if chain_dominant
+                                                              else p["ms_chain"]) * 1e3, 2)},
+            "path": {"algorithmic_bytes_per_step": p["bytes"],
+                     "GB/s": round(p["bytes"] / sec / 1e9, 1),
+                     "frac_of_hbm_peak": round(p["bytes"] / sec / 1e9 / HBM_PEAK_GBS, 4),
+                     "mfma_algorithmic_tflops": round(p["flops"] / sec / 1e12, 2),
+                     "mfma_frac_of_bf16_peak": round(p["flops"] / sec / 1e12 / BF16_PEAK_TFLOPS, 4)},
+            "one_pass": {"ms_per_step": round(p["ms_one_pass"], 5),
+                         "tokens_per_s": round(p["tokens"] / (p["ms_one_pass"] * 1e-3), 1)},
         })
     else:
         result.update({"value": None, "unit": "tokens/s", "ms_per_step": None,

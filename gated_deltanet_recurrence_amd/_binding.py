@@ -26,13 +26,17 @@ _DTYPES = {torch.float32: GDN_DTYPE_F32, torch.bfloat16: GDN_DTYPE_BF16}
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
 _f = ctypes.c_float
+_sz = ctypes.c_size_t
 
 # name -> argtypes (restype int for all)
 _SIGS = {
     "gdn_version": [],
     "gdn_status_string": [_i],
     "gdn_check_cu_seqlens": [_vp, _i, _i],
-    "gdn_prefill": [_vp] * 9 + [_i] * 6 + [_f, _i, _vp],
+    "gdn_prefill": [_vp] * 9 + [_i] * 6 + [_f, _i, _vp, _sz, _vp],
+    "gdn_prefill_workspace_size": [_i] * 8 + [_vp],
+    "gdn_prefill_prepare": [_vp] * 4 + [_i] * 7 + [_vp, _sz, _vp],
+    "gdn_prefill_apply": [_vp] * 8 + [_i] * 6 + [_f, _i, _vp, _sz, _vp],
     "gdn_prefill_recurrent": [_vp] * 9 + [_i] * 6 + [_f, _i, _vp],
     "gdn_decode_step": [_vp] * 7 + [_i] * 4 + [_f, _i, _vp],
     "gdn_mixer_prologue": [_vp] * 14 + [_i] * 7 + [_vp],
@@ -95,8 +99,17 @@ def _dtype_code(t: torch.Tensor) -> int:
     return _DTYPES[t.dtype]
 
 
+def gdn_prefill_workspace_size(B, T, H, d_k, d_v, N, varlen, dtype) -> int:
+    """Bytes of workspace gdn_prefill uses for these sizes (0: none)."""
+    code = dtype if isinstance(dtype, int) else _dtype_code(torch.empty(0, dtype=dtype))
+    out = ctypes.c_size_t(0)
+    _check(load().gdn_prefill_workspace_size(B, T, H, d_k, d_v, N, int(bool(varlen)), code,
+                                             ctypes.byref(out)))
+    return out.value
+
+
 def _prefill(entry, q, k, v, g, beta, initial_state=None, final_state=None, o=None,
-             cu_seqlens=None, scale=None):
+             cu_seqlens=None, scale=None, workspace=None):
     B, T, H, dk = q.shape
     dv = v.shape[3]
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
@@ -113,16 +126,72 @@ def _prefill(entry, q, k, v, g, beta, initial_state=None, final_state=None, o=No
         _dev(o, "o", dt, (B, T, H, dv)),
         _dev(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,)),
     ]
-    _check(getattr(load(), entry)(*args, B, T, H, dk, dv, N, float(scale), _dtype_code(q),
-                                  _stream(q.device)))
+    tail = [float(scale), _dtype_code(q)]
+    if entry == "gdn_prefill":
+        if isinstance(workspace, str):
+            if workspace != "auto":
+                raise GDNError(f"workspace must be None, 'auto' or a tensor, got {workspace!r}")
+            nbytes = gdn_prefill_workspace_size(B, T, H, dk, dv, N, cu_seqlens is not None,
+                                                _dtype_code(q))
+            workspace = (torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+                         if nbytes else None)
+        tail += list(_ws(workspace))
+    _check(getattr(load(), entry)(*args, B, T, H, dk, dv, N, *tail, _stream(q.device)))
     return o, final_state
 
 
 def gdn_prefill(q, k, v, g, beta, initial_state=None, final_state=None, o=None,
-                cu_seqlens=None, scale=None):
-    """Chunkwise forward (see include/gdn.h). Returns (o, final_state)."""
+                cu_seqlens=None, scale=None, workspace="auto"):
+    """Chunkwise forward (see include/gdn.h). Returns (o, final_state).
+
+    workspace: "auto" allocates the scratch memory of the two-pass path with
+    torch (size from gdn_prefill_workspace_size), a uint8 GPU tensor is used
+    as given, None selects the single-pass path that needs none."""
     return _prefill("gdn_prefill", q, k, v, g, beta, initial_state, final_state, o,
-                    cu_seqlens, scale)
+                    cu_seqlens, scale, workspace)
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise GDNError("workspace must be a contiguous GPU tensor")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def gdn_prefill_prepare(k, g, beta, workspace, cu_seqlens=None, d_v=None):
+    """First pass of the workspace path (see include/gdn.h): T diag(beta e^gamma)
+    and T diag(beta) of every chunk into `workspace`."""
+    B, T, H, dk = k.shape
+    dv = dk if d_v is None else d_v
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    _check(load().gdn_prefill_prepare(
+        _dev(k, "k"), _dev(g, "g", torch.float32, (B, T, H)),
+        _dev(beta, "beta", torch.float32, (B, T, H)),
+        _dev(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,)),
+        B, T, H, dk, dv, N, _dtype_code(k), *_ws(workspace), _stream(k.device)))
+
+
+def gdn_prefill_apply(q, k, v, g, workspace, initial_state=None, final_state=None, o=None,
+                      cu_seqlens=None, scale=None):
+    """Second pass of the workspace path: the state recurrence over chunks.
+    Returns (o, final_state)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    dt = q.dtype
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=q.device)
+    if scale is None:
+        scale = dk ** -0.5
+    _check(load().gdn_prefill_apply(
+        _dev(q, "q", dt), _dev(k, "k", dt, q.shape), _dev(v, "v", dt, (B, T, H, dv)),
+        _dev(g, "g", torch.float32, (B, T, H)),
+        _dev(initial_state, "initial_state", torch.float32, (N, H, dv, dk)),
+        _dev(final_state, "final_state", torch.float32, (N, H, dv, dk)),
+        _dev(o, "o", dt, (B, T, H, dv)), _dev(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,)),
+        B, T, H, dk, dv, N, float(scale), _dtype_code(q), *_ws(workspace), _stream(q.device)))
+    return o, final_state
 
 
 def gdn_prefill_recurrent(q, k, v, g, beta, initial_state=None, final_state=None, o=None,

@@ -18,6 +18,12 @@ hipError_t launch_prefill_recurrent(const void *, const void *, const void *, co
 hipError_t launch_prefill_chunk(const void *, const void *, const void *, const float *,
                                 const float *, const float *, float *, void *, const int32_t *,
                                 int, int, int, float, hipStream_t);
+hipError_t launch_prefill_prepare(const void *, const float *, const float *, const int32_t *,
+                                  int, int, int, void *, hipStream_t);
+hipError_t launch_prefill_apply(const void *, const void *, const void *, const float *,
+                                const float *, float *, void *, const int32_t *, int, int, int,
+                                float, const void *, hipStream_t);
+size_t prefill_split_workspace_bytes(long tokens, int H, int N);
 template <typename TIO>
 hipError_t launch_prologue(const void *, const void *, const void *, const void *, const void *,
                            const void *, const float *, const float *, const int32_t *, void *,
@@ -53,6 +59,17 @@ int check_prefill(const void *q, const void *k, const void *v, const float *g, c
     return GDN_OK;
 }
 
+// bf16 with d_k = d_v = 128 runs on the MFMA chunk kernels
+bool chunk_path(int dtype, int d_k, int d_v) {
+    return dtype == GDN_DTYPE_BF16 && d_k == 128 && d_v == 128;
+}
+
+// a caller's workspace for the two-pass chunk path: 256-byte aligned, large enough
+bool workspace_ok(const void *ws, size_t bytes, int B, int T, int H, int N) {
+    return (reinterpret_cast<uintptr_t>(ws) & 255) == 0 &&
+           bytes >= gdn::prefill_split_workspace_bytes((long)B * T, H, N);
+}
+
 }  // namespace
 
 extern "C" {
@@ -68,6 +85,7 @@ const char *gdn_status_string(int status)
     case GDN_ERR_DTYPE: return "unknown dtype";
     case GDN_ERR_UNSUPPORTED: return "valid arguments, but this size or mode is not implemented";
     case GDN_ERR_HIP: return "the HIP runtime reported an error at launch";
+    case GDN_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
     default: return "unknown status";
     }
 }
@@ -97,20 +115,77 @@ int gdn_prefill_recurrent(const void *q, const void *k, const void *v, const flo
     return status_of(e);
 }
 
+int gdn_prefill_workspace_size(int B, int T, int H, int d_k, int d_v, int N, int varlen,
+                               int dtype, size_t *bytes)
+{
+    if (!bytes) return GDN_ERR_NULL;
+    *bytes = 0;
+    // the pointer checks of gdn_prefill do not apply here: pass stand-ins
+    const int32_t *cu = varlen ? reinterpret_cast<const int32_t *>(bytes) : nullptr;
+    const void *p = bytes;
+    const int st = check_prefill(p, p, p, (const float *)p, (const float *)p, p, cu, B, T, H,
+                                 d_k, d_v, N, dtype);
+    if (st != GDN_OK) return st;
+    if (chunk_path(dtype, d_k, d_v))
+        *bytes = gdn::prefill_split_workspace_bytes((long)B * T, H, N);
+    return GDN_OK;
+}
+
 int gdn_prefill(const void *q, const void *k, const void *v, const float *g, const float *beta,
                 const float *initial_state, float *final_state, void *o,
                 const int32_t *cu_seqlens, int B, int T, int H, int d_k, int d_v, int N,
-                float scale, int dtype, void *stream)
+                float scale, int dtype, void *workspace, size_t workspace_bytes, void *stream)
 {
     int st = check_prefill(q, k, v, g, beta, o, cu_seqlens, B, T, H, d_k, d_v, N, dtype);
     if (st != GDN_OK) return st;
     hipStream_t s = (hipStream_t)stream;
-    if (dtype == GDN_DTYPE_BF16 && d_k == 128 && d_v == 128) {
-        return status_of(gdn::launch_prefill_chunk(q, k, v, g, beta, initial_state, final_state,
-                                                   o, cu_seqlens, T, H, N, scale, s));
+    if (chunk_path(dtype, d_k, d_v)) {
+        if (!workspace)
+            return status_of(gdn::launch_prefill_chunk(q, k, v, g, beta, initial_state,
+                                                       final_state, o, cu_seqlens, T, H, N,
+                                                       scale, s));
+        if (!workspace_ok(workspace, workspace_bytes, B, T, H, N)) return GDN_ERR_WORKSPACE;
+        hipError_t e = gdn::launch_prefill_prepare(k, g, beta, cu_seqlens, T, H, N, workspace, s);
+        if (e == hipSuccess)
+            e = gdn::launch_prefill_apply(q, k, v, g, initial_state, final_state, o, cu_seqlens,
+                                          T, H, N, scale, workspace, s);
+        return status_of(e);
     }
     return gdn_prefill_recurrent(q, k, v, g, beta, initial_state, final_state, o, cu_seqlens, B,
                                  T, H, d_k, d_v, N, scale, dtype, stream);
+}
+
+int gdn_prefill_prepare(const void *k, const float *g, const float *beta,
+                        const int32_t *cu_seqlens, int B, int T, int H, int d_k, int d_v, int N,
+                        int dtype, void *workspace, size_t workspace_bytes, void *stream)
+{
+    // q, v and o are not arguments of this pass: validate with stand-ins
+    const void *p = workspace ? workspace : (const void *)k;
+    int st = check_prefill(p, k, p, g, beta, p, cu_seqlens, B, T, H, d_k, d_v, N, dtype);
+    if (st != GDN_OK) return st;
+    if (!chunk_path(dtype, d_k, d_v)) return GDN_ERR_UNSUPPORTED;
+    if (!workspace) return GDN_ERR_NULL;
+    if (!workspace_ok(workspace, workspace_bytes, B, T, H, N)) return GDN_ERR_WORKSPACE;
+    return status_of(gdn::launch_prefill_prepare(k, g, beta, cu_seqlens, T, H, N, workspace,
+                                                 (hipStream_t)stream));
+}
+
+int gdn_prefill_apply(const void *q, const void *k, const void *v, const float *g,
+                      const float *initial_state, float *final_state, void *o,
+                      const int32_t *cu_seqlens, int B, int T, int H, int d_k, int d_v, int N,
+                      float scale, int dtype, const void *workspace, size_t workspace_bytes,
+                      void *stream)
+{
+    // beta is folded into the workspace: validate with a stand-in
+    const float *pb = workspace ? (const float *)workspace : g;
+    int st = check_prefill(q, k, v, g, pb, o, cu_seqlens, B, T, H, d_k, d_v, N, dtype);
+    if (st != GDN_OK) return st;
+    if (!chunk_path(dtype, d_k, d_v)) return GDN_ERR_UNSUPPORTED;
+    if (!workspace) return GDN_ERR_NULL;
+    if (!workspace_ok(workspace, workspace_bytes, B, T, H, N)) return GDN_ERR_WORKSPACE;
+    return status_of(gdn::launch_prefill_apply(q, k, v, g, initial_state, final_state, o,
+                                               cu_seqlens, T, H, N, scale, workspace,
+                                               (hipStream_t)stream));
 }
 
 int gdn_decode_step(const void *q, const void *k, const void *v, const float *g,

@@ -40,6 +40,7 @@
 #ifndef GDN_H
 #define GDN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -60,7 +61,9 @@ typedef enum {
                                  inconsistent with another argument                 */
     GDN_ERR_DTYPE = -3,       /* dtype is not a gdn_dtype_t value                   */
     GDN_ERR_UNSUPPORTED = -4, /* valid but not implemented (e.g. head dim > 128)    */
-    GDN_ERR_HIP = -5          /* the HIP runtime reported an error at launch        */
+    GDN_ERR_HIP = -5,         /* the HIP runtime reported an error at launch        */
+    GDN_ERR_WORKSPACE = -6    /* workspace smaller than gdn_prefill_workspace_size()
+                                 or not 256-byte aligned                            */
 } gdn_status_t;
 
 /* Library version (GDN_VERSION). */
@@ -101,16 +104,76 @@ const char *gdn_status_string(int status);
  *                 pointers (q, k, v, g, beta, o) are not read and may be NULL.
  *   d_k, d_v      d_k in {16, 32, 64, 128}; 1 <= d_v <= 128 (else
  *                 GDN_ERR_UNSUPPORTED). bf16 with d_k = d_v = 128 runs the
- *                 MFMA chunk kernel; every other case runs the fp32
+ *                 MFMA chunk kernels; every other case runs the fp32
  *                 token-serial kernel (same result up to rounding).
  *   scale         multiplies every output (d_k^-1/2 in the usual layer)
+ *   workspace     NULL, or DEVICE scratch memory owned by the caller, of at
+ *                 least gdn_prefill_workspace_size() bytes, 256-byte aligned
+ *                 (hipMalloc's alignment); its contents on entry do not
+ *                 matter and are garbage on exit. With a workspace the MFMA
+ *                 path runs in two passes: the per-chunk triangular systems
+ *                 of every chunk and head are solved in parallel first, and
+ *                 only the state recurrence walks the chunks in order (the
+ *                 fast path). With NULL it runs as one pass that solves each
+ *                 chunk's system on the sequential path (slower, no scratch).
+ *                 Both give the same result up to rounding order. Ignored by
+ *                 the token-serial path. Calls that share a workspace must be
+ *                 ordered on one stream.
+ *   workspace_bytes  size of workspace; GDN_ERR_WORKSPACE if workspace is
+ *                 non-NULL and too small or misaligned.
  */
 int gdn_prefill(const void *q, const void *k, const void *v,
                 const float *g, const float *beta,
                 const float *initial_state, float *final_state,
                 void *o, const int32_t *cu_seqlens,
                 int B, int T, int H, int d_k, int d_v, int N,
-                float scale, int dtype, void *stream);
+                float scale, int dtype,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gdn_prefill_workspace_size - bytes of workspace that gdn_prefill uses for
+ * these sizes (same meaning as there; varlen != 0 when cu_seqlens will be
+ * non-NULL). 0 when the path for these sizes uses none. The size depends on
+ * the token count and the number of heads only, not on the offsets: 12 KiB
+ * per (64-token chunk slot, head), with (B*T)/64 + N + 1 slots. Written to
+ * *bytes; returns GDN_OK or the error gdn_prefill would return for these
+ * sizes.
+ */
+int gdn_prefill_workspace_size(int B, int T, int H, int d_k, int d_v, int N,
+                               int varlen, int dtype, size_t *bytes);
+
+/*
+ * gdn_prefill_prepare, gdn_prefill_apply - the two passes of gdn_prefill's
+ * workspace path as separate calls; gdn_prefill with a workspace is exactly
+ * prepare followed by apply on one stream. Arguments have the meaning they
+ * have for gdn_prefill; both calls must see the same sizes, cu_seqlens, k
+ * and g. Only the MFMA chunk path has passes (bf16, d_k = d_v = 128; else
+ * GDN_ERR_UNSUPPORTED), and workspace is required (GDN_ERR_NULL).
+ *
+ * prepare reads k, g, beta and writes, for every 64-token chunk of every
+ * head, the chunk's T diag(beta e^gamma) and T diag(beta) into the workspace
+ * (T the inverse of the unit-lower-triangular key Gram system, gamma the
+ * in-chunk prefix sum of g: "5. Linear Attention" chapter, section "Chunk
+ * implementation of the Delta Rule", stage 1). All chunks are independent.
+ *
+ * apply reads q, k, v, g and the workspace, walks each sequence's chunks in
+ * order carrying the state, and writes o and final_state (stages 2-3 of the
+ * same section). beta enters only through the workspace.
+ *
+ * Splitting lets a caller overlap prepare of one batch with apply of
+ * another on two streams (with two workspaces).
+ */
+int gdn_prefill_prepare(const void *k, const float *g, const float *beta,
+                        const int32_t *cu_seqlens,
+                        int B, int T, int H, int d_k, int d_v, int N, int dtype,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+int gdn_prefill_apply(const void *q, const void *k, const void *v, const float *g,
+                      const float *initial_state, float *final_state,
+                      void *o, const int32_t *cu_seqlens,
+                      int B, int T, int H, int d_k, int d_v, int N,
+                      float scale, int dtype,
+                      const void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * gdn_prefill_recurrent - the same forward pass as gdn_prefill, computed by

@@ -11,6 +11,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gdn.h")
 
 GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_UNSUPPORTED = 0, -1, -2, -3, -4
+GDN_ERR_WORKSPACE = -6
 
 
 def declared_functions():
@@ -41,7 +42,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.gdn_version() == 1
-    for st in (GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_UNSUPPORTED, -5, 99):
+    for st in (GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_UNSUPPORTED, -5,
+               GDN_ERR_WORKSPACE, 99):
         s = lib.gdn_status_string(st)
         assert isinstance(s, bytes) and len(s) > 0
 
@@ -49,12 +51,43 @@ def test_version_and_status_strings(lib):
 P = ctypes.c_void_p(16)      # a non-null dummy pointer; never dereferenced on rejection
 
 
-def _prefill(lib, *, null=None, B=1, T=8, H=1, dk=128, dv=128, N=1, dtype=1, cu=None):
+def _prefill(lib, *, null=None, B=1, T=8, H=1, dk=128, dv=128, N=1, dtype=1, cu=None,
+             ws=None, ws_bytes=0):
     ptrs = [P] * 8
     if null is not None:
         ptrs[null] = None
     q, k, v, g, beta, s0, s1, o = ptrs
-    return lib.gdn_prefill(q, k, v, g, beta, s0, s1, o, cu, B, T, H, dk, dv, N, 1.0, dtype, None)
+    return lib.gdn_prefill(q, k, v, g, beta, s0, s1, o, cu, B, T, H, dk, dv, N, 1.0, dtype,
+                           ws, ws_bytes, None)
+
+
+def _ws_size(lib, B=1, T=8, H=1, dk=128, dv=128, N=1, varlen=0, dtype=1):
+    out = ctypes.c_size_t(12345)
+    st = lib.gdn_prefill_workspace_size(B, T, H, dk, dv, N, varlen, dtype, ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_size(lib):
+    # 12 KiB of bf16 T diag(beta e^gamma), T diag(beta) per (chunk slot, head);
+    # (tokens / 64 + N + 1) slots
+    assert _ws_size(lib, B=4, T=4096, H=16, N=4) == (GDN_OK, (4 * 4096 // 64 + 5) * 16 * 12288)
+    assert _ws_size(lib, B=1, T=1000, H=3, N=7, varlen=1) == (GDN_OK, (1000 // 64 + 8) * 3 * 12288)
+    assert _ws_size(lib, B=2, T=0, H=2, N=2) == (GDN_OK, 3 * 2 * 12288)
+    # paths that use no workspace
+    assert _ws_size(lib, dtype=0) == (GDN_OK, 0)
+    assert _ws_size(lib, dk=64, dv=64) == (GDN_OK, 0)
+    # the errors gdn_prefill would return
+    assert _ws_size(lib, dk=48)[0] == GDN_ERR_UNSUPPORTED
+    assert _ws_size(lib, B=2, N=1)[0] == GDN_ERR_SHAPE
+    assert _ws_size(lib, dtype=9)[0] == GDN_ERR_DTYPE
+    assert lib.gdn_prefill_workspace_size(1, 8, 1, 128, 128, 1, 0, 1, None) == GDN_ERR_NULL
+
+
+def test_prefill_workspace_rejected(lib):
+    need = _ws_size(lib, T=100)[1]
+    aligned = ctypes.c_void_p(1 << 20)      # never dereferenced: rejected before launch
+    assert _prefill(lib, T=100, ws=aligned, ws_bytes=need - 1) == GDN_ERR_WORKSPACE
+    assert _prefill(lib, T=100, ws=ctypes.c_void_p((1 << 20) + 64), ws_bytes=need) == GDN_ERR_WORKSPACE
 
 
 @pytest.mark.parametrize("which", [0, 1, 2, 3, 4, 7])
@@ -111,3 +144,24 @@ def test_check_cu_seqlens(lib):
     assert f(arr([1, 5, 12]), 2, 12) == GDN_ERR_SHAPE
     assert f(arr([0, 5, 11]), 2, 12) == GDN_ERR_SHAPE
     assert f(None, 2, 12) == GDN_ERR_NULL
+
+
+def test_prepare_apply_validation(lib):
+    need = _ws_size(lib, T=100)[1]
+    ws = ctypes.c_void_p(1 << 20)            # never dereferenced: rejected before launch
+    prep, app = lib.gdn_prefill_prepare, lib.gdn_prefill_apply
+    # only the MFMA chunk path has two passes
+    assert prep(P, P, P, None, 1, 100, 1, 64, 64, 1, 1, ws, need, None) == GDN_ERR_UNSUPPORTED
+    assert prep(P, P, P, None, 1, 100, 1, 128, 128, 1, 0, ws, need, None) == GDN_ERR_UNSUPPORTED
+    # the workspace is required and checked
+    assert prep(P, P, P, None, 1, 100, 1, 128, 128, 1, 1, None, 0, None) == GDN_ERR_NULL
+    assert prep(P, P, P, None, 1, 100, 1, 128, 128, 1, 1, ws, need - 1, None) == GDN_ERR_WORKSPACE
+    assert prep(None, P, P, None, 1, 100, 1, 128, 128, 1, 1, ws, need, None) == GDN_ERR_NULL
+    assert prep(P, P, P, None, 2, 100, 1, 128, 128, 1, 1, ws, need, None) == GDN_ERR_SHAPE
+    a = [P] * 3 + [P, None, None, P, None]
+    assert app(*a, 1, 100, 1, 128, 128, 1, 1.0, 1, None, 0, None) == GDN_ERR_NULL
+    assert app(*a, 1, 100, 1, 128, 128, 1, 1.0, 1, ws, need - 1, None) == GDN_ERR_WORKSPACE
+    assert app(*a, 1, 100, 1, 16, 16, 1, 1.0, 1, ws, need, None) == GDN_ERR_UNSUPPORTED
+    b = list(a)
+    b[6] = None                              # o
+    assert app(*b, 1, 100, 1, 128, 128, 1, 1.0, 1, ws, need, None) == GDN_ERR_NULL

@@ -22,13 +22,21 @@ def _tol(case):
     return TOL_F32 if case.dtype == "f32" else TOL_BF16
 
 
-def run_prefill(case, entry=None, with_final=True, init=True):
-    entry = entry or gdn.gdn_prefill
+# gdn_prefill's two execution paths of the MFMA chunk algorithm: with a
+# workspace (two passes: all chunks' triangular solves in parallel, then the
+# state recurrence) and without (one pass)
+PATHS = ["two_pass", "one_pass"]
+WS = {"two_pass": "auto", "one_pass": None}
+
+
+def run_prefill(case, entry=None, with_final=True, init=True, path="two_pass"):
     s0 = dev(case.s0) if (init and case.s0 is not None) else None
     fin = torch.empty((case.N, case.H, case.d_v, case.d_k), dtype=torch.float32,
                       device="cuda:0") if with_final else None
+    extra = {} if entry is not None else {"workspace": WS[path]}
+    entry = entry or gdn.gdn_prefill
     o, _ = entry(dev(case.q), dev(case.k), dev(case.v), dev(case.g), dev(case.beta), s0, fin,
-                 cu_seqlens=dev(case.cu_seqlens), scale=case.scale)
+                 cu_seqlens=dev(case.cu_seqlens), scale=case.scale, **extra)
     torch.cuda.synchronize()
     return o, fin
 
@@ -52,16 +60,17 @@ def test_tiny_fp32():
 
 @pytest.fixture(scope="module")
 def prefill_full():
-    return inputs.make_prefill()
+    c = inputs.make_prefill()
+    return c, oracle_prefill(c)
 
 
-def test_prefill_full_size(prefill_full):
+@pytest.mark.parametrize("path", PATHS)
+def test_prefill_full_size(prefill_full, path):
     """B=4, H=16, T=4096, d=128, bf16, zero initial state: all 64 chains."""
-    c = prefill_full
-    o, fin = run_prefill(c)
-    o_ref, s_ref = oracle_prefill(c)
+    c, (o_ref, s_ref) = prefill_full
+    o, fin = run_prefill(c, path=path)
     eo, es = o_err(o, o_ref), s_err(fin, s_ref)
-    report("prefill B4 H16 T4096", o=eo, state=es)
+    report(f"prefill B4 H16 T4096 {path}", o=eo, state=es)
     assert eo <= TOL_BF16 and es <= TOL_BF16
 
 
@@ -104,32 +113,42 @@ def test_mixer_full_size_sampled():
     assert e_y <= TOL_BF16 and e_out <= TOL_BF16
 
 
-def test_varlen_full_size_sampled():
+VARLEN_HEADS = [0, 5, 17, 31]
+
+
+@pytest.fixture(scope="module")
+def varlen_full():
+    c = inputs.make_varlen()
+    ref = oracle.gdn_recurrent_heads(c.q, c.k, c.v, c.g, c.beta, VARLEN_HEADS, c.s0,
+                                     c.cu_seqlens, c.scale, nthreads=0)
+    return c, ref
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_varlen_full_size_sampled(varlen_full, path):
     """H=32, d=128, 8 packed sequences (lengths log-uniform in [512, 65536]),
     non-zero initial states: every sequence, four heads."""
-    c = inputs.make_varlen()
-    o, fin = run_prefill(c)
-    heads = [0, 5, 17, 31]
+    c, (outs, s_ref) = varlen_full
+    o, fin = run_prefill(c, path=path)
     cu = [int(x) for x in c.cu_seqlens.tolist()]
-    outs, s_ref = oracle.gdn_recurrent_heads(c.q, c.k, c.v, c.g, c.beta, heads, c.s0,
-                                             c.cu_seqlens, c.scale, nthreads=0)
-    o_h = o.cpu()[:, :, heads]
+    o_h = o.cpu()[:, :, VARLEN_HEADS]
     eo = max(o_err(o_h[:, a:b], r) for (a, b), r in zip(zip(cu[:-1], cu[1:]), outs) if b > a)
-    es = s_err(fin.cpu()[:, heads], s_ref)
-    report(f"varlen lengths={c.meta['lengths']}", o=eo, state=es)
+    es = s_err(fin.cpu()[:, VARLEN_HEADS], s_ref)
+    report(f"varlen {path} lengths={c.meta['lengths']}", o=eo, state=es)
     assert eo <= TOL_BF16 and es <= TOL_BF16
 
 
 # --- smaller shapes: tiles, ragged tails, edge cases ------------------------
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 130, 257])
 @pytest.mark.parametrize("with_state", [False, True])
-def test_prefill_ragged_bf16(T, with_state):
+def test_prefill_ragged_bf16(T, with_state, path):
     c = inputs.make_prefill(seed=1000 + T, B=2, T=T, H=3, d=128, with_state=with_state)
-    o, fin = run_prefill(c)
+    o, fin = run_prefill(c, path=path)
     o_ref, s_ref = oracle_prefill(c)
     eo, es = o_err(o, o_ref), s_err(fin, s_ref)
-    report(f"prefill bf16 T={T} state={with_state}", o=eo, state=es)
+    report(f"prefill bf16 T={T} state={with_state} {path}", o=eo, state=es)
     assert eo <= TOL_BF16 and es <= TOL_BF16
 
 
@@ -179,40 +198,43 @@ def test_decode_head_dims(d):
     assert o_err(o[:, None], o_ref) <= TOL_F32 and s_err(st, s_ref) <= TOL_F32
 
 
-def test_packed_with_empty_and_tiny_sequences():
+@pytest.mark.parametrize("path", PATHS)
+def test_packed_with_empty_and_tiny_sequences(path):
     """Packed sequences including empty ones and ones shorter than a chunk; an
     empty sequence returns its initial state."""
     lengths = [0, 1, 64, 0, 3, 129, 70]
     c = inputs.make_varlen(seed=55, H=2, d=128, lengths=lengths)
-    o, fin = run_prefill(c)
+    o, fin = run_prefill(c, path=path)
     o_ref, s_ref = oracle_prefill(c)
     cu = [int(x) for x in c.cu_seqlens.tolist()]
     eo, es = o_err_packed(o, o_ref, cu), s_err(fin, s_ref)
-    report("packed with empties", o=eo, state=es)
+    report(f"packed with empties {path}", o=eo, state=es)
     assert eo <= TOL_BF16 and es <= TOL_BF16
     for n, L in enumerate(lengths):
         if L == 0:
             assert torch.equal(fin[n].cpu(), c.s0[n])
 
 
-def test_zero_length_batch():
+@pytest.mark.parametrize("path", PATHS)
+def test_zero_length_batch(path):
     """T = 0: nothing to compute; the final state is the initial state."""
     c = inputs.make_prefill(seed=3, B=2, T=0, H=2, d=128, with_state=True)
-    o, fin = run_prefill(c)
+    o, fin = run_prefill(c, path=path)
     assert o.numel() == 0 and torch.equal(fin.cpu(), c.s0)
 
 
-def test_gate_special_cases():
+@pytest.mark.parametrize("path", PATHS)
+def test_gate_special_cases(path):
     """beta = 0, alpha = 1 leaves the state unchanged; beta = 0 alone scales it."""
     c = inputs.make_prefill(seed=4, B=1, T=100, H=2, d=128, with_state=True)
     c.beta.zero_()
     c.g.zero_()
-    _, fin = run_prefill(c)
+    _, fin = run_prefill(c, path=path)
     assert s_err(fin, host64(c.s0)) <= 1e-6
     c = inputs.make_prefill(seed=5, B=1, T=100, H=2, d=128, with_state=True)
     c.beta.zero_()
     c.g.mul_(0.02)                     # keep the accumulated decay well above denormals
-    _, fin = run_prefill(c)
+    _, fin = run_prefill(c, path=path)
     decay = np.exp(host64(c.g)[0].sum(axis=0))            # [H]
     assert s_err(fin, host64(c.s0) * decay[None, :, None, None]) <= 1e-4
 
@@ -265,11 +287,36 @@ def test_chunk_matches_recurrent_on_gpu():
     assert o_err(o_c, host64(o_r)) <= TOL_BF16 and s_err(f_c, host64(f_r)) <= TOL_BF16
 
 
-def test_deterministic():
+@pytest.mark.parametrize("path", PATHS)
+def test_deterministic(path):
     c = inputs.make_prefill(seed=14, B=2, T=300, H=2, d=128, with_state=True)
-    o1, f1 = run_prefill(c)
-    o2, f2 = run_prefill(c)
+    o1, f1 = run_prefill(c, path=path)
+    o2, f2 = run_prefill(c, path=path)
     assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+def test_two_pass_and_one_pass_agree():
+    c = inputs.make_prefill(seed=15, B=3, T=700, H=3, d=128, with_state=True)
+    o1, f1 = run_prefill(c, path="two_pass")
+    o2, f2 = run_prefill(c, path="one_pass")
+    assert o_err(o1, host64(o2)) <= TOL_BF16 and s_err(f1, host64(f2)) <= TOL_BF16
+
+
+def test_workspace_reuse_and_dirty_contents():
+    """A caller-owned workspace full of garbage, reused by calls of different
+    sizes, gives the results of a fresh one."""
+    big = inputs.make_prefill(seed=16, B=2, T=500, H=3, d=128, with_state=True)
+    small = inputs.make_varlen(seed=17, H=3, d=128, lengths=[5, 0, 130, 64])
+    need = max(gdn.gdn_prefill_workspace_size(2, 500, 3, 128, 128, 2, False, torch.bfloat16),
+               gdn.gdn_prefill_workspace_size(1, 199, 3, 128, 128, 4, True, torch.bfloat16))
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda:0")   # NaN bf16 patterns
+    for c in (big, small, big):
+        s0 = dev(c.s0)
+        fin = torch.empty_like(s0)
+        o, _ = gdn.gdn_prefill(dev(c.q), dev(c.k), dev(c.v), dev(c.g), dev(c.beta), s0, fin,
+                               cu_seqlens=dev(c.cu_seqlens), scale=c.scale, workspace=ws)
+        o_ref, f_ref = run_prefill(c, path="two_pass")
+        assert torch.equal(o, o_ref) and torch.equal(fin, f_ref)
 
 
 def test_prologue_packed_sequences():
@@ -285,3 +332,18 @@ def test_prologue_packed_sequences():
     assert o_err(q.cpu(), mid["q"]) <= TOL_BF16
     assert o_err(k.cpu(), mid["k"]) <= TOL_BF16
     assert o_err(v.cpu(), mid["v"]) <= TOL_BF16
+
+
+def test_prepare_then_apply_equals_prefill():
+    """gdn_prefill with a workspace is gdn_prefill_prepare then gdn_prefill_apply."""
+    c = inputs.make_varlen(seed=18, H=2, d=128, lengths=[70, 0, 200, 1])
+    N = c.cu_seqlens.numel() - 1
+    ws = torch.empty(gdn.gdn_prefill_workspace_size(1, c.q.shape[1], 2, 128, 128, N, True,
+                                                    torch.bfloat16),
+                     dtype=torch.uint8, device="cuda:0")
+    q, k, v, g, beta, s0, cu = (dev(x) for x in (c.q, c.k, c.v, c.g, c.beta, c.s0, c.cu_seqlens))
+    gdn.gdn_prefill_prepare(k, g, beta, ws, cu_seqlens=cu)
+    fin = torch.empty_like(s0)
+    o, _ = gdn.gdn_prefill_apply(q, k, v, g, ws, s0, fin, cu_seqlens=cu, scale=c.scale)
+    o_ref, f_ref = run_prefill(c, path="two_pass")
+    assert torch.equal(o, o_ref) and torch.equal(fin, f_ref)
