@@ -24,7 +24,7 @@
 // q, k, v, o, g and beta.
 //
 // Workspace layout: for head h and chunk slot s, 6144 bf16 at
-// ((h * nslots) + s) * 6144: T_w then T_u, each as the three non-zero 32 x 32
+// ((h * nslots) + s) * 6144: -T_w then T_u, each as the three non-zero 32 x 32
 // blocks (rows 0-31 x cols 0-31, rows 32-63 x cols 0-31, rows 32-63 x cols
 // 32-63), row-major. Chunk c of sequence n has slot (bos_n / 64) + n + c,
 // where bos_n is its first token: slots of different sequences never
@@ -63,36 +63,94 @@ static_assert(P_LDS_BYTES <= 48 * 1024, "three prep workgroups per CU");
 
 // ---------------------------------------------------------------------------
 // Pass 2: chunk_chain. One workgroup of 8 waves per (32-wide d_v tile, head,
-// sequence).
+// sequence). Row strides are chosen for the v_mfma_f32_16x16x32_bf16 operand
+// reads (16 consecutive rows, four 16-byte column chunks): with a stride of
+// 32 bytes modulo 128 they hit every LDS bank equally.
 // ---------------------------------------------------------------------------
 constexpr int DVT = 32;
 constexpr int NT = 512;
-constexpr int LD_QK = DK + 8;                  // sQ, sK, sWn rows (bf16)
-constexpr int LD_T = C + 8;                    // token-contiguous bf16 rows
-constexpr int LD_S = DK + 8;                   // sS rows (bf16)
-constexpr int LD_O = DVT + 8;                  // output staging (bf16)
-constexpr int SZ_QK = C * LD_QK * 2;           // 17408
-constexpr int SZ_KT = DK * LD_T * 2;           // 18432
-constexpr int SZ_VT = DVT * LD_T * 2;          // 4608
-constexpr int SZ_TT = C * LD_T * 2;            // 9216
-constexpr int SZ_S = DVT * LD_S * 2;           // 8704
+constexpr int LD_R = DK + 16;                  // rows of 128 bf16 (288 B): Q, K, S
+constexpr int LD_64 = C + 16;                  // rows of 64 bf16 (160 B): T_w, T_u, P, Delta^T
+constexpr int LD_V = DVT + 8;                  // V rows (32 bf16 of this tile)
+constexpr int LD_O = DVT + 8;                  // output staging rows
+constexpr int SZ_R = C * LD_R * 2;             // 18432
+constexpr int SZ_V = C * LD_V * 2;             // 5120
+constexpr int SZ_64 = C * LD_64 * 2;           // 10240
+constexpr int SZ_S = DVT * LD_R * 2;           // 9216
+constexpr int SZ_DT = DVT * LD_64 * 2;         // 5120
 constexpr int SZ_O = C * LD_O * 2;             // 5120
 constexpr int SZ_SC = 3 * C * 4;               // gamma, e^gamma, e^{gamma_63 - gamma}
 constexpr int OFF_Q = 0;
-constexpr int OFF_K = OFF_Q + SZ_QK;
-constexpr int OFF_KT = OFF_K + SZ_QK;
-constexpr int OFF_VT = OFF_KT + SZ_KT;
-constexpr int OFF_TW = OFF_VT + SZ_VT;
-constexpr int OFF_TU = OFF_TW + SZ_TT;
-constexpr int OFF_WN = OFF_TU + SZ_TT;
-constexpr int OFF_P = OFF_WN + SZ_QK;
-constexpr int OFF_S = OFF_P + SZ_TT;
-constexpr int OFF_DT = OFF_S + SZ_S;
-constexpr int OFF_DTW = OFF_DT + SZ_VT;
-constexpr int OFF_O = OFF_DTW + SZ_VT;
+constexpr int OFF_K = OFF_Q + SZ_R;
+constexpr int OFF_V = OFF_K + SZ_R;
+constexpr int OFF_TW = OFF_V + SZ_V;
+constexpr int OFF_TU = OFF_TW + SZ_64;
+constexpr int OFF_P = OFF_TU + SZ_64;
+constexpr int OFF_S = OFF_P + SZ_64;           // two buffers
+constexpr int OFF_DT = OFF_S + 2 * SZ_S;
+constexpr int OFF_O = OFF_DT + SZ_DT;
 constexpr int OFF_SC = OFF_O + SZ_O;
 constexpr int LDS_BYTES = OFF_SC + SZ_SC;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// 16 x 8 operand slice of a row-major bf16 LDS matrix for
+// v_mfma_f32_16x16x32_bf16: row r0 + lane%16, columns k0 + 8 (lane/16) .. +8
+__device__ __forceinline__ bf16x8 frag16(const bf16 *m, int ld, int r0, int k0, int lane) {
+    return *reinterpret_cast<const bf16x8 *>(m + (r0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
+}
+// The same slice of a matrix stored with its 16-byte column chunks swizzled
+// by row: chunk c of row r sits at c ^ ((r / 4) % 4). Accumulator tiles are
+// written into such matrices 8 bytes per lane (row lane%16, columns 4 (lane/16)
+// ..), which without the swizzle would hit the same LDS banks 3x over; the
+// swizzle leaves these 16-byte reads conflict-free. r0 must be a multiple of 16.
+__device__ __forceinline__ int swz(int lane) { return ((lane & 15) >> 2) << 3; }
+__device__ __forceinline__ bf16x8 frag16_sw(const bf16 *m, int ld, int r0, int k0, int lane) {
+    return *reinterpret_cast<const bf16x8 *>(m + (r0 + (lane & 15)) * ld + ((k0 + 8 * (lane >> 4)) ^ swz(lane)));
+}
+// The same slice with the columns in the row order of a 16x16 accumulator
+// pair: k0 + 4 (lane/16) + {0..3} and k0 + 16 + 4 (lane/16) + {0..3}. A
+// product whose other operand is taken from accumulators (rows 4 (lane/16) +
+// r of two consecutive 16-row tiles) contracts over that order.
+__device__ __forceinline__ bf16x8 frag16_acc(const bf16 *m, int ld, int r0, int k0, int lane) {
+    const bf16 *p = m + (r0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4);
+    const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(p);
+    const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(p + 16);
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane L
+// names row k0 + L/4, columns c0 + 4 (L%4) .. +4 of a row-major matrix M, and
+// lane m receives M[k0 .. k0 + 3][c0 + m]. k0 may differ between groups.
+__device__ __forceinline__ bf16x4 tr4(const bf16 *m, int ld, int k0, int c0, int lane) {
+    const int L = lane & 15;
+    const bf16 *p = m + (k0 + (L >> 2)) * ld + c0 + 4 * (L & 3);
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p));
+}
+// Same with the four column groups at c0 + cstep (L%4): lane m receives
+// M[k0 .. k0 + 3][c0 + cstep (m/4) + m%4].
+__device__ __forceinline__ bf16x4 tr4s(const bf16 *m, int ld, int k0, int c0, int cstep, int lane) {
+    const int L = lane & 15;
+    const bf16 *p = m + (k0 + (L >> 2)) * ld + c0 + cstep * (L & 3);
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p));
+}
+// 16 x 8 operand slice whose row is chosen per lane (columns k0 + 8 (lane/16) ..)
+__device__ __forceinline__ bf16x8 frag16_row(const bf16 *m, int ld, int row, int k0, int lane) {
+    return *reinterpret_cast<const bf16x8 *>(m + row * ld + k0 + 8 * (lane >> 4));
+}
+__device__ __forceinline__ bf16x8 cat4(bf16x4 lo, bf16x4 hi) {
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+// two 16x16 fp32 accumulators as one bf16 B operand (rows 4 (lane/16) + r of
+// the first, then of the second)
+__device__ __forceinline__ bf16x8 acc_pair_bf16(f32x4 a, f32x4 b) {
+    return bf16x8{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],
+                  (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
+}
 
 // Bounds of sequence n: tokens [bos, eos) of the packed token axis.
 __device__ __forceinline__ void seq_bounds(const int32_t *cu, int n, int T, long &bos, long &eos) {
@@ -146,7 +204,7 @@ using namespace split;
 //          of every row's dot product, finished with two DPP quad sums
 //   L1/L2  the off-diagonal blocks of T by two levels of 2 x 2 block
 //          inversion, (L^-1)_21 = L22^-1 A21 L11^-1 (fp32 16x16x4 MFMA)
-//   store  T diag(beta e^gamma) and T diag(beta), bf16, to the workspace
+//   store  -T diag(beta e^gamma) and T diag(beta), bf16, to the workspace
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(P_NT)
 chunk_prep_kernel(const bf16 *__restrict__ k, const float *__restrict__ g,
@@ -326,6 +384,7 @@ chunk_prep_kernel(const bf16 *__restrict__ k, const float *__restrict__ g,
         const int blk = rem >> 7, row = (rem >> 2) & 31, cc = rem & 3;
         const int i = 32 * (blk > 0 ? 1 : 0) + row, j0 = 32 * (blk == 2 ? 1 : 0) + 8 * cc;
         const float *sc = mat ? sBeta : sBeg;
+        const float sgn = mat ? 1.f : -1.f;    // T_w is stored negated
         const f32x4 t0 = *reinterpret_cast<const f32x4 *>(sT + i * P_LD_A + j0);
         const f32x4 t1 = *reinterpret_cast<const f32x4 *>(sT + i * P_LD_A + j0 + 4);
         const f32x4 s0 = *reinterpret_cast<const f32x4 *>(sc + j0);
@@ -335,8 +394,8 @@ chunk_prep_kernel(const bf16 *__restrict__ k, const float *__restrict__ g,
         bf16x8 out;
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
-            out[e2] = (bf16)(zero ? 0.f : t0[e2] * s0[e2]);
-            out[e2 + 4] = (bf16)(zero ? 0.f : t1[e2] * s1[e2]);
+            out[e2] = (bf16)(zero ? 0.f : sgn * t0[e2] * s0[e2]);
+            out[e2 + 4] = (bf16)(zero ? 0.f : sgn * t1[e2] * s1[e2]);
         }
         *reinterpret_cast<bf16x8 *>(dst + 8 * e) = out;
     }
@@ -344,24 +403,33 @@ chunk_prep_kernel(const bf16 *__restrict__ k, const float *__restrict__ g,
 
 // ---------------------------------------------------------------------------
 // chunk_chain: the sequential pass. One workgroup of 8 waves per (32-wide d_v
-// tile, head, sequence); waves 0-3 keep S^T (128 x 32, fp32) in MFMA
-// accumulators for the whole sequence, 32 x 32 each; a bf16 copy of S in LDS
-// is the operand of the next chunk. The next chunk's q, k, v, T_w, T_u are
-// loaded into registers while the current one is computed.
+// tile, head, sequence), two LDS barriers per chunk.
 //
-//   load   Q, K row-major, K^T and V^T (token-contiguous, column-swizzled),
-//          T_w, T_u into LDS; gamma (wave 3); the previous chunk's output
-//          rows leave LDS for HBM
-//   prep   W^T = K^T T_w^T (one 32 x 32 tile per wave) -> LDS as -W;
-//          U = T_u V (waves 0-1, registers); P^T tiles of
-//          P = lower_incl_diag(Q K^T * Gamma) (waves 2, 3, 5) -> LDS;
-//          (Q S^T)^T = S Q^T (waves 6-7, registers)
-//   delta  Delta = U - W S^T (waves 0-1) -> LDS as Delta^T and Delta~^T
-//   out    O^T = (Q S^T)^T diag(e^gamma) + Delta^T P^T (waves 6-7) -> LDS;
-//          S^T <- e^{gamma_63} S^T + K^T Delta~ (waves 0-3)
+// Waves 0 and 1 carry the recurrence, each for 16 of the tile's d_v columns:
+// the wave keeps its slice of S^T (128 x 16, fp32) in eight 16x16 MFMA
+// accumulators for the whole sequence, and per chunk computes
+//   X     = K S^T                       (B operand: the state accumulators)
+//   Delta = T_u V - T_w X               (B operand: X's accumulators)
+//   S^T  <- e^{gamma_63} S^T + K^T Delta~,  Delta~_j = e^{gamma_63 - gamma_j} Delta_j
+//                                       (B operand: Delta~'s accumulators)
+// entirely in registers: an accumulator pair holds rows 4 (lane/16) + r of
+// two consecutive 16-row tiles, which is a B operand over that row order, and
+// the matching A operand is read from LDS in the same order (frag16_acc) or
+// transposed on the fly (tr4). Grouping T_w K S^T as T_w (K S^T) means W =
+// T_w K is never formed.
+// Waves 2 and 3 form the output, O^T = (S Q^T) diag(e^gamma) + Delta^T P^T,
+// for the same column halves; waves 6 and 7 form
+// P = lower_incl_diag(Q K^T * Gamma) (as P^T tiles, stored row-major);
+// waves 4 and 5 copy the previous chunk's output rows to HBM.
 //
-// Every product is arranged so that a lane's accumulator holds 4 consecutive
-// elements of a stored row (8-byte LDS writes).
+//   phase A  waves 0-1: the recurrence step of chunk c (Delta^T and the new
+//            S as bf16 into LDS); waves 2-3: S Q^T; waves 6-7: P
+//   phase B  waves 2-3: + Delta^T P^T -> output staging; the other waves store
+//            chunk c+1 (loaded into registers one chunk earlier) into LDS and
+//            issue the loads of chunk c+2
+//
+// Tokens past the end of a sequence are identity steps (q = k = v = 0,
+// g = 0, and T_w, T_u vanish on them) and their outputs are not stored.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(NT, 1)
 chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
@@ -373,15 +441,12 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     bf16 *sQ = reinterpret_cast<bf16 *>(smem + OFF_Q);
     bf16 *sK = reinterpret_cast<bf16 *>(smem + OFF_K);
-    bf16 *sKt = reinterpret_cast<bf16 *>(smem + OFF_KT);
-    bf16 *sVt = reinterpret_cast<bf16 *>(smem + OFF_VT);
-    bf16 *sTw = reinterpret_cast<bf16 *>(smem + OFF_TW);
+    bf16 *sV = reinterpret_cast<bf16 *>(smem + OFF_V);
+    bf16 *sTw = reinterpret_cast<bf16 *>(smem + OFF_TW);     // -T_w
     bf16 *sTu = reinterpret_cast<bf16 *>(smem + OFF_TU);
-    bf16 *sWn = reinterpret_cast<bf16 *>(smem + OFF_WN);
     bf16 *sP = reinterpret_cast<bf16 *>(smem + OFF_P);
-    bf16 *sS = reinterpret_cast<bf16 *>(smem + OFF_S);
+    bf16 *sS = reinterpret_cast<bf16 *>(smem + OFF_S);       // [2][DVT][LD_R]
     bf16 *sDt = reinterpret_cast<bf16 *>(smem + OFF_DT);
-    bf16 *sDtw = reinterpret_cast<bf16 *>(smem + OFF_DTW);
     bf16 *sO = reinterpret_cast<bf16 *>(smem + OFF_O);
     float *sGam = reinterpret_cast<float *>(smem + OFF_SC);
     float *sEg = sGam + C;
@@ -405,269 +470,356 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const int len = (int)(eos - bos);
     const int nchunks = (len + C - 1) / C;
     const bf16 *wsh = ws + ((size_t)h * nslots + (size_t)((bos >> 6) + n)) * TWU_ELEMS;
-
-    // ---- state: wave w < 4 holds S^T rows d = 32w.., columns c (this tile):
-    //      accS[r] = S[cbase + lane%32][32w + acc_row(r)] ----
-    f32x16 accS = {};
     const size_t sbase = ((size_t)n * H + h) * DV * DK;
-    if (wave < 4) {
-        const int lane = tid0 & 63;
+
+    // ---- state: wave hv < 2 holds Sacc[d][r] = S[cbase + 16 hv + lane%16][dk(d, lane/16, r)]
+    //      with dk(d, q, r) = 32 (d/2) + 8 q + 4 (d%2) + r: accumulator pair (2s, 2s+1)
+    //      then covers d_k 32 s + 8 q + 0..7 contiguously (see the state update)
+    f32x4 Sacc[8];
+    bf16x8 Sb[4];                           // the same as four bf16 B operands (32 d_k each)
+#pragma unroll
+    for (int d = 0; d < 8; ++d) Sacc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (wave < 2) {
+        const int lane = tid0 & 63, m = lane & 15, qq = lane >> 4;
+        const int col = cbase + 16 * wave + m;
         if (s_init) {
-            const float *src = s_init + sbase + (size_t)(cbase + (lane & 31)) * DK + 32 * wave + 4 * (lane >> 5);
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const f32x4 x = *reinterpret_cast<const f32x4 *>(src + 8 * qq);
-#pragma unroll
-                for (int s2 = 0; s2 < 4; ++s2) accS[4 * qq + s2] = x[s2];
-            }
+            for (int d = 0; d < 8; ++d)
+                Sacc[d] = *reinterpret_cast<const f32x4 *>(s_init + sbase + (size_t)col * DK + 32 * (d >> 1) + 8 * qq + 4 * (d & 1));
         }
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-            bf16x4 x;
+        for (int s2 = 0; s2 < 4; ++s2) Sb[s2] = acc_pair_bf16(Sacc[2 * s2], Sacc[2 * s2 + 1]);
 #pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2) x[s2] = (bf16)accS[4 * qq + s2];
-            *reinterpret_cast<bf16x4 *>(sS + (lane & 31) * LD_S + 32 * wave + 8 * qq + 4 * (lane >> 5)) = x;
+        for (int d = 0; d < 8; ++d) {
+            bf16x4 x = {(bf16)Sacc[d][0], (bf16)Sacc[d][1], (bf16)Sacc[d][2], (bf16)Sacc[d][3]};
+            *reinterpret_cast<bf16x4 *>(sS + (16 * wave + m) * LD_R + ((32 * (d >> 1) + 8 * qq + 4 * (d & 1)) ^ swz(lane))) = x;
         }
     }
 
-    // ---- register prefetch of one chunk ----
-    // Q: 2 x 16 B per thread. One 8 x 8 block per thread of threads 0..159: K
-    // for 0..127 (token block jb, d_k block cb), V for 128..159. T_w / T_u: one
-    // 16-byte piece of each per thread of threads 128..511. g: wave 3.
+    // ---- loads of one chunk into registers, by waves 2-7 (loader index
+    //      lt = tid - 128 in [0, 384)); each issues eight 16-byte loads p + r * stride:
+    //        lt in [0, 128)    Q rows row0 + 8 r, columns 8 (lt % 16) ..
+    //        lt in [128, 256)  K rows, the same pattern
+    //        lt in [256, 288)  V rows vrow0 + 8 r, 8 columns of this d_v tile
+    //        lt in [288, 384)  pieces e0 + 96 r of -T_w | T_u
+    //      and every loader loads g. Rows past the end of the sequence are read from
+    //      its last token and zeroed when stored (straight-line loads: a
+    //      data-dependent branch around them makes the compiler wait for them
+    //      at the join). ----
     const int tid = tid0;
     const int tstride = H * DK;
-    const bool blk_k = tid < 128, blk_v = tid >= 128 && tid < 160, has_tt = tid >= 128;
-    const int blk_jb = blk_k ? (tid >> 4) : ((tid - 128) >> 2);
-    const int blk_cb = blk_k ? (tid & 15) : ((tid - 128) & 3);
-    const int qrow0 = tid >> 4;
-    const int tt_e = tid - 128;                // piece index within T_w (and T_u)
+    const bool loader = wave >= 2;
+    const int lt = tid - 128;
+    const int role = lt < 128 ? 0 : lt < 256 ? 1 : lt < 288 ? 2 : 3;
+    const int qk = lt & 127;
+    const int row0 = role <= 1 ? (qk >> 4) : ((lt - 256) >> 2);
+    const int lcol = role <= 1 ? 8 * (qk & 15) : 8 * ((lt - 256) & 3);
+    const int tt_e0 = lt - 288;
     const bf16 *qbase = q + (size_t)bos * tstride + (size_t)h * DK;
     const bf16 *kbase = k + (size_t)bos * tstride + (size_t)h * DK;
     const bf16 *vbase = v + (size_t)bos * tstride + (size_t)h * DV + cbase;
-    const int qoff = qrow0 * tstride + 8 * (tid & 15);
-    const int boff = 8 * blk_jb * tstride + 8 * blk_cb;
-    bf16x8 rq[2], rb[8], rtt[2];
+    bf16x8 rb[8];
     float rg = 0.f;
+    bool rg_ok = true;
+    unsigned rvalid = 0xFF;
     auto fetch = [&](int ch) {
-        const bf16x8 z8 = {};
-        const size_t coff = (size_t)ch * C * tstride;
         const int base = ch * C;
         const int lane = tid & 63;
-        const bf16 *qc = qbase + coff, *kc = kbase + coff, *vc = vbase + coff;
-        if (base + C <= len) {
+        if (role == 3) {
+            const bf16 *src = wsh + (size_t)ch * TWU_ELEMS + 8 * tt_e0;
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
-                rq[u] = *reinterpret_cast<const bf16x8 *>(qc + qoff + 32 * u * tstride);
-            if (blk_k) {
+            for (int r = 0; r < 8; ++r) rb[r] = *reinterpret_cast<const bf16x8 *>(src + r * 8 * 96);
+            rvalid = 0xFF;
+        } else {
+            const bf16 *src = (role == 0 ? qbase : role == 1 ? kbase : vbase) + (size_t)base * tstride + lcol;
+            rvalid = 0;
 #pragma unroll
-                for (int r = 0; r < 8; ++r)
-                    rb[r] = *reinterpret_cast<const bf16x8 *>(kc + boff + r * tstride);
-            } else if (blk_v) {
-#pragma unroll
-                for (int r = 0; r < 8; ++r)
-                    rb[r] = *reinterpret_cast<const bf16x8 *>(vc + boff + r * tstride);
+            for (int r = 0; r < 8; ++r) {
+                const int t = row0 + 8 * r;
+                const bool ok = base + t < len;
+                rvalid |= (ok ? 1u : 0u) << r;
+                rb[r] = *reinterpret_cast<const bf16x8 *>(src + (size_t)(ok ? t : len - 1 - base) * tstride);
             }
+        }
+        // every loader loads g (only wave 7 uses it): a load under a wave-dependent
+        // branch would again make the compiler wait for it at the join
+        rg_ok = base + lane < len;
+        rg = g[((size_t)bos + base + (rg_ok ? lane : len - 1 - base)) * H + h];
+    };
+    auto store = [&]() {
+        if (rvalid != 0xFF) {
+            const bf16x8 z8 = {};
+#pragma unroll
+            for (int r = 0; r < 8; ++r) rb[r] = (rvalid >> r) & 1 ? rb[r] : z8;
+        }
+        if (role <= 1) {
+            bf16 *dst = (role == 0 ? sQ : sK) + row0 * LD_R + lcol;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) *reinterpret_cast<bf16x8 *>(dst + 8 * r * LD_R) = rb[r];
+        } else if (role == 2) {
+            bf16 *dst = sV + row0 * LD_V + lcol;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) *reinterpret_cast<bf16x8 *>(dst + 8 * r * LD_V) = rb[r];
         } else {
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                rq[u] = z8;
-                if (base + qrow0 + 32 * u < len)
-                    rq[u] = *reinterpret_cast<const bf16x8 *>(qc + qoff + 32 * u * tstride);
-            }
-            if (blk_k || blk_v) {
-                const bf16 *bc = blk_k ? kc : vc;
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    rb[r] = z8;
-                    if (base + 8 * blk_jb + r < len)
-                        rb[r] = *reinterpret_cast<const bf16x8 *>(bc + boff + r * tstride);
-                }
+            for (int r = 0; r < 8; ++r) {
+                const int e = tt_e0 + 96 * r;          // 0..767
+                const int mat = e >= 384 ? 1 : 0, rem = e - 384 * mat;
+                const int blk = rem >> 7, row = (rem >> 2) & 31, cc = rem & 3;
+                const int off = (32 * (blk > 0 ? 1 : 0) + row) * LD_64 + 32 * (blk == 2 ? 1 : 0) + 8 * cc;
+                *reinterpret_cast<bf16x8 *>((mat ? sTu : sTw) + off) = rb[r];
             }
         }
-        if (has_tt) {
-            const bf16 *wc = wsh + (size_t)ch * TWU_ELEMS;
-            rtt[0] = *reinterpret_cast<const bf16x8 *>(wc + 8 * tt_e);
-            rtt[1] = *reinterpret_cast<const bf16x8 *>(wc + 8 * (tt_e + 384));
-        }
-        if (wave == 3) {
-            const bool ok = base + lane < len;
-            rg = ok ? g[((size_t)bos + base + lane) * H + h] : 0.f;
-        }
-    };
-    if (nchunks > 0) fetch(0);
-
-    for (int ch = 0; ch < nchunks; ++ch) {
-        const int base = ch * C;
-        int tidl = tid0;
-        asm volatile("" : "+v"(tidl));         // keep lane-derived addresses out of loop-invariant hoisting
-        const int lane = tidl & 63;
-        const int l32 = lane & 31, lh = lane >> 5;
-
-        // ---------------- load: registers -> LDS; decay prefix sums ----------------
-        // the previous chunk's output rows (64 x 32 bf16) leave LDS first
-        if (ch > 0 && tidl < 256) {
-            const int row = tidl >> 2, col = 8 * (tidl & 3);
-            if (base - C + row < len)
-                *reinterpret_cast<bf16x8 *>(o + ((size_t)bos + base - C + row) * H * DV + (size_t)h * DV + cbase + col) =
-                    *reinterpret_cast<const bf16x8 *>(sO + row * LD_O + col);
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-            *reinterpret_cast<bf16x8 *>(sQ + (qrow0 + 32 * u) * LD_QK + 8 * (tidl & 15)) = rq[u];
-        if (blk_k || blk_v) {
-            bf16x8 tr[8];
-            transpose8x8(rb, tr);
-            if (blk_k) {
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    *reinterpret_cast<bf16x8 *>(sK + (8 * blk_jb + r) * LD_QK + 8 * blk_cb) = rb[r];
-                    *reinterpret_cast<bf16x8 *>(sKt + (8 * blk_cb + r) * LD_T + 8 * (blk_jb ^ ((blk_cb >> 1) & 7))) = tr[r];
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 8; ++r)
-                    *reinterpret_cast<bf16x8 *>(sVt + (8 * blk_cb + r) * LD_T + 8 * (blk_jb ^ (blk_cb >> 1))) = tr[r];
-            }
-        }
-        if (has_tt) {
-            const int e = tidl - 128;
-            const int blk = e >> 7, row = (e >> 2) & 31, cc = e & 3;
-            const int off = (32 * (blk > 0 ? 1 : 0) + row) * LD_T + 32 * (blk == 2 ? 1 : 0) + 8 * cc;
-            *reinterpret_cast<bf16x8 *>(sTw + off) = rtt[0];
-            *reinterpret_cast<bf16x8 *>(sTu + off) = rtt[1];
-        }
-        if (wave == 3) {
-            const float gam = wave_inclusive_scan(rg);
+        if (wave == 7) {
+            const int lane = tid & 63;
+            const float gam = wave_inclusive_scan(rg_ok ? rg : 0.f);
             const float glast = __builtin_bit_cast(
                 float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gam), 63));
             sGam[lane] = gam;
             sEg[lane] = __expf(gam);
             sDend[lane] = __expf(glast - gam);
         }
-        lds_barrier();
-        if (ch + 1 < nchunks) fetch(ch + 1);   // in flight during this chunk
+    };
+    // P's 16 x 16 tiles (0, 1) and (2, 3) lie above the diagonal but inside the
+    // 32-key k-steps of the output product: zero once, never written again.
+    // (The upper-right 32 x 32 blocks of T_w and T_u are never read.)
+    for (int e = tid; e < C * LD_64 / 8; e += NT)
+        reinterpret_cast<bf16x8 *>(sP)[e] = bf16x8{};
+    if (nchunks > 0 && loader) {
+        fetch(0);
+        store();
+        fetch(nchunks > 1 ? 1 : 0);
+    }
+    lds_barrier();
 
-        auto rows4 = [&](const float *vv, int i0, int qq) {
-            return *reinterpret_cast<const f32x4 *>(vv + i0 + 8 * qq + 4 * lh);
+    // Each wave role runs its own loop with the same two barriers per chunk;
+    // the loaders' register prefetch is then straight-line code (every
+    // iteration loads, the last two re-read the last chunk), so the compiler
+    // never waits for it at the loop back-edge.
+    if (wave < 2) {
+        // ============ waves 0-1: the recurrence ============
+        // the sequential path: these waves win instruction arbitration on their SIMDs
+        __builtin_amdgcn_s_setprio(3);
+        const int hv = wave;
+        for (int ch = 0; ch < nchunks; ++ch) {
+            int tidl = tid0;
+            asm volatile("" : "+v"(tidl));  // keep lane-derived addresses out of loop-invariant hoisting
+            const int lane = tidl & 63, m = lane & 15, qq = lane >> 4;
+            const int cur = ch & 1;
+            // U = T_u V and X = K S^T
+            f32x4 dacc[4], xacc[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) { dacc[t] = f32x4{0.f, 0.f, 0.f, 0.f}; xacc[t] = dacc[t]; }
+            {
+                // X tile t takes K rows 32 (t/2) + 8 (m/4) + 4 (t%2) + m%4, so that its
+                // accumulator pairs run over tokens 32 s + 8 q + 0..7 contiguously
+                bf16x8 fk[4][4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int row = 32 * (t >> 1) + 8 * (m >> 2) + 4 * (t & 1) + (m & 3);
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2) fk[t][s2] = frag16_row(sK, LD_R, row, 32 * s2, lane);
+                }
+                bf16x8 fv[2], fu[4][2];
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+                    fv[s2] = cat4(tr4(sV, LD_V, 32 * s2 + 8 * qq, 16 * hv, lane),
+                                  tr4(sV, LD_V, 32 * s2 + 8 * qq + 4, 16 * hv, lane));
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2)
+                        if (s2 <= (t >> 1)) fu[t][s2] = frag16(sTu, LD_64, 16 * t, 32 * s2, lane);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) xacc[t] = mfma16(fk[t][s2], Sb[s2], xacc[t]);
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2)
+                        if (s2 <= (t >> 1)) dacc[t] = mfma16(fu[t][s2], fv[s2], dacc[t]);
+            }
+            // Delta = U + (-T_w) X
+            {
+                bf16x8 fw[4][2];
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2)
+                        if (s2 <= (t >> 1)) fw[t][s2] = frag16(sTw, LD_64, 16 * t, 32 * s2, lane);
+                const bf16x8 xb0 = acc_pair_bf16(xacc[0], xacc[1]);
+                const bf16x8 xb1 = acc_pair_bf16(xacc[2], xacc[3]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    dacc[t] = mfma16(fw[t][0], xb0, dacc[t]);
+                    if (t >= 2) dacc[t] = mfma16(fw[t][1], xb1, dacc[t]);
+                }
+            }
+            // Delta^T -> LDS (output term); Delta~ as the B operand of the update
+            bf16x8 db[2];
+            {
+                f32x4 dend[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    dend[t] = *reinterpret_cast<const f32x4 *>(sDend + 16 * t + 4 * qq);
+                    bf16x4 x = {(bf16)dacc[t][0], (bf16)dacc[t][1], (bf16)dacc[t][2], (bf16)dacc[t][3]};
+                    *reinterpret_cast<bf16x4 *>(sDt + (16 * hv + m) * LD_64 + ((16 * t + 4 * qq) ^ swz(lane))) = x;
+                }
+                db[0] = acc_pair_bf16(dacc[0] * dend[0], dacc[1] * dend[1]);
+                db[1] = acc_pair_bf16(dacc[2] * dend[2], dacc[3] * dend[3]);
+            }
+            // S^T <- e^{gamma_63} S^T + K^T Delta~ (A operand: K transposed on read)
+            {
+                const float eend = sEg[C - 1];
+                bf16x8 fkt[8][2];
+#pragma unroll
+                for (int d = 0; d < 8; ++d)
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2)
+                        fkt[d][s2] = cat4(tr4s(sK, LD_R, 32 * s2 + 4 * qq, 32 * (d >> 1) + 4 * (d & 1), 8, lane),
+                                          tr4s(sK, LD_R, 32 * s2 + 16 + 4 * qq, 32 * (d >> 1) + 4 * (d & 1), 8, lane));
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int d = 0; d < 8; ++d) {
+                    Sacc[d] = Sacc[d] * eend;
+                    Sacc[d] = mfma16(fkt[d][0], db[0], Sacc[d]);
+                    Sacc[d] = mfma16(fkt[d][1], db[1], Sacc[d]);
+                }
+            }
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) Sb[s2] = acc_pair_bf16(Sacc[2 * s2], Sacc[2 * s2 + 1]);
+            bf16 *sSn = sS + (cur ^ 1) * DVT * LD_R;
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                bf16x4 x = {(bf16)Sacc[d][0], (bf16)Sacc[d][1], (bf16)Sacc[d][2], (bf16)Sacc[d][3]};
+                *reinterpret_cast<bf16x4 *>(sSn + (16 * hv + m) * LD_R + ((32 * (d >> 1) + 8 * qq + 4 * (d & 1)) ^ swz(lane))) = x;
+            }
+            lds_barrier();
+            lds_barrier();
+        }
+    } else if (wave < 4) {
+        // ============ waves 2-3: the output for d_v rows 16 hv .. ============
+        const int hv = wave - 2;
+        f32x4 oacc[4];
+        for (int ch = 0; ch < nchunks; ++ch) {
+            int tidl = tid0;
+            asm volatile("" : "+v"(tidl));
+            const int lane = tidl & 63, m = lane & 15, qq = lane >> 4;
+            const int cur = ch & 1;
+            // (Q S^T)^T = S Q^T, all 64 tokens, then e^gamma per token
+            {
+                const bf16 *sSc = sS + cur * DVT * LD_R;
+                bf16x8 fs[4], fq[4][4];
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) {
+                    fs[s2] = frag16_sw(sSc, LD_R, 16 * hv, 32 * s2, lane);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) fq[t][s2] = frag16(sQ, LD_R, 16 * t, 32 * s2, lane);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) oacc[t] = mfma16(fs[s2], fq[t][s2], oacc[t]);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) oacc[t] = oacc[t] * sEg[16 * t + m];
+            }
+            lds_barrier();
+            // O^T += Delta^T P^T; token tile t needs keys 0 .. 16 t + 15
+            {
+                bf16x8 fd[2], fp[4][2];
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    fd[s2] = frag16_sw(sDt, LD_64, 16 * hv, 32 * s2, lane);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        if (s2 <= (t >> 1)) fp[t][s2] = frag16_sw(sP, LD_64, 16 * t, 32 * s2, lane);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2)
+                        if (s2 <= (t >> 1)) oacc[t] = mfma16(fd[s2], fp[t][s2], oacc[t]);
+                // oacc[t][r] = O[token 16 t + m][d_v 16 hv + 4 qq + r]
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    bf16x4 x = {(bf16)(scale * oacc[t][0]), (bf16)(scale * oacc[t][1]),
+                                (bf16)(scale * oacc[t][2]), (bf16)(scale * oacc[t][3])};
+                    *reinterpret_cast<bf16x4 *>(sO + (16 * t + m) * LD_O + 16 * hv + 4 * qq) = x;
+                }
+            }
+            if (ch + 1 < nchunks) store();     // chunk ch + 1
+            fetch(ch + 2 < nchunks ? ch + 2 : nchunks - 1);
+            lds_barrier();
+        }
+    } else {
+        // ============ waves 4-7: P (one query row each; wave 5 also moves the
+        //              previous chunk's output rows to HBM), then loads ============
+        // a chunk's output rows (64 x 32 bf16) from the staging buffer to HBM
+        auto ostore = [&](int chp) {
+            const int e = (int)threadIdx.x & 63;        // one wave: 256 16-byte pieces
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int piece = e + 64 * u, row = piece >> 2, col = 8 * (piece & 3);
+                const int tok = chp * C + row;
+                if (tok < len)
+                    *reinterpret_cast<bf16x8 *>(o + ((size_t)bos + tok) * H * DV + (size_t)h * DV + cbase + col) =
+                        *reinterpret_cast<const bf16x8 *>(sO + row * LD_O + col);
+            }
         };
-
-        // ---------------- prep: -W, U, P, Q S^T (no dependence on the state but Q S^T) ----
-        f32x16 accD = {}, accOi = {};
-        {
-            // W^T tile: d_k rows 32 ct.., tokens 32 rt..; T_w is lower triangular,
-            // so token tile 0 needs tokens 0..31 only
-            const int rt = wave >> 2, ct = wave & 3;
-            f32x16 acc = {};
-            acc = rt == 0 ? mma32s<2, true, false>(acc, sKt, LD_T, 32 * ct, sTw, LD_T, 0, lane)
-                          : mma32s<4, true, false>(acc, sKt, LD_T, 32 * ct, sTw, LD_T, 32, lane);
+        for (int ch = 0; ch < nchunks; ++ch) {
+            int tidl = tid0;
+            asm volatile("" : "+v"(tidl));
+            const int lane = tidl & 63, m = lane & 15, qq = lane >> 4;
+            {
+                // P^T tiles (keys 16 J.., queries 16 I..) for J <= I, one query row
+                // I per wave: I = 3 (wave 6), 2 (wave 7), 1 (wave 4), 0 (wave 5);
+                // the row's Q fragments are loaded once
+                const int I = wave == 6 ? 3 : wave == 7 ? 2 : wave == 4 ? 1 : 0;
+                bf16x8 fq[4];
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                bf16x4 x;
+                for (int s2 = 0; s2 < 4; ++s2) fq[s2] = frag16(sQ, LD_R, 16 * I, 32 * s2, lane);
+                const int i = 16 * I + m;
+                const float gi = sGam[i];
+                for (int J = 0; J <= I; ++J) {
+                    bf16x8 fk[4];
 #pragma unroll
-                for (int s2 = 0; s2 < 4; ++s2) x[s2] = (bf16)(-acc[4 * qq + s2]);
-                *reinterpret_cast<bf16x4 *>(sWn + (32 * rt + l32) * LD_QK + 32 * ct + 8 * qq + 4 * lh) = x;
-            }
-        }
-        if (wave == 0) {
-            accD = mma32s<2, false, true>(accD, sTu, LD_T, 0, sVt, LD_T, 0, lane);
-        } else if (wave == 1) {
-            accD = mma32s<4, false, true>(accD, sTu, LD_T, 32, sVt, LD_T, 0, lane);
-        } else if (wave == 2 || wave == 3 || wave == 5) {
-            // P^T tile: rows j (keys) of tile tj, columns i (queries) of tile ti
-            const int ti = wave == 2 ? 0 : 1, tj = wave == 5 ? 1 : 0;
-            const int i = 32 * ti + l32;
-            const float gi = sGam[i];
-            f32x4 gj[4];
+                    for (int s2 = 0; s2 < 4; ++s2) fk[s2] = frag16(sK, LD_R, 16 * J, 32 * s2, lane);
+                    __builtin_amdgcn_sched_barrier(0);
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) gj[qq] = rows4(sGam, 32 * tj, qq);
-            f32x16 acc = {};
-            acc = mma32_2<4>(acc, sK, LD_QK, 32 * tj, sQ, LD_QK, 32 * ti, lane);
+                    for (int s2 = 0; s2 < 4; ++s2) acc = mfma16(fk[s2], fq[s2], acc);
+                    // acc[r] = q_i . k_j with i = 16 I + m, j = 16 J + 4 qq + r
+                    const int j0 = 16 * J + 4 * qq;
+                    const f32x4 gj = *reinterpret_cast<const f32x4 *>(sGam + j0);
+                    bf16x4 x;
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                bf16x4 x;
-#pragma unroll
-                for (int s2 = 0; s2 < 4; ++s2) {
-                    const int j = 32 * tj + 8 * qq + 4 * lh + s2;
-                    x[s2] = (bf16)(j <= i ? acc[4 * qq + s2] * __expf(gi - gj[qq][s2]) : 0.f);
+                    for (int r = 0; r < 4; ++r)
+                        x[r] = (bf16)(j0 + r <= i ? acc[r] * __expf(gi - gj[r]) : 0.f);
+                    *reinterpret_cast<bf16x4 *>(sP + i * LD_64 + (j0 ^ swz(lane))) = x;
                 }
-                *reinterpret_cast<bf16x4 *>(sP + i * LD_T + 32 * tj + 8 * qq + 4 * lh) = x;
             }
-        } else if (wave >= 6) {
-            // (Q S^T)^T tile: rows c (this d_v tile), columns tokens 32 (wave - 6)..
-            accOi = mma32_2<4>(accOi, sS, LD_S, 0, sQ, LD_QK, 32 * (wave - 6), lane);
+            if (wave == 5 && ch > 0) {
+                ostore(ch - 1);
+            }
+            lds_barrier();
+            if (ch + 1 < nchunks) store();     // chunk ch + 1
+            fetch(ch + 2 < nchunks ? ch + 2 : nchunks - 1);
+            lds_barrier();
         }
-        lds_barrier();
-
-        // ---------------- delta: Delta = U - W S^T (waves 0, 1; tokens 32 w ..) ----------
-        if (wave < 2) {
-            const int i0 = 32 * wave;
-            f32x4 de4[4];
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) de4[qq] = rows4(sDend, i0, qq);
-            accD = mma32_2<4>(accD, sWn, LD_QK, i0, sS, LD_S, 0, lane);
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const f32x4 de = de4[qq];
-                bf16x4 dv, dw;
-#pragma unroll
-                for (int s2 = 0; s2 < 4; ++s2) {
-                    const float d = accD[4 * qq + s2];
-                    dv[s2] = (bf16)d;
-                    dw[s2] = (bf16)(d * de[s2]);
-                }
-                const int i = i0 + 8 * qq + 4 * lh;
-                *reinterpret_cast<bf16x4 *>(sDt + l32 * LD_T + i) = dv;
-                *reinterpret_cast<bf16x4 *>(sDtw + l32 * LD_T + i) = dw;
-            }
-        }
-        lds_barrier();
-
-        // ---------------- out: O^T and the state update ----------------
-        if (wave >= 6) {
-            const int rt = wave - 6, tok = 32 * rt + l32;
-            const float eg = sEg[tok];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) accOi[r] *= eg;
-            accOi = rt == 0 ? mma32s<2, false, false>(accOi, sDt, LD_T, 0, sP, LD_T, 0, lane)
-                            : mma32s<4, false, false>(accOi, sDt, LD_T, 0, sP, LD_T, 32, lane);
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                bf16x4 x;
-#pragma unroll
-                for (int s2 = 0; s2 < 4; ++s2) x[s2] = (bf16)(scale * accOi[4 * qq + s2]);
-                *reinterpret_cast<bf16x4 *>(sO + tok * LD_O + 8 * qq + 4 * lh) = x;
-            }
-        } else if (wave < 4) {
-            const float eend = sEg[C - 1];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) accS[r] *= eend;
-            accS = mma32s<4, true, false>(accS, sKt, LD_T, 32 * wave, sDtw, LD_T, 0, lane);
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                bf16x4 x;
-#pragma unroll
-                for (int s2 = 0; s2 < 4; ++s2) x[s2] = (bf16)accS[4 * qq + s2];
-                *reinterpret_cast<bf16x4 *>(sS + l32 * LD_S + 32 * wave + 8 * qq + 4 * lh) = x;
-            }
-        }
-        lds_barrier();
+        if (wave == 5 && nchunks > 0) ostore(nchunks - 1);  // the last chunk's output rows
     }
-    // the last chunk's output rows
-    if (nchunks > 0 && tid0 < 256) {
-        const int row = tid0 >> 2, col = 8 * (tid0 & 3);
-        const int base = (nchunks - 1) * C;
-        if (base + row < len)
-            *reinterpret_cast<bf16x8 *>(o + ((size_t)bos + base + row) * H * DV + (size_t)h * DV + cbase + col) =
-                *reinterpret_cast<const bf16x8 *>(sO + row * LD_O + col);
-    }
-
-    if (s_final && wave < 4) {
-        const int lane = tid0 & 63;
-        float *dst = s_final + sbase + (size_t)(cbase + (lane & 31)) * DK + 32 * wave + 4 * (lane >> 5);
+    if (s_final && wave < 2) {
+        const int lane = tid0 & 63, m = lane & 15, qq = lane >> 4;
+        float *dst = s_final + sbase + (size_t)(cbase + 16 * wave + m) * DK + 8 * qq;
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
-            *reinterpret_cast<f32x4 *>(dst + 8 * qq) =
-                f32x4{accS[4 * qq], accS[4 * qq + 1], accS[4 * qq + 2], accS[4 * qq + 3]};
+        for (int d = 0; d < 8; ++d) *reinterpret_cast<f32x4 *>(dst + 32 * (d >> 1) + 4 * (d & 1)) = Sacc[d];
     }
 }
 
