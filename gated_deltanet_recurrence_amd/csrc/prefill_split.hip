@@ -24,11 +24,16 @@
 // q, k, v, o, g and beta.
 //
 // Workspace layout: for head h and chunk slot s, 6144 bf16 at
-// ((h * nslots) + s) * 6144: -T_w then T_u, each as the three non-zero 32 x 32
-// blocks (rows 0-31 x cols 0-31, rows 32-63 x cols 0-31, rows 32-63 x cols
-// 32-63), row-major. Chunk c of sequence n has slot (bos_n / 64) + n + c,
-// where bos_n is its first token: slots of different sequences never
-// collide and every slot is below nslots = total_tokens / 64 + N + 1.
+// ((h * nslots) + s) * 6144, as 768 pieces of 8 consecutive row elements of
+// -T_w and T_u (their non-zero lower 64 x 64 part: rows 0-31 span columns
+// 0-31 only): pieces 0..255 are rows 32-63 of -T_w (8 pieces per row),
+// 256..511 rows 32-63 of T_u, 512..639 rows 0-31 of -T_w (4 per row),
+// 640..767 rows 0-31 of T_u. Chunk c of sequence n has slot
+// (bos_n / 64) + n + c, where bos_n is its first token: slots of different
+// sequences never collide and every slot is below
+// nslots = total_tokens / 64 + N + 1.
+#include <type_traits>
+
 #include "chunk_common.h"
 
 namespace gdn {
@@ -63,35 +68,54 @@ static_assert(P_LDS_BYTES <= 48 * 1024, "three prep workgroups per CU");
 
 // ---------------------------------------------------------------------------
 // Pass 2: chunk_chain. One workgroup of 8 waves per (32-wide d_v tile, head,
-// sequence). Row strides are chosen for the v_mfma_f32_16x16x32_bf16 operand
-// reads (16 consecutive rows, four 16-byte column chunks): with a stride of
-// 32 bytes modulo 128 they hit every LDS bank equally.
+// sequence), one LDS barrier per chunk. LDS holds two staging buffers (the
+// chunk being computed and the next one, written meanwhile) and two copies of
+// every tile passed between waves. Row strides are chosen for the
+// v_mfma_f32_16x16x32_bf16 operand reads (16 consecutive rows, four 16-byte
+// column chunks), which then hit every LDS bank equally: 288 bytes for rows
+// of 128, 160 for rows of 64 and 80 for rows of 32. The lower-triangular
+// 64 x 64 tiles (T_w, T_u, P) keep rows 0-31 (read in columns 0-31 only) and
+// rows 32-63 as two tiles of different width.
 // ---------------------------------------------------------------------------
 constexpr int DVT = 32;
 constexpr int NT = 512;
-constexpr int LD_R = DK + 16;                  // rows of 128 bf16 (288 B): Q, K, S
-constexpr int LD_64 = C + 16;                  // rows of 64 bf16 (160 B): T_w, T_u, P, Delta^T
-constexpr int LD_V = DVT + 8;                  // V rows (32 bf16 of this tile)
-constexpr int LD_O = DVT + 8;                  // output staging rows
-constexpr int SZ_R = C * LD_R * 2;             // 18432
-constexpr int SZ_V = C * LD_V * 2;             // 5120
-constexpr int SZ_64 = C * LD_64 * 2;           // 10240
-constexpr int SZ_S = DVT * LD_R * 2;           // 9216
-constexpr int SZ_DT = DVT * LD_64 * 2;         // 5120
-constexpr int SZ_O = C * LD_O * 2;             // 5120
+constexpr int LD_R = DK + 16;                  // 144: Q, K, S rows
+constexpr int LD_L = C + 16;                   // 80: rows 32-63 of T_w, T_u, P; Delta^T rows
+constexpr int LD_H = 32 + 8;                   // 40: rows 0-31 of T_w, T_u, P; V rows
+constexpr int SZ_QK = C * LD_R * 2;            // 18432
+constexpr int SZ_V = C * LD_H * 2;             // 5120
+constexpr int SZ_TH = 2 * 32 * LD_H * 2;       // 5120: rows 0-31 of -T_w, then of T_u
+constexpr int SZ_TL = 2 * 32 * LD_L * 2;       // 10240: rows 32-63 of -T_w, then of T_u
 constexpr int SZ_SC = 3 * C * 4;               // gamma, e^gamma, e^{gamma_63 - gamma}
-constexpr int OFF_Q = 0;
-constexpr int OFF_K = OFF_Q + SZ_R;
-constexpr int OFF_V = OFF_K + SZ_R;
-constexpr int OFF_TW = OFF_V + SZ_V;
-constexpr int OFF_TU = OFF_TW + SZ_64;
-constexpr int OFF_P = OFF_TU + SZ_64;
-constexpr int OFF_S = OFF_P + SZ_64;           // two buffers
+constexpr int B_Q = 0;
+constexpr int B_K = B_Q + SZ_QK;
+constexpr int B_V = B_K + SZ_QK;
+constexpr int B_TH = B_V + SZ_V;
+constexpr int B_TL = B_TH + SZ_TH;
+constexpr int B_SC = B_TL + SZ_TL;
+constexpr int SZ_BUF = B_SC + SZ_SC;           // 58112
+constexpr int SZ_PH = 32 * LD_H * 2;           // 2560: P rows 0-31
+constexpr int SZ_P = SZ_PH + 32 * LD_L * 2;    // 7680: P rows 0-31, then 32-63
+constexpr int SZ_S = DVT * LD_R * 2;           // 9216: bf16 S [32][144]
+constexpr int SZ_DT = DVT * LD_L * 2;          // 5120: Delta^T [32][80]
+constexpr int OFF_BUF = 0;                     // two of each from here on
+constexpr int OFF_P = OFF_BUF + 2 * SZ_BUF;
+constexpr int OFF_S = OFF_P + 2 * SZ_P;
 constexpr int OFF_DT = OFF_S + 2 * SZ_S;
-constexpr int OFF_O = OFF_DT + SZ_DT;
-constexpr int OFF_SC = OFF_O + SZ_O;
-constexpr int LDS_BYTES = OFF_SC + SZ_SC;
+constexpr int LDS_BYTES = OFF_DT + 2 * SZ_DT;  // 160256
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+static_assert(SZ_BUF % 16 == 0 && SZ_P % 16 == 0, "16-byte aligned tiles");
+
+// Accumulator tiles are written 8 bytes per lane (row lane%16, columns
+// 4 (lane/16) ..); to spread those writes over the banks the 16-byte chunks
+// of row r are swapped by ((r / 4) % 4) within aligned groups of four, which
+// keeps the 16-row operand reads conflict-free and their addresses additive
+// in the k-step. swz gives the element XOR for a lane whose row is
+// (multiple of 16) + lane%16.
+__device__ __forceinline__ int swz(int lane) { return ((lane & 15) >> 2) << 3; }
+__device__ __forceinline__ bf16x8 lds8(const bf16 *base, int off) {
+    return *reinterpret_cast<const bf16x8 *>(base + off);
+}
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -99,48 +123,13 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-// 16 x 8 operand slice of a row-major bf16 LDS matrix for
-// v_mfma_f32_16x16x32_bf16: row r0 + lane%16, columns k0 + 8 (lane/16) .. +8
-__device__ __forceinline__ bf16x8 frag16(const bf16 *m, int ld, int r0, int k0, int lane) {
-    return *reinterpret_cast<const bf16x8 *>(m + (r0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
-}
-// The same slice of a matrix stored with its 16-byte column chunks swizzled
-// by row: chunk c of row r sits at c ^ ((r / 4) % 4). Accumulator tiles are
-// written into such matrices 8 bytes per lane (row lane%16, columns 4 (lane/16)
-// ..), which without the swizzle would hit the same LDS banks 3x over; the
-// swizzle leaves these 16-byte reads conflict-free. r0 must be a multiple of 16.
-__device__ __forceinline__ int swz(int lane) { return ((lane & 15) >> 2) << 3; }
-__device__ __forceinline__ bf16x8 frag16_sw(const bf16 *m, int ld, int r0, int k0, int lane) {
-    return *reinterpret_cast<const bf16x8 *>(m + (r0 + (lane & 15)) * ld + ((k0 + 8 * (lane >> 4)) ^ swz(lane)));
-}
-// The same slice with the columns in the row order of a 16x16 accumulator
-// pair: k0 + 4 (lane/16) + {0..3} and k0 + 16 + 4 (lane/16) + {0..3}. A
-// product whose other operand is taken from accumulators (rows 4 (lane/16) +
-// r of two consecutive 16-row tiles) contracts over that order.
-__device__ __forceinline__ bf16x8 frag16_acc(const bf16 *m, int ld, int r0, int k0, int lane) {
-    const bf16 *p = m + (r0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4);
-    const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(p);
-    const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(p + 16);
-    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
 // Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane L
-// names row k0 + L/4, columns c0 + 4 (L%4) .. +4 of a row-major matrix M, and
-// lane m receives M[k0 .. k0 + 3][c0 + m]. k0 may differ between groups.
-__device__ __forceinline__ bf16x4 tr4(const bf16 *m, int ld, int k0, int c0, int lane) {
-    const int L = lane & 15;
-    const bf16 *p = m + (k0 + (L >> 2)) * ld + c0 + 4 * (L & 3);
-    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p));
-}
-// Same with the four column groups at c0 + cstep (L%4): lane m receives
-// M[k0 .. k0 + 3][c0 + cstep (m/4) + m%4].
-__device__ __forceinline__ bf16x4 tr4s(const bf16 *m, int ld, int k0, int c0, int cstep, int lane) {
-    const int L = lane & 15;
-    const bf16 *p = m + (k0 + (L >> 2)) * ld + c0 + cstep * (L & 3);
-    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p));
-}
-// 16 x 8 operand slice whose row is chosen per lane (columns k0 + 8 (lane/16) ..)
-__device__ __forceinline__ bf16x8 frag16_row(const bf16 *m, int ld, int row, int k0, int lane) {
-    return *reinterpret_cast<const bf16x8 *>(m + row * ld + k0 + 8 * (lane >> 4));
+// names 8 bytes at element offset off (its row k0 + L/4 and 4 columns of a
+// row-major matrix M), and lane m receives four consecutive rows of one
+// column: M[k0 .. k0 + 3][c(m)], where columns c(4g .. 4g + 3) are the four
+// named by lanes with L % 4 = g. k0 may differ between groups.
+__device__ __forceinline__ bf16x4 tr4(const bf16 *base, int off) {
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + off)));
 }
 __device__ __forceinline__ bf16x8 cat4(bf16x4 lo, bf16x4 hi) {
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -378,11 +367,19 @@ chunk_prep_kernel(const bf16 *__restrict__ k, const float *__restrict__ g,
     bf16 *dst = ws + ((size_t)h * nslots + slot) * TWU_ELEMS;
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
-        const int e = tid + P_NT * u;          // 0..767
-        const int mat = e >= 384 ? 1 : 0;
-        const int rem = e - 384 * mat;
-        const int blk = rem >> 7, row = (rem >> 2) & 31, cc = rem & 3;
-        const int i = 32 * (blk > 0 ? 1 : 0) + row, j0 = 32 * (blk == 2 ? 1 : 0) + 8 * cc;
+        const int e = tid + P_NT * u;          // piece 0..767 (order in the chain pass's loads)
+        int mat, i, j0;
+        if (e < 512) {                         // rows 32-63, 8 pieces per row
+            mat = e >= 256 ? 1 : 0;
+            const int pp = e - 256 * mat;
+            i = 32 + (pp >> 3);
+            j0 = 8 * (pp & 7);
+        } else {                               // rows 0-31, columns 0-31
+            mat = e >= 640 ? 1 : 0;
+            const int pp = e - 512 - 128 * mat;
+            i = pp >> 2;
+            j0 = 8 * (pp & 3);
+        }
         const float *sc = mat ? sBeta : sBeg;
         const float sgn = mat ? 1.f : -1.f;    // T_w is stored negated
         const f32x4 t0 = *reinterpret_cast<const f32x4 *>(sT + i * P_LD_A + j0);
@@ -403,7 +400,7 @@ chunk_prep_kernel(const bf16 *__restrict__ k, const float *__restrict__ g,
 
 // ---------------------------------------------------------------------------
 // chunk_chain: the sequential pass. One workgroup of 8 waves per (32-wide d_v
-// tile, head, sequence), two LDS barriers per chunk.
+// tile, head, sequence), one LDS barrier per chunk.
 //
 // Waves 0 and 1 carry the recurrence, each for 16 of the tile's d_v columns:
 // the wave keeps its slice of S^T (128 x 16, fp32) in eight 16x16 MFMA
@@ -413,21 +410,24 @@ chunk_prep_kernel(const bf16 *__restrict__ k, const float *__restrict__ g,
 //   S^T  <- e^{gamma_63} S^T + K^T Delta~,  Delta~_j = e^{gamma_63 - gamma_j} Delta_j
 //                                       (B operand: Delta~'s accumulators)
 // entirely in registers: an accumulator pair holds rows 4 (lane/16) + r of
-// two consecutive 16-row tiles, which is a B operand over that row order, and
-// the matching A operand is read from LDS in the same order (frag16_acc) or
-// transposed on the fly (tr4). Grouping T_w K S^T as T_w (K S^T) means W =
-// T_w K is never formed.
-// Waves 2 and 3 form the output, O^T = (S Q^T) diag(e^gamma) + Delta^T P^T,
-// for the same column halves; waves 6 and 7 form
-// P = lower_incl_diag(Q K^T * Gamma) (as P^T tiles, stored row-major);
-// waves 4 and 5 copy the previous chunk's output rows to HBM.
+// two 16-row tiles, which is a B operand over that row order, and the A
+// operands are read in the matching order (K rows for X chosen per lane,
+// K^T for the update transposed on read). Grouping T_w K S^T as T_w (K S^T)
+// means W = T_w K is never formed.
+// Waves 2 and 3 form the output for the same column halves,
+// O^T = (S Q^T) diag(e^gamma) + Delta^T P^T, the second term one chunk later;
+// waves 4-7 form P = lower_incl_diag(Q K^T * Gamma), one query row of 16x16
+// tiles each. Waves 2-7 also stage the next chunk.
 //
-//   phase A  waves 0-1: the recurrence step of chunk c (Delta^T and the new
-//            S as bf16 into LDS); waves 2-3: S Q^T; waves 6-7: P
-//   phase B  waves 2-3: + Delta^T P^T -> output staging; the other waves store
-//            chunk c+1 (loaded into registers one chunk earlier) into LDS and
-//            issue the loads of chunk c+2
-//
+// Iteration c (buffers b = c % 2):
+//   waves 0-1  recurrence step of chunk c: reads staging b, writes Delta^T
+//              into copy b and the new bf16 S into copy (c + 1) % 2
+//   waves 2-3  S Q^T of chunk c (S copy b, staging b); finish chunk c - 1
+//              (Delta^T and P copies (c - 1) % 2) and store its output rows
+//   waves 4-7  P of chunk c into copy b
+//   waves 2-7  store chunk c + 1 (in registers since iteration c - 2) into
+//              staging (c + 1) % 2, load chunk c + 3 into the registers
+//   barrier
 // Tokens past the end of a sequence are identity steps (q = k = v = 0,
 // g = 0, and T_w, T_u vanish on them) and their outputs are not stored.
 // ---------------------------------------------------------------------------
@@ -439,18 +439,17 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                    int nslots, float scale)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    bf16 *sQ = reinterpret_cast<bf16 *>(smem + OFF_Q);
-    bf16 *sK = reinterpret_cast<bf16 *>(smem + OFF_K);
-    bf16 *sV = reinterpret_cast<bf16 *>(smem + OFF_V);
-    bf16 *sTw = reinterpret_cast<bf16 *>(smem + OFF_TW);     // -T_w
-    bf16 *sTu = reinterpret_cast<bf16 *>(smem + OFF_TU);
-    bf16 *sP = reinterpret_cast<bf16 *>(smem + OFF_P);
-    bf16 *sS = reinterpret_cast<bf16 *>(smem + OFF_S);       // [2][DVT][LD_R]
-    bf16 *sDt = reinterpret_cast<bf16 *>(smem + OFF_DT);
-    bf16 *sO = reinterpret_cast<bf16 *>(smem + OFF_O);
-    float *sGam = reinterpret_cast<float *>(smem + OFF_SC);
-    float *sEg = sGam + C;
-    float *sDend = sEg + C;
+    bf16 *lds = reinterpret_cast<bf16 *>(smem);
+    // tiles of staging buffer b, and copies b of the tiles passed between waves
+    auto stQ = [&](int b) { return lds + (OFF_BUF + b * SZ_BUF + B_Q) / 2; };
+    auto stK = [&](int b) { return lds + (OFF_BUF + b * SZ_BUF + B_K) / 2; };
+    auto stV = [&](int b) { return lds + (OFF_BUF + b * SZ_BUF + B_V) / 2; };
+    auto stTH = [&](int b) { return lds + (OFF_BUF + b * SZ_BUF + B_TH) / 2; };   // [64][LD_H]
+    auto stTL = [&](int b) { return lds + (OFF_BUF + b * SZ_BUF + B_TL) / 2; };   // [64][LD_L]
+    auto stSc = [&](int b) { return reinterpret_cast<float *>(smem + OFF_BUF + b * SZ_BUF + B_SC); };
+    auto cpP = [&](int b) { return lds + (OFF_P + b * SZ_P) / 2; };
+    auto cpS = [&](int b) { return lds + (OFF_S + b * SZ_S) / 2; };
+    auto cpDt = [&](int b) { return lds + (OFF_DT + b * SZ_DT) / 2; };
 
     const int tid0 = (int)threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
@@ -471,6 +470,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const int nchunks = (len + C - 1) / C;
     const bf16 *wsh = ws + ((size_t)h * nslots + (size_t)((bos >> 6) + n)) * TWU_ELEMS;
     const size_t sbase = ((size_t)n * H + h) * DV * DK;
+    const int lane0 = tid0 & 63;
 
     // ---- state: wave hv < 2 holds Sacc[d][r] = S[cbase + 16 hv + lane%16][dk(d, lane/16, r)]
     //      with dk(d, q, r) = 32 (d/2) + 8 q + 4 (d%2) + r: accumulator pair (2s, 2s+1)
@@ -480,7 +480,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
     for (int d = 0; d < 8; ++d) Sacc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (wave < 2) {
-        const int lane = tid0 & 63, m = lane & 15, qq = lane >> 4;
+        const int m = lane0 & 15, qq = lane0 >> 4;
         const int col = cbase + 16 * wave + m;
         if (s_init) {
 #pragma unroll
@@ -492,331 +492,364 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
         for (int d = 0; d < 8; ++d) {
             bf16x4 x = {(bf16)Sacc[d][0], (bf16)Sacc[d][1], (bf16)Sacc[d][2], (bf16)Sacc[d][3]};
-            *reinterpret_cast<bf16x4 *>(sS + (16 * wave + m) * LD_R + ((32 * (d >> 1) + 8 * qq + 4 * (d & 1)) ^ swz(lane))) = x;
+            *reinterpret_cast<bf16x4 *>(cpS(0) + (16 * wave + m) * LD_R + ((32 * (d >> 1) + 8 * qq + 4 * (d & 1)) ^ swz(lane0))) = x;
         }
     }
+    // P's 16 x 16 tiles (0, 1) and (2, 3) lie above the diagonal but inside the
+    // 32-key k-steps of the output product: both copies zeroed once, never
+    // written again. (The upper-right 32 x 32 blocks of T_w and T_u are never read.)
+    for (int e = tid0; e < 2 * SZ_P / 16; e += NT) reinterpret_cast<bf16x8 *>(cpP(0))[e] = bf16x8{};
 
-    // ---- loads of one chunk into registers, by waves 2-7 (loader index
-    //      lt = tid - 128 in [0, 384)); each issues eight 16-byte loads p + r * stride:
-    //        lt in [0, 128)    Q rows row0 + 8 r, columns 8 (lt % 16) ..
-    //        lt in [128, 256)  K rows, the same pattern
-    //        lt in [256, 288)  V rows vrow0 + 8 r, 8 columns of this d_v tile
-    //        lt in [288, 384)  pieces e0 + 96 r of -T_w | T_u
-    //      and every loader loads g. Rows past the end of the sequence are read from
-    //      its last token and zeroed when stored (straight-line loads: a
-    //      data-dependent branch around them makes the compiler wait for them
-    //      at the join). ----
-    const int tid = tid0;
-    const int tstride = H * DK;
-    const bool loader = wave >= 2;
-    const int lt = tid - 128;
-    const int role = lt < 128 ? 0 : lt < 256 ? 1 : lt < 288 ? 2 : 3;
-    const int qk = lt & 127;
-    const int row0 = role <= 1 ? (qk >> 4) : ((lt - 256) >> 2);
-    const int lcol = role <= 1 ? 8 * (qk & 15) : 8 * ((lt - 256) & 3);
-    const int tt_e0 = lt - 288;
-    const bf16 *qbase = q + (size_t)bos * tstride + (size_t)h * DK;
-    const bf16 *kbase = k + (size_t)bos * tstride + (size_t)h * DK;
-    const bf16 *vbase = v + (size_t)bos * tstride + (size_t)h * DV + cbase;
-    bf16x8 rb[8];
-    float rg = 0.f;
-    bool rg_ok = true;
-    unsigned rvalid = 0xFF;
-    auto fetch = [&](int ch) {
-        const int base = ch * C;
-        const int lane = tid & 63;
-        if (role == 3) {
-            const bf16 *src = wsh + (size_t)ch * TWU_ELEMS + 8 * tt_e0;
-#pragma unroll
-            for (int r = 0; r < 8; ++r) rb[r] = *reinterpret_cast<const bf16x8 *>(src + r * 8 * 96);
-            rvalid = 0xFF;
-        } else {
-            const bf16 *src = (role == 0 ? qbase : role == 1 ? kbase : vbase) + (size_t)base * tstride + lcol;
-            rvalid = 0;
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int t = row0 + 8 * r;
-                const bool ok = base + t < len;
-                rvalid |= (ok ? 1u : 0u) << r;
-                rb[r] = *reinterpret_cast<const bf16x8 *>(src + (size_t)(ok ? t : len - 1 - base) * tstride);
-            }
-        }
-        // every loader loads g (only wave 7 uses it): a load under a wave-dependent
-        // branch would again make the compiler wait for it at the join
-        rg_ok = base + lane < len;
-        rg = g[((size_t)bos + base + (rg_ok ? lane : len - 1 - base)) * H + h];
+    // ---- loads of one chunk into registers, by waves 2-7, eight 16-byte buffer
+    //      loads per lane (address pattern A for r < 4, B for r >= 4, plus
+    //      per-load constants):
+    //        waves 2-3  Q rows 32 (w-2) + lane/16 + 4 r, columns 8 (lane%16) ..
+    //        waves 4-5  K rows, the same
+    //        wave 6     V rows lane/4 + 16 r (r < 4), 8 columns of this tile;
+    //                   workspace pieces 64 (r-4) + lane (r >= 4)
+    //        wave 7     workspace pieces 256 + 64 r + lane, and g of token lane
+    //      A buffer resource per chunk spans the chunk's tokens inside the
+    //      sequence only: loads past its end read as zero, which turns tokens
+    //      past the end into identity steps with no clamping or masking.
+    //      Workspace piece order (8 bf16 each): 0..255 rows 32-63 of -T_w (8
+    //      per row), 256..511 rows 32-63 of T_u, 512..639 rows 0-31 of -T_w (4
+    //      per row: columns 0-31), 640..767 rows 0-31 of T_u. ----
+    const int tstride = H * DK;                // elements between tokens
+    const int lrole = wave <= 3 ? 0 : wave <= 5 ? 1 : wave;    // 0 Q, 1 K, 6, 7
+    const int half = (wave - 2) & 1;                          // Q/K: rows 32 half ..
+    const int qkrow = 32 * half + (lane0 >> 4), qkcol = 8 * (lane0 & 15);
+    int goffA, goffB;
+    if (lrole <= 1) {
+        goffA = goffB = 2 * (qkrow * tstride + qkcol);
+    } else if (lrole == 6) {
+        goffA = 2 * ((lane0 >> 2) * tstride + 8 * (lane0 & 3));
+        goffB = 16 * lane0;
+    } else {
+        goffA = goffB = 16 * lane0;
+    }
+    auto gconst = [&](int r) -> int {
+        if (lrole <= 1) return r * 4 * tstride * 2;
+        if (lrole == 6) return r < 4 ? r * 16 * tstride * 2 : (r - 4) * 1024;
+        return r < 4 ? 4096 + r * 1024 : 8192 + (r - 4) * 1024;
     };
-    auto store = [&]() {
-        if (rvalid != 0xFF) {
-            const bf16x8 z8 = {};
+    // LDS element offset of load r within a staging buffer
+    auto loff = [&](int r) -> int {
+        if (lrole <= 1) return (lrole == 0 ? B_Q : B_K) / 2 + (qkrow + 4 * r) * LD_R + qkcol;
+        if (lrole == 6)
+            return r < 4 ? B_V / 2 + ((lane0 >> 2) + 16 * r) * LD_H + 8 * (lane0 & 3)
+                         : B_TL / 2 + ((lane0 >> 3) + 8 * (r - 4)) * LD_L + 8 * (lane0 & 7);
+        return r < 4 ? B_TL / 2 + (32 + (lane0 >> 3) + 8 * r) * LD_L + 8 * (lane0 & 7)
+                     : B_TH / 2 + ((lane0 >> 2) + 16 * (r - 4)) * LD_H + 8 * (lane0 & 3);
+    };
+    const bf16 *qkv_head[3] = {q + (size_t)bos * tstride + (size_t)h * DK,
+                               k + (size_t)bos * tstride + (size_t)h * DK,
+                               v + (size_t)bos * tstride + (size_t)h * DV + cbase};
+    const float *g_head = g + (size_t)bos * H + h;
+    // Two register sets: chunk c is loaded into set c % 2 three iterations
+    // before its use and stored to LDS one iteration before.
+    struct Pref {
+        bf16x8 b[8];
+        float g;
+    };
+    Pref pA, pB;
+    // WG: whether this wave loads and scans g (wave 7 only; a compile-time
+    // flag, so that no loop holds a load it may not need)
+    auto fetch = [&](int ch, Pref &rs, auto WG) {
+        const int base = ch * C;
+        const int nrow = len - base < C ? len - base : C;      // tokens of the chunk in the sequence
+        const bf16 *pa = lrole <= 1 ? qkv_head[lrole] + (size_t)base * tstride
+                       : lrole == 6 ? qkv_head[2] + (size_t)base * tstride
+                                    : wsh + (size_t)ch * TWU_ELEMS;
+        const unsigned na = lrole == 7 ? (unsigned)(TWU_ELEMS * 2) : (unsigned)nrow * tstride * 2;
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void *)pa, 0, na, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rw =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(wsh + (size_t)ch * TWU_ELEMS), 0, TWU_ELEMS * 2, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rbq = lrole == 6 ? rw : ra;
 #pragma unroll
-            for (int r = 0; r < 8; ++r) rb[r] = (rvalid >> r) & 1 ? rb[r] : z8;
+        for (int r = 0; r < 8; ++r)
+            rs.b[r] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                          r < 4 ? ra : rbq, r < 4 ? goffA : goffB, gconst(r), 0));
+        if constexpr (decltype(WG)::value) {
+            const __amdgpu_buffer_rsrc_t rgs = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(g_head + (size_t)base * H), 0, (unsigned)nrow * H * 4, 0x00020000);
+            rs.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rgs, 4 * H * lane0, 0, 0));
         }
-        if (role <= 1) {
-            bf16 *dst = (role == 0 ? sQ : sK) + row0 * LD_R + lcol;
+    };
+    auto store = [&](const Pref &rs, int b, auto WG) {
+        bf16 *buf = lds + (OFF_BUF + b * SZ_BUF) / 2;
 #pragma unroll
-            for (int r = 0; r < 8; ++r) *reinterpret_cast<bf16x8 *>(dst + 8 * r * LD_R) = rb[r];
-        } else if (role == 2) {
-            bf16 *dst = sV + row0 * LD_V + lcol;
-#pragma unroll
-            for (int r = 0; r < 8; ++r) *reinterpret_cast<bf16x8 *>(dst + 8 * r * LD_V) = rb[r];
-        } else {
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int e = tt_e0 + 96 * r;          // 0..767
-                const int mat = e >= 384 ? 1 : 0, rem = e - 384 * mat;
-                const int blk = rem >> 7, row = (rem >> 2) & 31, cc = rem & 3;
-                const int off = (32 * (blk > 0 ? 1 : 0) + row) * LD_64 + 32 * (blk == 2 ? 1 : 0) + 8 * cc;
-                *reinterpret_cast<bf16x8 *>((mat ? sTu : sTw) + off) = rb[r];
-            }
-        }
-        if (wave == 7) {
-            const int lane = tid & 63;
-            const float gam = wave_inclusive_scan(rg_ok ? rg : 0.f);
+        for (int r = 0; r < 8; ++r) *reinterpret_cast<bf16x8 *>(buf + loff(r)) = rs.b[r];
+        if constexpr (decltype(WG)::value) {
+            float *sc = stSc(b);
+            const float gam = wave_inclusive_scan(rs.g);
             const float glast = __builtin_bit_cast(
                 float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gam), 63));
-            sGam[lane] = gam;
-            sEg[lane] = __expf(gam);
-            sDend[lane] = __expf(glast - gam);
+            sc[lane0] = gam;
+            sc[C + lane0] = __expf(gam);
+            sc[2 * C + lane0] = __expf(glast - gam);
         }
     };
-    // P's 16 x 16 tiles (0, 1) and (2, 3) lie above the diagonal but inside the
-    // 32-key k-steps of the output product: zero once, never written again.
-    // (The upper-right 32 x 32 blocks of T_w and T_u are never read.)
-    for (int e = tid; e < C * LD_64 / 8; e += NT)
-        reinterpret_cast<bf16x8 *>(sP)[e] = bf16x8{};
-    if (nchunks > 0 && loader) {
-        fetch(0);
-        store();
-        fetch(nchunks > 1 ? 1 : 0);
-    }
-    lds_barrier();
+    const std::true_type with_g{};
+    const std::false_type no_g{};
 
-    // Each wave role runs its own loop with the same two barriers per chunk;
-    // the loaders' register prefetch is then straight-line code (every
-    // iteration loads, the last two re-read the last chunk), so the compiler
-    // never waits for it at the loop back-edge.
-    if (wave < 2) {
+    // Each wave role runs its own loop, unrolled by two from the odd chunk -3
+    // so that every buffer and register-set index is a compile-time constant:
+    // in iteration c = ch0 + hf, c % 2 = 1 - hf and (c + 1) % 2 = hf. Every
+    // role runs the same iterations (-3 .. nchunks or nchunks + 1) and one
+    // barrier per iteration; iterations -3 and -2 only load, -1 also stores
+    // chunk 0, and nchunks finishes the last output. The loaders' prefetch is
+    // one straight-line site per role (every iteration loads, clamped to the
+    // last chunk), so the compiler never waits for it at a join or the loop
+    // back-edge.
+    if (nchunks == 0) {
+        // nothing to do but the state copy below
+    } else if (wave < 2) {
         // ============ waves 0-1: the recurrence ============
         // the sequential path: these waves win instruction arbitration on their SIMDs
         __builtin_amdgcn_s_setprio(3);
         const int hv = wave;
-        for (int ch = 0; ch < nchunks; ++ch) {
+        for (int ch0 = -3; ch0 <= nchunks; ch0 += 2)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int ch = ch0 + hf;
+            const int b = 1 - hf;              // ch % 2
             int tidl = tid0;
             asm volatile("" : "+v"(tidl));  // keep lane-derived addresses out of loop-invariant hoisting
             const int lane = tidl & 63, m = lane & 15, qq = lane >> 4;
-            const int cur = ch & 1;
-            // U = T_u V and X = K S^T
-            f32x4 dacc[4], xacc[4];
+            if (ch >= 0 && ch < nchunks) {
+                const bf16 *sK = stK(b), *sV = stV(b), *sTH = stTH(b), *sTL = stTL(b);
+                // rows 16 t + m of -T_w (u = 0) or T_u (u = 1), columns 32 s + 8 q ..
+                auto tfrag = [&](int u, int t, int s2) {
+                    return t < 2 ? lds8(sTH, (32 * u + 16 * t + m) * LD_H + 8 * qq)
+                                 : lds8(sTL, (32 * u + 16 * (t - 2) + m) * LD_L + 32 * s2 + 8 * qq);
+                };
+                const float *sEg = stSc(b) + C, *sDend = stSc(b) + 2 * C;
+                // U = T_u V and X = K S^T
+                f32x4 dacc[4], xacc[4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) { dacc[t] = f32x4{0.f, 0.f, 0.f, 0.f}; xacc[t] = dacc[t]; }
-            {
-                // X tile t takes K rows 32 (t/2) + 8 (m/4) + 4 (t%2) + m%4, so that its
-                // accumulator pairs run over tokens 32 s + 8 q + 0..7 contiguously
-                bf16x8 fk[4][4];
+                for (int t = 0; t < 4; ++t) { dacc[t] = f32x4{0.f, 0.f, 0.f, 0.f}; xacc[t] = dacc[t]; }
+                {
+                    // X tile t takes K rows 32 (t/2) + 8 (m/4) + 4 (t%2) + m%4, so that its
+                    // accumulator pairs run over tokens 32 s + 8 q + 0..7 contiguously
+                    bf16x8 fk[4][4];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int row = 32 * (t >> 1) + 8 * (m >> 2) + 4 * (t & 1) + (m & 3);
+                    for (int t = 0; t < 4; ++t) {
+                        const int row = 32 * (t >> 1) + 8 * (m >> 2) + 4 * (t & 1) + (m & 3);
 #pragma unroll
-                    for (int s2 = 0; s2 < 4; ++s2) fk[t][s2] = frag16_row(sK, LD_R, row, 32 * s2, lane);
+                        for (int s2 = 0; s2 < 4; ++s2) fk[t][s2] = lds8(sK, row * LD_R + 32 * s2 + 8 * qq);
+                    }
+                    // V as B operand: tokens 32 s + 8 q + 0..7 of column 16 hv + m
+                    bf16x8 fv[2], fu[4][2];
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        const int off = (32 * s2 + 8 * qq + (m >> 2)) * LD_H + 16 * hv + 4 * (m & 3);
+                        fv[s2] = cat4(tr4(sV, off), tr4(sV, off + 4 * LD_H));
+                    }
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+#pragma unroll
+                        for (int s2 = 0; s2 < 2; ++s2)
+                            if (s2 <= (t >> 1)) fu[t][s2] = tfrag(1, t, s2);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) xacc[t] = mfma16(fk[t][s2], Sb[s2], xacc[t]);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+#pragma unroll
+                        for (int s2 = 0; s2 < 2; ++s2)
+                            if (s2 <= (t >> 1)) dacc[t] = mfma16(fu[t][s2], fv[s2], dacc[t]);
                 }
-                bf16x8 fv[2], fu[4][2];
+                // Delta = U + (-T_w) X
+                {
+                    bf16x8 fw[4][2];
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2)
-                    fv[s2] = cat4(tr4(sV, LD_V, 32 * s2 + 8 * qq, 16 * hv, lane),
-                                  tr4(sV, LD_V, 32 * s2 + 8 * qq + 4, 16 * hv, lane));
+                    for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
+                        for (int s2 = 0; s2 < 2; ++s2)
+                            if (s2 <= (t >> 1)) fw[t][s2] = tfrag(0, t, s2);
+                    const bf16x8 xb0 = acc_pair_bf16(xacc[0], xacc[1]);
+                    const bf16x8 xb1 = acc_pair_bf16(xacc[2], xacc[3]);
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2)
-                        if (s2 <= (t >> 1)) fu[t][s2] = frag16(sTu, LD_64, 16 * t, 32 * s2, lane);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int s2 = 0; s2 < 4; ++s2)
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) xacc[t] = mfma16(fk[t][s2], Sb[s2], xacc[t]);
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-#pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2)
-                        if (s2 <= (t >> 1)) dacc[t] = mfma16(fu[t][s2], fv[s2], dacc[t]);
-            }
-            // Delta = U + (-T_w) X
-            {
-                bf16x8 fw[4][2];
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-#pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2)
-                        if (s2 <= (t >> 1)) fw[t][s2] = frag16(sTw, LD_64, 16 * t, 32 * s2, lane);
-                const bf16x8 xb0 = acc_pair_bf16(xacc[0], xacc[1]);
-                const bf16x8 xb1 = acc_pair_bf16(xacc[2], xacc[3]);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    dacc[t] = mfma16(fw[t][0], xb0, dacc[t]);
-                    if (t >= 2) dacc[t] = mfma16(fw[t][1], xb1, dacc[t]);
+                    for (int t = 0; t < 4; ++t) {
+                        dacc[t] = mfma16(fw[t][0], xb0, dacc[t]);
+                        if (t >= 2) dacc[t] = mfma16(fw[t][1], xb1, dacc[t]);
+                    }
                 }
-            }
-            // Delta^T -> LDS (output term); Delta~ as the B operand of the update
-            bf16x8 db[2];
-            {
-                f32x4 dend[4];
+                // Delta^T -> LDS (output term); Delta~ as the B operand of the update
+                bf16x8 db[2];
+                {
+                    bf16 *sDt = cpDt(b);
+                    f32x4 dend[4];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    dend[t] = *reinterpret_cast<const f32x4 *>(sDend + 16 * t + 4 * qq);
-                    bf16x4 x = {(bf16)dacc[t][0], (bf16)dacc[t][1], (bf16)dacc[t][2], (bf16)dacc[t][3]};
-                    *reinterpret_cast<bf16x4 *>(sDt + (16 * hv + m) * LD_64 + ((16 * t + 4 * qq) ^ swz(lane))) = x;
+                    for (int t = 0; t < 4; ++t) {
+                        dend[t] = *reinterpret_cast<const f32x4 *>(sDend + 16 * t + 4 * qq);
+                        bf16x4 x = {(bf16)dacc[t][0], (bf16)dacc[t][1], (bf16)dacc[t][2], (bf16)dacc[t][3]};
+                        *reinterpret_cast<bf16x4 *>(sDt + (16 * hv + m) * LD_L + ((16 * t + 4 * qq) ^ swz(lane))) = x;
+                    }
+                    db[0] = acc_pair_bf16(dacc[0] * dend[0], dacc[1] * dend[1]);
+                    db[1] = acc_pair_bf16(dacc[2] * dend[2], dacc[3] * dend[3]);
                 }
-                db[0] = acc_pair_bf16(dacc[0] * dend[0], dacc[1] * dend[1]);
-                db[1] = acc_pair_bf16(dacc[2] * dend[2], dacc[3] * dend[3]);
-            }
-            // S^T <- e^{gamma_63} S^T + K^T Delta~ (A operand: K transposed on read)
-            {
-                const float eend = sEg[C - 1];
-                bf16x8 fkt[8][2];
+                // S^T <- e^{gamma_63} S^T + K^T Delta~. A operand of tile d: lane m
+                // takes d_k column 32 (d/2) + 8 (m/4) + 4 (d%2) + m%4 (the state's
+                // row order) and tokens 32 s + 4 q + 0..3, 32 s + 16 + 4 q + 0..3
+                // (Delta~'s row order), transposed on read
+                {
+                    const float eend = sEg[C - 1];
+                    bf16x8 fkt[8][2];
 #pragma unroll
-                for (int d = 0; d < 8; ++d)
+                    for (int d = 0; d < 8; ++d)
 #pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2)
-                        fkt[d][s2] = cat4(tr4s(sK, LD_R, 32 * s2 + 4 * qq, 32 * (d >> 1) + 4 * (d & 1), 8, lane),
-                                          tr4s(sK, LD_R, 32 * s2 + 16 + 4 * qq, 32 * (d >> 1) + 4 * (d & 1), 8, lane));
-                __builtin_amdgcn_sched_barrier(0);
+                        for (int s2 = 0; s2 < 2; ++s2) {
+                            const int c0 = 32 * (d >> 1) + 4 * (d & 1) + 8 * (m & 3);
+                            const int r0 = 32 * s2 + 4 * qq + (m >> 2);
+                            fkt[d][s2] = cat4(tr4(sK, r0 * LD_R + c0), tr4(sK, (r0 + 16) * LD_R + c0));
+                        }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int d = 0; d < 8; ++d) {
+                        Sacc[d] = Sacc[d] * eend;
+                        Sacc[d] = mfma16(fkt[d][0], db[0], Sacc[d]);
+                        Sacc[d] = mfma16(fkt[d][1], db[1], Sacc[d]);
+                    }
+                }
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) Sb[s2] = acc_pair_bf16(Sacc[2 * s2], Sacc[2 * s2 + 1]);
+                bf16 *sSn = cpS(hf);           // (ch + 1) % 2
 #pragma unroll
                 for (int d = 0; d < 8; ++d) {
-                    Sacc[d] = Sacc[d] * eend;
-                    Sacc[d] = mfma16(fkt[d][0], db[0], Sacc[d]);
-                    Sacc[d] = mfma16(fkt[d][1], db[1], Sacc[d]);
+                    bf16x4 x = {(bf16)Sacc[d][0], (bf16)Sacc[d][1], (bf16)Sacc[d][2], (bf16)Sacc[d][3]};
+                    *reinterpret_cast<bf16x4 *>(sSn + (16 * hv + m) * LD_R + ((32 * (d >> 1) + 8 * qq + 4 * (d & 1)) ^ swz(lane))) = x;
                 }
             }
-#pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2) Sb[s2] = acc_pair_bf16(Sacc[2 * s2], Sacc[2 * s2 + 1]);
-            bf16 *sSn = sS + (cur ^ 1) * DVT * LD_R;
-#pragma unroll
-            for (int d = 0; d < 8; ++d) {
-                bf16x4 x = {(bf16)Sacc[d][0], (bf16)Sacc[d][1], (bf16)Sacc[d][2], (bf16)Sacc[d][3]};
-                *reinterpret_cast<bf16x4 *>(sSn + (16 * hv + m) * LD_R + ((32 * (d >> 1) + 8 * qq + 4 * (d & 1)) ^ swz(lane))) = x;
-            }
-            lds_barrier();
             lds_barrier();
         }
     } else if (wave < 4) {
-        // ============ waves 2-3: the output for d_v rows 16 hv .. ============
+        // ============ waves 2-3: the output for d_v rows 16 hv .., then loads ============
         const int hv = wave - 2;
-        f32x4 oacc[4];
-        for (int ch = 0; ch < nchunks; ++ch) {
+        f32x4 oacc[2][4];                  // by chunk parity: O^T tiles (16 d_v x 16 tokens)
+        for (int ch0 = -3; ch0 <= nchunks; ch0 += 2)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int ch = ch0 + hf;
+            const int b = 1 - hf;              // ch % 2; (ch + 1) % 2 = (ch - 1) % 2 = hf
+            Pref &ps = hf ? pB : pA;
             int tidl = tid0;
             asm volatile("" : "+v"(tidl));
             const int lane = tidl & 63, m = lane & 15, qq = lane >> 4;
-            const int cur = ch & 1;
-            // (Q S^T)^T = S Q^T, all 64 tokens, then e^gamma per token
-            {
-                const bf16 *sSc = sS + cur * DVT * LD_R;
+            if (ch >= 0 && ch < nchunks) {
+                // (Q S^T)^T = S Q^T, all 64 tokens, then e^gamma per token
+                const bf16 *sSc = cpS(b), *sQ = stQ(b);
+                const float *sEg = stSc(b) + C;
                 bf16x8 fs[4], fq[4][4];
 #pragma unroll
                 for (int s2 = 0; s2 < 4; ++s2) {
-                    fs[s2] = frag16_sw(sSc, LD_R, 16 * hv, 32 * s2, lane);
+                    fs[s2] = lds8(sSc, (16 * hv + m) * LD_R + ((32 * s2 + 8 * qq) ^ swz(lane)));
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) fq[t][s2] = frag16(sQ, LD_R, 16 * t, 32 * s2, lane);
+                    for (int t = 0; t < 4; ++t) fq[t][s2] = lds8(sQ, (16 * t + m) * LD_R + 32 * s2 + 8 * qq);
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int t = 0; t < 4; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int t = 0; t < 4; ++t) oacc[b][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s2 = 0; s2 < 4; ++s2)
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) oacc[t] = mfma16(fs[s2], fq[t][s2], oacc[t]);
+                    for (int t = 0; t < 4; ++t) oacc[b][t] = mfma16(fs[s2], fq[t][s2], oacc[b][t]);
 #pragma unroll
-                for (int t = 0; t < 4; ++t) oacc[t] = oacc[t] * sEg[16 * t + m];
+                for (int t = 0; t < 4; ++t) oacc[b][t] = oacc[b][t] * sEg[16 * t + m];
             }
-            lds_barrier();
-            // O^T += Delta^T P^T; token tile t needs keys 0 .. 16 t + 15
-            {
+            if (ch >= 1 && ch <= nchunks) {
+                // finish chunk ch - 1: O^T += Delta^T P^T (token tile t needs keys
+                // 0 .. 16 t + 15), then its rows to HBM
+                const int cp = ch - 1;
+                const bf16 *sDt = cpDt(hf), *sP = cpP(hf);
                 bf16x8 fd[2], fp[4][2];
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
-                    fd[s2] = frag16_sw(sDt, LD_64, 16 * hv, 32 * s2, lane);
+                    fd[s2] = lds8(sDt, (16 * hv + m) * LD_L + ((32 * s2 + 8 * qq) ^ swz(lane)));
 #pragma unroll
                     for (int t = 0; t < 4; ++t)
-                        if (s2 <= (t >> 1)) fp[t][s2] = frag16_sw(sP, LD_64, 16 * t, 32 * s2, lane);
+                        if (s2 <= (t >> 1))
+                            fp[t][s2] = t < 2 ? lds8(sP, (16 * t + m) * LD_H + ((8 * qq) ^ swz(lane)))
+                                              : lds8(sP + SZ_PH / 2, (16 * (t - 2) + m) * LD_L + ((32 * s2 + 8 * qq) ^ swz(lane)));
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
 #pragma unroll
                     for (int s2 = 0; s2 < 2; ++s2)
-                        if (s2 <= (t >> 1)) oacc[t] = mfma16(fd[s2], fp[t][s2], oacc[t]);
-                // oacc[t][r] = O[token 16 t + m][d_v 16 hv + 4 qq + r]
+                        if (s2 <= (t >> 1)) oacc[hf][t] = mfma16(fd[s2], fp[t][s2], oacc[hf][t]);
+                // oacc[t][r] = O[token 16 t + m][d_v 16 hv + 4 qq + r]: 8 bytes per lane
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    bf16x4 x = {(bf16)(scale * oacc[t][0]), (bf16)(scale * oacc[t][1]),
-                                (bf16)(scale * oacc[t][2]), (bf16)(scale * oacc[t][3])};
-                    *reinterpret_cast<bf16x4 *>(sO + (16 * t + m) * LD_O + 16 * hv + 4 * qq) = x;
+                    const int tok = cp * C + 16 * t + m;
+                    if (tok < len) {
+                        bf16x4 x = {(bf16)(scale * oacc[hf][t][0]), (bf16)(scale * oacc[hf][t][1]),
+                                    (bf16)(scale * oacc[hf][t][2]), (bf16)(scale * oacc[hf][t][3])};
+                        *reinterpret_cast<bf16x4 *>(o + ((size_t)bos + tok) * H * DV + (size_t)h * DV + cbase + 16 * hv + 4 * qq) = x;
+                    }
                 }
             }
-            if (ch + 1 < nchunks) store();     // chunk ch + 1
-            fetch(ch + 2 < nchunks ? ch + 2 : nchunks - 1);
+            if (ch + 1 >= 0 && ch + 1 < nchunks) store(ps, hf, no_g);   // chunk ch + 1
+            fetch(ch + 3 < nchunks ? ch + 3 : nchunks - 1, ps, no_g);
             lds_barrier();
         }
     } else {
-        // ============ waves 4-7: P (one query row each; wave 5 also moves the
-        //              previous chunk's output rows to HBM), then loads ============
-        // a chunk's output rows (64 x 32 bf16) from the staging buffer to HBM
-        auto ostore = [&](int chp) {
-            const int e = (int)threadIdx.x & 63;        // one wave: 256 16-byte pieces
+        // ============ waves 4-7: P (one query row each), then loads ============
+        auto ploop = [&](auto WG) {
+            for (int ch0 = -3; ch0 <= nchunks; ch0 += 2)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int piece = e + 64 * u, row = piece >> 2, col = 8 * (piece & 3);
-                const int tok = chp * C + row;
-                if (tok < len)
-                    *reinterpret_cast<bf16x8 *>(o + ((size_t)bos + tok) * H * DV + (size_t)h * DV + cbase + col) =
-                        *reinterpret_cast<const bf16x8 *>(sO + row * LD_O + col);
+            for (int hf = 0; hf < 2; ++hf) {
+                const int ch = ch0 + hf;
+                const int b = 1 - hf;
+                Pref &ps = hf ? pB : pA;
+                int tidl = tid0;
+                asm volatile("" : "+v"(tidl));
+                const int lane = tidl & 63, m = lane & 15, qq = lane >> 4;
+                if (ch >= 0 && ch < nchunks) {
+                    // P^T tiles (keys 16 J.., queries 16 I..) for J <= I, one query row
+                    // I per wave: I = 3 (wave 6), 2 (wave 7), 1 (wave 4), 0 (wave 5);
+                    // the row's Q fragments are loaded once
+                    const bf16 *sQ = stQ(b), *sK = stK(b);
+                    const float *sGam = stSc(b);
+                    bf16 *sP = cpP(b);
+                    const int I = wave == 6 ? 3 : wave == 7 ? 2 : wave == 4 ? 1 : 0;
+                    bf16x8 fq[4];
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2) fq[s2] = lds8(sQ, (16 * I + m) * LD_R + 32 * s2 + 8 * qq);
+                    const int i = 16 * I + m;
+                    const float gi = sGam[i];
+                    for (int J = 0; J <= I; ++J) {
+                        bf16x8 fk[4];
+#pragma unroll
+                        for (int s2 = 0; s2 < 4; ++s2) fk[s2] = lds8(sK, (16 * J + m) * LD_R + 32 * s2 + 8 * qq);
+                        __builtin_amdgcn_sched_barrier(0);
+                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int s2 = 0; s2 < 4; ++s2) acc = mfma16(fk[s2], fq[s2], acc);
+                        // acc[r] = q_i . k_j with i = 16 I + m, j = 16 J + 4 qq + r
+                        const int j0 = 16 * J + 4 * qq;
+                        const f32x4 gj = *reinterpret_cast<const f32x4 *>(sGam + j0);
+                        bf16x4 x;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            x[r] = (bf16)(j0 + r <= i ? acc[r] * __expf(gi - gj[r]) : 0.f);
+                        bf16 *dst = I < 2 ? sP + i * LD_H : sP + SZ_PH / 2 + (i - 32) * LD_L;
+                        *reinterpret_cast<bf16x4 *>(dst + (j0 ^ swz(lane))) = x;
+                    }
+                }
+                if (ch + 1 >= 0 && ch + 1 < nchunks) store(ps, hf, WG);   // chunk ch + 1
+                fetch(ch + 3 < nchunks ? ch + 3 : nchunks - 1, ps, WG);
+                lds_barrier();
             }
         };
-        for (int ch = 0; ch < nchunks; ++ch) {
-            int tidl = tid0;
-            asm volatile("" : "+v"(tidl));
-            const int lane = tidl & 63, m = lane & 15, qq = lane >> 4;
-            {
-                // P^T tiles (keys 16 J.., queries 16 I..) for J <= I, one query row
-                // I per wave: I = 3 (wave 6), 2 (wave 7), 1 (wave 4), 0 (wave 5);
-                // the row's Q fragments are loaded once
-                const int I = wave == 6 ? 3 : wave == 7 ? 2 : wave == 4 ? 1 : 0;
-                bf16x8 fq[4];
-#pragma unroll
-                for (int s2 = 0; s2 < 4; ++s2) fq[s2] = frag16(sQ, LD_R, 16 * I, 32 * s2, lane);
-                const int i = 16 * I + m;
-                const float gi = sGam[i];
-                for (int J = 0; J <= I; ++J) {
-                    bf16x8 fk[4];
-#pragma unroll
-                    for (int s2 = 0; s2 < 4; ++s2) fk[s2] = frag16(sK, LD_R, 16 * J, 32 * s2, lane);
-                    __builtin_amdgcn_sched_barrier(0);
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s2 = 0; s2 < 4; ++s2) acc = mfma16(fk[s2], fq[s2], acc);
-                    // acc[r] = q_i . k_j with i = 16 I + m, j = 16 J + 4 qq + r
-                    const int j0 = 16 * J + 4 * qq;
-                    const f32x4 gj = *reinterpret_cast<const f32x4 *>(sGam + j0);
-                    bf16x4 x;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        x[r] = (bf16)(j0 + r <= i ? acc[r] * __expf(gi - gj[r]) : 0.f);
-                    *reinterpret_cast<bf16x4 *>(sP + i * LD_64 + (j0 ^ swz(lane))) = x;
-                }
-            }
-            if (wave == 5 && ch > 0) {
-                ostore(ch - 1);
-            }
-            lds_barrier();
-            if (ch + 1 < nchunks) store();     // chunk ch + 1
-            fetch(ch + 2 < nchunks ? ch + 2 : nchunks - 1);
-            lds_barrier();
-        }
-        if (wave == 5 && nchunks > 0) ostore(nchunks - 1);  // the last chunk's output rows
+        if (wave == 7) ploop(with_g);
+        else ploop(no_g);
     }
     if (s_final && wave < 2) {
-        const int lane = tid0 & 63, m = lane & 15, qq = lane >> 4;
+        const int m = lane0 & 15, qq = lane0 >> 4;
         float *dst = s_final + sbase + (size_t)(cbase + 16 * wave + m) * DK + 8 * qq;
 #pragma unroll
         for (int d = 0; d < 8; ++d) *reinterpret_cast<f32x4 *>(dst + 32 * (d >> 1) + 4 * (d & 1)) = Sacc[d];
