@@ -809,19 +809,24 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                 asm volatile("" : "+v"(tidl));
                 const int lane = tidl & 63, m = lane & 15, qq = lane >> 4;
                 if (ch >= 0 && ch < nchunks) {
-                    // P^T tiles (keys 16 J.., queries 16 I..) for J <= I, one query row
-                    // I per wave: I = 3 (wave 6), 2 (wave 7), 1 (wave 4), 0 (wave 5);
-                    // the row's Q fragments are loaded once
+                    // P^T tiles (keys 16 J.., queries 16 I..) for J <= I, at most three
+                    // per wave: wave 6 (3, 0..2), wave 7 (2, 0..2), wave 4 (1, 0..1),
+                    // wave 5 (3, 3) and (0, 0); a query row's Q fragments are loaded once
                     const bf16 *sQ = stQ(b), *sK = stK(b);
                     const float *sGam = stSc(b);
                     bf16 *sP = cpP(b);
-                    const int I = wave == 6 ? 3 : wave == 7 ? 2 : wave == 4 ? 1 : 0;
+                    const int I0 = wave == 6 ? 3 : wave == 7 ? 2 : wave == 4 ? 1 : 3;
+                    const int ntile = wave == 6 || wave == 7 ? 3 : 2;
                     bf16x8 fq[4];
+                    for (int u = 0; u < ntile; ++u) {
+                        const int I = wave == 5 && u == 1 ? 0 : I0;
+                        const int J = wave == 5 ? I : u;
+                        if (u == 0 || I != I0) {
 #pragma unroll
-                    for (int s2 = 0; s2 < 4; ++s2) fq[s2] = lds8(sQ, (16 * I + m) * LD_R + 32 * s2 + 8 * qq);
-                    const int i = 16 * I + m;
-                    const float gi = sGam[i];
-                    for (int J = 0; J <= I; ++J) {
+                            for (int s2 = 0; s2 < 4; ++s2) fq[s2] = lds8(sQ, (16 * I + m) * LD_R + 32 * s2 + 8 * qq);
+                        }
+                        const int i = 16 * I + m;
+                        const float gi = sGam[i];
                         bf16x8 fk[4];
 #pragma unroll
                         for (int s2 = 0; s2 < 4; ++s2) fk[s2] = lds8(sK, (16 * J + m) * LD_R + 32 * s2 + 8 * qq);
