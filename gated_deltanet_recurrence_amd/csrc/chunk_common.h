@@ -163,5 +163,23 @@ __device__ __forceinline__ void transpose8x8(const bf16x8 (&in)[8], bf16x8 (&out
         for (int r = 0; r < 8; ++r) out[e][r] = in[r][e];
 }
 
+// Work mapping of the sequential chunk kernels: one workgroup per (sequence,
+// head) pair and 32-wide d_v tile, four tiles per pair. The dispatcher deals
+// workgroups to the eight XCDs in turn (workgroup w on XCD w % 8); the k-th
+// workgroup of an XCD takes tile k % 4 of pair 8 (k / 4) + w % 8. A pair's four
+// tiles then run side by side on one XCD and share its L2, while consecutive
+// pairs (the heads of one sequence, then the next sequence) go to different
+// XCDs, so a long sequence does not pile up on one of them. The grid is rounded
+// up to whole rounds of 32 workgroups; the surplus ones get false.
+constexpr int PAIR_TILES = 4;
+__host__ __device__ inline unsigned pair_grid(int npairs) { return (unsigned)((npairs + 7) / 8 * 8 * PAIR_TILES); }
+__device__ __forceinline__ bool pair_tile(int wid, int npairs, int &pair, int &tile)
+{
+    const int kx = wid >> 3;
+    pair = (kx / PAIR_TILES) * 8 + (wid & 7);
+    tile = kx % PAIR_TILES;
+    return pair < npairs;
+}
+
 }  // namespace chunk
 }  // namespace gdn

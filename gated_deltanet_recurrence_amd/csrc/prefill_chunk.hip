@@ -102,6 +102,7 @@ constexpr int OFF_S = OFF_P + SZ_P;
 constexpr int OFF_SC = OFF_S + SZ_S;
 constexpr int LDS_BYTES = OFF_SC + SZ_SC;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+static_assert(DV / DVT == PAIR_TILES, "one workgroup per d_v tile of a pair");
 static_assert(C * LD_QK * 2 <= SZ_A, "-W fits in the A region");
 static_assert(4 * 4 * 4 * 68 * 4 <= SZ_Y, "solve scratch fits");
 static_assert(2 * DVT * LD_T * 2 + C * LD_O * 2 <= SZ_Y, "chain buffers fit");
@@ -118,7 +119,7 @@ prefill_chunk_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                      const bf16 *__restrict__ v, const float *__restrict__ g,
                      const float *__restrict__ beta, const float *s_init, float *s_final,
                      bf16 *__restrict__ o, const int32_t *__restrict__ cu_seqlens, int T, int H,
-                     float scale)
+                     int npairs, float scale)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     bf16 *sQ = reinterpret_cast<bf16 *>(smem + OFF_Q);
@@ -145,15 +146,9 @@ prefill_chunk_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 
     const int tid0 = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);   // uniform: scalar branches
-    // work item of this workgroup: (sequence n, head h, d_v tile). Workgroup w
-    // runs on XCD w % 8; give each XCD a contiguous range of work items so the
-    // four tiles of a head share an L2.
-    int work = (int)blockIdx.x;
-    const int total = (int)gridDim.x;
-    if (total % (8 * (DV / DVT)) == 0) work = (work % 8) * (total / 8) + work / 8;
-    const int tile = work % (DV / DVT);
-    const int h = (work / (DV / DVT)) % H;
-    const int n = work / ((DV / DVT) * H);
+    int pair, tile;                            // (sequence, head) pair and d_v tile
+    if (!pair_tile((int)blockIdx.x, npairs, pair, tile)) return;   // uniform
+    const int h = pair % H, n = pair / H;
     const int cbase = tile * DVT;              // first d_v column of this tile
 
     long bos, eos;
@@ -571,10 +566,11 @@ hipError_t launch_prefill_chunk(const void *q, const void *k, const void *v, con
         if (e != hipSuccess) return e;
         attr_done = true;
     }
-    dim3 grid((unsigned)((DV / DVT) * H * N)), block(NT);
+    const int npairs = H * N;
+    dim3 grid(pair_grid(npairs)), block(NT);
     hipLaunchKernelGGL(prefill_chunk_kernel, grid, block, LDS_BYTES, stream, (const bf16 *)q,
                        (const bf16 *)k, (const bf16 *)v, g, beta, s_init, s_final, (bf16 *)o, cu,
-                       T, H, scale);
+                       T, H, npairs, scale);
     return hipGetLastError();
 }
 

@@ -104,6 +104,7 @@ constexpr int OFF_S = OFF_P + 2 * SZ_P;
 constexpr int OFF_DT = OFF_S + 2 * SZ_S;
 constexpr int LDS_BYTES = OFF_DT + 2 * SZ_DT;  // 160256
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+static_assert(DV / DVT == PAIR_TILES, "one workgroup per d_v tile of a pair");
 static_assert(SZ_BUF % 16 == 0 && SZ_P % 16 == 0, "16-byte aligned tiles");
 
 // Accumulator tiles are written 8 bytes per lane (row lane%16, columns
@@ -436,7 +437,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                    const bf16 *__restrict__ v, const float *__restrict__ g,
                    const bf16 *__restrict__ ws, const float *s_init, float *s_final,
                    bf16 *__restrict__ o, const int32_t *__restrict__ cu_seqlens, int T, int H,
-                   int nslots, float scale)
+                   int npairs, int nslots, float scale)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     bf16 *lds = reinterpret_cast<bf16 *>(smem);
@@ -453,15 +454,9 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 
     const int tid0 = (int)threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
-    // work item (sequence n, head h, d_v tile); workgroup w runs on XCD w % 8,
-    // so each XCD gets a contiguous range and the four tiles of a head share
-    // an L2
-    int work = (int)blockIdx.x;
-    const int total = (int)gridDim.x;
-    if (total % (8 * (DV / DVT)) == 0) work = (work % 8) * (total / 8) + work / 8;
-    const int tile = work % (DV / DVT);
-    const int h = (work / (DV / DVT)) % H;
-    const int n = work / ((DV / DVT) * H);
+    int pair, tile;                          // (sequence, head) pair and d_v tile
+    if (!pair_tile((int)blockIdx.x, npairs, pair, tile)) return;   // uniform
+    const int h = pair % H, n = pair / H;
     const int cbase = tile * DVT;
 
     long bos, eos;
@@ -895,10 +890,11 @@ hipError_t launch_prefill_apply(const void *q, const void *k, const void *v, con
     }
     const long tokens = cu ? (long)T : (long)N * T;
     const long nslots = tokens / C + N + 1;
-    dim3 grid((unsigned)((DV / DVT) * H * N)), block(NT);
+    const int npairs = H * N;
+    dim3 grid(pair_grid(npairs)), block(NT);
     hipLaunchKernelGGL(chunk_chain_kernel, grid, block, LDS_BYTES, stream, (const bf16 *)q,
                        (const bf16 *)k, (const bf16 *)v, g, (const bf16 *)ws, s_init, s_final,
-                       (bf16 *)o, cu, T, H, (int)nslots, scale);
+                       (bf16 *)o, cu, T, H, npairs, (int)nslots, scale);
     return hipGetLastError();
 }
 
