@@ -48,15 +48,17 @@ constexpr int DV = 128;
 constexpr int TWU_ELEMS = 2 * 3 * 32 * 32;    // bf16 per (chunk, head) in the workspace
 
 // ---------------------------------------------------------------------------
-// Pass 1: chunk_prep. One workgroup of 4 waves per (chunk slot, head).
+// Pass 1: chunk_prep. Workgroups of 4 waves, each looping over (chunk slot,
+// head) items.
 // ---------------------------------------------------------------------------
 constexpr int P_NT = 256;
 constexpr int P_LD_K = DK + 8;                 // bf16 row stride of K
-constexpr int P_LD_A = C + 4;                  // fp32 row stride of A and T
+constexpr int P_LD_A = C + 4;                  // fp32 row stride of T
+constexpr int P_LD_A2 = 52;                    // fp32 row stride of the off-diagonal part of A
 constexpr int P_QB = 4 * 68;                   // one 16 x 16 block in the quad layout (floats)
 constexpr int P_SZ_R1 = C * P_LD_K * 2;        // 17408: K, then T
-constexpr int P_SZ_A = C * P_LD_A * 4;         // 17408
-constexpr int P_SZ_Y = 2 * 4 * P_QB * 4;       // 8704: two diagonal 32 x 32 tiles, quad layout
+constexpr int P_SZ_A = 48 * P_LD_A2 * 4;       // 9984: rows 16-63, columns 0-47 of A
+constexpr int P_SZ_Y = 4 * P_QB * 4;           // 4352: the diagonal 16 x 16 blocks, quad layout
 constexpr int P_SZ_SC = 3 * C * 4;             // gamma, beta, beta e^gamma
 constexpr int P_OFF_R1 = 0;
 constexpr int P_OFF_A = P_OFF_R1 + P_SZ_R1;
@@ -64,7 +66,7 @@ constexpr int P_OFF_Y = P_OFF_A + P_SZ_A;
 constexpr int P_OFF_SC = P_OFF_Y + P_SZ_Y;
 constexpr int P_LDS_BYTES = P_OFF_SC + P_SZ_SC;
 static_assert(C * P_LD_A * 4 <= P_SZ_R1, "T fits where K was");
-static_assert(P_LDS_BYTES <= 48 * 1024, "three prep workgroups per CU");
+static_assert(P_LDS_BYTES <= 40 * 1024, "four prep workgroups per CU");
 
 // ---------------------------------------------------------------------------
 // Pass 2: chunk_chain. One workgroup of 8 waves per (32-wide d_v tile, head,
@@ -184,9 +186,12 @@ __device__ __forceinline__ f32x16 mma32s(f32x16 acc, const bf16 *a, int ld_a, in
 using namespace split;
 
 // ---------------------------------------------------------------------------
-// chunk_prep: T_w and T_u of one (chunk, head).
+// chunk_prep: T_w and T_u of (chunk, head) items. Item i is slot i / H of
+// head i % H; a workgroup takes items blockIdx.x, + gridDim.x, ... and loads
+// the next item's K, g and beta into registers while it works on the current
+// one, so that the HBM latency is paid once per workgroup.
 //
-//   load   K (64 x 128) into LDS; gamma = prefix sum of g (wave 0, DPP scan)
+//   stage  K (64 x 128) into LDS; gamma = prefix sum of g (wave 0, DPP scan)
 //   gram   wave 0: tile (0,0) of A, wave 1: tile (1,1), wave 2: tile (1,0)
 //          (v_mfma_f32_32x32x16_bf16, masked and scaled in registers)
 //   solve  wave w inverts the 16 x 16 diagonal block w of I - A by forward
@@ -196,7 +201,34 @@ using namespace split;
 //          inversion, (L^-1)_21 = L22^-1 A21 L11^-1 (fp32 16x16x4 MFMA)
 //   store  -T diag(beta e^gamma) and T diag(beta), bf16, to the workspace
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(P_NT)
+struct PrepItem {
+    int slot, h, nvalid;                       // nvalid = 0: nothing to do
+    long row0;                                 // first token of the chunk
+};
+__device__ __forceinline__ PrepItem prep_locate(const int32_t *cu, int item, int nitems, int T,
+                                                int H, int N) {
+    PrepItem it{0, 0, 0, 0};
+    if (item >= nitems) return it;
+    it.slot = item / H;
+    it.h = item - it.slot * H;
+    // sequence of the slot: the last n whose first slot is <= slot
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (first_slot(cu, mid, T) <= it.slot) lo = mid;
+        else hi = mid - 1;
+    }
+    long bos, eos;
+    seq_bounds(cu, lo, T, bos, eos);
+    const long c = it.slot - ((bos >> 6) + lo);
+    const long len = eos - bos;
+    if (c < 0 || c * C >= len) return it;      // unused slot
+    it.row0 = bos + c * C;
+    it.nvalid = (int)(len - c * C < C ? len - c * C : C);
+    return it;
+}
+
+__global__ void __launch_bounds__(P_NT, 4)
 chunk_prep_kernel(const bf16 *__restrict__ k, const float *__restrict__ g,
                   const float *__restrict__ beta, const int32_t *__restrict__ cu_seqlens,
                   bf16 *__restrict__ ws, int T, int H, int N, int nslots)
@@ -210,192 +242,221 @@ chunk_prep_kernel(const bf16 *__restrict__ k, const float *__restrict__ g,
     float *sBeta = sGam + C;
     float *sBeg = sBeta + C;
 
-    const int slot = (int)blockIdx.x, h = (int)blockIdx.y;
-    const int tid = (int)threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63;
+    const int tid0 = (int)threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
+    const int nitems = nslots * H;
+    const int stride = (int)gridDim.x;
+    const int tstride = H * DK;                // elements between consecutive tokens of K
 
-    // sequence of this slot: the last n whose first slot is <= slot
-    int lo = 0, hi = N - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (first_slot(cu_seqlens, mid, T) <= slot) lo = mid;
-        else hi = mid - 1;
-    }
-    const int n = lo;
-    long bos, eos;
-    seq_bounds(cu_seqlens, n, T, bos, eos);
-    const long c = slot - ((bos >> 6) + n);
-    const long len = eos - bos;
-    if (c < 0 || c * C >= len) return;         // unused slot (uniform)
-    const long row0 = bos + c * C;
-    const int nvalid = (int)(len - c * C < C ? len - c * C : C);
-
-    // ---- load K rows (zero past the end of the sequence), g and beta ----
-    {
-        const int col = 8 * (tid & 15);
+    // K rows (tid >> 4) + 16 u, columns 8 (tid & 15) ..; g and beta of token
+    // `lane` (wave 0). Buffer loads bounded by the chunk's valid tokens: rows
+    // past the end of the sequence (and every row of an empty item) read zero.
+    struct Pre {
+        bf16x8 kr[4];
+        float gv, bv;
+    };
+    auto fetch = [&](const PrepItem &it, Pre &p) {
+        const size_t tok0 = (size_t)it.row0;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(k + tok0 * tstride + (size_t)it.h * DK), 0, (unsigned)it.nvalid * tstride * 2, 0x00020000);
+        const unsigned off = (unsigned)(((tid0 >> 4) * tstride + 8 * (tid0 & 15)) * 2);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int r = (tid >> 4) + 16 * u;
-            bf16x8 x = {};
-            if (r < nvalid)
-                x = *reinterpret_cast<const bf16x8 *>(k + (size_t)(row0 + r) * H * DK + (size_t)h * DK + col);
-            *reinterpret_cast<bf16x8 *>(sK + r * P_LD_K + col) = x;
-        }
-    }
-    if (wave == 0) {
-        const bool ok = lane < nvalid;
-        const size_t t = (size_t)(row0 + lane) * H + h;
-        const float gv = ok ? g[t] : 0.f, bv = ok ? beta[t] : 0.f;
-        const float gam = wave_inclusive_scan(gv);
-        sGam[lane] = gam;
-        sBeta[lane] = bv;
-        sBeg[lane] = bv * __expf(gam);
-    }
-    lds_barrier();
-
-    const int l32 = lane & 31, lh = lane >> 5, lr = lane & 15, lq = lane >> 4;
-    auto rows4 = [&](const float *v, int i0, int qq) {
-        return *reinterpret_cast<const f32x4 *>(v + i0 + 8 * qq + 4 * lh);
+        for (int u = 0; u < 4; ++u)
+            p.kr[u] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                          rk, off, (unsigned)(16 * u * tstride * 2), 0));
+        const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(g + tok0 * H + it.h), 0, (unsigned)it.nvalid * H * 4, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(beta + tok0 * H + it.h), 0, (unsigned)it.nvalid * H * 4, 0x00020000);
+        p.gv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, 4 * H * (tid0 & 63), 0, 0));
+        p.bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, 4 * H * (tid0 & 63), 0, 0));
     };
 
-    // ---- gram tiles of A = -strict_lower(diag(beta) K K^T * Gamma) ----
-    if (wave < 3) {
-        const int ti = wave == 0 ? 0 : 1, tj = wave == 1 ? 1 : 0;
-        const int j = 32 * tj + l32;
-        const float gj = sGam[j];
-        f32x4 gi[4], bi[4];
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-            gi[qq] = rows4(sGam, 32 * ti, qq);
-            bi[qq] = rows4(sBeta, 32 * ti, qq);
-        }
-        f32x16 at = {};
-        at = mma32_2<4>(at, sK, P_LD_K, 32 * ti, sK, P_LD_K, 32 * tj, lane);
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
-#pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2) {
-                const int r = 4 * qq + s2, i = 32 * ti + acc_row(r, lane);
-                at[r] = j < i ? -bi[qq][s2] * at[r] * __expf(gi[qq][s2] - gj) : 0.f;
-            }
-        // whole tile into sA (only the off-diagonal 16 x 16 blocks are read there)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sA[(32 * ti + acc_row(r, lane)) * P_LD_A + j] = at[r];
-        if (wave < 2) {
-            // and the diagonal tile in the solve's quad layout: element (i, m) of
-            // 16 x 16 block b at b * P_QB + (m % 4) * 68 + 4 i + m / 4
-            float *ap = sY + wave * (4 * P_QB);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int it = acc_row(r, lane), jt = l32;
-                const int blk = 2 * (it >> 4) + (jt >> 4), i = it & 15, m = jt & 15;
-                ap[blk * P_QB + (m & 3) * 68 + i * 4 + (m >> 2)] = at[r];
-            }
-        }
-    }
-    lds_barrier();                             // A complete; K no longer read
-
-    // ---- diagonal blocks: D_w = (I - A_ww)^-1, D[i][j] = [i==j] + sum_{m<i} A[i][m] D[m][j]
-    {
-        const int jc = lane >> 2, p = lane & 3;
-        const float *myp = sY + (wave >> 1) * (4 * P_QB) + 3 * (wave & 1) * P_QB + p * 68;
-        f32x4 arow[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) arow[i] = *reinterpret_cast<const f32x4 *>(myp + 4 * i);
-        float xs[4] = {0.f, 0.f, 0.f, 0.f};   // xs[t] = D[p + 4t][jc]
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float part = arow[i][0] * xs[0] + arow[i][1] * xs[1] + arow[i][2] * xs[2]
-                       + arow[i][3] * xs[3];
-            part += dpp_f32<DPP_QUAD_XOR1>(part);
-            part += dpp_f32<DPP_QUAD_XOR2>(part);
-            const float xi = part + (i == jc ? 1.f : 0.f);
-            if (p == (i & 3)) xs[i >> 2] = xi;
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) sT[(16 * wave + p + 4 * t) * P_LD_A + 16 * wave + jc] = xs[t];
-    }
-    lds_barrier();
-
-    // ---- off-diagonal blocks of T. With D_b the diagonal inverses:
-    //   T10 = D1 A10 D0,  T32 = D3 A32 D2,  T21 = D2 A21 D1           (16-level)
-    //   T20 = D2 (A20 D0 + A21 T10)
-    //   T31 = T32 (A21 D1) + D3 (A31 D1)
-    //   T30 = T32 (A20 D0 + A21 T10) + D3 (A30 D0 + A31 T10)          (32-level)
-    auto blkA = [&](int I, int J) { return sA + (16 * I) * P_LD_A + 16 * J; };
+    // off-diagonal 16 x 16 blocks of A (I > J) and blocks of T
+    auto blkA = [&](int I, int J) { return sA + (16 * (I - 1)) * P_LD_A2 + 16 * J; };
     auto blkT = [&](int I, int J) { return sT + (16 * I) * P_LD_A + 16 * J; };
-    auto store_T = [&](int I, int J, f32x4 acc) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sT[(16 * I + 4 * lq + r) * P_LD_A + 16 * J + lr] = acc[r];
-    };
-    {
-        const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-        f32x4 h0 = z4, h1 = z4;
-        if (wave == 0) {
-            const f32x4 c10 = mm16(z4, blkA(1, 0), P_LD_A, blkT(0, 0), P_LD_A, lane);
-            h0 = mm16(z4, blkA(2, 0), P_LD_A, blkT(0, 0), P_LD_A, lane);              // A20 D0
-            store_T(1, 0, mm16_rb(z4, blkT(1, 1), P_LD_A, acc_to_bop(c10), lane));
-        } else if (wave == 1) {
-            const f32x4 c32 = mm16(z4, blkA(3, 2), P_LD_A, blkT(2, 2), P_LD_A, lane);
-            store_T(3, 2, mm16_rb(z4, blkT(3, 3), P_LD_A, acc_to_bop(c32), lane));
-        } else if (wave == 2) {
-            h0 = mm16(z4, blkA(2, 1), P_LD_A, blkT(1, 1), P_LD_A, lane);              // A21 D1
-            h1 = mm16(z4, blkA(3, 1), P_LD_A, blkT(1, 1), P_LD_A, lane);              // A31 D1
-            store_T(2, 1, mm16_rb(z4, blkT(2, 2), P_LD_A, acc_to_bop(h0), lane));
-        } else {
-            h0 = mm16(z4, blkA(2, 0), P_LD_A, blkT(0, 0), P_LD_A, lane);              // A20 D0
-            h1 = mm16(z4, blkA(3, 0), P_LD_A, blkT(0, 0), P_LD_A, lane);              // A30 D0
-        }
-        lds_barrier();
-        if (wave == 0) {
-            const f32x4 y00 = mm16(h0, blkA(2, 1), P_LD_A, blkT(1, 0), P_LD_A, lane);
-            store_T(2, 0, mm16_rb(z4, blkT(2, 2), P_LD_A, acc_to_bop(y00), lane));
-        } else if (wave == 2) {
-            const f32x4 t = mm16_rb(z4, blkT(3, 2), P_LD_A, acc_to_bop(h0), lane);
-            store_T(3, 1, mm16_rb(t, blkT(3, 3), P_LD_A, acc_to_bop(h1), lane));
-        } else if (wave == 3) {
-            const f32x4 y00 = mm16(h0, blkA(2, 1), P_LD_A, blkT(1, 0), P_LD_A, lane);
-            const f32x4 y10 = mm16(h1, blkA(3, 1), P_LD_A, blkT(1, 0), P_LD_A, lane);
-            const f32x4 t = mm16_rb(z4, blkT(3, 2), P_LD_A, acc_to_bop(y00), lane);
-            store_T(3, 0, mm16_rb(t, blkT(3, 3), P_LD_A, acc_to_bop(y10), lane));
-        }
-        lds_barrier();
-    }
 
-    // ---- T_w = T diag(beta e^gamma), T_u = T diag(beta) -> workspace (bf16,
-    //      three 32 x 32 blocks each; 16-byte pieces, consecutive per thread) ----
-    bf16 *dst = ws + ((size_t)h * nslots + slot) * TWU_ELEMS;
+    // one item: stage `p` (the current item's loads) into LDS, start the loads
+    // of `nit` into `pn` (which may be `p`), then compute and store T_w, T_u of `it`
+    auto item_step = [&](const PrepItem &it, const Pre &p, const PrepItem &nit, Pre &pn) {
+        // the lane index passes through an empty asm each item, so that the
+        // compiler rebuilds the per-lane LDS addresses here instead of keeping
+        // dozens of them live across the loop
+        int tid = tid0;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63;
+        const int l32 = lane & 31, lh = lane >> 5, lr = lane & 15, lq = lane >> 4;
+        auto rows4 = [&](const float *v, int i0, int qq) {
+            return *reinterpret_cast<const f32x4 *>(v + i0 + 8 * qq + 4 * lh);
+        };
+        auto store_T = [&](int I, int J, f32x4 acc) {
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
-        const int e = tid + P_NT * u;          // piece 0..767 (order in the chain pass's loads)
-        int mat, i, j0;
-        if (e < 512) {                         // rows 32-63, 8 pieces per row
-            mat = e >= 256 ? 1 : 0;
-            const int pp = e - 256 * mat;
-            i = 32 + (pp >> 3);
-            j0 = 8 * (pp & 7);
-        } else {                               // rows 0-31, columns 0-31
-            mat = e >= 640 ? 1 : 0;
-            const int pp = e - 512 - 128 * mat;
-            i = pp >> 2;
-            j0 = 8 * (pp & 3);
-        }
-        const float *sc = mat ? sBeta : sBeg;
-        const float sgn = mat ? 1.f : -1.f;    // T_w is stored negated
-        const f32x4 t0 = *reinterpret_cast<const f32x4 *>(sT + i * P_LD_A + j0);
-        const f32x4 t1 = *reinterpret_cast<const f32x4 *>(sT + i * P_LD_A + j0 + 4);
-        const f32x4 s0 = *reinterpret_cast<const f32x4 *>(sc + j0);
-        const f32x4 s1 = *reinterpret_cast<const f32x4 *>(sc + j0 + 4);
-        // the 16 x 16 blocks above the diagonal of T are zero (not stored in sT)
-        const bool zero = (j0 >> 4) > (i >> 4);
-        bf16x8 out;
+            for (int r = 0; r < 4; ++r) sT[(16 * I + 4 * lq + r) * P_LD_A + 16 * J + lr] = acc[r];
+        };
+        if (it.nvalid > 0) {
+            const int col = 8 * (tid & 15);
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-            out[e2] = (bf16)(zero ? 0.f : sgn * t0[e2] * s0[e2]);
-            out[e2 + 4] = (bf16)(zero ? 0.f : sgn * t1[e2] * s1[e2]);
+            for (int u = 0; u < 4; ++u)
+                *reinterpret_cast<bf16x8 *>(sK + ((tid >> 4) + 16 * u) * P_LD_K + col) = p.kr[u];
+            if (wave == 0) {
+                const float gam = wave_inclusive_scan(p.gv);
+                sGam[lane] = gam;
+                sBeta[lane] = p.bv;
+                sBeg[lane] = p.bv * __expf(gam);
+            }
         }
-        *reinterpret_cast<bf16x8 *>(dst + 8 * e) = out;
+        fetch(nit, pn);
+        if (it.nvalid == 0) return;            // uniform over the workgroup
+        lds_barrier();
+
+        // ---- gram tiles of A = -strict_lower(diag(beta) K K^T * Gamma) ----
+        if (wave < 3) {
+            const int ti = wave == 0 ? 0 : 1, tj = wave == 1 ? 1 : 0;
+            const int j = 32 * tj + l32;
+            const float gj = sGam[j];
+            f32x4 gi[4], bi[4];
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                gi[qq] = rows4(sGam, 32 * ti, qq);
+                bi[qq] = rows4(sBeta, 32 * ti, qq);
+            }
+            f32x16 at = {};
+            at = mma32<4>(at, sK, P_LD_K, 32 * ti, sK, P_LD_K, 32 * tj, lane, 0);
+            at = mma32<4>(at, sK, P_LD_K, 32 * ti, sK, P_LD_K, 32 * tj, lane, 64);
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) {
+                    const int r = 4 * qq + s2, i = 32 * ti + acc_row(r, lane);
+                    at[r] = j < i ? -bi[qq][s2] * at[r] * __expf(gi[qq][s2] - gj) : 0.f;
+                }
+            // rows 16-63, columns 0-47 into sA (the off-diagonal blocks are read
+            // from there); accumulator rows r < 8 of tile row 0 are rows 0-15
+            if (j < 48) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (ti == 1 || r >= 8) sA[(32 * ti + acc_row(r, lane) - 16) * P_LD_A2 + j] = at[r];
+            }
+            if (wave < 2) {
+                // and the two diagonal 16 x 16 blocks in the solve's quad layout:
+                // element (i, m) of diagonal block b at b * P_QB + (m % 4) * 68 + 4 i + m / 4
+                const int m = l32 & 15;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int it_ = acc_row(r, lane);
+                    if ((it_ >> 4) == (l32 >> 4))
+                        sY[(2 * wave + (it_ >> 4)) * P_QB + (m & 3) * 68 + (it_ & 15) * 4 + (m >> 2)] = at[r];
+                }
+            }
+        }
+        lds_barrier();                         // A complete; K no longer read
+
+        // ---- diagonal blocks: D_w = (I - A_ww)^-1, D[i][j] = [i==j] + sum_{m<i} A[i][m] D[m][j]
+        {
+            const int jc = lane >> 2, pq = lane & 3;
+            const float *myp = sY + wave * P_QB + pq * 68;
+            f32x4 arow[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) arow[i] = *reinterpret_cast<const f32x4 *>(myp + 4 * i);
+            float xs[4] = {0.f, 0.f, 0.f, 0.f};   // xs[t] = D[pq + 4t][jc]
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float part = arow[i][0] * xs[0] + arow[i][1] * xs[1] + arow[i][2] * xs[2]
+                           + arow[i][3] * xs[3];
+                part += dpp_f32<DPP_QUAD_XOR1>(part);
+                part += dpp_f32<DPP_QUAD_XOR2>(part);
+                const float xi = part + (i == jc ? 1.f : 0.f);
+                if (pq == (i & 3)) xs[i >> 2] = xi;
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) sT[(16 * wave + pq + 4 * t) * P_LD_A + 16 * wave + jc] = xs[t];
+        }
+        lds_barrier();
+
+        // ---- off-diagonal blocks of T. With D_b the diagonal inverses:
+        //   T10 = D1 A10 D0,  T32 = D3 A32 D2,  T21 = D2 A21 D1           (16-level)
+        //   T20 = D2 (A20 D0 + A21 T10)
+        //   T31 = T32 (A21 D1) + D3 (A31 D1)
+        //   T30 = T32 (A20 D0 + A21 T10) + D3 (A30 D0 + A31 T10)          (32-level)
+        {
+            const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+            f32x4 h0 = z4, h1 = z4;
+            if (wave == 0) {
+                const f32x4 c10 = mm16(z4, blkA(1, 0), P_LD_A2, blkT(0, 0), P_LD_A, lane);
+                h0 = mm16(z4, blkA(2, 0), P_LD_A2, blkT(0, 0), P_LD_A, lane);              // A20 D0
+                store_T(1, 0, mm16_rb(z4, blkT(1, 1), P_LD_A, acc_to_bop(c10), lane));
+            } else if (wave == 1) {
+                const f32x4 c32 = mm16(z4, blkA(3, 2), P_LD_A2, blkT(2, 2), P_LD_A, lane);
+                store_T(3, 2, mm16_rb(z4, blkT(3, 3), P_LD_A, acc_to_bop(c32), lane));
+            } else if (wave == 2) {
+                h0 = mm16(z4, blkA(2, 1), P_LD_A2, blkT(1, 1), P_LD_A, lane);              // A21 D1
+                h1 = mm16(z4, blkA(3, 1), P_LD_A2, blkT(1, 1), P_LD_A, lane);              // A31 D1
+                store_T(2, 1, mm16_rb(z4, blkT(2, 2), P_LD_A, acc_to_bop(h0), lane));
+            } else {
+                h0 = mm16(z4, blkA(2, 0), P_LD_A2, blkT(0, 0), P_LD_A, lane);              // A20 D0
+                h1 = mm16(z4, blkA(3, 0), P_LD_A2, blkT(0, 0), P_LD_A, lane);              // A30 D0
+            }
+            lds_barrier();
+            if (wave == 0) {
+                const f32x4 y00 = mm16(h0, blkA(2, 1), P_LD_A2, blkT(1, 0), P_LD_A, lane);
+                store_T(2, 0, mm16_rb(z4, blkT(2, 2), P_LD_A, acc_to_bop(y00), lane));
+            } else if (wave == 2) {
+                const f32x4 t = mm16_rb(z4, blkT(3, 2), P_LD_A, acc_to_bop(h0), lane);
+                store_T(3, 1, mm16_rb(t, blkT(3, 3), P_LD_A, acc_to_bop(h1), lane));
+            } else if (wave == 3) {
+                const f32x4 y00 = mm16(h0, blkA(2, 1), P_LD_A2, blkT(1, 0), P_LD_A, lane);
+                const f32x4 y10 = mm16(h1, blkA(3, 1), P_LD_A2, blkT(1, 0), P_LD_A, lane);
+                const f32x4 t = mm16_rb(z4, blkT(3, 2), P_LD_A, acc_to_bop(y00), lane);
+                store_T(3, 0, mm16_rb(t, blkT(3, 3), P_LD_A, acc_to_bop(y10), lane));
+            }
+            lds_barrier();
+        }
+
+        // ---- T_w = T diag(beta e^gamma), T_u = T diag(beta) -> workspace (bf16,
+        //      three 32 x 32 blocks each; 16-byte pieces, consecutive per thread) ----
+        bf16 *dst = ws + ((size_t)it.h * nslots + it.slot) * TWU_ELEMS;
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            const int e = tid + P_NT * u;      // piece 0..767 (order in the chain pass's loads)
+            int mat, i, j0;
+            if (e < 512) {                     // rows 32-63, 8 pieces per row
+                mat = e >= 256 ? 1 : 0;
+                const int pp = e - 256 * mat;
+                i = 32 + (pp >> 3);
+                j0 = 8 * (pp & 7);
+            } else {                           // rows 0-31, columns 0-31
+                mat = e >= 640 ? 1 : 0;
+                const int pp = e - 512 - 128 * mat;
+                i = pp >> 2;
+                j0 = 8 * (pp & 3);
+            }
+            const float *sc = mat ? sBeta : sBeg;
+            const float sgn = mat ? 1.f : -1.f;   // T_w is stored negated
+            const f32x4 t0 = *reinterpret_cast<const f32x4 *>(sT + i * P_LD_A + j0);
+            const f32x4 t1 = *reinterpret_cast<const f32x4 *>(sT + i * P_LD_A + j0 + 4);
+            const f32x4 s0 = *reinterpret_cast<const f32x4 *>(sc + j0);
+            const f32x4 s1 = *reinterpret_cast<const f32x4 *>(sc + j0 + 4);
+            // the 16 x 16 blocks above the diagonal of T are zero (not stored in sT)
+            const bool zero = (j0 >> 4) > (i >> 4);
+            bf16x8 out;
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                out[e2] = (bf16)(zero ? 0.f : sgn * t0[e2] * s0[e2]);
+                out[e2 + 4] = (bf16)(zero ? 0.f : sgn * t1[e2] * s1[e2]);
+            }
+            *reinterpret_cast<bf16x8 *>(dst + 8 * e) = out;
+        }
+        lds_barrier();                         // T and the scalars read before the next item
+    };
+
+    // one register set: each step stages it into LDS before refilling it
+    PrepItem it = prep_locate(cu_seqlens, (int)blockIdx.x, nitems, T, H, N);
+    Pre pre;
+    fetch(it, pre);
+    for (int item = (int)blockIdx.x; item < nitems; item += stride) {
+        const PrepItem nit = prep_locate(cu_seqlens, item + stride, nitems, T, H, N);
+        item_step(it, pre, nit, pre);
+        it = nit;
     }
 }
 
@@ -870,7 +931,22 @@ hipError_t launch_prefill_prepare(const void *k, const float *g, const float *be
     const long tokens = cu ? (long)T : (long)N * T;
     const long nslots = tokens / C + N + 1;
     if (tokens == 0) return hipSuccess;        // no chunk: nothing to prepare
-    dim3 grid((unsigned)nslots, (unsigned)H), block(P_NT);
+    // enough workgroups to fill every CU at the occupancy the kernel reaches,
+    // each looping over items
+    static int per_cu = 0, cus = 0;
+    if (per_cu == 0) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e == hipSuccess)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)chunk_prep_kernel,
+                                                             P_NT, P_LDS_BYTES);
+        if (e != hipSuccess) return e;
+        if (per_cu < 1) per_cu = 1;
+    }
+    const long nitems = nslots * H;
+    const long fill = (long)per_cu * cus;
+    dim3 grid((unsigned)(nitems < fill ? nitems : fill)), block(P_NT);
     hipLaunchKernelGGL(chunk_prep_kernel, grid, block, P_LDS_BYTES, stream, (const bf16 *)k, g,
                        beta, cu, (bf16 *)ws, T, H, N, (int)nslots);
     return hipGetLastError();
