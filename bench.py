@@ -12,10 +12,10 @@ carries:
 * ``roofline`` of the dominant kernel (the pass with the longer average
   duration, timed with HIP events around each pass): its algorithmic HBM
   bytes per launch over that duration, against 8 TB/s. Per token-head,
-  chunk_chain moves q, k, v, o (bf16), g (fp32) and the 192 B of bf16
-  T diag(beta e^gamma), T diag(beta) that chunk_prep left in the workspace
-  (1220 B), plus the fp32 final states; chunk_prep moves k, g, beta and
-  writes those 192 B (456 B). ``traffic`` is the measured HBM bytes per
+  chunk_chain moves q, k, v, o (bf16), g (fp32) and the 288 B of bf16
+  T diag(beta e^gamma), T diag(beta) (192 B) and P (96 B) that chunk_prep
+  left in the workspace (1316 B), plus the fp32 final states; chunk_prep
+  reads q, k, g, beta and writes those 288 B (808 B). ``traffic`` is the measured HBM bytes per
   launch from the committed counter summary (profiles/), or null when the
   kernel source has changed since. ``path`` gives the whole step against the
   method's own 1032 B per token-head (q, k, v, o, g, beta) and the
@@ -69,18 +69,20 @@ def prefill_bytes(B, T, H, dk=128, dv=128, n_states_out=None, n_states_in=0):
     return tok_head * per + states + n_states_in * H * dv * dk * 4
 
 
-TWU_BYTES_PER_TOKEN_HEAD = 2 * 3 * 32 * 32 * 2 // 64   # 192: bf16 T_w, T_u blocks per token
+# workspace per token-head: bf16 T_w, T_u (three 32 x 32 blocks each) and P
+# (rows 0-31 by columns 0-31, rows 32-63 by all 64) per 64-token chunk
+WS_BYTES_PER_TOKEN_HEAD = (2 * 3 * 32 * 32 + 32 * 32 + 32 * 64) * 2 // 64   # 288
 
 
 def chain_bytes(B, T, H, dk=128, dv=128):
-    """chunk_chain per launch: q, k, v, o bf16, g fp32, T_w/T_u read back, final states."""
-    per = 2 * (dk + dk + dv + dv) + 4 + TWU_BYTES_PER_TOKEN_HEAD
+    """chunk_chain per launch: q, k, v, o bf16, g fp32, the workspace read back, final states."""
+    per = 2 * (dk + dk + dv + dv) + 4 + WS_BYTES_PER_TOKEN_HEAD
     return B * T * H * per + B * H * dv * dk * 4
 
 
 def prep_bytes(B, T, H, dk=128):
-    """chunk_prep per launch: k bf16, g and beta fp32 read, T_w/T_u written."""
-    return B * T * H * (2 * dk + 4 + 4 + TWU_BYTES_PER_TOKEN_HEAD)
+    """chunk_prep per launch: q, k bf16, g and beta fp32 read, the workspace written."""
+    return B * T * H * (2 * dk + 2 * dk + 4 + 4 + WS_BYTES_PER_TOKEN_HEAD)
 
 
 def decode_bytes(B, H, dk=128, dv=128):
@@ -156,7 +158,7 @@ def bench_prefill(gdn, inputs, steps, warmup):
     for i in range(steps):
         s = sets[i & 1]
         ev[i][0].record(stream)
-        gdn.gdn_prefill_prepare(s["k"], s["g"], s["beta"], ws)
+        gdn.gdn_prefill_prepare(s["q"], s["k"], s["g"], s["beta"], ws)
         ev[i][1].record(stream)
         gdn.gdn_prefill_apply(s["q"], s["k"], s["v"], s["g"], ws, None, s["fin"], s["o"],
                               scale=c.scale)

@@ -35,7 +35,7 @@ _SIGS = {
     "gdn_check_cu_seqlens": [_vp, _i, _i],
     "gdn_prefill": [_vp] * 9 + [_i] * 6 + [_f, _i, _vp, _sz, _vp],
     "gdn_prefill_workspace_size": [_i] * 8 + [_vp],
-    "gdn_prefill_prepare": [_vp] * 4 + [_i] * 7 + [_vp, _sz, _vp],
+    "gdn_prefill_prepare": [_vp] * 5 + [_i] * 7 + [_vp, _sz, _vp],
     "gdn_prefill_apply": [_vp] * 8 + [_i] * 6 + [_f, _i, _vp, _sz, _vp],
     "gdn_prefill_recurrent": [_vp] * 9 + [_i] * 6 + [_f, _i, _vp],
     "gdn_decode_step": [_vp] * 7 + [_i] * 4 + [_f, _i, _vp],
@@ -159,14 +159,17 @@ def _ws(workspace):
     return workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
 
-def gdn_prefill_prepare(k, g, beta, workspace, cu_seqlens=None, d_v=None):
-    """First pass of the workspace path (see include/gdn.h): T diag(beta e^gamma)
-    and T diag(beta) of every chunk into `workspace`."""
+def gdn_prefill_prepare(q, k, g, beta, workspace, cu_seqlens=None, d_v=None):
+    """First pass of the workspace path (see include/gdn.h): T diag(beta e^gamma),
+    T diag(beta) and the decayed intra-chunk attention of every chunk into
+    `workspace`."""
     B, T, H, dk = k.shape
     dv = dk if d_v is None else d_v
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if q.shape != k.shape or q.dtype != k.dtype:
+        raise GDNError("q must match k in shape and dtype")
     _check(load().gdn_prefill_prepare(
-        _dev(k, "k"), _dev(g, "g", torch.float32, (B, T, H)),
+        _dev(q, "q"), _dev(k, "k"), _dev(g, "g", torch.float32, (B, T, H)),
         _dev(beta, "beta", torch.float32, (B, T, H)),
         _dev(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,)),
         B, T, H, dk, dv, N, _dtype_code(k), *_ws(workspace), _stream(k.device)))

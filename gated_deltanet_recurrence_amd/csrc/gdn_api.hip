@@ -18,8 +18,8 @@ hipError_t launch_prefill_recurrent(const void *, const void *, const void *, co
 hipError_t launch_prefill_chunk(const void *, const void *, const void *, const float *,
                                 const float *, const float *, float *, void *, const int32_t *,
                                 int, int, int, float, hipStream_t);
-hipError_t launch_prefill_prepare(const void *, const float *, const float *, const int32_t *,
-                                  int, int, int, void *, hipStream_t);
+hipError_t launch_prefill_prepare(const void *, const void *, const float *, const float *,
+                                  const int32_t *, int, int, int, void *, hipStream_t);
 hipError_t launch_prefill_apply(const void *, const void *, const void *, const float *,
                                 const float *, float *, void *, const int32_t *, int, int, int,
                                 float, const void *, hipStream_t);
@@ -145,7 +145,7 @@ int gdn_prefill(const void *q, const void *k, const void *v, const float *g, con
                                                        final_state, o, cu_seqlens, T, H, N,
                                                        scale, s));
         if (!workspace_ok(workspace, workspace_bytes, B, T, H, N)) return GDN_ERR_WORKSPACE;
-        hipError_t e = gdn::launch_prefill_prepare(k, g, beta, cu_seqlens, T, H, N, workspace, s);
+        hipError_t e = gdn::launch_prefill_prepare(q, k, g, beta, cu_seqlens, T, H, N, workspace, s);
         if (e == hipSuccess)
             e = gdn::launch_prefill_apply(q, k, v, g, initial_state, final_state, o, cu_seqlens,
                                           T, H, N, scale, workspace, s);
@@ -155,18 +155,18 @@ int gdn_prefill(const void *q, const void *k, const void *v, const float *g, con
                                  T, H, d_k, d_v, N, scale, dtype, stream);
 }
 
-int gdn_prefill_prepare(const void *k, const float *g, const float *beta,
+int gdn_prefill_prepare(const void *q, const void *k, const float *g, const float *beta,
                         const int32_t *cu_seqlens, int B, int T, int H, int d_k, int d_v, int N,
                         int dtype, void *workspace, size_t workspace_bytes, void *stream)
 {
-    // q, v and o are not arguments of this pass: validate with stand-ins
+    // v and o are not arguments of this pass: validate with stand-ins
     const void *p = workspace ? workspace : (const void *)k;
-    int st = check_prefill(p, k, p, g, beta, p, cu_seqlens, B, T, H, d_k, d_v, N, dtype);
+    int st = check_prefill(q, k, p, g, beta, p, cu_seqlens, B, T, H, d_k, d_v, N, dtype);
     if (st != GDN_OK) return st;
     if (!chunk_path(dtype, d_k, d_v)) return GDN_ERR_UNSUPPORTED;
     if (!workspace) return GDN_ERR_NULL;
     if (!workspace_ok(workspace, workspace_bytes, B, T, H, N)) return GDN_ERR_WORKSPACE;
-    return status_of(gdn::launch_prefill_prepare(k, g, beta, cu_seqlens, T, H, N, workspace,
+    return status_of(gdn::launch_prefill_prepare(q, k, g, beta, cu_seqlens, T, H, N, workspace,
                                                  (hipStream_t)stream));
 }
 

@@ -45,28 +45,33 @@ using namespace chunk;
 constexpr int C = 64;
 constexpr int DK = 128;
 constexpr int DV = 128;
-constexpr int TWU_ELEMS = 2 * 3 * 32 * 32;    // bf16 per (chunk, head) in the workspace
+constexpr int WS_TWU = 768;                   // 16-byte pieces of -T_w and T_u per (chunk, head)
+constexpr int WS_P = 384;                     // 16-byte pieces of P per (chunk, head)
+constexpr int ITEM_ELEMS = 8 * (WS_TWU + WS_P);   // 9216 bf16 per (chunk, head) in the workspace
 
 // ---------------------------------------------------------------------------
 // Pass 1: chunk_prep. Workgroups of 4 waves, each looping over (chunk slot,
 // head) items.
 // ---------------------------------------------------------------------------
 constexpr int P_NT = 256;
-constexpr int P_LD_K = DK + 8;                 // bf16 row stride of K
+constexpr int P_LD_K = DK + 8;                 // bf16 row stride of K and Q
 constexpr int P_LD_A = C + 4;                  // fp32 row stride of T
 constexpr int P_LD_A2 = 52;                    // fp32 row stride of the off-diagonal part of A
-constexpr int P_QB = 4 * 68;                   // one 16 x 16 block in the quad layout (floats)
+constexpr int P_DB = 16 * 16 + 4;              // floats per diagonal 16 x 16 block of A (padded
+                                               // so the four blocks' rows fall on different banks)
 constexpr int P_SZ_R1 = C * P_LD_K * 2;        // 17408: K, then T
+constexpr int P_SZ_R2 = C * P_LD_K * 2;        // 17408: Q
 constexpr int P_SZ_A = 48 * P_LD_A2 * 4;       // 9984: rows 16-63, columns 0-47 of A
-constexpr int P_SZ_Y = 4 * P_QB * 4;           // 4352: the diagonal 16 x 16 blocks, quad layout
-constexpr int P_SZ_SC = 3 * C * 4;             // gamma, beta, beta e^gamma
+constexpr int P_SZ_Y = 4 * P_DB * 4;           // 4160: the diagonal blocks of A, row-major
+constexpr int P_SZ_SC = 4 * C * 4;             // gamma log2(e), beta, -beta e^gamma, E
 constexpr int P_OFF_R1 = 0;
-constexpr int P_OFF_A = P_OFF_R1 + P_SZ_R1;
+constexpr int P_OFF_R2 = P_OFF_R1 + P_SZ_R1;
+constexpr int P_OFF_A = P_OFF_R2 + P_SZ_R2;
 constexpr int P_OFF_Y = P_OFF_A + P_SZ_A;
 constexpr int P_OFF_SC = P_OFF_Y + P_SZ_Y;
-constexpr int P_LDS_BYTES = P_OFF_SC + P_SZ_SC;
+constexpr int P_LDS_BYTES = P_OFF_SC + P_SZ_SC;   // 49984
 static_assert(C * P_LD_A * 4 <= P_SZ_R1, "T fits where K was");
-static_assert(P_LDS_BYTES <= 40 * 1024, "four prep workgroups per CU");
+static_assert(P_LDS_BYTES <= 160 * 1024 / 3, "three prep workgroups per CU");
 
 // ---------------------------------------------------------------------------
 // Pass 2: chunk_chain. One workgroup of 8 waves per (32-wide d_v tile, head,
@@ -186,17 +191,25 @@ __device__ __forceinline__ f32x16 mma32s(f32x16 acc, const bf16 *a, int ld_a, in
 using namespace split;
 
 // ---------------------------------------------------------------------------
-// chunk_prep: T_w and T_u of (chunk, head) items. Item i is slot i / H of
-// head i % H; a workgroup takes items blockIdx.x, + gridDim.x, ... and loads
-// the next item's K, g and beta into registers while it works on the current
-// one, so that the HBM latency is paid once per workgroup.
+// chunk_prep: the parts of a chunk that do not depend on the state, for
+// (chunk, head) items. Item i is slot i / H of head i % H; a workgroup takes
+// items blockIdx.x, + gridDim.x, ... and loads the next item's K, Q, g and
+// beta into registers while it works on the current one, so that the HBM
+// latency is paid once per workgroup.
 //
-//   stage  K (64 x 128) into LDS; gamma = prefix sum of g (wave 0, DPP scan)
-//   gram   wave 0: tile (0,0) of A, wave 1: tile (1,1), wave 2: tile (1,0)
-//          (v_mfma_f32_32x32x16_bf16, masked and scaled in registers)
-//   solve  wave w inverts the 16 x 16 diagonal block w of I - A by forward
-//          substitution: lane 4j + p owns column j and the terms m = p mod 4
-//          of every row's dot product, finished with two DPP quad sums
+//   stage  K and Q (64 x 128) into LDS; gamma = prefix sum of g (wave 0)
+//   gram   waves 0-2, one 32 x 32 tile each of A = -strict_lower(diag(beta)
+//          K K^T * Gamma) and of P^T, P = lower_incl(Q K^T * Gamma), sharing
+//          the K fragments (v_mfma_f32_32x32x16_bf16): wave 0 tiles (0,0) of
+//          both, wave 1 tiles (1,1), wave 2 A (1,0) and P^T (0,1). On the
+//          diagonal tiles one exponential per element serves A (below the
+//          diagonal) or P (on and above it); across the halves,
+//          Gamma_ij = E_i E_j with E_t = e^{gamma_t - gamma_32} (t >= 32) or
+//          e^{gamma_32 - gamma_t} (t < 32), two factors no larger than 1 for
+//          gates in (0, 1]
+//          P goes from the accumulators straight to the workspace
+//   solve  wave 0 inverts the four 16 x 16 diagonal blocks of I - A by
+//          forward substitution, 16 lanes per block and one column per lane
 //   L1/L2  the off-diagonal blocks of T by two levels of 2 x 2 block
 //          inversion, (L^-1)_21 = L22^-1 A21 L11^-1 (fp32 16x16x4 MFMA)
 //   store  -T diag(beta e^gamma) and T diag(beta), bf16, to the workspace
@@ -228,42 +241,50 @@ __device__ __forceinline__ PrepItem prep_locate(const int32_t *cu, int item, int
     return it;
 }
 
-__global__ void __launch_bounds__(P_NT, 4)
-chunk_prep_kernel(const bf16 *__restrict__ k, const float *__restrict__ g,
-                  const float *__restrict__ beta, const int32_t *__restrict__ cu_seqlens,
-                  bf16 *__restrict__ ws, int T, int H, int N, int nslots)
+__global__ void __launch_bounds__(P_NT, 3)
+chunk_prep_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
+                  const float *__restrict__ g, const float *__restrict__ beta,
+                  const int32_t *__restrict__ cu_seqlens, bf16 *__restrict__ ws, int T, int H,
+                  int N, int nslots)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     bf16 *sK = reinterpret_cast<bf16 *>(smem + P_OFF_R1);
     float *sT = reinterpret_cast<float *>(smem + P_OFF_R1);
+    bf16 *sQ = reinterpret_cast<bf16 *>(smem + P_OFF_R2);
     float *sA = reinterpret_cast<float *>(smem + P_OFF_A);
     float *sY = reinterpret_cast<float *>(smem + P_OFF_Y);
-    float *sGam = reinterpret_cast<float *>(smem + P_OFF_SC);
-    float *sBeta = sGam + C;
-    float *sBeg = sBeta + C;
+    float *sGl = reinterpret_cast<float *>(smem + P_OFF_SC);   // gamma log2(e)
+    float *sBeta = sGl + C;
+    float *sBegN = sBeta + C;                                  // -beta e^gamma
+    float *sE = sBegN + C;
 
     const int tid0 = (int)threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
     const int nitems = nslots * H;
     const int stride = (int)gridDim.x;
-    const int tstride = H * DK;                // elements between consecutive tokens of K
+    const int tstride = H * DK;                // elements between consecutive tokens of K, Q
 
-    // K rows (tid >> 4) + 16 u, columns 8 (tid & 15) ..; g and beta of token
-    // `lane` (wave 0). Buffer loads bounded by the chunk's valid tokens: rows
+    // K and Q rows (tid >> 4) + 16 u, columns 8 (tid & 15) ..; g and beta of
+    // token `lane`. Buffer loads bounded by the chunk's valid tokens: rows
     // past the end of the sequence (and every row of an empty item) read zero.
     struct Pre {
-        bf16x8 kr[4];
+        bf16x8 kr[4], qr[4];
         float gv, bv;
     };
     auto fetch = [&](const PrepItem &it, Pre &p) {
         const size_t tok0 = (size_t)it.row0;
-        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(k + tok0 * tstride + (size_t)it.h * DK), 0, (unsigned)it.nvalid * tstride * 2, 0x00020000);
+        const unsigned nb = (unsigned)it.nvalid * tstride * 2;
+        const size_t hoff = tok0 * tstride + (size_t)it.h * DK;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(k + hoff), 0, nb, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)(q + hoff), 0, nb, 0x00020000);
         const unsigned off = (unsigned)(((tid0 >> 4) * tstride + 8 * (tid0 & 15)) * 2);
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 4; ++u) {
             p.kr[u] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
                           rk, off, (unsigned)(16 * u * tstride * 2), 0));
+            p.qr[u] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                          rq, off, (unsigned)(16 * u * tstride * 2), 0));
+        }
         const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(g + tok0 * H + it.h), 0, (unsigned)it.nvalid * H * 4, 0x00020000);
         const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
@@ -277,8 +298,10 @@ chunk_prep_kernel(const bf16 *__restrict__ k, const float *__restrict__ g,
     auto blkT = [&](int I, int J) { return sT + (16 * I) * P_LD_A + 16 * J; };
 
     // one item: stage `p` (the current item's loads) into LDS, start the loads
-    // of `nit` into `pn` (which may be `p`), then compute and store T_w, T_u of `it`
-    auto item_step = [&](const PrepItem &it, const Pre &p, const PrepItem &nit, Pre &pn) {
+    // of `nit` into `pn` (which may be `p`), locate item `after` into `ait`,
+    // then compute and store the item
+    auto item_step = [&](const PrepItem &it, const Pre &p, const PrepItem &nit, Pre &pn,
+                         int after, PrepItem &ait) {
         // the lane index passes through an empty asm each item, so that the
         // compiler rebuilds the per-lane LDS addresses here instead of keeping
         // dozens of them live across the loop
@@ -293,83 +316,149 @@ chunk_prep_kernel(const bf16 *__restrict__ k, const float *__restrict__ g,
 #pragma unroll
             for (int r = 0; r < 4; ++r) sT[(16 * I + 4 * lq + r) * P_LD_A + 16 * J + lr] = acc[r];
         };
+
         if (it.nvalid > 0) {
             const int col = 8 * (tid & 15);
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < 4; ++u) {
                 *reinterpret_cast<bf16x8 *>(sK + ((tid >> 4) + 16 * u) * P_LD_K + col) = p.kr[u];
+                *reinterpret_cast<bf16x8 *>(sQ + ((tid >> 4) + 16 * u) * P_LD_K + col) = p.qr[u];
+            }
             if (wave == 0) {
                 const float gam = wave_inclusive_scan(p.gv);
-                sGam[lane] = gam;
+                const float g32 = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gam), 32));
+                sGl[lane] = gam * 1.4426950408889634f;
                 sBeta[lane] = p.bv;
-                sBeg[lane] = p.bv * __expf(gam);
+                sBegN[lane] = -p.bv * __expf(gam);
+                sE[lane] = __expf(lane >= 32 ? gam - g32 : g32 - gam);
             }
         }
         fetch(nit, pn);
+        ait = prep_locate(cu_seqlens, after, nitems, T, H, N);
         if (it.nvalid == 0) return;            // uniform over the workgroup
         lds_barrier();
+        bf16 *dst = ws + ((size_t)it.h * nslots + it.slot) * ITEM_ELEMS;
 
-        // ---- gram tiles of A = -strict_lower(diag(beta) K K^T * Gamma) ----
+        // ---- gram tiles of A and P^T ----
         if (wave < 3) {
-            const int ti = wave == 0 ? 0 : 1, tj = wave == 1 ? 1 : 0;
-            const int j = 32 * tj + l32;
-            const float gj = sGam[j];
-            f32x4 gi[4], bi[4];
+            const int ti = wave == 0 ? 0 : 1, tj = wave == 1 ? 1 : 0, qb = wave == 0 ? 0 : 1;
+            f32x16 at = {}, pt = {};
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                gi[qq] = rows4(sGam, 32 * ti, qq);
-                bi[qq] = rows4(sBeta, 32 * ti, qq);
-            }
-            f32x16 at = {};
-            at = mma32<4>(at, sK, P_LD_K, 32 * ti, sK, P_LD_K, 32 * tj, lane, 0);
-            at = mma32<4>(at, sK, P_LD_K, 32 * ti, sK, P_LD_K, 32 * tj, lane, 64);
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq)
+            for (int hk = 0; hk < 2; ++hk) {
+                bf16x8 fa[4], fb[4], fq[4];
 #pragma unroll
                 for (int s2 = 0; s2 < 4; ++s2) {
-                    const int r = 4 * qq + s2, i = 32 * ti + acc_row(r, lane);
-                    at[r] = j < i ? -bi[qq][s2] * at[r] * __expf(gi[qq][s2] - gj) : 0.f;
+                    fa[s2] = frag32(sK, P_LD_K, 32 * ti, 64 * hk + 16 * s2, lane);
+                    fb[s2] = frag32(sK, P_LD_K, 32 * tj, 64 * hk + 16 * s2, lane);
+                    fq[s2] = frag32(sQ, P_LD_K, 32 * qb, 64 * hk + 16 * s2, lane);
                 }
-            // rows 16-63, columns 0-47 into sA (the off-diagonal blocks are read
-            // from there); accumulator rows r < 8 of tile row 0 are rows 0-15
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) {
+                    at = mfma32(fa[s2], fb[s2], at);
+                    pt = mfma32(fb[s2], fq[s2], pt);
+                }
+            }
+            // element r: A row i = 32 ti + acc_row(r), column j = 32 tj + l32;
+            // P^T row (key) 32 tj + acc_row(r), column (query) 32 qb + l32
+            if (wave < 2) {
+                const int j = 32 * tj + l32;
+                const float glj = sGl[j];
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const f32x4 gli = rows4(sGl, 32 * ti, qq), bi = rows4(sBeta, 32 * ti, qq);
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2) {
+                        const int r = 4 * qq + s2, i = 32 * ti + acc_row(r, lane);
+                        const bool below = j < i;
+                        const float d = gli[s2] - glj;
+                        const float e = __builtin_amdgcn_exp2f(below ? d : -d);
+                        at[r] = below ? -(bi[s2] * at[r]) * e : 0.f;
+                        pt[r] = below ? 0.f : pt[r] * e;
+                    }
+                }
+            } else {
+                const float ej = sE[l32], eq = sE[32 + l32];
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const f32x4 ei = rows4(sE, 32, qq), bi = rows4(sBeta, 32, qq), ek = rows4(sE, 0, qq);
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2) {
+                        const int r = 4 * qq + s2;
+                        at[r] = -(bi[s2] * at[r]) * (ei[s2] * ej);
+                        pt[r] = pt[r] * (ek[s2] * eq);
+                    }
+                }
+            }
+            // P straight to the workspace: query row 32 qb + l32 (rows 0-31 keep
+            // keys 0-31, rows 32-63 all 64), keys 32 tj + 8 (r / 4) + 4 lh + 0..3
+            {
+                const int qrow = 32 * qb + l32;
+                bf16 *prow = dst + 8 * WS_TWU + (qrow < 32 ? 32 * qrow : 1024 + 64 * (qrow - 32));
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    bf16x4 x = {(bf16)pt[4 * gq], (bf16)pt[4 * gq + 1], (bf16)pt[4 * gq + 2], (bf16)pt[4 * gq + 3]};
+                    *reinterpret_cast<bf16x4 *>(prow + 32 * tj + 8 * gq + 4 * lh) = x;
+                }
+            }
+            // rows 16-63, columns 0-47 of A into sA (the off-diagonal blocks are
+            // read from there); accumulator rows r < 8 of tile row 0 are rows 0-15
+            const int j = 32 * tj + l32;
             if (j < 48) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     if (ti == 1 || r >= 8) sA[(32 * ti + acc_row(r, lane) - 16) * P_LD_A2 + j] = at[r];
             }
             if (wave < 2) {
-                // and the two diagonal 16 x 16 blocks in the solve's quad layout:
-                // element (i, m) of diagonal block b at b * P_QB + (m % 4) * 68 + 4 i + m / 4
-                const int m = l32 & 15;
+                // and the two diagonal 16 x 16 blocks, row-major, into sY
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int it_ = acc_row(r, lane);
                     if ((it_ >> 4) == (l32 >> 4))
-                        sY[(2 * wave + (it_ >> 4)) * P_QB + (m & 3) * 68 + (it_ & 15) * 4 + (m >> 2)] = at[r];
+                        sY[(2 * wave + (it_ >> 4)) * P_DB + (it_ & 15) * 16 + (l32 & 15)] = at[r];
                 }
             }
         }
-        lds_barrier();                         // A complete; K no longer read
+        lds_barrier();                         // A complete; K and Q no longer read
 
-        // ---- diagonal blocks: D_w = (I - A_ww)^-1, D[i][j] = [i==j] + sum_{m<i} A[i][m] D[m][j]
-        {
-            const int jc = lane >> 2, pq = lane & 3;
-            const float *myp = sY + wave * P_QB + pq * 68;
-            f32x4 arow[16];
+        if (wave == 0) {
+            // ---- diagonal blocks, one per 16 lanes: lane 16 b + c computes
+            //      column c of D_b = (I - A_bb)^-1 row by row,
+            //      D[i][c] = [i == c] + sum_{m < i} A[i][m] D[m][c]
+            //      (the block's row i read by all 16 lanes: an LDS broadcast);
+            //      row i + 1 is loaded while row i is summed ----
+            const int bb = lane >> 4, c = lane & 15;
+            const float *Ab = sY + bb * P_DB;
+            float D[16];
+            f32x4 rowv[2][4];
+            auto load_row = [&](int i, f32x4 (&dstv)[4]) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) arow[i] = *reinterpret_cast<const f32x4 *>(myp + 4 * i);
-            float xs[4] = {0.f, 0.f, 0.f, 0.f};   // xs[t] = D[pq + 4t][jc]
+                for (int t = 0; t < 4; ++t)
+                    if (4 * t < i) dstv[t] = *reinterpret_cast<const f32x4 *>(Ab + i * 16 + 4 * t);
+            };
+            load_row(1, rowv[1]);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                float part = arow[i][0] * xs[0] + arow[i][1] * xs[1] + arow[i][2] * xs[2]
-                           + arow[i][3] * xs[3];
-                part += dpp_f32<DPP_QUAD_XOR1>(part);
-                part += dpp_f32<DPP_QUAD_XOR2>(part);
-                const float xi = part + (i == jc ? 1.f : 0.f);
-                if (pq == (i & 3)) xs[i >> 2] = xi;
+                if (i + 1 < 16) load_row(i + 1, rowv[(i + 1) & 1]);
+                float acc = i == c ? 1.f : 0.f;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * t + e < i) acc += rowv[i & 1][t][e] * D[4 * t + e];
+                D[i] = acc;
             }
 #pragma unroll
-            for (int t = 0; t < 4; ++t) sT[(16 * wave + pq + 4 * t) * P_LD_A + 16 * wave + jc] = xs[t];
+            for (int i = 0; i < 16; ++i) sT[(16 * bb + i) * P_LD_A + 16 * bb + c] = D[i];
+        } else if (wave == 1) {
+            // the 16 x 16 blocks (0,1) and (2,3) of T are zero; the output reads them
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int e = lane + 64 * u;   // 128 four-float pieces
+                const int blk = e >> 6, row = (e >> 2) & 15, c4 = 4 * (e & 3);
+                *reinterpret_cast<f32x4 *>(sT + (32 * blk + row) * P_LD_A + 32 * blk + 16 + c4) = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         }
         lds_barrier();
 
@@ -412,51 +501,57 @@ chunk_prep_kernel(const bf16 *__restrict__ k, const float *__restrict__ g,
             lds_barrier();
         }
 
-        // ---- T_w = T diag(beta e^gamma), T_u = T diag(beta) -> workspace (bf16,
-        //      three 32 x 32 blocks each; 16-byte pieces, consecutive per thread) ----
-        bf16 *dst = ws + ((size_t)it.h * nslots + it.slot) * TWU_ELEMS;
+        // ---- -T diag(beta e^gamma) and T diag(beta) -> workspace as 16-byte
+        //      pieces (bf16), consecutive per thread. Piece order:
+        //        0..255     rows 32-63 of -T_w (8 per row)
+        //        256..511   rows 32-63 of T_u
+        //        512..639   rows 0-31 of -T_w, columns 0-31 (4 per row)
+        //        640..767   rows 0-31 of T_u, columns 0-31
+        //      followed by P (written above): rows 0-31 by keys 0-31, then
+        //      rows 32-63 by keys 0-63, row-major ----
 #pragma unroll
         for (int u = 0; u < 3; ++u) {
-            const int e = tid + P_NT * u;      // piece 0..767 (order in the chain pass's loads)
+            const int e = tid + P_NT * u;
             int mat, i, j0;
-            if (e < 512) {                     // rows 32-63, 8 pieces per row
+            if (e < 512) {
                 mat = e >= 256 ? 1 : 0;
                 const int pp = e - 256 * mat;
                 i = 32 + (pp >> 3);
                 j0 = 8 * (pp & 7);
-            } else {                           // rows 0-31, columns 0-31
+            } else {
                 mat = e >= 640 ? 1 : 0;
                 const int pp = e - 512 - 128 * mat;
                 i = pp >> 2;
                 j0 = 8 * (pp & 3);
             }
-            const float *sc = mat ? sBeta : sBeg;
-            const float sgn = mat ? 1.f : -1.f;   // T_w is stored negated
+            const float *sc = mat ? sBeta : sBegN;
             const f32x4 t0 = *reinterpret_cast<const f32x4 *>(sT + i * P_LD_A + j0);
             const f32x4 t1 = *reinterpret_cast<const f32x4 *>(sT + i * P_LD_A + j0 + 4);
             const f32x4 s0 = *reinterpret_cast<const f32x4 *>(sc + j0);
             const f32x4 s1 = *reinterpret_cast<const f32x4 *>(sc + j0 + 4);
-            // the 16 x 16 blocks above the diagonal of T are zero (not stored in sT)
-            const bool zero = (j0 >> 4) > (i >> 4);
             bf16x8 out;
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
-                out[e2] = (bf16)(zero ? 0.f : sgn * t0[e2] * s0[e2]);
-                out[e2 + 4] = (bf16)(zero ? 0.f : sgn * t1[e2] * s1[e2]);
+                out[e2] = (bf16)(t0[e2] * s0[e2]);
+                out[e2 + 4] = (bf16)(t1[e2] * s1[e2]);
             }
             *reinterpret_cast<bf16x8 *>(dst + 8 * e) = out;
         }
         lds_barrier();                         // T and the scalars read before the next item
     };
 
-    // one register set: each step stages it into LDS before refilling it
-    PrepItem it = prep_locate(cu_seqlens, (int)blockIdx.x, nitems, T, H, N);
+    // one register set: each step stages it into LDS before refilling it; the
+    // item after next is located while the current one is computed
+    const int first = (int)blockIdx.x;
+    PrepItem it = prep_locate(cu_seqlens, first, nitems, T, H, N);
+    PrepItem nit = prep_locate(cu_seqlens, first + stride, nitems, T, H, N);
     Pre pre;
     fetch(it, pre);
-    for (int item = (int)blockIdx.x; item < nitems; item += stride) {
-        const PrepItem nit = prep_locate(cu_seqlens, item + stride, nitems, T, H, N);
-        item_step(it, pre, nit, pre);
+    for (int item = first; item < nitems; item += stride) {
+        PrepItem ait;
+        item_step(it, pre, nit, pre, item + 2 * stride, ait);
         it = nit;
+        nit = ait;
     }
 }
 
@@ -477,17 +572,17 @@ chunk_prep_kernel(const bf16 *__restrict__ k, const float *__restrict__ g,
 // K^T for the update transposed on read). Grouping T_w K S^T as T_w (K S^T)
 // means W = T_w K is never formed.
 // Waves 2 and 3 form the output for the same column halves,
-// O^T = (S Q^T) diag(e^gamma) + Delta^T P^T, the second term one chunk later;
-// waves 4-7 form P = lower_incl_diag(Q K^T * Gamma), one query row of 16x16
-// tiles each. Waves 2-7 also stage the next chunk.
+// O^T = (S Q^T) diag(e^gamma) + Delta^T P^T, the second term one chunk later,
+// with P = lower_incl_diag(Q K^T * Gamma) from the prep pass. Waves 4-7 stage
+// the next chunk; waves 4 and 5 also stage P.
 //
 // Iteration c (buffers b = c % 2):
 //   waves 0-1  recurrence step of chunk c: reads staging b, writes Delta^T
 //              into copy b and the new bf16 S into copy (c + 1) % 2
 //   waves 2-3  S Q^T of chunk c (S copy b, staging b); finish chunk c - 1
 //              (Delta^T and P copies (c - 1) % 2) and store its output rows
-//   waves 4-7  P of chunk c into copy b
-//   waves 2-7  store chunk c + 1 (in registers since iteration c - 2) into
+//   waves 4-5  P of chunk c (in registers since iteration c - 2) into copy b
+//   waves 4-7  store chunk c + 1 (in registers since iteration c - 2) into
 //              staging (c + 1) % 2, load chunk c + 3 into the registers
 //   barrier
 // Tokens past the end of a sequence are identity steps (q = k = v = 0,
@@ -524,7 +619,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     seq_bounds(cu_seqlens, n, T, bos, eos);
     const int len = (int)(eos - bos);
     const int nchunks = (len + C - 1) / C;
-    const bf16 *wsh = ws + ((size_t)h * nslots + (size_t)((bos >> 6) + n)) * TWU_ELEMS;
+    const bf16 *wsh = ws + ((size_t)h * nslots + (size_t)((bos >> 6) + n)) * ITEM_ELEMS;
     const size_t sbase = ((size_t)n * H + h) * DV * DK;
     const int lane0 = tid0 & 63;
 
@@ -551,19 +646,15 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             *reinterpret_cast<bf16x4 *>(cpS(0) + (16 * wave + m) * LD_R + ((32 * (d >> 1) + 8 * qq + 4 * (d & 1)) ^ swz(lane0))) = x;
         }
     }
-    // P's 16 x 16 tiles (0, 1) and (2, 3) lie above the diagonal but inside the
-    // 32-key k-steps of the output product: both copies zeroed once, never
-    // written again. (The upper-right 32 x 32 blocks of T_w and T_u are never read.)
-    for (int e = tid0; e < 2 * SZ_P / 16; e += NT) reinterpret_cast<bf16x8 *>(cpP(0))[e] = bf16x8{};
 
-    // ---- loads of one chunk into registers, by waves 2-7, eight 16-byte buffer
-    //      loads per lane (address pattern A for r < 4, B for r >= 4, plus
-    //      per-load constants):
-    //        waves 2-3  Q rows 32 (w-2) + lane/16 + 4 r, columns 8 (lane%16) ..
-    //        waves 4-5  K rows, the same
-    //        wave 6     V rows lane/4 + 16 r (r < 4), 8 columns of this tile;
-    //                   workspace pieces 64 (r-4) + lane (r >= 4)
-    //        wave 7     workspace pieces 256 + 64 r + lane, and g of token lane
+    // ---- loads of one chunk into registers, by waves 4-7 (wi = wave - 4), as
+    //      16-byte buffer loads per lane:
+    //        b[0..7]  Q (wi 0, 1) or K (wi 2, 3) rows 32 (wi % 2) + lane/16 + 4 r,
+    //                 columns 8 (lane % 16) ..
+    //        t[0..2]  workspace pieces 192 wi + 64 r + lane of -T_w, T_u
+    //        v[0..1]  (wi 2, 3) V rows lane/4 + 16 (2 (wi - 2) + r), 8 columns of
+    //                 this tile
+    //        g        (wi 3) g of token lane
     //      A buffer resource per chunk spans the chunk's tokens inside the
     //      sequence only: loads past its end read as zero, which turns tokens
     //      past the end into identity steps with no clamping or masking.
@@ -571,82 +662,85 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     //      per row), 256..511 rows 32-63 of T_u, 512..639 rows 0-31 of -T_w (4
     //      per row: columns 0-31), 640..767 rows 0-31 of T_u. ----
     const int tstride = H * DK;                // elements between tokens
-    const int lrole = wave <= 3 ? 0 : wave <= 5 ? 1 : wave;    // 0 Q, 1 K, 6, 7
-    const int half = (wave - 2) & 1;                          // Q/K: rows 32 half ..
-    const int qkrow = 32 * half + (lane0 >> 4), qkcol = 8 * (lane0 & 15);
-    int goffA, goffB;
-    if (lrole <= 1) {
-        goffA = goffB = 2 * (qkrow * tstride + qkcol);
-    } else if (lrole == 6) {
-        goffA = 2 * ((lane0 >> 2) * tstride + 8 * (lane0 & 3));
-        goffB = 16 * lane0;
-    } else {
-        goffA = goffB = 16 * lane0;
-    }
-    auto gconst = [&](int r) -> int {
-        if (lrole <= 1) return r * 4 * tstride * 2;
-        if (lrole == 6) return r < 4 ? r * 16 * tstride * 2 : (r - 4) * 1024;
-        return r < 4 ? 4096 + r * 1024 : 8192 + (r - 4) * 1024;
+    const int wi = wave - 4;
+    const int qkmat = wi >> 1;                 // 0 Q, 1 K
+    const int qkrow = 32 * (wi & 1) + (lane0 >> 4), qkcol = 8 * (lane0 & 15);
+    const int goffQK = 2 * (qkrow * tstride + qkcol);
+    const int goffV = 2 * ((lane0 >> 2) * tstride + 8 * (lane0 & 3));
+    const int vr0 = 2 * (wi - 2);              // first V row group (wi 2, 3)
+    // LDS element offset of workspace piece e within a staging buffer (uniform
+    // per 64-piece group)
+    auto tpiece_loff = [&](int e) {
+        return e < 512 ? B_TL / 2 + (e >> 3) * LD_L + 8 * (e & 7)
+                       : B_TH / 2 + ((e - 512) >> 2) * LD_H + 8 * (e & 3);
     };
-    // LDS element offset of load r within a staging buffer
-    auto loff = [&](int r) -> int {
-        if (lrole <= 1) return (lrole == 0 ? B_Q : B_K) / 2 + (qkrow + 4 * r) * LD_R + qkcol;
-        if (lrole == 6)
-            return r < 4 ? B_V / 2 + ((lane0 >> 2) + 16 * r) * LD_H + 8 * (lane0 & 3)
-                         : B_TL / 2 + ((lane0 >> 3) + 8 * (r - 4)) * LD_L + 8 * (lane0 & 7);
-        return r < 4 ? B_TL / 2 + (32 + (lane0 >> 3) + 8 * r) * LD_L + 8 * (lane0 & 7)
-                     : B_TH / 2 + ((lane0 >> 2) + 16 * (r - 4)) * LD_H + 8 * (lane0 & 3);
-    };
-    const bf16 *qkv_head[3] = {q + (size_t)bos * tstride + (size_t)h * DK,
-                               k + (size_t)bos * tstride + (size_t)h * DK,
-                               v + (size_t)bos * tstride + (size_t)h * DV + cbase};
+    const bf16 *qk_head = (qkmat ? k : q) + (size_t)bos * tstride + (size_t)h * DK;
+    const bf16 *v_head = v + (size_t)bos * tstride + (size_t)h * DV + cbase;
     const float *g_head = g + (size_t)bos * H + h;
     // Two register sets: chunk c is loaded into set c % 2 three iterations
     // before its use and stored to LDS one iteration before.
     struct Pref {
-        bf16x8 b[8];
+        bf16x8 b[8], t[3], v[2];
         float g;
     };
     Pref pA, pB;
-    // WG: whether this wave loads and scans g (wave 7 only; a compile-time
-    // flag, so that no loop holds a load it may not need)
-    auto fetch = [&](int ch, Pref &rs, auto WG) {
+    // WG: whether this wave loads and scans g, WV: whether it loads V
+    // (compile-time flags, so that no loop holds a load it may not need)
+    auto fetch = [&](int ch, Pref &rs, auto WG, auto WV) {
         const int base = ch * C;
         const int nrow = len - base < C ? len - base : C;      // tokens of the chunk in the sequence
-        const bf16 *pa = lrole <= 1 ? qkv_head[lrole] + (size_t)base * tstride
-                       : lrole == 6 ? qkv_head[2] + (size_t)base * tstride
-                                    : wsh + (size_t)ch * TWU_ELEMS;
-        const unsigned na = lrole == 7 ? (unsigned)(TWU_ELEMS * 2) : (unsigned)nrow * tstride * 2;
-        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void *)pa, 0, na, 0x00020000);
-        const __amdgpu_buffer_rsrc_t rw =
-            __builtin_amdgcn_make_buffer_rsrc((void *)(wsh + (size_t)ch * TWU_ELEMS), 0, TWU_ELEMS * 2, 0x00020000);
-        const __amdgpu_buffer_rsrc_t rbq = lrole == 6 ? rw : ra;
+        const unsigned nb = (unsigned)nrow * tstride * 2;
+        const __amdgpu_buffer_rsrc_t rqk = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(qk_head + (size_t)base * tstride), 0, nb, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(wsh + (size_t)ch * ITEM_ELEMS), 0, WS_TWU * 16, 0x00020000);
 #pragma unroll
         for (int r = 0; r < 8; ++r)
             rs.b[r] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                          r < 4 ? ra : rbq, r < 4 ? goffA : goffB, gconst(r), 0));
+                          rqk, goffQK, r * 4 * tstride * 2, 0));
+#pragma unroll
+        for (int r = 0; r < 3; ++r)
+            rs.t[r] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                          rw, 16 * lane0, 16 * (192 * wi + 64 * r), 0));
+        if constexpr (decltype(WV)::value) {
+            const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(v_head + (size_t)base * tstride), 0, nb, 0x00020000);
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+                rs.v[r] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                              rv, goffV, (vr0 + r) * 16 * tstride * 2, 0));
+        }
         if constexpr (decltype(WG)::value) {
             const __amdgpu_buffer_rsrc_t rgs = __builtin_amdgcn_make_buffer_rsrc(
                 (void *)(g_head + (size_t)base * H), 0, (unsigned)nrow * H * 4, 0x00020000);
             rs.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rgs, 4 * H * lane0, 0, 0));
         }
     };
-    auto store = [&](const Pref &rs, int b, auto WG) {
+    auto store = [&](const Pref &rs, int b, auto WG, auto WV, int lane) {
         bf16 *buf = lds + (OFF_BUF + b * SZ_BUF) / 2;
+        const int lrow = (qkmat ? B_K : B_Q) / 2 + (32 * (wi & 1) + (lane >> 4)) * LD_R + 8 * (lane & 15);
 #pragma unroll
-        for (int r = 0; r < 8; ++r) *reinterpret_cast<bf16x8 *>(buf + loff(r)) = rs.b[r];
+        for (int r = 0; r < 8; ++r) *reinterpret_cast<bf16x8 *>(buf + lrow + 4 * r * LD_R) = rs.b[r];
+#pragma unroll
+        for (int r = 0; r < 3; ++r)
+            *reinterpret_cast<bf16x8 *>(buf + tpiece_loff(192 * wi + 64 * r + lane)) = rs.t[r];
+        if constexpr (decltype(WV)::value) {
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+                *reinterpret_cast<bf16x8 *>(buf + B_V / 2 + ((lane >> 2) + 16 * (vr0 + r)) * LD_H + 8 * (lane & 3)) = rs.v[r];
+        }
         if constexpr (decltype(WG)::value) {
             float *sc = stSc(b);
             const float gam = wave_inclusive_scan(rs.g);
             const float glast = __builtin_bit_cast(
                 float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gam), 63));
-            sc[lane0] = gam;
-            sc[C + lane0] = __expf(gam);
-            sc[2 * C + lane0] = __expf(glast - gam);
+            sc[lane] = gam;
+            sc[C + lane] = __expf(gam);
+            sc[2 * C + lane] = __expf(glast - gam);
         }
     };
-    const std::true_type with_g{};
-    const std::false_type no_g{};
+    const std::true_type with_g{}, with_v{}, with_p{};
+    const std::false_type no_g{}, no_v{}, no_p{};
 
     // Each wave role runs its own loop, unrolled by two from the odd chunk -3
     // so that every buffer and register-set index is a compile-time constant:
@@ -783,7 +877,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             lds_barrier();
         }
     } else if (wave < 4) {
-        // ============ waves 2-3: the output for d_v rows 16 hv .., then loads ============
+        // ============ waves 2-3: the output for d_v rows 16 hv .. ============
         const int hv = wave - 2;
         f32x4 oacc[2][4];                  // by chunk parity: O^T tiles (16 d_v x 16 tokens)
         for (int ch0 = -3; ch0 <= nchunks; ch0 += 2)
@@ -791,7 +885,6 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         for (int hf = 0; hf < 2; ++hf) {
             const int ch = ch0 + hf;
             const int b = 1 - hf;              // ch % 2; (ch + 1) % 2 = (ch - 1) % 2 = hf
-            Pref &ps = hf ? pB : pA;
             int tidl = tid0;
             asm volatile("" : "+v"(tidl));
             const int lane = tidl & 63, m = lane & 15, qq = lane >> 4;
@@ -848,66 +941,60 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                     }
                 }
             }
-            if (ch + 1 >= 0 && ch + 1 < nchunks) store(ps, hf, no_g);   // chunk ch + 1
-            fetch(ch + 3 < nchunks ? ch + 3 : nchunks - 1, ps, no_g);
             lds_barrier();
         }
     } else {
-        // ============ waves 4-7: P (one query row each), then loads ============
-        auto ploop = [&](auto WG) {
+        // ============ waves 4-7: staging; waves 4-5 also stage P ============
+        // P pieces 192 (wave - 4) + 64 r + lane (r < 3) of the workspace item,
+        // held in one of two register sets by chunk parity: chunk c's pieces
+        // are loaded in iteration c - 2 and written into P copy c % 2 in
+        // iteration c (the output waves read that copy in iteration c + 1).
+        // P copy layout: rows 0-31 (columns 0-31) at row stride LD_H, rows
+        // 32-63 at LD_L, 16-byte column groups swapped as for the other
+        // accumulator-order tiles.
+        const int pe0 = 192 * (wave - 4);
+        auto pfetch = [&](int ch, bf16x8 (&pr)[3]) {
+            const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(wsh + (size_t)ch * ITEM_ELEMS + 8 * WS_TWU), 0, WS_P * 16, 0x00020000);
+#pragma unroll
+            for (int r = 0; r < 3; ++r)
+                pr[r] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                            rp, 16 * (pe0 + lane0), 1024 * r, 0));
+        };
+        auto pstore = [&](const bf16x8 (&pr)[3], bf16 *sP, int lane) {
+#pragma unroll
+            for (int r = 0; r < 3; ++r) {
+                const int e = pe0 + 64 * r + lane;
+                const int row = e < 128 ? e >> 2 : (e - 128) >> 3;
+                const int grp = e < 128 ? e & 3 : (e - 128) & 7;
+                const int off = e < 128 ? row * LD_H : SZ_PH / 2 + row * LD_L;
+                *reinterpret_cast<bf16x8 *>(sP + off + 8 * (grp ^ ((row & 15) >> 2))) = pr[r];
+            }
+        };
+        auto lloop = [&](auto WG, auto WV, auto WP) {
+            bf16x8 pp[2][3];
             for (int ch0 = -3; ch0 <= nchunks; ch0 += 2)
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 const int ch = ch0 + hf;
-                const int b = 1 - hf;
+                const int b = 1 - hf;          // ch % 2
                 Pref &ps = hf ? pB : pA;
                 int tidl = tid0;
                 asm volatile("" : "+v"(tidl));
-                const int lane = tidl & 63, m = lane & 15, qq = lane >> 4;
-                if (ch >= 0 && ch < nchunks) {
-                    // P^T tiles (keys 16 J.., queries 16 I..) for J <= I, at most three
-                    // per wave: wave 6 (3, 0..2), wave 7 (2, 0..2), wave 4 (1, 0..1),
-                    // wave 5 (3, 3) and (0, 0); a query row's Q fragments are loaded once
-                    const bf16 *sQ = stQ(b), *sK = stK(b);
-                    const float *sGam = stSc(b);
-                    bf16 *sP = cpP(b);
-                    const int I0 = wave == 6 ? 3 : wave == 7 ? 2 : wave == 4 ? 1 : 3;
-                    const int ntile = wave == 6 || wave == 7 ? 3 : 2;
-                    bf16x8 fq[4];
-                    for (int u = 0; u < ntile; ++u) {
-                        const int I = wave == 5 && u == 1 ? 0 : I0;
-                        const int J = wave == 5 ? I : u;
-                        if (u == 0 || I != I0) {
-#pragma unroll
-                            for (int s2 = 0; s2 < 4; ++s2) fq[s2] = lds8(sQ, (16 * I + m) * LD_R + 32 * s2 + 8 * qq);
-                        }
-                        const int i = 16 * I + m;
-                        const float gi = sGam[i];
-                        bf16x8 fk[4];
-#pragma unroll
-                        for (int s2 = 0; s2 < 4; ++s2) fk[s2] = lds8(sK, (16 * J + m) * LD_R + 32 * s2 + 8 * qq);
-                        __builtin_amdgcn_sched_barrier(0);
-                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int s2 = 0; s2 < 4; ++s2) acc = mfma16(fk[s2], fq[s2], acc);
-                        // acc[r] = q_i . k_j with i = 16 I + m, j = 16 J + 4 qq + r
-                        const int j0 = 16 * J + 4 * qq;
-                        const f32x4 gj = *reinterpret_cast<const f32x4 *>(sGam + j0);
-                        bf16x4 x;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            x[r] = (bf16)(j0 + r <= i ? acc[r] * __expf(gi - gj[r]) : 0.f);
-                        bf16 *dst = I < 2 ? sP + i * LD_H : sP + SZ_PH / 2 + (i - 32) * LD_L;
-                        *reinterpret_cast<bf16x4 *>(dst + (j0 ^ swz(lane))) = x;
-                    }
+                const int lane = tidl & 63;
+                if constexpr (decltype(WP)::value) {
+                    if (ch >= 0 && ch < nchunks) pstore(pp[b], cpP(b), lane);
+                    const int cf = ch + 2 < 0 ? 0 : ch + 2 < nchunks ? ch + 2 : nchunks - 1;
+                    pfetch(cf, pp[b]);
                 }
-                if (ch + 1 >= 0 && ch + 1 < nchunks) store(ps, hf, WG);   // chunk ch + 1
-                fetch(ch + 3 < nchunks ? ch + 3 : nchunks - 1, ps, WG);
+                if (ch + 1 >= 0 && ch + 1 < nchunks) store(ps, hf, WG, WV, lane);   // chunk ch + 1
+                fetch(ch + 3 < nchunks ? ch + 3 : nchunks - 1, ps, WG, WV);
                 lds_barrier();
             }
         };
-        if (wave == 7) ploop(with_g);
-        else ploop(no_g);
+        if (wave == 7) lloop(with_g, with_v, no_p);
+        else if (wave == 6) lloop(no_g, with_v, no_p);
+        else lloop(no_g, no_v, with_p);
     }
     if (s_final && wave < 2) {
         const int m = lane0 & 15, qq = lane0 >> 4;
@@ -921,10 +1008,10 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 // sequences of H heads.
 size_t prefill_split_workspace_bytes(long tokens, int H, int N) {
     const long nslots = tokens / C + N + 1;
-    return (size_t)nslots * H * TWU_ELEMS * sizeof(bf16);
+    return (size_t)nslots * H * ITEM_ELEMS * sizeof(bf16);
 }
 
-hipError_t launch_prefill_prepare(const void *k, const float *g, const float *beta,
+hipError_t launch_prefill_prepare(const void *q, const void *k, const float *g, const float *beta,
                                   const int32_t *cu, int T, int H, int N, void *ws,
                                   hipStream_t stream)
 {
@@ -947,8 +1034,8 @@ hipError_t launch_prefill_prepare(const void *k, const float *g, const float *be
     const long nitems = nslots * H;
     const long fill = (long)per_cu * cus;
     dim3 grid((unsigned)(nitems < fill ? nitems : fill)), block(P_NT);
-    hipLaunchKernelGGL(chunk_prep_kernel, grid, block, P_LDS_BYTES, stream, (const bf16 *)k, g,
-                       beta, cu, (bf16 *)ws, T, H, N, (int)nslots);
+    hipLaunchKernelGGL(chunk_prep_kernel, grid, block, P_LDS_BYTES, stream, (const bf16 *)q,
+                       (const bf16 *)k, g, beta, cu, (bf16 *)ws, T, H, N, (int)nslots);
     return hipGetLastError();
 }
 

@@ -134,7 +134,7 @@ int gdn_prefill(const void *q, const void *k, const void *v,
  * gdn_prefill_workspace_size - bytes of workspace that gdn_prefill uses for
  * these sizes (same meaning as there; varlen != 0 when cu_seqlens will be
  * non-NULL). 0 when the path for these sizes uses none. The size depends on
- * the token count and the number of heads only, not on the offsets: 12 KiB
+ * the token count and the number of heads only, not on the offsets: 18 KiB
  * per (64-token chunk slot, head), with (B*T)/64 + N + 1 slots. Written to
  * *bytes; returns GDN_OK or the error gdn_prefill would return for these
  * sizes.
@@ -146,15 +146,16 @@ int gdn_prefill_workspace_size(int B, int T, int H, int d_k, int d_v, int N,
  * gdn_prefill_prepare, gdn_prefill_apply - the two passes of gdn_prefill's
  * workspace path as separate calls; gdn_prefill with a workspace is exactly
  * prepare followed by apply on one stream. Arguments have the meaning they
- * have for gdn_prefill; both calls must see the same sizes, cu_seqlens, k
- * and g. Only the MFMA chunk path has passes (bf16, d_k = d_v = 128; else
+ * have for gdn_prefill; both calls must see the same sizes, cu_seqlens, q,
+ * k and g. Only the MFMA chunk path has passes (bf16, d_k = d_v = 128; else
  * GDN_ERR_UNSUPPORTED), and workspace is required (GDN_ERR_NULL).
  *
- * prepare reads k, g, beta and writes, for every 64-token chunk of every
- * head, the chunk's T diag(beta e^gamma) and T diag(beta) into the workspace
- * (T the inverse of the unit-lower-triangular key Gram system, gamma the
- * in-chunk prefix sum of g: "5. Linear Attention" chapter, section "Chunk
- * implementation of the Delta Rule", stage 1). All chunks are independent.
+ * prepare reads q, k, g, beta and writes, for every 64-token chunk of every
+ * head, the chunk's T diag(beta e^gamma) and T diag(beta) (T the inverse of
+ * the unit-lower-triangular key Gram system, gamma the in-chunk prefix sum
+ * of g: "5. Linear Attention" chapter, section "Chunk implementation of the
+ * Delta Rule", stage 1) and its decayed intra-chunk attention matrix
+ * lower(Q K^T * Gamma) into the workspace. All chunks are independent.
  *
  * apply reads q, k, v, g and the workspace, walks each sequence's chunks in
  * order carrying the state, and writes o and final_state (stages 2-3 of the
@@ -163,7 +164,7 @@ int gdn_prefill_workspace_size(int B, int T, int H, int d_k, int d_v, int N,
  * Splitting lets a caller overlap prepare of one batch with apply of
  * another on two streams (with two workspaces).
  */
-int gdn_prefill_prepare(const void *k, const float *g, const float *beta,
+int gdn_prefill_prepare(const void *q, const void *k, const float *g, const float *beta,
                         const int32_t *cu_seqlens,
                         int B, int T, int H, int d_k, int d_v, int N, int dtype,
                         void *workspace, size_t workspace_bytes, void *stream);

@@ -68,11 +68,11 @@ def _ws_size(lib, B=1, T=8, H=1, dk=128, dv=128, N=1, varlen=0, dtype=1):
 
 
 def test_workspace_size(lib):
-    # 12 KiB of bf16 T diag(beta e^gamma), T diag(beta) per (chunk slot, head);
-    # (tokens / 64 + N + 1) slots
-    assert _ws_size(lib, B=4, T=4096, H=16, N=4) == (GDN_OK, (4 * 4096 // 64 + 5) * 16 * 12288)
-    assert _ws_size(lib, B=1, T=1000, H=3, N=7, varlen=1) == (GDN_OK, (1000 // 64 + 8) * 3 * 12288)
-    assert _ws_size(lib, B=2, T=0, H=2, N=2) == (GDN_OK, 3 * 2 * 12288)
+    # 18 KiB of bf16 T diag(beta e^gamma), T diag(beta) (12 KiB) and the chunk's
+    # attention matrix (6 KiB) per (chunk slot, head); (tokens / 64 + N + 1) slots
+    assert _ws_size(lib, B=4, T=4096, H=16, N=4) == (GDN_OK, (4 * 4096 // 64 + 5) * 16 * 18432)
+    assert _ws_size(lib, B=1, T=1000, H=3, N=7, varlen=1) == (GDN_OK, (1000 // 64 + 8) * 3 * 18432)
+    assert _ws_size(lib, B=2, T=0, H=2, N=2) == (GDN_OK, 3 * 2 * 18432)
     # paths that use no workspace
     assert _ws_size(lib, dtype=0) == (GDN_OK, 0)
     assert _ws_size(lib, dk=64, dv=64) == (GDN_OK, 0)
@@ -151,13 +151,14 @@ def test_prepare_apply_validation(lib):
     ws = ctypes.c_void_p(1 << 20)            # never dereferenced: rejected before launch
     prep, app = lib.gdn_prefill_prepare, lib.gdn_prefill_apply
     # only the MFMA chunk path has two passes
-    assert prep(P, P, P, None, 1, 100, 1, 64, 64, 1, 1, ws, need, None) == GDN_ERR_UNSUPPORTED
-    assert prep(P, P, P, None, 1, 100, 1, 128, 128, 1, 0, ws, need, None) == GDN_ERR_UNSUPPORTED
+    assert prep(P, P, P, P, None, 1, 100, 1, 64, 64, 1, 1, ws, need, None) == GDN_ERR_UNSUPPORTED
+    assert prep(P, P, P, P, None, 1, 100, 1, 128, 128, 1, 0, ws, need, None) == GDN_ERR_UNSUPPORTED
     # the workspace is required and checked
-    assert prep(P, P, P, None, 1, 100, 1, 128, 128, 1, 1, None, 0, None) == GDN_ERR_NULL
-    assert prep(P, P, P, None, 1, 100, 1, 128, 128, 1, 1, ws, need - 1, None) == GDN_ERR_WORKSPACE
-    assert prep(None, P, P, None, 1, 100, 1, 128, 128, 1, 1, ws, need, None) == GDN_ERR_NULL
-    assert prep(P, P, P, None, 2, 100, 1, 128, 128, 1, 1, ws, need, None) == GDN_ERR_SHAPE
+    assert prep(P, P, P, P, None, 1, 100, 1, 128, 128, 1, 1, None, 0, None) == GDN_ERR_NULL
+    assert prep(P, P, P, P, None, 1, 100, 1, 128, 128, 1, 1, ws, need - 1, None) == GDN_ERR_WORKSPACE
+    assert prep(None, P, P, P, None, 1, 100, 1, 128, 128, 1, 1, ws, need, None) == GDN_ERR_NULL
+    assert prep(P, None, P, P, None, 1, 100, 1, 128, 128, 1, 1, ws, need, None) == GDN_ERR_NULL
+    assert prep(P, P, P, P, None, 2, 100, 1, 128, 128, 1, 1, ws, need, None) == GDN_ERR_SHAPE
     a = [P] * 3 + [P, None, None, P, None]
     assert app(*a, 1, 100, 1, 128, 128, 1, 1.0, 1, None, 0, None) == GDN_ERR_NULL
     assert app(*a, 1, 100, 1, 128, 128, 1, 1.0, 1, ws, need - 1, None) == GDN_ERR_WORKSPACE

@@ -342,7 +342,7 @@ def test_prepare_then_apply_equals_prefill():
                                                     torch.bfloat16),
                      dtype=torch.uint8, device="cuda:0")
     q, k, v, g, beta, s0, cu = (dev(x) for x in (c.q, c.k, c.v, c.g, c.beta, c.s0, c.cu_seqlens))
-    gdn.gdn_prefill_prepare(k, g, beta, ws, cu_seqlens=cu)
+    gdn.gdn_prefill_prepare(q, k, g, beta, ws, cu_seqlens=cu)
     fin = torch.empty_like(s0)
     o, _ = gdn.gdn_prefill_apply(q, k, v, g, ws, s0, fin, cu_seqlens=cu, scale=c.scale)
     o_ref, f_ref = run_prefill(c, path="two_pass")
