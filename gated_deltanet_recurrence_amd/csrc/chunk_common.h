@@ -181,5 +181,41 @@ __device__ __forceinline__ bool pair_tile(int wid, int npairs, int &pair, int &t
     return pair < npairs;
 }
 
+// Longest-first dispatch of packed sequences. Workgroups start in index
+// order, so when the pairs of the longest sequences take the lowest indices
+// the short ones fill in behind them (list scheduling, longest processing
+// time first) instead of a long chain starting last. seq_of_rank returns the
+// sequence of rank r in the order by length, longest first, ties by index.
+// Every thread of the workgroup calls it (it holds one barrier); lens is LDS
+// scratch for RANK_MAX ints that no wave writes again before the caller's
+// next barrier. Costs N * ceil(N / 64) LDS broadcast reads per wave; above
+// RANK_MAX sequences the identity order is used instead.
+constexpr int RANK_MAX = 256;
+__device__ inline int seq_of_rank(const int32_t *cu, int N, int T, int r, int *lens)
+{
+    for (int n = (int)threadIdx.x; n < N; n += (int)blockDim.x) {
+        long a = cu[n], b = cu[n + 1];
+        a = a < 0 ? 0 : (a > T ? T : a);
+        b = b < a ? a : (b > T ? T : b);
+        lens[n] = (int)(b - a);
+    }
+    lds_barrier();
+    const int lane = (int)threadIdx.x & 63;
+    for (int j = 0; j < N; j += 64) {
+        const int nn = j + lane;
+        int rank = 0;
+        if (nn < N) {
+            const int ln = lens[nn];
+            for (int m = 0; m < N; ++m) {
+                const int lm = lens[m];
+                rank += (lm > ln) | ((lm == ln) & (m < nn));
+            }
+        }
+        const unsigned long long hit = __ballot(nn < N && rank == r);
+        if (hit) return j + __ffsll((long long)hit) - 1;
+    }
+    return r;                                  // not reached: ranks are a permutation
+}
+
 }  // namespace chunk
 }  // namespace gdn

@@ -612,7 +612,12 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
     int pair, tile;                          // (sequence, head) pair and d_v tile
     if (!pair_tile((int)blockIdx.x, npairs, pair, tile)) return;   // uniform
-    const int h = pair % H, n = pair / H;
+    // packed sequences are dealt longest first (staging buffer 0 is free
+    // until the loaders' first store, two barriers into the loop)
+    const int h = pair % H, nsq = npairs / H;
+    const int n = (cu_seqlens && nsq <= RANK_MAX)
+        ? seq_of_rank(cu_seqlens, nsq, T, pair / H, reinterpret_cast<int *>(smem + OFF_BUF))
+        : pair / H;
     const int cbase = tile * DVT;
 
     long bos, eos;
