@@ -33,13 +33,13 @@ _SIGS = {
     "gdn_version": [],
     "gdn_status_string": [_i],
     "gdn_check_cu_seqlens": [_vp, _i, _i],
-    "gdn_prefill": [_vp] * 9 + [_i] * 6 + [_f, _i, _vp, _sz, _vp],
+    "gdn_prefill": [_vp] * 9 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
     "gdn_prefill_workspace_size": [_i] * 8 + [_vp],
-    "gdn_prefill_prepare": [_vp] * 5 + [_i] * 7 + [_vp, _sz, _vp],
-    "gdn_prefill_apply": [_vp] * 8 + [_i] * 6 + [_f, _i, _vp, _sz, _vp],
-    "gdn_prefill_recurrent": [_vp] * 9 + [_i] * 6 + [_f, _i, _vp],
-    "gdn_decode_step": [_vp] * 7 + [_i] * 4 + [_f, _i, _vp],
-    "gdn_mixer_prologue": [_vp] * 14 + [_i] * 7 + [_vp],
+    "gdn_prefill_prepare": [_vp] * 5 + [_i] * 8 + [_vp, _sz, _vp],
+    "gdn_prefill_apply": [_vp] * 8 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
+    "gdn_prefill_recurrent": [_vp] * 9 + [_i] * 7 + [_f, _i, _vp],
+    "gdn_decode_step": [_vp] * 7 + [_i] * 5 + [_f, _i, _vp],
+    "gdn_mixer_prologue": [_vp] * 14 + [_i] * 8 + [_vp],
     "gdn_mixer_epilogue": [_vp] * 4 + [_i] * 3 + [_f, _i, _vp],
 }
 EXPORTED = tuple(_SIGS)
@@ -110,8 +110,8 @@ def gdn_prefill_workspace_size(B, T, H, d_k, d_v, N, varlen, dtype) -> int:
 
 def _prefill(entry, q, k, v, g, beta, initial_state=None, final_state=None, o=None,
              cu_seqlens=None, scale=None, workspace=None):
-    B, T, H, dk = q.shape
-    dv = v.shape[3]
+    B, T, Hk, dk = q.shape
+    H, dv = v.shape[2], v.shape[3]
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
     dt = q.dtype
     if o is None:
@@ -136,7 +136,7 @@ def _prefill(entry, q, k, v, g, beta, initial_state=None, final_state=None, o=No
             workspace = (torch.empty(nbytes, dtype=torch.uint8, device=q.device)
                          if nbytes else None)
         tail += list(_ws(workspace))
-    _check(getattr(load(), entry)(*args, B, T, H, dk, dv, N, *tail, _stream(q.device)))
+    _check(getattr(load(), entry)(*args, B, T, H, Hk, dk, dv, N, *tail, _stream(q.device)))
     return o, final_state
 
 
@@ -162,8 +162,9 @@ def _ws(workspace):
 def gdn_prefill_prepare(q, k, g, beta, workspace, cu_seqlens=None, d_v=None):
     """First pass of the workspace path (see include/gdn.h): T diag(beta e^gamma),
     T diag(beta) and the decayed intra-chunk attention of every chunk into
-    `workspace`."""
-    B, T, H, dk = k.shape
+    `workspace`. The value heads H are those of g and beta."""
+    B, T, Hk, dk = k.shape
+    H = g.shape[2]
     dv = dk if d_v is None else d_v
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
     if q.shape != k.shape or q.dtype != k.dtype:
@@ -172,15 +173,15 @@ def gdn_prefill_prepare(q, k, g, beta, workspace, cu_seqlens=None, d_v=None):
         _dev(q, "q"), _dev(k, "k"), _dev(g, "g", torch.float32, (B, T, H)),
         _dev(beta, "beta", torch.float32, (B, T, H)),
         _dev(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,)),
-        B, T, H, dk, dv, N, _dtype_code(k), *_ws(workspace), _stream(k.device)))
+        B, T, H, Hk, dk, dv, N, _dtype_code(k), *_ws(workspace), _stream(k.device)))
 
 
 def gdn_prefill_apply(q, k, v, g, workspace, initial_state=None, final_state=None, o=None,
                       cu_seqlens=None, scale=None):
     """Second pass of the workspace path: the state recurrence over chunks.
     Returns (o, final_state)."""
-    B, T, H, dk = q.shape
-    dv = v.shape[3]
+    B, T, Hk, dk = q.shape
+    H, dv = v.shape[2], v.shape[3]
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
     dt = q.dtype
     if o is None:
@@ -193,7 +194,8 @@ def gdn_prefill_apply(q, k, v, g, workspace, initial_state=None, final_state=Non
         _dev(initial_state, "initial_state", torch.float32, (N, H, dv, dk)),
         _dev(final_state, "final_state", torch.float32, (N, H, dv, dk)),
         _dev(o, "o", dt, (B, T, H, dv)), _dev(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,)),
-        B, T, H, dk, dv, N, float(scale), _dtype_code(q), *_ws(workspace), _stream(q.device)))
+        B, T, H, Hk, dk, dv, N, float(scale), _dtype_code(q), *_ws(workspace),
+        _stream(q.device)))
     return o, final_state
 
 
@@ -205,10 +207,10 @@ def gdn_prefill_recurrent(q, k, v, g, beta, initial_state=None, final_state=None
 
 
 def gdn_decode_step(q, k, v, g, beta, state, o=None, scale=None):
-    """One in-place recurrent step. q,k: [B,H,d_k]; v: [B,H,d_v]; g,beta: [B,H];
+    """One in-place recurrent step. q,k: [B,H_k,d_k]; v: [B,H,d_v]; g,beta: [B,H];
     state: [B,H,d_v,d_k] fp32 (updated). Returns o [B,H,d_v]."""
-    B, H, dk = q.shape
-    dv = v.shape[2]
+    B, Hk, dk = q.shape
+    H, dv = v.shape[1], v.shape[2]
     dt = q.dtype
     if o is None:
         o = torch.empty((B, H, dv), dtype=dt, device=q.device)
@@ -218,15 +220,16 @@ def gdn_decode_step(q, k, v, g, beta, state, o=None, scale=None):
         _dev(q, "q", dt), _dev(k, "k", dt, q.shape), _dev(v, "v", dt, (B, H, dv)),
         _dev(g, "g", torch.float32, (B, H)), _dev(beta, "beta", torch.float32, (B, H)),
         _dev(state, "state", torch.float32, (B, H, dv, dk)), _dev(o, "o", dt, (B, H, dv)),
-        B, H, dk, dv, float(scale), _dtype_code(q), _stream(q.device)))
+        B, H, Hk, dk, dv, float(scale), _dtype_code(q), _stream(q.device)))
     return o
 
 
 def gdn_mixer_prologue(q_raw, k_raw, v_raw, conv_w, a, b, A, dt_bias=None, cu_seqlens=None,
                        out=None):
-    """Conv+SiLU, L2-norm of q,k, gates. Returns (q, k, v, g, beta)."""
-    B, T, H, dk = q_raw.shape
-    dv = v_raw.shape[3]
+    """Conv+SiLU, L2-norm of q,k, gates. q_raw, k_raw: [B,T,H_k,d_k]; v_raw:
+    [B,T,H,d_v]; a, b: [B,T,H]. Returns (q, k, v, g, beta)."""
+    B, T, Hk, dk = q_raw.shape
+    H, dv = v_raw.shape[2], v_raw.shape[3]
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
     dt = q_raw.dtype
     if out is None:
@@ -237,14 +240,14 @@ def gdn_mixer_prologue(q_raw, k_raw, v_raw, conv_w, a, b, A, dt_bias=None, cu_se
     _check(load().gdn_mixer_prologue(
         _dev(q_raw, "q_raw", dt), _dev(k_raw, "k_raw", dt, q_raw.shape),
         _dev(v_raw, "v_raw", dt, (B, T, H, dv)),
-        _dev(conv_w, "conv_w", dt, (H * (2 * dk + dv), 4)),
+        _dev(conv_w, "conv_w", dt, (2 * Hk * dk + H * dv, 4)),
         _dev(a, "a", dt, (B, T, H)), _dev(b, "b", dt, (B, T, H)),
         _dev(A, "A", torch.float32, (H,)), _dev(dt_bias, "dt_bias", torch.float32, (H,)),
         _dev(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,)),
         _dev(q, "q", dt, q_raw.shape), _dev(k, "k", dt, q_raw.shape),
         _dev(v, "v", dt, (B, T, H, dv)), _dev(g, "g", torch.float32, (B, T, H)),
         _dev(beta, "beta", torch.float32, (B, T, H)),
-        B, T, H, dk, dv, N, _dtype_code(q_raw), _stream(q_raw.device)))
+        B, T, H, Hk, dk, dv, N, _dtype_code(q_raw), _stream(q_raw.device)))
     return q, k, v, g, beta
 
 

@@ -13,6 +13,10 @@
 // is one streaming pass: each state row is read once and written once, and
 // the only reductions run along d_k, inside a group of d_k/8 lanes, with DPP.
 //
+// Grouped heads: q and k have H_k heads, everything else H; value head h
+// reads query/key head h / (H / H_k) (the repeat_interleave head expansion of
+// the "Gated DeltaNet body" layer code, "5. Linear Attention").
+//
 // Work mapping: a row of d_k floats is owned by G = d_k/8 consecutive lanes;
 // lane j of the group holds columns [4j, 4j+4) and [d_k/2 + 4j, d_k/2 + 4j + 4),
 // so each 16-byte load instruction of a group covers one contiguous half row
@@ -34,7 +38,7 @@ __global__ void __launch_bounds__(DEC_NT)
 decode_step_kernel(const TIO *__restrict__ q, const TIO *__restrict__ k,
                    const TIO *__restrict__ v, const float *__restrict__ g,
                    const float *__restrict__ beta, float *__restrict__ state,
-                   TIO *__restrict__ o, int d_v, int wg_per_head, float scale)
+                   TIO *__restrict__ o, int grp, int d_v, int wg_per_head, float scale)
 {
     constexpr int G = DK / 8;                 // lanes per state row
     constexpr int RPW = DEC_NT / G;           // rows per workgroup
@@ -47,9 +51,13 @@ decode_step_kernel(const TIO *__restrict__ q, const TIO *__restrict__ k,
     float *rp = state + ((size_t)bh * d_v + row) * DK;
     const f32x4 s0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(rp + c0));
     const f32x4 s1 = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(rp + c1));
+    __builtin_amdgcn_sched_barrier(0);        // the state request goes out first
 
-    const TIO *qp = q + (size_t)bh * DK;
-    const TIO *kp = k + (size_t)bh * DK;
+    // grp = H / H_k value heads per query/key head; (b H + h) / grp = b H_k + h / grp
+    // is the query/key row of value head h
+    const int kbh = bh / grp;
+    const TIO *qp = q + (size_t)kbh * DK;
+    const TIO *kp = k + (size_t)kbh * DK;
     const f32x4 k0 = load4(kp + c0), k1 = load4(kp + c1);
     const f32x4 q0 = load4(qp + c0), q1 = load4(qp + c1);
     const float vv = to_f32(v[(size_t)bh * d_v + row]);
@@ -80,36 +88,36 @@ decode_step_kernel(const TIO *__restrict__ q, const TIO *__restrict__ k,
 template <int DK, typename TIO>
 static hipError_t launch_decode_dk(const void *q, const void *k, const void *v, const float *g,
                                    const float *beta, float *state, void *o, int B, int H,
-                                   int d_v, float scale, hipStream_t stream)
+                                   int Hk, int d_v, float scale, hipStream_t stream)
 {
     constexpr int RPW = DEC_NT / (DK / 8);
     const int wg_per_head = (d_v + RPW - 1) / RPW;
     dim3 grid((unsigned)((long)B * H * wg_per_head)), block(DEC_NT);
     hipLaunchKernelGGL((decode_step_kernel<DK, TIO>), grid, block, 0, stream,
                        (const TIO *)q, (const TIO *)k, (const TIO *)v, g, beta, state,
-                       (TIO *)o, d_v, wg_per_head, scale);
+                       (TIO *)o, H / Hk, d_v, wg_per_head, scale);
     return hipGetLastError();
 }
 
 template <typename TIO>
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *g,
-                         const float *beta, float *state, void *o, int B, int H, int d_k,
-                         int d_v, float scale, hipStream_t stream)
+                         const float *beta, float *state, void *o, int B, int H, int Hk,
+                         int d_k, int d_v, float scale, hipStream_t stream)
 {
     switch (d_k) {
-    case 16: return launch_decode_dk<16, TIO>(q, k, v, g, beta, state, o, B, H, d_v, scale, stream);
-    case 32: return launch_decode_dk<32, TIO>(q, k, v, g, beta, state, o, B, H, d_v, scale, stream);
-    case 64: return launch_decode_dk<64, TIO>(q, k, v, g, beta, state, o, B, H, d_v, scale, stream);
-    case 128: return launch_decode_dk<128, TIO>(q, k, v, g, beta, state, o, B, H, d_v, scale, stream);
+    case 16: return launch_decode_dk<16, TIO>(q, k, v, g, beta, state, o, B, H, Hk, d_v, scale, stream);
+    case 32: return launch_decode_dk<32, TIO>(q, k, v, g, beta, state, o, B, H, Hk, d_v, scale, stream);
+    case 64: return launch_decode_dk<64, TIO>(q, k, v, g, beta, state, o, B, H, Hk, d_v, scale, stream);
+    case 128: return launch_decode_dk<128, TIO>(q, k, v, g, beta, state, o, B, H, Hk, d_v, scale, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
 template hipError_t launch_decode<float>(const void *, const void *, const void *, const float *,
                                          const float *, float *, void *, int, int, int, int,
-                                         float, hipStream_t);
+                                         int, float, hipStream_t);
 template hipError_t launch_decode<bf16>(const void *, const void *, const void *, const float *,
                                         const float *, float *, void *, int, int, int, int,
-                                        float, hipStream_t);
+                                        int, float, hipStream_t);
 
 }  // namespace gdn

@@ -10,24 +10,25 @@
 namespace gdn {
 template <typename TIO>
 hipError_t launch_decode(const void *, const void *, const void *, const float *, const float *,
-                         float *, void *, int, int, int, int, float, hipStream_t);
+                         float *, void *, int, int, int, int, int, float, hipStream_t);
 template <typename TIO>
 hipError_t launch_prefill_recurrent(const void *, const void *, const void *, const float *,
                                     const float *, const float *, float *, void *,
-                                    const int32_t *, int, int, int, int, int, float, hipStream_t);
+                                    const int32_t *, int, int, int, int, int, int, float,
+                                    hipStream_t);
 hipError_t launch_prefill_chunk(const void *, const void *, const void *, const float *,
                                 const float *, const float *, float *, void *, const int32_t *,
-                                int, int, int, float, hipStream_t);
+                                int, int, int, int, float, hipStream_t);
 hipError_t launch_prefill_prepare(const void *, const void *, const float *, const float *,
-                                  const int32_t *, int, int, int, void *, hipStream_t);
+                                  const int32_t *, int, int, int, int, void *, hipStream_t);
 hipError_t launch_prefill_apply(const void *, const void *, const void *, const float *,
                                 const float *, float *, void *, const int32_t *, int, int, int,
-                                float, const void *, hipStream_t);
+                                int, float, const void *, hipStream_t);
 size_t prefill_split_workspace_bytes(long tokens, int H, int N);
 template <typename TIO>
 hipError_t launch_prologue(const void *, const void *, const void *, const void *, const void *,
                            const void *, const float *, const float *, const int32_t *, void *,
-                           void *, void *, float *, float *, int, int, int, int, int, int,
+                           void *, void *, float *, float *, int, int, int, int, int, int, int,
                            hipStream_t);
 template <typename TIO>
 hipError_t launch_epilogue(const void *, const void *, const float *, void *, long, int, float,
@@ -41,16 +42,21 @@ bool mixer_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128 || d ==
 bool valid_dtype(int dt) { return dt == GDN_DTYPE_F32 || dt == GDN_DTYPE_BF16; }
 int status_of(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
 
+// Value heads H, query/key heads H_k: each query/key head serves H / H_k
+// consecutive value heads.
+bool heads_ok(int H, int Hk) { return H >= 1 && Hk >= 1 && Hk <= H && H % Hk == 0; }
+
 // Shared validation of the prefill arguments.
 int check_prefill(const void *q, const void *k, const void *v, const float *g, const float *beta,
-                  const void *o, const int32_t *cu, int B, int T, int H, int d_k, int d_v, int N,
-                  int dtype)
+                  const void *o, const int32_t *cu, int B, int T, int H, int Hk, int d_k,
+                  int d_v, int N, int dtype)
 {
     // with no tokens at all the activation pointers are never dereferenced
     const bool no_tokens = (int64_t)B * T == 0;
     if (!no_tokens && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
     if (!valid_dtype(dtype)) return GDN_ERR_DTYPE;
     if (B < 1 || T < 0 || H < 1 || N < 1 || d_k < 1 || d_v < 1) return GDN_ERR_SHAPE;
+    if (!heads_ok(H, Hk)) return GDN_ERR_SHAPE;
     if (cu ? B != 1 : N != B) return GDN_ERR_SHAPE;
     if ((int64_t)B * T > (int64_t)INT32_MAX) return GDN_ERR_SHAPE;   // token index fits int32
     if (H > 65535 || N > 65535) return GDN_ERR_UNSUPPORTED;           // launch grid y / z
@@ -101,17 +107,17 @@ int gdn_check_cu_seqlens(const int32_t *cu, int N, int T)
 
 int gdn_prefill_recurrent(const void *q, const void *k, const void *v, const float *g,
                           const float *beta, const float *initial_state, float *final_state,
-                          void *o, const int32_t *cu_seqlens, int B, int T, int H, int d_k,
-                          int d_v, int N, float scale, int dtype, void *stream)
+                          void *o, const int32_t *cu_seqlens, int B, int T, int H, int H_k,
+                          int d_k, int d_v, int N, float scale, int dtype, void *stream)
 {
-    int st = check_prefill(q, k, v, g, beta, o, cu_seqlens, B, T, H, d_k, d_v, N, dtype);
+    int st = check_prefill(q, k, v, g, beta, o, cu_seqlens, B, T, H, H_k, d_k, d_v, N, dtype);
     if (st != GDN_OK) return st;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = dtype == GDN_DTYPE_BF16
         ? gdn::launch_prefill_recurrent<gdn::bf16>(q, k, v, g, beta, initial_state, final_state, o,
-                                                   cu_seqlens, T, H, d_k, d_v, N, scale, s)
+                                                   cu_seqlens, T, H, H_k, d_k, d_v, N, scale, s)
         : gdn::launch_prefill_recurrent<float>(q, k, v, g, beta, initial_state, final_state, o,
-                                               cu_seqlens, T, H, d_k, d_v, N, scale, s);
+                                               cu_seqlens, T, H, H_k, d_k, d_v, N, scale, s);
     return status_of(e);
 }
 
@@ -124,7 +130,7 @@ int gdn_prefill_workspace_size(int B, int T, int H, int d_k, int d_v, int N, int
     const int32_t *cu = varlen ? reinterpret_cast<const int32_t *>(bytes) : nullptr;
     const void *p = bytes;
     const int st = check_prefill(p, p, p, (const float *)p, (const float *)p, p, cu, B, T, H,
-                                 d_k, d_v, N, dtype);
+                                 H, d_k, d_v, N, dtype);
     if (st != GDN_OK) return st;
     if (chunk_path(dtype, d_k, d_v))
         *bytes = gdn::prefill_split_workspace_bytes((long)B * T, H, N);
@@ -133,96 +139,101 @@ int gdn_prefill_workspace_size(int B, int T, int H, int d_k, int d_v, int N, int
 
 int gdn_prefill(const void *q, const void *k, const void *v, const float *g, const float *beta,
                 const float *initial_state, float *final_state, void *o,
-                const int32_t *cu_seqlens, int B, int T, int H, int d_k, int d_v, int N,
-                float scale, int dtype, void *workspace, size_t workspace_bytes, void *stream)
+                const int32_t *cu_seqlens, int B, int T, int H, int H_k, int d_k, int d_v,
+                int N, float scale, int dtype, void *workspace, size_t workspace_bytes,
+                void *stream)
 {
-    int st = check_prefill(q, k, v, g, beta, o, cu_seqlens, B, T, H, d_k, d_v, N, dtype);
+    int st = check_prefill(q, k, v, g, beta, o, cu_seqlens, B, T, H, H_k, d_k, d_v, N, dtype);
     if (st != GDN_OK) return st;
     hipStream_t s = (hipStream_t)stream;
     if (chunk_path(dtype, d_k, d_v)) {
         if (!workspace)
             return status_of(gdn::launch_prefill_chunk(q, k, v, g, beta, initial_state,
-                                                       final_state, o, cu_seqlens, T, H, N,
-                                                       scale, s));
+                                                       final_state, o, cu_seqlens, T, H, H_k,
+                                                       N, scale, s));
         if (!workspace_ok(workspace, workspace_bytes, B, T, H, N)) return GDN_ERR_WORKSPACE;
-        hipError_t e = gdn::launch_prefill_prepare(q, k, g, beta, cu_seqlens, T, H, N, workspace, s);
+        hipError_t e = gdn::launch_prefill_prepare(q, k, g, beta, cu_seqlens, T, H, H_k, N,
+                                                   workspace, s);
         if (e == hipSuccess)
             e = gdn::launch_prefill_apply(q, k, v, g, initial_state, final_state, o, cu_seqlens,
-                                          T, H, N, scale, workspace, s);
+                                          T, H, H_k, N, scale, workspace, s);
         return status_of(e);
     }
     return gdn_prefill_recurrent(q, k, v, g, beta, initial_state, final_state, o, cu_seqlens, B,
-                                 T, H, d_k, d_v, N, scale, dtype, stream);
+                                 T, H, H_k, d_k, d_v, N, scale, dtype, stream);
 }
 
 int gdn_prefill_prepare(const void *q, const void *k, const float *g, const float *beta,
-                        const int32_t *cu_seqlens, int B, int T, int H, int d_k, int d_v, int N,
-                        int dtype, void *workspace, size_t workspace_bytes, void *stream)
+                        const int32_t *cu_seqlens, int B, int T, int H, int H_k, int d_k,
+                        int d_v, int N, int dtype, void *workspace, size_t workspace_bytes,
+                        void *stream)
 {
     // v and o are not arguments of this pass: validate with stand-ins
     const void *p = workspace ? workspace : (const void *)k;
-    int st = check_prefill(q, k, p, g, beta, p, cu_seqlens, B, T, H, d_k, d_v, N, dtype);
+    int st = check_prefill(q, k, p, g, beta, p, cu_seqlens, B, T, H, H_k, d_k, d_v, N, dtype);
     if (st != GDN_OK) return st;
     if (!chunk_path(dtype, d_k, d_v)) return GDN_ERR_UNSUPPORTED;
     if (!workspace) return GDN_ERR_NULL;
     if (!workspace_ok(workspace, workspace_bytes, B, T, H, N)) return GDN_ERR_WORKSPACE;
-    return status_of(gdn::launch_prefill_prepare(q, k, g, beta, cu_seqlens, T, H, N, workspace,
-                                                 (hipStream_t)stream));
+    return status_of(gdn::launch_prefill_prepare(q, k, g, beta, cu_seqlens, T, H, H_k, N,
+                                                 workspace, (hipStream_t)stream));
 }
 
 int gdn_prefill_apply(const void *q, const void *k, const void *v, const float *g,
                       const float *initial_state, float *final_state, void *o,
-                      const int32_t *cu_seqlens, int B, int T, int H, int d_k, int d_v, int N,
-                      float scale, int dtype, const void *workspace, size_t workspace_bytes,
-                      void *stream)
+                      const int32_t *cu_seqlens, int B, int T, int H, int H_k, int d_k,
+                      int d_v, int N, float scale, int dtype, const void *workspace,
+                      size_t workspace_bytes, void *stream)
 {
     // beta is folded into the workspace: validate with a stand-in
     const float *pb = workspace ? (const float *)workspace : g;
-    int st = check_prefill(q, k, v, g, pb, o, cu_seqlens, B, T, H, d_k, d_v, N, dtype);
+    int st = check_prefill(q, k, v, g, pb, o, cu_seqlens, B, T, H, H_k, d_k, d_v, N, dtype);
     if (st != GDN_OK) return st;
     if (!chunk_path(dtype, d_k, d_v)) return GDN_ERR_UNSUPPORTED;
     if (!workspace) return GDN_ERR_NULL;
     if (!workspace_ok(workspace, workspace_bytes, B, T, H, N)) return GDN_ERR_WORKSPACE;
     return status_of(gdn::launch_prefill_apply(q, k, v, g, initial_state, final_state, o,
-                                               cu_seqlens, T, H, N, scale, workspace,
+                                               cu_seqlens, T, H, H_k, N, scale, workspace,
                                                (hipStream_t)stream));
 }
 
 int gdn_decode_step(const void *q, const void *k, const void *v, const float *g,
-                    const float *beta, float *state, void *o, int B, int H, int d_k, int d_v,
-                    float scale, int dtype, void *stream)
+                    const float *beta, float *state, void *o, int B, int H, int H_k, int d_k,
+                    int d_v, float scale, int dtype, void *stream)
 {
     if (!q || !k || !v || !g || !beta || !state || !o) return GDN_ERR_NULL;
     if (!valid_dtype(dtype)) return GDN_ERR_DTYPE;
-    if (B < 1 || H < 1 || d_k < 1 || d_v < 1) return GDN_ERR_SHAPE;
+    if (B < 1 || H < 1 || d_k < 1 || d_v < 1 || !heads_ok(H, H_k)) return GDN_ERR_SHAPE;
     if ((int64_t)B * H > (int64_t)INT32_MAX) return GDN_ERR_SHAPE;
     if (!head_dim_pow2(d_k) || d_v > 4096) return GDN_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = dtype == GDN_DTYPE_BF16
-        ? gdn::launch_decode<gdn::bf16>(q, k, v, g, beta, state, o, B, H, d_k, d_v, scale, s)
-        : gdn::launch_decode<float>(q, k, v, g, beta, state, o, B, H, d_k, d_v, scale, s);
+        ? gdn::launch_decode<gdn::bf16>(q, k, v, g, beta, state, o, B, H, H_k, d_k, d_v, scale, s)
+        : gdn::launch_decode<float>(q, k, v, g, beta, state, o, B, H, H_k, d_k, d_v, scale, s);
     return status_of(e);
 }
 
 int gdn_mixer_prologue(const void *q_raw, const void *k_raw, const void *v_raw,
                        const void *conv_w, const void *a, const void *b, const float *A,
                        const float *dt_bias, const int32_t *cu_seqlens, void *q, void *k,
-                       void *v, float *g, float *beta, int B, int T, int H, int d_k, int d_v,
-                       int N, int dtype, void *stream)
+                       void *v, float *g, float *beta, int B, int T, int H, int H_k, int d_k,
+                       int d_v, int N, int dtype, void *stream)
 {
     if (!q_raw || !k_raw || !v_raw || !conv_w || !a || !b || !A || !q || !k || !v || !g || !beta)
         return GDN_ERR_NULL;
     if (!valid_dtype(dtype)) return GDN_ERR_DTYPE;
     if (B < 1 || T < 0 || H < 1 || N < 1 || d_k < 1 || d_v < 1) return GDN_ERR_SHAPE;
+    if (!heads_ok(H, H_k)) return GDN_ERR_SHAPE;
     if (cu_seqlens ? B != 1 : N != B) return GDN_ERR_SHAPE;
     if ((int64_t)B * T > (int64_t)INT32_MAX) return GDN_ERR_SHAPE;
+    if (H > 65535) return GDN_ERR_UNSUPPORTED;                        // launch grid y
     if (!mixer_dim(d_k) || !mixer_dim(d_v)) return GDN_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = dtype == GDN_DTYPE_BF16
         ? gdn::launch_prologue<gdn::bf16>(q_raw, k_raw, v_raw, conv_w, a, b, A, dt_bias, cu_seqlens,
-                                          q, k, v, g, beta, B, T, H, d_k, d_v, N, s)
+                                          q, k, v, g, beta, B, T, H, H_k, d_k, d_v, N, s)
         : gdn::launch_prologue<float>(q_raw, k_raw, v_raw, conv_w, a, b, A, dt_bias, cu_seqlens, q,
-                                      k, v, g, beta, B, T, H, d_k, d_v, N, s);
+                                      k, v, g, beta, B, T, H, H_k, d_k, d_v, N, s);
     return status_of(e);
 }
 

@@ -11,6 +11,11 @@
 //   6.6.3 (alpha = exp(-A * softplus(.)), beta = sigmoid(.)) and the l2norm
 //   of section 6.6.4 (eps 1e-6 added to the sum of squares).
 //
+// Grouped heads: q and k have H_k heads, v, z, the gates and the output H
+// (the conv channels are H_k d_k of q, H_k d_k of k, then H d_v of v, as the
+// layer code of "5. Linear Attention" orders them); the gates are per value
+// head and are computed by the v lane groups.
+//
 // Work mapping (both kernels): one (token, head) row of D channels is owned
 // by G = D/8 lanes, 8 channels (16 B of bf16) per lane, so row reductions are
 // DPP sums inside the group. In the prologue each group walks a tile of TT
@@ -56,12 +61,13 @@ prologue_conv_kernel(const TIO *__restrict__ x_q, const TIO *__restrict__ x_k,
                      const float *__restrict__ A, const float *__restrict__ dt_bias,
                      float *__restrict__ g, float *__restrict__ beta,
                      const int32_t *__restrict__ cu, long total, long T, int N, int H,
-                     int d_k, int which0)
+                     int Hk, int d_k, int which0)
 {
     constexpr int G = D / 8;
     constexpr int GPB = 256 / G;                  // lane groups per block
     const int which = which0 + (int)blockIdx.z;   // 0 = q, 1 = k, 2 = v
-    const int h = blockIdx.y;
+    const int h = blockIdx.y;                     // head of this tensor
+    const int Ht = which < 2 ? Hk : H;            // heads of this tensor
     const int lr = threadIdx.x % G;
     const long t0 = ((long)blockIdx.x * GPB + threadIdx.x / G) * PRO_TT;
     if (t0 >= total) return;
@@ -71,7 +77,7 @@ prologue_conv_kernel(const TIO *__restrict__ x_q, const TIO *__restrict__ x_k,
     TIO *y = which == 0 ? y_q : (which == 1 ? y_k : y_v);
     const int c = 8 * lr;
     // conv channel of (tensor, head, c): q channels, then k, then v
-    const long ch = (long)which * H * d_k + (long)h * D + c;
+    const long ch = (long)which * Hk * d_k + (long)h * D + c;
     float w[8][4];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
@@ -82,7 +88,7 @@ prologue_conv_kernel(const TIO *__restrict__ x_q, const TIO *__restrict__ x_k,
     int n;
     seq_bounds(cu, N, T, t0, start, end, n);
 
-    auto row = [&](long t) { return ((size_t)t * H + h) * D + c; };
+    auto row = [&](long t) { return ((size_t)t * Ht + h) * D + c; };
     float x1[8], x2[8], x3[8];                    // inputs at t-1, t-2, t-3
 #pragma unroll
     for (int e = 0; e < 8; ++e) { x1[e] = 0.f; x2[e] = 0.f; x3[e] = 0.f; }
@@ -116,7 +122,7 @@ prologue_conv_kernel(const TIO *__restrict__ x_q, const TIO *__restrict__ x_k,
             for (int e = 0; e < 8; ++e) out[e] *= inv;
         }
         store8(y + row(t), out);
-        if (which == 0 && lr == 0) {              // gates, once per (token, head)
+        if (which == 2 && lr == 0) {              // gates, once per (token, value head)
             const size_t i = (size_t)t * H + h;
             const float bias = dt_bias ? dt_bias[h] : 0.f;
             g[i] = -A[h] * softplus_f32(to_f32(a[i]) + bias);
@@ -159,16 +165,17 @@ template <int D, typename TIO>
 static hipError_t launch_conv(const void *xq, const void *xk, const void *xv, const void *w,
                               void *yq, void *yk, void *yv, const void *a, const void *b,
                               const float *A, const float *dtb, float *g, float *beta,
-                              const int32_t *cu, long total, long T, int N, int H, int d_k,
-                              int which0, int nwhich, hipStream_t stream)
+                              const int32_t *cu, long total, long T, int N, int H, int Hk,
+                              int d_k, int which0, int nwhich, hipStream_t stream)
 {
     constexpr int GPB = 256 / (D / 8);
     const long tiles = (total + PRO_TT - 1) / PRO_TT;
-    dim3 grid((unsigned)((tiles + GPB - 1) / GPB), (unsigned)H, (unsigned)nwhich), block(256);
+    const int heads = which0 < 2 ? Hk : H;
+    dim3 grid((unsigned)((tiles + GPB - 1) / GPB), (unsigned)heads, (unsigned)nwhich), block(256);
     hipLaunchKernelGGL((prologue_conv_kernel<D, TIO>), grid, block, 0, stream,
                        (const TIO *)xq, (const TIO *)xk, (const TIO *)xv, (const TIO *)w,
                        (TIO *)yq, (TIO *)yk, (TIO *)yv, (const TIO *)a, (const TIO *)b, A, dtb,
-                       g, beta, cu, total, T, N, H, d_k, which0);
+                       g, beta, cu, total, T, N, H, Hk, d_k, which0);
     return hipGetLastError();
 }
 
@@ -177,14 +184,14 @@ static hipError_t conv_dispatch(int D, const void *xq, const void *xk, const voi
                                 const void *w, void *yq, void *yk, void *yv, const void *a,
                                 const void *b, const float *A, const float *dtb, float *g,
                                 float *beta, const int32_t *cu, long total, long T, int N, int H,
-                                int d_k, int which0, int nwhich, hipStream_t s)
+                                int Hk, int d_k, int which0, int nwhich, hipStream_t s)
 {
     switch (D) {
-    case 16: return launch_conv<16, TIO>(xq, xk, xv, w, yq, yk, yv, a, b, A, dtb, g, beta, cu, total, T, N, H, d_k, which0, nwhich, s);
-    case 32: return launch_conv<32, TIO>(xq, xk, xv, w, yq, yk, yv, a, b, A, dtb, g, beta, cu, total, T, N, H, d_k, which0, nwhich, s);
-    case 64: return launch_conv<64, TIO>(xq, xk, xv, w, yq, yk, yv, a, b, A, dtb, g, beta, cu, total, T, N, H, d_k, which0, nwhich, s);
-    case 128: return launch_conv<128, TIO>(xq, xk, xv, w, yq, yk, yv, a, b, A, dtb, g, beta, cu, total, T, N, H, d_k, which0, nwhich, s);
-    case 256: return launch_conv<256, TIO>(xq, xk, xv, w, yq, yk, yv, a, b, A, dtb, g, beta, cu, total, T, N, H, d_k, which0, nwhich, s);
+    case 16: return launch_conv<16, TIO>(xq, xk, xv, w, yq, yk, yv, a, b, A, dtb, g, beta, cu, total, T, N, H, Hk, d_k, which0, nwhich, s);
+    case 32: return launch_conv<32, TIO>(xq, xk, xv, w, yq, yk, yv, a, b, A, dtb, g, beta, cu, total, T, N, H, Hk, d_k, which0, nwhich, s);
+    case 64: return launch_conv<64, TIO>(xq, xk, xv, w, yq, yk, yv, a, b, A, dtb, g, beta, cu, total, T, N, H, Hk, d_k, which0, nwhich, s);
+    case 128: return launch_conv<128, TIO>(xq, xk, xv, w, yq, yk, yv, a, b, A, dtb, g, beta, cu, total, T, N, H, Hk, d_k, which0, nwhich, s);
+    case 256: return launch_conv<256, TIO>(xq, xk, xv, w, yq, yk, yv, a, b, A, dtb, g, beta, cu, total, T, N, H, Hk, d_k, which0, nwhich, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -193,17 +200,17 @@ template <typename TIO>
 hipError_t launch_prologue(const void *q_raw, const void *k_raw, const void *v_raw,
                            const void *conv_w, const void *a, const void *b, const float *A,
                            const float *dt_bias, const int32_t *cu, void *q, void *k, void *v,
-                           float *g, float *beta, int B, int T, int H, int d_k, int d_v, int N,
-                           hipStream_t stream)
+                           float *g, float *beta, int B, int T, int H, int Hk, int d_k,
+                           int d_v, int N, hipStream_t stream)
 {
     const long total = (long)B * T;
     if (total == 0) return hipSuccess;
     // q and k share a launch (same head size); v has its own.
     hipError_t e = conv_dispatch<TIO>(d_k, q_raw, k_raw, v_raw, conv_w, q, k, v, a, b, A, dt_bias,
-                                      g, beta, cu, total, (long)T, N, H, d_k, 0, 2, stream);
+                                      g, beta, cu, total, (long)T, N, H, Hk, d_k, 0, 2, stream);
     if (e != hipSuccess) return e;
     return conv_dispatch<TIO>(d_v, q_raw, k_raw, v_raw, conv_w, q, k, v, a, b, A, dt_bias, g,
-                              beta, cu, total, (long)T, N, H, d_k, 2, 1, stream);
+                              beta, cu, total, (long)T, N, H, Hk, d_k, 2, 1, stream);
 }
 
 template <typename TIO>
@@ -231,12 +238,12 @@ hipError_t launch_epilogue(const void *y, const void *z, const float *w, void *o
 template hipError_t launch_prologue<float>(const void *, const void *, const void *, const void *,
                                            const void *, const void *, const float *,
                                            const float *, const int32_t *, void *, void *, void *,
-                                           float *, float *, int, int, int, int, int, int,
+                                           float *, float *, int, int, int, int, int, int, int,
                                            hipStream_t);
 template hipError_t launch_prologue<bf16>(const void *, const void *, const void *, const void *,
                                           const void *, const void *, const float *,
                                           const float *, const int32_t *, void *, void *, void *,
-                                          float *, float *, int, int, int, int, int, int,
+                                          float *, float *, int, int, int, int, int, int, int,
                                           hipStream_t);
 template hipError_t launch_epilogue<float>(const void *, const void *, const float *, void *,
                                            long, int, float, hipStream_t);

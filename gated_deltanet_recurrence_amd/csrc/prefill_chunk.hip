@@ -17,6 +17,10 @@
 // the chunk reproduces the token-by-token recurrence exactly (A is
 // nilpotent, so the inverse is a finite series).
 //
+// q and k may have fewer heads (H_k) than v, g, beta, o and the state (H):
+// value head h reads query/key head h / (H / H_k) (the repeat_interleave head
+// expansion of the "Gated DeltaNet body" layer code in the same chapter).
+//
 // Work mapping: one workgroup of 8 waves (two per SIMD) per (32-wide d_v
 // tile, head, sequence); the columns of S (rows of our d_v x d_k state)
 // evolve independently, so the four d_v tiles of a head never communicate.
@@ -119,7 +123,7 @@ prefill_chunk_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                      const bf16 *__restrict__ v, const float *__restrict__ g,
                      const float *__restrict__ beta, const float *s_init, float *s_final,
                      bf16 *__restrict__ o, const int32_t *__restrict__ cu_seqlens, int T, int H,
-                     int npairs, float scale)
+                     int Hk, int npairs, float scale)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     bf16 *sQ = reinterpret_cast<bf16 *>(smem + OFF_Q);
@@ -198,33 +202,36 @@ prefill_chunk_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     // block jb, d_k block cb), V for 128..159 (token block jb, d_v block cb of
     // this tile). g, beta: wave 3, one token per lane.
     const int tid = tid0;
-    const int tstride = H * DK;                // elements between tokens (q, k, v)
+    const int tstride = H * DK;                // elements between tokens of v
+    const int tsqk = Hk * DK;                  // ... and of q, k (H_k <= H heads)
+    const int kh = h / (H / Hk);               // query/key head of value head h
     const bool blk_k = tid < 128, blk_v = tid >= 128 && tid < 160;
     const int blk_jb = blk_k ? (tid >> 4) : ((tid - 128) >> 2);
     const int blk_cb = blk_k ? (tid & 15) : ((tid - 128) & 3);
     const int qrow0 = tid >> 4;                // rows qrow0 and qrow0 + 32
     // uniform bases; per-lane offsets fit in 32 bits (row < 64, H * 128 < 2^23)
-    const bf16 *qbase = q + (size_t)bos * tstride + (size_t)h * DK;
-    const bf16 *kbase = k + (size_t)bos * tstride + (size_t)h * DK;
+    const bf16 *qbase = q + (size_t)bos * tsqk + (size_t)kh * DK;
+    const bf16 *kbase = k + (size_t)bos * tsqk + (size_t)kh * DK;
     const bf16 *vbase = v + (size_t)bos * tstride + (size_t)h * DV + cbase;
-    const int qoff = qrow0 * tstride + 8 * (tid & 15);
-    const int boff = 8 * blk_jb * tstride + 8 * blk_cb;
+    const int bstride = blk_k ? tsqk : tstride;   // K or V rows of this thread's block
+    const int qoff = qrow0 * tsqk + 8 * (tid & 15);
+    const int boff = 8 * blk_jb * bstride + 8 * blk_cb;
     bf16x8 rq[2], rb[8];
     float rg = 0.f, rbeta = 0.f;
     auto fetch = [&](int ch) {
         const bf16x8 z8 = {};
-        const size_t coff = (size_t)ch * C * tstride;   // uniform
+        const size_t coff = (size_t)ch * C * tstride, coffqk = (size_t)ch * C * tsqk;   // uniform
         const int base = ch * C;
         const int lane = tid & 63;
-        const bf16 *qc = qbase + coff, *kc = kbase + coff, *vc = vbase + coff;
+        const bf16 *qc = qbase + coffqk, *kc = kbase + coffqk, *vc = vbase + coff;
         if (base + C <= len) {                 // whole chunk inside the sequence (uniform)
 #pragma unroll
             for (int u = 0; u < 2; ++u)
-                rq[u] = *reinterpret_cast<const bf16x8 *>(qc + qoff + 32 * u * tstride);
+                rq[u] = *reinterpret_cast<const bf16x8 *>(qc + qoff + 32 * u * tsqk);
             if (blk_k) {
 #pragma unroll
                 for (int r = 0; r < 8; ++r)
-                    rb[r] = *reinterpret_cast<const bf16x8 *>(kc + boff + r * tstride);
+                    rb[r] = *reinterpret_cast<const bf16x8 *>(kc + boff + r * tsqk);
             } else if (blk_v) {
 #pragma unroll
                 for (int r = 0; r < 8; ++r)
@@ -235,7 +242,7 @@ prefill_chunk_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             for (int u = 0; u < 2; ++u) {
                 rq[u] = z8;
                 if (base + qrow0 + 32 * u < len)
-                    rq[u] = *reinterpret_cast<const bf16x8 *>(qc + qoff + 32 * u * tstride);
+                    rq[u] = *reinterpret_cast<const bf16x8 *>(qc + qoff + 32 * u * tsqk);
             }
             if (blk_k || blk_v) {
                 const bf16 *bc = blk_k ? kc : vc;
@@ -243,7 +250,7 @@ prefill_chunk_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                 for (int r = 0; r < 8; ++r) {
                     rb[r] = z8;
                     if (base + 8 * blk_jb + r < len)
-                        rb[r] = *reinterpret_cast<const bf16x8 *>(bc + boff + r * tstride);
+                        rb[r] = *reinterpret_cast<const bf16x8 *>(bc + boff + r * bstride);
                 }
             }
         }
@@ -556,7 +563,7 @@ prefill_chunk_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 
 hipError_t launch_prefill_chunk(const void *q, const void *k, const void *v, const float *g,
                                 const float *beta, const float *s_init, float *s_final, void *o,
-                                const int32_t *cu, int T, int H, int N, float scale,
+                                const int32_t *cu, int T, int H, int Hk, int N, float scale,
                                 hipStream_t stream)
 {
     static bool attr_done = false;
@@ -570,7 +577,7 @@ hipError_t launch_prefill_chunk(const void *q, const void *k, const void *v, con
     dim3 grid(pair_grid(npairs)), block(NT);
     hipLaunchKernelGGL(prefill_chunk_kernel, grid, block, LDS_BYTES, stream, (const bf16 *)q,
                        (const bf16 *)k, (const bf16 *)v, g, beta, s_init, s_final, (bf16 *)o, cu,
-                       T, H, npairs, scale);
+                       T, H, Hk, npairs, scale);
     return hipGetLastError();
 }
 

@@ -9,6 +9,11 @@
 // accuracy), head sizes other than 128, and is the on-GPU cross-check of the
 // chunkwise kernel.
 //
+// Grouped heads: q and k may have fewer heads (H_k) than v, g, beta, o and
+// the state (H); value head h reads query/key head h / (H / H_k), the
+// repeat_interleave head expansion of the "Gated DeltaNet body" layer code in
+// "5. Linear Attention" (LinkQwen ch. 5).
+//
 // Work mapping: grid (row blocks, H, N). A state row (d_k floats) lives in
 // the registers of G = d_k/8 lanes for the whole sequence; rows never
 // exchange data, so there is no barrier anywhere. Per token each lane group
@@ -25,12 +30,13 @@ prefill_recurrent_kernel(const TIO *__restrict__ q, const TIO *__restrict__ k,
                          const TIO *__restrict__ v, const float *__restrict__ g,
                          const float *__restrict__ beta, const float *s_init,
                          float *s_final, TIO *__restrict__ o,
-                         const int32_t *__restrict__ cu_seqlens, int T, int H, int d_v,
-                         float scale)
+                         const int32_t *__restrict__ cu_seqlens, int T, int H, int Hk,
+                         int d_v, float scale)
 {
     constexpr int G = DK / 8;
     constexpr int RPB = 256 / G;              // state rows per workgroup
     const int h = blockIdx.y, n = blockIdx.z;
+    const int kh = h / (H / Hk);              // query/key head of value head h
     const int tid = threadIdx.x;
     const int lr = tid % G;
     const int row = blockIdx.x * RPB + tid / G;
@@ -59,7 +65,7 @@ prefill_recurrent_kernel(const TIO *__restrict__ q, const TIO *__restrict__ k,
     const int vrow = active ? row : 0;
     auto fetch = [&](long t, f32x4 &k0, f32x4 &k1, f32x4 &q0, f32x4 &q1, float &vv, float &gg,
                      float &bb) {
-        const size_t tk = ((size_t)t * H + h) * DK;
+        const size_t tk = ((size_t)t * Hk + kh) * DK;
         k0 = load4(k + tk + c0);
         k1 = load4(k + tk + c1);
         q0 = load4(q + tk + c0);
@@ -111,14 +117,14 @@ prefill_recurrent_kernel(const TIO *__restrict__ q, const TIO *__restrict__ k,
 template <typename TIO>
 hipError_t launch_prefill_recurrent(const void *q, const void *k, const void *v, const float *g,
                                     const float *beta, const float *s_init, float *s_final,
-                                    void *o, const int32_t *cu_seqlens, int T, int H, int d_k,
-                                    int d_v, int N, float scale, hipStream_t stream)
+                                    void *o, const int32_t *cu_seqlens, int T, int H, int Hk,
+                                    int d_k, int d_v, int N, float scale, hipStream_t stream)
 {
     auto go = [&](auto kern, int rpb) {
         dim3 grid((unsigned)((d_v + rpb - 1) / rpb), (unsigned)H, (unsigned)N), block(256);
         hipLaunchKernelGGL(kern, grid, block, 0, stream, (const TIO *)q, (const TIO *)k,
                            (const TIO *)v, g, beta, s_init, s_final, (TIO *)o, cu_seqlens, T,
-                           H, d_v, scale);
+                           H, Hk, d_v, scale);
         return hipGetLastError();
     };
     switch (d_k) {
@@ -133,10 +139,10 @@ hipError_t launch_prefill_recurrent(const void *q, const void *k, const void *v,
 template hipError_t launch_prefill_recurrent<float>(const void *, const void *, const void *,
                                                     const float *, const float *, const float *,
                                                     float *, void *, const int32_t *, int, int,
-                                                    int, int, int, float, hipStream_t);
+                                                    int, int, int, int, float, hipStream_t);
 template hipError_t launch_prefill_recurrent<bf16>(const void *, const void *, const void *,
                                                    const float *, const float *, const float *,
                                                    float *, void *, const int32_t *, int, int,
-                                                   int, int, int, float, hipStream_t);
+                                                   int, int, int, int, float, hipStream_t);
 
 }  // namespace gdn

@@ -23,6 +23,11 @@
 // read back: 384 B of HBM traffic per token-head on top of the 1032 B of
 // q, k, v, o, g and beta.
 //
+// q and k may have fewer heads (H_k) than v, g, beta, o and the state (H):
+// value head h reads query/key head h / (H / H_k) (the repeat_interleave head
+// expansion of the "Gated DeltaNet body" layer code, "5. Linear Attention").
+// The workspace is per value head, since beta and g are.
+//
 // Workspace layout: for head h and chunk slot s, 6144 bf16 at
 // ((h * nslots) + s) * 6144, as 768 pieces of 8 consecutive row elements of
 // -T_w and T_u (their non-zero lower 64 x 64 part: rows 0-31 span columns
@@ -245,7 +250,7 @@ __global__ void __launch_bounds__(P_NT, 3)
 chunk_prep_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                   const float *__restrict__ g, const float *__restrict__ beta,
                   const int32_t *__restrict__ cu_seqlens, bf16 *__restrict__ ws, int T, int H,
-                  int N, int nslots)
+                  int Hk, int N, int nslots)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     bf16 *sK = reinterpret_cast<bf16 *>(smem + P_OFF_R1);
@@ -262,7 +267,7 @@ chunk_prep_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
     const int nitems = nslots * H;
     const int stride = (int)gridDim.x;
-    const int tstride = H * DK;                // elements between consecutive tokens of K, Q
+    const int tstride = Hk * DK;               // elements between consecutive tokens of K, Q
 
     // K and Q rows (tid >> 4) + 16 u, columns 8 (tid & 15) ..; g and beta of
     // token `lane`. Buffer loads bounded by the chunk's valid tokens: rows
@@ -274,7 +279,7 @@ chunk_prep_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     auto fetch = [&](const PrepItem &it, Pre &p) {
         const size_t tok0 = (size_t)it.row0;
         const unsigned nb = (unsigned)it.nvalid * tstride * 2;
-        const size_t hoff = tok0 * tstride + (size_t)it.h * DK;
+        const size_t hoff = tok0 * tstride + (size_t)(it.h / (H / Hk)) * DK;   // query/key head
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(k + hoff), 0, nb, 0x00020000);
         const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)(q + hoff), 0, nb, 0x00020000);
         const unsigned off = (unsigned)(((tid0 >> 4) * tstride + 8 * (tid0 & 15)) * 2);
@@ -593,7 +598,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                    const bf16 *__restrict__ v, const float *__restrict__ g,
                    const bf16 *__restrict__ ws, const float *s_init, float *s_final,
                    bf16 *__restrict__ o, const int32_t *__restrict__ cu_seqlens, int T, int H,
-                   int npairs, int nslots, float scale)
+                   int Hk, int npairs, int nslots, float scale)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     bf16 *lds = reinterpret_cast<bf16 *>(smem);
@@ -666,12 +671,13 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     //      Workspace piece order (8 bf16 each): 0..255 rows 32-63 of -T_w (8
     //      per row), 256..511 rows 32-63 of T_u, 512..639 rows 0-31 of -T_w (4
     //      per row: columns 0-31), 640..767 rows 0-31 of T_u. ----
-    const int tstride = H * DK;                // elements between tokens
+    const int tstride = Hk * DK;               // elements between tokens of q, k
+    const int tsv = H * DV;                    // ... and of v
     const int wi = wave - 4;
     const int qkmat = wi >> 1;                 // 0 Q, 1 K
     const int qkrow = 32 * (wi & 1) + (lane0 >> 4), qkcol = 8 * (lane0 & 15);
     const int goffQK = 2 * (qkrow * tstride + qkcol);
-    const int goffV = 2 * ((lane0 >> 2) * tstride + 8 * (lane0 & 3));
+    const int goffV = 2 * ((lane0 >> 2) * tsv + 8 * (lane0 & 3));
     const int vr0 = 2 * (wi - 2);              // first V row group (wi 2, 3)
     // LDS element offset of workspace piece e within a staging buffer (uniform
     // per 64-piece group)
@@ -679,8 +685,8 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         return e < 512 ? B_TL / 2 + (e >> 3) * LD_L + 8 * (e & 7)
                        : B_TH / 2 + ((e - 512) >> 2) * LD_H + 8 * (e & 3);
     };
-    const bf16 *qk_head = (qkmat ? k : q) + (size_t)bos * tstride + (size_t)h * DK;
-    const bf16 *v_head = v + (size_t)bos * tstride + (size_t)h * DV + cbase;
+    const bf16 *qk_head = (qkmat ? k : q) + (size_t)bos * tstride + (size_t)(h / (H / Hk)) * DK;
+    const bf16 *v_head = v + (size_t)bos * tsv + (size_t)h * DV + cbase;
     const float *g_head = g + (size_t)bos * H + h;
     // Two register sets: chunk c is loaded into set c % 2 three iterations
     // before its use and stored to LDS one iteration before.
@@ -709,11 +715,11 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                           rw, 16 * lane0, 16 * (192 * wi + 64 * r), 0));
         if constexpr (decltype(WV)::value) {
             const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(v_head + (size_t)base * tstride), 0, nb, 0x00020000);
+                (void *)(v_head + (size_t)base * tsv), 0, (unsigned)nrow * tsv * 2, 0x00020000);
 #pragma unroll
             for (int r = 0; r < 2; ++r)
                 rs.v[r] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                              rv, goffV, (vr0 + r) * 16 * tstride * 2, 0));
+                              rv, goffV, (vr0 + r) * 16 * tsv * 2, 0));
         }
         if constexpr (decltype(WG)::value) {
             const __amdgpu_buffer_rsrc_t rgs = __builtin_amdgcn_make_buffer_rsrc(
@@ -1017,7 +1023,7 @@ size_t prefill_split_workspace_bytes(long tokens, int H, int N) {
 }
 
 hipError_t launch_prefill_prepare(const void *q, const void *k, const float *g, const float *beta,
-                                  const int32_t *cu, int T, int H, int N, void *ws,
+                                  const int32_t *cu, int T, int H, int Hk, int N, void *ws,
                                   hipStream_t stream)
 {
     const long tokens = cu ? (long)T : (long)N * T;
@@ -1040,13 +1046,13 @@ hipError_t launch_prefill_prepare(const void *q, const void *k, const float *g, 
     const long fill = (long)per_cu * cus;
     dim3 grid((unsigned)(nitems < fill ? nitems : fill)), block(P_NT);
     hipLaunchKernelGGL(chunk_prep_kernel, grid, block, P_LDS_BYTES, stream, (const bf16 *)q,
-                       (const bf16 *)k, g, beta, cu, (bf16 *)ws, T, H, N, (int)nslots);
+                       (const bf16 *)k, g, beta, cu, (bf16 *)ws, T, H, Hk, N, (int)nslots);
     return hipGetLastError();
 }
 
 hipError_t launch_prefill_apply(const void *q, const void *k, const void *v, const float *g,
                                 const float *s_init, float *s_final, void *o, const int32_t *cu,
-                                int T, int H, int N, float scale, const void *ws,
+                                int T, int H, int Hk, int N, float scale, const void *ws,
                                 hipStream_t stream)
 {
     static bool attr_done = false;
@@ -1062,7 +1068,7 @@ hipError_t launch_prefill_apply(const void *q, const void *k, const void *v, con
     dim3 grid(pair_grid(npairs)), block(NT);
     hipLaunchKernelGGL(chunk_chain_kernel, grid, block, LDS_BYTES, stream, (const bf16 *)q,
                        (const bf16 *)k, (const bf16 *)v, g, (const bf16 *)ws, s_init, s_final,
-                       (bf16 *)o, cu, T, H, npairs, (int)nslots, scale);
+                       (bf16 *)o, cu, T, H, Hk, npairs, (int)nslots, scale);
     return hipGetLastError();
 }
 

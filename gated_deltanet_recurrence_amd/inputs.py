@@ -43,9 +43,10 @@ __all__ = [
 class GDNCase:
     """Inputs of one recurrence call (prefill or decode), on the host.
 
-    q, k: [B, T, H, d_k]; v: [B, T, H, d_v] in ``dtype`` (decode: T=1 folded
-    away by the caller); g, beta: [B, T, H] fp32; s0: [N, H, d_v, d_k] fp32
-    or None; cu_seqlens: int32 [N+1] or None.
+    q, k: [B, T, H_k, d_k]; v: [B, T, H, d_v] in ``dtype`` (decode: T=1
+    folded away by the caller); g, beta: [B, T, H] fp32; s0: [N, H, d_v, d_k]
+    fp32 or None; cu_seqlens: int32 [N+1] or None. H counts the value heads,
+    H_k (dividing H) the query/key heads.
     """
     name: str
     q: torch.Tensor
@@ -69,6 +70,10 @@ class GDNCase:
 
     @property
     def H(self) -> int:
+        return self.v.shape[2]
+
+    @property
+    def Hk(self) -> int:
         return self.q.shape[2]
 
     @property
@@ -88,8 +93,8 @@ class GDNCase:
 class MixerCase:
     """Raw (pre-convolution) inputs of the full token mixer, on the host.
 
-    q_raw, k_raw: [B, T, H, d_k]; v_raw, z: [B, T, H, d_v]; a, b: [B, T, H];
-    conv_w: [H*(2*d_k + d_v), 4] (channel order q, k, v; tap 3 multiplies the
+    q_raw, k_raw: [B, T, H_k, d_k]; v_raw, z: [B, T, H, d_v]; a, b: [B, T, H];
+    conv_w: [2*H_k*d_k + H*d_v, 4] (channel order q, k, v; tap 3 multiplies the
     current token); A: [H] fp32; dt_bias: [H] fp32 or None; norm_w: [d_v]
     fp32 or None (ones).
     """
@@ -171,14 +176,17 @@ def make_tiny(seed: int = 1, T: int = 64, d: int = 16, H: int = 1, B: int = 1,
 
 
 def make_prefill(seed: int = 2, B: int = 4, T: int = 4096, H: int = 16, d: int = 128,
-                 dtype: str = "bf16", with_state: bool = False) -> GDNCase:
+                 dtype: str = "bf16", with_state: bool = False,
+                 Hk: Optional[int] = None) -> GDNCase:
     """Chunked-prefill workload: q,k unit Gaussian, v ~ N(0,1), log(alpha) =
     -A*softplus(a) with a ~ N(0,1) and A ~ U(0.5, 2) per head, beta =
-    sigmoid(N(0,1)), zero initial state unless ``with_state``."""
+    sigmoid(N(0,1)), zero initial state unless ``with_state``. ``Hk`` query/key
+    heads (default H)."""
     gen = _gen(seed)
     td = _TORCH_DTYPE[dtype]
-    q = unit_gaussian(gen, (B, T, H, d)).to(td)
-    k = unit_gaussian(gen, (B, T, H, d)).to(td)
+    Hk = H if Hk is None else Hk
+    q = unit_gaussian(gen, (B, T, Hk, d)).to(td)
+    k = unit_gaussian(gen, (B, T, Hk, d)).to(td)
     v = _normal(gen, (B, T, H, d)).to(td)
     a = _normal(gen, (B, T, H))
     A = _uniform(gen, (H,), 0.5, 2.0)
@@ -190,14 +198,15 @@ def make_prefill(seed: int = 2, B: int = 4, T: int = 4096, H: int = 16, d: int =
 
 
 def make_decode(seed: int = 3, B: int = 256, H: int = 32, d: int = 128,
-                dtype: str = "bf16") -> GDNCase:
+                dtype: str = "bf16", Hk: Optional[int] = None) -> GDNCase:
     """Single-token decode: fp32 state N(0, 0.02) [B,H,d,d]; q,k unit Gaussian,
     v ~ N(0,1); alpha ~ U(0.8, 1); beta = sigmoid(N(0,1)). Tensors carry a
-    T=1 axis: q,k,v [B,1,H,d], g,beta [B,1,H]."""
+    T=1 axis: q,k [B,1,Hk,d], v [B,1,H,d], g,beta [B,1,H]."""
     gen = _gen(seed)
     td = _TORCH_DTYPE[dtype]
-    q = unit_gaussian(gen, (B, 1, H, d)).to(td)
-    k = unit_gaussian(gen, (B, 1, H, d)).to(td)
+    Hk = H if Hk is None else Hk
+    q = unit_gaussian(gen, (B, 1, Hk, d)).to(td)
+    k = unit_gaussian(gen, (B, 1, Hk, d)).to(td)
     v = _normal(gen, (B, 1, H, d)).to(td)
     alpha = _uniform(gen, (B, 1, H), 0.8, 1.0)
     g = torch.log(alpha)
@@ -207,19 +216,21 @@ def make_decode(seed: int = 3, B: int = 256, H: int = 32, d: int = 128,
 
 
 def make_mixer(seed: int = 4, B: int = 8, T: int = 8192, H: int = 16, d: int = 128,
-               dtype: str = "bf16") -> MixerCase:
+               dtype: str = "bf16", Hk: Optional[int] = None) -> MixerCase:
     """Full token mixer from pre-projected inputs: q,k,v,z,a,b ~ N(0,1);
     depthwise conv weights N(0, 0.5) with 4 taps; A ~ U(0.5, 2) per head;
-    no dt_bias; RMSNorm weight ones, eps 1e-6; scale d^-1/2."""
+    no dt_bias; RMSNorm weight ones, eps 1e-6; scale d^-1/2. ``Hk`` query/key
+    heads (default H)."""
     gen = _gen(seed)
     td = _TORCH_DTYPE[dtype]
-    q = _normal(gen, (B, T, H, d)).to(td)
-    k = _normal(gen, (B, T, H, d)).to(td)
+    Hk = H if Hk is None else Hk
+    q = _normal(gen, (B, T, Hk, d)).to(td)
+    k = _normal(gen, (B, T, Hk, d)).to(td)
     v = _normal(gen, (B, T, H, d)).to(td)
     z = _normal(gen, (B, T, H, d)).to(td)
     a = _normal(gen, (B, T, H)).to(td)
     b = _normal(gen, (B, T, H)).to(td)
-    conv_w = _normal(gen, (3 * H * d, 4), std=0.5).to(td)
+    conv_w = _normal(gen, (2 * Hk * d + H * d, 4), std=0.5).to(td)
     A = _uniform(gen, (H,), 0.5, 2.0)
     return MixerCase("mixer", q, k, v, z, a, b, conv_w, A, None, None,
                      1.0 / math.sqrt(d), 1e-6, dtype)
@@ -227,11 +238,12 @@ def make_mixer(seed: int = 4, B: int = 8, T: int = 8192, H: int = 16, d: int = 1
 
 def make_varlen(seed: int = 5, n_seq: int = 8, H: int = 32, d: int = 128,
                 lo: int = 512, hi: int = 65536, dtype: str = "bf16",
-                lengths: Optional[list] = None) -> GDNCase:
+                lengths: Optional[list] = None, Hk: Optional[int] = None) -> GDNCase:
     """Packed variable-length prefill: lengths log-uniform in [lo, hi];
     q,k unit Gaussian, v ~ N(0,1); initial states N(0, 0.02); a ~ N(-2, 1),
     A ~ U(0.5, 2) per head, log(alpha) = -A*softplus(a); beta = sigmoid(N(0,1)).
-    Shapes: q,k,v [1, sum(lengths), H, d], cu_seqlens int32 [n_seq+1]."""
+    Shapes: q,k [1, sum(lengths), Hk, d] (Hk defaults to H), v [1, sum(lengths),
+    H, d], cu_seqlens int32 [n_seq+1]."""
     gen = _gen(seed)
     td = _TORCH_DTYPE[dtype]
     if lengths is None:
@@ -240,8 +252,9 @@ def make_varlen(seed: int = 5, n_seq: int = 8, H: int = 32, d: int = 128,
     total = int(sum(lengths))
     cu = torch.zeros(n_seq + 1, dtype=torch.int32)
     cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
-    q = unit_gaussian(gen, (1, total, H, d)).to(td)
-    k = unit_gaussian(gen, (1, total, H, d)).to(td)
+    Hk = H if Hk is None else Hk
+    q = unit_gaussian(gen, (1, total, Hk, d)).to(td)
+    k = unit_gaussian(gen, (1, total, Hk, d)).to(td)
     v = _normal(gen, (1, total, H, d)).to(td)
     s0 = _normal(gen, (n_seq, H, d, d), std=0.02)
     a = _normal(gen, (1, total, H), mean=-2.0)

@@ -19,8 +19,14 @@
  *    device allocator on the device current when the call is made). The
  *    caller owns and allocates every buffer; the library keeps no pointer
  *    after a call returns and allocates no device memory.
- *  - Activations are token-major and C-contiguous: q, k are [B][T][H][d_k];
+ *  - Activations are token-major and C-contiguous: q, k are [B][T][H_k][d_k];
  *    v, o are [B][T][H][d_v]; per-token scalars are [B][T][H].
+ *  - Grouped heads: H counts the value heads (v, o, g, beta, states) and H_k
+ *    the query/key heads, 1 <= H_k <= H with H divisible by H_k; value head h
+ *    reads query/key head h / (H / H_k), i.e. q and k repeated along the head
+ *    axis with repeat_interleave ("5. Linear Attention" chapter, "Gated
+ *    DeltaNet body" layer code, the KV head expansion before the core). H_k =
+ *    H is the ungrouped layer. A bad pair gives GDN_ERR_SHAPE.
  *  - States are fp32, [N][H][d_v][d_k] with d_k contiguous.
  *  - The decay gate is passed in log space: g = log(alpha), fp32 (alpha =
  *    exp(g) <= 1 for g <= 0). beta is fp32, one scalar per (token, head).
@@ -47,7 +53,7 @@
 extern "C" {
 #endif
 
-#define GDN_VERSION 1
+#define GDN_VERSION 2
 
 typedef enum {
     GDN_DTYPE_F32 = 0,
@@ -81,7 +87,7 @@ const char *gdn_status_string(int status);
  * state as one update; the state is carried in fp32 from chunk to chunk.
  * The result equals the token-by-token recurrence up to rounding.
  *
- *   q, k          [B][T][H][d_k], dtype
+ *   q, k          [B][T][H_k][d_k], dtype
  *   v             [B][T][H][d_v], dtype
  *   g, beta       [B][T][H] fp32 (g = log alpha)
  *   initial_state [N][H][d_v][d_k] fp32, or NULL for a zero initial state
@@ -99,6 +105,7 @@ const char *gdn_status_string(int status);
  *                 as an empty sequence, so malformed offsets give wrong
  *                 results but never out-of-range accesses. Check offsets on
  *                 the host with gdn_check_cu_seqlens() when in doubt.
+ *   H_k           query/key heads (see the conventions above)
  *   B, T, H, N    B >= 1, T >= 0, 1 <= H <= 65535, 1 <= N <= 65535,
  *                 B*T < 2^31. When B*T = 0 the activation
  *                 pointers (q, k, v, g, beta, o) are not read and may be NULL.
@@ -126,14 +133,14 @@ int gdn_prefill(const void *q, const void *k, const void *v,
                 const float *g, const float *beta,
                 const float *initial_state, float *final_state,
                 void *o, const int32_t *cu_seqlens,
-                int B, int T, int H, int d_k, int d_v, int N,
+                int B, int T, int H, int H_k, int d_k, int d_v, int N,
                 float scale, int dtype,
                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * gdn_prefill_workspace_size - bytes of workspace that gdn_prefill uses for
- * these sizes (same meaning as there; varlen != 0 when cu_seqlens will be
- * non-NULL). 0 when the path for these sizes uses none. The size depends on
+ * these sizes (same meaning as there, H the value heads; varlen != 0 when
+ * cu_seqlens will be non-NULL). 0 when the path for these sizes uses none. The size depends on
  * the token count and the number of heads only, not on the offsets: 18 KiB
  * per (64-token chunk slot, head), with (B*T)/64 + N + 1 slots. Written to
  * *bytes; returns GDN_OK or the error gdn_prefill would return for these
@@ -166,13 +173,13 @@ int gdn_prefill_workspace_size(int B, int T, int H, int d_k, int d_v, int N,
  */
 int gdn_prefill_prepare(const void *q, const void *k, const float *g, const float *beta,
                         const int32_t *cu_seqlens,
-                        int B, int T, int H, int d_k, int d_v, int N, int dtype,
+                        int B, int T, int H, int H_k, int d_k, int d_v, int N, int dtype,
                         void *workspace, size_t workspace_bytes, void *stream);
 
 int gdn_prefill_apply(const void *q, const void *k, const void *v, const float *g,
                       const float *initial_state, float *final_state,
                       void *o, const int32_t *cu_seqlens,
-                      int B, int T, int H, int d_k, int d_v, int N,
+                      int B, int T, int H, int H_k, int d_k, int d_v, int N,
                       float scale, int dtype,
                       const void *workspace, size_t workspace_bytes, void *stream);
 
@@ -188,7 +195,7 @@ int gdn_prefill_recurrent(const void *q, const void *k, const void *v,
                           const float *g, const float *beta,
                           const float *initial_state, float *final_state,
                           void *o, const int32_t *cu_seqlens,
-                          int B, int T, int H, int d_k, int d_v, int N,
+                          int B, int T, int H, int H_k, int d_k, int d_v, int N,
                           float scale, int dtype, void *stream);
 
 /*
@@ -201,7 +208,7 @@ int gdn_prefill_recurrent(const void *q, const void *k, const void *v,
  *
  * Each state row is read once and written once.
  *
- *   q, k       [B][H][d_k], dtype
+ *   q, k       [B][H_k][d_k], dtype (H_k query/key heads, as above)
  *   v          [B][H][d_v], dtype
  *   g, beta    [B][H] fp32
  *   state      [B][H][d_v][d_k] fp32, read and overwritten in place
@@ -211,7 +218,7 @@ int gdn_prefill_recurrent(const void *q, const void *k, const void *v,
 int gdn_decode_step(const void *q, const void *k, const void *v,
                     const float *g, const float *beta,
                     float *state, void *o,
-                    int B, int H, int d_k, int d_v,
+                    int B, int H, int H_k, int d_k, int d_v,
                     float scale, int dtype, void *stream);
 
 /*
@@ -225,18 +232,19 @@ int gdn_decode_step(const void *q, const void *k, const void *v,
  *      x / sqrt(sum x^2 + 1e-6);
  *   3. gates: g = -A[h] * softplus(a + dt_bias[h]),  beta = sigmoid(b).
  *
- *   q_raw, k_raw   [B][T][H][d_k], dtype        (projection outputs)
+ *   q_raw, k_raw   [B][T][H_k][d_k], dtype      (projection outputs)
  *   v_raw          [B][T][H][d_v], dtype
- *   conv_w         [H*(2*d_k + d_v)][4], dtype; channel order: all q
+ *   conv_w         [2*H_k*d_k + H*d_v][4], dtype; channel order: all q
  *                  channels (head-major), then k, then v; tap 3 multiplies
  *                  the current token, tap 0 the token three steps back
- *   a, b           [B][T][H], dtype
+ *   a, b           [B][T][H], dtype (per value head)
  *   A              [H] fp32 (positive decay rates)
  *   dt_bias        [H] fp32, or NULL for zero
  *   cu_seqlens     as for gdn_prefill (NULL: each batch row is a sequence)
  *   q, k, v        outputs, same shapes and dtype as the raw inputs; must not
  *                  alias them
  *   g, beta        outputs [B][T][H] fp32
+ *   H, H_k         value and query/key heads as above, H <= 65535
  *   d_k, d_v       each in {16, 32, 64, 128, 256} (else GDN_ERR_UNSUPPORTED)
  */
 int gdn_mixer_prologue(const void *q_raw, const void *k_raw, const void *v_raw,
@@ -244,7 +252,7 @@ int gdn_mixer_prologue(const void *q_raw, const void *k_raw, const void *v_raw,
                        const float *A, const float *dt_bias,
                        const int32_t *cu_seqlens,
                        void *q, void *k, void *v, float *g, float *beta,
-                       int B, int T, int H, int d_k, int d_v, int N,
+                       int B, int T, int H, int H_k, int d_k, int d_v, int N,
                        int dtype, void *stream);
 
 /*

@@ -10,8 +10,8 @@ slices out the (sequence, head) pairs a caller asks for, and calls the C code.
 Pinned by ``tests/test_oracle_pins.py`` against the worked example of the
 "Linear Attention" chapter (chunk section), the invariant S_t k_t = v_t for
 unit keys and beta = 1, the gate special cases, a closed form for mutually
-orthogonal keys, the unrolled product form, and brute-force checks of the
-convolution, norms and gates.
+orthogonal keys (also with grouped query/key heads), the unrolled product
+form, and brute-force checks of the convolution, norms and gates.
 """
 from __future__ import annotations
 
@@ -102,17 +102,34 @@ def _cu64(cu, n_tokens: int, n_seq: int) -> np.ndarray:
     return c
 
 
+def expand_heads(x, H: int) -> np.ndarray:
+    """The KV head expansion of the "Gated DeltaNet body" layer code ("5. Linear
+    Attention" chapter): when there are fewer query/key heads than value heads,
+    q and k are repeated along the head axis (axis 2) with repeat_interleave,
+    each head H / H_k times in a row, so value head h reads query/key head
+    h // (H / H_k)."""
+    x = _f64(x)
+    Hk = x.shape[2]
+    if H % Hk != 0:
+        raise ValueError("value heads must be a multiple of query/key heads")
+    return x if Hk == H else np.ascontiguousarray(np.repeat(x, H // Hk, axis=2))
+
+
 def gdn_recurrent(q, k, v, g, beta, s0=None, cu_seqlens=None, scale: float = 1.0,
                   nthreads: int = 0):
     """Gated delta rule over token-major inputs.
 
-    q, k: [B, T, H, d_k]; v: [B, T, H, d_v]; g (= log alpha), beta: [B, T, H];
-    s0: [N, H, d_v, d_k] or None. With ``cu_seqlens`` (N+1 offsets) B must be 1
-    and the T axis holds N packed sequences; otherwise N = B.
+    q, k: [B, T, H_k, d_k]; v: [B, T, H, d_v]; g (= log alpha), beta: [B, T, H];
+    s0: [N, H, d_v, d_k] or None. With fewer query/key heads than value heads
+    (H_k dividing H) q and k are first expanded by ``expand_heads``. With
+    ``cu_seqlens`` (N+1 offsets) B must be 1 and the T axis holds N packed
+    sequences; otherwise N = B.
     Returns (o [B, T, H, d_v], s_final [N, H, d_v, d_k]) as float64.
     """
-    q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
-    B, T, H, dk = q.shape
+    v, g, beta = (_f64(x) for x in (v, g, beta))
+    H = v.shape[2]
+    q, k = expand_heads(q, H), expand_heads(k, H)
+    B, T, _, dk = q.shape
     dv = v.shape[3]
     if k.shape != q.shape or v.shape[:3] != (B, T, H) or g.shape != (B, T, H) \
             or beta.shape != (B, T, H):
@@ -145,19 +162,23 @@ def gdn_recurrent_heads(q, k, v, g, beta, heads: Sequence[int], s0=None, cu_seql
     batch rows ``seqs``). Returns (o [b', T, h', d_v], s_final [n', h', d_v, d_k])
     for the selected rows/sequences and heads, in the order given."""
     heads = list(heads)
+    grp = v.shape[2] // q.shape[2]            # value heads per query/key head
+    kheads = [h // grp for h in heads]         # the query/key head of each, as expanded
     if cu_seqlens is None:
         rows = list(range(q.shape[0])) if seqs is None else list(seqs)
         sl = lambda x: x[rows][:, :, heads]
+        slk = lambda x: x[rows][:, :, kheads]
         s0s = None if s0 is None else s0[rows][:, heads]
-        return gdn_recurrent(sl(q), sl(k), sl(v), sl(g), sl(beta), s0s, None, scale, nthreads)
+        return gdn_recurrent(slk(q), slk(k), sl(v), sl(g), sl(beta), s0s, None, scale, nthreads)
     cu = [int(c) for c in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist") else cu_seqlens)]
     seq_ids = list(range(len(cu) - 1)) if seqs is None else list(seqs)
     outs, states = [], []
     for n in seq_ids:
         a, b = cu[n], cu[n + 1]
         sl = lambda x: x[:, a:b][:, :, heads]
+        slk = lambda x: x[:, a:b][:, :, kheads]
         s0n = None if s0 is None else s0[n:n + 1][:, heads]
-        o, s1 = gdn_recurrent(sl(q), sl(k), sl(v), sl(g), sl(beta), s0n, None, scale, nthreads)
+        o, s1 = gdn_recurrent(slk(q), slk(k), sl(v), sl(g), sl(beta), s0n, None, scale, nthreads)
         outs.append(o)
         states.append(s1)
     return outs, np.concatenate(states, axis=0)
@@ -226,39 +247,49 @@ def mixer(q_raw, k_raw, v_raw, z, a, b, conv_w, A, dt_bias=None, norm_w=None,
     """The whole token mixer from pre-projected inputs, in the order of the
     "Gated DeltaNet body" of the Linear Attention chapter: causal conv + SiLU
     over the concatenated q|k|v channels, split, L2-norm of q and k (eps 1e-6),
-    gates, the recurrence with ``scale``, then the gated RMSNorm with z.
+    gates, the KV head expansion when q and k have fewer heads than v, the
+    recurrence with ``scale``, then the gated RMSNorm with z.
 
-    q_raw, k_raw: [B, T, H, d_k]; v_raw, z: [B, T, H, d_v]; a, b: [B, T, H];
-    conv_w: [H*(2 d_k + d_v), 4] in channel order q, k, v. ``heads``/``rows``
-    restrict the computation to some heads / batch rows (channels of other
-    heads never mix with these ones). Returns out [b', T, h', d_v] (and the
-    intermediates when asked).
+    q_raw, k_raw: [B, T, H_k, d_k]; v_raw, z: [B, T, H, d_v]; a, b: [B, T, H];
+    conv_w: [2 H_k d_k + H d_v, 4] in channel order q, k, v. ``heads``/``rows``
+    restrict the computation to some value heads / batch rows (channels of
+    other heads never mix with these ones). Returns out [b', T, h', d_v] (and
+    the intermediates when asked; q and k there are per query/key head of the
+    selection, before the expansion).
     """
-    B, T, H, dk = q_raw.shape
-    dv = v_raw.shape[3]
+    B, T, Hk, dk = q_raw.shape
+    H, dv = v_raw.shape[2], v_raw.shape[3]
+    if H % Hk != 0:
+        raise ValueError("value heads must be a multiple of query/key heads")
+    grp = H // Hk
     heads = list(range(H)) if heads is None else list(heads)
+    kheads = sorted({h // grp for h in heads})     # query/key heads the selection reads
     rows = list(range(B)) if rows is None else list(rows)
     if cu_seqlens is not None and rows != [0]:
         raise ValueError("packed sequences use B == 1")
     cw = _f64(conv_w)
-    ch_q = [h * dk + j for h in heads for j in range(dk)]
-    ch_k = [H * dk + h * dk + j for h in heads for j in range(dk)]
-    ch_v = [2 * H * dk + h * dv + j for h in heads for j in range(dv)]
+    ch_q = [kh * dk + j for kh in kheads for j in range(dk)]
+    ch_k = [Hk * dk + kh * dk + j for kh in kheads for j in range(dk)]
+    ch_v = [2 * Hk * dk + h * dv + j for h in heads for j in range(dv)]
     w_sel = cw[ch_q + ch_k + ch_v]
     sel = lambda x: _f64(x)[rows][:, :, heads]
-    qs, ks, vs = sel(q_raw), sel(k_raw), sel(v_raw)
-    nb, nh = len(rows), len(heads)
-    mixed = np.concatenate([qs.reshape(nb, T, nh * dk), ks.reshape(nb, T, nh * dk),
+    selk = lambda x: _f64(x)[rows][:, :, kheads]
+    qs, ks, vs = selk(q_raw), selk(k_raw), sel(v_raw)
+    nb, nh, nk = len(rows), len(heads), len(kheads)
+    mixed = np.concatenate([qs.reshape(nb, T, nk * dk), ks.reshape(nb, T, nk * dk),
                             vs.reshape(nb, T, nh * dv)], axis=2)
     conv = causal_conv_silu(mixed, w_sel, cu_seqlens)
-    qc = conv[:, :, :nh * dk].reshape(nb, T, nh, dk)
-    kc = conv[:, :, nh * dk:2 * nh * dk].reshape(nb, T, nh, dk)
-    vc = conv[:, :, 2 * nh * dk:].reshape(nb, T, nh, dv)
+    qc = conv[:, :, :nk * dk].reshape(nb, T, nk, dk)
+    kc = conv[:, :, nk * dk:2 * nk * dk].reshape(nb, T, nk, dk)
+    vc = conv[:, :, 2 * nk * dk:].reshape(nb, T, nh, dv)
     qn, kn = l2norm(qc), l2norm(kc)
+    # the expansion, restricted to the selected value heads
+    pick = [kheads.index(h // grp) for h in heads]
+    qe, ke = qn[:, :, pick], kn[:, :, pick]
     Asel = _f64(A)[heads]
     dtb = None if dt_bias is None else _f64(dt_bias)[heads]
     g, beta = gates(sel(a), sel(b), Asel, dtb)
-    y, s1 = gdn_recurrent(qn, kn, vc, g, beta, None, cu_seqlens, scale)
+    y, s1 = gdn_recurrent(qe, ke, vc, g, beta, None, cu_seqlens, scale)
     out = gated_rmsnorm(y, sel(z), norm_w, eps)
     if return_intermediates:
         return out, dict(q=qn, k=kn, v=vc, g=g, beta=beta, y=y, s_final=s1)

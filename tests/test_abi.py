@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdn_version() == 1
+    assert lib.gdn_version() == 2
     for st in (GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_UNSUPPORTED, -5,
                GDN_ERR_WORKSPACE, 99):
         s = lib.gdn_status_string(st)
@@ -51,13 +51,14 @@ def test_version_and_status_strings(lib):
 P = ctypes.c_void_p(16)      # a non-null dummy pointer; never dereferenced on rejection
 
 
-def _prefill(lib, *, null=None, B=1, T=8, H=1, dk=128, dv=128, N=1, dtype=1, cu=None,
+def _prefill(lib, *, null=None, B=1, T=8, H=1, Hk=None, dk=128, dv=128, N=1, dtype=1, cu=None,
              ws=None, ws_bytes=0):
     ptrs = [P] * 8
     if null is not None:
         ptrs[null] = None
     q, k, v, g, beta, s0, s1, o = ptrs
-    return lib.gdn_prefill(q, k, v, g, beta, s0, s1, o, cu, B, T, H, dk, dv, N, 1.0, dtype,
+    Hk = H if Hk is None else Hk
+    return lib.gdn_prefill(q, k, v, g, beta, s0, s1, o, cu, B, T, H, Hk, dk, dv, N, 1.0, dtype,
                            ws, ws_bytes, None)
 
 
@@ -111,14 +112,19 @@ def test_prefill_validation(lib):
     assert _prefill(lib, dk=48) == GDN_ERR_UNSUPPORTED
     assert _prefill(lib, dv=256) == GDN_ERR_UNSUPPORTED
     assert _prefill(lib, B=1 << 16, N=1 << 16, T=1 << 16) == GDN_ERR_SHAPE
+    # grouped heads: H_k must divide H
+    assert _prefill(lib, H=4, Hk=0) == GDN_ERR_SHAPE
+    assert _prefill(lib, H=4, Hk=3) == GDN_ERR_SHAPE
+    assert _prefill(lib, H=4, Hk=8) == GDN_ERR_SHAPE
 
 
 def test_decode_validation(lib):
     f = lib.gdn_decode_step
-    assert f(P, P, P, P, P, None, P, 1, 1, 128, 128, 1.0, 1, None) == GDN_ERR_NULL
-    assert f(P, P, P, P, P, P, P, 1, 1, 128, 128, 1.0, 2, None) == GDN_ERR_DTYPE
-    assert f(P, P, P, P, P, P, P, 0, 1, 128, 128, 1.0, 1, None) == GDN_ERR_SHAPE
-    assert f(P, P, P, P, P, P, P, 1, 1, 100, 128, 1.0, 1, None) == GDN_ERR_UNSUPPORTED
+    assert f(P, P, P, P, P, None, P, 1, 1, 1, 128, 128, 1.0, 1, None) == GDN_ERR_NULL
+    assert f(P, P, P, P, P, P, P, 1, 1, 1, 128, 128, 1.0, 2, None) == GDN_ERR_DTYPE
+    assert f(P, P, P, P, P, P, P, 0, 1, 1, 128, 128, 1.0, 1, None) == GDN_ERR_SHAPE
+    assert f(P, P, P, P, P, P, P, 1, 6, 4, 128, 128, 1.0, 1, None) == GDN_ERR_SHAPE
+    assert f(P, P, P, P, P, P, P, 1, 1, 1, 100, 128, 1.0, 1, None) == GDN_ERR_UNSUPPORTED
 
 
 def test_mixer_validation(lib):
@@ -126,10 +132,11 @@ def test_mixer_validation(lib):
     args = [P] * 7 + [None, None] + [P] * 5
     bad = list(args)
     bad[0] = None
-    assert pro(*bad, 1, 4, 1, 128, 128, 1, 1, None) == GDN_ERR_NULL
-    assert pro(*args, 1, 4, 1, 128, 128, 1, 5, None) == GDN_ERR_DTYPE
-    assert pro(*args, 1, 4, 1, 96, 128, 1, 1, None) == GDN_ERR_UNSUPPORTED
-    assert pro(*args, 2, 4, 1, 128, 128, 1, 1, None) == GDN_ERR_SHAPE
+    assert pro(*bad, 1, 4, 1, 1, 128, 128, 1, 1, None) == GDN_ERR_NULL
+    assert pro(*args, 1, 4, 1, 1, 128, 128, 1, 5, None) == GDN_ERR_DTYPE
+    assert pro(*args, 1, 4, 1, 1, 96, 128, 1, 1, None) == GDN_ERR_UNSUPPORTED
+    assert pro(*args, 2, 4, 1, 1, 128, 128, 1, 1, None) == GDN_ERR_SHAPE
+    assert pro(*args, 1, 4, 2, 4, 128, 128, 1, 1, None) == GDN_ERR_SHAPE
     epi = lib.gdn_mixer_epilogue
     assert epi(None, P, None, P, 4, 1, 128, 1e-6, 1, None) == GDN_ERR_NULL
     assert epi(P, P, None, P, 4, 1, 100, 1e-6, 1, None) == GDN_ERR_UNSUPPORTED
@@ -151,18 +158,18 @@ def test_prepare_apply_validation(lib):
     ws = ctypes.c_void_p(1 << 20)            # never dereferenced: rejected before launch
     prep, app = lib.gdn_prefill_prepare, lib.gdn_prefill_apply
     # only the MFMA chunk path has two passes
-    assert prep(P, P, P, P, None, 1, 100, 1, 64, 64, 1, 1, ws, need, None) == GDN_ERR_UNSUPPORTED
-    assert prep(P, P, P, P, None, 1, 100, 1, 128, 128, 1, 0, ws, need, None) == GDN_ERR_UNSUPPORTED
+    assert prep(P, P, P, P, None, 1, 100, 1, 1, 64, 64, 1, 1, ws, need, None) == GDN_ERR_UNSUPPORTED
+    assert prep(P, P, P, P, None, 1, 100, 1, 1, 128, 128, 1, 0, ws, need, None) == GDN_ERR_UNSUPPORTED
     # the workspace is required and checked
-    assert prep(P, P, P, P, None, 1, 100, 1, 128, 128, 1, 1, None, 0, None) == GDN_ERR_NULL
-    assert prep(P, P, P, P, None, 1, 100, 1, 128, 128, 1, 1, ws, need - 1, None) == GDN_ERR_WORKSPACE
-    assert prep(None, P, P, P, None, 1, 100, 1, 128, 128, 1, 1, ws, need, None) == GDN_ERR_NULL
-    assert prep(P, None, P, P, None, 1, 100, 1, 128, 128, 1, 1, ws, need, None) == GDN_ERR_NULL
-    assert prep(P, P, P, P, None, 2, 100, 1, 128, 128, 1, 1, ws, need, None) == GDN_ERR_SHAPE
+    assert prep(P, P, P, P, None, 1, 100, 1, 1, 128, 128, 1, 1, None, 0, None) == GDN_ERR_NULL
+    assert prep(P, P, P, P, None, 1, 100, 1, 1, 128, 128, 1, 1, ws, need - 1, None) == GDN_ERR_WORKSPACE
+    assert prep(None, P, P, P, None, 1, 100, 1, 1, 128, 128, 1, 1, ws, need, None) == GDN_ERR_NULL
+    assert prep(P, None, P, P, None, 1, 100, 1, 1, 128, 128, 1, 1, ws, need, None) == GDN_ERR_NULL
+    assert prep(P, P, P, P, None, 2, 100, 1, 1, 128, 128, 1, 1, ws, need, None) == GDN_ERR_SHAPE
     a = [P] * 3 + [P, None, None, P, None]
-    assert app(*a, 1, 100, 1, 128, 128, 1, 1.0, 1, None, 0, None) == GDN_ERR_NULL
-    assert app(*a, 1, 100, 1, 128, 128, 1, 1.0, 1, ws, need - 1, None) == GDN_ERR_WORKSPACE
-    assert app(*a, 1, 100, 1, 16, 16, 1, 1.0, 1, ws, need, None) == GDN_ERR_UNSUPPORTED
+    assert app(*a, 1, 100, 1, 1, 128, 128, 1, 1.0, 1, None, 0, None) == GDN_ERR_NULL
+    assert app(*a, 1, 100, 1, 1, 128, 128, 1, 1.0, 1, ws, need - 1, None) == GDN_ERR_WORKSPACE
+    assert app(*a, 1, 100, 1, 1, 16, 16, 1, 1.0, 1, ws, need, None) == GDN_ERR_UNSUPPORTED
     b = list(a)
     b[6] = None                              # o
-    assert app(*b, 1, 100, 1, 128, 128, 1, 1.0, 1, ws, need, None) == GDN_ERR_NULL
+    assert app(*b, 1, 100, 1, 1, 128, 128, 1, 1.0, 1, ws, need, None) == GDN_ERR_NULL

@@ -132,6 +132,35 @@ def test_orthogonal_keys_closed_form(oracle_mod, seed):
         np.testing.assert_allclose(s[0, h], ref_s, rtol=1e-12, atol=1e-13)
 
 
+def test_grouped_heads_closed_form(oracle_mod):
+    """Grouped heads ("Linear Attention" chapter, "Gated DeltaNet body" layer
+    code: q and k repeated along the head axis with repeat_interleave): with
+    H_k = 2 query/key heads and H = 4 value heads, value head h reads key
+    head h // 2 (heads 0, 1 -> 0; 2, 3 -> 1), checked against the orthogonal-
+    keys closed form written with that index."""
+    rng = np.random.default_rng(12)
+    T, dk, dv, H, Hk = 5, 6, 3, 4, 2
+    q = rng.standard_normal((1, T, Hk, dk))
+    k = np.stack([_orthonormal_keys(rng, T, dk) for _ in range(Hk)], axis=1)[None]
+    v = rng.standard_normal((1, T, H, dv))
+    g = np.log(rng.uniform(0.3, 1.0, (1, T, H)))
+    beta = rng.uniform(0.1, 1.0, (1, T, H))
+    o, s = oracle_mod.gdn_recurrent(q, k, v, g, beta, scale=1.0)
+    assert o.shape == (1, T, H, dv) and s.shape == (1, H, dv, dk)
+    for h in range(H):
+        kh = h // (H // Hk)
+        for t in range(T):
+            ref = np.zeros(dv)
+            for i in range(t + 1):
+                dec = math.exp(g[0, i + 1:t + 1, h].sum())
+                ref += dec * beta[0, i, h] * v[0, i, h] * (k[0, i, kh] @ q[0, t, kh])
+            np.testing.assert_allclose(o[0, t, h], ref, rtol=1e-12, atol=1e-13)
+    # the sampled-heads form picks the same query/key heads
+    o2, s2 = oracle_mod.gdn_recurrent_heads(q, k, v, g, beta, heads=[3, 0], scale=1.0)
+    np.testing.assert_array_equal(o2, o[:, :, [3, 0]])
+    np.testing.assert_array_equal(s2, s[:, [3, 0]])
+
+
 def test_linear_attention_special_case(oracle_mod):
     """alpha = 1, beta = 1 and orthonormal keys: exactly causal linear attention
     o_t = sum_{i<=t} v_i (k_i . q_t) ("Overwrite and Forget" section 1)."""
@@ -305,3 +334,39 @@ def test_mixer_composition(oracle_mod):
     np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12)
     part = oracle_mod.mixer(qr, kr, vr, z, a, b, w, A, scale=scale, heads=[2, 0], rows=[1])
     np.testing.assert_allclose(part, out[[1]][:, :, [2, 0]], rtol=1e-13, atol=1e-14)
+
+
+def test_mixer_composition_grouped_heads(oracle_mod):
+    """The mixer with H_k = 2 query/key heads and H = 4 value heads: conv
+    channels are 2 H_k d_k of q|k then H d_v of v, the gates are per value
+    head, and value head h reads the normalised q, k of head h // 2; rebuilt
+    from numpy/scipy pieces around the pinned recurrence."""
+    rng = np.random.default_rng(10)
+    B, T, H, Hk, dk, dv = 1, 8, 4, 2, 4, 3
+    qr = rng.standard_normal((B, T, Hk, dk))
+    kr = rng.standard_normal((B, T, Hk, dk))
+    vr = rng.standard_normal((B, T, H, dv))
+    z = rng.standard_normal((B, T, H, dv))
+    a = rng.standard_normal((B, T, H))
+    b = rng.standard_normal((B, T, H))
+    w = rng.standard_normal((2 * Hk * dk + H * dv, 4)) * 0.5
+    A = rng.uniform(0.5, 2, H)
+    out = oracle_mod.mixer(qr, kr, vr, z, a, b, w, A, scale=0.5)
+
+    def conv(x, wc):
+        pre = np.convolve(x, wc[::-1])[:T]
+        return pre * expit(pre)
+    mixed = np.concatenate([qr.reshape(B, T, -1), kr.reshape(B, T, -1), vr.reshape(B, T, -1)], 2)
+    y = np.stack([conv(mixed[0, :, c], w[c]) for c in range(mixed.shape[2])], 1)[None]
+    q = y[:, :, :Hk * dk].reshape(B, T, Hk, dk)
+    k = y[:, :, Hk * dk:2 * Hk * dk].reshape(B, T, Hk, dk)
+    v = y[:, :, 2 * Hk * dk:].reshape(B, T, H, dv)
+    q = q / np.sqrt((q ** 2).sum(-1, keepdims=True) + 1e-6)
+    k = k / np.sqrt((k ** 2).sum(-1, keepdims=True) + 1e-6)
+    idx = [h // (H // Hk) for h in range(H)]
+    core, _ = oracle_mod.gdn_recurrent(q[:, :, idx], k[:, :, idx], v, -A * np.logaddexp(0, a),
+                                       expit(b), scale=0.5)
+    ref = core / np.sqrt((core ** 2).mean(-1, keepdims=True) + 1e-6) * z * expit(z)
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12)
+    part = oracle_mod.mixer(qr, kr, vr, z, a, b, w, A, scale=0.5, heads=[3, 1])
+    np.testing.assert_allclose(part, out[:, :, [3, 1]], rtol=1e-13, atol=1e-14)

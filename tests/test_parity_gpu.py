@@ -347,3 +347,75 @@ def test_prepare_then_apply_equals_prefill():
     o, _ = gdn.gdn_prefill_apply(q, k, v, g, ws, s0, fin, cu_seqlens=cu, scale=c.scale)
     o_ref, f_ref = run_prefill(c, path="two_pass")
     assert torch.equal(o, o_ref) and torch.equal(fin, f_ref)
+
+
+# --- grouped query/key heads (H_k < H) -----------------------------------------
+
+@pytest.mark.parametrize("Hk", [1, 2])
+@pytest.mark.parametrize("path", PATHS)
+def test_prefill_grouped_heads(Hk, path):
+    """H = 4 value heads reading H_k query/key heads (value head h uses key
+    head h // (H / H_k)), bf16 d=128 on both chunk paths, several chunks and a
+    ragged tail, non-zero initial state."""
+    c = inputs.make_prefill(seed=61 + Hk, B=2, T=193, H=4, Hk=Hk, with_state=True)
+    o, fin = run_prefill(c, path=path)
+    o_ref, s_ref = oracle_prefill(c)
+    eo, es = o_err(o, o_ref), s_err(fin, s_ref)
+    report(f"grouped heads H4 Hk{Hk} {path}", o=eo, state=es)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_varlen_grouped_heads(path):
+    """Packed sequences with grouped heads (H = 6, H_k = 3)."""
+    c = inputs.make_varlen(seed=63, H=6, Hk=3, d=128, lengths=[130, 0, 64, 7, 200])
+    o, fin = run_prefill(c, path=path)
+    o_ref, s_ref = oracle_prefill(c)
+    cu = [int(x) for x in c.cu_seqlens.tolist()]
+    eo, es = o_err_packed(o, o_ref, cu), s_err(fin, s_ref)
+    report(f"varlen grouped heads {path}", o=eo, state=es)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 32)])
+def test_prefill_recurrent_grouped_heads(dtype, d):
+    """The token-serial kernel with grouped heads (fp32 1e-4, bf16 2e-2)."""
+    c = inputs.make_prefill(seed=64, B=2, T=70, H=6, Hk=2, d=d, dtype=dtype, with_state=True)
+    o, fin = run_prefill(c, entry=gdn.gdn_prefill_recurrent)
+    o_ref, s_ref = oracle_prefill(c)
+    eo, es = o_err(o, o_ref), s_err(fin, s_ref)
+    report(f"recurrent grouped heads {dtype} d{d}", o=eo, state=es)
+    assert eo <= _tol(c) and es <= _tol(c)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_grouped_heads(dtype):
+    c = inputs.make_decode(seed=65, B=3, H=8, Hk=2, d=128, dtype=dtype)
+    st = dev(c.s0)
+    o = gdn.gdn_decode_step(dev(c.q[:, 0]), dev(c.k[:, 0]), dev(c.v[:, 0]), dev(c.g[:, 0]),
+                            dev(c.beta[:, 0]), st, scale=c.scale)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_prefill(c)
+    eo, es = o_err(o[:, None], o_ref), s_err(st, s_ref)
+    report(f"decode grouped heads {dtype}", o=eo, state=es)
+    assert eo <= _tol(c) and es <= _tol(c)
+
+
+def test_mixer_grouped_heads():
+    """Prologue -> prefill -> epilogue with H_k = 2 query/key heads and H = 4
+    value heads: conv channels 2 H_k d + H d, gates per value head."""
+    c = inputs.make_mixer(seed=66, B=2, T=150, H=4, Hk=2, d=128)
+    q, k, v, g, beta = gdn.gdn_mixer_prologue(dev(c.q_raw), dev(c.k_raw), dev(c.v_raw),
+                                              dev(c.conv_w), dev(c.a), dev(c.b), dev(c.A))
+    y, _ = gdn.gdn_prefill(q, k, v, g, beta, scale=c.scale)
+    out = gdn.gdn_mixer_epilogue(y, dev(c.z), eps=c.eps)
+    torch.cuda.synchronize()
+    ref, mid = oracle.mixer(c.q_raw, c.k_raw, c.v_raw, c.z, c.a, c.b, c.conv_w, c.A,
+                            scale=c.scale, eps=c.eps, return_intermediates=True)
+    e_out, e_y = o_err(out.cpu(), ref), o_err(y.cpu(), mid["y"])
+    e_q, e_k, e_v = o_err(q.cpu(), mid["q"]), o_err(k.cpu(), mid["k"]), o_err(v.cpu(), mid["v"])
+    e_g = float(np.abs(host64(g.cpu()) - mid["g"]).max() / np.abs(mid["g"]).max())
+    e_b = float(np.abs(host64(beta.cpu()) - mid["beta"]).max())
+    report("mixer grouped heads", out=e_out, y=e_y, q=e_q, k=e_k, v=e_v, g=e_g, beta=e_b)
+    assert max(e_q, e_k, e_v) <= TOL_BF16 and e_g <= 1e-5 and e_b <= 1e-6
+    assert e_y <= TOL_BF16 and e_out <= TOL_BF16
