@@ -24,6 +24,9 @@ carries:
   each chunk's system on the sequential path);
 * ``decode``: one in-place step of B=256, H=32, d=128 fp32 states (512 MiB),
   GB/s of algorithmic traffic and its fraction of 8 TB/s;
+* ``decode_mixer``: one fused single-token mixer step (conv against the
+  3-token cache, norms, gates, state update, gated RMSNorm) at B=256, H=32,
+  d=128, GB/s of algorithmic traffic against 8 TB/s;
 * ``mixer``: prologue -> prefill -> epilogue at B=8, T=8192, H=16, d=128;
 * ``varlen``: packed prefill, H=32, 8 sequences, lengths log-uniform in
   [512, 65536], non-zero initial states;
@@ -191,6 +194,39 @@ def bench_decode(gdn, inputs, steps, warmup):
                 frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
 
 
+def decode_mixer_bytes(B, H, Hk, dk=128, dv=128, elt=2):
+    """Algorithmic HBM bytes of one fused mixer step: the fp32 state read and
+    written; the conv cache (3 inputs per channel) read and written; the
+    token's raw q, k, v, z, a, b read and the output written; the conv
+    weights and A read once."""
+    C = 2 * Hk * dk + H * dv
+    per_seq = 2 * H * dv * dk * 4 + 2 * 3 * C * elt + (C + H * dv) * elt + 2 * H * elt + H * dv * elt
+    return B * per_seq + C * 4 * elt + H * 4
+
+
+def bench_decode_mixer(gdn, inputs, steps, warmup):
+    import torch
+    c = inputs.make_decode_mixer()
+    d = lambda t: t.cuda().contiguous()
+    q, k, v, z, a, b, w, A = (d(x) for x in (c.q_raw, c.k_raw, c.v_raw, c.z, c.a, c.b,
+                                               c.conv_w, c.A))
+    cache, st = d(c.conv_state), d(c.state)
+    out = torch.empty_like(v)
+
+    def step(i):
+        gdn.gdn_decode_mixer_step(q, k, v, w, cache, a, b, A, z, st, out=out, scale=c.scale,
+                                  eps=c.eps)
+    ms = event_time(step, steps, warmup)
+    B, H, dv = v.shape
+    nbytes = decode_mixer_bytes(B, H, q.shape[1], q.shape[2], dv)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return dict(workload="fused mixer decode step B=256 H=32 d=128 bf16: conv against a 3-token "
+                         "cache + SiLU, L2-norm, gates, state update (512 MiB fp32 in place), "
+                         "gated RMSNorm",
+                us_per_step=round(ms * 1e3, 2), bytes_per_step=nbytes,
+                **{"GB/s": round(gbs, 1)}, frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
+
+
 def bench_mixer(gdn, inputs, steps, warmup):
     import torch
     c = inputs.make_mixer()
@@ -289,8 +325,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="prefill,decode,mixer,varlen,cpu",
-                    help="comma list of: prefill, decode, mixer, varlen, cpu, copy")
+    ap.add_argument("--only", default="prefill,decode,decode_mixer,mixer,varlen,cpu",
+                    help="comma list of: prefill, decode, decode_mixer, mixer, varlen, cpu, copy")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -342,6 +378,8 @@ def main():
                        "config": {"workload": "partial run: " + args.only}})
     if "decode" in which:
         result["decode"] = bench_decode(gdn, inputs, args.steps, args.warmup)
+    if "decode_mixer" in which:
+        result["decode_mixer"] = bench_decode_mixer(gdn, inputs, args.steps, args.warmup)
     if "mixer" in which:
         result["mixer"] = bench_mixer(gdn, inputs, args.steps, args.warmup)
     if "varlen" in which:

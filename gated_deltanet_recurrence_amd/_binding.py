@@ -41,6 +41,7 @@ _SIGS = {
     "gdn_decode_step": [_vp] * 7 + [_i] * 5 + [_f, _i, _vp],
     "gdn_mixer_prologue": [_vp] * 14 + [_i] * 8 + [_vp],
     "gdn_mixer_epilogue": [_vp] * 4 + [_i] * 3 + [_f, _i, _vp],
+    "gdn_decode_mixer_step": [_vp] * 11 + [_f, _vp, _vp] + [_i] * 5 + [_f, _i, _vp],
 }
 EXPORTED = tuple(_SIGS)
 
@@ -261,4 +262,29 @@ def gdn_mixer_epilogue(y, z, norm_w=None, out=None, eps=1e-6):
         _dev(y, "y", dt), _dev(z, "z", dt, y.shape), _dev(norm_w, "norm_w", torch.float32, (dv,)),
         _dev(out, "out", dt, y.shape), B * T, H, dv, float(eps), _dtype_code(y),
         _stream(y.device)))
+    return out
+
+
+def gdn_decode_mixer_step(q_raw, k_raw, v_raw, conv_w, conv_state, a, b, A, z, state,
+                          dt_bias=None, norm_w=None, out=None, scale=None, eps=1e-6):
+    """One token of the whole mixer (see include/gdn.h). q_raw, k_raw: [B,H_k,d_k];
+    v_raw, z: [B,H,d_v]; a, b: [B,H]; conv_state: [B,3,2*H_k*d_k + H*d_v] and
+    state: [B,H,d_v,d_k] fp32 are updated in place. Returns out [B,H,d_v]."""
+    B, Hk, dk = q_raw.shape
+    H, dv = v_raw.shape[1], v_raw.shape[2]
+    dt = q_raw.dtype
+    C = 2 * Hk * dk + H * dv
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=dt, device=q_raw.device)
+    if scale is None:
+        scale = dk ** -0.5
+    _check(load().gdn_decode_mixer_step(
+        _dev(q_raw, "q_raw", dt), _dev(k_raw, "k_raw", dt, q_raw.shape),
+        _dev(v_raw, "v_raw", dt, (B, H, dv)), _dev(conv_w, "conv_w", dt, (C, 4)),
+        _dev(conv_state, "conv_state", dt, (B, 3, C)),
+        _dev(a, "a", dt, (B, H)), _dev(b, "b", dt, (B, H)), _dev(A, "A", torch.float32, (H,)),
+        _dev(dt_bias, "dt_bias", torch.float32, (H,)), _dev(z, "z", dt, (B, H, dv)),
+        _dev(norm_w, "norm_w", torch.float32, (dv,)), float(eps),
+        _dev(state, "state", torch.float32, (B, H, dv, dk)), _dev(out, "out", dt, (B, H, dv)),
+        B, H, Hk, dk, dv, float(scale), _dtype_code(q_raw), _stream(q_raw.device)))
     return out

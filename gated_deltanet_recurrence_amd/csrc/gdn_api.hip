@@ -31,6 +31,12 @@ hipError_t launch_prologue(const void *, const void *, const void *, const void 
                            void *, void *, float *, float *, int, int, int, int, int, int, int,
                            hipStream_t);
 template <typename TIO>
+hipError_t launch_decode_mixer(const void *, const void *, const void *, const void *, void *,
+                               const void *, const void *, const float *, const float *,
+                               const void *, const float *, float, float *, void *, int, int,
+                               int, int, int, float, hipStream_t);
+constexpr int DECODE_MIXER_MAX_ROWS = 4096;
+template <typename TIO>
 hipError_t launch_epilogue(const void *, const void *, const float *, void *, long, int, float,
                            hipStream_t);
 }  // namespace gdn
@@ -249,6 +255,31 @@ int gdn_mixer_epilogue(const void *y, const void *z, const float *norm_w, void *
     hipError_t e = dtype == GDN_DTYPE_BF16
         ? gdn::launch_epilogue<gdn::bf16>(y, z, norm_w, out, r, d_v, eps, s)
         : gdn::launch_epilogue<float>(y, z, norm_w, out, r, d_v, eps, s);
+    return status_of(e);
+}
+
+int gdn_decode_mixer_step(const void *q_raw, const void *k_raw, const void *v_raw,
+                          const void *conv_w, void *conv_state, const void *a, const void *b,
+                          const float *A, const float *dt_bias, const void *z,
+                          const float *norm_w, float eps, float *state, void *out, int B, int H,
+                          int H_k, int d_k, int d_v, float scale, int dtype, void *stream)
+{
+    if (!q_raw || !k_raw || !v_raw || !conv_w || !conv_state || !a || !b || !A || !z || !state ||
+        !out)
+        return GDN_ERR_NULL;
+    if (!valid_dtype(dtype)) return GDN_ERR_DTYPE;
+    if (B < 1 || d_k < 1 || d_v < 1 || !heads_ok(H, H_k) || !(eps >= 0.0f)) return GDN_ERR_SHAPE;
+    if ((int64_t)B * H > (int64_t)INT32_MAX) return GDN_ERR_SHAPE;
+    if (!head_dim_pow2(d_k) || !mixer_dim(d_v)) return GDN_ERR_UNSUPPORTED;
+    if ((int64_t)(H / H_k) * d_v > gdn::DECODE_MIXER_MAX_ROWS) return GDN_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = dtype == GDN_DTYPE_BF16
+        ? gdn::launch_decode_mixer<gdn::bf16>(q_raw, k_raw, v_raw, conv_w, conv_state, a, b, A,
+                                              dt_bias, z, norm_w, eps, state, out, B, H, H_k,
+                                              d_k, d_v, scale, s)
+        : gdn::launch_decode_mixer<float>(q_raw, k_raw, v_raw, conv_w, conv_state, a, b, A,
+                                          dt_bias, z, norm_w, eps, state, out, B, H, H_k, d_k,
+                                          d_v, scale, s);
     return status_of(e);
 }
 

@@ -14,6 +14,8 @@ Workloads (all shapes token-major, ``[B, T, H, D]``):
 * ``mixer``   - B=8, T=8192, H=16, d=128, raw (pre-conv) bf16 projections.
 * ``varlen``  - H=32, d=128, 8 packed sequences, lengths log-uniform in
                 [512, 65536], non-zero initial states.
+* ``decode_mixer`` - one token of the whole mixer at B=256, H=32, d=128:
+                raw projections, a conv cache and the fp32 state.
 
 Conventions shared by every recipe:
 
@@ -33,8 +35,9 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "GDNCase", "MixerCase", "unit_gaussian", "log_uniform_lengths",
+    "GDNCase", "MixerCase", "DecodeMixerCase", "unit_gaussian", "log_uniform_lengths",
     "make_tiny", "make_prefill", "make_decode", "make_mixer", "make_varlen",
+    "make_decode_mixer",
     "make_case", "WORKLOADS",
 ]
 
@@ -265,12 +268,62 @@ def make_varlen(seed: int = 5, n_seq: int = 8, H: int = 32, d: int = 128,
                    meta={"lengths": lengths, "A": A})
 
 
+@dataclass
+class DecodeMixerCase:
+    """Inputs of one fused single-token mixer step, on the host.
+
+    q_raw, k_raw: [B, H_k, d_k]; v_raw, z: [B, H, d_v]; a, b: [B, H];
+    conv_w: [C, 4], C = 2*H_k*d_k + H*d_v; conv_state: [B, 3, C] (the last
+    three raw inputs per channel, oldest first); state: [B, H, d_v, d_k] fp32;
+    A: [H] fp32.
+    """
+    name: str
+    q_raw: torch.Tensor
+    k_raw: torch.Tensor
+    v_raw: torch.Tensor
+    z: torch.Tensor
+    a: torch.Tensor
+    b: torch.Tensor
+    conv_w: torch.Tensor
+    conv_state: torch.Tensor
+    A: torch.Tensor
+    state: torch.Tensor
+    scale: float
+    eps: float
+    dtype: str
+
+
+def make_decode_mixer(seed: int = 6, B: int = 256, H: int = 32, d: int = 128,
+                      dtype: str = "bf16", Hk: Optional[int] = None) -> DecodeMixerCase:
+    """One token of the mixer at the decode shape: the token's projections
+    q,k,v,z,a,b ~ N(0,1); conv weights N(0, 0.5); a conv cache of three earlier
+    raw inputs N(0,1) per channel; fp32 state N(0, 0.02); A ~ U(0.5, 2) per
+    head; no dt_bias, norm weight ones, eps 1e-6, scale d^-1/2."""
+    gen = _gen(seed)
+    td = _TORCH_DTYPE[dtype]
+    Hk = H if Hk is None else Hk
+    C = 2 * Hk * d + H * d
+    q = _normal(gen, (B, Hk, d)).to(td)
+    k = _normal(gen, (B, Hk, d)).to(td)
+    v = _normal(gen, (B, H, d)).to(td)
+    z = _normal(gen, (B, H, d)).to(td)
+    a = _normal(gen, (B, H)).to(td)
+    b = _normal(gen, (B, H)).to(td)
+    conv_w = _normal(gen, (C, 4), std=0.5).to(td)
+    conv_state = _normal(gen, (B, 3, C)).to(td)
+    A = _uniform(gen, (H,), 0.5, 2.0)
+    state = _normal(gen, (B, H, d, d), std=0.02)
+    return DecodeMixerCase("decode_mixer", q, k, v, z, a, b, conv_w, conv_state, A, state,
+                           1.0 / math.sqrt(d), 1e-6, dtype)
+
+
 WORKLOADS = {
     "tiny": make_tiny,
     "prefill": make_prefill,
     "decode": make_decode,
     "mixer": make_mixer,
     "varlen": make_varlen,
+    "decode_mixer": make_decode_mixer,
 }
 
 

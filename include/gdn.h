@@ -270,6 +270,47 @@ int gdn_mixer_epilogue(const void *y, const void *z, const float *norm_w, void *
                        int rows, int H, int d_v, float eps, int dtype, void *stream);
 
 /*
+ * gdn_decode_mixer_step - one token of the whole token mixer for B
+ * sequences, fused into one launch ("6.6 Gated DeltaNet" section 6.6.8,
+ * inference flow; the conv cache is the convolution state a deployment keeps
+ * besides the matrix state, "Overwrite and Forget" section 13.4):
+ *
+ *   1. per conv channel, the causal 4-tap convolution of the three cached
+ *      inputs and the new one, then SiLU (as gdn_mixer_prologue over a
+ *      sequence); the cache is shifted by one token in place;
+ *   2. L2-norm of q and k; g = -A softplus(a + dt_bias), beta = sigmoid(b);
+ *   3. the gated delta rule step of gdn_decode_step on the state (in place),
+ *      value head h reading query/key head h / (H / H_k);
+ *   4. out = norm_w * y / sqrt(mean(y^2) + eps) * silu(z) per (sequence,
+ *      value head), y the step's output.
+ *
+ * Running T steps from a zero cache and a zero state gives the same outputs as
+ * gdn_mixer_prologue -> gdn_prefill -> gdn_mixer_epilogue over those T tokens
+ * (up to rounding: intermediates stay fp32 here).
+ *
+ *   q_raw, k_raw  [B][H_k][d_k], dtype     the token's projections
+ *   v_raw, z      [B][H][d_v], dtype
+ *   conv_w        [2*H_k*d_k + H*d_v][4], dtype (channel order q, k, v; tap 3
+ *                 multiplies the new token)
+ *   conv_state    [B][3][2*H_k*d_k + H*d_v], dtype, read and updated in place:
+ *                 row 0 = the input three tokens back, row 2 = the previous
+ *                 token; all zeros for a sequence that has not started
+ *   a, b          [B][H], dtype;  A [H] fp32;  dt_bias [H] fp32 or NULL (zero)
+ *   norm_w        [d_v] fp32 or NULL (ones);  eps >= 0
+ *   state         [B][H][d_v][d_k] fp32, read and updated in place
+ *   out           [B][H][d_v], dtype; may alias z, no other argument
+ *   d_k, d_v      d_k in {16, 32, 64, 128}; d_v in {16, 32, 64, 128, 256};
+ *                 (H / H_k) * d_v <= 4096 (else GDN_ERR_UNSUPPORTED)
+ */
+int gdn_decode_mixer_step(const void *q_raw, const void *k_raw, const void *v_raw,
+                          const void *conv_w, void *conv_state,
+                          const void *a, const void *b, const float *A, const float *dt_bias,
+                          const void *z, const float *norm_w, float eps,
+                          float *state, void *out,
+                          int B, int H, int H_k, int d_k, int d_v,
+                          float scale, int dtype, void *stream);
+
+/*
  * gdn_check_cu_seqlens - host-side validation of packed-sequence offsets.
  * cu is a HOST array of N+1 entries. Returns GDN_OK when cu[0] = 0, the
  * offsets are non-decreasing and cu[N] = T; GDN_ERR_SHAPE otherwise;

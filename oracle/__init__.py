@@ -294,3 +294,34 @@ def mixer(q_raw, k_raw, v_raw, z, a, b, conv_w, A, dt_bias=None, norm_w=None,
     if return_intermediates:
         return out, dict(q=qn, k=kn, v=vc, g=g, beta=beta, y=y, s_final=s1)
     return out
+
+
+def mixer_decode_step(q_raw, k_raw, v_raw, z, a, b, conv_w, conv_state, A, state,
+                      dt_bias=None, norm_w=None, scale: float = 1.0, eps: float = 1e-6):
+    """One token of the token mixer for B sequences, in the order of the
+    inference flow of "6.6 Gated DeltaNet" (section 6.6.8): the new token's
+    q, k, v and gates, the state update, the read with q, the gated RMSNorm.
+    The short convolution keeps, per channel, the inputs of the three previous
+    tokens (the convolution state a deployment caches beside the matrix state,
+    "Overwrite and Forget" section 13.4); the output for the new token is the
+    causal convolution over that window, exactly as ``causal_conv_silu`` would
+    produce it for the last token of the sequence.
+
+    q_raw, k_raw: [B, H_k, d_k]; v_raw, z: [B, H, d_v]; a, b: [B, H];
+    conv_w: [C, 4], C = 2 H_k d_k + H d_v (channel order q, k, v);
+    conv_state: [B, 3, C], oldest input first; state: [B, H, d_v, d_k].
+    Returns (out [B, H, d_v], new state, new conv_state), float64.
+    """
+    qr, kr, vr = _f64(q_raw), _f64(k_raw), _f64(v_raw)
+    B, Hk, dk = qr.shape
+    H, dv = vr.shape[1], vr.shape[2]
+    x_t = np.concatenate([qr.reshape(B, -1), kr.reshape(B, -1), vr.reshape(B, -1)], axis=1)
+    window = np.concatenate([_f64(conv_state), x_t[:, None, :]], axis=1)     # [B, 4, C]
+    conv = causal_conv_silu(window, conv_w)[:, 3]                             # [B, C]
+    q = l2norm(conv[:, :Hk * dk].reshape(B, 1, Hk, dk))
+    k = l2norm(conv[:, Hk * dk:2 * Hk * dk].reshape(B, 1, Hk, dk))
+    v = conv[:, 2 * Hk * dk:].reshape(B, 1, H, dv)
+    g, beta = gates(_f64(a)[:, None], _f64(b)[:, None], A, dt_bias)
+    y, s1 = gdn_recurrent(q, k, v, g, beta, _f64(state), None, scale)
+    out = gated_rmsnorm(y[:, 0], z, norm_w, eps)
+    return out, s1, np.ascontiguousarray(window[:, 1:])

@@ -370,3 +370,35 @@ def test_mixer_composition_grouped_heads(oracle_mod):
     np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12)
     part = oracle_mod.mixer(qr, kr, vr, z, a, b, w, A, scale=0.5, heads=[3, 1])
     np.testing.assert_allclose(part, out[:, :, [3, 1]], rtol=1e-13, atol=1e-14)
+
+
+def test_mixer_decode_steps_continue_the_sequence(oracle_mod):
+    """T single-token mixer steps from an empty conv cache and a zero state
+    give the outputs and the final state of the pinned mixer over the same T
+    tokens (the cache holds each channel's last three inputs, oldest first),
+    and the cache then holds the last three raw inputs."""
+    rng = np.random.default_rng(13)
+    B, T, H, Hk, dk, dv = 2, 6, 4, 2, 4, 3
+    qr = rng.standard_normal((B, T, Hk, dk))
+    kr = rng.standard_normal((B, T, Hk, dk))
+    vr = rng.standard_normal((B, T, H, dv))
+    z = rng.standard_normal((B, T, H, dv))
+    a = rng.standard_normal((B, T, H))
+    b = rng.standard_normal((B, T, H))
+    C = 2 * Hk * dk + H * dv
+    w = rng.standard_normal((C, 4)) * 0.5
+    A = rng.uniform(0.5, 2, H)
+    dtb = rng.standard_normal(H)
+    nw = rng.uniform(0.5, 1.5, dv)
+    ref, mid = oracle_mod.mixer(qr, kr, vr, z, a, b, w, A, dt_bias=dtb, norm_w=nw, scale=0.5,
+                                return_intermediates=True)
+    cache = np.zeros((B, 3, C))
+    st = np.zeros((B, H, dv, dk))
+    for t in range(T):
+        out, st, cache = oracle_mod.mixer_decode_step(qr[:, t], kr[:, t], vr[:, t], z[:, t],
+                                                      a[:, t], b[:, t], w, cache, A, st,
+                                                      dt_bias=dtb, norm_w=nw, scale=0.5)
+        np.testing.assert_allclose(out, ref[:, t], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(st, mid["s_final"], rtol=1e-11, atol=1e-13)
+    raw = np.concatenate([qr.reshape(B, T, -1), kr.reshape(B, T, -1), vr.reshape(B, T, -1)], 2)
+    np.testing.assert_array_equal(cache, raw[:, T - 3:])

@@ -419,3 +419,66 @@ def test_mixer_grouped_heads():
     report("mixer grouped heads", out=e_out, y=e_y, q=e_q, k=e_k, v=e_v, g=e_g, beta=e_b)
     assert max(e_q, e_k, e_v) <= TOL_BF16 and e_g <= 1e-5 and e_b <= 1e-6
     assert e_y <= TOL_BF16 and e_out <= TOL_BF16
+
+
+# --- the fused single-token mixer step --------------------------------------------
+
+@pytest.mark.parametrize("dtype,H,Hk,dk,dv", [("bf16", 4, 2, 128, 128), ("f32", 3, 3, 64, 32),
+                                              ("bf16", 2, 1, 32, 256), ("f32", 4, 4, 16, 16)])
+def test_decode_mixer_steps_continue_the_sequence(dtype, H, Hk, dk, dv):
+    """T = 7 fused steps from an empty conv cache and a zero state on the GPU
+    against the oracle's mixer over the same 7 tokens (every step's output),
+    the final state, and the cache, which must hold the last three raw inputs
+    bit for bit."""
+    B, T = 2, 7
+    gen = torch.Generator().manual_seed(71)
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    rnd = lambda *shape, std=1.0: (torch.randn(shape, generator=gen) * std).to(td)
+    qr, kr = rnd(B, T, Hk, dk), rnd(B, T, Hk, dk)
+    vr, z = rnd(B, T, H, dv), rnd(B, T, H, dv)
+    a, b = rnd(B, T, H), rnd(B, T, H)
+    C = 2 * Hk * dk + H * dv
+    w = rnd(C, 4, std=0.5)
+    A = torch.rand(H, generator=gen) * 1.5 + 0.5
+    dtb = torch.randn(H, generator=gen)
+    nw = torch.rand(dv, generator=gen) + 0.5
+    scale = dk ** -0.5
+    ref, mid = oracle.mixer(qr, kr, vr, z, a, b, w, A, dt_bias=dtb, norm_w=nw, scale=scale,
+                            return_intermediates=True)
+    cache = torch.zeros((B, 3, C), dtype=td, device="cuda:0")
+    st = torch.zeros((B, H, dv, dk), dtype=torch.float32, device="cuda:0")
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    errs = []
+    for t in range(T):
+        out = gdn.gdn_decode_mixer_step(dev(qr[:, t]), dev(kr[:, t]), dev(vr[:, t]), dev(w), cache,
+                                        dev(a[:, t]), dev(b[:, t]), dev(A), dev(z[:, t]), st,
+                                        dt_bias=dev(dtb), norm_w=dev(nw), scale=scale)
+        torch.cuda.synchronize()
+        errs.append(o_err(out.cpu()[:, None], ref[:, t:t + 1]))
+    es = s_err(st, mid["s_final"])
+    report(f"decode mixer steps {dtype} H{H} Hk{Hk} dk{dk} dv{dv}", out=max(errs), state=es)
+    assert max(errs) <= tol and es <= tol
+    raw = torch.cat([qr.reshape(B, T, -1), kr.reshape(B, T, -1), vr.reshape(B, T, -1)], 2)
+    assert torch.equal(cache.cpu(), raw[:, T - 3:])
+
+
+def test_decode_mixer_full_size_sampled():
+    """B=256, H=32, d=128 bf16 (512 MiB state, a random conv cache): one fused
+    step; the oracle recomputes four sequences (all heads) from the same
+    inputs."""
+    c = inputs.make_decode_mixer()
+    cache, st = dev(c.conv_state), dev(c.state)
+    out = gdn.gdn_decode_mixer_step(dev(c.q_raw), dev(c.k_raw), dev(c.v_raw), dev(c.conv_w),
+                                    cache, dev(c.a), dev(c.b), dev(c.A), dev(c.z), st,
+                                    scale=c.scale, eps=c.eps)
+    torch.cuda.synchronize()
+    rows = [0, 1, 128, 255]
+    r = lambda x: x[rows]
+    o_ref, s_ref, c_ref = oracle.mixer_decode_step(r(c.q_raw), r(c.k_raw), r(c.v_raw), r(c.z),
+                                                   r(c.a), r(c.b), c.conv_w, r(c.conv_state),
+                                                   c.A, r(c.state), scale=c.scale, eps=c.eps)
+    eo = o_err(out.cpu()[rows][:, None], o_ref[:, None])
+    es = s_err(st.cpu()[rows], s_ref)
+    report("decode mixer B256 H32", out=eo, state=es)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+    assert torch.equal(cache.cpu()[rows], torch.from_numpy(c_ref).to(cache.dtype))
