@@ -416,12 +416,19 @@ chunk_prep_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                     if (ti == 1 || r >= 8) sA[(32 * ti + acc_row(r, lane) - 16) * P_LD_A2 + j] = at[r];
             }
             if (wave < 2) {
-                // and the two diagonal 16 x 16 blocks, row-major, into sY
+                // and the two diagonal 16 x 16 blocks, row-major, into sY: lanes
+                // with l32 < 16 hold rows of block 0 in accumulators 0-7, the
+                // others rows of block 1 in accumulators 8-15 (acc_row(r + 8) =
+                // acc_row(r) + 16); one select per element (the empty asm keeps
+                // the compiler from turning it into a per-lane vector index,
+                // which it would expand into a 16-way select chain)
+                const bool hi = l32 >= 16;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int it_ = acc_row(r, lane);
-                    if ((it_ >> 4) == (l32 >> 4))
-                        sY[(2 * wave + (it_ >> 4)) * P_DB + (it_ & 15) * 16 + (l32 & 15)] = at[r];
+                for (int r = 0; r < 8; ++r) {
+                    float lo_v = at[r], hi_v = at[r + 8];
+                    asm volatile("" : "+v"(lo_v), "+v"(hi_v));
+                    const float val = hi ? hi_v : lo_v;
+                    sY[(2 * wave + (hi ? 1 : 0)) * P_DB + acc_row(r, lane) * 16 + (l32 & 15)] = val;
                 }
             }
         }
