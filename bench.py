@@ -27,6 +27,8 @@ carries:
 * ``decode_mixer``: one fused single-token mixer step (conv against the
   3-token cache, norms, gates, state update, gated RMSNorm) at B=256, H=32,
   d=128, GB/s of algorithmic traffic against 8 TB/s;
+* ``channel_gated``: one decay rate per key channel, the token-serial
+  prefill at the prefill shape and one decode step at the decode shape;
 * ``mixer``: prologue -> prefill -> epilogue at B=8, T=8192, H=16, d=128;
 * ``varlen``: packed prefill, H=32, 8 sequences, lengths log-uniform in
   [512, 65536], non-zero initial states;
@@ -227,6 +229,40 @@ def bench_decode_mixer(gdn, inputs, steps, warmup):
                 **{"GB/s": round(gbs, 1)}, frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
 
 
+def bench_channel_gated(gdn, inputs, steps, warmup):
+    """Per-channel decay: the token-serial prefill at the prefill workload's
+    shape (B=4, H=16, T=4096, d=128, bf16) and one decode step at the decode
+    shape (B=256, H=32, d=128), with one log-decay per key channel."""
+    import torch
+    c = inputs.make_channel_gated(seed=7, B=4, T=4096, H=16, d=128, with_state=False)
+    d = lambda t: t.cuda().contiguous()
+    q, k, v, g, beta = (d(x) for x in (c.q, c.k, c.v, c.g, c.beta))
+    fin = torch.empty((4, 16, 128, 128), dtype=torch.float32, device="cuda")
+    o = torch.empty_like(v)
+
+    def pre(i):
+        gdn.gdn_prefill_channel_gated(q, k, v, g, beta, None, fin, o, scale=c.scale)
+    ms_pre = event_time(pre, max(1, steps // 4), 1)
+    dc = inputs.make_decode()
+    st = dc.s0.cuda()
+    qd, kd, vd = (x[:, 0].cuda().contiguous() for x in (dc.q, dc.k, dc.v))
+    gd = dc.g[:, 0, :, None].expand(-1, -1, 128).cuda().contiguous()
+    bd = dc.beta[:, 0].cuda().contiguous()
+    od = torch.empty_like(vd)
+
+    def dec(i):
+        gdn.gdn_decode_step_channel_gated(qd, kd, vd, gd, bd, st, od, scale=dc.scale)
+    ms_dec = event_time(dec, steps, warmup)
+    nbytes = decode_bytes(dc.B, dc.H) + dc.B * dc.H * 128 * 4 - dc.B * dc.H * 4
+    gbs = nbytes / (ms_dec * 1e-3) / 1e9
+    return dict(workload="per-channel decay: token-serial prefill B=4 H=16 T=4096 d=128 bf16; "
+                         "decode step B=256 H=32 d=128 (fp32 state in place)",
+                prefill_tokens_per_s=round(4 * 4096 / (ms_pre * 1e-3), 1),
+                prefill_ms=round(ms_pre, 4), decode_us=round(ms_dec * 1e3, 2),
+                decode_bytes=nbytes, **{"decode_GB/s": round(gbs, 1)},
+                decode_frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
+
+
 def bench_mixer(gdn, inputs, steps, warmup):
     import torch
     c = inputs.make_mixer()
@@ -325,8 +361,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="prefill,decode,decode_mixer,mixer,varlen,cpu",
-                    help="comma list of: prefill, decode, decode_mixer, mixer, varlen, cpu, copy")
+    ap.add_argument("--only", default="prefill,decode,decode_mixer,channel,mixer,varlen,cpu",
+                    help="comma list of: prefill, decode, decode_mixer, channel, mixer, varlen, "
+                         "cpu, copy")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -380,6 +417,8 @@ def main():
         result["decode"] = bench_decode(gdn, inputs, args.steps, args.warmup)
     if "decode_mixer" in which:
         result["decode_mixer"] = bench_decode_mixer(gdn, inputs, args.steps, args.warmup)
+    if "channel" in which:
+        result["channel_gated"] = bench_channel_gated(gdn, inputs, args.steps, args.warmup)
     if "mixer" in which:
         result["mixer"] = bench_mixer(gdn, inputs, args.steps, args.warmup)
     if "varlen" in which:

@@ -41,6 +41,8 @@ _SIGS = {
     "gdn_decode_step": [_vp] * 7 + [_i] * 5 + [_f, _i, _vp],
     "gdn_mixer_prologue": [_vp] * 14 + [_i] * 8 + [_vp],
     "gdn_mixer_epilogue": [_vp] * 4 + [_i] * 3 + [_f, _i, _vp],
+    "gdn_prefill_channel_gated": [_vp] * 9 + [_i] * 7 + [_f, _i, _vp],
+    "gdn_decode_step_channel_gated": [_vp] * 7 + [_i] * 5 + [_f, _i, _vp],
     "gdn_decode_mixer_step": [_vp] * 11 + [_f, _vp, _vp] + [_i] * 5 + [_f, _i, _vp],
 }
 EXPORTED = tuple(_SIGS)
@@ -121,7 +123,9 @@ def _prefill(entry, q, k, v, g, beta, initial_state=None, final_state=None, o=No
         scale = dk ** -0.5
     args = [
         _dev(q, "q", dt), _dev(k, "k", dt, q.shape), _dev(v, "v", dt, (B, T, H, dv)),
-        _dev(g, "g", torch.float32, (B, T, H)), _dev(beta, "beta", torch.float32, (B, T, H)),
+        _dev(g, "g", torch.float32,
+             (B, T, H, dk) if entry == "gdn_prefill_channel_gated" else (B, T, H)),
+        _dev(beta, "beta", torch.float32, (B, T, H)),
         _dev(initial_state, "initial_state", torch.float32, (N, H, dv, dk)),
         _dev(final_state, "final_state", torch.float32, (N, H, dv, dk)),
         _dev(o, "o", dt, (B, T, H, dv)),
@@ -207,9 +211,26 @@ def gdn_prefill_recurrent(q, k, v, g, beta, initial_state=None, final_state=None
                     cu_seqlens, scale)
 
 
+def gdn_prefill_channel_gated(q, k, v, g, beta, initial_state=None, final_state=None, o=None,
+                              cu_seqlens=None, scale=None):
+    """Forward pass with one decay rate per key channel: g [B,T,H,d_k] fp32
+    (see include/gdn.h). Returns (o, final_state)."""
+    return _prefill("gdn_prefill_channel_gated", q, k, v, g, beta, initial_state, final_state, o,
+                    cu_seqlens, scale)
+
+
+def gdn_decode_step_channel_gated(q, k, v, g, beta, state, o=None, scale=None):
+    """One in-place step with one decay rate per key channel: g [B,H,d_k] fp32."""
+    return _decode("gdn_decode_step_channel_gated", q, k, v, g, beta, state, o, scale)
+
+
 def gdn_decode_step(q, k, v, g, beta, state, o=None, scale=None):
     """One in-place recurrent step. q,k: [B,H_k,d_k]; v: [B,H,d_v]; g,beta: [B,H];
     state: [B,H,d_v,d_k] fp32 (updated). Returns o [B,H,d_v]."""
+    return _decode("gdn_decode_step", q, k, v, g, beta, state, o, scale)
+
+
+def _decode(entry, q, k, v, g, beta, state, o, scale):
     B, Hk, dk = q.shape
     H, dv = v.shape[1], v.shape[2]
     dt = q.dtype
@@ -217,9 +238,10 @@ def gdn_decode_step(q, k, v, g, beta, state, o=None, scale=None):
         o = torch.empty((B, H, dv), dtype=dt, device=q.device)
     if scale is None:
         scale = dk ** -0.5
-    _check(load().gdn_decode_step(
+    _check(getattr(load(), entry)(
         _dev(q, "q", dt), _dev(k, "k", dt, q.shape), _dev(v, "v", dt, (B, H, dv)),
-        _dev(g, "g", torch.float32, (B, H)), _dev(beta, "beta", torch.float32, (B, H)),
+        _dev(g, "g", torch.float32, (B, H, dk) if entry.endswith("channel_gated") else (B, H)),
+        _dev(beta, "beta", torch.float32, (B, H)),
         _dev(state, "state", torch.float32, (B, H, dv, dk)), _dev(o, "o", dt, (B, H, dv)),
         B, H, Hk, dk, dv, float(scale), _dtype_code(q), _stream(q.device)))
     return o

@@ -17,6 +17,10 @@
 // reads query/key head h / (H / H_k) (the repeat_interleave head expansion of
 // the "Gated DeltaNet body" layer code, "5. Linear Attention").
 //
+// Per-channel decay (PERCH; "6.6 Gated DeltaNet" section 6.6.7): g is
+// [B][H][d_k] and column j of the state decays by exp(g[j]) before the
+// retrieval; each lane decays its own 8 columns.
+//
 // Work mapping: a row of d_k floats is owned by G = d_k/8 consecutive lanes;
 // lane j of the group holds columns [4j, 4j+4) and [d_k/2 + 4j, d_k/2 + 4j + 4),
 // so each 16-byte load instruction of a group covers one contiguous half row
@@ -33,7 +37,7 @@ namespace gdn {
 
 constexpr int DEC_NT = 512;
 
-template <int DK, typename TIO>
+template <int DK, typename TIO, bool PERCH>
 __global__ void __launch_bounds__(DEC_NT)
 decode_step_kernel(const TIO *__restrict__ q, const TIO *__restrict__ k,
                    const TIO *__restrict__ v, const float *__restrict__ g,
@@ -49,8 +53,8 @@ decode_step_kernel(const TIO *__restrict__ q, const TIO *__restrict__ k,
     const int c0 = 4 * lr, c1 = DK / 2 + 4 * lr;
 
     float *rp = state + ((size_t)bh * d_v + row) * DK;
-    const f32x4 s0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(rp + c0));
-    const f32x4 s1 = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(rp + c1));
+    f32x4 s0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(rp + c0));
+    f32x4 s1 = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(rp + c1));
     __builtin_amdgcn_sched_barrier(0);        // the state request goes out first
 
     // grp = H / H_k value heads per query/key head; (b H + h) / grp = b H_k + h / grp
@@ -61,8 +65,18 @@ decode_step_kernel(const TIO *__restrict__ q, const TIO *__restrict__ k,
     const f32x4 k0 = load4(kp + c0), k1 = load4(kp + c1);
     const f32x4 q0 = load4(qp + c0), q1 = load4(qp + c1);
     const float vv = to_f32(v[(size_t)bh * d_v + row]);
-    const float alpha = __expf(g[bh]);
     const float b = beta[bh];
+    float alpha = 1.0f;                        // scalar gate; folded into s with PERCH
+    if constexpr (PERCH) {
+        const f32x4 g0 = load4(g + (size_t)bh * DK + c0), g1 = load4(g + (size_t)bh * DK + c1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            s0[e] *= __expf(g0[e]);
+            s1[e] *= __expf(g1[e]);
+        }
+    } else {
+        alpha = __expf(g[bh]);
+    }
 
     float kq = k0[0] * q0[0] + k0[1] * q0[1] + k0[2] * q0[2] + k0[3] * q0[3]
              + k1[0] * q1[0] + k1[1] * q1[1] + k1[2] * q1[2] + k1[3] * q1[3];
@@ -88,12 +102,14 @@ decode_step_kernel(const TIO *__restrict__ q, const TIO *__restrict__ k,
 template <int DK, typename TIO>
 static hipError_t launch_decode_dk(const void *q, const void *k, const void *v, const float *g,
                                    const float *beta, float *state, void *o, int B, int H,
-                                   int Hk, int d_v, float scale, hipStream_t stream)
+                                   int Hk, int d_v, float scale, bool per_channel,
+                                   hipStream_t stream)
 {
     constexpr int RPW = DEC_NT / (DK / 8);
     const int wg_per_head = (d_v + RPW - 1) / RPW;
     dim3 grid((unsigned)((long)B * H * wg_per_head)), block(DEC_NT);
-    hipLaunchKernelGGL((decode_step_kernel<DK, TIO>), grid, block, 0, stream,
+    auto kern = per_channel ? decode_step_kernel<DK, TIO, true> : decode_step_kernel<DK, TIO, false>;
+    hipLaunchKernelGGL(kern, grid, block, 0, stream,
                        (const TIO *)q, (const TIO *)k, (const TIO *)v, g, beta, state,
                        (TIO *)o, H / Hk, d_v, wg_per_head, scale);
     return hipGetLastError();
@@ -102,22 +118,22 @@ static hipError_t launch_decode_dk(const void *q, const void *k, const void *v, 
 template <typename TIO>
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *g,
                          const float *beta, float *state, void *o, int B, int H, int Hk,
-                         int d_k, int d_v, float scale, hipStream_t stream)
+                         int d_k, int d_v, float scale, bool per_channel, hipStream_t stream)
 {
     switch (d_k) {
-    case 16: return launch_decode_dk<16, TIO>(q, k, v, g, beta, state, o, B, H, Hk, d_v, scale, stream);
-    case 32: return launch_decode_dk<32, TIO>(q, k, v, g, beta, state, o, B, H, Hk, d_v, scale, stream);
-    case 64: return launch_decode_dk<64, TIO>(q, k, v, g, beta, state, o, B, H, Hk, d_v, scale, stream);
-    case 128: return launch_decode_dk<128, TIO>(q, k, v, g, beta, state, o, B, H, Hk, d_v, scale, stream);
+    case 16: return launch_decode_dk<16, TIO>(q, k, v, g, beta, state, o, B, H, Hk, d_v, scale, per_channel, stream);
+    case 32: return launch_decode_dk<32, TIO>(q, k, v, g, beta, state, o, B, H, Hk, d_v, scale, per_channel, stream);
+    case 64: return launch_decode_dk<64, TIO>(q, k, v, g, beta, state, o, B, H, Hk, d_v, scale, per_channel, stream);
+    case 128: return launch_decode_dk<128, TIO>(q, k, v, g, beta, state, o, B, H, Hk, d_v, scale, per_channel, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
 template hipError_t launch_decode<float>(const void *, const void *, const void *, const float *,
                                          const float *, float *, void *, int, int, int, int,
-                                         int, float, hipStream_t);
+                                         int, float, bool, hipStream_t);
 template hipError_t launch_decode<bf16>(const void *, const void *, const void *, const float *,
                                         const float *, float *, void *, int, int, int, int,
-                                        int, float, hipStream_t);
+                                        int, float, bool, hipStream_t);
 
 }  // namespace gdn

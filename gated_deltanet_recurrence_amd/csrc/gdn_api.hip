@@ -10,11 +10,11 @@
 namespace gdn {
 template <typename TIO>
 hipError_t launch_decode(const void *, const void *, const void *, const float *, const float *,
-                         float *, void *, int, int, int, int, int, float, hipStream_t);
+                         float *, void *, int, int, int, int, int, float, bool, hipStream_t);
 template <typename TIO>
 hipError_t launch_prefill_recurrent(const void *, const void *, const void *, const float *,
                                     const float *, const float *, float *, void *,
-                                    const int32_t *, int, int, int, int, int, int, float,
+                                    const int32_t *, int, int, int, int, int, int, float, bool,
                                     hipStream_t);
 hipError_t launch_prefill_chunk(const void *, const void *, const void *, const float *,
                                 const float *, const float *, float *, void *, const int32_t *,
@@ -121,9 +121,11 @@ int gdn_prefill_recurrent(const void *q, const void *k, const void *v, const flo
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = dtype == GDN_DTYPE_BF16
         ? gdn::launch_prefill_recurrent<gdn::bf16>(q, k, v, g, beta, initial_state, final_state, o,
-                                                   cu_seqlens, T, H, H_k, d_k, d_v, N, scale, s)
+                                                   cu_seqlens, T, H, H_k, d_k, d_v, N, scale,
+                                                   false, s)
         : gdn::launch_prefill_recurrent<float>(q, k, v, g, beta, initial_state, final_state, o,
-                                               cu_seqlens, T, H, H_k, d_k, d_v, N, scale, s);
+                                               cu_seqlens, T, H, H_k, d_k, d_v, N, scale, false,
+                                               s);
     return status_of(e);
 }
 
@@ -214,8 +216,10 @@ int gdn_decode_step(const void *q, const void *k, const void *v, const float *g,
     if (!head_dim_pow2(d_k) || d_v > 4096) return GDN_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = dtype == GDN_DTYPE_BF16
-        ? gdn::launch_decode<gdn::bf16>(q, k, v, g, beta, state, o, B, H, H_k, d_k, d_v, scale, s)
-        : gdn::launch_decode<float>(q, k, v, g, beta, state, o, B, H, H_k, d_k, d_v, scale, s);
+        ? gdn::launch_decode<gdn::bf16>(q, k, v, g, beta, state, o, B, H, H_k, d_k, d_v, scale,
+                                        false, s)
+        : gdn::launch_decode<float>(q, k, v, g, beta, state, o, B, H, H_k, d_k, d_v, scale, false,
+                                    s);
     return status_of(e);
 }
 
@@ -280,6 +284,42 @@ int gdn_decode_mixer_step(const void *q_raw, const void *k_raw, const void *v_ra
         : gdn::launch_decode_mixer<float>(q_raw, k_raw, v_raw, conv_w, conv_state, a, b, A,
                                           dt_bias, z, norm_w, eps, state, out, B, H, H_k, d_k,
                                           d_v, scale, s);
+    return status_of(e);
+}
+
+int gdn_prefill_channel_gated(const void *q, const void *k, const void *v, const float *g,
+                              const float *beta, const float *initial_state, float *final_state,
+                              void *o, const int32_t *cu_seqlens, int B, int T, int H, int H_k,
+                              int d_k, int d_v, int N, float scale, int dtype, void *stream)
+{
+    int st = check_prefill(q, k, v, g, beta, o, cu_seqlens, B, T, H, H_k, d_k, d_v, N, dtype);
+    if (st != GDN_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = dtype == GDN_DTYPE_BF16
+        ? gdn::launch_prefill_recurrent<gdn::bf16>(q, k, v, g, beta, initial_state, final_state, o,
+                                                   cu_seqlens, T, H, H_k, d_k, d_v, N, scale,
+                                                   true, s)
+        : gdn::launch_prefill_recurrent<float>(q, k, v, g, beta, initial_state, final_state, o,
+                                               cu_seqlens, T, H, H_k, d_k, d_v, N, scale, true,
+                                               s);
+    return status_of(e);
+}
+
+int gdn_decode_step_channel_gated(const void *q, const void *k, const void *v, const float *g,
+                                  const float *beta, float *state, void *o, int B, int H,
+                                  int H_k, int d_k, int d_v, float scale, int dtype, void *stream)
+{
+    if (!q || !k || !v || !g || !beta || !state || !o) return GDN_ERR_NULL;
+    if (!valid_dtype(dtype)) return GDN_ERR_DTYPE;
+    if (B < 1 || H < 1 || d_k < 1 || d_v < 1 || !heads_ok(H, H_k)) return GDN_ERR_SHAPE;
+    if ((int64_t)B * H > (int64_t)INT32_MAX) return GDN_ERR_SHAPE;
+    if (!head_dim_pow2(d_k) || d_v > 4096) return GDN_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = dtype == GDN_DTYPE_BF16
+        ? gdn::launch_decode<gdn::bf16>(q, k, v, g, beta, state, o, B, H, H_k, d_k, d_v, scale,
+                                        true, s)
+        : gdn::launch_decode<float>(q, k, v, g, beta, state, o, B, H, H_k, d_k, d_v, scale, true,
+                                    s);
     return status_of(e);
 }
 

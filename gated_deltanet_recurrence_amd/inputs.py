@@ -37,7 +37,7 @@ import torch
 __all__ = [
     "GDNCase", "MixerCase", "DecodeMixerCase", "unit_gaussian", "log_uniform_lengths",
     "make_tiny", "make_prefill", "make_decode", "make_mixer", "make_varlen",
-    "make_decode_mixer",
+    "make_decode_mixer", "make_channel_gated",
     "make_case", "WORKLOADS",
 ]
 
@@ -268,6 +268,35 @@ def make_varlen(seed: int = 5, n_seq: int = 8, H: int = 32, d: int = 128,
                    meta={"lengths": lengths, "A": A})
 
 
+def make_channel_gated(seed: int = 7, B: int = 2, T: int = 300, H: int = 4, d: int = 128,
+                       dtype: str = "bf16", Hk: Optional[int] = None, with_state: bool = True,
+                       lengths: Optional[list] = None) -> GDNCase:
+    """Per-channel decay (one rate per key channel): q,k unit Gaussian, v ~
+    N(0,1), log(alpha)[.., c] = -A[h]*softplus(a[.., c]) with a ~ N(0,1) per
+    channel and A ~ U(0.5, 2) per head, beta = sigmoid(N(0,1)), initial states
+    N(0, 0.02) when ``with_state``. g is [B, T, H, d]. With ``lengths`` the
+    sequences are packed (B = 1, cu_seqlens)."""
+    gen = _gen(seed)
+    td = _TORCH_DTYPE[dtype]
+    Hk = H if Hk is None else Hk
+    cu = None
+    if lengths is not None:
+        B, T = 1, int(sum(lengths))
+        cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
+        cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+    N = B if cu is None else len(lengths)
+    q = unit_gaussian(gen, (B, T, Hk, d)).to(td)
+    k = unit_gaussian(gen, (B, T, Hk, d)).to(td)
+    v = _normal(gen, (B, T, H, d)).to(td)
+    a = _normal(gen, (B, T, H, d))
+    A = _uniform(gen, (H,), 0.5, 2.0)
+    g = -(A.view(1, 1, -1, 1) * torch.nn.functional.softplus(a)).contiguous()
+    beta = _sigmoid_gaussian(gen, (B, T, H))
+    s0 = _normal(gen, (N, H, d, d), std=0.02) if with_state else None
+    return GDNCase("channel_gated", q, k, v, g, beta, s0, cu, 1.0 / math.sqrt(d), dtype,
+                   meta={"A": A, "lengths": lengths})
+
+
 @dataclass
 class DecodeMixerCase:
     """Inputs of one fused single-token mixer step, on the host.
@@ -324,6 +353,7 @@ WORKLOADS = {
     "mixer": make_mixer,
     "varlen": make_varlen,
     "decode_mixer": make_decode_mixer,
+    "channel_gated": make_channel_gated,
 }
 
 

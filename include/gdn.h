@@ -222,6 +222,34 @@ int gdn_decode_step(const void *q, const void *k, const void *v,
                     float scale, int dtype, void *stream);
 
 /*
+ * gdn_prefill_channel_gated, gdn_decode_step_channel_gated - the same
+ * forward pass and decode step with one decay rate per key channel instead
+ * of one per head ("6.6 Gated DeltaNet" section 6.6.7: Kimi Linear's gate,
+ * alpha_t in R^d). Column j of each d_v x d_k state decays by exp(g[j])
+ * before the retrieval:
+ *
+ *     S_t = S_{t-1} diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *
+ * Arguments, layouts and errors as gdn_prefill_recurrent (token-serial fp32
+ * arithmetic; no workspace) and gdn_decode_step, except g:
+ *   prefill: g [B][T][H][d_k] fp32;  decode: g [B][H][d_k] fp32.
+ * With every channel of g equal, the results equal those of the per-head
+ * entry points.
+ */
+int gdn_prefill_channel_gated(const void *q, const void *k, const void *v,
+                              const float *g, const float *beta,
+                              const float *initial_state, float *final_state,
+                              void *o, const int32_t *cu_seqlens,
+                              int B, int T, int H, int H_k, int d_k, int d_v, int N,
+                              float scale, int dtype, void *stream);
+
+int gdn_decode_step_channel_gated(const void *q, const void *k, const void *v,
+                                  const float *g, const float *beta,
+                                  float *state, void *o,
+                                  int B, int H, int H_k, int d_k, int d_v,
+                                  float scale, int dtype, void *stream);
+
+/*
  * gdn_mixer_prologue - everything between the input projections and the
  * recurrence ("5. Linear Attention" chapter, sections "Causal Conv1d" and
  * "Gated DeltaNet body"; "6.6 Gated DeltaNet" sections 6.6.3-6.6.4):

@@ -10,8 +10,9 @@ slices out the (sequence, head) pairs a caller asks for, and calls the C code.
 Pinned by ``tests/test_oracle_pins.py`` against the worked example of the
 "Linear Attention" chapter (chunk section), the invariant S_t k_t = v_t for
 unit keys and beta = 1, the gate special cases, a closed form for mutually
-orthogonal keys (also with grouped query/key heads), the unrolled product
-form, and brute-force checks of the convolution, norms and gates.
+orthogonal keys (also with grouped query/key heads and with per-channel
+decay), the unrolled product form (also per channel), and brute-force checks
+of the convolution, norms and gates.
 """
 from __future__ import annotations
 
@@ -58,6 +59,8 @@ def _load():
                                              ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                              ctypes.c_int, ctypes.c_double, ctypes.c_int]
         lib.oracle_gdn_recurrent.restype = ctypes.c_int
+        lib.oracle_gdn_recurrent_channel.argtypes = lib.oracle_gdn_recurrent.argtypes
+        lib.oracle_gdn_recurrent_channel.restype = ctypes.c_int
         lib.oracle_causal_conv_silu.argtypes = [_dp, _dp, _dp, _i64p, ctypes.c_int,
                                                 ctypes.c_int, ctypes.c_int, ctypes.c_int]
         lib.oracle_causal_conv_silu.restype = ctypes.c_int
@@ -152,6 +155,43 @@ def gdn_recurrent(q, k, v, g, beta, s0=None, cu_seqlens=None, scale: float = 1.0
                                       N, H, dk, dv, float(scale), int(nthreads))
     if rc != 0:
         raise ValueError("oracle_gdn_recurrent rejected its arguments")
+    return o, s1
+
+
+def gdn_recurrent_channel(q, k, v, g, beta, s0=None, cu_seqlens=None, scale: float = 1.0,
+                          nthreads: int = 0):
+    """The gated delta rule with one decay rate per key channel ("6.6 Gated
+    DeltaNet" section 6.6.7, the Kimi Linear gate): g = log(alpha) is
+    [B, T, H, d_k] and column j of the d_v x d_k state decays by alpha[j]
+    before the retrieval. Other arguments and the result as for
+    ``gdn_recurrent`` (grouped query/key heads included)."""
+    v, g, beta = (_f64(x) for x in (v, g, beta))
+    H = v.shape[2]
+    q, k = expand_heads(q, H), expand_heads(k, H)
+    B, T, _, dk = q.shape
+    dv = v.shape[3]
+    if k.shape != q.shape or v.shape[:3] != (B, T, H) or g.shape != (B, T, H, dk) \
+            or beta.shape != (B, T, H):
+        raise ValueError("shape mismatch")
+    if cu_seqlens is None:
+        N = B
+        cu = np.arange(B + 1, dtype=np.int64) * T
+    else:
+        if B != 1:
+            raise ValueError("cu_seqlens requires B == 1")
+        N = len(cu_seqlens) - 1
+        cu = _cu64(cu_seqlens, T, N)
+    s0a = None if s0 is None else _f64(s0)
+    if s0a is not None and s0a.shape != (N, H, dv, dk):
+        raise ValueError("bad initial state shape")
+    o = np.zeros((B, T, H, dv), dtype=np.float64)
+    s1 = np.zeros((N, H, dv, dk), dtype=np.float64)
+    rc = _load().oracle_gdn_recurrent_channel(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                              _ptr(s0a), _ptr(s1), _ptr(o),
+                                              cu.ctypes.data_as(_i64p), N, H, dk, dv,
+                                              float(scale), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_gdn_recurrent_channel rejected its arguments")
     return o, s1
 
 

@@ -245,3 +245,89 @@ int oracle_gated_rmsnorm(const double *y, const double *z, const double *w, doub
     }
     return 0;
 }
+
+/*
+ * Per-channel decay ("6.6 Gated DeltaNet", section 6.6.7: Kimi Linear makes
+ * the decay gate a vector alpha_t in R^d, one rate per feature channel of the
+ * key space, instead of one scalar per head). With the state stored d_v x d_k
+ * the decay scales column j of S by alpha_t[j]; the retrieval reads the
+ * decayed state, as for the scalar gate:
+ *
+ *   S <- S diag(alpha_t);  r <- S k_t;  d <- beta_t (v_t - r);
+ *   S <- S + d k_t^T;      o_t <- scale * S q_t
+ *
+ * i.e. S_t = S_{t-1} diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T.
+ * g holds log(alpha) per channel: [T_total][H][dk]. Other arguments as in
+ * oracle_gdn_recurrent.
+ */
+static void chain_channel(const double *q, const double *k, const double *v,
+                          const double *g, const double *beta, double *S, double *o,
+                          int64_t bos, int64_t eos, int h, int H, int dk, int dv,
+                          double scale, double *r)
+{
+    for (int64_t t = bos; t < eos; ++t) {
+        const double *qt = q + (t * H + h) * (int64_t)dk;
+        const double *kt = k + (t * H + h) * (int64_t)dk;
+        const double *vt = v + (t * H + h) * (int64_t)dv;
+        const double *gt = g + (t * H + h) * (int64_t)dk;
+        const double b = beta[t * H + h];
+
+        for (int i = 0; i < dv; ++i)
+            for (int j = 0; j < dk; ++j)
+                S[(int64_t)i * dk + j] *= exp(gt[j]);
+
+        for (int i = 0; i < dv; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < dk; ++j)
+                acc += S[(int64_t)i * dk + j] * kt[j];
+            r[i] = acc;
+        }
+        for (int i = 0; i < dv; ++i) {
+            const double d = b * (vt[i] - r[i]);
+            for (int j = 0; j < dk; ++j)
+                S[(int64_t)i * dk + j] += d * kt[j];
+        }
+        double *ot = o + (t * H + h) * (int64_t)dv;
+        for (int i = 0; i < dv; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < dk; ++j)
+                acc += S[(int64_t)i * dk + j] * qt[j];
+            ot[i] = scale * acc;
+        }
+    }
+}
+
+int oracle_gdn_recurrent_channel(const double *q, const double *k, const double *v,
+                                 const double *g, const double *beta,
+                                 const double *S0, double *S1, double *o,
+                                 const int64_t *cu, int N, int H, int dk, int dv,
+                                 double scale, int nthreads)
+{
+    if (!q || !k || !v || !g || !beta || !o || !cu || N < 0 || H <= 0 || dk <= 0 || dv <= 0)
+        return -1;
+    for (int n = 0; n < N; ++n)
+        if (cu[n + 1] < cu[n] || cu[n] < 0)
+            return -1;
+    const int64_t pairs = (int64_t)N * H;
+    const int64_t ssz = (int64_t)dv * dk;
+#ifdef _OPENMP
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t p = 0; p < pairs; ++p) {
+        const int n = (int)(p / H), h = (int)(p % H);
+        double *S = (double *)malloc(sizeof(double) * (size_t)ssz);
+        double *r = (double *)malloc(sizeof(double) * (size_t)dv);
+        if (S0)
+            memcpy(S, S0 + p * ssz, sizeof(double) * (size_t)ssz);
+        else
+            memset(S, 0, sizeof(double) * (size_t)ssz);
+        chain_channel(q, k, v, g, beta, S, o, cu[n], cu[n + 1], h, H, dk, dv, scale, r);
+        if (S1)
+            memcpy(S1 + p * ssz, S, sizeof(double) * (size_t)ssz);
+        free(S);
+        free(r);
+    }
+    return 0;
+}

@@ -173,3 +173,17 @@ def test_prepare_apply_validation(lib):
     b = list(a)
     b[6] = None                              # o
     assert app(*b, 1, 100, 1, 1, 128, 128, 1, 1.0, 1, ws, need, None) == GDN_ERR_NULL
+
+
+def test_channel_gated_validation(lib):
+    f = lib.gdn_prefill_channel_gated
+    a = [P] * 5 + [None, None, P, None]
+    bad = list(a)
+    bad[3] = None                            # g
+    assert f(*bad, 1, 8, 2, 2, 128, 128, 1, 1.0, 1, None) == GDN_ERR_NULL
+    assert f(*a, 1, 8, 4, 3, 128, 128, 1, 1.0, 1, None) == GDN_ERR_SHAPE
+    assert f(*a, 1, 8, 2, 2, 48, 128, 1, 1.0, 1, None) == GDN_ERR_UNSUPPORTED
+    d = lib.gdn_decode_step_channel_gated
+    assert d(P, P, P, None, P, P, P, 1, 2, 2, 128, 128, 1.0, 1, None) == GDN_ERR_NULL
+    assert d(P, P, P, P, P, P, P, 1, 2, 2, 128, 128, 1.0, 3, None) == GDN_ERR_DTYPE
+    assert d(P, P, P, P, P, P, P, 1, 6, 4, 128, 128, 1.0, 1, None) == GDN_ERR_SHAPE

@@ -402,3 +402,70 @@ def test_mixer_decode_steps_continue_the_sequence(oracle_mod):
     np.testing.assert_allclose(st, mid["s_final"], rtol=1e-11, atol=1e-13)
     raw = np.concatenate([qr.reshape(B, T, -1), kr.reshape(B, T, -1), vr.reshape(B, T, -1)], 2)
     np.testing.assert_array_equal(cache, raw[:, T - 3:])
+
+
+# --- Per-channel decay ("6.6 Gated DeltaNet", section 6.6.7) -------------------
+
+def test_channel_decay_equal_channels_is_the_scalar_gate(oracle_mod):
+    """With the same rate on every key channel the per-channel form is the
+    pinned scalar-gated recurrence."""
+    rng = np.random.default_rng(14)
+    T, H, dk, dv = 9, 2, 6, 4
+    q, k, v, g, beta = _rand_case(rng, T, H, dk, dv)
+    s0 = rng.standard_normal((1, H, dv, dk))
+    gc = np.repeat(g[..., None], dk, axis=-1)
+    o1, s1 = oracle_mod.gdn_recurrent(q, k, v, g, beta, s0, scale=0.7)
+    o2, s2 = oracle_mod.gdn_recurrent_channel(q, k, v, gc, beta, s0, scale=0.7)
+    np.testing.assert_allclose(o2, o1, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(s2, s1, rtol=1e-13, atol=1e-14)
+
+
+def test_channel_decay_coordinate_keys_closed_form(oracle_mod):
+    """Keys on distinct coordinate axes (k_t = e_{c_t}) and a zero initial
+    state: nothing is retrieved, the write of token i lands in state column
+    c_i and then decays by that channel's rates only, so
+    o_t = scale * sum_{i<=t} (prod_{s=i+1..t} alpha_s[c_i]) beta_i v_i q_t[c_i]."""
+    rng = np.random.default_rng(15)
+    T, dk, dv, H = 6, 8, 3, 2
+    cols = np.stack([rng.permutation(dk)[:T] for _ in range(H)], axis=1)   # [T, H]
+    k = np.zeros((1, T, H, dk))
+    for t in range(T):
+        for h in range(H):
+            k[0, t, h, cols[t, h]] = 1.0
+    q = rng.standard_normal((1, T, H, dk))
+    v = rng.standard_normal((1, T, H, dv))
+    g = np.log(rng.uniform(0.3, 1.0, (1, T, H, dk)))
+    beta = rng.uniform(0.1, 1.0, (1, T, H))
+    o, s = oracle_mod.gdn_recurrent_channel(q, k, v, g, beta, scale=0.6)
+    for h in range(H):
+        for t in range(T):
+            ref = np.zeros(dv)
+            for i in range(t + 1):
+                c = cols[i, h]
+                dec = math.exp(g[0, i + 1:t + 1, h, c].sum())
+                ref += dec * beta[0, i, h] * v[0, i, h] * q[0, t, h, c]
+            np.testing.assert_allclose(o[0, t, h], 0.6 * ref, rtol=1e-12, atol=1e-13)
+        for i in range(T):
+            c = cols[i, h]
+            np.testing.assert_allclose(s[0, h][:, c], math.exp(g[0, i + 1:, h, c].sum()) *
+                                       beta[0, i, h] * v[0, i, h], rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_channel_decay_product_form(oracle_mod, seed):
+    """S_t = S_{t-1} A_t + B_t with A_t = diag(alpha_t) (I - beta_t k_t k_t^T)
+    and B_t = beta_t v_t k_t^T, multiplied out with dense matrices."""
+    rng = np.random.default_rng(20 + seed)
+    T, dk, dv, H = 6, 5, 3, 2
+    q, k, v, _, beta = _rand_case(rng, T, H, dk, dv, unit_keys=False)
+    g = np.log(rng.uniform(0.4, 1.0, (1, T, H, dk)))
+    s0 = rng.standard_normal((1, H, dv, dk))
+    o, s = oracle_mod.gdn_recurrent_channel(q, k, v, g, beta, s0, scale=1.3)
+    for h in range(H):
+        st = s0[0, h]
+        for t in range(T):
+            A = np.diag(np.exp(g[0, t, h])) @ (np.eye(dk) - beta[0, t, h] *
+                                                 np.outer(k[0, t, h], k[0, t, h]))
+            st = st @ A + beta[0, t, h] * np.outer(v[0, t, h], k[0, t, h])
+            np.testing.assert_allclose(o[0, t, h], 1.3 * (st @ q[0, t, h]), rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(s[0, h], st, rtol=1e-11, atol=1e-12)

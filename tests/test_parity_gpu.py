@@ -482,3 +482,69 @@ def test_decode_mixer_full_size_sampled():
     report("decode mixer B256 H32", out=eo, state=es)
     assert eo <= TOL_BF16 and es <= TOL_BF16
     assert torch.equal(cache.cpu()[rows], torch.from_numpy(c_ref).to(cache.dtype))
+
+
+# --- per-channel decay (one rate per key channel) -----------------------------------
+
+def _oracle_channel(c, init=True):
+    return oracle.gdn_recurrent_channel(c.q, c.k, c.v, c.g, c.beta, c.s0 if init else None,
+                                        c.cu_seqlens, c.scale)
+
+
+@pytest.mark.parametrize("dtype,d,Hk", [("bf16", 128, 4), ("bf16", 128, 2), ("f32", 64, 4),
+                                        ("f32", 16, 1)])
+def test_channel_gated_prefill(dtype, d, Hk):
+    c = inputs.make_channel_gated(seed=81, B=2, T=150, H=4, Hk=Hk, d=d, dtype=dtype)
+    o, fin = run_prefill(c, entry=gdn.gdn_prefill_channel_gated)
+    o_ref, s_ref = _oracle_channel(c)
+    eo, es = o_err(o, o_ref), s_err(fin, s_ref)
+    report(f"channel gated prefill {dtype} d{d} Hk{Hk}", o=eo, state=es)
+    assert eo <= _tol(c) and es <= _tol(c)
+
+
+def test_channel_gated_packed():
+    c = inputs.make_channel_gated(seed=82, H=3, d=128, lengths=[40, 0, 1, 129, 64])
+    o, fin = run_prefill(c, entry=gdn.gdn_prefill_channel_gated)
+    o_ref, s_ref = _oracle_channel(c)
+    cu = [int(x) for x in c.cu_seqlens.tolist()]
+    eo, es = o_err_packed(o, o_ref, cu), s_err(fin, s_ref)
+    report("channel gated packed", o=eo, state=es)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+    assert torch.equal(fin[1].cpu(), c.s0[1])          # the empty sequence keeps its state
+
+
+def test_channel_gated_equal_channels_match_the_head_gate():
+    """Equal rates on every channel: the per-channel kernels give the per-head
+    kernels' result (fp32, same token-serial arithmetic up to rounding)."""
+    c = inputs.make_prefill(seed=83, B=2, T=100, H=3, d=64, dtype="f32", with_state=True)
+    gc = c.g[..., None].expand(-1, -1, -1, 64).contiguous()
+    s0 = dev(c.s0)
+    f1 = torch.empty_like(s0)
+    f2 = torch.empty_like(s0)
+    o1, _ = gdn.gdn_prefill_recurrent(dev(c.q), dev(c.k), dev(c.v), dev(c.g), dev(c.beta), s0, f1,
+                                      scale=c.scale)
+    o2, _ = gdn.gdn_prefill_channel_gated(dev(c.q), dev(c.k), dev(c.v), dev(gc), dev(c.beta), s0,
+                                          f2, scale=c.scale)
+    torch.cuda.synchronize()
+    assert o_err(o2, host64(o1)) <= 1e-5 and s_err(f2, host64(f1)) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_channel_gated_decode_continues_prefill(dtype):
+    """Prefill of 70 tokens then 3 decode steps, all per-channel gated, against
+    the oracle over the 73 tokens."""
+    c = inputs.make_channel_gated(seed=84, B=3, T=73, H=4, Hk=2, d=128, dtype=dtype)
+    fin = torch.empty((3, 4, 128, 128), dtype=torch.float32, device="cuda:0")
+    o1, _ = gdn.gdn_prefill_channel_gated(dev(c.q[:, :70]), dev(c.k[:, :70]), dev(c.v[:, :70]),
+                                          dev(c.g[:, :70]), dev(c.beta[:, :70]), dev(c.s0), fin,
+                                          scale=c.scale)
+    outs = [o1.cpu()]
+    for t in range(70, 73):
+        o = gdn.gdn_decode_step_channel_gated(dev(c.q[:, t]), dev(c.k[:, t]), dev(c.v[:, t]),
+                                              dev(c.g[:, t]), dev(c.beta[:, t]), fin, scale=c.scale)
+        outs.append(o.cpu()[:, None])
+    torch.cuda.synchronize()
+    o_ref, s_ref = _oracle_channel(c)
+    eo, es = o_err(torch.cat(outs, 1), o_ref), s_err(fin, s_ref)
+    report(f"channel gated prefill + decode {dtype}", o=eo, state=es)
+    assert eo <= _tol(c) and es <= _tol(c)
