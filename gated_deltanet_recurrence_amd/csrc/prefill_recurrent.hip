@@ -22,13 +22,41 @@
 //
 // Work mapping: grid (row blocks, H, N). A state row (d_k floats) lives in
 // the registers of G = d_k/8 lanes for the whole sequence; rows never
-// exchange data, so there is no barrier anywhere. Per token each lane group
-// needs three length-d_k dot products (S.k, S.q, k.q), reduced with DPP.
-// The next token's q, k, v, g, beta are fetched while the current token is
-// being processed.
+// exchange data. Per token each lane group needs three length-d_k dot
+// products (S.k, S.q, k.q), reduced with DPP. Tokens are staged through LDS
+// in blocks of TB: the workgroup's 256 threads fetch a block's q, k, g and
+// beta with 16-byte loads (once per workgroup, not once per lane group) and
+// its rows of v, one block ahead in registers, so the memory latency is paid
+// once per block and overlaps the previous block's tokens. One barrier per
+// block.
 #include "common.h"
 
 namespace gdn {
+
+template <int DK, typename TIO, bool PERCH>
+struct RecurrentShape {
+    static constexpr int G = DK / 8;                    // lanes per state row
+    static constexpr int RPB = 256 / G;                 // state rows per workgroup
+    static constexpr int TB = 32;                       // tokens per staged block
+    static constexpr int SZ = (int)sizeof(TIO);
+    static constexpr int CPT = DK * SZ / 16;            // 16-byte chunks of a q or k row
+    static constexpr int NQK = (2 * TB * CPT + 255) / 256;
+    static constexpr int NV = (TB * RPB + 255) / 256;   // v elements per thread
+    static constexpr int GCH = PERCH ? TB * DK / 4 : 0; // 16-byte chunks of per-channel g
+    static constexpr int NG = PERCH ? (GCH + 255) / 256 : 0;
+    static constexpr int GD = PERCH ? DK : 1;           // g values per token
+    // LDS bytes of one block buffer: q, k [TB][DK] TIO; g [TB][GD] (per channel:
+    // exp(g), the decay factors), beta [TB] fp32;
+    // v [TB][RPB] fp32
+    static constexpr int L_Q = 0;
+    static constexpr int L_K = L_Q + TB * DK * SZ;
+    static constexpr int L_G = L_K + TB * DK * SZ;
+    static constexpr int L_B = L_G + TB * GD * 4;
+    static constexpr int L_V = L_B + TB * 4;
+    static constexpr int L_BUF = L_V + TB * RPB * 4;
+    static_assert(L_BUF % 16 == 0 && L_G % 16 == 0, "16-byte aligned block buffers");
+    static_assert(TB % 4 == 0, "token groups of four never run past the block buffer");
+};
 
 template <int DK, typename TIO, bool PERCH>
 __global__ void __launch_bounds__(256)
@@ -39,13 +67,17 @@ prefill_recurrent_kernel(const TIO *__restrict__ q, const TIO *__restrict__ k,
                          const int32_t *__restrict__ cu_seqlens, int T, int H, int Hk,
                          int d_v, float scale)
 {
-    constexpr int G = DK / 8;
-    constexpr int RPB = 256 / G;              // state rows per workgroup
+    using Sh = RecurrentShape<DK, TIO, PERCH>;
+    constexpr int G = Sh::G, RPB = Sh::RPB, TB = Sh::TB, CPT = Sh::CPT;
+    __shared__ __attribute__((aligned(16))) unsigned char sbuf[2 * Sh::L_BUF];
+
     const int h = blockIdx.y, n = blockIdx.z;
     const int kh = h / (H / Hk);              // query/key head of value head h
     const int tid = threadIdx.x;
     const int lr = tid % G;
-    const int row = blockIdx.x * RPB + tid / G;
+    const int row0 = blockIdx.x * RPB;
+    const int rip = tid / G;                  // row within the block
+    const int row = row0 + rip;
     const bool active = row < d_v;            // uniform inside a row group
     const int c0 = 4 * lr, c1 = DK / 2 + 4 * lr;
 
@@ -68,87 +100,169 @@ prefill_recurrent_kernel(const TIO *__restrict__ q, const TIO *__restrict__ k,
         s1 = load4(s_init + sbase + c1);
     }
 
-    const int vrow = active ? row : 0;
-    // gg: the scalar log-decay; with PERCH, gc0/gc1 those of this lane's columns
-    auto fetch = [&](long t, f32x4 &k0, f32x4 &k1, f32x4 &q0, f32x4 &q1, float &vv, float &gg,
-                     f32x4 &gc0, f32x4 &gc1, float &bb) {
-        const size_t tk = ((size_t)t * Hk + kh) * DK;
-        k0 = load4(k + tk + c0);
-        k1 = load4(k + tk + c1);
-        q0 = load4(q + tk + c0);
-        q1 = load4(q + tk + c1);
-        vv = to_f32(v[((size_t)t * H + h) * d_v + vrow]);
-        if constexpr (PERCH) {
-            const float *gp = g + ((size_t)t * H + h) * DK;
-            gc0 = load4(gp + c0);
-            gc1 = load4(gp + c1);
-        } else {
-            gg = g[(size_t)t * H + h];
+    // ---- one block's loads, into registers (tokens past the sequence read
+    //      as zero: identity steps, and their outputs are not stored) ----
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 rqk[Sh::NQK], rg[Sh::NG > 0 ? Sh::NG : 1];
+    float rv[Sh::NV], rgs = 0.f, rbs = 0.f;
+    auto fetch = [&](long t0) {
+#pragma unroll
+        for (int i = 0; i < Sh::NQK; ++i) {
+            const int c = tid + 256 * i;
+            rqk[i] = u32x4{0u, 0u, 0u, 0u};
+            if (c < 2 * TB * CPT) {
+                const int mat = c / (TB * CPT), rem = c - mat * TB * CPT;
+                const int tok = rem / CPT, part = rem - tok * CPT;
+                const long t = t0 + tok;
+                if (t < eos)
+                    rqk[i] = *reinterpret_cast<const u32x4 *>((mat ? k : q) + ((size_t)t * Hk + kh) * DK +
+                                                              part * (16 / Sh::SZ));
+            }
         }
-        bb = beta[(size_t)t * H + h];
+#pragma unroll
+        for (int i = 0; i < Sh::NV; ++i) {
+            const int e = tid + 256 * i;
+            const int tok = e / RPB, r = e - tok * RPB;
+            const long t = t0 + tok;
+            rv[i] = (e < TB * RPB && t < eos && row0 + r < d_v)
+                        ? to_f32(v[((size_t)t * H + h) * d_v + row0 + r]) : 0.f;
+        }
+        if constexpr (PERCH) {
+#pragma unroll
+            for (int i = 0; i < Sh::NG; ++i) {
+                const int c = tid + 256 * i;
+                const int tok = c / (DK / 4), part = c - tok * (DK / 4);
+                const long t = t0 + tok;
+                rg[i] = u32x4{0u, 0u, 0u, 0u};
+                if (c < Sh::GCH && t < eos)
+                    rg[i] = *reinterpret_cast<const u32x4 *>(g + ((size_t)t * H + h) * DK + 4 * part);
+            }
+        } else {
+            rgs = (tid < TB && t0 + tid < eos) ? g[(size_t)(t0 + tid) * H + h] : 0.f;
+        }
+        rbs = (tid < TB && t0 + tid < eos) ? beta[(size_t)(t0 + tid) * H + h] : 0.f;
+    };
+    auto stage = [&](int buf) {
+        unsigned char *base = sbuf + buf * Sh::L_BUF;
+#pragma unroll
+        for (int i = 0; i < Sh::NQK; ++i) {
+            const int c = tid + 256 * i;
+            if (c < 2 * TB * CPT) *reinterpret_cast<u32x4 *>(base + 16 * c) = rqk[i];   // q then k
+        }
+        float *sv = reinterpret_cast<float *>(base + Sh::L_V);
+#pragma unroll
+        for (int i = 0; i < Sh::NV; ++i) {
+            const int e = tid + 256 * i;
+            if (e < TB * RPB) sv[e] = rv[i];
+        }
+        if constexpr (PERCH) {
+#pragma unroll
+            for (int i = 0; i < Sh::NG; ++i) {
+                const int c = tid + 256 * i;
+                if (c < Sh::GCH) {             // stored as the decay factors exp(g)
+                    const f32x4 gv = __builtin_bit_cast(f32x4, rg[i]);
+                    *reinterpret_cast<f32x4 *>(base + Sh::L_G + 16 * c) =
+                        f32x4{__expf(gv[0]), __expf(gv[1]), __expf(gv[2]), __expf(gv[3])};
+                }
+            }
+        } else {
+            if (tid < TB) reinterpret_cast<float *>(base + Sh::L_G)[tid] = rgs;
+        }
+        if (tid < TB) reinterpret_cast<float *>(base + Sh::L_B)[tid] = rbs;
     };
 
-    f32x4 k0, k1, q0, q1, gc0 = {0.f, 0.f, 0.f, 0.f}, gc1 = gc0;
-    float vv = 0.f, gg = 0.f, bb = 0.f;
-    if (bos < eos)
-        fetch(bos, k0, k1, q0, q1, vv, gg, gc0, gc1, bb);
-    for (long t = bos; t < eos; ++t) {
-        f32x4 nk0 = k0, nk1 = k1, nq0 = q0, nq1 = q1, ngc0 = gc0, ngc1 = gc1;
-        float nvv = vv, ngg = gg, nbb = bb;
-        if (t + 1 < eos)
-            fetch(t + 1, nk0, nk1, nq0, nq1, nvv, ngg, ngc0, ngc1, nbb);
-
-        float delta, sq, kq = 0.f;
-        if constexpr (PERCH) {
-            // decay each column first, then read the decayed row
+    const long len = eos - bos;
+    const int nblocks = (int)((len + TB - 1) / TB);
+    if (nblocks > 0) {
+        fetch(bos);
+        stage(0);
+    }
+    for (int blk = 0; blk < nblocks; ++blk) {
+        __syncthreads();                       // block blk staged; buffer (blk + 1) % 2 free
+        const long t0 = bos + (long)blk * TB;
+        if (blk + 1 < nblocks) fetch(t0 + TB);
+        const unsigned char *base = sbuf + (blk & 1) * Sh::L_BUF;
+        const TIO *sq = reinterpret_cast<const TIO *>(base + Sh::L_Q);
+        const TIO *sk = reinterpret_cast<const TIO *>(base + Sh::L_K);
+        const float *sg = reinterpret_cast<const float *>(base + Sh::L_G);
+        const float *sb = reinterpret_cast<const float *>(base + Sh::L_B);
+        const float *sv = reinterpret_cast<const float *>(base + Sh::L_V);
+        const int nt = (int)(eos - t0 < TB ? eos - t0 : TB);
+        // four tokens' operands are read from LDS together, then the four
+        // steps run in order: the reads of a group overlap the previous
+        // group's arithmetic instead of sitting on every token's critical path
+        constexpr int U = 4;
+        for (int j0 = 0; j0 < nt; j0 += U) {
+            f32x4 k0[U], k1[U], q0[U], q1[U], g0[U], g1[U];
+            float bb[U], vv[U], ga[U];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                s0[e] *= __expf(gc0[e]);
-                s1[e] *= __expf(gc1[e]);
+            for (int u = 0; u < U; ++u) {
+                const int j = j0 + u;           // < TB: the buffers hold TB tokens
+                k0[u] = load4(sk + j * DK + c0); k1[u] = load4(sk + j * DK + c1);
+                q0[u] = load4(sq + j * DK + c0); q1[u] = load4(sq + j * DK + c1);
+                if constexpr (PERCH) {
+                    g0[u] = load4(sg + j * DK + c0);
+                    g1[u] = load4(sg + j * DK + c1);
+                } else {
+                    ga[u] = sg[j];
+                }
+                bb[u] = sb[j];
+                vv[u] = sv[j * RPB + rip];
             }
-            float sk = 0.f;
-            sq = 0.f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sk += s0[e] * k0[e] + s1[e] * k1[e];
-                sq += s0[e] * q0[e] + s1[e] * q1[e];
-                kq += k0[e] * q0[e] + k1[e] * q1[e];
-            }
-            sk = group_sum<G>(sk);
-            sq = group_sum<G>(sq);
-            kq = group_sum<G>(kq);
-            delta = bb * (vv - sk);
+            for (int u = 0; u < U; ++u) {
+                if (j0 + u >= nt) break;        // uniform
+                float delta, sq_ = 0.f, kq = 0.f;
+                if constexpr (PERCH) {
+                    // decay each column first (the block holds exp(g)), then read
+                    // the decayed row
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                s0[e] += delta * k0[e];
-                s1[e] += delta * k1[e];
-            }
-        } else {
-            const float alpha = __expf(gg);
-            float sk = 0.f;
-            sq = 0.f;
+                    for (int e = 0; e < 4; ++e) {
+                        s0[e] *= g0[u][e];
+                        s1[e] *= g1[u][e];
+                    }
+                    float sk_ = 0.f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sk += s0[e] * k0[e] + s1[e] * k1[e];
-                sq += s0[e] * q0[e] + s1[e] * q1[e];
-                kq += k0[e] * q0[e] + k1[e] * q1[e];
-            }
-            sk = group_sum<G>(sk);
-            sq = group_sum<G>(sq);
-            kq = group_sum<G>(kq);
-            delta = bb * (vv - alpha * sk);
-            sq *= alpha;
+                    for (int e = 0; e < 4; ++e) {
+                        sk_ += s0[e] * k0[u][e] + s1[e] * k1[u][e];
+                        sq_ += s0[e] * q0[u][e] + s1[e] * q1[u][e];
+                        kq += k0[u][e] * q0[u][e] + k1[u][e] * q1[u][e];
+                    }
+                    sk_ = group_sum<G>(sk_);
+                    sq_ = group_sum<G>(sq_);
+                    kq = group_sum<G>(kq);
+                    delta = bb[u] * (vv[u] - sk_);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                s0[e] = alpha * s0[e] + delta * k0[e];
-                s1[e] = alpha * s1[e] + delta * k1[e];
+                    for (int e = 0; e < 4; ++e) {
+                        s0[e] += delta * k0[u][e];
+                        s1[e] += delta * k1[u][e];
+                    }
+                } else {
+                    const float alpha = __expf(ga[u]);
+                    float sk_ = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        sk_ += s0[e] * k0[u][e] + s1[e] * k1[u][e];
+                        sq_ += s0[e] * q0[u][e] + s1[e] * q1[u][e];
+                        kq += k0[u][e] * q0[u][e] + k1[u][e] * q1[u][e];
+                    }
+                    sk_ = group_sum<G>(sk_);
+                    sq_ = group_sum<G>(sq_);
+                    kq = group_sum<G>(kq);
+                    delta = bb[u] * (vv[u] - alpha * sk_);
+                    sq_ *= alpha;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        s0[e] = alpha * s0[e] + delta * k0[u][e];
+                        s1[e] = alpha * s1[e] + delta * k1[u][e];
+                    }
+                }
+                if (active && lr == 0)
+                    o[((size_t)(t0 + j0 + u) * H + h) * d_v + row] =
+                        from_f32<TIO>(scale * (sq_ + delta * kq));
             }
         }
-        if (active && lr == 0)
-            o[((size_t)t * H + h) * d_v + row] = from_f32<TIO>(scale * (sq + delta * kq));
-
-        k0 = nk0; k1 = nk1; q0 = nq0; q1 = nq1;
-        vv = nvv; gg = ngg; bb = nbb; gc0 = ngc0; gc1 = ngc1;
+        if (blk + 1 < nblocks) stage((blk + 1) & 1);
     }
     if (s_final && active) {
         store4(s_final + sbase + c0, s0);
