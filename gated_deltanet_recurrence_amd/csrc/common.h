@@ -98,7 +98,16 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
-__device__ __forceinline__ float silu_f32(float x) { return x / (1.0f + __expf(-x)); }
+// SiLU(x) = x * sigmoid(x) with the hardware exponential and reciprocal
+// (v_exp_f32, v_rcp_f32, about 1 ulp each) instead of an IEEE division: the
+// elementwise stages are bound by memory, and a correctly rounded divide per
+// channel costs them more than their loads. Large negative x gives
+// exp(-x) = inf, rcp(inf) = 0 and -0, the limit.
+__device__ __forceinline__ float silu_f32(float x) {
+    return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
+// 1 / sqrt(x) for x > 0 by the hardware reciprocal square root (about 1 ulp).
+__device__ __forceinline__ float rsqrt_f32(float x) { return __builtin_amdgcn_rsqf(x); }
 
 // softplus(x) = log(1 + e^x), evaluated without overflow.
 __device__ __forceinline__ float softplus_f32(float x) {

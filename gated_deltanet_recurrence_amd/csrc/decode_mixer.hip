@@ -135,7 +135,7 @@ decode_mixer_kernel(const TIO *__restrict__ q_raw, const TIO *__restrict__ k_raw
     }
     ssq = group_sum<G>(ssq);
     ssk = group_sum<G>(ssk);
-    const float iq = 1.0f / sqrtf(ssq + 1e-6f), ik = 1.0f / sqrtf(ssk + 1e-6f);
+    const float iq = rsqrt_f32(ssq + 1e-6f), ik = rsqrt_f32(ssk + 1e-6f);
     q0 *= iq; q1 *= iq; k0 *= ik; k1 *= ik;
     float kq = 0.f;
 #pragma unroll
@@ -200,7 +200,7 @@ decode_mixer_kernel(const TIO *__restrict__ q_raw, const TIO *__restrict__ k_raw
     for (int i = tid; i < R; i += DM_NT) {
         const int j = i / d_v, c = i - j * d_v;
         const size_t oi = ((size_t)bb * H + h0) * d_v + i;
-        const float inv = 1.0f / sqrtf(sss[j] * (1.0f / d_v) + eps);
+        const float inv = rsqrt_f32(sss[j] * (1.0f / d_v) + eps);
         const float wv = norm_w ? norm_w[c] : 1.0f;
         out[oi] = from_f32<TIO>(wv * (sy[i] * inv) * silu_f32(to_f32(z[oi])));
     }

@@ -18,15 +18,39 @@
 //
 // Work mapping (both kernels): one (token, head) row of D channels is owned
 // by G = D/8 lanes, 8 channels (16 B of bf16) per lane, so row reductions are
-// DPP sums inside the group. In the prologue each group walks a tile of TT
+// DPP sums inside the group. In the prologue the lane groups of a workgroup
+// take consecutive heads of one tensor (so a workgroup streams whole token
+// rows) and each group walks a tile of TT
 // consecutive tokens of one head of one tensor and keeps the three previous
 // inputs of its channels in registers (the convolution window), so every
-// input element is read from HBM once.
+// input element is read from HBM once (plus three tokens of history per
+// tile); the tile's loads are all issued before its first token is computed.
 #include "common.h"
 
 namespace gdn {
 
 constexpr int PRO_TT = 16;          // tokens per lane group in the prologue
+
+// Eight consecutive elements of a storage type as loaded (16 B of bf16, 32 B
+// of fp32), converted to fp32 only where they are used, so that a lane can
+// keep many tokens' loads in flight in few registers.
+template <typename TIO> struct Raw8;
+template <> struct Raw8<bf16> {
+    bf16x8 v;
+    __device__ __forceinline__ void load(const bf16 *p) { v = *reinterpret_cast<const bf16x8 *>(p); }
+    __device__ __forceinline__ void get(float (&x)[8]) const {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = (float)v[i];
+    }
+};
+template <> struct Raw8<float> {
+    f32x4 a, b;
+    __device__ __forceinline__ void load(const float *p) { a = load4(p); b = load4(p + 4); }
+    __device__ __forceinline__ void get(float (&x)[8]) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[4 + i] = b[i]; }
+    }
+};
 
 // Sequence of global token t: [start, end). cu == nullptr: rows of T tokens.
 __device__ __forceinline__ void seq_bounds(const int32_t *cu, int N, long T, long t, long &start,
@@ -66,11 +90,14 @@ prologue_conv_kernel(const TIO *__restrict__ x_q, const TIO *__restrict__ x_k,
     constexpr int G = D / 8;
     constexpr int GPB = 256 / G;                  // lane groups per block
     const int which = which0 + (int)blockIdx.z;   // 0 = q, 1 = k, 2 = v
-    const int h = blockIdx.y;                     // head of this tensor
-    const int Ht = which < 2 ? Hk : H;            // heads of this tensor
+    const int Ht0 = which < 2 ? Hk : H;
+    // the lane groups of a workgroup take consecutive heads of one token tile,
+    // so that together they stream whole token rows
+    const int h = (int)blockIdx.y * GPB + (int)threadIdx.x / G;   // head of this tensor
+    if (h >= Ht0) return;                         // whole lane groups
+    const int Ht = Ht0;                           // heads of this tensor
     const int lr = threadIdx.x % G;
-    const long t0 = ((long)blockIdx.x * GPB + threadIdx.x / G) * PRO_TT;
-    if (t0 >= total) return;
+    const long t0 = (long)blockIdx.x * PRO_TT;
     const long t1 = t0 + PRO_TT < total ? t0 + PRO_TT : total;
 
     const TIO *x = which == 0 ? x_q : (which == 1 ? x_k : x_v);
@@ -78,11 +105,16 @@ prologue_conv_kernel(const TIO *__restrict__ x_q, const TIO *__restrict__ x_k,
     const int c = 8 * lr;
     // conv channel of (tensor, head, c): q channels, then k, then v
     const long ch = (long)which * Hk * d_k + (long)h * D + c;
-    float w[8][4];
+    // the 4 taps of this lane's 8 channels are 32 consecutive weights: four
+    // 8-element loads, kept as loaded
+    float w[4][8];                                // w[u][8 r + j]: channel 2 u + r, tap j
+    {
+        Raw8<TIO> wr[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+        for (int i = 0; i < 4; ++i) wr[i].load(conv_w + ch * 4 + 8 * i);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) w[e][j] = to_f32(conv_w[(ch + e) * 4 + j]);
+        for (int i = 0; i < 4; ++i) wr[i].get(w[i]);
+    }
 
     long start, end;
     int n;
@@ -96,7 +128,15 @@ prologue_conv_kernel(const TIO *__restrict__ x_q, const TIO *__restrict__ x_k,
     if (t0 - 2 >= start) load8(x + row(t0 - 2), x2);
     if (t0 - 3 >= start) load8(x + row(t0 - 3), x3);
 
-    for (long t = t0; t < t1; ++t) {
+    Raw8<TIO> xr[PRO_TT];                         // the tile's inputs, requested up front
+#pragma unroll
+    for (int i = 0; i < PRO_TT; ++i)
+        if (t0 + i < t1) xr[i].load(x + row(t0 + i));
+
+#pragma unroll
+    for (int i = 0; i < PRO_TT; ++i) {
+        const long t = t0 + i;
+        if (t >= t1) break;                       // uniform across the lane group
         while (t >= end && n < N - 1) {           // crossed into the next sequence
             ++n;
             start = end;
@@ -106,18 +146,18 @@ prologue_conv_kernel(const TIO *__restrict__ x_q, const TIO *__restrict__ x_k,
             for (int e = 0; e < 8; ++e) { x1[e] = 0.f; x2[e] = 0.f; x3[e] = 0.f; }
         }
         float xt[8], out[8];
-        load8(x + row(t), xt);
+        xr[i].get(xt);
         float ss = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float pre = w[e][3] * xt[e] + w[e][2] * x1[e] + w[e][1] * x2[e]
-                            + w[e][0] * x3[e];
+            const float *we = &w[e >> 1][4 * (e & 1)];      // taps 0..3 of channel e
+            const float pre = we[3] * xt[e] + we[2] * x1[e] + we[1] * x2[e] + we[0] * x3[e];
             out[e] = silu_f32(pre);
             ss += out[e] * out[e];
         }
         if (which < 2) {                          // L2-norm of q and k rows
             ss = group_sum<G>(ss);
-            const float inv = 1.0f / sqrtf(ss + 1e-6f);
+            const float inv = rsqrt_f32(ss + 1e-6f);
 #pragma unroll
             for (int e = 0; e < 8; ++e) out[e] *= inv;
         }
@@ -154,7 +194,7 @@ epilogue_kernel(const TIO *y, const TIO *__restrict__ z, const float *__restrict
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss += yv[e] * yv[e];
         ss = group_sum<G>(ss);
-        const float inv = 1.0f / sqrtf(ss * (1.0f / D) + eps);
+        const float inv = rsqrt_f32(ss * (1.0f / D) + eps);
 #pragma unroll
         for (int e = 0; e < 8; ++e) ov[e] = wv[e] * (yv[e] * inv) * silu_f32(zv[e]);
         store8(out + (size_t)r * D + c, ov);
@@ -171,7 +211,7 @@ static hipError_t launch_conv(const void *xq, const void *xk, const void *xv, co
     constexpr int GPB = 256 / (D / 8);
     const long tiles = (total + PRO_TT - 1) / PRO_TT;
     const int heads = which0 < 2 ? Hk : H;
-    dim3 grid((unsigned)((tiles + GPB - 1) / GPB), (unsigned)heads, (unsigned)nwhich), block(256);
+    dim3 grid((unsigned)tiles, (unsigned)((heads + GPB - 1) / GPB), (unsigned)nwhich), block(256);
     hipLaunchKernelGGL((prologue_conv_kernel<D, TIO>), grid, block, 0, stream,
                        (const TIO *)xq, (const TIO *)xk, (const TIO *)xv, (const TIO *)w,
                        (TIO *)yq, (TIO *)yk, (TIO *)yv, (const TIO *)a, (const TIO *)b, A, dtb,
