@@ -32,6 +32,8 @@ carries:
 * ``mixer``: prologue -> prefill -> epilogue at B=8, T=8192, H=16, d=128;
 * ``varlen``: packed prefill, H=32, 8 sequences, lengths log-uniform in
   [512, 65536], non-zero initial states;
+* ``seqpar``: one long sequence (B=1, H=16, T=32768) by the plain two-pass
+  prefill and by the sequence-parallel prefill with 4, 8, 16 segments;
 * ``cpu_baseline``: the fp64 CPU oracle timed on this host on the prefill
   workload (a reported baseline, not a target).
 
@@ -263,6 +265,38 @@ def bench_channel_gated(gdn, inputs, steps, warmup):
                 decode_frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
 
 
+def bench_seqpar(gdn, inputs, steps, warmup):
+    """One long sequence (B=1, H=16, T=32768, d=128, bf16): the plain two-pass
+    prefill (16 (sequence, head) pairs = 64 chain workgroups on 256 CUs)
+    against the sequence-parallel prefill with 4, 8 and 16 segments."""
+    import torch
+    c = inputs.make_prefill(seed=92, B=1, T=32768, H=16)
+    d = lambda t: t.cuda().contiguous()
+    q, k, v, g, beta = (d(x) for x in (c.q, c.k, c.v, c.g, c.beta))
+    fin = torch.empty((1, 16, 128, 128), dtype=torch.float32, device="cuda")
+    o = torch.empty_like(v)
+    ws = torch.empty(gdn.gdn_prefill_workspace_size(1, 32768, 16, 128, 128, 1, False,
+                                                    torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    ms_plain = event_time(lambda i: gdn.gdn_prefill(q, k, v, g, beta, None, fin, o,
+                                                    scale=c.scale, workspace=ws),
+                          max(1, steps // 4), 1)
+    res = dict(workload="one sequence B=1 H=16 T=32768 d=128 bf16",
+               plain_ms=round(ms_plain, 4),
+               plain_tokens_per_s=round(32768 / (ms_plain * 1e-3), 1))
+    for P in (4, 8, 16):
+        wsp = torch.empty(gdn.gdn_prefill_seqpar_workspace_size(1, 32768, 16, 128, 128, P,
+                                                                torch.bfloat16),
+                          dtype=torch.uint8, device="cuda")
+        ms = event_time(lambda i: gdn.gdn_prefill_seqpar(q, k, v, g, beta, P, None, fin, o,
+                                                         scale=c.scale, workspace=wsp),
+                        max(1, steps // 4), 1)
+        res[f"segments_{P}_ms"] = round(ms, 4)
+        res[f"segments_{P}_tokens_per_s"] = round(32768 / (ms * 1e-3), 1)
+        del wsp
+    return res
+
+
 def bench_mixer(gdn, inputs, steps, warmup):
     import torch
     c = inputs.make_mixer()
@@ -361,9 +395,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="prefill,decode,decode_mixer,channel,mixer,varlen,cpu",
+    ap.add_argument("--only", default="prefill,decode,decode_mixer,channel,mixer,varlen,seqpar,cpu",
                     help="comma list of: prefill, decode, decode_mixer, channel, mixer, varlen, "
-                         "cpu, copy")
+                         "seqpar, cpu, copy")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -423,6 +457,8 @@ def main():
         result["mixer"] = bench_mixer(gdn, inputs, args.steps, args.warmup)
     if "varlen" in which:
         result["varlen"] = bench_varlen(gdn, inputs, args.steps, args.warmup)
+    if "seqpar" in which:
+        result["seqpar"] = bench_seqpar(gdn, inputs, args.steps, args.warmup)
     if "copy" in which:
         result["copy_calibration"] = bench_copy(args.steps, args.warmup)
     if "cpu" in which:

@@ -23,7 +23,7 @@ hipError_t launch_prefill_prepare(const void *, const void *, const float *, con
                                   const int32_t *, int, int, int, int, void *, hipStream_t);
 hipError_t launch_prefill_apply(const void *, const void *, const void *, const float *,
                                 const float *, float *, void *, const int32_t *, int, int, int,
-                                int, float, const void *, hipStream_t);
+                                int, float, const void *, hipStream_t, int flags = 0);
 size_t prefill_split_workspace_bytes(long tokens, int H, int N);
 template <typename TIO>
 hipError_t launch_prologue(const void *, const void *, const void *, const void *, const void *,
@@ -36,6 +36,10 @@ hipError_t launch_decode_mixer(const void *, const void *, const void *, const v
                                const void *, const float *, float, float *, void *, int, int,
                                int, int, int, float, hipStream_t);
 constexpr int DECODE_MIXER_MAX_ROWS = 4096;
+size_t prefill_seqpar_workspace_bytes(int B, int T, int H, int P);
+hipError_t launch_prefill_seqpar(const void *, const void *, const void *, const float *,
+                                 const float *, const float *, float *, void *, int, int, int,
+                                 int, int, float, void *, hipStream_t);
 template <typename TIO>
 hipError_t launch_epilogue(const void *, const void *, const float *, void *, long, int, float,
                            hipStream_t);
@@ -321,6 +325,48 @@ int gdn_decode_step_channel_gated(const void *q, const void *k, const void *v, c
         : gdn::launch_decode<float>(q, k, v, g, beta, state, o, B, H, H_k, d_k, d_v, scale, true,
                                     s);
     return status_of(e);
+}
+
+// Shared validation of the sequence-parallel prefill's sizes.
+static int check_seqpar(int B, int T, int H, int H_k, int d_k, int d_v, int segments, int dtype)
+{
+    if (!valid_dtype(dtype)) return GDN_ERR_DTYPE;
+    if (B < 1 || T < 0 || segments < 1 || !heads_ok(H, H_k)) return GDN_ERR_SHAPE;
+    if ((int64_t)B * T > (int64_t)INT32_MAX) return GDN_ERR_SHAPE;
+    if (!chunk_path(dtype, d_k, d_v)) return GDN_ERR_UNSUPPORTED;
+    if (H > 65535 || (int64_t)B * segments > 65535) return GDN_ERR_UNSUPPORTED;
+    if ((int64_t)H * B * segments * 4 > (int64_t)INT32_MAX) return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+int gdn_prefill_seqpar_workspace_size(int B, int T, int H, int d_k, int d_v, int segments,
+                                      int dtype, size_t *bytes)
+{
+    if (!bytes) return GDN_ERR_NULL;
+    *bytes = 0;
+    const int st = check_seqpar(B, T, H, H, d_k, d_v, segments, dtype);
+    if (st != GDN_OK) return st;
+    *bytes = gdn::prefill_seqpar_workspace_bytes(B, T, H, segments);
+    return GDN_OK;
+}
+
+int gdn_prefill_seqpar(const void *q, const void *k, const void *v, const float *g,
+                       const float *beta, const float *initial_state, float *final_state,
+                       void *o, int B, int T, int H, int H_k, int d_k, int d_v, int segments,
+                       float scale, int dtype, void *workspace, size_t workspace_bytes,
+                       void *stream)
+{
+    const bool no_tokens = (int64_t)B * T == 0;
+    if (!no_tokens && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
+    if (!workspace) return GDN_ERR_NULL;
+    const int st = check_seqpar(B, T, H, H_k, d_k, d_v, segments, dtype);
+    if (st != GDN_OK) return st;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0 ||
+        workspace_bytes < gdn::prefill_seqpar_workspace_bytes(B, T, H, segments))
+        return GDN_ERR_WORKSPACE;
+    return status_of(gdn::launch_prefill_seqpar(q, k, v, g, beta, initial_state, final_state, o,
+                                                B, T, H, H_k, segments, scale, workspace,
+                                                (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -91,6 +91,11 @@ static_assert(P_LDS_BYTES <= 160 * 1024 / 3, "three prep workgroups per CU");
 // ---------------------------------------------------------------------------
 constexpr int DVT = 32;
 constexpr int NT = 512;
+// chain_kernel flags: V read as zero; initial state the identity (s_init
+// ignored). With both and d_v = d_k the final state of a token range is the
+// linear part A of its state map S_end = S_start A + B.
+constexpr int CHAIN_ZERO_V = 1;
+constexpr int CHAIN_INIT_IDENTITY = 2;
 constexpr int LD_R = DK + 16;                  // 144: Q, K, S rows
 constexpr int LD_L = C + 16;                   // 80: rows 32-63 of T_w, T_u, P; Delta^T rows
 constexpr int LD_H = 32 + 8;                   // 40: rows 0-31 of T_w, T_u, P; V rows
@@ -605,7 +610,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                    const bf16 *__restrict__ v, const float *__restrict__ g,
                    const bf16 *__restrict__ ws, const float *s_init, float *s_final,
                    bf16 *__restrict__ o, const int32_t *__restrict__ cu_seqlens, int T, int H,
-                   int Hk, int npairs, int nslots, float scale)
+                   int Hk, int npairs, int nslots, float scale, int flags)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     bf16 *lds = reinterpret_cast<bf16 *>(smem);
@@ -650,7 +655,14 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     if (wave < 2) {
         const int m = lane0 & 15, qq = lane0 >> 4;
         const int col = cbase + 16 * wave + m;
-        if (s_init) {
+        if (flags & CHAIN_INIT_IDENTITY) {
+            // S = I: this lane's entries S[col][32 (d/2) + 8 qq + 4 (d%2) + r]
+#pragma unroll
+            for (int d = 0; d < 8; ++d)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    Sacc[d][r] = (32 * (d >> 1) + 8 * qq + 4 * (d & 1) + r == col) ? 1.f : 0.f;
+        } else if (s_init) {
 #pragma unroll
             for (int d = 0; d < 8; ++d)
                 Sacc[d] = *reinterpret_cast<const f32x4 *>(s_init + sbase + (size_t)col * DK + 32 * (d >> 1) + 8 * qq + 4 * (d & 1));
@@ -721,8 +733,10 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             rs.t[r] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
                           rw, 16 * lane0, 16 * (192 * wi + 64 * r), 0));
         if constexpr (decltype(WV)::value) {
+            // with CHAIN_ZERO_V the resource spans nothing and every load reads zero
             const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(v_head + (size_t)base * tsv), 0, (unsigned)nrow * tsv * 2, 0x00020000);
+                (void *)(v_head + (size_t)base * tsv), 0,
+                (flags & CHAIN_ZERO_V) ? 0u : (unsigned)nrow * tsv * 2, 0x00020000);
 #pragma unroll
             for (int r = 0; r < 2; ++r)
                 rs.v[r] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
@@ -906,7 +920,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             int tidl = tid0;
             asm volatile("" : "+v"(tidl));
             const int lane = tidl & 63, m = lane & 15, qq = lane >> 4;
-            if (ch >= 0 && ch < nchunks) {
+            if (o && ch >= 0 && ch < nchunks) {   // o == NULL: the states only
                 // (Q S^T)^T = S Q^T, all 64 tokens, then e^gamma per token
                 const bf16 *sSc = cpS(b), *sQ = stQ(b);
                 const float *sEg = stSc(b) + C;
@@ -927,7 +941,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
                 for (int t = 0; t < 4; ++t) oacc[b][t] = oacc[b][t] * sEg[16 * t + m];
             }
-            if (ch >= 1 && ch <= nchunks) {
+            if (o && ch >= 1 && ch <= nchunks) {
                 // finish chunk ch - 1: O^T += Delta^T P^T (token tile t needs keys
                 // 0 .. 16 t + 15), then its rows to HBM
                 const int cp = ch - 1;
@@ -1060,7 +1074,7 @@ hipError_t launch_prefill_prepare(const void *q, const void *k, const float *g, 
 hipError_t launch_prefill_apply(const void *q, const void *k, const void *v, const float *g,
                                 const float *s_init, float *s_final, void *o, const int32_t *cu,
                                 int T, int H, int Hk, int N, float scale, const void *ws,
-                                hipStream_t stream)
+                                hipStream_t stream, int flags)
 {
     static bool attr_done = false;
     if (!attr_done) {
@@ -1075,7 +1089,7 @@ hipError_t launch_prefill_apply(const void *q, const void *k, const void *v, con
     dim3 grid(pair_grid(npairs)), block(NT);
     hipLaunchKernelGGL(chunk_chain_kernel, grid, block, LDS_BYTES, stream, (const bf16 *)q,
                        (const bf16 *)k, (const bf16 *)v, g, (const bf16 *)ws, s_init, s_final,
-                       (bf16 *)o, cu, T, H, Hk, npairs, (int)nslots, scale);
+                       (bf16 *)o, cu, T, H, Hk, npairs, (int)nslots, scale, flags);
     return hipGetLastError();
 }
 

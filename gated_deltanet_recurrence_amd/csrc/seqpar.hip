@@ -1,0 +1,192 @@
+// seqpar.hip - sequence-parallel chunked prefill: one long sequence is cut
+// into segments whose chains run side by side.
+//
+// "[LLM Algorithms-2] Gated DeltaNet: Teaching Linear Attention to Overwrite
+// and Forget", section 7: a run of tokens acts on the state as one affine map,
+// S_end = S_start A + B (A = the product of the tokens' alpha (I - beta k k^T),
+// B = the decayed sum of their writes). So, with the sequence cut into P
+// segments of whole 64-token chunks:
+//   1. every segment's chain runs from a zero state on its own values:
+//      its final state is B_s;
+//   2. every segment's chain runs with v = 0 from the identity: its final
+//      state (d_v = d_k rows e_j A_s) is A_s;
+//   3. the segment start states follow in order, S_{s+1} = S_s A_s + B_s,
+//      S_0 the caller's initial state; S_P is the final state;
+//   4. every segment's chain runs again from S_s and writes the outputs.
+// Steps 1, 2 and 4 are the chain pass over P times more (shorter) sequences,
+// so a batch with too few (sequence, head) pairs to fill the GPU fills it;
+// the price is three chain passes instead of one, and step 3's P dependent
+// 128 x 128 x 128 products per head.
+#include "chunk_common.h"
+
+namespace gdn {
+
+constexpr int SP_D = 128;                      // d_k = d_v of the chunk kernels
+
+hipError_t launch_prefill_prepare(const void *, const void *, const float *, const float *,
+                                  const int32_t *, int, int, int, int, void *, hipStream_t);
+hipError_t launch_prefill_apply(const void *, const void *, const void *, const float *,
+                                const float *, float *, void *, const int32_t *, int, int, int,
+                                int, float, const void *, hipStream_t, int flags);
+size_t prefill_split_workspace_bytes(long tokens, int H, int N);
+
+namespace split {
+constexpr int CHAIN_ZERO_V = 1;                // as in prefill_split.hip
+constexpr int CHAIN_INIT_IDENTITY = 2;
+}
+
+// Segment offsets of B sequences of T tokens cut into P segments of L tokens
+// (the last ones shorter or empty), packed along the token axis.
+__global__ void seg_offsets_kernel(int32_t *cu, int B, int T, int P, int L)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    const int n = B * P;
+    if (i > n) return;
+    if (i == n) { cu[i] = B * T; return; }
+    const int b = i / P, s = i - b * P;
+    const long start = (long)s * L;
+    cu[i] = (int32_t)((long)b * T + (start < T ? start : T));
+}
+
+// The final state when there is no token: the initial state, or zeros.
+__global__ void state_copy_kernel(const float *src, float *dst, long n4)
+{
+    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n4)
+        reinterpret_cast<f32x4 *>(dst)[i] =
+            src ? reinterpret_cast<const f32x4 *>(src)[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Step 3. One workgroup per (sequence, head, block of 16 state rows); a lane
+// group of 16 lanes owns one row, 8 columns per lane. For s = 0 .. P-1:
+// inits[s] = S, then S <- S A_s + B_s (the row block of S staged in LDS, A_s
+// rows read by all row groups at once); finally final_state = S.
+__global__ void __launch_bounds__(256)
+seg_compose_kernel(const float *__restrict__ Amat, const float *__restrict__ Bmat,
+                   const float *s_init, float *__restrict__ inits, float *s_final, int H, int P)
+{
+    __shared__ float sS[16][SP_D + 4];
+    const int bh = blockIdx.x, b = bh / H, h = bh - b * H;
+    const int tid = threadIdx.x, r = tid >> 4, l = tid & 15;
+    const int row = blockIdx.y * 16 + r, c0 = 8 * l;
+    const size_t mat = (size_t)SP_D * SP_D;
+    float cur[8];
+    if (s_init) {
+        const float *p = s_init + ((size_t)bh * SP_D + row) * SP_D + c0;
+        const f32x4 x0 = *reinterpret_cast<const f32x4 *>(p), x1 = *reinterpret_cast<const f32x4 *>(p + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { cur[e] = x0[e]; cur[4 + e] = x1[e]; }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cur[e] = 0.f;
+    }
+    for (int s = 0; s < P; ++s) {
+        const size_t seg = ((size_t)b * P + s) * H + h;
+        float *ip = inits + seg * mat + (size_t)row * SP_D + c0;
+        *reinterpret_cast<f32x4 *>(ip) = f32x4{cur[0], cur[1], cur[2], cur[3]};
+        *reinterpret_cast<f32x4 *>(ip + 4) = f32x4{cur[4], cur[5], cur[6], cur[7]};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sS[r][c0 + e] = cur[e];
+        __syncthreads();
+        const float *bp = Bmat + seg * mat + (size_t)row * SP_D + c0;
+        const f32x4 b0 = *reinterpret_cast<const f32x4 *>(bp), b1 = *reinterpret_cast<const f32x4 *>(bp + 4);
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { acc[e] = b0[e]; acc[4 + e] = b1[e]; }
+        const float *ap = Amat + seg * mat + c0;
+#pragma unroll 4
+        for (int j = 0; j < SP_D; ++j) {
+            const float sj = sS[r][j];
+            const f32x4 a0 = *reinterpret_cast<const f32x4 *>(ap + (size_t)j * SP_D);
+            const f32x4 a1 = *reinterpret_cast<const f32x4 *>(ap + (size_t)j * SP_D + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[e] += sj * a0[e];
+                acc[4 + e] += sj * a1[e];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cur[e] = acc[e];
+        __syncthreads();                       // sS read before the next segment's write
+    }
+    if (s_final) {
+        float *p = s_final + ((size_t)bh * SP_D + row) * SP_D + c0;
+        *reinterpret_cast<f32x4 *>(p) = f32x4{cur[0], cur[1], cur[2], cur[3]};
+        *reinterpret_cast<f32x4 *>(p + 4) = f32x4{cur[4], cur[5], cur[6], cur[7]};
+    }
+}
+
+// Workspace: the two-pass workspace for B * P segments, their offsets, and
+// A, B and the start states of every (segment, head).
+struct SeqparLayout {
+    size_t prep, cu, amat, bmat, inits, total;
+};
+static SeqparLayout seqpar_layout(int B, int T, int H, int P)
+{
+    const int nseg = B * P;
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    SeqparLayout L;
+    L.prep = 0;
+    L.cu = up(prefill_split_workspace_bytes((long)B * T, H, nseg));
+    const size_t mats = (size_t)nseg * H * SP_D * SP_D * sizeof(float);
+    L.amat = L.cu + up((size_t)(nseg + 1) * sizeof(int32_t));
+    L.bmat = L.amat + up(mats);
+    L.inits = L.bmat + up(mats);
+    L.total = L.inits + up(mats);
+    return L;
+}
+
+size_t prefill_seqpar_workspace_bytes(int B, int T, int H, int P)
+{
+    return seqpar_layout(B, T, H, P).total;
+}
+
+hipError_t launch_prefill_seqpar(const void *q, const void *k, const void *v, const float *g,
+                                 const float *beta, const float *s_init, float *s_final,
+                                 void *o, int B, int T, int H, int Hk, int P, float scale,
+                                 void *ws, hipStream_t stream)
+{
+    if ((long)B * T == 0) {
+        // nothing to run: the final state is the initial state (or zero),
+        // copied by a kernel (no memset or copy node if the caller captures)
+        if (!s_final) return hipSuccess;
+        const long n4 = (long)B * H * SP_D * SP_D / 4;
+        hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0,
+                           stream, s_init, s_final, n4);
+        return hipGetLastError();
+    }
+    const SeqparLayout Ly = seqpar_layout(B, T, H, P);
+    unsigned char *base = static_cast<unsigned char *>(ws);
+    void *prep = base + Ly.prep;
+    int32_t *cu = reinterpret_cast<int32_t *>(base + Ly.cu);
+    float *Am = reinterpret_cast<float *>(base + Ly.amat);
+    float *Bm = reinterpret_cast<float *>(base + Ly.bmat);
+    float *In = reinterpret_cast<float *>(base + Ly.inits);
+    const int nseg = B * P;
+    const int chunks = (T + 63) / 64;
+    const int L = ((chunks + P - 1) / P) * 64;     // tokens per segment, whole chunks
+    const int total = B * T;
+
+    hipLaunchKernelGGL(seg_offsets_kernel, dim3((nseg + 1 + 255) / 256), dim3(256), 0, stream,
+                       cu, B, T, P, L);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess)
+        e = launch_prefill_prepare(q, k, g, beta, cu, total, H, Hk, nseg, prep, stream);
+    if (e == hipSuccess)          // 1: B_s, the segments from a zero state
+        e = launch_prefill_apply(q, k, v, g, nullptr, Bm, nullptr, cu, total, H, Hk, nseg, scale,
+                                 prep, stream, 0);
+    if (e == hipSuccess)          // 2: A_s, v = 0 from the identity
+        e = launch_prefill_apply(q, k, v, g, nullptr, Am, nullptr, cu, total, H, Hk, nseg, scale,
+                                 prep, stream, split::CHAIN_ZERO_V | split::CHAIN_INIT_IDENTITY);
+    if (e == hipSuccess) {        // 3: the start states, in order
+        hipLaunchKernelGGL(seg_compose_kernel, dim3((unsigned)(B * H), SP_D / 16), dim3(256), 0,
+                           stream, Am, Bm, s_init, In, s_final, H, P);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess)          // 4: the outputs
+        e = launch_prefill_apply(q, k, v, g, In, nullptr, o, cu, total, H, Hk, nseg, scale, prep,
+                                 stream, 0);
+    return e;
+}
+
+}  // namespace gdn

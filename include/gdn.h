@@ -184,6 +184,38 @@ int gdn_prefill_apply(const void *q, const void *k, const void *v, const float *
                       const void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * gdn_prefill_seqpar - the same forward pass as gdn_prefill for B sequences
+ * of T tokens, with each sequence cut into `segments` runs of whole 64-token
+ * chunks whose chains run side by side: for batches with too few (sequence,
+ * head) pairs to fill the GPU (a single long sequence, few heads). A run of
+ * tokens acts on the state as one affine map S_end = S_start A + B
+ * ("Overwrite and Forget", section 7); the call computes B and A of every
+ * segment by two chain passes (zero start state; v = 0 from the identity),
+ * the segment start states in order, then a third chain pass with the true
+ * start states that writes o. Three chain passes instead of one: use it when
+ * B * H * 4 is well below the number of compute units. The result equals
+ * gdn_prefill's up to rounding (the segment maps carry the bf16 rounding of
+ * the chunk kernels once more).
+ *
+ *   arguments     as gdn_prefill, without cu_seqlens (N = B); bf16 and
+ *                 d_k = d_v = 128 only (else GDN_ERR_UNSUPPORTED)
+ *   segments      >= 1 segments per sequence (B * segments <= 65535);
+ *                 segments past the sequence's chunks are empty
+ *   workspace     required, gdn_prefill_seqpar_workspace_size() bytes,
+ *                 256-byte aligned; contents on entry do not matter
+ */
+int gdn_prefill_seqpar(const void *q, const void *k, const void *v,
+                       const float *g, const float *beta,
+                       const float *initial_state, float *final_state, void *o,
+                       int B, int T, int H, int H_k, int d_k, int d_v, int segments,
+                       float scale, int dtype,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace gdn_prefill_seqpar needs (H the value heads). */
+int gdn_prefill_seqpar_workspace_size(int B, int T, int H, int d_k, int d_v, int segments,
+                                      int dtype, size_t *bytes);
+
+/*
  * gdn_prefill_recurrent - the same forward pass as gdn_prefill, computed by
  * the token-serial recurrence in fp32 arithmetic (the "recurrent" execution
  * path of "Overwrite and Forget", section 7). Same arguments, layouts and

@@ -187,3 +187,22 @@ def test_channel_gated_validation(lib):
     assert d(P, P, P, None, P, P, P, 1, 2, 2, 128, 128, 1.0, 1, None) == GDN_ERR_NULL
     assert d(P, P, P, P, P, P, P, 1, 2, 2, 128, 128, 1.0, 3, None) == GDN_ERR_DTYPE
     assert d(P, P, P, P, P, P, P, 1, 6, 4, 128, 128, 1.0, 1, None) == GDN_ERR_SHAPE
+
+
+def test_seqpar_validation(lib):
+    out = ctypes.c_size_t(0)
+    f = lib.gdn_prefill_seqpar_workspace_size
+    assert f(1, 4096, 16, 128, 128, 8, 1, ctypes.byref(out)) == GDN_OK and out.value > 0
+    assert f(1, 4096, 16, 64, 64, 8, 1, ctypes.byref(out)) == GDN_ERR_UNSUPPORTED
+    assert f(1, 4096, 16, 128, 128, 0, 1, ctypes.byref(out)) == GDN_ERR_SHAPE
+    assert f(1, 4096, 16, 128, 128, 8, 0, ctypes.byref(out)) == GDN_ERR_UNSUPPORTED
+    assert f(1, 4096, 16, 128, 128, 8, 1, None) == GDN_ERR_NULL
+    sp = lib.gdn_prefill_seqpar
+    ws = ctypes.c_void_p(1 << 20)            # never dereferenced: rejected before launch
+    a = [P] * 5 + [None, None, P]
+    assert sp(*a, 1, 4096, 16, 16, 128, 128, 8, 1.0, 1, None, 0, None) == GDN_ERR_NULL
+    assert sp(*a, 1, 4096, 16, 16, 128, 128, 8, 1.0, 1, ws, 10, None) == GDN_ERR_WORKSPACE
+    assert sp(*a, 1, 4096, 16, 5, 128, 128, 8, 1.0, 1, ws, 1 << 40, None) == GDN_ERR_SHAPE
+    b = list(a)
+    b[7] = None                              # o
+    assert sp(*b, 1, 4096, 16, 16, 128, 128, 8, 1.0, 1, ws, 1 << 40, None) == GDN_ERR_NULL

@@ -548,3 +548,47 @@ def test_channel_gated_decode_continues_prefill(dtype):
     eo, es = o_err(torch.cat(outs, 1), o_ref), s_err(fin, s_ref)
     report(f"channel gated prefill + decode {dtype}", o=eo, state=es)
     assert eo <= _tol(c) and es <= _tol(c)
+
+
+# --- sequence-parallel prefill (segments of one sequence side by side) ---------------
+
+@pytest.mark.parametrize("segments,Hk", [(1, 3), (3, 3), (4, 1), (40, 3)])
+def test_seqpar_matches_oracle(segments, Hk):
+    """B=2 sequences of 1000 tokens (16 chunks, a ragged tail) cut into 1, 3,
+    4 or 40 segments (more segments than chunks: empty ones), non-zero initial
+    states, grouped heads."""
+    c = inputs.make_prefill(seed=91, B=2, T=1000, H=3, Hk=Hk, with_state=True)
+    fin = torch.empty((2, 3, 128, 128), dtype=torch.float32, device="cuda:0")
+    o, _ = gdn.gdn_prefill_seqpar(dev(c.q), dev(c.k), dev(c.v), dev(c.g), dev(c.beta), segments,
+                                  dev(c.s0), fin, scale=c.scale)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_prefill(c)
+    eo, es = o_err(o, o_ref), s_err(fin, s_ref)
+    report(f"seqpar segments={segments} Hk={Hk}", o=eo, state=es)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_seqpar_long_sequence_sampled():
+    """One sequence of 32768 tokens, H=16, 8 segments: every head against the
+    oracle on the final state and on the outputs of the last 2048 tokens plus
+    the first 2048 (the oracle runs the whole sequence)."""
+    c = inputs.make_prefill(seed=92, B=1, T=32768, H=16)
+    fin = torch.empty((1, 16, 128, 128), dtype=torch.float32, device="cuda:0")
+    o, _ = gdn.gdn_prefill_seqpar(dev(c.q), dev(c.k), dev(c.v), dev(c.g), dev(c.beta), 8,
+                                  None, fin, scale=c.scale)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_prefill(c)
+    oc = o.cpu()
+    eo = max(o_err(oc[:, :2048], o_ref[:, :2048]), o_err(oc[:, -2048:], o_ref[:, -2048:]))
+    es = s_err(fin, s_ref)
+    report("seqpar B1 H16 T32768 segments=8", o=eo, state=es)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_seqpar_zero_tokens_keeps_the_state():
+    c = inputs.make_prefill(seed=93, B=2, T=0, H=2, with_state=True)
+    fin = torch.full((2, 2, 128, 128), 7.0, dtype=torch.float32, device="cuda:0")
+    gdn.gdn_prefill_seqpar(dev(c.q), dev(c.k), dev(c.v), dev(c.g), dev(c.beta), 4, dev(c.s0),
+                           fin, scale=c.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(fin.cpu(), c.s0)
