@@ -566,13 +566,10 @@ hipError_t launch_prefill_chunk(const void *q, const void *k, const void *v, con
                                 const int32_t *cu, int T, int H, int Hk, int N, float scale,
                                 hipStream_t stream)
 {
-    static bool attr_done = false;
-    if (!attr_done) {
-        hipError_t e = hipFuncSetAttribute((const void *)prefill_chunk_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-        if (e != hipSuccess) return e;
-        attr_done = true;
-    }
+    // the dynamic LDS limit, raised once per process (thread-safe static)
+    static const hipError_t attr = hipFuncSetAttribute(
+        (const void *)prefill_chunk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    if (attr != hipSuccess) return attr;
     const int npairs = H * N;
     dim3 grid(pair_grid(npairs)), block(NT);
     hipLaunchKernelGGL(prefill_chunk_kernel, grid, block, LDS_BYTES, stream, (const bf16 *)q,

@@ -37,6 +37,7 @@
 // (bos_n / 64) + n + c, where bos_n is its first token: slots of different
 // sequences never collide and every slot is below
 // nslots = total_tokens / 64 + N + 1.
+#include <atomic>
 #include <type_traits>
 
 #include "chunk_common.h"
@@ -89,6 +90,7 @@ static_assert(P_LDS_BYTES <= 160 * 1024 / 3, "three prep workgroups per CU");
 // 64 x 64 tiles (T_w, T_u, P) keep rows 0-31 (read in columns 0-31 only) and
 // rows 32-63 as two tiles of different width.
 // ---------------------------------------------------------------------------
+constexpr int MAX_DEVICES = 64;               // per-device launch caches
 constexpr int DVT = 32;
 constexpr int NT = 512;
 // chain_kernel flags: V read as zero; initial state the identity (s_init
@@ -1050,21 +1052,25 @@ hipError_t launch_prefill_prepare(const void *q, const void *k, const float *g, 
     const long tokens = cu ? (long)T : (long)N * T;
     const long nslots = tokens / C + N + 1;
     if (tokens == 0) return hipSuccess;        // no chunk: nothing to prepare
-    // enough workgroups to fill every CU at the occupancy the kernel reaches,
-    // each looping over items
-    static int per_cu = 0, cus = 0;
-    if (per_cu == 0) {
-        int dev = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    // enough workgroups to fill every CU of the current device at the
+    // occupancy the kernel reaches, each looping over items (cached per
+    // device; concurrent first calls compute the same value)
+    static std::atomic<long> fill_of[MAX_DEVICES];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    long fill = dev < MAX_DEVICES ? fill_of[dev].load(std::memory_order_relaxed) : 0;
+    if (fill == 0) {
+        int cus = 0, per_cu = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e == hipSuccess)
             e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)chunk_prep_kernel,
                                                              P_NT, P_LDS_BYTES);
         if (e != hipSuccess) return e;
-        if (per_cu < 1) per_cu = 1;
+        fill = (long)(per_cu < 1 ? 1 : per_cu) * (cus < 1 ? 1 : cus);
+        if (dev < MAX_DEVICES) fill_of[dev].store(fill, std::memory_order_relaxed);
     }
     const long nitems = nslots * H;
-    const long fill = (long)per_cu * cus;
     dim3 grid((unsigned)(nitems < fill ? nitems : fill)), block(P_NT);
     hipLaunchKernelGGL(chunk_prep_kernel, grid, block, P_LDS_BYTES, stream, (const bf16 *)q,
                        (const bf16 *)k, g, beta, cu, (bf16 *)ws, T, H, Hk, N, (int)nslots);
@@ -1076,13 +1082,10 @@ hipError_t launch_prefill_apply(const void *q, const void *k, const void *v, con
                                 int T, int H, int Hk, int N, float scale, const void *ws,
                                 hipStream_t stream, int flags)
 {
-    static bool attr_done = false;
-    if (!attr_done) {
-        hipError_t e = hipFuncSetAttribute((const void *)chunk_chain_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-        if (e != hipSuccess) return e;
-        attr_done = true;
-    }
+    // the dynamic LDS limit, raised once per process (thread-safe static)
+    static const hipError_t attr = hipFuncSetAttribute(
+        (const void *)chunk_chain_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    if (attr != hipSuccess) return attr;
     const long tokens = cu ? (long)T : (long)N * T;
     const long nslots = tokens / C + N + 1;
     const int npairs = H * N;

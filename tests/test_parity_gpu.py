@@ -592,3 +592,45 @@ def test_seqpar_zero_tokens_keeps_the_state():
                            fin, scale=c.scale)
     torch.cuda.synchronize()
     assert torch.equal(fin.cpu(), c.s0)
+
+
+# --- value head sizes that are not a multiple of the row blocks ----------------------
+
+def _with_dv(c, dv):
+    """The case with v (and the state's rows) cut to the first dv channels."""
+    import dataclasses
+    return dataclasses.replace(c, v=c.v[..., :dv].contiguous(),
+                               s0=None if c.s0 is None else c.s0[:, :, :dv, :].contiguous())
+
+
+@pytest.mark.parametrize("dtype,dk,dv", [("bf16", 128, 100), ("f32", 128, 36), ("f32", 16, 7)])
+def test_decode_ragged_value_rows(dtype, dk, dv):
+    c = _with_dv(inputs.make_decode(seed=95, B=3, H=4, Hk=2, d=dk, dtype=dtype), dv)
+    st = dev(c.s0)
+    o = gdn.gdn_decode_step(dev(c.q[:, 0]), dev(c.k[:, 0]), dev(c.v[:, 0]), dev(c.g[:, 0]),
+                            dev(c.beta[:, 0]), st, scale=c.scale)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_prefill(c)
+    eo, es = o_err(o[:, None], o_ref), s_err(st, s_ref)
+    report(f"decode d_k={dk} d_v={dv} {dtype}", o=eo, state=es)
+    assert eo <= _tol(c) and es <= _tol(c)
+
+
+@pytest.mark.parametrize("dtype,dk,dv", [("bf16", 128, 100), ("f32", 64, 48), ("f32", 32, 5)])
+def test_prefill_ragged_value_rows(dtype, dk, dv):
+    """Token-serial path (d_v < 128 leaves the MFMA kernels) with a partial
+    last row block, packed sequences and initial states."""
+    c = _with_dv(inputs.make_varlen(seed=96, H=2, d=dk, dtype=dtype, lengths=[33, 0, 100]), dv)
+    o, fin = run_prefill(c)
+    o_ref, s_ref = oracle_prefill(c)
+    cu = [int(x) for x in c.cu_seqlens.tolist()]
+    eo, es = o_err_packed(o, o_ref, cu), s_err(fin, s_ref)
+    report(f"prefill d_k={dk} d_v={dv} {dtype}", o=eo, state=es)
+    assert eo <= _tol(c) and es <= _tol(c)
+
+
+def test_channel_gated_ragged_value_rows():
+    c = _with_dv(inputs.make_channel_gated(seed=97, B=2, T=70, H=2, d=64, dtype="f32"), 40)
+    o, fin = run_prefill(c, entry=gdn.gdn_prefill_channel_gated)
+    o_ref, s_ref = oracle.gdn_recurrent_channel(c.q, c.k, c.v, c.g, c.beta, c.s0, None, c.scale)
+    assert o_err(o, o_ref) <= TOL_F32 and s_err(fin, s_ref) <= TOL_F32
