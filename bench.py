@@ -112,7 +112,13 @@ def event_time(fn, steps, warmup):
 
 
 def _src_hash(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """Hash of the kernel source's code: comments and blank space are dropped,
+    so that an edit of the comments keeps the recorded counters valid."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def measured_traffic(kernel):

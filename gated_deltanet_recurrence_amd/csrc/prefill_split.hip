@@ -133,6 +133,14 @@ static_assert(SZ_BUF % 16 == 0 && SZ_P % 16 == 0, "16-byte aligned tiles");
 // in the k-step. swz gives the element XOR for a lane whose row is
 // (multiple of 16) + lane%16.
 __device__ __forceinline__ int swz(int lane) { return ((lane & 15) >> 2) << 3; }
+// The bf16 copies of S (row stride LD_R) and Delta^T (LD_L) that the recurrence
+// waves pass to the output waves are read 16 rows at a time in the order
+// 8 (i/4) + 4 u + i%4 (i = 0..15, u = 0 or 1), and both strides repeat the bank
+// pattern every 8 rows; XOR-ing each row's 16-byte chunk index by these
+// functions of its row bits 3 and 4 puts the 16 rows of a read on distinct
+// banks (32 or 64 four-byte banks alike). Element XORs, by d_v row r < 32.
+__device__ __forceinline__ int swS(int r) { return (((r >> 3) & 1) << 3) | (((r >> 4) & 1) << 6); }
+__device__ __forceinline__ int swD(int r) { return ((r >> 3) & 3) << 3; }
 __device__ __forceinline__ bf16x8 lds8(const bf16 *base, int off) {
     return *reinterpret_cast<const bf16x8 *>(base + off);
 }
@@ -590,10 +598,13 @@ chunk_prep_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 // operands are read in the matching order (K rows for X chosen per lane,
 // K^T for the update transposed on read). Grouping T_w K S^T as T_w (K S^T)
 // means W = T_w K is never formed.
-// Waves 2 and 3 form the output for the same column halves,
+// Waves 2 and 3 form the output, wave 2 for tokens 0-31 of the chunk and
+// wave 3 for tokens 32-63, each over all 32 columns of the tile:
 // O^T = (S Q^T) diag(e^gamma) + Delta^T P^T, the second term one chunk later,
-// with P = lower_incl_diag(Q K^T * Gamma) from the prep pass. Waves 4-7 stage
-// the next chunk; waves 4 and 5 also stage P.
+// with P = lower_incl_diag(Q K^T * Gamma) from the prep pass; the rows of S and
+// Delta^T are taken in an order that leaves 8 consecutive d_v of one token in
+// each lane, stored as 16 bytes. Waves 4-7 stage the next chunk; waves 4 and 5
+// also stage P.
 //
 // Iteration c (buffers b = c % 2):
 //   waves 0-1  recurrence step of chunk c: reads staging b, writes Delta^T
@@ -674,7 +685,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
         for (int d = 0; d < 8; ++d) {
             bf16x4 x = {(bf16)Sacc[d][0], (bf16)Sacc[d][1], (bf16)Sacc[d][2], (bf16)Sacc[d][3]};
-            *reinterpret_cast<bf16x4 *>(cpS(0) + (16 * wave + m) * LD_R + ((32 * (d >> 1) + 8 * qq + 4 * (d & 1)) ^ swz(lane0))) = x;
+            *reinterpret_cast<bf16x4 *>(cpS(0) + (16 * wave + m) * LD_R + ((32 * (d >> 1) + 8 * qq + 4 * (d & 1)) ^ swS(16 * wave + m))) = x;
         }
     }
 
@@ -808,10 +819,19 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                                  : lds8(sTL, (32 * u + 16 * (t - 2) + m) * LD_L + 32 * s2 + 8 * qq);
                 };
                 const float *sEg = stSc(b) + C, *sDend = stSc(b) + 2 * C;
+                // Every LDS operand of the chunk is read before it is needed, so
+                // that no LDS round trip sits between two dependent products:
+                // the gates, K, V, T_u and -T_w first; K^T once X's products
+                // have been issued (into K's registers).
+                f32x4 dend[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) dend[t] = *reinterpret_cast<const f32x4 *>(sDend + 16 * t + 4 * qq);
+                const float eend = sEg[C - 1];
                 // U = T_u V and X = K S^T
                 f32x4 dacc[4], xacc[4];
 #pragma unroll
                 for (int t = 0; t < 4; ++t) { dacc[t] = f32x4{0.f, 0.f, 0.f, 0.f}; xacc[t] = dacc[t]; }
+                bf16x8 fw[4][2];
                 {
                     // X tile t takes K rows 32 (t/2) + 8 (m/4) + 4 (t%2) + m%4, so that its
                     // accumulator pairs run over tokens 32 s + 8 q + 0..7 contiguously
@@ -834,6 +854,11 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
                         for (int s2 = 0; s2 < 2; ++s2)
                             if (s2 <= (t >> 1)) fu[t][s2] = tfrag(1, t, s2);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+#pragma unroll
+                        for (int s2 = 0; s2 < 2; ++s2)
+                            if (s2 <= (t >> 1)) fw[t][s2] = tfrag(0, t, s2);
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int s2 = 0; s2 < 4; ++s2)
@@ -844,18 +869,29 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
                         for (int s2 = 0; s2 < 2; ++s2)
                             if (s2 <= (t >> 1)) dacc[t] = mfma16(fu[t][s2], fv[s2], dacc[t]);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
+                // K^T as the A operand of the state update: tile d, lane m takes d_k
+                // column 32 (d/2) + 8 (m/4) + 4 (d%2) + m%4 (the state's row order)
+                // and tokens 32 s + 4 q + 0..3, 32 s + 16 + 4 q + 0..3 (Delta~'s row
+                // order), transposed on read
+                // (the wait retires the reads above, -T_w's included, so that
+                // Delta's products wait for none of these)
+                __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+                bf16x8 fkt[8][2];
+#pragma unroll
+                for (int d = 0; d < 8; ++d)
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        const int c0 = 32 * (d >> 1) + 4 * (d & 1) + 8 * (m & 3);
+                        const int r0 = 32 * s2 + 4 * qq + (m >> 2);
+                        fkt[d][s2] = cat4(tr4(sK, r0 * LD_R + c0), tr4(sK, (r0 + 16) * LD_R + c0));
+                    }
+                __builtin_amdgcn_sched_barrier(0);
                 // Delta = U + (-T_w) X
                 {
-                    bf16x8 fw[4][2];
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-#pragma unroll
-                        for (int s2 = 0; s2 < 2; ++s2)
-                            if (s2 <= (t >> 1)) fw[t][s2] = tfrag(0, t, s2);
                     const bf16x8 xb0 = acc_pair_bf16(xacc[0], xacc[1]);
                     const bf16x8 xb1 = acc_pair_bf16(xacc[2], xacc[3]);
-                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
                         dacc[t] = mfma16(fw[t][0], xb0, dacc[t]);
@@ -866,38 +902,22 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                 bf16x8 db[2];
                 {
                     bf16 *sDt = cpDt(b);
-                    f32x4 dend[4];
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
-                        dend[t] = *reinterpret_cast<const f32x4 *>(sDend + 16 * t + 4 * qq);
                         bf16x4 x = {(bf16)dacc[t][0], (bf16)dacc[t][1], (bf16)dacc[t][2], (bf16)dacc[t][3]};
-                        *reinterpret_cast<bf16x4 *>(sDt + (16 * hv + m) * LD_L + ((16 * t + 4 * qq) ^ swz(lane))) = x;
+                        *reinterpret_cast<bf16x4 *>(sDt + (16 * hv + m) * LD_L + ((16 * t + 4 * qq) ^ swD(16 * hv + m))) = x;
                     }
                     db[0] = acc_pair_bf16(dacc[0] * dend[0], dacc[1] * dend[1]);
                     db[1] = acc_pair_bf16(dacc[2] * dend[2], dacc[3] * dend[3]);
                 }
-                // S^T <- e^{gamma_63} S^T + K^T Delta~. A operand of tile d: lane m
-                // takes d_k column 32 (d/2) + 8 (m/4) + 4 (d%2) + m%4 (the state's
-                // row order) and tokens 32 s + 4 q + 0..3, 32 s + 16 + 4 q + 0..3
-                // (Delta~'s row order), transposed on read
-                {
-                    const float eend = sEg[C - 1];
-                    bf16x8 fkt[8][2];
+                // S^T <- e^{gamma_63} S^T + K^T Delta~ (the decay while Delta is formed)
 #pragma unroll
-                    for (int d = 0; d < 8; ++d)
+                for (int d = 0; d < 8; ++d) Sacc[d] = Sacc[d] * eend;
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                        for (int s2 = 0; s2 < 2; ++s2) {
-                            const int c0 = 32 * (d >> 1) + 4 * (d & 1) + 8 * (m & 3);
-                            const int r0 = 32 * s2 + 4 * qq + (m >> 2);
-                            fkt[d][s2] = cat4(tr4(sK, r0 * LD_R + c0), tr4(sK, (r0 + 16) * LD_R + c0));
-                        }
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int d = 0; d < 8; ++d) {
-                        Sacc[d] = Sacc[d] * eend;
-                        Sacc[d] = mfma16(fkt[d][0], db[0], Sacc[d]);
-                        Sacc[d] = mfma16(fkt[d][1], db[1], Sacc[d]);
-                    }
+                for (int d = 0; d < 8; ++d) {
+                    Sacc[d] = mfma16(fkt[d][0], db[0], Sacc[d]);
+                    Sacc[d] = mfma16(fkt[d][1], db[1], Sacc[d]);
                 }
 #pragma unroll
                 for (int s2 = 0; s2 < 4; ++s2) Sb[s2] = acc_pair_bf16(Sacc[2 * s2], Sacc[2 * s2 + 1]);
@@ -905,78 +925,106 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
                 for (int d = 0; d < 8; ++d) {
                     bf16x4 x = {(bf16)Sacc[d][0], (bf16)Sacc[d][1], (bf16)Sacc[d][2], (bf16)Sacc[d][3]};
-                    *reinterpret_cast<bf16x4 *>(sSn + (16 * hv + m) * LD_R + ((32 * (d >> 1) + 8 * qq + 4 * (d & 1)) ^ swz(lane))) = x;
+                    *reinterpret_cast<bf16x4 *>(sSn + (16 * hv + m) * LD_R + ((32 * (d >> 1) + 8 * qq + 4 * (d & 1)) ^ swS(16 * hv + m))) = x;
                 }
             }
             lds_barrier();
         }
     } else if (wave < 4) {
-        // ============ waves 2-3: the output for d_v rows 16 hv .. ============
-        const int hv = wave - 2;
-        f32x4 oacc[2][4];                  // by chunk parity: O^T tiles (16 d_v x 16 tokens)
-        for (int ch0 = -3; ch0 <= nchunks; ch0 += 2)
+        // ============ waves 2-3: the output for tokens 32 hw .. 32 hw + 31 ============
+        // Per token tile two O^T tiles, over the d_v rows 8 (i/4) + 4 u + i%4 of
+        // tile row i (u = 0, 1): a lane's accumulators then hold d_v 8 q .. 8 q + 7
+        // of one token, stored as 16 contiguous bytes (64 per token row and
+        // instruction), and the wave reads Q only for its own tokens.
+        auto oloop = [&](auto HW) {
+            constexpr int hw = decltype(HW)::value;
+            constexpr int NS = hw + 1;         // key blocks of 32 that tokens 32 hw .. need
+            f32x4 oacc[2][2][2];               // [chunk parity][u][token tile 2 hw + tt]
+            for (int ch0 = -3; ch0 <= nchunks; ch0 += 2)
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const int ch = ch0 + hf;
-            const int b = 1 - hf;              // ch % 2; (ch + 1) % 2 = (ch - 1) % 2 = hf
-            int tidl = tid0;
-            asm volatile("" : "+v"(tidl));
-            const int lane = tidl & 63, m = lane & 15, qq = lane >> 4;
-            if (o && ch >= 0 && ch < nchunks) {   // o == NULL: the states only
-                // (Q S^T)^T = S Q^T, all 64 tokens, then e^gamma per token
-                const bf16 *sSc = cpS(b), *sQ = stQ(b);
-                const float *sEg = stSc(b) + C;
-                bf16x8 fs[4], fq[4][4];
+            for (int hf = 0; hf < 2; ++hf) {
+                const int ch = ch0 + hf;
+                const int b = 1 - hf;          // ch % 2; (ch + 1) % 2 = (ch - 1) % 2 = hf
+                int tidl = tid0;
+                asm volatile("" : "+v"(tidl));
+                const int lane = tidl & 63, m = lane & 15, qq = lane >> 4;
+                const int r0 = 8 * (m >> 2) + (m & 3);     // d_v row of tile row m, u = 0
+                if (o && ch >= 0 && ch < nchunks) {   // o == NULL: the states only
+                    // (Q S^T)^T = S Q^T for the wave's 32 tokens, then e^gamma per token
+                    const bf16 *sSc = cpS(b), *sQ = stQ(b);
+                    const float *sEg = stSc(b) + C;
+                    bf16x8 fs[2][4], fq[2][4];
 #pragma unroll
-                for (int s2 = 0; s2 < 4; ++s2) {
-                    fs[s2] = lds8(sSc, (16 * hv + m) * LD_R + ((32 * s2 + 8 * qq) ^ swz(lane)));
+                    for (int s2 = 0; s2 < 4; ++s2) {
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) fq[t][s2] = lds8(sQ, (16 * t + m) * LD_R + 32 * s2 + 8 * qq);
-                }
-                __builtin_amdgcn_sched_barrier(0);
+                        for (int u = 0; u < 2; ++u)
+                            fs[u][s2] = lds8(sSc, (r0 + 4 * u) * LD_R + ((32 * s2 + 8 * qq) ^ swS(r0 + 4 * u)));
 #pragma unroll
-                for (int t = 0; t < 4; ++t) oacc[b][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        for (int tt = 0; tt < 2; ++tt)
+                            fq[tt][s2] = lds8(sQ, (16 * (2 * hw + tt) + m) * LD_R + 32 * s2 + 8 * qq);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int s2 = 0; s2 < 4; ++s2)
+                    for (int u = 0; u < 2; ++u)
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) oacc[b][t] = mfma16(fs[s2], fq[t][s2], oacc[b][t]);
+                        for (int tt = 0; tt < 2; ++tt) oacc[b][u][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int t = 0; t < 4; ++t) oacc[b][t] = oacc[b][t] * sEg[16 * t + m];
-            }
-            if (o && ch >= 1 && ch <= nchunks) {
-                // finish chunk ch - 1: O^T += Delta^T P^T (token tile t needs keys
-                // 0 .. 16 t + 15), then its rows to HBM
-                const int cp = ch - 1;
-                const bf16 *sDt = cpDt(hf), *sP = cpP(hf);
-                bf16x8 fd[2], fp[4][2];
+                    for (int s2 = 0; s2 < 4; ++s2)
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    fd[s2] = lds8(sDt, (16 * hv + m) * LD_L + ((32 * s2 + 8 * qq) ^ swz(lane)));
+                        for (int u = 0; u < 2; ++u)
 #pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        if (s2 <= (t >> 1))
-                            fp[t][s2] = t < 2 ? lds8(sP, (16 * t + m) * LD_H + ((8 * qq) ^ swz(lane)))
-                                              : lds8(sP + SZ_PH / 2, (16 * (t - 2) + m) * LD_L + ((32 * s2 + 8 * qq) ^ swz(lane)));
-                }
-                __builtin_amdgcn_sched_barrier(0);
+                            for (int tt = 0; tt < 2; ++tt)
+                                oacc[b][u][tt] = mfma16(fs[u][s2], fq[tt][s2], oacc[b][u][tt]);
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
+                    for (int tt = 0; tt < 2; ++tt) {
+                        const float e = sEg[16 * (2 * hw + tt) + m];
 #pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2)
-                        if (s2 <= (t >> 1)) oacc[hf][t] = mfma16(fd[s2], fp[t][s2], oacc[hf][t]);
-                // oacc[t][r] = O[token 16 t + m][d_v 16 hv + 4 qq + r]: 8 bytes per lane
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int tok = cp * C + 16 * t + m;
-                    if (tok < len) {
-                        bf16x4 x = {(bf16)(scale * oacc[hf][t][0]), (bf16)(scale * oacc[hf][t][1]),
-                                    (bf16)(scale * oacc[hf][t][2]), (bf16)(scale * oacc[hf][t][3])};
-                        *reinterpret_cast<bf16x4 *>(o + ((size_t)bos + tok) * H * DV + (size_t)h * DV + cbase + 16 * hv + 4 * qq) = x;
+                        for (int u = 0; u < 2; ++u) oacc[b][u][tt] = oacc[b][u][tt] * e;
                     }
                 }
+                if (o && ch >= 1 && ch <= nchunks) {
+                    // finish chunk ch - 1: O^T += Delta^T P^T (token tile t needs keys
+                    // 0 .. 16 t + 15), then its rows to HBM
+                    const int cp = ch - 1;
+                    const bf16 *sDt = cpDt(hf), *sP = cpP(hf);
+                    bf16x8 fd[2][NS], fp[2][NS];
+#pragma unroll
+                    for (int s2 = 0; s2 < NS; ++s2) {
+#pragma unroll
+                        for (int u = 0; u < 2; ++u)
+                            fd[u][s2] = lds8(sDt, (r0 + 4 * u) * LD_L + ((32 * s2 + 8 * qq) ^ swD(r0 + 4 * u)));
+#pragma unroll
+                        for (int tt = 0; tt < 2; ++tt) {
+                            const int t = 2 * hw + tt;
+                            fp[tt][s2] = t < 2 ? lds8(sP, (16 * t + m) * LD_H + ((8 * qq) ^ swz(lane)))
+                                               : lds8(sP + SZ_PH / 2, (16 * (t - 2) + m) * LD_L + ((32 * s2 + 8 * qq) ^ swz(lane)));
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int s2 = 0; s2 < NS; ++s2)
+#pragma unroll
+                        for (int u = 0; u < 2; ++u)
+#pragma unroll
+                            for (int tt = 0; tt < 2; ++tt)
+                                oacc[hf][u][tt] = mfma16(fd[u][s2], fp[tt][s2], oacc[hf][u][tt]);
+                    // oacc[u][tt][r] = O[token 16 (2 hw + tt) + m][d_v 8 qq + 4 u + r]
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt) {
+                        const int tok = cp * C + 16 * (2 * hw + tt) + m;
+                        if (tok < len) {
+                            const f32x4 a = oacc[hf][0][tt], c = oacc[hf][1][tt];
+                            const bf16x8 x = {(bf16)(scale * a[0]), (bf16)(scale * a[1]), (bf16)(scale * a[2]), (bf16)(scale * a[3]),
+                                              (bf16)(scale * c[0]), (bf16)(scale * c[1]), (bf16)(scale * c[2]), (bf16)(scale * c[3])};
+                            *reinterpret_cast<bf16x8 *>(o + ((size_t)bos + tok) * H * DV + (size_t)h * DV + cbase + 8 * qq) = x;
+                        }
+                    }
+                }
+                lds_barrier();
             }
-            lds_barrier();
-        }
+        };
+        if (wave == 2) oloop(std::integral_constant<int, 0>{});
+        else oloop(std::integral_constant<int, 1>{});
     } else {
         // ============ waves 4-7: staging; waves 4-5 also stage P ============
         // P pieces 192 (wave - 4) + 64 r + lane (r < 3) of the workspace item,
