@@ -121,17 +121,47 @@ prologue_conv_kernel(const TIO *__restrict__ x_q, const TIO *__restrict__ x_k,
     seq_bounds(cu, N, T, t0, start, end, n);
 
     auto row = [&](long t) { return ((size_t)t * Ht + h) * D + c; };
-    float x1[8], x2[8], x3[8];                    // inputs at t-1, t-2, t-3
+    // the three inputs before the tile (taken as zero before the sequence
+    // start), then the tile's inputs: all requested, without branches (rows
+    // out of range are read at a valid row and not used), before any is used
+    Raw8<TIO> hr[3];
+    bool hok[3];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) { x1[e] = 0.f; x2[e] = 0.f; x3[e] = 0.f; }
-    if (t0 - 1 >= start) load8(x + row(t0 - 1), x1);
-    if (t0 - 2 >= start) load8(x + row(t0 - 2), x2);
-    if (t0 - 3 >= start) load8(x + row(t0 - 3), x3);
+    for (int j = 0; j < 3; ++j) {
+        hok[j] = t0 - 1 - j >= start;
+        hr[j].load(x + row(hok[j] ? t0 - 1 - j : t0));
+    }
+    Raw8<TIO> xr[PRO_TT];
+#pragma unroll
+    for (int i = 0; i < PRO_TT; ++i) xr[i].load(x + row(t0 + i < t1 ? t0 + i : t1 - 1));
 
-    Raw8<TIO> xr[PRO_TT];                         // the tile's inputs, requested up front
+    if (which == 2) {
+        // the gates of the tile's (token, value head) pairs, spread over the
+        // threads of the lane groups that have a head (the first nh groups),
+        // their loads issued together behind the tile's
+        const int hb = (int)blockIdx.y * GPB;
+        const int nh = H - hb < GPB ? H - hb : GPB;
+        for (int e = (int)threadIdx.x; e < PRO_TT * nh; e += nh * G) {
+            const long t = t0 + e / nh;
+            const int hh = hb + e % nh;
+            if (t < t1) {
+                const size_t i = (size_t)t * H + hh;
+                const float bias = dt_bias ? dt_bias[hh] : 0.f;
+                g[i] = -A[hh] * softplus_f32(to_f32(a[i]) + bias);
+                beta[i] = 1.0f / (1.0f + expf(-to_f32(b[i])));
+            }
+        }
+    }
+    float x1[8], x2[8], x3[8];                    // inputs at t-1, t-2, t-3
+    hr[0].get(x1);
+    hr[1].get(x2);
+    hr[2].get(x3);
 #pragma unroll
-    for (int i = 0; i < PRO_TT; ++i)
-        if (t0 + i < t1) xr[i].load(x + row(t0 + i));
+    for (int e = 0; e < 8; ++e) {
+        x1[e] = hok[0] ? x1[e] : 0.f;
+        x2[e] = hok[1] ? x2[e] : 0.f;
+        x3[e] = hok[2] ? x3[e] : 0.f;
+    }
 
 #pragma unroll
     for (int i = 0; i < PRO_TT; ++i) {
@@ -162,12 +192,6 @@ prologue_conv_kernel(const TIO *__restrict__ x_q, const TIO *__restrict__ x_k,
             for (int e = 0; e < 8; ++e) out[e] *= inv;
         }
         store8(y + row(t), out);
-        if (which == 2 && lr == 0) {              // gates, once per (token, value head)
-            const size_t i = (size_t)t * H + h;
-            const float bias = dt_bias ? dt_bias[h] : 0.f;
-            g[i] = -A[h] * softplus_f32(to_f32(a[i]) + bias);
-            beta[i] = 1.0f / (1.0f + expf(-to_f32(b[i])));
-        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) { x3[e] = x2[e]; x2[e] = x1[e]; x1[e] = xt[e]; }
     }
