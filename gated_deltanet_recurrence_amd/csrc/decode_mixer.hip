@@ -78,6 +78,17 @@ decode_mixer_kernel(const TIO *__restrict__ q_raw, const TIO *__restrict__ k_raw
         }
     }
 
+    // this thread's first output gate z and norm weight, requested with the
+    // state so that the epilogue does not wait for memory
+    const int oc = tid - (tid / d_v) * d_v;
+    const size_t oi0 = ((size_t)bb * H + h0) * d_v + tid;
+    TIO zraw{};
+    float wpre = 1.0f;
+    if (tid < R) {
+        zraw = z[oi0];
+        if (norm_w) wpre = norm_w[oc];
+    }
+
     extern __shared__ __attribute__((aligned(16))) float sm[];
     float *sq = sm;                            // conv + SiLU outputs: q [DK], k [DK], v [R]
     float *sk = sq + DK;
@@ -201,8 +212,10 @@ decode_mixer_kernel(const TIO *__restrict__ q_raw, const TIO *__restrict__ k_raw
         const int j = i / d_v, c = i - j * d_v;
         const size_t oi = ((size_t)bb * H + h0) * d_v + i;
         const float inv = rsqrt_f32(sss[j] * (1.0f / d_v) + eps);
-        const float wv = norm_w ? norm_w[c] : 1.0f;
-        out[oi] = from_f32<TIO>(wv * (sy[i] * inv) * silu_f32(to_f32(z[oi])));
+        const bool first = i == tid;
+        const float wv = first ? wpre : (norm_w ? norm_w[c] : 1.0f);
+        const float zv = to_f32(first ? zraw : z[oi]);
+        out[oi] = from_f32<TIO>(wv * (sy[i] * inv) * silu_f32(zv));
     }
 }
 
