@@ -22,8 +22,9 @@
 //
 // Work mapping: grid (row blocks, H, N). A state row (d_k floats) lives in
 // the registers of G = d_k/8 lanes for the whole sequence; rows never
-// exchange data. Per token each lane group needs three length-d_k dot
-// products (S.k, S.q, k.q), reduced with DPP. Tokens are staged through LDS
+// exchange data. Per token each lane group needs two length-d_k dot
+// products, reduced with DPP: S.k on the decayed row before the write and
+// S.q on the updated row. Tokens are staged through LDS
 // in blocks of TB: the workgroup's 256 threads fetch a block's q, k, g and
 // beta with 16-byte loads (once per workgroup, not once per lane group) and
 // its rows of v, one block ahead in registers, so the memory latency is paid
@@ -212,7 +213,10 @@ prefill_recurrent_kernel(const TIO *__restrict__ q, const TIO *__restrict__ k,
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 if (j0 + u >= nt) break;        // uniform
-                float delta, sq_ = 0.f, kq = 0.f;
+                // retrieve at k, write the gated error along k, then read the
+                // updated row with q (two reductions per token; the read is off
+                // the next token's dependency chain)
+                float sk_ = 0.f;
                 if constexpr (PERCH) {
                     // decay each column first (the block holds exp(g)), then read
                     // the decayed row
@@ -221,17 +225,10 @@ prefill_recurrent_kernel(const TIO *__restrict__ q, const TIO *__restrict__ k,
                         s0[e] *= g0[u][e];
                         s1[e] *= g1[u][e];
                     }
-                    float sk_ = 0.f;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        sk_ += s0[e] * k0[u][e] + s1[e] * k1[u][e];
-                        sq_ += s0[e] * q0[u][e] + s1[e] * q1[u][e];
-                        kq += k0[u][e] * q0[u][e] + k1[u][e] * q1[u][e];
-                    }
+                    for (int e = 0; e < 4; ++e) sk_ += s0[e] * k0[u][e] + s1[e] * k1[u][e];
                     sk_ = group_sum<G>(sk_);
-                    sq_ = group_sum<G>(sq_);
-                    kq = group_sum<G>(kq);
-                    delta = bb[u] * (vv[u] - sk_);
+                    const float delta = bb[u] * (vv[u] - sk_);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         s0[e] += delta * k0[u][e];
@@ -239,27 +236,22 @@ prefill_recurrent_kernel(const TIO *__restrict__ q, const TIO *__restrict__ k,
                     }
                 } else {
                     const float alpha = __expf(ga[u]);
-                    float sk_ = 0.f;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        sk_ += s0[e] * k0[u][e] + s1[e] * k1[u][e];
-                        sq_ += s0[e] * q0[u][e] + s1[e] * q1[u][e];
-                        kq += k0[u][e] * q0[u][e] + k1[u][e] * q1[u][e];
-                    }
+                    for (int e = 0; e < 4; ++e) sk_ += s0[e] * k0[u][e] + s1[e] * k1[u][e];
                     sk_ = group_sum<G>(sk_);
-                    sq_ = group_sum<G>(sq_);
-                    kq = group_sum<G>(kq);
-                    delta = bb[u] * (vv[u] - alpha * sk_);
-                    sq_ *= alpha;
+                    const float delta = bb[u] * (vv[u] - alpha * sk_);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         s0[e] = alpha * s0[e] + delta * k0[u][e];
                         s1[e] = alpha * s1[e] + delta * k1[u][e];
                     }
                 }
+                float sq_ = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sq_ += s0[e] * q0[u][e] + s1[e] * q1[u][e];
+                sq_ = group_sum<G>(sq_);
                 if (active && lr == 0)
-                    o[((size_t)(t0 + j0 + u) * H + h) * d_v + row] =
-                        from_f32<TIO>(scale * (sq_ + delta * kq));
+                    o[((size_t)(t0 + j0 + u) * H + h) * d_v + row] = from_f32<TIO>(scale * sq_);
             }
         }
         if (blk + 1 < nblocks) stage((blk + 1) & 1);
