@@ -210,6 +210,143 @@ __device__ __forceinline__ f32x16 mma32s(f32x16 acc, const bf16 *a, int ld_a, in
 
 using namespace split;
 
+// The triangular solve and the stores of one (chunk, head) item, shared by the
+// prep passes: with A = -strict_lower(...) given as its four diagonal 16 x 16
+// blocks (sY, row-major, P_DB floats apart) and rows 16-63, columns 0-47
+// (sA, row stride P_LD_A2), T = (I - A)^-1 is formed in sT (row stride
+// P_LD_A) and written to the workspace item dst as 16-byte bf16 pieces,
+// -T_w = T diag(colw) and T_u = T diag(colu) (colw = -beta e^gamma for a
+// scalar gate). All four waves of the workgroup call it.
+__device__ __forceinline__ void solve_store(const float *sA, const float *sY, float *sT,
+                                            const float *colw, const float *colu, bf16 *dst,
+                                            int tid, int wave)
+{
+    const int lane = tid & 63;
+    const int lr = lane & 15, lq = lane >> 4;
+    auto blkA = [&](int I, int J) { return sA + (16 * (I - 1)) * P_LD_A2 + 16 * J; };
+    auto blkT = [&](int I, int J) { return sT + (16 * I) * P_LD_A + 16 * J; };
+    auto store_T = [&](int I, int J, f32x4 acc) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sT[(16 * I + 4 * lq + r) * P_LD_A + 16 * J + lr] = acc[r];
+    };
+
+    if (wave == 0) {
+        // ---- diagonal blocks, one per 16 lanes: lane 16 b + c computes
+        //      column c of D_b = (I - A_bb)^-1 row by row,
+        //      D[i][c] = [i == c] + sum_{m < i} A[i][m] D[m][c]
+        //      (the block's row i read by all 16 lanes: an LDS broadcast);
+        //      row i + 1 is loaded while row i is summed ----
+        const int bb = lane >> 4, c = lane & 15;
+        const float *Ab = sY + bb * P_DB;
+        float D[16];
+        f32x4 rowv[2][4];
+        auto load_row = [&](int i, f32x4 (&dstv)[4]) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                if (4 * t < i) dstv[t] = *reinterpret_cast<const f32x4 *>(Ab + i * 16 + 4 * t);
+        };
+        load_row(1, rowv[1]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (i + 1 < 16) load_row(i + 1, rowv[(i + 1) & 1]);
+            float acc = i == c ? 1.f : 0.f;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (4 * t + e < i) acc += rowv[i & 1][t][e] * D[4 * t + e];
+            D[i] = acc;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sT[(16 * bb + i) * P_LD_A + 16 * bb + c] = D[i];
+    } else if (wave == 1) {
+        // the 16 x 16 blocks (0,1) and (2,3) of T are zero; the output reads them
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int e = lane + 64 * u;   // 128 four-float pieces
+            const int blk = e >> 6, row = (e >> 2) & 15, c4 = 4 * (e & 3);
+            *reinterpret_cast<f32x4 *>(sT + (32 * blk + row) * P_LD_A + 32 * blk + 16 + c4) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    lds_barrier();
+
+    // ---- off-diagonal blocks of T. With D_b the diagonal inverses:
+    //   T10 = D1 A10 D0,  T32 = D3 A32 D2,  T21 = D2 A21 D1           (16-level)
+    //   T20 = D2 (A20 D0 + A21 T10)
+    //   T31 = T32 (A21 D1) + D3 (A31 D1)
+    //   T30 = T32 (A20 D0 + A21 T10) + D3 (A30 D0 + A31 T10)          (32-level)
+    {
+        const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+        f32x4 h0 = z4, h1 = z4;
+        if (wave == 0) {
+            const f32x4 c10 = mm16(z4, blkA(1, 0), P_LD_A2, blkT(0, 0), P_LD_A, lane);
+            h0 = mm16(z4, blkA(2, 0), P_LD_A2, blkT(0, 0), P_LD_A, lane);              // A20 D0
+            store_T(1, 0, mm16_rb(z4, blkT(1, 1), P_LD_A, acc_to_bop(c10), lane));
+        } else if (wave == 1) {
+            const f32x4 c32 = mm16(z4, blkA(3, 2), P_LD_A2, blkT(2, 2), P_LD_A, lane);
+            store_T(3, 2, mm16_rb(z4, blkT(3, 3), P_LD_A, acc_to_bop(c32), lane));
+        } else if (wave == 2) {
+            h0 = mm16(z4, blkA(2, 1), P_LD_A2, blkT(1, 1), P_LD_A, lane);              // A21 D1
+            h1 = mm16(z4, blkA(3, 1), P_LD_A2, blkT(1, 1), P_LD_A, lane);              // A31 D1
+            store_T(2, 1, mm16_rb(z4, blkT(2, 2), P_LD_A, acc_to_bop(h0), lane));
+        } else {
+            h0 = mm16(z4, blkA(2, 0), P_LD_A2, blkT(0, 0), P_LD_A, lane);              // A20 D0
+            h1 = mm16(z4, blkA(3, 0), P_LD_A2, blkT(0, 0), P_LD_A, lane);              // A30 D0
+        }
+        lds_barrier();
+        if (wave == 0) {
+            const f32x4 y00 = mm16(h0, blkA(2, 1), P_LD_A2, blkT(1, 0), P_LD_A, lane);
+            store_T(2, 0, mm16_rb(z4, blkT(2, 2), P_LD_A, acc_to_bop(y00), lane));
+        } else if (wave == 2) {
+            const f32x4 t = mm16_rb(z4, blkT(3, 2), P_LD_A, acc_to_bop(h0), lane);
+            store_T(3, 1, mm16_rb(t, blkT(3, 3), P_LD_A, acc_to_bop(h1), lane));
+        } else if (wave == 3) {
+            const f32x4 y00 = mm16(h0, blkA(2, 1), P_LD_A2, blkT(1, 0), P_LD_A, lane);
+            const f32x4 y10 = mm16(h1, blkA(3, 1), P_LD_A2, blkT(1, 0), P_LD_A, lane);
+            const f32x4 t = mm16_rb(z4, blkT(3, 2), P_LD_A, acc_to_bop(y00), lane);
+            store_T(3, 0, mm16_rb(t, blkT(3, 3), P_LD_A, acc_to_bop(y10), lane));
+        }
+        lds_barrier();
+    }
+
+    // ---- -T diag(beta e^gamma) and T diag(beta) -> workspace as 16-byte
+    //      pieces (bf16), consecutive per thread. Piece order:
+    //        0..255     rows 32-63 of -T_w (8 per row)
+    //        256..511   rows 32-63 of T_u
+    //        512..639   rows 0-31 of -T_w, columns 0-31 (4 per row)
+    //        640..767   rows 0-31 of T_u, columns 0-31
+    //      followed by P (written above): rows 0-31 by keys 0-31, then
+    //      rows 32-63 by keys 0-63, row-major ----
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+        const int e = tid + P_NT * u;
+        int mat, i, j0;
+        if (e < 512) {
+            mat = e >= 256 ? 1 : 0;
+            const int pp = e - 256 * mat;
+            i = 32 + (pp >> 3);
+            j0 = 8 * (pp & 7);
+        } else {
+            mat = e >= 640 ? 1 : 0;
+            const int pp = e - 512 - 128 * mat;
+            i = pp >> 2;
+            j0 = 8 * (pp & 3);
+        }
+        const float *sc = mat ? colu : colw;
+        const f32x4 t0 = *reinterpret_cast<const f32x4 *>(sT + i * P_LD_A + j0);
+        const f32x4 t1 = *reinterpret_cast<const f32x4 *>(sT + i * P_LD_A + j0 + 4);
+        const f32x4 s0 = *reinterpret_cast<const f32x4 *>(sc + j0);
+        const f32x4 s1 = *reinterpret_cast<const f32x4 *>(sc + j0 + 4);
+        bf16x8 out;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+            out[e2] = (bf16)(t0[e2] * s0[e2]);
+            out[e2 + 4] = (bf16)(t1[e2] * s1[e2]);
+        }
+        *reinterpret_cast<bf16x8 *>(dst + 8 * e) = out;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // chunk_prep: the parts of a chunk that do not depend on the state, for
 // (chunk, head) items. Item i is slot i / H of head i % H; a workgroup takes
@@ -313,9 +450,6 @@ chunk_prep_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         p.bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, 4 * H * (tid0 & 63), 0, 0));
     };
 
-    // off-diagonal 16 x 16 blocks of A (I > J) and blocks of T
-    auto blkA = [&](int I, int J) { return sA + (16 * (I - 1)) * P_LD_A2 + 16 * J; };
-    auto blkT = [&](int I, int J) { return sT + (16 * I) * P_LD_A + 16 * J; };
 
     // one item: stage `p` (the current item's loads) into LDS, start the loads
     // of `nit` into `pn` (which may be `p`), locate item `after` into `ait`,
@@ -328,13 +462,9 @@ chunk_prep_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         int tid = tid0;
         asm volatile("" : "+v"(tid));
         const int lane = tid & 63;
-        const int l32 = lane & 31, lh = lane >> 5, lr = lane & 15, lq = lane >> 4;
+        const int l32 = lane & 31, lh = lane >> 5;
         auto rows4 = [&](const float *v, int i0, int qq) {
             return *reinterpret_cast<const f32x4 *>(v + i0 + 8 * qq + 4 * lh);
-        };
-        auto store_T = [&](int I, int J, f32x4 acc) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sT[(16 * I + 4 * lq + r) * P_LD_A + 16 * J + lr] = acc[r];
         };
 
         if (it.nvalid > 0) {
@@ -449,121 +579,7 @@ chunk_prep_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         }
         lds_barrier();                         // A complete; K and Q no longer read
 
-        if (wave == 0) {
-            // ---- diagonal blocks, one per 16 lanes: lane 16 b + c computes
-            //      column c of D_b = (I - A_bb)^-1 row by row,
-            //      D[i][c] = [i == c] + sum_{m < i} A[i][m] D[m][c]
-            //      (the block's row i read by all 16 lanes: an LDS broadcast);
-            //      row i + 1 is loaded while row i is summed ----
-            const int bb = lane >> 4, c = lane & 15;
-            const float *Ab = sY + bb * P_DB;
-            float D[16];
-            f32x4 rowv[2][4];
-            auto load_row = [&](int i, f32x4 (&dstv)[4]) {
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    if (4 * t < i) dstv[t] = *reinterpret_cast<const f32x4 *>(Ab + i * 16 + 4 * t);
-            };
-            load_row(1, rowv[1]);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                if (i + 1 < 16) load_row(i + 1, rowv[(i + 1) & 1]);
-                float acc = i == c ? 1.f : 0.f;
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (4 * t + e < i) acc += rowv[i & 1][t][e] * D[4 * t + e];
-                D[i] = acc;
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sT[(16 * bb + i) * P_LD_A + 16 * bb + c] = D[i];
-        } else if (wave == 1) {
-            // the 16 x 16 blocks (0,1) and (2,3) of T are zero; the output reads them
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int e = lane + 64 * u;   // 128 four-float pieces
-                const int blk = e >> 6, row = (e >> 2) & 15, c4 = 4 * (e & 3);
-                *reinterpret_cast<f32x4 *>(sT + (32 * blk + row) * P_LD_A + 32 * blk + 16 + c4) = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-        }
-        lds_barrier();
-
-        // ---- off-diagonal blocks of T. With D_b the diagonal inverses:
-        //   T10 = D1 A10 D0,  T32 = D3 A32 D2,  T21 = D2 A21 D1           (16-level)
-        //   T20 = D2 (A20 D0 + A21 T10)
-        //   T31 = T32 (A21 D1) + D3 (A31 D1)
-        //   T30 = T32 (A20 D0 + A21 T10) + D3 (A30 D0 + A31 T10)          (32-level)
-        {
-            const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-            f32x4 h0 = z4, h1 = z4;
-            if (wave == 0) {
-                const f32x4 c10 = mm16(z4, blkA(1, 0), P_LD_A2, blkT(0, 0), P_LD_A, lane);
-                h0 = mm16(z4, blkA(2, 0), P_LD_A2, blkT(0, 0), P_LD_A, lane);              // A20 D0
-                store_T(1, 0, mm16_rb(z4, blkT(1, 1), P_LD_A, acc_to_bop(c10), lane));
-            } else if (wave == 1) {
-                const f32x4 c32 = mm16(z4, blkA(3, 2), P_LD_A2, blkT(2, 2), P_LD_A, lane);
-                store_T(3, 2, mm16_rb(z4, blkT(3, 3), P_LD_A, acc_to_bop(c32), lane));
-            } else if (wave == 2) {
-                h0 = mm16(z4, blkA(2, 1), P_LD_A2, blkT(1, 1), P_LD_A, lane);              // A21 D1
-                h1 = mm16(z4, blkA(3, 1), P_LD_A2, blkT(1, 1), P_LD_A, lane);              // A31 D1
-                store_T(2, 1, mm16_rb(z4, blkT(2, 2), P_LD_A, acc_to_bop(h0), lane));
-            } else {
-                h0 = mm16(z4, blkA(2, 0), P_LD_A2, blkT(0, 0), P_LD_A, lane);              // A20 D0
-                h1 = mm16(z4, blkA(3, 0), P_LD_A2, blkT(0, 0), P_LD_A, lane);              // A30 D0
-            }
-            lds_barrier();
-            if (wave == 0) {
-                const f32x4 y00 = mm16(h0, blkA(2, 1), P_LD_A2, blkT(1, 0), P_LD_A, lane);
-                store_T(2, 0, mm16_rb(z4, blkT(2, 2), P_LD_A, acc_to_bop(y00), lane));
-            } else if (wave == 2) {
-                const f32x4 t = mm16_rb(z4, blkT(3, 2), P_LD_A, acc_to_bop(h0), lane);
-                store_T(3, 1, mm16_rb(t, blkT(3, 3), P_LD_A, acc_to_bop(h1), lane));
-            } else if (wave == 3) {
-                const f32x4 y00 = mm16(h0, blkA(2, 1), P_LD_A2, blkT(1, 0), P_LD_A, lane);
-                const f32x4 y10 = mm16(h1, blkA(3, 1), P_LD_A2, blkT(1, 0), P_LD_A, lane);
-                const f32x4 t = mm16_rb(z4, blkT(3, 2), P_LD_A, acc_to_bop(y00), lane);
-                store_T(3, 0, mm16_rb(t, blkT(3, 3), P_LD_A, acc_to_bop(y10), lane));
-            }
-            lds_barrier();
-        }
-
-        // ---- -T diag(beta e^gamma) and T diag(beta) -> workspace as 16-byte
-        //      pieces (bf16), consecutive per thread. Piece order:
-        //        0..255     rows 32-63 of -T_w (8 per row)
-        //        256..511   rows 32-63 of T_u
-        //        512..639   rows 0-31 of -T_w, columns 0-31 (4 per row)
-        //        640..767   rows 0-31 of T_u, columns 0-31
-        //      followed by P (written above): rows 0-31 by keys 0-31, then
-        //      rows 32-63 by keys 0-63, row-major ----
-#pragma unroll
-        for (int u = 0; u < 3; ++u) {
-            const int e = tid + P_NT * u;
-            int mat, i, j0;
-            if (e < 512) {
-                mat = e >= 256 ? 1 : 0;
-                const int pp = e - 256 * mat;
-                i = 32 + (pp >> 3);
-                j0 = 8 * (pp & 7);
-            } else {
-                mat = e >= 640 ? 1 : 0;
-                const int pp = e - 512 - 128 * mat;
-                i = pp >> 2;
-                j0 = 8 * (pp & 3);
-            }
-            const float *sc = mat ? sBeta : sBegN;
-            const f32x4 t0 = *reinterpret_cast<const f32x4 *>(sT + i * P_LD_A + j0);
-            const f32x4 t1 = *reinterpret_cast<const f32x4 *>(sT + i * P_LD_A + j0 + 4);
-            const f32x4 s0 = *reinterpret_cast<const f32x4 *>(sc + j0);
-            const f32x4 s1 = *reinterpret_cast<const f32x4 *>(sc + j0 + 4);
-            bf16x8 out;
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                out[e2] = (bf16)(t0[e2] * s0[e2]);
-                out[e2 + 4] = (bf16)(t1[e2] * s1[e2]);
-            }
-            *reinterpret_cast<bf16x8 *>(dst + 8 * e) = out;
-        }
+        solve_store(sA, sY, sT, sBegN, sBeta, dst, tid, wave);
         lds_barrier();                         // T and the scalars read before the next item
     };
 
