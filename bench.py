@@ -238,9 +238,10 @@ def bench_decode_mixer(gdn, inputs, steps, warmup):
 
 
 def bench_channel_gated(gdn, inputs, steps, warmup):
-    """Per-channel decay: the token-serial prefill at the prefill workload's
-    shape (B=4, H=16, T=4096, d=128, bf16) and one decode step at the decode
-    shape (B=256, H=32, d=128), with one log-decay per key channel."""
+    """Per-channel decay: the prefill at the prefill workload's shape (B=4,
+    H=16, T=4096, d=128, bf16) by the chunkwise two-pass path and by the
+    token-serial one, and one decode step at the decode shape (B=256, H=32,
+    d=128), with one log-decay per key channel."""
     import torch
     c = inputs.make_channel_gated(seed=7, B=4, T=4096, H=16, d=128, with_state=False)
     d = lambda t: t.cuda().contiguous()
@@ -248,9 +249,21 @@ def bench_channel_gated(gdn, inputs, steps, warmup):
     fin = torch.empty((4, 16, 128, 128), dtype=torch.float32, device="cuda")
     o = torch.empty_like(v)
 
+    ws = torch.empty(gdn.gdn_prefill_channel_workspace_size(4, 4096, 16, 128, 128, 4, False,
+                                                            torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+
     def pre(i):
-        gdn.gdn_prefill_channel_gated(q, k, v, g, beta, None, fin, o, scale=c.scale)
-    ms_pre = event_time(pre, max(1, steps // 4), 1)
+        gdn.gdn_prefill_channel_gated(q, k, v, g, beta, None, fin, o, scale=c.scale, workspace=ws)
+
+    def pre_serial(i):
+        gdn.gdn_prefill_channel_gated(q, k, v, g, beta, None, fin, o, scale=c.scale,
+                                      workspace=None)
+    ms_pre = event_time(pre, steps, warmup)
+    ms_serial = event_time(pre_serial, max(1, steps // 4), 1)
+    # the method's bytes: q, k, v, o bf16, one fp32 log-decay per key channel,
+    # beta, and the final states
+    pre_bytes = 4 * 4096 * 16 * (4 * 128 * 2 + 128 * 4 + 4) + 4 * 16 * 128 * 128 * 4
     dc = inputs.make_decode()
     st = dc.s0.cuda()
     qd, kd, vd = (x[:, 0].cuda().contiguous() for x in (dc.q, dc.k, dc.v))
@@ -263,10 +276,14 @@ def bench_channel_gated(gdn, inputs, steps, warmup):
     ms_dec = event_time(dec, steps, warmup)
     nbytes = decode_bytes(dc.B, dc.H) + dc.B * dc.H * 128 * 4 - dc.B * dc.H * 4
     gbs = nbytes / (ms_dec * 1e-3) / 1e9
-    return dict(workload="per-channel decay: token-serial prefill B=4 H=16 T=4096 d=128 bf16; "
-                         "decode step B=256 H=32 d=128 (fp32 state in place)",
+    return dict(workload="per-channel decay: prefill B=4 H=16 T=4096 d=128 bf16 (chunkwise, two "
+                         "passes; and token-serial); decode step B=256 H=32 d=128 (fp32 state "
+                         "in place)",
                 prefill_tokens_per_s=round(4 * 4096 / (ms_pre * 1e-3), 1),
-                prefill_ms=round(ms_pre, 4), decode_us=round(ms_dec * 1e3, 2),
+                prefill_ms=round(ms_pre, 4),
+                **{"prefill_GB/s": round(pre_bytes / (ms_pre * 1e-3) / 1e9, 1)},
+                serial_prefill_tokens_per_s=round(4 * 4096 / (ms_serial * 1e-3), 1),
+                serial_prefill_ms=round(ms_serial, 4), decode_us=round(ms_dec * 1e3, 2),
                 decode_bytes=nbytes, **{"decode_GB/s": round(gbs, 1)},
                 decode_frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
 

@@ -7,6 +7,7 @@ library; the first call does, and fails loudly if it has not been built.
 """
 from ._binding import (GDNError, gdn_decode_mixer_step, gdn_decode_step,  # noqa: F401
                        gdn_decode_step_channel_gated, gdn_prefill_channel_gated,
+                       gdn_prefill_channel_workspace_size,
                        gdn_prefill_seqpar, gdn_prefill_seqpar_workspace_size,
                        gdn_mixer_epilogue,
                        gdn_mixer_prologue, gdn_prefill, gdn_prefill_recurrent,
@@ -16,6 +17,7 @@ from ._binding import (GDNError, gdn_decode_mixer_step, gdn_decode_step,  # noqa
 __all__ = ["GDNError", "gdn_prefill", "gdn_prefill_workspace_size", "gdn_prefill_prepare",
            "gdn_prefill_apply", "gdn_prefill_recurrent", "gdn_decode_step",
            "gdn_decode_mixer_step", "gdn_prefill_channel_gated",
+           "gdn_prefill_channel_workspace_size",
            "gdn_decode_step_channel_gated", "gdn_prefill_seqpar",
            "gdn_prefill_seqpar_workspace_size",
            "gdn_mixer_prologue", "gdn_mixer_epilogue", "load"]

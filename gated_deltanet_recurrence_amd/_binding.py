@@ -43,7 +43,8 @@ _SIGS = {
     "gdn_mixer_epilogue": [_vp] * 4 + [_i] * 3 + [_f, _i, _vp],
     "gdn_prefill_seqpar": [_vp] * 8 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
     "gdn_prefill_seqpar_workspace_size": [_i] * 7 + [_vp],
-    "gdn_prefill_channel_gated": [_vp] * 9 + [_i] * 7 + [_f, _i, _vp],
+    "gdn_prefill_channel_gated": [_vp] * 9 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
+    "gdn_prefill_channel_workspace_size": [_i] * 8 + [_vp],
     "gdn_decode_step_channel_gated": [_vp] * 7 + [_i] * 5 + [_f, _i, _vp],
     "gdn_decode_mixer_step": [_vp] * 11 + [_f, _vp, _vp] + [_i] * 5 + [_f, _i, _vp],
 }
@@ -113,6 +114,15 @@ def gdn_prefill_workspace_size(B, T, H, d_k, d_v, N, varlen, dtype) -> int:
     return out.value
 
 
+def gdn_prefill_channel_workspace_size(B, T, H, d_k, d_v, N, varlen, dtype) -> int:
+    """Bytes of workspace gdn_prefill_channel_gated uses for these sizes (0: none)."""
+    code = dtype if isinstance(dtype, int) else _dtype_code(torch.empty(0, dtype=dtype))
+    out = ctypes.c_size_t(0)
+    _check(load().gdn_prefill_channel_workspace_size(B, T, H, d_k, d_v, N, int(bool(varlen)),
+                                                     code, ctypes.byref(out)))
+    return out.value
+
+
 def _prefill(entry, q, k, v, g, beta, initial_state=None, final_state=None, o=None,
              cu_seqlens=None, scale=None, workspace=None):
     B, T, Hk, dk = q.shape
@@ -134,12 +144,13 @@ def _prefill(entry, q, k, v, g, beta, initial_state=None, final_state=None, o=No
         _dev(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,)),
     ]
     tail = [float(scale), _dtype_code(q)]
-    if entry == "gdn_prefill":
+    if entry in ("gdn_prefill", "gdn_prefill_channel_gated"):
         if isinstance(workspace, str):
             if workspace != "auto":
                 raise GDNError(f"workspace must be None, 'auto' or a tensor, got {workspace!r}")
-            nbytes = gdn_prefill_workspace_size(B, T, H, dk, dv, N, cu_seqlens is not None,
-                                                _dtype_code(q))
+            size = (gdn_prefill_workspace_size if entry == "gdn_prefill"
+                    else gdn_prefill_channel_workspace_size)
+            nbytes = size(B, T, H, dk, dv, N, cu_seqlens is not None, _dtype_code(q))
             workspace = (torch.empty(nbytes, dtype=torch.uint8, device=q.device)
                          if nbytes else None)
         tail += list(_ws(workspace))
@@ -249,11 +260,14 @@ def gdn_prefill_seqpar(q, k, v, g, beta, segments, initial_state=None, final_sta
 
 
 def gdn_prefill_channel_gated(q, k, v, g, beta, initial_state=None, final_state=None, o=None,
-                              cu_seqlens=None, scale=None):
+                              cu_seqlens=None, scale=None, workspace="auto"):
     """Forward pass with one decay rate per key channel: g [B,T,H,d_k] fp32
-    (see include/gdn.h). Returns (o, final_state)."""
+    (see include/gdn.h). Returns (o, final_state). workspace: "auto" allocates
+    the scratch memory of the chunkwise path (bf16, d_k = d_v = 128) with
+    torch, a uint8 GPU tensor is used as given, None selects the token-serial
+    path."""
     return _prefill("gdn_prefill_channel_gated", q, k, v, g, beta, initial_state, final_state, o,
-                    cu_seqlens, scale)
+                    cu_seqlens, scale, workspace)
 
 
 def gdn_decode_step_channel_gated(q, k, v, g, beta, state, o=None, scale=None):

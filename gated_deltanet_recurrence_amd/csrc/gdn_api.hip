@@ -20,11 +20,13 @@ hipError_t launch_prefill_chunk(const void *, const void *, const void *, const 
                                 const float *, const float *, float *, void *, const int32_t *,
                                 int, int, int, int, float, hipStream_t);
 hipError_t launch_prefill_prepare(const void *, const void *, const float *, const float *,
-                                  const int32_t *, int, int, int, int, void *, hipStream_t);
+                                  const int32_t *, int, int, int, int, void *, hipStream_t,
+                                  bool per_channel = false);
 hipError_t launch_prefill_apply(const void *, const void *, const void *, const float *,
                                 const float *, float *, void *, const int32_t *, int, int, int,
-                                int, float, const void *, hipStream_t, int flags = 0);
-size_t prefill_split_workspace_bytes(long tokens, int H, int N);
+                                int, float, const void *, hipStream_t, int flags = 0,
+                                bool per_channel = false);
+size_t prefill_split_workspace_bytes(long tokens, int H, int N, bool per_channel = false);
 template <typename TIO>
 hipError_t launch_prologue(const void *, const void *, const void *, const void *, const void *,
                            const void *, const float *, const float *, const int32_t *, void *,
@@ -81,9 +83,10 @@ bool chunk_path(int dtype, int d_k, int d_v) {
 }
 
 // a caller's workspace for the two-pass chunk path: 256-byte aligned, large enough
-bool workspace_ok(const void *ws, size_t bytes, int B, int T, int H, int N) {
+bool workspace_ok(const void *ws, size_t bytes, int B, int T, int H, int N,
+                  bool per_channel = false) {
     return (reinterpret_cast<uintptr_t>(ws) & 255) == 0 &&
-           bytes >= gdn::prefill_split_workspace_bytes((long)B * T, H, N);
+           bytes >= gdn::prefill_split_workspace_bytes((long)B * T, H, N, per_channel);
 }
 
 }  // namespace
@@ -291,14 +294,39 @@ int gdn_decode_mixer_step(const void *q_raw, const void *k_raw, const void *v_ra
     return status_of(e);
 }
 
+int gdn_prefill_channel_workspace_size(int B, int T, int H, int d_k, int d_v, int N, int varlen,
+                                       int dtype, size_t *bytes)
+{
+    if (!bytes) return GDN_ERR_NULL;
+    *bytes = 0;
+    const int32_t *cu = varlen ? reinterpret_cast<const int32_t *>(bytes) : nullptr;
+    const void *p = bytes;
+    const int st = check_prefill(p, p, p, (const float *)p, (const float *)p, p, cu, B, T, H,
+                                 H, d_k, d_v, N, dtype);
+    if (st != GDN_OK) return st;
+    if (chunk_path(dtype, d_k, d_v))
+        *bytes = gdn::prefill_split_workspace_bytes((long)B * T, H, N, true);
+    return GDN_OK;
+}
+
 int gdn_prefill_channel_gated(const void *q, const void *k, const void *v, const float *g,
                               const float *beta, const float *initial_state, float *final_state,
                               void *o, const int32_t *cu_seqlens, int B, int T, int H, int H_k,
-                              int d_k, int d_v, int N, float scale, int dtype, void *stream)
+                              int d_k, int d_v, int N, float scale, int dtype, void *workspace,
+                              size_t workspace_bytes, void *stream)
 {
     int st = check_prefill(q, k, v, g, beta, o, cu_seqlens, B, T, H, H_k, d_k, d_v, N, dtype);
     if (st != GDN_OK) return st;
     hipStream_t s = (hipStream_t)stream;
+    if (workspace && chunk_path(dtype, d_k, d_v)) {
+        if (!workspace_ok(workspace, workspace_bytes, B, T, H, N, true)) return GDN_ERR_WORKSPACE;
+        hipError_t e = gdn::launch_prefill_prepare(q, k, g, beta, cu_seqlens, T, H, H_k, N,
+                                                   workspace, s, true);
+        if (e == hipSuccess)
+            e = gdn::launch_prefill_apply(q, k, v, g, initial_state, final_state, o, cu_seqlens,
+                                          T, H, H_k, N, scale, workspace, s, 0, true);
+        return status_of(e);
+    }
     hipError_t e = dtype == GDN_DTYPE_BF16
         ? gdn::launch_prefill_recurrent<gdn::bf16>(q, k, v, g, beta, initial_state, final_state, o,
                                                    cu_seqlens, T, H, H_k, d_k, d_v, N, scale,

@@ -105,7 +105,8 @@ constexpr int SZ_QK = C * LD_R * 2;            // 18432
 constexpr int SZ_V = C * LD_H * 2;             // 5120
 constexpr int SZ_TH = 2 * 32 * LD_H * 2;       // 5120: rows 0-31 of -T_w, then of T_u
 constexpr int SZ_TL = 2 * 32 * LD_L * 2;       // 10240: rows 32-63 of -T_w, then of T_u
-constexpr int SZ_SC = 3 * C * 4;               // gamma, e^gamma, e^{gamma_63 - gamma}
+constexpr int SZ_SC = 3 * C * 4 + DK * 4;      // gamma, e^gamma, e^{gamma_63 - gamma};
+                                               // per-channel decay: e^{gamma_63} per channel
 constexpr int B_Q = 0;
 constexpr int B_K = B_Q + SZ_QK;
 constexpr int B_V = B_K + SZ_QK;
@@ -599,6 +600,365 @@ chunk_prep_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 }
 
 // ---------------------------------------------------------------------------
+// chunk_prep_channel: the prep pass for a per-channel decay ("6.6 Gated
+// DeltaNet", section 6.6.7: alpha_t in R^{d_k}, g = log alpha of shape
+// [T][H][d_k]). With gamma_t[c] the chunk's running sum of g[c] (t inclusive)
+// the chunk algebra keeps its shape once the keys and queries carry the decay
+// channel by channel:
+//   K+ = K e^gamma, Q+ = Q e^gamma, K^ = K e^{gamma_63 - gamma}  (factors <= 1)
+//   M[i][j] = sum_c k_i[c] k_j[c] e^{gamma_i[c] - gamma_j[c]},  A = -strict_lower(diag(beta) M)
+//   T = (I - A)^-1,  T_u = T diag(beta),  P = lower_incl(sum_c q_i k_j e^{gamma_i - gamma_j})
+//   Delta = T_u (V - K+ S^T),  O = Q+ S^T + P Delta,  S <- S diag(e^{gamma_63}) + Delta^T K^
+// M and P are products only after the exponent is split at a reference per
+// 16-token row block I, rho_I = gamma at the token before the block:
+// e^{gamma_i - gamma_j} = e^{gamma_i - rho_I} e^{rho_I - gamma_j}. The first
+// factor is <= 1; the second is <= 1 below the block diagonal and at most the
+// block's own decay on it (e^{rho_I - gamma_j}, j in block I). While every
+// channel decays by less than e^-80 inside every 16-token block of the item
+// (both factors then fit bf16 and fp32), the diagonal blocks come from the same
+// products; otherwise the item's diagonal blocks are summed element by element
+// with exact exponentials.
+//
+// One item per loop step per workgroup of 4 waves; thread (c8, tg) = (tid %
+// 16, tid / 16) owns tokens 4 tg .. 4 tg + 3 and channels 8 c8 .. 8 c8 + 7
+// (wave I owns row block I), loads them (the next item's loads are issued
+// while the current item computes), scans gamma, and writes every scaled copy
+// of its elements: LDS operand tiles (KR = K e^{gamma - rho_I}, QR likewise,
+// KC_I = K e^{rho_I - gamma} over tokens 0 .. 16 I + 15 for each I), and K+,
+// K^, Q+ to the workspace. Wave I then forms row block I of M and of P^T on
+// the matrix cores (16x16x32 bf16, operand tiles with 256-byte rows and
+// 16-byte chunks XOR-swizzled by the row); the triangular solve and the T
+// stores are those of the scalar prep pass (with -T_u in the -T_w slot).
+// Workspace item (CH_ITEM_ELEMS bf16): pieces of -T_u and T_u, P, as in the
+// scalar item; then K+ and K^ ([64][128] row-major); Q+ in the output waves'
+// operand order (fragment f = 4 (t / 16) + c / 32 of 1 KiB, lane 16 ((c / 8)
+// % 4) + t % 16, 8 channels); then e^{gamma_63} (128 fp32).
+// ---------------------------------------------------------------------------
+constexpr int CH_KP = ITEM_ELEMS;              // element offsets inside the item
+constexpr int CH_KH = CH_KP + C * DK;
+constexpr int CH_QP = CH_KH + C * DK;
+constexpr int CH_EC = CH_QP + C * DK;          // 128 fp32 = 256 bf16 slots
+constexpr int CH_ITEM_ELEMS = CH_EC + 2 * DK;
+static_assert((CH_ITEM_ELEMS * 2) % 256 == 0, "items stay 256-byte aligned");
+// LDS (bytes)
+constexpr int CP_ROW = DK * 2;                 // 256-byte operand rows (swizzled)
+constexpr int CP_KR = 0;
+constexpr int CP_QR = CP_KR + C * CP_ROW;
+constexpr int CP_KC = CP_QR + C * CP_ROW;      // KC_0 .. KC_3: 16, 32, 48, 64 rows
+constexpr int CP_RHO = CP_KC + 160 * CP_ROW;   // rho_1 .. rho_4 [4][128] fp32
+constexpr int CP_BETA = CP_RHO + 4 * DK * 4;   // beta [64], -beta [64]
+constexpr int CP_FLAG = CP_BETA + 2 * C * 4;
+constexpr int CP_TAB = CP_FLAG + 16;           // e^rho_1..4, F21 F31 F32, G1 G2 G3: [10][128]
+constexpr int CP_LDS_BYTES = CP_TAB + 10 * DK * 4;
+static_assert(CP_LDS_BYTES <= 160 * 1024 / 2, "two workgroups per CU");
+static_assert(C * P_LD_A * 4 <= CP_KC, "T fits in the KR, QR tiles");
+static_assert(P_SZ_A + P_SZ_Y <= 160 * CP_ROW, "A fits in the KC tiles");
+static_assert(16 * DK * 4 <= 160 * CP_ROW, "the block totals fit in the KC tiles");
+constexpr float CH_EXP_MAX = 80.f;             // largest exponent the products take
+// KC_I starts at row kc_row0(I) of the KC area
+__device__ __forceinline__ int kc_row0(int I) { return 8 * I * (I + 1); }
+// byte offset of the 16-byte chunk holding channels 8 g .. 8 g + 7 of row r of
+// a swizzled operand tile
+__device__ __forceinline__ int cp_off(int r, int g) { return r * CP_ROW + 16 * (g ^ (r & 15)); }
+
+__global__ void __launch_bounds__(P_NT, 2)
+chunk_prep_channel_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
+                          const float *__restrict__ g, const float *__restrict__ beta,
+                          const int32_t *__restrict__ cu_seqlens, bf16 *__restrict__ ws, int T,
+                          int H, int Hk, int N, int nslots)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    float *sRho = reinterpret_cast<float *>(smem + CP_RHO);
+    float *sBeta = reinterpret_cast<float *>(smem + CP_BETA);
+    float *sNegBeta = sBeta + C;
+    int *sFlag = reinterpret_cast<int *>(smem + CP_FLAG);
+    float *sTab = reinterpret_cast<float *>(smem + CP_TAB);
+    float *sTot = reinterpret_cast<float *>(smem + CP_KC);       // [16][128], before KC
+    float *sT = reinterpret_cast<float *>(smem);                 // solve: T over KR, QR
+    float *sA = reinterpret_cast<float *>(smem + CP_KC);         // and A over KC
+    float *sY = sA + P_SZ_A / 4;
+
+    const int tid0 = (int)threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
+    const int nitems = nslots * H;
+    const int stride = (int)gridDim.x;
+    const int tstride = Hk * DK;
+
+    struct Pre {
+        bf16x8 kr[4], qr[4];
+        f32x4 gr[8];
+        float bv;
+    };
+    auto fetch = [&](const PrepItem &it, Pre &p) {
+        const size_t tok0 = (size_t)it.row0;
+        const int c8 = tid0 & 15, tg = tid0 >> 4;
+        const unsigned nb = (unsigned)it.nvalid * tstride * 2;
+        const size_t hoff = tok0 * tstride + (size_t)(it.h / (H / Hk)) * DK;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(k + hoff), 0, nb, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)(q + hoff), 0, nb, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(g + (tok0 * H + it.h) * DK), 0, (unsigned)it.nvalid * H * DK * 4, 0x00020000);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = 4 * tg + j;
+            const unsigned o = (unsigned)((t * tstride + 8 * c8) * 2);
+            p.kr[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
+            p.qr[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, 0));
+            const unsigned og = (unsigned)(((size_t)t * H * DK + 8 * c8) * 4);
+            p.gr[2 * j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, og, 0, 0));
+            p.gr[2 * j + 1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, og + 16, 0, 0));
+        }
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(beta + tok0 * H + it.h), 0, (unsigned)it.nvalid * H * 4, 0x00020000);
+        p.bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, 4 * H * (tid0 & 63), 0, 0));
+    };
+
+    auto item_step = [&](const PrepItem &it, const Pre &p, const PrepItem &nit, Pre &pn,
+                         int after, PrepItem &ait) {
+        int tid = tid0;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, c8 = tid & 15, tg = tid >> 4;
+        const int m = lane & 15, kq = lane >> 4;
+        const int I = wave;                    // row block of this wave's tokens and products
+        bf16 *dst = ws + ((size_t)it.h * nslots + it.slot) * CH_ITEM_ELEMS;
+
+        // ---- gamma: running sums over the thread's 4 tokens, then the
+        //      totals of the earlier token groups ----
+        if (it.nvalid == 0) {                  // uniform over the workgroup
+            fetch(nit, pn);
+            ait = prep_locate(cu_seqlens, after, nitems, T, H, N);
+            return;
+        }
+        float gm[4][8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = e < 4 ? p.gr[2 * j][e] : p.gr[2 * j + 1][e - 4];
+                gm[j][e] = j ? gm[j - 1][e] + x : x;
+            }
+        *reinterpret_cast<f32x4 *>(sTot + tg * DK + 8 * c8) = f32x4{gm[3][0], gm[3][1], gm[3][2], gm[3][3]};
+        *reinterpret_cast<f32x4 *>(sTot + tg * DK + 8 * c8 + 4) = f32x4{gm[3][4], gm[3][5], gm[3][6], gm[3][7]};
+        if (tid < C) {
+            sBeta[tid] = p.bv;
+            sNegBeta[tid] = -p.bv;
+        }
+        if (tid == 0) *sFlag = 0;
+        lds_barrier();
+        {
+            float off[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) off[e] = 0.f;
+            for (int u = 0; u < tg; ++u) {
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(sTot + u * DK + 8 * c8);
+                const f32x4 b = *reinterpret_cast<const f32x4 *>(sTot + u * DK + 8 * c8 + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { off[e] += a[e]; off[4 + e] += b[e]; }
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) gm[j][e] += off[e];
+            if ((tg & 3) == 3) {               // token 16 (I + 1) - 1: rho_{I+1}
+                *reinterpret_cast<f32x4 *>(sRho + I * DK + 8 * c8) = f32x4{gm[3][0], gm[3][1], gm[3][2], gm[3][3]};
+                *reinterpret_cast<f32x4 *>(sRho + I * DK + 8 * c8 + 4) = f32x4{gm[3][4], gm[3][5], gm[3][6], gm[3][7]};
+            }
+        }
+        lds_barrier();
+        // ---- per-channel tables: e^{rho_1..4}; F21, F31, F32 = e^{rho_I -
+        //      rho_J}; G1..G3 = e^{rho_4 - rho_J} (rho_4 = gamma_63) ----
+        for (int x = tid; x < 10 * DK; x += P_NT) {
+            const int id = x / DK, c = x - id * DK;
+            const float *r = sRho + c;         // r[(I - 1) * DK] = rho_I
+            float ex;
+            if (id < 4) ex = r[id * DK];
+            else if (id == 4) ex = r[DK] - r[0];
+            else if (id == 5) ex = r[2 * DK] - r[0];
+            else if (id == 6) ex = r[2 * DK] - r[DK];
+            else ex = r[3 * DK] - r[(id - 7) * DK];
+            sTab[x] = __expf(ex);
+        }
+        lds_barrier();
+        // ---- the scaled copies of the thread's elements ----
+        {
+            auto tab = [&](int id, int e) { return sTab[id * DK + 8 * c8 + e]; };
+            // per channel of the thread: rho_I, rho_{I+1}, e^{rho_I}, e^{rho_4 -
+            // rho_{I+1}} (K^), e^{rho_{I+2} - rho_{I+1}}, e^{rho_3 - rho_1}
+            float rho0[8], rho1[8], eI[8], gI[8], fI2[8], f31[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                rho0[e] = I ? sRho[(I - 1) * DK + 8 * c8 + e] : 0.f;
+                rho1[e] = sRho[I * DK + 8 * c8 + e];
+                eI[e] = I ? tab(I - 1, e) : 1.f;
+                gI[e] = I < 3 ? tab(7 + I, e) : 1.f;
+                fI2[e] = I == 0 ? tab(4, e) : (I == 1 ? tab(6, e) : 0.f);
+                f31[e] = I == 0 ? tab(5, e) : 0.f;
+            }
+            bool big = false;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = 4 * tg + j;
+                bf16x8 kr, qr, kd, kp, kh, qp, kc1, kc2, kc3;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float rf = __expf(gm[j][e] - rho0[e]);
+                    const float dx = rho0[e] - gm[j][e];
+                    big |= dx > CH_EXP_MAX;
+                    const float df = __expf(dx < CH_EXP_MAX ? dx : CH_EXP_MAX);
+                    const float nf = __expf(rho1[e] - gm[j][e]);
+                    const float E = eI[e] * rf;
+                    const float kk = (float)p.kr[j][e], qq2 = (float)p.qr[j][e];
+                    kr[e] = (bf16)(kk * rf);
+                    qr[e] = (bf16)(qq2 * rf);
+                    kd[e] = (bf16)(kk * df);
+                    kp[e] = (bf16)(kk * E);
+                    qp[e] = (bf16)(qq2 * E);
+                    kh[e] = (bf16)(kk * nf * gI[e]);
+                    // KC_{I'} for I' > I: nf e^{rho_I' - rho_{I+1}}
+                    kc1[e] = (bf16)(kk * nf);                  // I' = I + 1
+                    kc2[e] = (bf16)(kk * nf * fI2[e]);         // I' = I + 2
+                    kc3[e] = (bf16)(kk * nf * f31[e]);         // I' = 3 (I = 0)
+                }
+                *reinterpret_cast<bf16x8 *>(smem + CP_KR + cp_off(t, c8)) = kr;
+                *reinterpret_cast<bf16x8 *>(smem + CP_QR + cp_off(t, c8)) = qr;
+                *reinterpret_cast<bf16x8 *>(smem + CP_KC + cp_off(kc_row0(I) + t, c8)) = kd;
+                if (I + 1 <= 3) *reinterpret_cast<bf16x8 *>(smem + CP_KC + cp_off(kc_row0(I + 1) + t, c8)) = kc1;
+                if (I + 2 <= 3) *reinterpret_cast<bf16x8 *>(smem + CP_KC + cp_off(kc_row0(I + 2) + t, c8)) = kc2;
+                if (I == 0) *reinterpret_cast<bf16x8 *>(smem + CP_KC + cp_off(kc_row0(3) + t, c8)) = kc3;
+                *reinterpret_cast<bf16x8 *>(dst + CH_KP + t * DK + 8 * c8) = kp;
+                *reinterpret_cast<bf16x8 *>(dst + CH_KH + t * DK + 8 * c8) = kh;
+                const int f = 4 * (t >> 4) + (c8 >> 2), ln = 16 * (c8 & 3) + (t & 15);
+                *reinterpret_cast<bf16x8 *>(dst + CH_QP + 512 * f + 8 * ln) = qp;
+            }
+            if (big) *sFlag = 1;
+            if (tg == 0) {                     // e^{gamma_63} of the thread's channels
+                float *ec = reinterpret_cast<float *>(dst + CH_EC) + 8 * c8;
+                *reinterpret_cast<f32x4 *>(ec) = f32x4{tab(3, 0), tab(3, 1), tab(3, 2), tab(3, 3)};
+                *reinterpret_cast<f32x4 *>(ec + 4) = f32x4{tab(3, 4), tab(3, 5), tab(3, 6), tab(3, 7)};
+            }
+        }
+        // the item's loads are consumed: the next item's are issued now and
+        // overlap the products, the solve and the stores
+        fetch(nit, pn);
+        ait = prep_locate(cu_seqlens, after, nitems, T, H, N);
+        lds_barrier();
+        // ---- wave I: row block I of M (accM[J]) and of P^T (accP[J], rows =
+        //      keys 16 J + .., columns = queries 16 I + ..), J <= I ----
+        f32x4 accM[4], accP[4];
+#pragma unroll
+        for (int J = 0; J < 4; ++J) { accM[J] = f32x4{0.f, 0.f, 0.f, 0.f}; accP[J] = accM[J]; }
+        {
+            const unsigned char *kcI = smem + CP_KC + kc_row0(I) * CP_ROW;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int gr = 4 * s + kq;
+                const bf16x8 ak = *reinterpret_cast<const bf16x8 *>(smem + CP_KR + cp_off(16 * I + m, gr));
+                const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(smem + CP_QR + cp_off(16 * I + m, gr));
+#pragma unroll
+                for (int J = 0; J < 4; ++J) {
+                    if (J > I) break;          // uniform
+                    const bf16x8 b = *reinterpret_cast<const bf16x8 *>(kcI + cp_off(16 * J + m, gr));
+                    accM[J] = mfma16(ak, b, accM[J]);
+                    accP[J] = mfma16(b, aq, accP[J]);
+                }
+            }
+        }
+        lds_barrier();                         // operand tiles read
+        if (*sFlag) {
+            // ---- exact diagonal blocks (rare: a channel decays by more than
+            //      e^-80 inside a 16-token block). k, q and g of the item are
+            //      read again from memory (the registers hold the next item's),
+            //      gamma is summed per channel into LDS, then lane (n, qq) of
+            //      wave I sums entries (4 qq + r, n) of block (I, I) with one
+            //      exponential per channel ----
+            float *sG = reinterpret_cast<float *>(smem);              // [64][128] fp32
+            bf16 *sKr = reinterpret_cast<bf16 *>(smem + C * DK * 4);  // [64][128]
+            bf16 *sQr = sKr + C * DK;
+            const size_t kqh = (size_t)it.row0 * tstride + (size_t)(it.h / (H / Hk)) * DK;
+            for (int x = tid; x < C * DK / 8; x += P_NT) {
+                const int t = x >> 4, cg = x & 15;
+                const bool ok = t < it.nvalid;
+                *reinterpret_cast<bf16x8 *>(sKr + t * DK + 8 * cg) =
+                    ok ? *reinterpret_cast<const bf16x8 *>(k + kqh + (size_t)t * tstride + 8 * cg) : bf16x8{};
+                *reinterpret_cast<bf16x8 *>(sQr + t * DK + 8 * cg) =
+                    ok ? *reinterpret_cast<const bf16x8 *>(q + kqh + (size_t)t * tstride + 8 * cg) : bf16x8{};
+            }
+            if (tid < DK) {
+                const float *gp = g + ((size_t)it.row0 * H + it.h) * DK + tid;
+                float run = 0.f;
+                for (int t = 0; t < C; ++t) {
+                    run += t < it.nvalid ? gp[(size_t)t * H * DK] : 0.f;
+                    sG[t * DK + tid] = run;
+                }
+            }
+            lds_barrier();
+            const int jn = 16 * I + m;         // key (column of M, row of P^T)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int iq = 16 * I + 4 * kq + r;   // query/key row of M
+                float sm = 0.f, sp = 0.f;
+                if (jn < iq) {                 // M[iq][jn]
+                    for (int c = 0; c < DK; ++c)
+                        sm += (float)sKr[iq * DK + c] * (float)sKr[jn * DK + c] *
+                              __expf(sG[iq * DK + c] - sG[jn * DK + c]);
+                }
+                // P^T[key 16 I + 4 kq + r][query 16 I + m] = P[query][key]
+                const int qi = 16 * I + m, kj = 16 * I + 4 * kq + r;
+                if (kj <= qi) {
+                    for (int c = 0; c < DK; ++c)
+                        sp += (float)sQr[qi * DK + c] * (float)sKr[kj * DK + c] *
+                              __expf(sG[qi * DK + c] - sG[kj * DK + c]);
+                }
+                accM[I][r] = sm;
+                accP[I][r] = sp;
+            }
+            lds_barrier();                     // scratch read before A is written over it
+        }
+        // ---- A = -strict_lower(diag(beta) M) into sY (diagonal blocks) and
+        //      sA (rows 16-63, columns 0-47); P (queries x keys, lower incl.)
+        //      straight to the workspace ----
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            if (J > I) break;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * I + 4 * kq + r, j = 16 * J + m;
+                const float a = j < i ? -sBeta[i] * accM[J][r] : 0.f;
+                if (J == I) sY[I * P_DB + (4 * kq + r) * 16 + m] = a;
+                else if (j < 48) sA[(i - 16) * P_LD_A2 + j] = a;
+            }
+            // P^T accumulator r: key 16 J + 4 kq + r, query 16 I + m
+            const int qi = 16 * I + m;
+            bf16x4 x;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[r] = (bf16)(16 * J + 4 * kq + r <= qi ? accP[J][r] : 0.f);
+            bf16 *prow = dst + 8 * WS_TWU + (qi < 32 ? 32 * qi : 1024 + 64 * (qi - 32));
+            *reinterpret_cast<bf16x4 *>(prow + 16 * J + 4 * kq) = x;
+        }
+        if (I == 0 || I == 2) {                // keys 16 I + 16 .. 16 I + 31 of these rows are stored: zero
+            const int qi = 16 * I + m;
+            bf16 *prow = dst + 8 * WS_TWU + (qi < 32 ? 32 * qi : 1024 + 64 * (qi - 32));
+            *reinterpret_cast<bf16x4 *>(prow + 16 * (I + 1) + 4 * kq) = bf16x4{};
+        }
+        lds_barrier();                         // A complete
+        solve_store(sA, sY, sT, sNegBeta, sBeta, dst, tid, wave);
+        lds_barrier();                         // T and the scalars read before the next item
+    };
+
+    const int first = (int)blockIdx.x;
+    PrepItem it = prep_locate(cu_seqlens, first, nitems, T, H, N);
+    PrepItem nit = prep_locate(cu_seqlens, first + stride, nitems, T, H, N);
+    Pre pre;
+    fetch(it, pre);
+    for (int item = first; item < nitems; item += stride) {
+        PrepItem ait;
+        item_step(it, pre, nit, pre, item + 2 * stride, ait);
+        it = nit;
+        nit = ait;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // chunk_chain: the sequential pass. One workgroup of 8 waves per (32-wide d_v
 // tile, head, sequence), one LDS barrier per chunk.
 //
@@ -634,6 +994,7 @@ chunk_prep_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 // Tokens past the end of a sequence are identity steps (q = k = v = 0,
 // g = 0, and T_w, T_u vanish on them) and their outputs are not stored.
 // ---------------------------------------------------------------------------
+template <bool PERCH>
 __global__ void __launch_bounds__(NT, 1)
 chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                    const bf16 *__restrict__ v, const float *__restrict__ g,
@@ -670,7 +1031,10 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     seq_bounds(cu_seqlens, n, T, bos, eos);
     const int len = (int)(eos - bos);
     const int nchunks = (len + C - 1) / C;
-    const bf16 *wsh = ws + ((size_t)h * nslots + (size_t)((bos >> 6) + n)) * ITEM_ELEMS;
+    // workspace item stride: the per-channel item also holds K+, K^, Q+ and
+    // the chunk's per-channel decay
+    constexpr int IST = PERCH ? CH_ITEM_ELEMS : ITEM_ELEMS;
+    const bf16 *wsh = ws + ((size_t)h * nslots + (size_t)((bos >> 6) + n)) * IST;
     const size_t sbase = ((size_t)n * H + h) * DV * DK;
     const int lane0 = tid0 & 63;
 
@@ -719,7 +1083,9 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     //      Workspace piece order (8 bf16 each): 0..255 rows 32-63 of -T_w (8
     //      per row), 256..511 rows 32-63 of T_u, 512..639 rows 0-31 of -T_w (4
     //      per row: columns 0-31), 640..767 rows 0-31 of T_u. ----
-    const int tstride = Hk * DK;               // elements between tokens of q, k
+    // elements between tokens of the staged Q and K tiles (per channel: the
+    // workspace's K^ and K+ rows)
+    const int tstride = PERCH ? DK : Hk * DK;
     const int tsv = H * DV;                    // ... and of v
     const int wi = wave - 4;
     const int qkmat = wi >> 1;                 // 0 Q, 1 K
@@ -733,7 +1099,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         return e < 512 ? B_TL / 2 + (e >> 3) * LD_L + 8 * (e & 7)
                        : B_TH / 2 + ((e - 512) >> 2) * LD_H + 8 * (e & 3);
     };
-    const bf16 *qk_head = (qkmat ? k : q) + (size_t)bos * tstride + (size_t)(h / (H / Hk)) * DK;
+    const bf16 *qk_head = (qkmat ? k : q) + (size_t)bos * (Hk * DK) + (size_t)(h / (H / Hk)) * DK;
     const bf16 *v_head = v + (size_t)bos * tsv + (size_t)h * DV + cbase;
     const float *g_head = g + (size_t)bos * H + h;
     // Two register sets: chunk c is loaded into set c % 2 three iterations
@@ -741,6 +1107,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     struct Pref {
         bf16x8 b[8], t[3], v[2];
         float g;
+        f32x2 ec;                              // per channel: e^{gamma_63}, channels 2 lane ..
     };
     Pref pA, pB;
     // WG: whether this wave loads and scans g, WV: whether it loads V
@@ -749,10 +1116,13 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         const int base = ch * C;
         const int nrow = len - base < C ? len - base : C;      // tokens of the chunk in the sequence
         const unsigned nb = (unsigned)nrow * tstride * 2;
+        // per channel the Q tile is K^ and the K tile K+, both from the workspace
+        const bf16 *qk_src = PERCH ? wsh + (size_t)ch * IST + (qkmat ? CH_KP : CH_KH)
+                                   : qk_head + (size_t)base * tstride;
         const __amdgpu_buffer_rsrc_t rqk = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(qk_head + (size_t)base * tstride), 0, nb, 0x00020000);
+            (void *)qk_src, 0, nb, 0x00020000);
         const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(wsh + (size_t)ch * ITEM_ELEMS), 0, WS_TWU * 16, 0x00020000);
+            (void *)(wsh + (size_t)ch * IST), 0, WS_TWU * 16, 0x00020000);
 #pragma unroll
         for (int r = 0; r < 8; ++r)
             rs.b[r] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
@@ -772,9 +1142,17 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                               rv, goffV, (vr0 + r) * 16 * tsv * 2, 0));
         }
         if constexpr (decltype(WG)::value) {
-            const __amdgpu_buffer_rsrc_t rgs = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(g_head + (size_t)base * H), 0, (unsigned)nrow * H * 4, 0x00020000);
-            rs.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rgs, 4 * H * lane0, 0, 0));
+            if constexpr (PERCH) {
+                // no per-token gate (the decay is in K+, K^, Q+); the state's
+                // per-channel decay of the chunk instead
+                rs.g = 0.f;
+                rs.ec = *reinterpret_cast<const f32x2 *>(
+                    reinterpret_cast<const float *>(wsh + (size_t)ch * IST + CH_EC) + 2 * lane0);
+            } else {
+                const __amdgpu_buffer_rsrc_t rgs = __builtin_amdgcn_make_buffer_rsrc(
+                    (void *)(g_head + (size_t)base * H), 0, (unsigned)nrow * H * 4, 0x00020000);
+                rs.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rgs, 4 * H * lane0, 0, 0));
+            }
         }
     };
     auto store = [&](const Pref &rs, int b, auto WG, auto WV, int lane) {
@@ -798,6 +1176,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             sc[lane] = gam;
             sc[C + lane] = __expf(gam);
             sc[2 * C + lane] = __expf(glast - gam);
+            if constexpr (PERCH) *reinterpret_cast<f32x2 *>(sc + 3 * C + 2 * lane) = rs.ec;
         }
     };
     const std::true_type with_g{}, with_v{}, with_p{};
@@ -901,7 +1280,9 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                     for (int s2 = 0; s2 < 2; ++s2) {
                         const int c0 = 32 * (d >> 1) + 4 * (d & 1) + 8 * (m & 3);
                         const int r0 = 32 * s2 + 4 * qq + (m >> 2);
-                        fkt[d][s2] = cat4(tr4(sK, r0 * LD_R + c0), tr4(sK, (r0 + 16) * LD_R + c0));
+                        // per channel the update's keys are K^ (in the Q tile)
+                        const bf16 *sKu = PERCH ? stQ(b) : sK;
+                        fkt[d][s2] = cat4(tr4(sKu, r0 * LD_R + c0), tr4(sKu, (r0 + 16) * LD_R + c0));
                     }
                 __builtin_amdgcn_sched_barrier(0);
                 // Delta = U + (-T_w) X
@@ -929,6 +1310,13 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                 // S^T <- e^{gamma_63} S^T + K^T Delta~ (the decay while Delta is formed)
 #pragma unroll
                 for (int d = 0; d < 8; ++d) Sacc[d] = Sacc[d] * eend;
+                if constexpr (PERCH) {
+                    // S <- S diag(e^{gamma_63}): row dk(d, q, r) of S^T by its channel's factor
+                    const float *ec = stSc(b) + 3 * C;
+#pragma unroll
+                    for (int d = 0; d < 8; ++d)
+                        Sacc[d] = Sacc[d] * *reinterpret_cast<const f32x4 *>(ec + 32 * (d >> 1) + 8 * qq + 4 * (d & 1));
+                }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int d = 0; d < 8; ++d) {
@@ -956,6 +1344,9 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             constexpr int hw = decltype(HW)::value;
             constexpr int NS = hw + 1;         // key blocks of 32 that tokens 32 hw .. need
             f32x4 oacc[2][2][2];               // [chunk parity][u][token tile 2 hw + tt]
+            // per channel: the wave's fragments of Q+ (Q e^gamma, from the
+            // workspace in operand order), by chunk parity, loaded one chunk ahead
+            bf16x8 fqg[PERCH ? 2 : 1][2][4];
             for (int ch0 = -3; ch0 <= nchunks; ch0 += 2)
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
@@ -965,6 +1356,16 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                 asm volatile("" : "+v"(tidl));
                 const int lane = tidl & 63, m = lane & 15, qq = lane >> 4;
                 const int r0 = 8 * (m >> 2) + (m & 3);     // d_v row of tile row m, u = 0
+                if constexpr (PERCH) {
+                    if (o && ch + 1 >= 0 && ch + 1 < nchunks) {
+                        const bf16 *qp = wsh + (size_t)(ch + 1) * IST + CH_QP + 8 * lane;
+#pragma unroll
+                        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                            for (int s2 = 0; s2 < 4; ++s2)
+                                fqg[hf][tt][s2] = *reinterpret_cast<const bf16x8 *>(qp + 512 * (4 * (2 * hw + tt) + s2));
+                    }
+                }
                 if (o && ch >= 0 && ch < nchunks) {   // o == NULL: the states only
                     // (Q S^T)^T = S Q^T for the wave's 32 tokens, then e^gamma per token
                     const bf16 *sSc = cpS(b), *sQ = stQ(b);
@@ -976,8 +1377,10 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                         for (int u = 0; u < 2; ++u)
                             fs[u][s2] = lds8(sSc, (r0 + 4 * u) * LD_R + ((32 * s2 + 8 * qq) ^ swS(r0 + 4 * u)));
 #pragma unroll
-                        for (int tt = 0; tt < 2; ++tt)
-                            fq[tt][s2] = lds8(sQ, (16 * (2 * hw + tt) + m) * LD_R + 32 * s2 + 8 * qq);
+                        for (int tt = 0; tt < 2; ++tt) {
+                            if constexpr (PERCH) fq[tt][s2] = fqg[b][tt][s2];
+                            else fq[tt][s2] = lds8(sQ, (16 * (2 * hw + tt) + m) * LD_R + 32 * s2 + 8 * qq);
+                        }
                     }
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -991,11 +1394,13 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
                             for (int tt = 0; tt < 2; ++tt)
                                 oacc[b][u][tt] = mfma16(fs[u][s2], fq[tt][s2], oacc[b][u][tt]);
+                    if constexpr (!PERCH) {            // per channel the decay is in Q+
 #pragma unroll
-                    for (int tt = 0; tt < 2; ++tt) {
-                        const float e = sEg[16 * (2 * hw + tt) + m];
+                        for (int tt = 0; tt < 2; ++tt) {
+                            const float e = sEg[16 * (2 * hw + tt) + m];
 #pragma unroll
-                        for (int u = 0; u < 2; ++u) oacc[b][u][tt] = oacc[b][u][tt] * e;
+                            for (int u = 0; u < 2; ++u) oacc[b][u][tt] = oacc[b][u][tt] * e;
+                        }
                     }
                 }
                 if (o && ch >= 1 && ch <= nchunks) {
@@ -1053,7 +1458,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         const int pe0 = 192 * (wave - 4);
         auto pfetch = [&](int ch, bf16x8 (&pr)[3]) {
             const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(wsh + (size_t)ch * ITEM_ELEMS + 8 * WS_TWU), 0, WS_P * 16, 0x00020000);
+                (void *)(wsh + (size_t)ch * IST + 8 * WS_TWU), 0, WS_P * 16, 0x00020000);
 #pragma unroll
             for (int r = 0; r < 3; ++r)
                 pr[r] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
@@ -1103,61 +1508,92 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 }
 
 // Workspace bytes of the two-pass path for `tokens` packed tokens in N
-// sequences of H heads.
-size_t prefill_split_workspace_bytes(long tokens, int H, int N) {
+// sequences of H heads (per_channel: the larger per-channel item).
+size_t prefill_split_workspace_bytes(long tokens, int H, int N, bool per_channel) {
     const long nslots = tokens / C + N + 1;
-    return (size_t)nslots * H * ITEM_ELEMS * sizeof(bf16);
+    return (size_t)nslots * H * (per_channel ? CH_ITEM_ELEMS : ITEM_ELEMS) * sizeof(bf16);
+}
+
+// Workgroups that fill every CU of the current device at the occupancy a
+// persistent prep kernel reaches (cached per device; concurrent first calls
+// compute the same value).
+static hipError_t prep_fill(const void *kern, int lds, std::atomic<long> *cache, long &fill)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    fill = dev < MAX_DEVICES ? cache[dev].load(std::memory_order_relaxed) : 0;
+    if (fill == 0) {
+        int cus = 0, per_cu = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, P_NT, lds);
+        if (e != hipSuccess) return e;
+        fill = (long)(per_cu < 1 ? 1 : per_cu) * (cus < 1 ? 1 : cus);
+        if (dev < MAX_DEVICES) cache[dev].store(fill, std::memory_order_relaxed);
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_prefill_prepare(const void *q, const void *k, const float *g, const float *beta,
                                   const int32_t *cu, int T, int H, int Hk, int N, void *ws,
-                                  hipStream_t stream)
+                                  hipStream_t stream, bool per_channel)
 {
     const long tokens = cu ? (long)T : (long)N * T;
     const long nslots = tokens / C + N + 1;
     if (tokens == 0) return hipSuccess;        // no chunk: nothing to prepare
-    // enough workgroups to fill every CU of the current device at the
-    // occupancy the kernel reaches, each looping over items (cached per
-    // device; concurrent first calls compute the same value)
-    static std::atomic<long> fill_of[MAX_DEVICES];
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    long fill = dev < MAX_DEVICES ? fill_of[dev].load(std::memory_order_relaxed) : 0;
-    if (fill == 0) {
-        int cus = 0, per_cu = 0;
-        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e == hipSuccess)
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)chunk_prep_kernel,
-                                                             P_NT, P_LDS_BYTES);
-        if (e != hipSuccess) return e;
-        fill = (long)(per_cu < 1 ? 1 : per_cu) * (cus < 1 ? 1 : cus);
-        if (dev < MAX_DEVICES) fill_of[dev].store(fill, std::memory_order_relaxed);
-    }
     const long nitems = nslots * H;
+    static std::atomic<long> fill_scalar[MAX_DEVICES], fill_channel[MAX_DEVICES];
+    long fill = 0;
+    if (per_channel) {
+        static const hipError_t attr = hipFuncSetAttribute(
+            (const void *)chunk_prep_channel_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+            CP_LDS_BYTES);
+        if (attr != hipSuccess) return attr;
+        hipError_t e = prep_fill((const void *)chunk_prep_channel_kernel, CP_LDS_BYTES, fill_channel, fill);
+        if (e != hipSuccess) return e;
+        dim3 grid((unsigned)(nitems < fill ? nitems : fill)), block(P_NT);
+        hipLaunchKernelGGL(chunk_prep_channel_kernel, grid, block, CP_LDS_BYTES, stream,
+                           (const bf16 *)q, (const bf16 *)k, g, beta, cu, (bf16 *)ws, T, H, Hk, N,
+                           (int)nslots);
+        return hipGetLastError();
+    }
+    hipError_t e = prep_fill((const void *)chunk_prep_kernel, P_LDS_BYTES, fill_scalar, fill);
+    if (e != hipSuccess) return e;
     dim3 grid((unsigned)(nitems < fill ? nitems : fill)), block(P_NT);
     hipLaunchKernelGGL(chunk_prep_kernel, grid, block, P_LDS_BYTES, stream, (const bf16 *)q,
                        (const bf16 *)k, g, beta, cu, (bf16 *)ws, T, H, Hk, N, (int)nslots);
     return hipGetLastError();
 }
 
-hipError_t launch_prefill_apply(const void *q, const void *k, const void *v, const float *g,
-                                const float *s_init, float *s_final, void *o, const int32_t *cu,
-                                int T, int H, int Hk, int N, float scale, const void *ws,
-                                hipStream_t stream, int flags)
+template <bool PERCH>
+static hipError_t launch_chain(const void *q, const void *k, const void *v, const float *g,
+                               const float *s_init, float *s_final, void *o, const int32_t *cu,
+                               int T, int H, int Hk, int N, float scale, const void *ws,
+                               hipStream_t stream, int flags)
 {
     // the dynamic LDS limit, raised once per process (thread-safe static)
     static const hipError_t attr = hipFuncSetAttribute(
-        (const void *)chunk_chain_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+        (const void *)chunk_chain_kernel<PERCH>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (attr != hipSuccess) return attr;
     const long tokens = cu ? (long)T : (long)N * T;
     const long nslots = tokens / C + N + 1;
     const int npairs = H * N;
     dim3 grid(pair_grid(npairs)), block(NT);
-    hipLaunchKernelGGL(chunk_chain_kernel, grid, block, LDS_BYTES, stream, (const bf16 *)q,
+    hipLaunchKernelGGL(chunk_chain_kernel<PERCH>, grid, block, LDS_BYTES, stream, (const bf16 *)q,
                        (const bf16 *)k, (const bf16 *)v, g, (const bf16 *)ws, s_init, s_final,
                        (bf16 *)o, cu, T, H, Hk, npairs, (int)nslots, scale, flags);
     return hipGetLastError();
+}
+
+hipError_t launch_prefill_apply(const void *q, const void *k, const void *v, const float *g,
+                                const float *s_init, float *s_final, void *o, const int32_t *cu,
+                                int T, int H, int Hk, int N, float scale, const void *ws,
+                                hipStream_t stream, int flags, bool per_channel)
+{
+    return per_channel ? launch_chain<true>(q, k, v, g, s_init, s_final, o, cu, T, H, Hk, N, scale,
+                                            ws, stream, flags)
+                       : launch_chain<false>(q, k, v, g, s_init, s_final, o, cu, T, H, Hk, N, scale,
+                                             ws, stream, flags);
 }
 
 }  // namespace gdn

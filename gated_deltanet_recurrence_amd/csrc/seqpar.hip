@@ -24,11 +24,13 @@ namespace gdn {
 constexpr int SP_D = 128;                      // d_k = d_v of the chunk kernels
 
 hipError_t launch_prefill_prepare(const void *, const void *, const float *, const float *,
-                                  const int32_t *, int, int, int, int, void *, hipStream_t);
+                                  const int32_t *, int, int, int, int, void *, hipStream_t,
+                                  bool per_channel = false);
 hipError_t launch_prefill_apply(const void *, const void *, const void *, const float *,
                                 const float *, float *, void *, const int32_t *, int, int, int,
-                                int, float, const void *, hipStream_t, int flags);
-size_t prefill_split_workspace_bytes(long tokens, int H, int N);
+                                int, float, const void *, hipStream_t, int flags,
+                                bool per_channel = false);
+size_t prefill_split_workspace_bytes(long tokens, int H, int N, bool per_channel = false);
 
 namespace split {
 constexpr int CHAIN_ZERO_V = 1;                // as in prefill_split.hip

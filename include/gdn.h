@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define GDN_VERSION 2
+#define GDN_VERSION 3
 
 typedef enum {
     GDN_DTYPE_F32 = 0,
@@ -262,18 +262,32 @@ int gdn_decode_step(const void *q, const void *k, const void *v,
  *
  *     S_t = S_{t-1} diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
  *
- * Arguments, layouts and errors as gdn_prefill_recurrent (token-serial fp32
- * arithmetic; no workspace) and gdn_decode_step, except g:
+ * Arguments, layouts and errors as gdn_prefill and gdn_decode_step, except g:
  *   prefill: g [B][T][H][d_k] fp32;  decode: g [B][H][d_k] fp32.
  * With every channel of g equal, the results equal those of the per-head
  * entry points.
+ *
+ * Prefill paths. bf16 with d_k = d_v = 128 and a workspace (size from
+ * gdn_prefill_channel_workspace_size; 256-byte aligned, caller-owned, contents
+ * on entry irrelevant, GDN_ERR_WORKSPACE if too small or misaligned) runs the
+ * chunkwise form in two passes: with gamma the running sum of g over a
+ * 64-token chunk, the keys and queries carry the decay channel by channel
+ * (K e^gamma, K e^{gamma_63 - gamma}, Q e^gamma), the in-chunk products
+ * sum_c k_i[c] k_j[c] e^{gamma_i[c] - gamma_j[c]} are split at a reference
+ * token per 16-token block so that they run on the matrix cores, and the
+ * state decays by e^{gamma_63} per channel at each chunk end. Otherwise
+ * (no workspace, fp32, other head sizes) the token-serial fp32 recurrence.
  */
+int gdn_prefill_channel_workspace_size(int B, int T, int H, int d_k, int d_v, int N,
+                                       int varlen, int dtype, size_t *bytes);
+
 int gdn_prefill_channel_gated(const void *q, const void *k, const void *v,
                               const float *g, const float *beta,
                               const float *initial_state, float *final_state,
                               void *o, const int32_t *cu_seqlens,
                               int B, int T, int H, int H_k, int d_k, int d_v, int N,
-                              float scale, int dtype, void *stream);
+                              float scale, int dtype, void *workspace,
+                              size_t workspace_bytes, void *stream);
 
 int gdn_decode_step_channel_gated(const void *q, const void *k, const void *v,
                                   const float *g, const float *beta,

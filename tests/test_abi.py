@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdn_version() == 2
+    assert lib.gdn_version() == 3
     for st in (GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_UNSUPPORTED, -5,
                GDN_ERR_WORKSPACE, 99):
         s = lib.gdn_status_string(st)
@@ -180,9 +180,22 @@ def test_channel_gated_validation(lib):
     a = [P] * 5 + [None, None, P, None]
     bad = list(a)
     bad[3] = None                            # g
-    assert f(*bad, 1, 8, 2, 2, 128, 128, 1, 1.0, 1, None) == GDN_ERR_NULL
-    assert f(*a, 1, 8, 4, 3, 128, 128, 1, 1.0, 1, None) == GDN_ERR_SHAPE
-    assert f(*a, 1, 8, 2, 2, 48, 128, 1, 1.0, 1, None) == GDN_ERR_UNSUPPORTED
+    assert f(*bad, 1, 8, 2, 2, 128, 128, 1, 1.0, 1, None, 0, None) == GDN_ERR_NULL
+    assert f(*a, 1, 8, 4, 3, 128, 128, 1, 1.0, 1, None, 0, None) == GDN_ERR_SHAPE
+    assert f(*a, 1, 8, 2, 2, 48, 128, 1, 1.0, 1, None, 0, None) == GDN_ERR_UNSUPPORTED
+    # the chunkwise path's workspace: sized per item, checked before any launch
+    out = ctypes.c_size_t(0)
+    ws_size = lib.gdn_prefill_channel_workspace_size
+    assert ws_size(1, 100, 2, 128, 128, 1, 0, 1, ctypes.byref(out)) == GDN_OK
+    need = out.value
+    scalar = ctypes.c_size_t(0)
+    assert lib.gdn_prefill_workspace_size(1, 100, 2, 128, 128, 1, 0, 1, ctypes.byref(scalar)) == GDN_OK
+    assert need > scalar.value > 0
+    assert ws_size(1, 100, 2, 64, 64, 1, 0, 1, ctypes.byref(out)) == GDN_OK and out.value == 0
+    assert ws_size(1, 100, 2, 128, 128, 1, 0, 1, None) == GDN_ERR_NULL
+    ws = 256 * 1024                          # aligned stand-in address, never dereferenced
+    assert f(*a, 1, 100, 2, 2, 128, 128, 1, 1.0, 1, ws, need - 1, None) == GDN_ERR_WORKSPACE
+    assert f(*a, 1, 100, 2, 2, 128, 128, 1, 1.0, 1, ws + 16, need, None) == GDN_ERR_WORKSPACE
     d = lib.gdn_decode_step_channel_gated
     assert d(P, P, P, None, P, P, P, 1, 2, 2, 128, 128, 1.0, 1, None) == GDN_ERR_NULL
     assert d(P, P, P, P, P, P, P, 1, 2, 2, 128, 128, 1.0, 3, None) == GDN_ERR_DTYPE

@@ -641,3 +641,80 @@ def test_channel_gated_ragged_value_rows():
     o, fin = run_prefill(c, entry=gdn.gdn_prefill_channel_gated)
     o_ref, s_ref = oracle.gdn_recurrent_channel(c.q, c.k, c.v, c.g, c.beta, c.s0, None, c.scale)
     assert o_err(o, o_ref) <= TOL_F32 and s_err(fin, s_ref) <= TOL_F32
+
+
+# --- per-channel decay, chunkwise (two passes through the workspace) -----------------
+
+def _channel_run(c, workspace="auto", init=True):
+    s0 = dev(c.s0) if (init and c.s0 is not None) else None
+    fin = torch.empty((c.N, c.H, c.d_v, c.d_k), dtype=torch.float32, device="cuda:0")
+    o, _ = gdn.gdn_prefill_channel_gated(dev(c.q), dev(c.k), dev(c.v), dev(c.g), dev(c.beta), s0,
+                                         fin, cu_seqlens=dev(c.cu_seqlens), scale=c.scale,
+                                         workspace=workspace)
+    torch.cuda.synchronize()
+    return o, fin
+
+
+@pytest.mark.parametrize("T,init,Hk", [(1, True, 3), (63, False, 3), (64, True, 1), (130, True, 3),
+                                       (257, False, 1)])
+def test_channel_gated_chunk_ragged(T, init, Hk):
+    """Chunkwise per-channel path: partial chunks, with and without initial
+    states, grouped query/key heads."""
+    c = inputs.make_channel_gated(seed=120 + T, B=2, T=T, H=3, Hk=Hk, d=128, dtype="bf16")
+    o, fin = _channel_run(c, init=init)
+    o_ref, s_ref = _oracle_channel(c, init=init)
+    eo, es = o_err(o, o_ref), s_err(fin, s_ref)
+    report(f"channel chunk T={T} init={init} Hk={Hk}", o=eo, state=es)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_channel_gated_chunk_and_serial_agree():
+    """The chunkwise and token-serial per-channel paths on the same inputs,
+    both against the oracle."""
+    c = inputs.make_channel_gated(seed=131, B=2, T=200, H=4, Hk=2, d=128, dtype="bf16")
+    o_ref, s_ref = _oracle_channel(c)
+    for ws in ("auto", None):
+        o, fin = _channel_run(c, workspace=ws)
+        eo, es = o_err(o, o_ref), s_err(fin, s_ref)
+        report(f"channel {'chunk' if ws else 'serial'}", o=eo, state=es)
+        assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+@pytest.mark.parametrize("rate", [30.0, 200.0])
+def test_channel_gated_chunk_strong_decay(rate):
+    """Channels that decay by more than e^-80 inside 16 tokens take the exact
+    element-wise diagonal blocks; the others, in the same chunks, the
+    products. Both against the oracle."""
+    import dataclasses
+    c = inputs.make_channel_gated(seed=132, B=2, T=150, H=3, d=128, dtype="bf16")
+    g = c.g.clone()
+    g[:, :, :, :16] = -rate                  # 16 channels forget almost at once
+    g[:, 40:60, 1, 16:32] = -rate / 3.0      # a burst on one head
+    c = dataclasses.replace(c, g=g)
+    o, fin = _channel_run(c)
+    o_ref, s_ref = _oracle_channel(c)
+    eo, es = o_err(o, o_ref), s_err(fin, s_ref)
+    report(f"channel chunk strong decay {rate}", o=eo, state=es)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_channel_gated_chunk_packed_with_states():
+    c = inputs.make_channel_gated(seed=133, H=2, d=128, lengths=[64, 0, 1, 200, 65])
+    o, fin = _channel_run(c)
+    o_ref, s_ref = _oracle_channel(c)
+    cu = [int(x) for x in c.cu_seqlens.tolist()]
+    eo, es = o_err_packed(o, o_ref, cu), s_err(fin, s_ref)
+    report("channel chunk packed", o=eo, state=es)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+    assert torch.equal(fin[1].cpu(), c.s0[1])          # the empty sequence keeps its state
+
+
+def test_channel_gated_chunk_full_size():
+    """The per-channel workload bench.py times (B=4, T=4096, H=16, d=128),
+    every output and final state against the oracle."""
+    c = inputs.make_channel_gated(seed=7, B=4, T=4096, H=16, d=128, dtype="bf16", with_state=False)
+    o, fin = _channel_run(c, init=False)
+    o_ref, s_ref = _oracle_channel(c, init=False)
+    eo, es = o_err(o, o_ref), s_err(fin, s_ref)
+    report("channel chunk full size", o=eo, state=es)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
