@@ -682,14 +682,14 @@ def test_channel_gated_chunk_and_serial_agree():
 
 @pytest.mark.parametrize("rate", [30.0, 200.0])
 def test_channel_gated_chunk_strong_decay(rate):
-    """Channels that decay by more than e^-80 inside 16 tokens take the exact
-    element-wise diagonal blocks; the others, in the same chunks, the
-    products. Both against the oracle."""
+    """Chunks in which a channel decays by more than e^-80 inside 16 tokens
+    take the exact element-wise diagonal blocks, the others (other heads,
+    other chunks of the same head) the products; against the oracle."""
     import dataclasses
     c = inputs.make_channel_gated(seed=132, B=2, T=150, H=3, d=128, dtype="bf16")
     g = c.g.clone()
-    g[:, :, :, :16] = -rate                  # 16 channels forget almost at once
-    g[:, 40:60, 1, 16:32] = -rate / 3.0      # a burst on one head
+    g[:, :, 0, :16] = -rate                  # head 0: 16 channels forget almost at once
+    g[:, 40:60, 1, 16:32] = -rate / 3.0      # head 1: a burst in one chunk; head 2 as drawn
     c = dataclasses.replace(c, g=g)
     o, fin = _channel_run(c)
     o_ref, s_ref = _oracle_channel(c)
