@@ -746,14 +746,17 @@ chunk_prep_channel_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k
         if (tid == 0) *sFlag = 0;
         lds_barrier();
         {
+            // the totals of the earlier token groups, all read at once
             float off[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) off[e] = 0.f;
-            for (int u = 0; u < tg; ++u) {
+#pragma unroll
+            for (int u = 0; u < 15; ++u) {
                 const f32x4 a = *reinterpret_cast<const f32x4 *>(sTot + u * DK + 8 * c8);
                 const f32x4 b = *reinterpret_cast<const f32x4 *>(sTot + u * DK + 8 * c8 + 4);
+                const float w = u < tg ? 1.f : 0.f;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) { off[e] += a[e]; off[4 + e] += b[e]; }
+                for (int e = 0; e < 4; ++e) { off[e] += w * a[e]; off[4 + e] += w * b[e]; }
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j)
@@ -765,36 +768,55 @@ chunk_prep_channel_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k
             }
         }
         lds_barrier();
-        // ---- per-channel tables: e^{rho_1..4}; F21, F31, F32 = e^{rho_I -
-        //      rho_J}; G1..G3 = e^{rho_4 - rho_J} (rho_4 = gamma_63) ----
+        // ---- per-channel tables (rho_0 = 0, rho_4 = gamma_63):
+        //      0-2  e^{rho_1}, e^{rho_2}, e^{rho_3}
+        //      3-5  e^{rho_2 - rho_1}, e^{rho_3 - rho_2}, e^{rho_4 - rho_3}
+        //      6-9  e^{rho_I - rho_{I+1}}, I = 0..3: the inverse of block I's decay,
+        //           clamped at e^80; beyond it the item takes the exact
+        //           diagonal blocks ----
         for (int x = tid; x < 10 * DK; x += P_NT) {
             const int id = x / DK, c = x - id * DK;
             const float *r = sRho + c;         // r[(I - 1) * DK] = rho_I
             float ex;
-            if (id < 4) ex = r[id * DK];
-            else if (id == 4) ex = r[DK] - r[0];
-            else if (id == 5) ex = r[2 * DK] - r[0];
-            else if (id == 6) ex = r[2 * DK] - r[DK];
-            else ex = r[3 * DK] - r[(id - 7) * DK];
+            if (id < 3) ex = r[id * DK];
+            else if (id < 6) ex = r[(id - 2) * DK] - r[(id - 3) * DK];
+            else {
+                const int I2 = id - 6;
+                ex = (I2 ? r[(I2 - 1) * DK] : 0.f) - r[I2 * DK];
+                if (ex > CH_EXP_MAX) {
+                    *sFlag = 1;
+                    ex = CH_EXP_MAX;
+                }
+            }
             sTab[x] = __expf(ex);
         }
+        if (tg == 0) {                         // e^{gamma_63} of the thread's channels
+            float *ec = reinterpret_cast<float *>(dst + CH_EC) + 8 * c8;
+            const float *r4 = sRho + 3 * DK + 8 * c8;
+            *reinterpret_cast<f32x4 *>(ec) = f32x4{__expf(r4[0]), __expf(r4[1]), __expf(r4[2]), __expf(r4[3])};
+            *reinterpret_cast<f32x4 *>(ec + 4) = f32x4{__expf(r4[4]), __expf(r4[5]), __expf(r4[6]), __expf(r4[7])};
+        }
         lds_barrier();
-        // ---- the scaled copies of the thread's elements ----
-        {
+        // ---- the scaled copies of the thread's elements (wave I: tokens of
+        //      row block I; specialised per block so that only its copies are
+        //      formed) ----
+        auto scaled_copies = [&](auto IC) {
+            constexpr int BI = decltype(IC)::value;
             auto tab = [&](int id, int e) { return sTab[id * DK + 8 * c8 + e]; };
-            // per channel of the thread: rho_I, rho_{I+1}, e^{rho_I}, e^{rho_4 -
-            // rho_{I+1}} (K^), e^{rho_{I+2} - rho_{I+1}}, e^{rho_3 - rho_1}
-            float rho0[8], rho1[8], eI[8], gI[8], fI2[8], f31[8];
+            // per channel: rho_I, rho_{I+1}, e^{rho_I}, e^{rho_4 - rho_{I+1}} (K^),
+            // e^{rho_I - rho_{I+1}}, e^{rho_{I+2} - rho_{I+1}}, e^{rho_3 - rho_1}
+            float rho0[8], rho1[8], eI[8], gI[8], dI[8], fI2[8], f31[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                rho0[e] = I ? sRho[(I - 1) * DK + 8 * c8 + e] : 0.f;
-                rho1[e] = sRho[I * DK + 8 * c8 + e];
-                eI[e] = I ? tab(I - 1, e) : 1.f;
-                gI[e] = I < 3 ? tab(7 + I, e) : 1.f;
-                fI2[e] = I == 0 ? tab(4, e) : (I == 1 ? tab(6, e) : 0.f);
-                f31[e] = I == 0 ? tab(5, e) : 0.f;
+                rho0[e] = BI ? sRho[(BI - 1) * DK + 8 * c8 + e] : 0.f;
+                rho1[e] = sRho[BI * DK + 8 * c8 + e];
+                eI[e] = BI ? tab(BI - 1, e) : 1.f;
+                const float f21 = tab(3, e), f32 = tab(4, e), g3 = tab(5, e);
+                gI[e] = BI == 3 ? 1.f : BI == 2 ? g3 : BI == 1 ? g3 * f32 : g3 * f32 * f21;
+                dI[e] = tab(6 + BI, e);
+                fI2[e] = BI == 0 ? f21 : f32;
+                f31[e] = f21 * f32;
             }
-            bool big = false;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int t = 4 * tg + j;
@@ -802,40 +824,36 @@ chunk_prep_channel_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float rf = __expf(gm[j][e] - rho0[e]);
-                    const float dx = rho0[e] - gm[j][e];
-                    big |= dx > CH_EXP_MAX;
-                    const float df = __expf(dx < CH_EXP_MAX ? dx : CH_EXP_MAX);
                     const float nf = __expf(rho1[e] - gm[j][e]);
                     const float E = eI[e] * rf;
                     const float kk = (float)p.kr[j][e], qq2 = (float)p.qr[j][e];
                     kr[e] = (bf16)(kk * rf);
                     qr[e] = (bf16)(qq2 * rf);
-                    kd[e] = (bf16)(kk * df);
+                    kd[e] = (bf16)(kk * nf * dI[e]);   // e^{rho_I - gamma}
                     kp[e] = (bf16)(kk * E);
                     qp[e] = (bf16)(qq2 * E);
                     kh[e] = (bf16)(kk * nf * gI[e]);
-                    // KC_{I'} for I' > I: nf e^{rho_I' - rho_{I+1}}
-                    kc1[e] = (bf16)(kk * nf);                  // I' = I + 1
-                    kc2[e] = (bf16)(kk * nf * fI2[e]);         // I' = I + 2
-                    kc3[e] = (bf16)(kk * nf * f31[e]);         // I' = 3 (I = 0)
+                    if constexpr (BI <= 2) kc1[e] = (bf16)(kk * nf);            // KC_{I+1}
+                    if constexpr (BI <= 1) kc2[e] = (bf16)(kk * nf * fI2[e]);   // KC_{I+2}
+                    if constexpr (BI == 0) kc3[e] = (bf16)(kk * nf * f31[e]);   // KC_3
                 }
                 *reinterpret_cast<bf16x8 *>(smem + CP_KR + cp_off(t, c8)) = kr;
                 *reinterpret_cast<bf16x8 *>(smem + CP_QR + cp_off(t, c8)) = qr;
-                *reinterpret_cast<bf16x8 *>(smem + CP_KC + cp_off(kc_row0(I) + t, c8)) = kd;
-                if (I + 1 <= 3) *reinterpret_cast<bf16x8 *>(smem + CP_KC + cp_off(kc_row0(I + 1) + t, c8)) = kc1;
-                if (I + 2 <= 3) *reinterpret_cast<bf16x8 *>(smem + CP_KC + cp_off(kc_row0(I + 2) + t, c8)) = kc2;
-                if (I == 0) *reinterpret_cast<bf16x8 *>(smem + CP_KC + cp_off(kc_row0(3) + t, c8)) = kc3;
+                *reinterpret_cast<bf16x8 *>(smem + CP_KC + cp_off(kc_row0(BI) + t, c8)) = kd;
+                if constexpr (BI <= 2) *reinterpret_cast<bf16x8 *>(smem + CP_KC + cp_off(kc_row0(BI + 1) + t, c8)) = kc1;
+                if constexpr (BI <= 1) *reinterpret_cast<bf16x8 *>(smem + CP_KC + cp_off(kc_row0(BI + 2) + t, c8)) = kc2;
+                if constexpr (BI == 0) *reinterpret_cast<bf16x8 *>(smem + CP_KC + cp_off(kc_row0(3) + t, c8)) = kc3;
                 *reinterpret_cast<bf16x8 *>(dst + CH_KP + t * DK + 8 * c8) = kp;
                 *reinterpret_cast<bf16x8 *>(dst + CH_KH + t * DK + 8 * c8) = kh;
                 const int f = 4 * (t >> 4) + (c8 >> 2), ln = 16 * (c8 & 3) + (t & 15);
                 *reinterpret_cast<bf16x8 *>(dst + CH_QP + 512 * f + 8 * ln) = qp;
             }
-            if (big) *sFlag = 1;
-            if (tg == 0) {                     // e^{gamma_63} of the thread's channels
-                float *ec = reinterpret_cast<float *>(dst + CH_EC) + 8 * c8;
-                *reinterpret_cast<f32x4 *>(ec) = f32x4{tab(3, 0), tab(3, 1), tab(3, 2), tab(3, 3)};
-                *reinterpret_cast<f32x4 *>(ec + 4) = f32x4{tab(3, 4), tab(3, 5), tab(3, 6), tab(3, 7)};
-            }
+        };
+        switch (I) {
+        case 0: scaled_copies(std::integral_constant<int, 0>{}); break;
+        case 1: scaled_copies(std::integral_constant<int, 1>{}); break;
+        case 2: scaled_copies(std::integral_constant<int, 2>{}); break;
+        default: scaled_copies(std::integral_constant<int, 3>{}); break;
         }
         // the item's loads are consumed: the next item's are issued now and
         // overlap the products, the solve and the stores
