@@ -613,8 +613,10 @@ chunk_prep_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 // 16-token row block I, rho_I = gamma at the token before the block:
 // e^{gamma_i - gamma_j} = e^{gamma_i - rho_I} e^{rho_I - gamma_j}. The first
 // factor is <= 1; the second is <= 1 below the block diagonal and at most the
-// block's own decay on it (e^{rho_I - gamma_j}, j in block I). While every
-// channel decays by less than e^-80 inside every 16-token block of the item
+// block's own decay on it (e^{rho_I - gamma_j}, j in block I); these bounds hold
+// for gates in (0, 1] (g <= 0, gamma non-increasing), as the pages define the
+// decay. While every channel decays by less than e^-80 inside every 16-token
+// block of the item
 // (both factors then fit bf16 and fp32), the diagonal blocks come from the same
 // products; otherwise the item's diagonal blocks are summed element by element
 // with exact exponentials.
