@@ -718,3 +718,24 @@ def test_channel_gated_chunk_full_size():
     eo, es = o_err(o, o_ref), s_err(fin, s_ref)
     report("channel chunk full size", o=eo, state=es)
     assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_channel_gated_chunk_equal_channels_match_the_head_gate():
+    """Equal rates on every channel through the chunkwise per-channel path
+    give the scalar-gate chunkwise path's result, and both the oracle's."""
+    c = inputs.make_prefill(seed=134, B=2, T=300, H=4, d=128, dtype="bf16", with_state=True)
+    gc = c.g[..., None].expand(-1, -1, -1, 128).contiguous()
+    s0 = dev(c.s0)
+    f1 = torch.empty_like(s0)
+    f2 = torch.empty_like(s0)
+    o1, _ = gdn.gdn_prefill(dev(c.q), dev(c.k), dev(c.v), dev(c.g), dev(c.beta), s0, f1,
+                            scale=c.scale)
+    o2, _ = gdn.gdn_prefill_channel_gated(dev(c.q), dev(c.k), dev(c.v), dev(gc), dev(c.beta), s0,
+                                          f2, scale=c.scale)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_prefill(c)
+    e12 = o_err(o2, host64(o1))
+    report("channel chunk, equal channels vs head gate", o_vs_head=e12,
+           o=o_err(o2, o_ref), state=s_err(f2, s_ref))
+    assert e12 <= TOL_BF16
+    assert o_err(o2, o_ref) <= TOL_BF16 and s_err(f2, s_ref) <= TOL_BF16
