@@ -61,17 +61,29 @@ __global__ void state_copy_kernel(const float *src, float *dst, long n4)
 
 // Step 3. One workgroup per (sequence, head, block of 16 state rows); a lane
 // group of 16 lanes owns one row, 8 columns per lane. For s = 0 .. P-1:
-// inits[s] = S, then S <- S A_s + B_s (the row block of S staged in LDS, A_s
-// rows read by all row groups at once); finally final_state = S.
+// inits[s] = S, then S <- S A_s + B_s, with A_s staged in LDS (loaded into
+// registers one segment ahead, so that the next map's loads overlap this
+// segment's products) and the row block of S in LDS; finally final_state = S.
+constexpr int SC_LDS_BYTES = (SP_D * SP_D + 16 * (SP_D + 4)) * 4;
 __global__ void __launch_bounds__(256)
 seg_compose_kernel(const float *__restrict__ Amat, const float *__restrict__ Bmat,
                    const float *s_init, float *__restrict__ inits, float *s_final, int H, int P)
 {
-    __shared__ float sS[16][SP_D + 4];
+    extern __shared__ __attribute__((aligned(16))) float sm[];
+    float *sA = sm;                                  // [128][128]: A_s
+    float(*sS)[SP_D + 4] = reinterpret_cast<float(*)[SP_D + 4]>(sm + SP_D * SP_D);
     const int bh = blockIdx.x, b = bh / H, h = bh - b * H;
     const int tid = threadIdx.x, r = tid >> 4, l = tid & 15;
     const int row = blockIdx.y * 16 + r, c0 = 8 * l;
     const size_t mat = (size_t)SP_D * SP_D;
+    auto seg_of = [&](int s2) { return ((size_t)b * P + s2) * H + h; };
+    // A_s as 16 f32x4 per thread: elements 4 (tid + 256 i) ..
+    f32x4 ar[16];
+    auto load_a = [&](int s2) {
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(Amat + seg_of(s2) * mat);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ar[i] = src[tid + 256 * i];
+    };
     float cur[8];
     if (s_init) {
         const float *p = s_init + ((size_t)bh * SP_D + row) * SP_D + c0;
@@ -82,25 +94,28 @@ seg_compose_kernel(const float *__restrict__ Amat, const float *__restrict__ Bma
 #pragma unroll
         for (int e = 0; e < 8; ++e) cur[e] = 0.f;
     }
+    if (P > 0) load_a(0);
     for (int s = 0; s < P; ++s) {
-        const size_t seg = ((size_t)b * P + s) * H + h;
+        const size_t seg = seg_of(s);
         float *ip = inits + seg * mat + (size_t)row * SP_D + c0;
         *reinterpret_cast<f32x4 *>(ip) = f32x4{cur[0], cur[1], cur[2], cur[3]};
         *reinterpret_cast<f32x4 *>(ip + 4) = f32x4{cur[4], cur[5], cur[6], cur[7]};
 #pragma unroll
         for (int e = 0; e < 8; ++e) sS[r][c0 + e] = cur[e];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) reinterpret_cast<f32x4 *>(sA)[tid + 256 * i] = ar[i];
         __syncthreads();
+        if (s + 1 < P) load_a(s + 1);          // in flight during the products
         const float *bp = Bmat + seg * mat + (size_t)row * SP_D + c0;
         const f32x4 b0 = *reinterpret_cast<const f32x4 *>(bp), b1 = *reinterpret_cast<const f32x4 *>(bp + 4);
         float acc[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) { acc[e] = b0[e]; acc[4 + e] = b1[e]; }
-        const float *ap = Amat + seg * mat + c0;
-#pragma unroll 4
+#pragma unroll 8
         for (int j = 0; j < SP_D; ++j) {
             const float sj = sS[r][j];
-            const f32x4 a0 = *reinterpret_cast<const f32x4 *>(ap + (size_t)j * SP_D);
-            const f32x4 a1 = *reinterpret_cast<const f32x4 *>(ap + (size_t)j * SP_D + 4);
+            const f32x4 a0 = *reinterpret_cast<const f32x4 *>(sA + j * SP_D + c0);
+            const f32x4 a1 = *reinterpret_cast<const f32x4 *>(sA + j * SP_D + c0 + 4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 acc[e] += sj * a0[e];
@@ -109,7 +124,7 @@ seg_compose_kernel(const float *__restrict__ Amat, const float *__restrict__ Bma
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) cur[e] = acc[e];
-        __syncthreads();                       // sS read before the next segment's write
+        __syncthreads();                       // sS and sA read before the next segment's writes
     }
     if (s_final) {
         float *p = s_final + ((size_t)bh * SP_D + row) * SP_D + c0;
@@ -181,9 +196,14 @@ hipError_t launch_prefill_seqpar(const void *q, const void *k, const void *v, co
         e = launch_prefill_apply(q, k, v, g, nullptr, Am, nullptr, cu, total, H, Hk, nseg, scale,
                                  prep, stream, split::CHAIN_ZERO_V | split::CHAIN_INIT_IDENTITY);
     if (e == hipSuccess) {        // 3: the start states, in order
-        hipLaunchKernelGGL(seg_compose_kernel, dim3((unsigned)(B * H), SP_D / 16), dim3(256), 0,
-                           stream, Am, Bm, s_init, In, s_final, H, P);
-        e = hipGetLastError();
+        static const hipError_t attr = hipFuncSetAttribute(
+            (const void *)seg_compose_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, SC_LDS_BYTES);
+        e = attr;
+        if (e == hipSuccess) {
+            hipLaunchKernelGGL(seg_compose_kernel, dim3((unsigned)(B * H), SP_D / 16), dim3(256),
+                               SC_LDS_BYTES, stream, Am, Bm, s_init, In, s_final, H, P);
+            e = hipGetLastError();
+        }
     }
     if (e == hipSuccess)          // 4: the outputs
         e = launch_prefill_apply(q, k, v, g, In, nullptr, o, cu, total, H, Hk, nseg, scale, prep,
