@@ -29,7 +29,10 @@
  *    H is the ungrouped layer. A bad pair gives GDN_ERR_SHAPE.
  *  - States are fp32, [N][H][d_v][d_k] with d_k contiguous.
  *  - The decay gate is passed in log space: g = log(alpha), fp32 (alpha =
- *    exp(g) <= 1 for g <= 0). beta is fp32, one scalar per (token, head).
+ *    exp(g) <= 1 for g <= 0). g must be finite; the chunkwise paths split
+ *    decay factors into pieces bounded by 1, which holds for g <= 0, the
+ *    pages' gate range (alpha in (0, 1]). beta is fp32, one scalar per
+ *    (token, head).
  *  - dtype (gdn_dtype_t) selects the storage type of q, k, v and of the
  *    output o: GDN_DTYPE_F32 or GDN_DTYPE_BF16. All arithmetic accumulates in
  *    fp32; bf16 tensors are rounded to nearest-even on store.
