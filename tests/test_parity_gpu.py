@@ -739,3 +739,19 @@ def test_channel_gated_chunk_equal_channels_match_the_head_gate():
            o=o_err(o2, o_ref), state=s_err(f2, s_ref))
     assert e12 <= TOL_BF16
     assert o_err(o2, o_ref) <= TOL_BF16 and s_err(f2, s_ref) <= TOL_BF16
+
+
+def test_channel_gated_chunk_strong_decay_packed():
+    """The exact diagonal blocks in packed sequences (partial chunks at every
+    sequence end), against the oracle."""
+    import dataclasses
+    c = inputs.make_channel_gated(seed=135, H=2, d=128, lengths=[70, 1, 130, 0, 33])
+    g = c.g.clone()
+    g[:, :, 1, 64:96] = -50.0                # head 1: 32 channels forget at once
+    c = dataclasses.replace(c, g=g)
+    o, fin = _channel_run(c)
+    o_ref, s_ref = _oracle_channel(c)
+    cu = [int(x) for x in c.cu_seqlens.tolist()]
+    eo, es = o_err_packed(o, o_ref, cu), s_err(fin, s_ref)
+    report("channel chunk strong decay packed", o=eo, state=es)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
