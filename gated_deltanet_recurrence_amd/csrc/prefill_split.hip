@@ -801,27 +801,32 @@ chunk_prep_channel_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k
         lds_barrier();
         // ---- the scaled copies of the thread's elements (wave I: tokens of
         //      row block I; specialised per block so that only its copies are
-        //      formed) ----
+        //      formed). The operands of the diagonal block (I, I) of P are also
+        //      split into bf16 hi + lo parts; the lo parts stay in registers ----
+        bf16x8 qlo[4], dlo[4];
         auto scaled_copies = [&](auto IC) {
             constexpr int BI = decltype(IC)::value;
             auto tab = [&](int id, int e) { return sTab[id * DK + 8 * c8 + e]; };
-            // per channel: rho_I, rho_{I+1}, e^{rho_I}, e^{rho_4 - rho_{I+1}} (K^),
-            // e^{rho_I - rho_{I+1}}, e^{rho_{I+2} - rho_{I+1}}, e^{rho_3 - rho_1}
-            float rho0[8], rho1[8], eI[8], gI[8], dI[8], fI2[8], f31[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                rho0[e] = BI ? sRho[(BI - 1) * DK + 8 * c8 + e] : 0.f;
-                rho1[e] = sRho[BI * DK + 8 * c8 + e];
-                eI[e] = BI ? tab(BI - 1, e) : 1.f;
-                const float f21 = tab(3, e), f32 = tab(4, e), g3 = tab(5, e);
-                gI[e] = BI == 3 ? 1.f : BI == 2 ? g3 : BI == 1 ? g3 * f32 : g3 * f32 * f21;
-                dI[e] = tab(6 + BI, e);
-                fI2[e] = BI == 0 ? f21 : f32;
-                f31[e] = f21 * f32;
-            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int t = 4 * tg + j;
+                // per channel: rho_I, rho_{I+1}, e^{rho_I}, e^{rho_4 - rho_{I+1}} (K^),
+                // e^{rho_I - rho_{I+1}}, e^{rho_{I+2} - rho_{I+1}}, e^{rho_3 - rho_1};
+                // read again for each token (the clobber keeps them from being
+                // held in registers over the four)
+                asm volatile("" ::: "memory");
+                float rho0[8], rho1[8], eI[8], gI[8], dI[8], fI2[8], f31[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    rho0[e] = BI ? sRho[(BI - 1) * DK + 8 * c8 + e] : 0.f;
+                    rho1[e] = sRho[BI * DK + 8 * c8 + e];
+                    eI[e] = BI ? tab(BI - 1, e) : 1.f;
+                    const float f21 = tab(3, e), f32 = tab(4, e), g3 = tab(5, e);
+                    gI[e] = BI == 3 ? 1.f : BI == 2 ? g3 : BI == 1 ? g3 * f32 : g3 * f32 * f21;
+                    dI[e] = tab(6 + BI, e);
+                    fI2[e] = BI == 0 ? f21 : f32;
+                    f31[e] = f21 * f32;
+                }
                 bf16x8 kr, qr, kd, kp, kh, qp, kc1, kc2, kc3;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -829,9 +834,12 @@ chunk_prep_channel_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k
                     const float nf = __expf(rho1[e] - gm[j][e]);
                     const float E = eI[e] * rf;
                     const float kk = (float)p.kr[j][e], qq2 = (float)p.qr[j][e];
+                    const float vq = qq2 * rf, vd = kk * nf * dI[e];   // e^{rho_I - gamma}
                     kr[e] = (bf16)(kk * rf);
-                    qr[e] = (bf16)(qq2 * rf);
-                    kd[e] = (bf16)(kk * nf * dI[e]);   // e^{rho_I - gamma}
+                    qr[e] = (bf16)vq;
+                    kd[e] = (bf16)vd;
+                    qlo[j][e] = (bf16)(vq - (float)qr[e]);
+                    dlo[j][e] = (bf16)(vd - (float)kd[e]);
                     kp[e] = (bf16)(kk * E);
                     qp[e] = (bf16)(qq2 * E);
                     kh[e] = (bf16)(kk * nf * gI[e]);
@@ -857,30 +865,68 @@ chunk_prep_channel_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k
         case 2: scaled_copies(std::integral_constant<int, 2>{}); break;
         default: scaled_copies(std::integral_constant<int, 3>{}); break;
         }
+        // ---- wave I, diagonal block (I, I) of M (dM) and of P^T (dP). Its
+        //      operands are rows this wave wrote and only it reads, so it is
+        //      summed before the workgroup barrier. P's block is summed as
+        //      hi hi + hi lo + lo hi, which keeps fp32-level products: with
+        //      bf16 operands alone an entry loses its relative precision where
+        //      q_i k_j nearly cancels, and P weights the outputs directly (a
+        //      one-token sequence's output is P_00 Delta_0). M's block enters
+        //      the outputs only through T, against v, and keeps bf16 operands.
+        //      ak, aq (rows 16 I + m of KR, QR) stay in registers for the
+        //      off-diagonal blocks; the lo parts are written over the QR and
+        //      KC rows once these are read ----
+        unsigned char *kcI = smem + CP_KC + kc_row0(I) * CP_ROW;
+        bf16x8 ak[4], aq[4];
+        f32x4 dM = f32x4{0.f, 0.f, 0.f, 0.f}, dP = dM;
+        {
+            bf16x8 bd[4];
+            wave_lds_order();
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int gr = 4 * s + kq;
+                ak[s] = *reinterpret_cast<const bf16x8 *>(smem + CP_KR + cp_off(16 * I + m, gr));
+                aq[s] = *reinterpret_cast<const bf16x8 *>(smem + CP_QR + cp_off(16 * I + m, gr));
+                bd[s] = *reinterpret_cast<const bf16x8 *>(kcI + cp_off(16 * I + m, gr));
+                dM = mfma16(ak[s], bd[s], dM);
+                dP = mfma16(bd[s], aq[s], dP);
+            }
+            wave_lds_order();
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = 4 * tg + j;
+                *reinterpret_cast<bf16x8 *>(smem + CP_QR + cp_off(t, c8)) = qlo[j];
+                *reinterpret_cast<bf16x8 *>(kcI + cp_off(t, c8)) = dlo[j];
+            }
+            wave_lds_order();
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int gr = 4 * s + kq;
+                const bf16x8 ql = *reinterpret_cast<const bf16x8 *>(smem + CP_QR + cp_off(16 * I + m, gr));
+                const bf16x8 dl = *reinterpret_cast<const bf16x8 *>(kcI + cp_off(16 * I + m, gr));
+                dP = mfma16(dl, aq[s], mfma16(bd[s], ql, dP));
+            }
+        }
         // the item's loads are consumed: the next item's are issued now and
         // overlap the products, the solve and the stores
         fetch(nit, pn);
         ait = prep_locate(cu_seqlens, after, nitems, T, H, N);
         lds_barrier();
-        // ---- wave I: row block I of M (accM[J]) and of P^T (accP[J], rows =
-        //      keys 16 J + .., columns = queries 16 I + ..), J <= I ----
-        f32x4 accM[4], accP[4];
+        // ---- wave I: off-diagonal blocks J < I of row block I of M (accM[J])
+        //      and of P^T (accP[J], rows = keys 16 J + .., columns = queries
+        //      16 I + ..) ----
+        f32x4 accM[3], accP[3];
 #pragma unroll
-        for (int J = 0; J < 4; ++J) { accM[J] = f32x4{0.f, 0.f, 0.f, 0.f}; accP[J] = accM[J]; }
-        {
-            const unsigned char *kcI = smem + CP_KC + kc_row0(I) * CP_ROW;
+        for (int J = 0; J < 3; ++J) { accM[J] = f32x4{0.f, 0.f, 0.f, 0.f}; accP[J] = accM[J]; }
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int gr = 4 * s + kq;
-                const bf16x8 ak = *reinterpret_cast<const bf16x8 *>(smem + CP_KR + cp_off(16 * I + m, gr));
-                const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(smem + CP_QR + cp_off(16 * I + m, gr));
+        for (int s = 0; s < 4; ++s) {
+            const int gr = 4 * s + kq;
 #pragma unroll
-                for (int J = 0; J < 4; ++J) {
-                    if (J > I) break;          // uniform
-                    const bf16x8 b = *reinterpret_cast<const bf16x8 *>(kcI + cp_off(16 * J + m, gr));
-                    accM[J] = mfma16(ak, b, accM[J]);
-                    accP[J] = mfma16(b, aq, accP[J]);
-                }
+            for (int J = 0; J < 3; ++J) {
+                if (J >= I) break;             // uniform
+                const bf16x8 b = *reinterpret_cast<const bf16x8 *>(kcI + cp_off(16 * J + m, gr));
+                accM[J] = mfma16(ak[s], b, accM[J]);
+                accP[J] = mfma16(b, aq[s], accP[J]);
             }
         }
         lds_barrier();                         // operand tiles read
@@ -929,8 +975,8 @@ chunk_prep_channel_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k
                         sp += (float)sQr[qi * DK + c] * (float)sKr[kj * DK + c] *
                               __expf(sG[qi * DK + c] - sG[kj * DK + c]);
                 }
-                accM[I][r] = sm;
-                accP[I][r] = sp;
+                dM[r] = sm;
+                dP[r] = sp;
             }
             lds_barrier();                     // scratch read before A is written over it
         }
@@ -940,10 +986,11 @@ chunk_prep_channel_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
             if (J > I) break;
+            const f32x4 aM = J == I ? dM : accM[J < 3 ? J : 0], aP = J == I ? dP : accP[J < 3 ? J : 0];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * I + 4 * kq + r, j = 16 * J + m;
-                const float a = j < i ? -sBeta[i] * accM[J][r] : 0.f;
+                const float a = j < i ? -sBeta[i] * aM[r] : 0.f;
                 if (J == I) sY[I * P_DB + (4 * kq + r) * 16 + m] = a;
                 else if (j < 48) sA[(i - 16) * P_LD_A2 + j] = a;
             }
@@ -951,7 +998,7 @@ chunk_prep_channel_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k
             const int qi = 16 * I + m;
             bf16x4 x;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) x[r] = (bf16)(16 * J + 4 * kq + r <= qi ? accP[J][r] : 0.f);
+            for (int r = 0; r < 4; ++r) x[r] = (bf16)(16 * J + 4 * kq + r <= qi ? aP[r] : 0.f);
             bf16 *prow = dst + 8 * WS_TWU + (qi < 32 ? 32 * qi : 1024 + 64 * (qi - 32));
             *reinterpret_cast<bf16x4 *>(prow + 16 * J + 4 * kq) = x;
         }

@@ -755,3 +755,24 @@ def test_channel_gated_chunk_strong_decay_packed():
     eo, es = o_err_packed(o, o_ref, cu), s_err(fin, s_ref)
     report("channel chunk strong decay packed", o=eo, state=es)
     assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_channel_gated_chunk_near_orthogonal_query_key():
+    """Short packed sequences whose queries are nearly orthogonal to the keys
+    of their own 16-token block: the intra-block products q_i k_j nearly
+    cancel, so the output of a one-token sequence (P_00 Delta_0, no initial
+    state) is small and carries the full relative error of P_00. Against
+    the oracle, per sequence and head."""
+    import dataclasses
+    c = inputs.make_channel_gated(seed=136, H=2, d=128, lengths=[1, 2, 1, 3, 16, 1, 17])
+    q = c.q.float()
+    k = c.k.float()
+    kn = k / k.norm(dim=-1, keepdim=True).clamp_min(1e-6)
+    q = q - (q * kn).sum(-1, keepdim=True) * kn + 0.02 * q.norm(dim=-1, keepdim=True) * kn
+    c = dataclasses.replace(c, q=q.to(c.q.dtype))
+    o, fin = _channel_run(c, init=False)
+    o_ref, s_ref = _oracle_channel(c, init=False)
+    cu = [int(x) for x in c.cu_seqlens.tolist()]
+    eo, es = o_err_packed(o, o_ref, cu), s_err(fin, s_ref)
+    report("channel chunk near-orthogonal q, k", o=eo, state=es)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
