@@ -277,7 +277,9 @@ int gdn_decode_step(const void *q, const void *k, const void *v,
  * 64-token chunk, the keys and queries carry the decay channel by channel
  * (K e^gamma, K e^{gamma_63 - gamma}, Q e^gamma), the in-chunk products
  * sum_c k_i[c] k_j[c] e^{gamma_i[c] - gamma_j[c]} are split at a reference
- * token per 16-token block so that they run on the matrix cores, and the
+ * token per 16-token block so that they run on the matrix cores (the
+ * query-key sums of a block with itself from bf16 hi + lo operand splits, so
+ * that nearly cancelling sums keep their relative precision), and the
  * state decays by e^{gamma_63} per channel at each chunk end. Otherwise
  * (no workspace, fp32, other head sizes) the token-serial fp32 recurrence.
  */
