@@ -739,8 +739,33 @@ chunk_prep_channel_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k
                 const float x = e < 4 ? p.gr[2 * j][e] : p.gr[2 * j + 1][e - 4];
                 gm[j][e] = j ? gm[j - 1][e] + x : x;
             }
-        *reinterpret_cast<f32x4 *>(sTot + tg * DK + 8 * c8) = f32x4{gm[3][0], gm[3][1], gm[3][2], gm[3][3]};
-        *reinterpret_cast<f32x4 *>(sTot + tg * DK + 8 * c8 + 4) = f32x4{gm[3][4], gm[3][5], gm[3][6], gm[3][7]};
+        // the wave's four token groups of the same channels sit 16 lanes
+        // apart: an inclusive scan over them by two lane shifts, then the
+        // wave totals (row 3) through LDS for the later waves
+        float inc[8];
+        {
+            const int row = (tid & 63) >> 4;
+            auto from = [&](int dl, float v) {
+                return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                    4 * (((tid & 63) - dl) & 63), __builtin_bit_cast(int, v)));
+            };
+#pragma unroll
+            for (int e = 0; e < 8; ++e) inc[e] = gm[3][e];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float t = from(16, inc[e]);
+                if (row >= 1) inc[e] += t;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float t = from(32, inc[e]);
+                if (row >= 2) inc[e] += t;
+            }
+            if (row == 3) {
+                *reinterpret_cast<f32x4 *>(sTot + wave * DK + 8 * c8) = f32x4{inc[0], inc[1], inc[2], inc[3]};
+                *reinterpret_cast<f32x4 *>(sTot + wave * DK + 8 * c8 + 4) = f32x4{inc[4], inc[5], inc[6], inc[7]};
+            }
+        }
         if (tid < C) {
             sBeta[tid] = p.bv;
             sNegBeta[tid] = -p.bv;
@@ -748,17 +773,16 @@ chunk_prep_channel_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k
         if (tid == 0) *sFlag = 0;
         lds_barrier();
         {
-            // the totals of the earlier token groups, all read at once
+            // the group's offset: the earlier groups of its wave, then the
+            // totals of the earlier waves
             float off[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) off[e] = 0.f;
+            for (int e = 0; e < 8; ++e) off[e] = inc[e] - gm[3][e];
+            for (int w = 0; w < wave; ++w) {   // uniform
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(sTot + w * DK + 8 * c8);
+                const f32x4 b = *reinterpret_cast<const f32x4 *>(sTot + w * DK + 8 * c8 + 4);
 #pragma unroll
-            for (int u = 0; u < 15; ++u) {
-                const f32x4 a = *reinterpret_cast<const f32x4 *>(sTot + u * DK + 8 * c8);
-                const f32x4 b = *reinterpret_cast<const f32x4 *>(sTot + u * DK + 8 * c8 + 4);
-                const float w = u < tg ? 1.f : 0.f;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) { off[e] += w * a[e]; off[4 + e] += w * b[e]; }
+                for (int e = 0; e < 4; ++e) { off[e] += a[e]; off[4 + e] += b[e]; }
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j)
@@ -776,21 +800,28 @@ chunk_prep_channel_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k
         //      6-9  e^{rho_I - rho_{I+1}}, I = 0..3: the inverse of block I's decay,
         //           clamped at e^80; beyond it the item takes the exact
         //           diagonal blocks ----
-        for (int x = tid; x < 10 * DK; x += P_NT) {
-            const int id = x / DK, c = x - id * DK;
-            const float *r = sRho + c;         // r[(I - 1) * DK] = rho_I
-            float ex;
-            if (id < 3) ex = r[id * DK];
-            else if (id < 6) ex = r[(id - 2) * DK] - r[(id - 3) * DK];
-            else {
-                const int I2 = id - 6;
-                ex = (I2 ? r[(I2 - 1) * DK] : 0.f) - r[I2 * DK];
-                if (ex > CH_EXP_MAX) {
-                    *sFlag = 1;
-                    ex = CH_EXP_MAX;
+        //      (all exponents read before any table entry or the flag is
+        //      written, so that the five entries of a thread are independent)
+        {
+            static_assert(10 * DK == 5 * P_NT, "five table entries per thread");
+            float ex[5];
+            bool big = false;
+#pragma unroll
+            for (int u = 0; u < 5; ++u) {
+                const int x = tid + P_NT * u, id = x / DK, c = x - id * DK;
+                const float *r = sRho + c;     // r[(I - 1) * DK] = rho_I
+                if (id < 3) ex[u] = r[id * DK];
+                else if (id < 6) ex[u] = r[(id - 2) * DK] - r[(id - 3) * DK];
+                else {
+                    const int I2 = id - 6;
+                    const float e2 = (I2 ? r[(I2 - 1) * DK] : 0.f) - r[I2 * DK];
+                    big = big || e2 > CH_EXP_MAX;
+                    ex[u] = e2 > CH_EXP_MAX ? CH_EXP_MAX : e2;
                 }
             }
-            sTab[x] = __expf(ex);
+#pragma unroll
+            for (int u = 0; u < 5; ++u) sTab[tid + P_NT * u] = __expf(ex[u]);
+            if (big) *sFlag = 1;
         }
         if (tg == 0) {                         // e^{gamma_63} of the thread's channels
             float *ec = reinterpret_cast<float *>(dst + CH_EC) + 8 * c8;
@@ -983,6 +1014,9 @@ chunk_prep_channel_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k
         // ---- A = -strict_lower(diag(beta) M) into sY (diagonal blocks) and
         //      sA (rows 16-63, columns 0-47); P (queries x keys, lower incl.)
         //      straight to the workspace ----
+        float nbeta[4];                        // -beta of rows 16 I + 4 kq + r, read once
+#pragma unroll
+        for (int r = 0; r < 4; ++r) nbeta[r] = sNegBeta[16 * I + 4 * kq + r];
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
             if (J > I) break;
@@ -990,7 +1024,7 @@ chunk_prep_channel_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * I + 4 * kq + r, j = 16 * J + m;
-                const float a = j < i ? -sBeta[i] * aM[r] : 0.f;
+                const float a = j < i ? nbeta[r] * aM[r] : 0.f;
                 if (J == I) sY[I * P_DB + (4 * kq + r) * 16 + m] = a;
                 else if (j < 48) sA[(i - 16) * P_LD_A2 + j] = a;
             }
