@@ -624,13 +624,17 @@ chunk_prep_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 // One item per loop step per workgroup of 4 waves; thread (c8, tg) = (tid %
 // 16, tid / 16) owns tokens 4 tg .. 4 tg + 3 and channels 8 c8 .. 8 c8 + 7
 // (wave I owns row block I), loads them (the next item's loads are issued
-// while the current item computes), scans gamma, and writes every scaled copy
-// of its elements: LDS operand tiles (KR = K e^{gamma - rho_I}, QR likewise,
-// KC_I = K e^{rho_I - gamma} over tokens 0 .. 16 I + 15 for each I), and K+,
-// K^, Q+ to the workspace. Wave I then forms row block I of M and of P^T on
-// the matrix cores (16x16x32 bf16, operand tiles with 256-byte rows and
-// 16-byte chunks XOR-swizzled by the row); the triangular solve and the T
-// stores are those of the scalar prep pass (with -T_u in the -T_w slot).
+// while the current item computes), scans gamma (its four tokens in
+// registers, the wave's four token groups by lane shifts, the earlier waves'
+// totals through LDS), and writes every scaled copy of its elements: LDS
+// operand tiles (KR = K e^{gamma - rho_I}, QR likewise, KC_I = K e^{rho_I -
+// gamma} over tokens 0 .. 16 I + 15 for each I), and K+, K^, Q+ to the
+// workspace. Wave I then forms row block I of M and of P^T on the matrix cores
+// (16x16x32 bf16, operand tiles with 256-byte rows and 16-byte chunks
+// XOR-swizzled by the row): the diagonal block from its own rows before the
+// workgroup barrier (P's with bf16 hi + lo operand splits), the blocks left
+// of it after. The triangular solve and the T stores are those of the scalar
+// prep pass (with -T_u in the -T_w slot).
 // Workspace item (CH_ITEM_ELEMS bf16): pieces of -T_u and T_u, P, as in the
 // scalar item; then K+ and K^ ([64][128] row-major); Q+ in the output waves'
 // operand order (fragment f = 4 (t / 16) + c / 32 of 1 KiB, lane 16 ((c / 8)
