@@ -396,21 +396,27 @@ def bench_copy(steps, warmup, nbytes=1 << 30):
                 GBps=round(2 * nbytes / (ms * 1e-3) / 1e9, 1))
 
 
-def cpu_baseline():
+def cpu_baseline(min_seconds=10.0, max_runs=100):
     """fp64 oracle on the prefill workload's host arrays (all 4 x 16 chains of
-    4096 tokens), timed once after a small warm-up run."""
+    4096 tokens), run back to back after a small warm-up until at least
+    `min_seconds` of wall time have passed; the rate is the mean over the runs."""
     import oracle
     from gated_deltanet_recurrence_amd import inputs
     c = inputs.make_prefill()
     oracle.gdn_recurrent(c.q[:1, :64], c.k[:1, :64], c.v[:1, :64], c.g[:1, :64],
                          c.beta[:1, :64], None, None, c.scale)
+    runs = 0
     t = time.perf_counter()
-    oracle.gdn_recurrent(c.q, c.k, c.v, c.g, c.beta, None, None, c.scale)
-    dt = time.perf_counter() - t
-    return {"value": round(c.B * c.T / dt, 1), "unit": "tokens/s", "cores": oracle.num_threads(),
+    while True:
+        oracle.gdn_recurrent(c.q, c.k, c.v, c.g, c.beta, None, None, c.scale)
+        runs += 1
+        dt = time.perf_counter() - t
+        if dt >= min_seconds or runs >= max_runs:
+            break
+    return {"value": round(runs * c.B * c.T / dt, 1), "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": "the whole prefill workload (B=4, T=4096, H=16, d=128) once, fp64 "
-                      f"token recurrence, {dt:.2f} s"}
+            "sample": f"the whole prefill workload (B=4, T=4096, H=16, d=128), {runs} runs back to "
+                      f"back, fp64 token recurrence, {dt:.1f} s in all"}
 
 
 def main():
