@@ -776,3 +776,44 @@ def test_channel_gated_chunk_near_orthogonal_query_key():
     eo, es = o_err_packed(o, o_ref, cu), s_err(fin, s_ref)
     report("channel chunk near-orthogonal q, k", o=eo, state=es)
     assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_prefill_and_decode_replay_from_a_captured_graph():
+    """The two-pass prefill (caller workspace) and a decode step captured into
+    one HIP graph: the library allocates nothing and clears nothing with
+    memset nodes, so every replay (three, with eager work and synchronisation
+    between them) gives the eager results bit for bit."""
+    c = inputs.make_prefill(seed=150, B=2, T=300, H=4, d=128, dtype="bf16", with_state=True)
+    q, k, v, g, b = dev(c.q), dev(c.k), dev(c.v), dev(c.g), dev(c.beta)
+    s0 = dev(c.s0)
+    ws = torch.empty(gdn.gdn_prefill_workspace_size(2, 300, 4, 128, 128, 2, 0, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda:0")
+    o, fin, st = torch.empty_like(v), torch.empty_like(s0), torch.empty_like(s0)
+    q1, k1, v1, g1, b1 = (x[:, -1].contiguous() for x in (q, k, v, g, b))
+    o1 = torch.empty_like(v1)
+
+    def step():
+        gdn.gdn_prefill(q, k, v, g, b, s0, fin, o, scale=c.scale, workspace=ws)
+        torch.add(fin, 0.0, out=st)            # the decode step updates its own copy
+        gdn.gdn_decode_step(q1, k1, v1, g1, b1, st, o1, scale=c.scale)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (o, fin, st, o1)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        for x in (o, fin, st, o1):
+            x.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((o, fin, st, o1), ref):
+            assert torch.equal(got, want)
