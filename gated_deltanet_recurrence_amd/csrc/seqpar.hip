@@ -59,78 +59,72 @@ __global__ void state_copy_kernel(const float *src, float *dst, long n4)
             src ? reinterpret_cast<const f32x4 *>(src)[i] : f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-// Step 3. One workgroup per (sequence, head, block of 16 state rows); a lane
-// group of 16 lanes owns one row, 8 columns per lane. For s = 0 .. P-1:
-// inits[s] = S, then S <- S A_s + B_s, with A_s staged in LDS (loaded into
-// registers one segment ahead, so that the next map's loads overlap this
-// segment's products) and the row block of S in LDS; finally final_state = S.
-constexpr int SC_LDS_BYTES = (SP_D * SP_D + 16 * (SP_D + 4)) * 4;
-__global__ void __launch_bounds__(256)
+// Step 3. One workgroup of 8 waves per (sequence, head, block of 16 state
+// rows), the row block of S in LDS. For s = 0 .. P-1: inits[s] = S, then
+// S <- S A_s + B_s on the fp32 matrix cores (v_mfma_f32_16x16x4f32), wave w
+// forming columns 16 w .. 16 w + 15. The k index of the product is dealt as
+// k = 32 (lane / 16) + q over the 32 k-steps q, so that a lane's S operands
+// are 32 consecutive floats of its row (eight 16-byte LDS reads) and its A_s
+// operands one column of rows 32 (lane / 16) .. + 31, read from memory one
+// segment ahead; two accumulators halve the dependent chain.
+constexpr int SC_NT = 512;
+constexpr int SC_LDS_BYTES = 16 * (SP_D + 4) * 4;
+__global__ void __launch_bounds__(SC_NT)
 seg_compose_kernel(const float *__restrict__ Amat, const float *__restrict__ Bmat,
                    const float *s_init, float *__restrict__ inits, float *s_final, int H, int P)
 {
     extern __shared__ __attribute__((aligned(16))) float sm[];
-    float *sA = sm;                                  // [128][128]: A_s
-    float(*sS)[SP_D + 4] = reinterpret_cast<float(*)[SP_D + 4]>(sm + SP_D * SP_D);
+    float(*sS)[SP_D + 4] = reinterpret_cast<float(*)[SP_D + 4]>(sm);
     const int bh = blockIdx.x, b = bh / H, h = bh - b * H;
-    const int tid = threadIdx.x, r = tid >> 4, l = tid & 15;
-    const int row = blockIdx.y * 16 + r, c0 = 8 * l;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int m = lane & 15, kq = lane >> 4;
+    const int r0 = blockIdx.y * 16, col = 16 * wave + m;
+    const int vr = tid >> 5, vc = 4 * (tid & 31);      // this thread's 16-byte piece of the row block
     const size_t mat = (size_t)SP_D * SP_D;
     auto seg_of = [&](int s2) { return ((size_t)b * P + s2) * H + h; };
-    // A_s as 16 f32x4 per thread: elements 4 (tid + 256 i) ..
-    f32x4 ar[16];
-    auto load_a = [&](int s2) {
-        const f32x4 *src = reinterpret_cast<const f32x4 *>(Amat + seg_of(s2) * mat);
+    auto load_a = [&](int s2, float (&dst)[32]) {
+        const float *a = Amat + seg_of(s2) * mat + (size_t)(32 * kq) * SP_D + col;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) ar[i] = src[tid + 256 * i];
+        for (int q = 0; q < 32; ++q) dst[q] = a[(size_t)q * SP_D];
     };
-    float cur[8];
-    if (s_init) {
-        const float *p = s_init + ((size_t)bh * SP_D + row) * SP_D + c0;
-        const f32x4 x0 = *reinterpret_cast<const f32x4 *>(p), x1 = *reinterpret_cast<const f32x4 *>(p + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { cur[e] = x0[e]; cur[4 + e] = x1[e]; }
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) cur[e] = 0.f;
-    }
-    if (P > 0) load_a(0);
-    for (int s = 0; s < P; ++s) {
+    *reinterpret_cast<f32x4 *>(&sS[vr][vc]) =
+        s_init ? *reinterpret_cast<const f32x4 *>(s_init + ((size_t)bh * SP_D + r0 + vr) * SP_D + vc)
+               : f32x4{0.f, 0.f, 0.f, 0.f};
+    __syncthreads();
+    // one segment with the A_s operands in `cur`; the next segment's go to `nxt`
+    auto step = [&](int s, const float (&cur)[32], float (&nxt)[32]) {
         const size_t seg = seg_of(s);
-        float *ip = inits + seg * mat + (size_t)row * SP_D + c0;
-        *reinterpret_cast<f32x4 *>(ip) = f32x4{cur[0], cur[1], cur[2], cur[3]};
-        *reinterpret_cast<f32x4 *>(ip + 4) = f32x4{cur[4], cur[5], cur[6], cur[7]};
+        *reinterpret_cast<f32x4 *>(inits + seg * mat + (size_t)(r0 + vr) * SP_D + vc) =
+            *reinterpret_cast<const f32x4 *>(&sS[vr][vc]);
+        if (s + 1 < P) load_a(s + 1, nxt);
+        const float *bp = Bmat + seg * mat + (size_t)(r0 + 4 * kq) * SP_D + col;
+        float bv[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sS[r][c0 + e] = cur[e];
+        for (int i = 0; i < 4; ++i) bv[i] = bp[(size_t)i * SP_D];
+        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+        const float *srow = &sS[m][32 * kq];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) reinterpret_cast<f32x4 *>(sA)[tid + 256 * i] = ar[i];
-        __syncthreads();
-        if (s + 1 < P) load_a(s + 1);          // in flight during the products
-        const float *bp = Bmat + seg * mat + (size_t)row * SP_D + c0;
-        const f32x4 b0 = *reinterpret_cast<const f32x4 *>(bp), b1 = *reinterpret_cast<const f32x4 *>(bp + 4);
-        float acc[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { acc[e] = b0[e]; acc[4 + e] = b1[e]; }
-#pragma unroll 8
-        for (int j = 0; j < SP_D; ++j) {
-            const float sj = sS[r][j];
-            const f32x4 a0 = *reinterpret_cast<const f32x4 *>(sA + j * SP_D + c0);
-            const f32x4 a1 = *reinterpret_cast<const f32x4 *>(sA + j * SP_D + c0 + 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc[e] += sj * a0[e];
-                acc[4 + e] += sj * a1[e];
-            }
+        for (int q4 = 0; q4 < 8; ++q4) {
+            const f32x4 a4 = *reinterpret_cast<const f32x4 *>(srow + 4 * q4);
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[0], cur[4 * q4], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[1], cur[4 * q4 + 1], acc1, 0, 0, 0);
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[2], cur[4 * q4 + 2], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[3], cur[4 * q4 + 3], acc1, 0, 0, 0);
         }
+        __syncthreads();                       // every wave has read the row block
 #pragma unroll
-        for (int e = 0; e < 8; ++e) cur[e] = acc[e];
-        __syncthreads();                       // sS and sA read before the next segment's writes
+        for (int i = 0; i < 4; ++i) sS[4 * kq + i][col] = (acc0[i] + acc1[i]) + bv[i];
+        __syncthreads();                       // the new row block complete
+    };
+    float a0[32], a1[32];
+    if (P > 0) load_a(0, a0);
+    for (int s = 0; s < P; s += 2) {
+        step(s, a0, a1);
+        if (s + 1 < P) step(s + 1, a1, a0);
     }
-    if (s_final) {
-        float *p = s_final + ((size_t)bh * SP_D + row) * SP_D + c0;
-        *reinterpret_cast<f32x4 *>(p) = f32x4{cur[0], cur[1], cur[2], cur[3]};
-        *reinterpret_cast<f32x4 *>(p + 4) = f32x4{cur[4], cur[5], cur[6], cur[7]};
-    }
+    if (s_final)
+        *reinterpret_cast<f32x4 *>(s_final + ((size_t)bh * SP_D + r0 + vr) * SP_D + vc) =
+            *reinterpret_cast<const f32x4 *>(&sS[vr][vc]);
 }
 
 // Workspace: the two-pass workspace for B * P segments, their offsets, and
@@ -200,7 +194,7 @@ hipError_t launch_prefill_seqpar(const void *q, const void *k, const void *v, co
             (const void *)seg_compose_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, SC_LDS_BYTES);
         e = attr;
         if (e == hipSuccess) {
-            hipLaunchKernelGGL(seg_compose_kernel, dim3((unsigned)(B * H), SP_D / 16), dim3(256),
+            hipLaunchKernelGGL(seg_compose_kernel, dim3((unsigned)(B * H), SP_D / 16), dim3(SC_NT),
                                SC_LDS_BYTES, stream, Am, Bm, s_init, In, s_final, H, P);
             e = hipGetLastError();
         }
