@@ -817,3 +817,36 @@ def test_prefill_and_decode_replay_from_a_captured_graph():
         torch.cuda.synchronize()
         for got, want in zip((o, fin, st, o1), ref):
             assert torch.equal(got, want)
+
+
+@pytest.mark.parametrize("seed", range(500, 512))
+def test_seed_sweep_short_and_packed(seed):
+    """Many small cases per seed, every chunk path against the oracle: a short
+    batch (1-200 tokens, with or without initial states) and packed sequences
+    of 1, 64, 0, 2, 129, 17 and 1 tokens through the two-pass, one-pass and
+    per-channel chunk paths, and a sequence-parallel run with 1-12 segments."""
+    import random
+    rnd = random.Random(seed)
+    cases = [inputs.make_prefill(seed=seed, B=2, T=rnd.randint(1, 200), H=3, d=128, dtype="bf16",
+                                 with_state=rnd.random() < 0.5),
+             inputs.make_varlen(seed=seed, H=3, d=128, lengths=[1, 64, 0, 2, 129, 17, 1])]
+    for c in cases:
+        o_ref, s_ref = oracle_prefill(c)
+        cu = None if c.cu_seqlens is None else [int(x) for x in c.cu_seqlens.tolist()]
+        for path in WS:
+            o, fin = run_prefill(c, path=path)
+            eo = o_err(o, o_ref) if cu is None else o_err_packed(o, o_ref, cu)
+            assert eo <= TOL_BF16 and s_err(fin, s_ref) <= TOL_BF16, (path, cu)
+    cc = inputs.make_channel_gated(seed=seed, H=2, d=128, lengths=[rnd.randint(1, 80), 1, 2, 65])
+    o, fin = _channel_run(cc)
+    o_ref, s_ref = _oracle_channel(cc)
+    cu = [int(x) for x in cc.cu_seqlens.tolist()]
+    assert o_err_packed(o, o_ref, cu) <= TOL_BF16 and s_err(fin, s_ref) <= TOL_BF16
+    c = inputs.make_prefill(seed=seed, B=2, T=rnd.randint(1, 700), H=2, d=128, dtype="bf16",
+                            with_state=True)
+    fin = torch.empty((2, 2, 128, 128), dtype=torch.float32, device="cuda:0")
+    o, _ = gdn.gdn_prefill_seqpar(dev(c.q), dev(c.k), dev(c.v), dev(c.g), dev(c.beta),
+                                  rnd.randint(1, 12), dev(c.s0), fin, scale=c.scale)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_prefill(c)
+    assert o_err(o, o_ref) <= TOL_BF16 and s_err(fin, s_ref) <= TOL_BF16
