@@ -232,6 +232,9 @@ __device__ __forceinline__ void solve_store(const float *sA, const float *sY, fl
     };
 
     if (wave == 0) {
+        // the other waves wait at the barrier below: this wave wins issue
+        // arbitration against the co-resident workgroups' waves meanwhile
+        __builtin_amdgcn_s_setprio(2);
         // ---- diagonal blocks, one per 16 lanes: lane 16 b + c computes
         //      column c of D_b = (I - A_bb)^-1 row by row,
         //      D[i][c] = [i == c] + sum_{m < i} A[i][m] D[m][c]
@@ -260,6 +263,7 @@ __device__ __forceinline__ void solve_store(const float *sA, const float *sY, fl
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) sT[(16 * bb + i) * P_LD_A + 16 * bb + c] = D[i];
+        __builtin_amdgcn_s_setprio(0);
     } else if (wave == 1) {
         // the 16 x 16 blocks (0,1) and (2,3) of T are zero; the output reads them
 #pragma unroll
@@ -476,6 +480,7 @@ chunk_prep_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                 *reinterpret_cast<bf16x8 *>(sQ + ((tid >> 4) + 16 * u) * P_LD_K + col) = p.qr[u];
             }
             if (wave == 0) {
+                __builtin_amdgcn_s_setprio(2);     // as in the solve: the others wait for it
                 const float gam = wave_inclusive_scan(p.gv);
                 const float g32 = __builtin_bit_cast(
                     float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gam), 32));
@@ -483,6 +488,7 @@ chunk_prep_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                 sBeta[lane] = p.bv;
                 sBegN[lane] = -p.bv * __expf(gam);
                 sE[lane] = __expf(lane >= 32 ? gam - g32 : g32 - gam);
+                __builtin_amdgcn_s_setprio(0);
             }
         }
         fetch(nit, pn);
