@@ -900,12 +900,16 @@ chunk_prep_channel_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k
                 *reinterpret_cast<bf16x8 *>(dst + CH_QP + 512 * f + 8 * ln) = qp;
             }
         };
+        // wave 0 writes the most copies (KC_1 .. KC_3 besides its own): it
+        // goes first in issue arbitration
+        if (I == 0) __builtin_amdgcn_s_setprio(1);
         switch (I) {
         case 0: scaled_copies(std::integral_constant<int, 0>{}); break;
         case 1: scaled_copies(std::integral_constant<int, 1>{}); break;
         case 2: scaled_copies(std::integral_constant<int, 2>{}); break;
         default: scaled_copies(std::integral_constant<int, 3>{}); break;
         }
+        __builtin_amdgcn_s_setprio(0);
         // ---- wave I, diagonal block (I, I) of M (dM) and of P^T (dP). Its
         //      operands are rows this wave wrote and only it reads, so it is
         //      summed before the workgroup barrier. P's block is summed as
@@ -953,6 +957,9 @@ chunk_prep_channel_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k
         fetch(nit, pn);
         ait = prep_locate(cu_seqlens, after, nitems, T, H, N);
         lds_barrier();
+        // waves with more column blocks ahead of the next barrier go first
+        if (I == 3) __builtin_amdgcn_s_setprio(2);
+        else if (I == 2) __builtin_amdgcn_s_setprio(1);
         // ---- wave I: off-diagonal blocks J < I of row block I of M (accM[J])
         //      and of P^T (accP[J], rows = keys 16 J + .., columns = queries
         //      16 I + ..) ----
@@ -1051,6 +1058,7 @@ chunk_prep_channel_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k
             bf16 *prow = dst + 8 * WS_TWU + (qi < 32 ? 32 * qi : 1024 + 64 * (qi - 32));
             *reinterpret_cast<bf16x4 *>(prow + 16 * (I + 1) + 4 * kq) = bf16x4{};
         }
+        __builtin_amdgcn_s_setprio(0);
         lds_barrier();                         // A complete
         solve_store(sA, sY, sT, sNegBeta, sBeta, dst, tid, wave);
         lds_barrier();                         // T and the scalars read before the next item
