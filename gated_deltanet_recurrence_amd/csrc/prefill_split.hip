@@ -283,6 +283,8 @@ __device__ __forceinline__ void solve_store(const float *sA, const float *sY, fl
     {
         const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
         f32x4 h0 = z4, h1 = z4;
+        // the waves with the most products in a level go first in issue
+        if (wave == 0 || wave == 2) __builtin_amdgcn_s_setprio(1);
         if (wave == 0) {
             const f32x4 c10 = mm16(z4, blkA(1, 0), P_LD_A2, blkT(0, 0), P_LD_A, lane);
             h0 = mm16(z4, blkA(2, 0), P_LD_A2, blkT(0, 0), P_LD_A, lane);              // A20 D0
@@ -299,6 +301,8 @@ __device__ __forceinline__ void solve_store(const float *sA, const float *sY, fl
             h1 = mm16(z4, blkA(3, 0), P_LD_A2, blkT(0, 0), P_LD_A, lane);              // A30 D0
         }
         lds_barrier();
+        __builtin_amdgcn_s_setprio(0);
+        if (wave == 3) __builtin_amdgcn_s_setprio(2);
         if (wave == 0) {
             const f32x4 y00 = mm16(h0, blkA(2, 1), P_LD_A2, blkT(1, 0), P_LD_A, lane);
             store_T(2, 0, mm16_rb(z4, blkT(2, 2), P_LD_A, acc_to_bop(y00), lane));
@@ -314,6 +318,7 @@ __device__ __forceinline__ void solve_store(const float *sA, const float *sY, fl
         lds_barrier();
     }
 
+    __builtin_amdgcn_s_setprio(0);
     // ---- -T diag(beta e^gamma) and T diag(beta) -> workspace as 16-byte
     //      pieces (bf16), consecutive per thread. Piece order:
     //        0..255     rows 32-63 of -T_w (8 per row)
@@ -497,7 +502,9 @@ chunk_prep_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         lds_barrier();
         bf16 *dst = ws + ((size_t)it.h * nslots + it.slot) * ITEM_ELEMS;
 
-        // ---- gram tiles of A and P^T ----
+        // ---- gram tiles of A and P^T (waves 0 and 1, whose diagonal tiles
+        //      take an exponential per element, go first in issue) ----
+        if (wave < 2) __builtin_amdgcn_s_setprio(1);
         if (wave < 3) {
             const int ti = wave == 0 ? 0 : 1, tj = wave == 1 ? 1 : 0, qb = wave == 0 ? 0 : 1;
             f32x16 at = {}, pt = {};
@@ -586,6 +593,7 @@ chunk_prep_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         }
         lds_barrier();                         // A complete; K and Q no longer read
 
+        __builtin_amdgcn_s_setprio(0);
         solve_store(sA, sY, sT, sBegN, sBeta, dst, tid, wave);
         lds_barrier();                         // T and the scalars read before the next item
     };
