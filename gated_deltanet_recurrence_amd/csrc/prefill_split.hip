@@ -1575,6 +1575,10 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         else oloop(std::integral_constant<int, 1>{});
     } else {
         // ============ waves 4-7: staging; waves 4-5 also stage P ============
+        // below the recurrence and above the output waves in issue arbitration:
+        // the next chunk's tiles must be in LDS by the barrier (per channel the
+        // output waves also load Q+ from memory and keep the default)
+        if constexpr (!PERCH) __builtin_amdgcn_s_setprio(1);
         // P pieces 192 (wave - 4) + 64 r + lane (r < 3) of the workspace item,
         // held in one of two register sets by chunk parity: chunk c's pieces
         // are loaded in iteration c - 2 and written into P copy c % 2 in
