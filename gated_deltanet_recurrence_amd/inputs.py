@@ -37,7 +37,7 @@ import torch
 __all__ = [
     "GDNCase", "MixerCase", "DecodeMixerCase", "unit_gaussian", "log_uniform_lengths",
     "make_tiny", "make_prefill", "make_decode", "make_mixer", "make_varlen",
-    "make_decode_mixer", "make_channel_gated",
+    "make_decode_mixer", "make_channel_gated", "make_long_memory",
     "make_case", "WORKLOADS",
 ]
 
@@ -297,6 +297,33 @@ def make_channel_gated(seed: int = 7, B: int = 2, T: int = 300, H: int = 4, d: i
                    meta={"A": A, "lengths": lengths})
 
 
+def make_long_memory(seed: int = 200, B: int = 2, T: int = 1024, H: int = 2, d: int = 128,
+                     gate: str = "zero", with_state: bool = False, dtype: str = "bf16",
+                     per_channel: bool = False) -> GDNCase:
+    """Long-memory regime: what is written survives many chunks.
+
+    ``gate="zero"``: g = 0 (alpha = 1), the delta rule without forgetting;
+    ``gate="near_one"``: alpha ~ U(0.99, 1), g = log(alpha) (per key channel
+    when ``per_channel``, g then [B, T, H, d]). q,k unit Gaussian, v ~ N(0,1),
+    beta = sigmoid(N(0,1)), initial states N(0, 0.02) when ``with_state``."""
+    gen = _gen(seed)
+    td = _TORCH_DTYPE[dtype]
+    q = unit_gaussian(gen, (B, T, H, d)).to(td)
+    k = unit_gaussian(gen, (B, T, H, d)).to(td)
+    v = _normal(gen, (B, T, H, d)).to(td)
+    gshape = (B, T, H, d) if per_channel else (B, T, H)
+    if gate == "zero":
+        g = torch.zeros(gshape, dtype=torch.float32)
+    elif gate == "near_one":
+        g = torch.log(_uniform(gen, gshape, 0.99, 1.0))
+    else:
+        raise ValueError(f"unknown gate recipe {gate!r}")
+    beta = _sigmoid_gaussian(gen, (B, T, H))
+    s0 = _normal(gen, (B, H, d, d), std=0.02) if with_state else None
+    return GDNCase("long_memory", q, k, v, g.contiguous(), beta, s0, None, 1.0 / math.sqrt(d),
+                   dtype, meta={"gate": gate, "per_channel": per_channel})
+
+
 @dataclass
 class DecodeMixerCase:
     """Inputs of one fused single-token mixer step, on the host.
@@ -354,6 +381,7 @@ WORKLOADS = {
     "varlen": make_varlen,
     "decode_mixer": make_decode_mixer,
     "channel_gated": make_channel_gated,
+    "long_memory": make_long_memory,
 }
 
 
