@@ -97,6 +97,9 @@ def decode_bytes(B, H, dk=128, dv=128):
 
 
 def event_time(fn, steps, warmup):
+    """Mean ms per call over `steps` calls bracketed by device synchronisation
+    and one pair of HIP events (recorded on torch's current stream, the one
+    the binding launches on)."""
     import torch
     for _ in range(warmup):
         fn(0)
@@ -109,6 +112,33 @@ def event_time(fn, steps, warmup):
     stop.record()
     torch.cuda.synchronize()
     return start.elapsed_time(stop) / steps        # ms per call
+
+
+def launch_times(fns, steps, warmup):
+    """Per-launch durations (ms) of a sequence of launches: each call in
+    `fns` is bracketed by its own pair of HIP events on the launch stream,
+    for `steps` repetitions after `warmup` untimed ones. Returns one list of
+    `steps` durations per function."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        for f in fns:
+            f(i)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        for j, f in enumerate(fns):
+            f(i)
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    return [[ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)] for j in range(len(fns))]
+
+
+def _median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
 
 
 def _src_hash(path):
@@ -396,27 +426,42 @@ def bench_copy(steps, warmup, nbytes=1 << 30):
                 GBps=round(2 * nbytes / (ms * 1e-3) / 1e9, 1))
 
 
-def cpu_baseline(min_seconds=10.0, max_runs=100):
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(runs=3):
     """fp64 oracle on the prefill workload's host arrays (all 4 x 16 chains of
-    4096 tokens), run back to back after a small warm-up until at least
-    `min_seconds` of wall time have passed; the rate is the mean over the runs."""
+    4096 tokens): one untimed run, then the median of `runs` timed runs. The
+    oracle runs its OpenMP loop over the (sequence, head) pairs on every
+    thread it is given (`cores`)."""
     import oracle
     from gated_deltanet_recurrence_amd import inputs
     c = inputs.make_prefill()
-    oracle.gdn_recurrent(c.q[:1, :64], c.k[:1, :64], c.v[:1, :64], c.g[:1, :64],
-                         c.beta[:1, :64], None, None, c.scale)
-    runs = 0
-    t = time.perf_counter()
-    while True:
+    oracle.gdn_recurrent(c.q, c.k, c.v, c.g, c.beta, None, None, c.scale)
+    times = []
+    for _ in range(runs):
+        t = time.perf_counter()
         oracle.gdn_recurrent(c.q, c.k, c.v, c.g, c.beta, None, None, c.scale)
-        runs += 1
-        dt = time.perf_counter() - t
-        if dt >= min_seconds or runs >= max_runs:
-            break
-    return {"value": round(runs * c.B * c.T / dt, 1), "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"the whole prefill workload (B=4, T=4096, H=16, d=128), {runs} runs back to "
-                      f"back, fp64 token recurrence, {dt:.1f} s in all"}
+        times.append(time.perf_counter() - t)
+    med = _median(times)
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
+    return {"value": round(c.B * c.T / med, 1), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "host_cpus": os.cpu_count(), "host_cpus_usable": affinity,
+            "cpu_model": _cpu_model(),
+            "run_seconds": [round(x, 3) for x in times],
+            "sample": f"the whole prefill workload (B=4, T=4096, H=16, d=128), fp64 token "
+                      f"recurrence: one untimed run, then the median of {runs} timed runs"}
 
 
 def main():
