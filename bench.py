@@ -10,15 +10,16 @@ chunks). ``value`` is prefill tokens/s (B*T per step). The same JSON line
 carries:
 
 * ``roofline`` of the dominant kernel (the pass with the longer average
-  duration, timed with HIP events around each pass): its algorithmic HBM
-  bytes per launch over that duration, against 8 TB/s. Per token-head,
-  chunk_chain moves q, k, v, o (bf16), g (fp32) and the 288 B of bf16
-  T diag(beta e^gamma), T diag(beta) (192 B) and P (96 B) that chunk_prep
-  left in the workspace (1316 B), plus the fp32 final states; chunk_prep
-  reads q, k, g, beta and writes those 288 B (808 B). ``traffic`` is the measured HBM bytes per
-  launch from the committed counter summary (profiles/), or null when the
-  kernel source has changed since. ``path`` gives the whole step against the
-  method's own 1032 B per token-head (q, k, v, o, g, beta) and the
+  launch, timed with a pair of HIP events around every launch): the method's
+  own bytes per step (1032 B per token-head: q, k, v, o bf16, g, beta fp32,
+  plus the fp32 final states) over that kernel's average launch, against
+  8 TB/s, with the matrix-core rate of the step's algorithmic flops over the
+  same time. ``overhead_bytes`` counts what the two-pass design moves beyond
+  them (the 96 B per token-head of bf16 T diag(beta) written by chunk_prep
+  and read back by chunk_chain, and chunk_prep's second read of k, g, beta).
+  ``traffic`` is the measured HBM bytes per launch from the committed counter
+  summary (profiles/), or null when the kernel source has changed since.
+  ``path`` gives the whole step against the method's bytes and the
   matrix-core rate against the 2.5 PFLOP/s dense bf16 peak;
 * ``one_pass``: the same call without a workspace (one kernel that solves
   each chunk's system on the sequential path);
@@ -39,7 +40,9 @@ carries:
 
 Timing: warm-up launches, then K launches bracketed by device
 synchronisation and timed with HIP events recorded on the stream the kernels
-run on (torch's current stream, which the binding launches on). Prefill
+run on (torch's current stream, which the binding launches on); the per-pass
+figures come from an event pair around every launch (mean and median over at
+least 20). Prefill
 inputs and outputs alternate between two copies so that successive launches
 read from HBM rather than from the 256 MB last-level cache.
 """
@@ -76,20 +79,22 @@ def prefill_bytes(B, T, H, dk=128, dv=128, n_states_out=None, n_states_in=0):
     return tok_head * per + states + n_states_in * H * dv * dk * 4
 
 
-# workspace per token-head: bf16 T_w, T_u (three 32 x 32 blocks each) and P
-# (rows 0-31 by columns 0-31, rows 32-63 by all 64) per 64-token chunk
-WS_BYTES_PER_TOKEN_HEAD = (2 * 3 * 32 * 32 + 32 * 32 + 32 * 64) * 2 // 64   # 288
+# workspace per token-head: bf16 T diag(beta) per 64-token chunk (its lower
+# 64 x 64 part: rows 0-31 by columns 0-31, rows 32-63 by all 64)
+WS_BYTES_PER_TOKEN_HEAD = (32 * 32 + 32 * 64) * 2 // 64     # 96
 
 
 def chain_bytes(B, T, H, dk=128, dv=128):
-    """chunk_chain per launch: q, k, v, o bf16, g fp32, the workspace read back, final states."""
+    """chunk_chain per launch as it runs: q, k, v, o bf16, g fp32, the
+    workspace read back, the final states."""
     per = 2 * (dk + dk + dv + dv) + 4 + WS_BYTES_PER_TOKEN_HEAD
     return B * T * H * per + B * H * dv * dk * 4
 
 
 def prep_bytes(B, T, H, dk=128):
-    """chunk_prep per launch: q, k bf16, g and beta fp32 read, the workspace written."""
-    return B * T * H * (2 * dk + 2 * dk + 4 + 4 + WS_BYTES_PER_TOKEN_HEAD)
+    """chunk_prep per launch as it runs: k bf16, g and beta fp32 read, the
+    workspace written."""
+    return B * T * H * (2 * dk + 4 + 4 + WS_BYTES_PER_TOKEN_HEAD)
 
 
 def decode_bytes(B, H, dk=128, dv=128):
@@ -192,27 +197,25 @@ def bench_prefill(gdn, inputs, steps, warmup):
     ms = event_time(step, steps, warmup)
     ms_one = event_time(step_one_pass, max(2, steps // 4), 2)
 
-    # each pass alone: events recorded between the launches, on the stream both run on
-    stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    for i in range(steps):
+    # each pass alone: one pair of events around every launch, on the stream
+    # both run on, over max(steps, 20) repetitions
+    def prep(i):
         s = sets[i & 1]
-        ev[i][0].record(stream)
         gdn.gdn_prefill_prepare(s["q"], s["k"], s["g"], s["beta"], ws)
-        ev[i][1].record(stream)
+
+    def chain(i):
+        s = sets[i & 1]
         gdn.gdn_prefill_apply(s["q"], s["k"], s["v"], s["g"], ws, None, s["fin"], s["o"],
                               scale=c.scale)
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    ms_prep = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
-    ms_chain = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    t_prep, t_chain = launch_times([prep, chain], max(steps, 20), warmup)
     tokens = c.B * c.T
-    return dict(ms=ms, ms_one_pass=ms_one, ms_prep=ms_prep, ms_chain=ms_chain, tokens=tokens,
+    return dict(ms=ms, ms_one_pass=ms_one, tokens=tokens,
+                ms_prep=sum(t_prep) / len(t_prep), ms_chain=sum(t_chain) / len(t_chain),
+                med_prep=_median(t_prep), med_chain=_median(t_chain), n_launch=len(t_prep),
                 bytes=prefill_bytes(c.B, c.T, c.H), chain_bytes=chain_bytes(c.B, c.T, c.H),
                 prep_bytes=prep_bytes(c.B, c.T, c.H),
+                ws_bytes=2 * WS_BYTES_PER_TOKEN_HEAD * c.B * c.T * c.H,
+                reread_bytes=(2 * 128 + 4 + 4) * c.B * c.T * c.H,
                 flops=prefill_flops_per_token_head() * c.B * c.T * c.H, case=c)
 
 
@@ -493,8 +496,11 @@ def main():
         chain_dominant = p["ms_chain"] >= p["ms_prep"]
         kname = "chunk_chain_kernel" if chain_dominant else "chunk_prep_kernel"
         k_ms = p["ms_chain"] if chain_dominant else p["ms_prep"]
-        k_bytes = p["chain_bytes"] if chain_dominant else p["prep_bytes"]
-        achieved = k_bytes / (k_ms * 1e-3) / 1e9
+        k_med = p["med_chain"] if chain_dominant else p["med_prep"]
+        # the method's bytes (1032 B per token-head plus the final states),
+        # over the dominant kernel's average launch
+        achieved = p["bytes"] / (k_ms * 1e-3) / 1e9
+        k_flops = p["flops"] / (k_ms * 1e-3) / 1e12
         traffic, why = measured_traffic(kname)
         result.update({
             "value": round(p["tokens"] / sec, 1), "unit": "tokens/s",
@@ -506,15 +512,29 @@ def main():
             "roofline": {"kernel": kname, "bound": "hbm",
                          "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                         "traffic_note": why, "algorithmic_bytes_per_launch": k_bytes,
+                         "traffic_note": why,
+                         "algorithmic_bytes_per_launch": p["bytes"],
+                         "algorithmic_bytes_note": "1032 B per token-head (q, k, v, o bf16; g, "
+                                                   "beta fp32) plus the fp32 final states",
+                         "overhead_bytes": p["ws_bytes"] + p["reread_bytes"],
+                         "overhead_note": "workspace T diag(beta) written and read back (96 B "
+                                          "each way per token-head) and k, g, beta read a "
+                                          "second time by the prep pass (264 B)",
+                         "mfma_tflops": round(k_flops, 2),
+                         "mfma_frac_of_bf16_peak": round(k_flops / BF16_PEAK_TFLOPS, 4),
                          "avg_launch_us": round(k_ms * 1e3, 2),
+                         "median_launch_us": round(k_med * 1e3, 2),
+                         "launches_timed": p["n_launch"],
                          "other_kernel_avg_launch_us": round((p["ms_prep"] if chain_dominant
-                                                              else p["ms_chain"]) * 1e3, 2)},
+                                                              else p["ms_chain"]) * 1e3, 2),
+                         "other_kernel_median_launch_us": round((p["med_prep"] if chain_dominant
+                                                                 else p["med_chain"]) * 1e3, 2)},
             "path": {"algorithmic_bytes_per_step": p["bytes"],
                      "GB/s": round(p["bytes"] / sec / 1e9, 1),
                      "frac_of_hbm_peak": round(p["bytes"] / sec / 1e9 / HBM_PEAK_GBS, 4),
                      "mfma_algorithmic_tflops": round(p["flops"] / sec / 1e12, 2),
-                     "mfma_frac_of_bf16_peak": round(p["flops"] / sec / 1e12 / BF16_PEAK_TFLOPS, 4)},
+                     "mfma_frac_of_bf16_peak": round(p["flops"] / sec / 1e12 / BF16_PEAK_TFLOPS, 4),
+                     "bytes_moved_per_step_by_design": p["chain_bytes"] + p["prep_bytes"]},
             "one_pass": {"ms_per_step": round(p["ms_one_pass"], 5),
                          "tokens_per_s": round(p["tokens"] / (p["ms_one_pass"] * 1e-3), 1)},
         })

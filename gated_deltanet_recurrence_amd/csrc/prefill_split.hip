@@ -13,30 +13,34 @@
 //   O        = scale (diag(e^gamma) Q S^T + lower_incl_diag(Q K^T * Gamma) Delta)
 //   S       <- e^{gamma_63} S + Delta~^T K,  Delta~_j = e^{gamma_63 - gamma_j} Delta_j
 //
-// Everything up to T_w and T_u depends on one chunk of one head only, and
-// is the same for every d_v column. The first pass (chunk_prep) computes it
-// once per (chunk, head), fully in parallel over all chunks; the second pass
-// (chunk_chain) walks the chunks of each sequence in order and carries the
-// state. Splitting takes the triangular solve off the sequential path and
-// stops the d_v tiles of a head from each repeating it; the price is 12 KiB
-// of bf16 T_w / T_u per (chunk, head) written to the caller's workspace and
-// read back: 384 B of HBM traffic per token-head on top of the 1032 B of
-// q, k, v, o, g and beta.
+// Everything up to T_u = T diag(beta) depends on one chunk of one head only,
+// and is the same for every d_v column. The first pass (chunk_prep)
+// computes it once per (chunk, head), fully in parallel over all chunks,
+// from k, g and beta alone; the second pass (chunk_chain) walks the chunks
+// of each sequence in order and carries the state. The chain folds the
+// decay into the delta,
+//   Delta = T_u (V - diag(e^gamma) K S^T)      (T_w K S^T = T_u diag(e^gamma) K S^T)
+// so only T_u crosses between the passes, and it forms P = lower_incl_diag(
+// Q K^T * Gamma) itself from the q and k tiles it stages anyway. Splitting
+// takes the triangular solve off the sequential path and stops the d_v tiles
+// of a head from each repeating it; the price is the 6 KiB bf16 T_u per
+// (chunk, head) written to the caller's workspace and read back: 96 B of
+// HBM traffic each way per token-head, on top of the 1032 B of q, k, v, o,
+// g and beta (the prep pass also reads k, g and beta a second time, 264 B).
 //
 // q and k may have fewer heads (H_k) than v, g, beta, o and the state (H):
 // value head h reads query/key head h / (H / H_k) (the repeat_interleave head
 // expansion of the "Gated DeltaNet body" layer code, "5. Linear Attention").
 // The workspace is per value head, since beta and g are.
 //
-// Workspace layout: for head h and chunk slot s, 6144 bf16 at
-// ((h * nslots) + s) * 6144, as 768 pieces of 8 consecutive row elements of
-// -T_w and T_u (their non-zero lower 64 x 64 part: rows 0-31 span columns
-// 0-31 only): pieces 0..255 are rows 32-63 of -T_w (8 pieces per row),
-// 256..511 rows 32-63 of T_u, 512..639 rows 0-31 of -T_w (4 per row),
-// 640..767 rows 0-31 of T_u. Chunk c of sequence n has slot
-// (bos_n / 64) + n + c, where bos_n is its first token: slots of different
-// sequences never collide and every slot is below
-// nslots = total_tokens / 64 + N + 1.
+// Workspace layout: for head h and chunk slot s, 3072 bf16 at
+// ((h * nslots) + s) * 3072, as 384 pieces of 8 consecutive row elements of
+// T_u (its non-zero lower 64 x 64 part: rows 0-31 span columns 0-31 only):
+// pieces 0..255 are rows 32-63 (8 pieces per row), 256..383 rows 0-31 (4 per
+// row). Chunk c of sequence n has slot (bos_n / 64) + n + c, where bos_n is
+// its first token: slots of different sequences never collide and every slot
+// is below nslots = total_tokens / 64 + N + 1. The per-channel item (below)
+// starts with the same T_u pieces.
 #include <atomic>
 #include <type_traits>
 
@@ -51,33 +55,32 @@ using namespace chunk;
 constexpr int C = 64;
 constexpr int DK = 128;
 constexpr int DV = 128;
-constexpr int WS_TWU = 768;                   // 16-byte pieces of -T_w and T_u per (chunk, head)
-constexpr int WS_P = 384;                     // 16-byte pieces of P per (chunk, head)
-constexpr int ITEM_ELEMS = 8 * (WS_TWU + WS_P);   // 9216 bf16 per (chunk, head) in the workspace
+constexpr int WS_T = 384;                     // 16-byte pieces of T_u per (chunk, head)
+constexpr int WS_P = 384;                     // 16-byte pieces of P (per-channel items)
+constexpr int ITEM_ELEMS = 8 * WS_T;          // 3072 bf16 per (chunk, head) in the workspace
 
 // ---------------------------------------------------------------------------
 // Pass 1: chunk_prep. Workgroups of 4 waves, each looping over (chunk slot,
 // head) items.
 // ---------------------------------------------------------------------------
 constexpr int P_NT = 256;
-constexpr int P_LD_K = DK + 8;                 // bf16 row stride of K and Q
+constexpr int P_LD_K = DK + 8;                 // bf16 row stride of K
 constexpr int P_LD_A = C + 4;                  // fp32 row stride of T
 constexpr int P_LD_A2 = 52;                    // fp32 row stride of the off-diagonal part of A
 constexpr int P_DB = 16 * 16 + 4;              // floats per diagonal 16 x 16 block of A (padded
                                                // so the four blocks' rows fall on different banks)
 constexpr int P_SZ_R1 = C * P_LD_K * 2;        // 17408: K, then T
-constexpr int P_SZ_R2 = C * P_LD_K * 2;        // 17408: Q
 constexpr int P_SZ_A = 48 * P_LD_A2 * 4;       // 9984: rows 16-63, columns 0-47 of A
 constexpr int P_SZ_Y = 4 * P_DB * 4;           // 4160: the diagonal blocks of A, row-major
-constexpr int P_SZ_SC = 4 * C * 4;             // gamma log2(e), beta, -beta e^gamma, E
+constexpr int P_SZ_SC = 3 * C * 4;             // gamma log2(e), beta, E
 constexpr int P_OFF_R1 = 0;
-constexpr int P_OFF_R2 = P_OFF_R1 + P_SZ_R1;
-constexpr int P_OFF_A = P_OFF_R2 + P_SZ_R2;
+constexpr int P_OFF_A = P_OFF_R1 + P_SZ_R1;
 constexpr int P_OFF_Y = P_OFF_A + P_SZ_A;
 constexpr int P_OFF_SC = P_OFF_Y + P_SZ_Y;
-constexpr int P_LDS_BYTES = P_OFF_SC + P_SZ_SC;   // 49984
+constexpr int P_LDS_BYTES = P_OFF_SC + P_SZ_SC;   // 32320
+constexpr int P_WG_PER_CU = 4;
 static_assert(C * P_LD_A * 4 <= P_SZ_R1, "T fits where K was");
-static_assert(P_LDS_BYTES <= 160 * 1024 / 3, "three prep workgroups per CU");
+static_assert(P_LDS_BYTES * P_WG_PER_CU <= 160 * 1024, "four prep workgroups per CU");
 
 // ---------------------------------------------------------------------------
 // Pass 2: chunk_chain. One workgroup of 8 waves per (32-wide d_v tile, head,
@@ -87,8 +90,8 @@ static_assert(P_LDS_BYTES <= 160 * 1024 / 3, "three prep workgroups per CU");
 // v_mfma_f32_16x16x32_bf16 operand reads (16 consecutive rows, four 16-byte
 // column chunks), which then hit every LDS bank equally: 288 bytes for rows
 // of 128, 160 for rows of 64 and 80 for rows of 32. The lower-triangular
-// 64 x 64 tiles (T_w, T_u, P) keep rows 0-31 (read in columns 0-31 only) and
-// rows 32-63 as two tiles of different width.
+// 64 x 64 tiles (T_u, and P with a per-channel decay) keep rows 0-31 (read in
+// columns 0-31 only) and rows 32-63 as two tiles of different width.
 // ---------------------------------------------------------------------------
 constexpr int MAX_DEVICES = 64;               // per-device launch caches
 constexpr int DVT = 32;
@@ -99,12 +102,12 @@ constexpr int NT = 512;
 constexpr int CHAIN_ZERO_V = 1;
 constexpr int CHAIN_INIT_IDENTITY = 2;
 constexpr int LD_R = DK + 16;                  // 144: Q, K, S rows
-constexpr int LD_L = C + 16;                   // 80: rows 32-63 of T_w, T_u, P; Delta^T rows
-constexpr int LD_H = 32 + 8;                   // 40: rows 0-31 of T_w, T_u, P; V rows
+constexpr int LD_L = C + 16;                   // 80: rows 32-63 of T_u, P; Delta^T rows
+constexpr int LD_H = 32 + 8;                   // 40: rows 0-31 of T_u, P; V rows
 constexpr int SZ_QK = C * LD_R * 2;            // 18432
 constexpr int SZ_V = C * LD_H * 2;             // 5120
-constexpr int SZ_TH = 2 * 32 * LD_H * 2;       // 5120: rows 0-31 of -T_w, then of T_u
-constexpr int SZ_TL = 2 * 32 * LD_L * 2;       // 10240: rows 32-63 of -T_w, then of T_u
+constexpr int SZ_TH = 32 * LD_H * 2;           // 2560: rows 0-31 of T_u
+constexpr int SZ_TL = 32 * LD_L * 2;           // 5120: rows 32-63 of T_u
 constexpr int SZ_SC = 3 * C * 4 + DK * 4;      // gamma, e^gamma, e^{gamma_63 - gamma};
                                                // per-channel decay: e^{gamma_63} per channel
 constexpr int B_Q = 0;
@@ -113,16 +116,16 @@ constexpr int B_V = B_K + SZ_QK;
 constexpr int B_TH = B_V + SZ_V;
 constexpr int B_TL = B_TH + SZ_TH;
 constexpr int B_SC = B_TL + SZ_TL;
-constexpr int SZ_BUF = B_SC + SZ_SC;           // 58112
+constexpr int SZ_BUF = B_SC + SZ_SC;           // 50944
 constexpr int SZ_PH = 32 * LD_H * 2;           // 2560: P rows 0-31
 constexpr int SZ_P = SZ_PH + 32 * LD_L * 2;    // 7680: P rows 0-31, then 32-63
 constexpr int SZ_S = DVT * LD_R * 2;           // 9216: bf16 S [32][144]
 constexpr int SZ_DT = DVT * LD_L * 2;          // 5120: Delta^T [32][80]
 constexpr int OFF_BUF = 0;                     // two of each from here on
-constexpr int OFF_P = OFF_BUF + 2 * SZ_BUF;
+constexpr int OFF_P = OFF_BUF + 2 * SZ_BUF;    // (P copies: per-channel decay only)
 constexpr int OFF_S = OFF_P + 2 * SZ_P;
 constexpr int OFF_DT = OFF_S + 2 * SZ_S;
-constexpr int LDS_BYTES = OFF_DT + 2 * SZ_DT;  // 160256
+constexpr int LDS_BYTES = OFF_DT + 2 * SZ_DT;  // 145920
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 static_assert(DV / DVT == PAIR_TILES, "one workgroup per d_v tile of a pair");
 static_assert(SZ_BUF % 16 == 0 && SZ_P % 16 == 0, "16-byte aligned tiles");
@@ -215,12 +218,10 @@ using namespace split;
 // prep passes: with A = -strict_lower(...) given as its four diagonal 16 x 16
 // blocks (sY, row-major, P_DB floats apart) and rows 16-63, columns 0-47
 // (sA, row stride P_LD_A2), T = (I - A)^-1 is formed in sT (row stride
-// P_LD_A) and written to the workspace item dst as 16-byte bf16 pieces,
-// -T_w = T diag(colw) and T_u = T diag(colu) (colw = -beta e^gamma for a
-// scalar gate). All four waves of the workgroup call it.
+// P_LD_A) and T_u = T diag(colu) (colu = beta) is written to the workspace
+// item dst as 16-byte bf16 pieces. All four waves of the workgroup call it.
 __device__ __forceinline__ void solve_store(const float *sA, const float *sY, float *sT,
-                                            const float *colw, const float *colu, bf16 *dst,
-                                            int tid, int wave)
+                                            const float *colu, bf16 *dst, int tid, int wave)
 {
     const int lane = tid & 63;
     const int lr = lane & 15, lq = lane >> 4;
@@ -319,34 +320,25 @@ __device__ __forceinline__ void solve_store(const float *sA, const float *sY, fl
     }
 
     __builtin_amdgcn_s_setprio(0);
-    // ---- -T diag(beta e^gamma) and T diag(beta) -> workspace as 16-byte
-    //      pieces (bf16), consecutive per thread. Piece order:
-    //        0..255     rows 32-63 of -T_w (8 per row)
-    //        256..511   rows 32-63 of T_u
-    //        512..639   rows 0-31 of -T_w, columns 0-31 (4 per row)
-    //        640..767   rows 0-31 of T_u, columns 0-31
-    //      followed by P (written above): rows 0-31 by keys 0-31, then
-    //      rows 32-63 by keys 0-63, row-major ----
+    // ---- T diag(beta) -> workspace as 16-byte pieces (bf16). Piece order:
+    //        0..255     rows 32-63 (8 per row)
+    //        256..383   rows 0-31, columns 0-31 (4 per row) ----
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
+    for (int u = 0; u < 2; ++u) {
         const int e = tid + P_NT * u;
-        int mat, i, j0;
-        if (e < 512) {
-            mat = e >= 256 ? 1 : 0;
-            const int pp = e - 256 * mat;
-            i = 32 + (pp >> 3);
-            j0 = 8 * (pp & 7);
+        if (e >= WS_T) break;                  // uniform per wave
+        int i, j0;
+        if (e < 256) {
+            i = 32 + (e >> 3);
+            j0 = 8 * (e & 7);
         } else {
-            mat = e >= 640 ? 1 : 0;
-            const int pp = e - 512 - 128 * mat;
-            i = pp >> 2;
-            j0 = 8 * (pp & 3);
+            i = (e - 256) >> 2;
+            j0 = 8 * (e & 3);
         }
-        const float *sc = mat ? colu : colw;
         const f32x4 t0 = *reinterpret_cast<const f32x4 *>(sT + i * P_LD_A + j0);
         const f32x4 t1 = *reinterpret_cast<const f32x4 *>(sT + i * P_LD_A + j0 + 4);
-        const f32x4 s0 = *reinterpret_cast<const f32x4 *>(sc + j0);
-        const f32x4 s1 = *reinterpret_cast<const f32x4 *>(sc + j0 + 4);
+        const f32x4 s0 = *reinterpret_cast<const f32x4 *>(colu + j0);
+        const f32x4 s1 = *reinterpret_cast<const f32x4 *>(colu + j0 + 4);
         bf16x8 out;
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
@@ -360,26 +352,22 @@ __device__ __forceinline__ void solve_store(const float *sA, const float *sY, fl
 // ---------------------------------------------------------------------------
 // chunk_prep: the parts of a chunk that do not depend on the state, for
 // (chunk, head) items. Item i is slot i / H of head i % H; a workgroup takes
-// items blockIdx.x, + gridDim.x, ... and loads the next item's K, Q, g and
-// beta into registers while it works on the current one, so that the HBM
-// latency is paid once per workgroup.
+// items blockIdx.x, + gridDim.x, ... and loads the next item's K, g and beta
+// into registers while it works on the current one, so that the HBM latency
+// is paid once per workgroup.
 //
-//   stage  K and Q (64 x 128) into LDS; gamma = prefix sum of g (wave 0)
+//   stage  K (64 x 128) into LDS; gamma = prefix sum of g (wave 0)
 //   gram   waves 0-2, one 32 x 32 tile each of A = -strict_lower(diag(beta)
-//          K K^T * Gamma) and of P^T, P = lower_incl(Q K^T * Gamma), sharing
-//          the K fragments (v_mfma_f32_32x32x16_bf16): wave 0 tiles (0,0) of
-//          both, wave 1 tiles (1,1), wave 2 A (1,0) and P^T (0,1). On the
-//          diagonal tiles one exponential per element serves A (below the
-//          diagonal) or P (on and above it); across the halves,
-//          Gamma_ij = E_i E_j with E_t = e^{gamma_t - gamma_32} (t >= 32) or
-//          e^{gamma_32 - gamma_t} (t < 32), two factors no larger than 1 for
-//          gates in (0, 1]
-//          P goes from the accumulators straight to the workspace
+//          K K^T * Gamma) (v_mfma_f32_32x32x16_bf16): wave 0 tile (0,0),
+//          wave 1 (1,1), wave 2 (1,0). On the diagonal tiles one exponential
+//          per element; across the halves Gamma_ij = E_i E_j with
+//          E_t = e^{gamma_t - gamma_32} (t >= 32) or e^{gamma_32 - gamma_t}
+//          (t < 32), two factors no larger than 1 for gates in (0, 1]
 //   solve  wave 0 inverts the four 16 x 16 diagonal blocks of I - A by
 //          forward substitution, 16 lanes per block and one column per lane
 //   L1/L2  the off-diagonal blocks of T by two levels of 2 x 2 block
 //          inversion, (L^-1)_21 = L22^-1 A21 L11^-1 (fp32 16x16x4 MFMA)
-//   store  -T diag(beta e^gamma) and T diag(beta), bf16, to the workspace
+//   store  T diag(beta), bf16, to the workspace
 // ---------------------------------------------------------------------------
 struct PrepItem {
     int slot, h, nvalid;                       // nvalid = 0: nothing to do
@@ -408,34 +396,31 @@ __device__ __forceinline__ PrepItem prep_locate(const int32_t *cu, int item, int
     return it;
 }
 
-__global__ void __launch_bounds__(P_NT, 3)
-chunk_prep_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
-                  const float *__restrict__ g, const float *__restrict__ beta,
-                  const int32_t *__restrict__ cu_seqlens, bf16 *__restrict__ ws, int T, int H,
-                  int Hk, int N, int nslots)
+__global__ void __launch_bounds__(P_NT, P_WG_PER_CU)
+chunk_prep_kernel(const bf16 *__restrict__ k, const float *__restrict__ g,
+                  const float *__restrict__ beta, const int32_t *__restrict__ cu_seqlens,
+                  bf16 *__restrict__ ws, int T, int H, int Hk, int N, int nslots)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     bf16 *sK = reinterpret_cast<bf16 *>(smem + P_OFF_R1);
     float *sT = reinterpret_cast<float *>(smem + P_OFF_R1);
-    bf16 *sQ = reinterpret_cast<bf16 *>(smem + P_OFF_R2);
     float *sA = reinterpret_cast<float *>(smem + P_OFF_A);
     float *sY = reinterpret_cast<float *>(smem + P_OFF_Y);
     float *sGl = reinterpret_cast<float *>(smem + P_OFF_SC);   // gamma log2(e)
     float *sBeta = sGl + C;
-    float *sBegN = sBeta + C;                                  // -beta e^gamma
-    float *sE = sBegN + C;
+    float *sE = sBeta + C;
 
     const int tid0 = (int)threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
     const int nitems = nslots * H;
     const int stride = (int)gridDim.x;
-    const int tstride = Hk * DK;               // elements between consecutive tokens of K, Q
+    const int tstride = Hk * DK;               // elements between consecutive tokens of K
 
-    // K and Q rows (tid >> 4) + 16 u, columns 8 (tid & 15) ..; g and beta of
-    // token `lane`. Buffer loads bounded by the chunk's valid tokens: rows
-    // past the end of the sequence (and every row of an empty item) read zero.
+    // K rows (tid >> 4) + 16 u, columns 8 (tid & 15) ..; g and beta of token
+    // `lane`. Buffer loads bounded by the chunk's valid tokens: rows past the
+    // end of the sequence (and every row of an empty item) read zero.
     struct Pre {
-        bf16x8 kr[4], qr[4];
+        bf16x8 kr[4];
         float gv, bv;
     };
     auto fetch = [&](const PrepItem &it, Pre &p) {
@@ -443,15 +428,11 @@ chunk_prep_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         const unsigned nb = (unsigned)it.nvalid * tstride * 2;
         const size_t hoff = tok0 * tstride + (size_t)(it.h / (H / Hk)) * DK;   // query/key head
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(k + hoff), 0, nb, 0x00020000);
-        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)(q + hoff), 0, nb, 0x00020000);
         const unsigned off = (unsigned)(((tid0 >> 4) * tstride + 8 * (tid0 & 15)) * 2);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 4; ++u)
             p.kr[u] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
                           rk, off, (unsigned)(16 * u * tstride * 2), 0));
-            p.qr[u] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                          rq, off, (unsigned)(16 * u * tstride * 2), 0));
-        }
         const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(g + tok0 * H + it.h), 0, (unsigned)it.nvalid * H * 4, 0x00020000);
         const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
@@ -459,7 +440,6 @@ chunk_prep_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         p.gv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, 4 * H * (tid0 & 63), 0, 0));
         p.bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, 4 * H * (tid0 & 63), 0, 0));
     };
-
 
     // one item: stage `p` (the current item's loads) into LDS, start the loads
     // of `nit` into `pn` (which may be `p`), locate item `after` into `ait`,
@@ -480,10 +460,8 @@ chunk_prep_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         if (it.nvalid > 0) {
             const int col = 8 * (tid & 15);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < 4; ++u)
                 *reinterpret_cast<bf16x8 *>(sK + ((tid >> 4) + 16 * u) * P_LD_K + col) = p.kr[u];
-                *reinterpret_cast<bf16x8 *>(sQ + ((tid >> 4) + 16 * u) * P_LD_K + col) = p.qr[u];
-            }
             if (wave == 0) {
                 __builtin_amdgcn_s_setprio(2);     // as in the solve: the others wait for it
                 const float gam = wave_inclusive_scan(p.gv);
@@ -491,7 +469,6 @@ chunk_prep_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                     float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gam), 32));
                 sGl[lane] = gam * 1.4426950408889634f;
                 sBeta[lane] = p.bv;
-                sBegN[lane] = -p.bv * __expf(gam);
                 sE[lane] = __expf(lane >= 32 ? gam - g32 : g32 - gam);
                 __builtin_amdgcn_s_setprio(0);
             }
@@ -502,30 +479,25 @@ chunk_prep_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         lds_barrier();
         bf16 *dst = ws + ((size_t)it.h * nslots + it.slot) * ITEM_ELEMS;
 
-        // ---- gram tiles of A and P^T (waves 0 and 1, whose diagonal tiles
-        //      take an exponential per element, go first in issue) ----
+        // ---- gram tiles of A (waves 0 and 1, whose diagonal tiles take an
+        //      exponential per element, go first in issue) ----
         if (wave < 2) __builtin_amdgcn_s_setprio(1);
         if (wave < 3) {
-            const int ti = wave == 0 ? 0 : 1, tj = wave == 1 ? 1 : 0, qb = wave == 0 ? 0 : 1;
-            f32x16 at = {}, pt = {};
+            const int ti = wave == 0 ? 0 : 1, tj = wave == 1 ? 1 : 0;
+            f32x16 at = {};
 #pragma unroll
             for (int hk = 0; hk < 2; ++hk) {
-                bf16x8 fa[4], fb[4], fq[4];
+                bf16x8 fa[4], fb[4];
 #pragma unroll
                 for (int s2 = 0; s2 < 4; ++s2) {
                     fa[s2] = frag32(sK, P_LD_K, 32 * ti, 64 * hk + 16 * s2, lane);
                     fb[s2] = frag32(sK, P_LD_K, 32 * tj, 64 * hk + 16 * s2, lane);
-                    fq[s2] = frag32(sQ, P_LD_K, 32 * qb, 64 * hk + 16 * s2, lane);
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int s2 = 0; s2 < 4; ++s2) {
-                    at = mfma32(fa[s2], fb[s2], at);
-                    pt = mfma32(fb[s2], fq[s2], pt);
-                }
+                for (int s2 = 0; s2 < 4; ++s2) at = mfma32(fa[s2], fb[s2], at);
             }
-            // element r: A row i = 32 ti + acc_row(r), column j = 32 tj + l32;
-            // P^T row (key) 32 tj + acc_row(r), column (query) 32 qb + l32
+            // element r: A row i = 32 ti + acc_row(r), column j = 32 tj + l32
             if (wave < 2) {
                 const int j = 32 * tj + l32;
                 const float glj = sGl[j];
@@ -535,35 +507,20 @@ chunk_prep_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
                     for (int s2 = 0; s2 < 4; ++s2) {
                         const int r = 4 * qq + s2, i = 32 * ti + acc_row(r, lane);
-                        const bool below = j < i;
-                        const float d = gli[s2] - glj;
-                        const float e = __builtin_amdgcn_exp2f(below ? d : -d);
-                        at[r] = below ? -(bi[s2] * at[r]) * e : 0.f;
-                        pt[r] = below ? 0.f : pt[r] * e;
+                        const float e = __builtin_amdgcn_exp2f(gli[s2] - glj);
+                        at[r] = j < i ? -(bi[s2] * at[r]) * e : 0.f;
                     }
                 }
             } else {
-                const float ej = sE[l32], eq = sE[32 + l32];
+                const float ej = sE[l32];
 #pragma unroll
                 for (int qq = 0; qq < 4; ++qq) {
-                    const f32x4 ei = rows4(sE, 32, qq), bi = rows4(sBeta, 32, qq), ek = rows4(sE, 0, qq);
+                    const f32x4 ei = rows4(sE, 32, qq), bi = rows4(sBeta, 32, qq);
 #pragma unroll
                     for (int s2 = 0; s2 < 4; ++s2) {
                         const int r = 4 * qq + s2;
                         at[r] = -(bi[s2] * at[r]) * (ei[s2] * ej);
-                        pt[r] = pt[r] * (ek[s2] * eq);
                     }
-                }
-            }
-            // P straight to the workspace: query row 32 qb + l32 (rows 0-31 keep
-            // keys 0-31, rows 32-63 all 64), keys 32 tj + 8 (r / 4) + 4 lh + 0..3
-            {
-                const int qrow = 32 * qb + l32;
-                bf16 *prow = dst + 8 * WS_TWU + (qrow < 32 ? 32 * qrow : 1024 + 64 * (qrow - 32));
-#pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
-                    bf16x4 x = {(bf16)pt[4 * gq], (bf16)pt[4 * gq + 1], (bf16)pt[4 * gq + 2], (bf16)pt[4 * gq + 3]};
-                    *reinterpret_cast<bf16x4 *>(prow + 32 * tj + 8 * gq + 4 * lh) = x;
                 }
             }
             // rows 16-63, columns 0-47 of A into sA (the off-diagonal blocks are
@@ -591,10 +548,10 @@ chunk_prep_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                 }
             }
         }
-        lds_barrier();                         // A complete; K and Q no longer read
+        lds_barrier();                         // A complete; K no longer read
 
         __builtin_amdgcn_s_setprio(0);
-        solve_store(sA, sY, sT, sBegN, sBeta, dst, tid, wave);
+        solve_store(sA, sY, sT, sBeta, dst, tid, wave);
         lds_barrier();                         // T and the scalars read before the next item
     };
 
@@ -648,13 +605,15 @@ chunk_prep_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 // XOR-swizzled by the row): the diagonal block from its own rows before the
 // workgroup barrier (P's with bf16 hi + lo operand splits), the blocks left
 // of it after. The triangular solve and the T stores are those of the scalar
-// prep pass (with -T_u in the -T_w slot).
-// Workspace item (CH_ITEM_ELEMS bf16): pieces of -T_u and T_u, P, as in the
-// scalar item; then K+ and K^ ([64][128] row-major); Q+ in the output waves'
+// prep pass.
+// Workspace item (CH_ITEM_ELEMS bf16): the pieces of T_u as in the scalar
+// item, then P (rows 0-31 by keys 0-31, rows 32-63 by keys 0-63,
+// row-major); then K+ and K^ ([64][128] row-major); Q+ in the output waves'
 // operand order (fragment f = 4 (t / 16) + c / 32 of 1 KiB, lane 16 ((c / 8)
 // % 4) + t % 16, 8 channels); then e^{gamma_63} (128 fp32).
 // ---------------------------------------------------------------------------
-constexpr int CH_KP = ITEM_ELEMS;              // element offsets inside the item
+constexpr int CH_P = ITEM_ELEMS;               // element offsets inside the item
+constexpr int CH_KP = CH_P + 8 * WS_P;
 constexpr int CH_KH = CH_KP + C * DK;
 constexpr int CH_QP = CH_KH + C * DK;
 constexpr int CH_EC = CH_QP + C * DK;          // 128 fp32 = 256 bf16 slots
@@ -1058,17 +1017,17 @@ chunk_prep_channel_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k
             bf16x4 x;
 #pragma unroll
             for (int r = 0; r < 4; ++r) x[r] = (bf16)(16 * J + 4 * kq + r <= qi ? aP[r] : 0.f);
-            bf16 *prow = dst + 8 * WS_TWU + (qi < 32 ? 32 * qi : 1024 + 64 * (qi - 32));
+            bf16 *prow = dst + CH_P + (qi < 32 ? 32 * qi : 1024 + 64 * (qi - 32));
             *reinterpret_cast<bf16x4 *>(prow + 16 * J + 4 * kq) = x;
         }
         if (I == 0 || I == 2) {                // keys 16 I + 16 .. 16 I + 31 of these rows are stored: zero
             const int qi = 16 * I + m;
-            bf16 *prow = dst + 8 * WS_TWU + (qi < 32 ? 32 * qi : 1024 + 64 * (qi - 32));
+            bf16 *prow = dst + CH_P + (qi < 32 ? 32 * qi : 1024 + 64 * (qi - 32));
             *reinterpret_cast<bf16x4 *>(prow + 16 * (I + 1) + 4 * kq) = bf16x4{};
         }
         __builtin_amdgcn_s_setprio(0);
         lds_barrier();                         // A complete
-        solve_store(sA, sY, sT, sNegBeta, sBeta, dst, tid, wave);
+        solve_store(sA, sY, sT, sBeta, dst, tid, wave);
         lds_barrier();                         // T and the scalars read before the next item
     };
 
@@ -1093,33 +1052,39 @@ chunk_prep_channel_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k
 // the wave keeps its slice of S^T (128 x 16, fp32) in eight 16x16 MFMA
 // accumulators for the whole sequence, and per chunk computes
 //   X     = K S^T                       (B operand: the state accumulators)
-//   Delta = T_u V - T_w X               (B operand: X's accumulators)
+//   R     = V - diag(e^gamma) X         (vector ALU, on X's accumulators)
+//   Delta = T_u R                       (B operand: R from X's accumulators)
 //   S^T  <- e^{gamma_63} S^T + K^T Delta~,  Delta~_j = e^{gamma_63 - gamma_j} Delta_j
 //                                       (B operand: Delta~'s accumulators)
 // entirely in registers: an accumulator pair holds rows 4 (lane/16) + r of
 // two 16-row tiles, which is a B operand over that row order, and the A
 // operands are read in the matching order (K rows for X chosen per lane,
-// K^T for the update transposed on read). Grouping T_w K S^T as T_w (K S^T)
-// means W = T_w K is never formed.
-// Waves 2 and 3 form the output, wave 2 for tokens 0-31 of the chunk and
-// wave 3 for tokens 32-63, each over all 32 columns of the tile:
-// O^T = (S Q^T) diag(e^gamma) + Delta^T P^T, the second term one chunk later,
-// with P = lower_incl_diag(Q K^T * Gamma) from the prep pass; the rows of S and
-// Delta^T are taken in an order that leaves 8 consecutive d_v of one token in
-// each lane, stored as 16 bytes. Waves 4-7 stage the next chunk; waves 4 and 5
-// also stage P.
+// K^T for the update transposed on read). T_u (V - diag(e^gamma) K S^T) is
+// "5. Linear Attention"'s U - W S^T with W = T diag(beta e^gamma) K: neither
+// W nor U is formed.
+// Waves 2 and 3 form the output, each for two of the chunk's four 16-token
+// tiles (wave 2 tiles 0 and 3, wave 3 tiles 1 and 2: equal work) over all 32
+// columns of the tile: O^T = (S Q^T) diag(e^gamma) + Delta^T P^T, the second
+// term one chunk later. P^T = upper_incl(K Q^T * Gamma^T) is formed by the
+// same waves from the staged K and Q tiles (its Q operand is the one S Q^T
+// reads) and held in registers until Delta arrives; the rows of S and
+// Delta^T are taken in an order that leaves 8 consecutive d_v of one token
+// in each lane, stored as 16 bytes. With a per-channel decay P comes from the
+// workspace instead (its decay is per channel) and waves 2 and 3 take tokens
+// 0-31 and 32-63. Waves 4-7 stage the next chunk.
 //
 // Iteration c (buffers b = c % 2):
 //   waves 0-1  recurrence step of chunk c: reads staging b, writes Delta^T
 //              into copy b and the new bf16 S into copy (c + 1) % 2
-//   waves 2-3  S Q^T of chunk c (S copy b, staging b); finish chunk c - 1
-//              (Delta^T and P copies (c - 1) % 2) and store its output rows
-//   waves 4-5  P of chunk c (in registers since iteration c - 2) into copy b
+//   waves 2-3  S Q^T and P^T of chunk c (S copy b, staging b); finish chunk
+//              c - 1 (Delta^T copy (c - 1) % 2) and store its output rows
+//   waves 4-5  (per-channel decay) P of chunk c, loaded in iteration c - 2,
+//              into copy b
 //   waves 4-7  store chunk c + 1 (in registers since iteration c - 2) into
 //              staging (c + 1) % 2, load chunk c + 3 into the registers
 //   barrier
 // Tokens past the end of a sequence are identity steps (q = k = v = 0,
-// g = 0, and T_w, T_u vanish on them) and their outputs are not stored.
+// g = 0, and T_u vanishes on them) and their outputs are not stored.
 // ---------------------------------------------------------------------------
 template <bool PERCH>
 __global__ void __launch_bounds__(NT, 1)
@@ -1135,8 +1100,8 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     auto stQ = [&](int b) { return lds + (OFF_BUF + b * SZ_BUF + B_Q) / 2; };
     auto stK = [&](int b) { return lds + (OFF_BUF + b * SZ_BUF + B_K) / 2; };
     auto stV = [&](int b) { return lds + (OFF_BUF + b * SZ_BUF + B_V) / 2; };
-    auto stTH = [&](int b) { return lds + (OFF_BUF + b * SZ_BUF + B_TH) / 2; };   // [64][LD_H]
-    auto stTL = [&](int b) { return lds + (OFF_BUF + b * SZ_BUF + B_TL) / 2; };   // [64][LD_L]
+    auto stTH = [&](int b) { return lds + (OFF_BUF + b * SZ_BUF + B_TH) / 2; };   // [32][LD_H]
+    auto stTL = [&](int b) { return lds + (OFF_BUF + b * SZ_BUF + B_TL) / 2; };   // [32][LD_L]
     auto stSc = [&](int b) { return reinterpret_cast<float *>(smem + OFF_BUF + b * SZ_BUF + B_SC); };
     auto cpP = [&](int b) { return lds + (OFF_P + b * SZ_P) / 2; };
     auto cpS = [&](int b) { return lds + (OFF_S + b * SZ_S) / 2; };
@@ -1158,7 +1123,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     seq_bounds(cu_seqlens, n, T, bos, eos);
     const int len = (int)(eos - bos);
     const int nchunks = (len + C - 1) / C;
-    // workspace item stride: the per-channel item also holds K+, K^, Q+ and
+    // workspace item stride: the per-channel item also holds P, K+, K^, Q+ and
     // the chunk's per-channel decay
     constexpr int IST = PERCH ? CH_ITEM_ELEMS : ITEM_ELEMS;
     const bf16 *wsh = ws + ((size_t)h * nslots + (size_t)((bos >> 6) + n)) * IST;
@@ -1200,16 +1165,15 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     //      16-byte buffer loads per lane:
     //        b[0..7]  Q (wi 0, 1) or K (wi 2, 3) rows 32 (wi % 2) + lane/16 + 4 r,
     //                 columns 8 (lane % 16) ..
-    //        t[0..2]  workspace pieces 192 wi + 64 r + lane of -T_w, T_u
+    //        t[0..2]  (wi 0, 1) workspace pieces 192 wi + 64 r + lane of T_u
     //        v[0..1]  (wi 2, 3) V rows lane/4 + 16 (2 (wi - 2) + r), 8 columns of
     //                 this tile
     //        g        (wi 3) g of token lane
     //      A buffer resource per chunk spans the chunk's tokens inside the
     //      sequence only: loads past its end read as zero, which turns tokens
     //      past the end into identity steps with no clamping or masking.
-    //      Workspace piece order (8 bf16 each): 0..255 rows 32-63 of -T_w (8
-    //      per row), 256..511 rows 32-63 of T_u, 512..639 rows 0-31 of -T_w (4
-    //      per row: columns 0-31), 640..767 rows 0-31 of T_u. ----
+    //      Workspace piece order (8 bf16 each): 0..255 rows 32-63 of T_u (8
+    //      per row), 256..383 rows 0-31 (4 per row: columns 0-31). ----
     // elements between tokens of the staged Q and K tiles (per channel: the
     // workspace's K^ and K+ rows)
     const int tstride = PERCH ? DK : Hk * DK;
@@ -1223,8 +1187,8 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     // LDS element offset of workspace piece e within a staging buffer (uniform
     // per 64-piece group)
     auto tpiece_loff = [&](int e) {
-        return e < 512 ? B_TL / 2 + (e >> 3) * LD_L + 8 * (e & 7)
-                       : B_TH / 2 + ((e - 512) >> 2) * LD_H + 8 * (e & 3);
+        return e < 256 ? B_TL / 2 + (e >> 3) * LD_L + 8 * (e & 7)
+                       : B_TH / 2 + ((e - 256) >> 2) * LD_H + 8 * (e & 3);
     };
     const bf16 *qk_head = (qkmat ? k : q) + (size_t)bos * (Hk * DK) + (size_t)(h / (H / Hk)) * DK;
     const bf16 *v_head = v + (size_t)bos * tsv + (size_t)h * DV + cbase;
@@ -1237,9 +1201,10 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         f32x2 ec;                              // per channel: e^{gamma_63}, channels 2 lane ..
     };
     Pref pA, pB;
-    // WG: whether this wave loads and scans g, WV: whether it loads V
-    // (compile-time flags, so that no loop holds a load it may not need)
-    auto fetch = [&](int ch, Pref &rs, auto WG, auto WV) {
+    // WT: whether this wave loads T_u pieces, WG: whether it loads and scans
+    // g, WV: whether it loads V (compile-time flags, so that no loop holds a
+    // load it may not need)
+    auto fetch = [&](int ch, Pref &rs, auto WT, auto WG, auto WV) {
         const int base = ch * C;
         const int nrow = len - base < C ? len - base : C;      // tokens of the chunk in the sequence
         const unsigned nb = (unsigned)nrow * tstride * 2;
@@ -1248,16 +1213,18 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                                    : qk_head + (size_t)base * tstride;
         const __amdgpu_buffer_rsrc_t rqk = __builtin_amdgcn_make_buffer_rsrc(
             (void *)qk_src, 0, nb, 0x00020000);
-        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(wsh + (size_t)ch * IST), 0, WS_TWU * 16, 0x00020000);
 #pragma unroll
         for (int r = 0; r < 8; ++r)
             rs.b[r] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
                           rqk, goffQK, r * 4 * tstride * 2, 0));
+        if constexpr (decltype(WT)::value) {
+            const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(wsh + (size_t)ch * IST), 0, WS_T * 16, 0x00020000);
 #pragma unroll
-        for (int r = 0; r < 3; ++r)
-            rs.t[r] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                          rw, 16 * lane0, 16 * (192 * wi + 64 * r), 0));
+            for (int r = 0; r < 3; ++r)
+                rs.t[r] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                              rw, 16 * lane0, 16 * (192 * wi + 64 * r), 0));
+        }
         if constexpr (decltype(WV)::value) {
             // with CHAIN_ZERO_V the resource spans nothing and every load reads zero
             const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
@@ -1282,14 +1249,16 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             }
         }
     };
-    auto store = [&](const Pref &rs, int b, auto WG, auto WV, int lane) {
+    auto store = [&](const Pref &rs, int b, auto WT, auto WG, auto WV, int lane) {
         bf16 *buf = lds + (OFF_BUF + b * SZ_BUF) / 2;
         const int lrow = (qkmat ? B_K : B_Q) / 2 + (32 * (wi & 1) + (lane >> 4)) * LD_R + 8 * (lane & 15);
 #pragma unroll
         for (int r = 0; r < 8; ++r) *reinterpret_cast<bf16x8 *>(buf + lrow + 4 * r * LD_R) = rs.b[r];
+        if constexpr (decltype(WT)::value) {
 #pragma unroll
-        for (int r = 0; r < 3; ++r)
-            *reinterpret_cast<bf16x8 *>(buf + tpiece_loff(192 * wi + 64 * r + lane)) = rs.t[r];
+            for (int r = 0; r < 3; ++r)
+                *reinterpret_cast<bf16x8 *>(buf + tpiece_loff(192 * wi + 64 * r + lane)) = rs.t[r];
+        }
         if constexpr (decltype(WV)::value) {
 #pragma unroll
             for (int r = 0; r < 2; ++r)
@@ -1306,8 +1275,8 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             if constexpr (PERCH) *reinterpret_cast<f32x2 *>(sc + 3 * C + 2 * lane) = rs.ec;
         }
     };
-    const std::true_type with_g{}, with_v{}, with_p{};
-    const std::false_type no_g{}, no_v{}, no_p{};
+    const std::true_type with_t{}, with_g{}, with_v{}, with_p{};
+    const std::false_type no_t{}, no_g{}, no_v{}, no_p{};
 
     // Each wave role runs its own loop, unrolled by two from the odd chunk -3
     // so that every buffer and register-set index is a compile-time constant:
@@ -1335,25 +1304,30 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             const int lane = tidl & 63, m = lane & 15, qq = lane >> 4;
             if (ch >= 0 && ch < nchunks) {
                 const bf16 *sK = stK(b), *sV = stV(b), *sTH = stTH(b), *sTL = stTL(b);
-                // rows 16 t + m of -T_w (u = 0) or T_u (u = 1), columns 32 s + 8 q ..
-                auto tfrag = [&](int u, int t, int s2) {
-                    return t < 2 ? lds8(sTH, (32 * u + 16 * t + m) * LD_H + 8 * qq)
-                                 : lds8(sTL, (32 * u + 16 * (t - 2) + m) * LD_L + 32 * s2 + 8 * qq);
+                // rows 16 t + m of T_u, columns 32 s + 8 q ..
+                auto tfrag = [&](int t, int s2) {
+                    return t < 2 ? lds8(sTH, (16 * t + m) * LD_H + 8 * qq)
+                                 : lds8(sTL, (16 * (t - 2) + m) * LD_L + 32 * s2 + 8 * qq);
                 };
                 const float *sEg = stSc(b) + C, *sDend = stSc(b) + 2 * C;
                 // Every LDS operand of the chunk is read before it is needed, so
                 // that no LDS round trip sits between two dependent products:
-                // the gates, K, V, T_u and -T_w first; K^T once X's products
-                // have been issued (into K's registers).
-                f32x4 dend[4];
+                // the gates, K, V and T_u first; K^T once X's products have
+                // been issued (into K's registers).
+                f32x4 dend[4], eg[2][2];
 #pragma unroll
                 for (int t = 0; t < 4; ++t) dend[t] = *reinterpret_cast<const f32x4 *>(sDend + 16 * t + 4 * qq);
+                // e^gamma of tokens 32 s + 8 q + 0..7 (R's rows)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+                        eg[s2][u] = *reinterpret_cast<const f32x4 *>(sEg + 32 * s2 + 8 * qq + 4 * u);
                 const float eend = sEg[C - 1];
-                // U = T_u V and X = K S^T
                 f32x4 dacc[4], xacc[4];
 #pragma unroll
                 for (int t = 0; t < 4; ++t) { dacc[t] = f32x4{0.f, 0.f, 0.f, 0.f}; xacc[t] = dacc[t]; }
-                bf16x8 fw[4][2];
+                bf16x8 fv[2], fu[4][2];
                 {
                     // X tile t takes K rows 32 (t/2) + 8 (m/4) + 4 (t%2) + m%4, so that its
                     // accumulator pairs run over tokens 32 s + 8 q + 0..7 contiguously
@@ -1364,8 +1338,8 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
                         for (int s2 = 0; s2 < 4; ++s2) fk[t][s2] = lds8(sK, row * LD_R + 32 * s2 + 8 * qq);
                     }
-                    // V as B operand: tokens 32 s + 8 q + 0..7 of column 16 hv + m
-                    bf16x8 fv[2], fu[4][2];
+                    // V in X's accumulator-pair layout: tokens 32 s + 8 q + 0..7 of
+                    // column 16 hv + m
 #pragma unroll
                     for (int s2 = 0; s2 < 2; ++s2) {
                         const int off = (32 * s2 + 8 * qq + (m >> 2)) * LD_H + 16 * hv + 4 * (m & 3);
@@ -1375,30 +1349,20 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                     for (int t = 0; t < 4; ++t)
 #pragma unroll
                         for (int s2 = 0; s2 < 2; ++s2)
-                            if (s2 <= (t >> 1)) fu[t][s2] = tfrag(1, t, s2);
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-#pragma unroll
-                        for (int s2 = 0; s2 < 2; ++s2)
-                            if (s2 <= (t >> 1)) fw[t][s2] = tfrag(0, t, s2);
+                            if (s2 <= (t >> 1)) fu[t][s2] = tfrag(t, s2);
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int s2 = 0; s2 < 4; ++s2)
 #pragma unroll
                         for (int t = 0; t < 4; ++t) xacc[t] = mfma16(fk[t][s2], Sb[s2], xacc[t]);
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-#pragma unroll
-                        for (int s2 = 0; s2 < 2; ++s2)
-                            if (s2 <= (t >> 1)) dacc[t] = mfma16(fu[t][s2], fv[s2], dacc[t]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 // K^T as the A operand of the state update: tile d, lane m takes d_k
                 // column 32 (d/2) + 8 (m/4) + 4 (d%2) + m%4 (the state's row order)
                 // and tokens 32 s + 4 q + 0..3, 32 s + 16 + 4 q + 0..3 (Delta~'s row
                 // order), transposed on read
-                // (the wait retires the reads above, -T_w's included, so that
-                // Delta's products wait for none of these)
+                // (the wait retires the reads above, so that Delta's products
+                // wait for none of these)
                 __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
                 bf16x8 fkt[8][2];
 #pragma unroll
@@ -1412,24 +1376,44 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                         fkt[d][s2] = cat4(tr4(sKu, r0 * LD_R + c0), tr4(sKu, (r0 + 16) * LD_R + c0));
                     }
                 __builtin_amdgcn_sched_barrier(0);
-                // Delta = U + (-T_w) X
+                // R = V - diag(e^gamma) X (per channel e^gamma = 1: the decay is
+                // in K+), then Delta = T_u R
                 {
-                    const bf16x8 xb0 = acc_pair_bf16(xacc[0], xacc[1]);
-                    const bf16x8 xb1 = acc_pair_bf16(xacc[2], xacc[3]);
+                    bf16x8 rb[2];
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        dacc[t] = mfma16(fw[t][0], xb0, dacc[t]);
-                        if (t >= 2) dacc[t] = mfma16(fw[t][1], xb1, dacc[t]);
-                    }
+                    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float x = e < 4 ? xacc[2 * s2][e] : xacc[2 * s2 + 1][e - 4];
+                            rb[s2][e] = (bf16)((float)fv[s2][e] - eg[s2][e >> 2][e & 3] * x);
+                        }
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+#pragma unroll
+                        for (int s2 = 0; s2 < 2; ++s2)
+                            if (s2 <= (t >> 1)) dacc[t] = mfma16(fu[t][s2], rb[s2], dacc[t]);
                 }
                 // Delta^T -> LDS (output term); Delta~ as the B operand of the update
                 bf16x8 db[2];
                 {
                     bf16 *sDt = cpDt(b);
+                    const int row = 16 * hv + m;
+                    if constexpr (PERCH) {
+                        // keys in order: the per-channel P from the workspace is
+                        // read with consecutive keys
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        bf16x4 x = {(bf16)dacc[t][0], (bf16)dacc[t][1], (bf16)dacc[t][2], (bf16)dacc[t][3]};
-                        *reinterpret_cast<bf16x4 *>(sDt + (16 * hv + m) * LD_L + ((16 * t + 4 * qq) ^ swD(16 * hv + m))) = x;
+                        for (int t = 0; t < 4; ++t) {
+                            bf16x4 x = {(bf16)dacc[t][0], (bf16)dacc[t][1], (bf16)dacc[t][2], (bf16)dacc[t][3]};
+                            *reinterpret_cast<bf16x4 *>(sDt + row * LD_L + ((16 * t + 4 * qq) ^ swD(row))) = x;
+                        }
+                    } else {
+                        // key position 32 s + 8 q + e holds key 32 s + 4 q + e (e < 4)
+                        // or 32 s + 16 + 4 q + e - 4: the order of the output waves'
+                        // P^T accumulator pairs
+#pragma unroll
+                        for (int s2 = 0; s2 < 2; ++s2)
+                            *reinterpret_cast<bf16x8 *>(sDt + row * LD_L + ((32 * s2 + 8 * qq) ^ swD(row))) =
+                                acc_pair_bf16(dacc[2 * s2], dacc[2 * s2 + 1]);
                     }
                     db[0] = acc_pair_bf16(dacc[0] * dend[0], dacc[1] * dend[1]);
                     db[1] = acc_pair_bf16(dacc[2] * dend[2], dacc[3] * dend[3]);
@@ -1462,18 +1446,33 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             lds_barrier();
         }
     } else if (wave < 4) {
-        // ============ waves 2-3: the output for tokens 32 hw .. 32 hw + 31 ============
-        // Per token tile two O^T tiles, over the d_v rows 8 (i/4) + 4 u + i%4 of
-        // tile row i (u = 0, 1): a lane's accumulators then hold d_v 8 q .. 8 q + 7
-        // of one token, stored as 16 contiguous bytes (64 per token row and
-        // instruction), and the wave reads Q only for its own tokens.
-        auto oloop = [&](auto HW) {
-            constexpr int hw = decltype(HW)::value;
-            constexpr int NS = hw + 1;         // key blocks of 32 that tokens 32 hw .. need
-            f32x4 oacc[2][2][2];               // [chunk parity][u][token tile 2 hw + tt]
-            // per channel: the wave's fragments of Q+ (Q e^gamma, from the
-            // workspace in operand order), by chunk parity, loaded one chunk ahead
-            bf16x8 fqg[PERCH ? 2 : 1][2][4];
+        // ============ waves 2-3: the output ============
+        // Per 16-token tile two O^T accumulators, over the d_v rows 8 (i/4) +
+        // 4 u + i%4 of tile row i (u = 0, 1): a lane's accumulators then hold
+        // d_v 8 q .. 8 q + 7 of one token, stored as 16 contiguous bytes (64 per
+        // token row and instruction), and the wave reads Q only for its own
+        // tokens.
+        auto store_rows = [&](const f32x4 (&acc)[2], int cp, int tt, int m, int qq) {
+            const int tok = cp * C + 16 * tt + m;
+            if (tok < len) {
+                const f32x4 a = acc[0], c = acc[1];
+                const bf16x8 x = {(bf16)(scale * a[0]), (bf16)(scale * a[1]), (bf16)(scale * a[2]), (bf16)(scale * a[3]),
+                                  (bf16)(scale * c[0]), (bf16)(scale * c[1]), (bf16)(scale * c[2]), (bf16)(scale * c[3])};
+                *reinterpret_cast<bf16x8 *>(o + ((size_t)bos + tok) * H * DV + (size_t)h * DV + cbase + 8 * qq) = x;
+            }
+        };
+        // scalar gate: token tiles TA < TB of every chunk. P^T tile (key tile
+        // kt, token tile TX) = K_kt Q_TX^T (the Q fragments of S Q^T as B
+        // operand), masked to keys j <= token i and scaled by e^{gamma_i -
+        // gamma_j} <= 1 elementwise; the accumulator pair of key tiles 2 s,
+        // 2 s + 1 is the B operand of Delta^T P^T over keys 32 s + 4 q + 0..3,
+        // 32 s + 16 + 4 q + 0..3, the order the recurrence writes Delta^T in.
+        auto oloop_scalar = [&](auto TAc, auto TBc) {
+            constexpr int TA = decltype(TAc)::value, TB = decltype(TBc)::value;
+            constexpr int TX[2] = {TA, TB};
+            constexpr int NKB[2] = {TA / 2 + 1, TB / 2 + 1};    // 32-key blocks per tile
+            f32x4 oacc[2][2][2];               // [chunk parity][tile][u]
+            bf16x8 pb[2][2][2];                // [chunk parity][tile][key block]
             for (int ch0 = -3; ch0 <= nchunks; ch0 += 2)
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
@@ -1483,20 +1482,9 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                 asm volatile("" : "+v"(tidl));
                 const int lane = tidl & 63, m = lane & 15, qq = lane >> 4;
                 const int r0 = 8 * (m >> 2) + (m & 3);     // d_v row of tile row m, u = 0
-                if constexpr (PERCH) {
-                    if (o && ch + 1 >= 0 && ch + 1 < nchunks) {
-                        const bf16 *qp = wsh + (size_t)(ch + 1) * IST + CH_QP + 8 * lane;
-#pragma unroll
-                        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                            for (int s2 = 0; s2 < 4; ++s2)
-                                fqg[hf][tt][s2] = *reinterpret_cast<const bf16x8 *>(qp + 512 * (4 * (2 * hw + tt) + s2));
-                    }
-                }
                 if (o && ch >= 0 && ch < nchunks) {   // o == NULL: the states only
-                    // (Q S^T)^T = S Q^T for the wave's 32 tokens, then e^gamma per token
-                    const bf16 *sSc = cpS(b), *sQ = stQ(b);
-                    const float *sEg = stSc(b) + C;
+                    const bf16 *sSc = cpS(b), *sQ = stQ(b), *sK = stK(b);
+                    const float *sG = stSc(b), *sEg = stSc(b) + C;
                     bf16x8 fs[2][4], fq[2][4];
 #pragma unroll
                     for (int s2 = 0; s2 < 4; ++s2) {
@@ -1504,35 +1492,128 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                         for (int u = 0; u < 2; ++u)
                             fs[u][s2] = lds8(sSc, (r0 + 4 * u) * LD_R + ((32 * s2 + 8 * qq) ^ swS(r0 + 4 * u)));
 #pragma unroll
-                        for (int tt = 0; tt < 2; ++tt) {
-                            if constexpr (PERCH) fq[tt][s2] = fqg[b][tt][s2];
-                            else fq[tt][s2] = lds8(sQ, (16 * (2 * hw + tt) + m) * LD_R + 32 * s2 + 8 * qq);
-                        }
+                        for (int x = 0; x < 2; ++x)
+                            fq[x][s2] = lds8(sQ, (16 * TX[x] + m) * LD_R + 32 * s2 + 8 * qq);
                     }
                     __builtin_amdgcn_sched_barrier(0);
+                    // (Q S^T)^T = S Q^T for the wave's tokens, then e^gamma per token
 #pragma unroll
-                    for (int u = 0; u < 2; ++u)
+                    for (int x = 0; x < 2; ++x)
 #pragma unroll
-                        for (int tt = 0; tt < 2; ++tt) oacc[b][u][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        for (int u = 0; u < 2; ++u) {
+                            f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int s2 = 0; s2 < 4; ++s2) a = mfma16(fs[u][s2], fq[x][s2], a);
+                            oacc[b][x][u] = a;
+                        }
+                    // P^T, one key tile at a time (its K fragments serve both tiles)
+                    f32x4 pacc[2][4];
+#pragma unroll
+                    for (int kt = 0; kt <= TB; ++kt) {
+                        bf16x8 fk[4];
+#pragma unroll
+                        for (int s2 = 0; s2 < 4; ++s2) fk[s2] = lds8(sK, (16 * kt + m) * LD_R + 32 * s2 + 8 * qq);
+#pragma unroll
+                        for (int x = 0; x < 2; ++x) {
+                            if (kt > TX[x]) continue;
+                            f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int s2 = 0; s2 < 4; ++s2) a = mfma16(fk[s2], fq[x][s2], a);
+                            pacc[x][kt] = a;
+                        }
+                    }
+#pragma unroll
+                    for (int x = 0; x < 2; ++x) {
+                        const int ti = 16 * TX[x] + m;             // this lane's token
+                        const float gi = sG[ti], e_i = sEg[ti];
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) oacc[b][x][u] = oacc[b][x][u] * e_i;
+#pragma unroll
+                        for (int kt = 0; kt <= TX[x]; ++kt) {
+                            const f32x4 gj = *reinterpret_cast<const f32x4 *>(sG + 16 * kt + 4 * qq);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const int j = 16 * kt + 4 * qq + r;
+                                const float e = __builtin_amdgcn_exp2f((gi - gj[r]) * 1.4426950408889634f);
+                                pacc[x][kt][r] = (kt < TX[x] || j <= ti) ? pacc[x][kt][r] * e : 0.f;
+                            }
+                        }
+#pragma unroll
+                        for (int s = 0; s < NKB[x]; ++s)
+                            pb[b][x][s] = acc_pair_bf16(pacc[x][2 * s],
+                                                        2 * s + 1 <= TX[x] ? pacc[x][2 * s + 1] : f32x4{0.f, 0.f, 0.f, 0.f});
+                    }
+                }
+                if (o && ch >= 1 && ch <= nchunks) {
+                    // finish chunk ch - 1: O^T += Delta^T P^T, then its rows to HBM
+                    const int cp = ch - 1;
+                    const bf16 *sDt = cpDt(hf);
+                    bf16x8 fd[2][2];
+#pragma unroll
+                    for (int s = 0; s < NKB[1]; ++s)
+#pragma unroll
+                        for (int u = 0; u < 2; ++u)
+                            fd[u][s] = lds8(sDt, (r0 + 4 * u) * LD_L + ((32 * s + 8 * qq) ^ swD(r0 + 4 * u)));
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int x = 0; x < 2; ++x) {
+#pragma unroll
+                        for (int s = 0; s < NKB[x]; ++s)
+#pragma unroll
+                            for (int u = 0; u < 2; ++u)
+                                oacc[hf][x][u] = mfma16(fd[u][s], pb[hf][x][s], oacc[hf][x][u]);
+                        // oacc[x][u][r] = O[token 16 TX + m][d_v 8 qq + 4 u + r]
+                        store_rows(oacc[hf][x], cp, TX[x], m, qq);
+                    }
+                }
+                lds_barrier();
+            }
+        };
+        // per-channel decay: tokens 32 hw .. 32 hw + 31, P from the workspace
+        // (staged into the P copies by waves 4-5), Q+ from the workspace in
+        // operand order, one chunk ahead
+        auto oloop_channel = [&](auto HW) {
+            constexpr int hw = decltype(HW)::value;
+            constexpr int NS = hw + 1;         // key blocks of 32 that tokens 32 hw .. need
+            f32x4 oacc[2][2][2];               // [chunk parity][token tile 2 hw + tt][u]
+            bf16x8 fqg[2][2][4];
+            for (int ch0 = -3; ch0 <= nchunks; ch0 += 2)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int ch = ch0 + hf;
+                const int b = 1 - hf;
+                int tidl = tid0;
+                asm volatile("" : "+v"(tidl));
+                const int lane = tidl & 63, m = lane & 15, qq = lane >> 4;
+                const int r0 = 8 * (m >> 2) + (m & 3);
+                if (o && ch + 1 >= 0 && ch + 1 < nchunks) {
+                    const bf16 *qp = wsh + (size_t)(ch + 1) * IST + CH_QP + 8 * lane;
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                        for (int s2 = 0; s2 < 4; ++s2)
+                            fqg[hf][tt][s2] = *reinterpret_cast<const bf16x8 *>(qp + 512 * (4 * (2 * hw + tt) + s2));
+                }
+                if (o && ch >= 0 && ch < nchunks) {
+                    const bf16 *sSc = cpS(b);
+                    bf16x8 fs[2][4];
 #pragma unroll
                     for (int s2 = 0; s2 < 4; ++s2)
 #pragma unroll
                         for (int u = 0; u < 2; ++u)
+                            fs[u][s2] = lds8(sSc, (r0 + 4 * u) * LD_R + ((32 * s2 + 8 * qq) ^ swS(r0 + 4 * u)));
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                            for (int tt = 0; tt < 2; ++tt)
-                                oacc[b][u][tt] = mfma16(fs[u][s2], fq[tt][s2], oacc[b][u][tt]);
-                    if constexpr (!PERCH) {            // per channel the decay is in Q+
+                    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                        for (int tt = 0; tt < 2; ++tt) {
-                            const float e = sEg[16 * (2 * hw + tt) + m];
+                        for (int u = 0; u < 2; ++u) {
+                            f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                            for (int u = 0; u < 2; ++u) oacc[b][u][tt] = oacc[b][u][tt] * e;
+                            for (int s2 = 0; s2 < 4; ++s2) a = mfma16(fs[u][s2], fqg[b][tt][s2], a);
+                            oacc[b][tt][u] = a;
                         }
-                    }
                 }
                 if (o && ch >= 1 && ch <= nchunks) {
-                    // finish chunk ch - 1: O^T += Delta^T P^T (token tile t needs keys
-                    // 0 .. 16 t + 15), then its rows to HBM
                     const int cp = ch - 1;
                     const bf16 *sDt = cpDt(hf), *sP = cpP(hf);
                     bf16x8 fd[2][NS], fp[2][NS];
@@ -1550,31 +1631,27 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                     }
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int s2 = 0; s2 < NS; ++s2)
-#pragma unroll
-                        for (int u = 0; u < 2; ++u)
-#pragma unroll
-                            for (int tt = 0; tt < 2; ++tt)
-                                oacc[hf][u][tt] = mfma16(fd[u][s2], fp[tt][s2], oacc[hf][u][tt]);
-                    // oacc[u][tt][r] = O[token 16 (2 hw + tt) + m][d_v 8 qq + 4 u + r]
-#pragma unroll
                     for (int tt = 0; tt < 2; ++tt) {
-                        const int tok = cp * C + 16 * (2 * hw + tt) + m;
-                        if (tok < len) {
-                            const f32x4 a = oacc[hf][0][tt], c = oacc[hf][1][tt];
-                            const bf16x8 x = {(bf16)(scale * a[0]), (bf16)(scale * a[1]), (bf16)(scale * a[2]), (bf16)(scale * a[3]),
-                                              (bf16)(scale * c[0]), (bf16)(scale * c[1]), (bf16)(scale * c[2]), (bf16)(scale * c[3])};
-                            *reinterpret_cast<bf16x8 *>(o + ((size_t)bos + tok) * H * DV + (size_t)h * DV + cbase + 8 * qq) = x;
-                        }
+#pragma unroll
+                        for (int s2 = 0; s2 < NS; ++s2)
+#pragma unroll
+                            for (int u = 0; u < 2; ++u)
+                                oacc[hf][tt][u] = mfma16(fd[u][s2], fp[tt][s2], oacc[hf][tt][u]);
+                        store_rows(oacc[hf][tt], cp, 2 * hw + tt, m, qq);
                     }
                 }
                 lds_barrier();
             }
         };
-        if (wave == 2) oloop(std::integral_constant<int, 0>{});
-        else oloop(std::integral_constant<int, 1>{});
+        if constexpr (PERCH) {
+            if (wave == 2) oloop_channel(std::integral_constant<int, 0>{});
+            else oloop_channel(std::integral_constant<int, 1>{});
+        } else {
+            if (wave == 2) oloop_scalar(std::integral_constant<int, 0>{}, std::integral_constant<int, 3>{});
+            else oloop_scalar(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{});
+        }
     } else {
-        // ============ waves 4-7: staging; waves 4-5 also stage P ============
+        // ============ waves 4-7: staging; waves 4-5 also stage P (per channel) ============
         // below the recurrence and above the output waves in issue arbitration:
         // the next chunk's tiles must be in LDS by the barrier (per channel the
         // output waves also load Q+ from memory and keep the default)
@@ -1589,7 +1666,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         const int pe0 = 192 * (wave - 4);
         auto pfetch = [&](int ch, bf16x8 (&pr)[3]) {
             const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(wsh + (size_t)ch * IST + 8 * WS_TWU), 0, WS_P * 16, 0x00020000);
+                (void *)(wsh + (size_t)ch * IST + CH_P), 0, WS_P * 16, 0x00020000);
 #pragma unroll
             for (int r = 0; r < 3; ++r)
                 pr[r] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
@@ -1605,7 +1682,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                 *reinterpret_cast<bf16x8 *>(sP + off + 8 * (grp ^ ((row & 15) >> 2))) = pr[r];
             }
         };
-        auto lloop = [&](auto WG, auto WV, auto WP) {
+        auto lloop = [&](auto WT, auto WG, auto WV, auto WP) {
             bf16x8 pp[2][3];
             for (int ch0 = -3; ch0 <= nchunks; ch0 += 2)
 #pragma unroll
@@ -1621,14 +1698,15 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                     const int cf = ch + 2 < 0 ? 0 : ch + 2 < nchunks ? ch + 2 : nchunks - 1;
                     pfetch(cf, pp[b]);
                 }
-                if (ch + 1 >= 0 && ch + 1 < nchunks) store(ps, hf, WG, WV, lane);   // chunk ch + 1
-                fetch(ch + 3 < nchunks ? ch + 3 : nchunks - 1, ps, WG, WV);
+                if (ch + 1 >= 0 && ch + 1 < nchunks) store(ps, hf, WT, WG, WV, lane);   // chunk ch + 1
+                fetch(ch + 3 < nchunks ? ch + 3 : nchunks - 1, ps, WT, WG, WV);
                 lds_barrier();
             }
         };
-        if (wave == 7) lloop(with_g, with_v, no_p);
-        else if (wave == 6) lloop(no_g, with_v, no_p);
-        else lloop(no_g, no_v, with_p);
+        if (wave == 7) lloop(no_t, with_g, with_v, no_p);
+        else if (wave == 6) lloop(no_t, no_g, with_v, no_p);
+        else if constexpr (PERCH) lloop(with_t, no_g, no_v, with_p);
+        else lloop(with_t, no_g, no_v, no_p);
     }
     if (s_final && wave < 2) {
         const int m = lane0 & 15, qq = lane0 >> 4;
@@ -1691,8 +1769,8 @@ hipError_t launch_prefill_prepare(const void *q, const void *k, const float *g, 
     hipError_t e = prep_fill((const void *)chunk_prep_kernel, P_LDS_BYTES, fill_scalar, fill);
     if (e != hipSuccess) return e;
     dim3 grid((unsigned)(nitems < fill ? nitems : fill)), block(P_NT);
-    hipLaunchKernelGGL(chunk_prep_kernel, grid, block, P_LDS_BYTES, stream, (const bf16 *)q,
-                       (const bf16 *)k, g, beta, cu, (bf16 *)ws, T, H, Hk, N, (int)nslots);
+    hipLaunchKernelGGL(chunk_prep_kernel, grid, block, P_LDS_BYTES, stream, (const bf16 *)k, g,
+                       beta, cu, (bf16 *)ws, T, H, Hk, N, (int)nslots);
     return hipGetLastError();
 }
 

@@ -69,11 +69,13 @@ def _ws_size(lib, B=1, T=8, H=1, dk=128, dv=128, N=1, varlen=0, dtype=1):
 
 
 def test_workspace_size(lib):
-    # 18 KiB of bf16 T diag(beta e^gamma), T diag(beta) (12 KiB) and the chunk's
-    # attention matrix (6 KiB) per (chunk slot, head); (tokens / 64 + N + 1) slots
-    assert _ws_size(lib, B=4, T=4096, H=16, N=4) == (GDN_OK, (4 * 4096 // 64 + 5) * 16 * 18432)
-    assert _ws_size(lib, B=1, T=1000, H=3, N=7, varlen=1) == (GDN_OK, (1000 // 64 + 8) * 3 * 18432)
-    assert _ws_size(lib, B=2, T=0, H=2, N=2) == (GDN_OK, 3 * 2 * 18432)
+    # 6 KiB of bf16 T diag(beta) (its lower 64 x 64 part: 32 x 32 + 32 x 64)
+    # per (chunk slot, head); (tokens / 64 + N + 1) slots
+    item = (32 * 32 + 32 * 64) * 2
+    assert item == 6144
+    assert _ws_size(lib, B=4, T=4096, H=16, N=4) == (GDN_OK, (4 * 4096 // 64 + 5) * 16 * item)
+    assert _ws_size(lib, B=1, T=1000, H=3, N=7, varlen=1) == (GDN_OK, (1000 // 64 + 8) * 3 * item)
+    assert _ws_size(lib, B=2, T=0, H=2, N=2) == (GDN_OK, 3 * 2 * item)
     # paths that use no workspace
     assert _ws_size(lib, dtype=0) == (GDN_OK, 0)
     assert _ws_size(lib, dk=64, dv=64) == (GDN_OK, 0)
