@@ -143,9 +143,10 @@ int gdn_prefill(const void *q, const void *k, const void *v,
 /*
  * gdn_prefill_workspace_size - bytes of workspace that gdn_prefill uses for
  * these sizes (same meaning as there, H the value heads; varlen != 0 when
- * cu_seqlens will be non-NULL). 0 when the path for these sizes uses none. The size depends on
- * the token count and the number of heads only, not on the offsets: 18 KiB
- * per (64-token chunk slot, head), with (B*T)/64 + N + 1 slots. Written to
+ * cu_seqlens will be non-NULL). 0 when the path for these sizes uses none.
+ * The size depends on the token count and the number of heads only, not on
+ * the offsets: 6 KiB per (64-token chunk slot, head), with (B*T)/64 + N + 1
+ * slots. Written to
  * *bytes; returns GDN_OK or the error gdn_prefill would return for these
  * sizes.
  */
@@ -160,16 +161,16 @@ int gdn_prefill_workspace_size(int B, int T, int H, int d_k, int d_v, int N,
  * k and g. Only the MFMA chunk path has passes (bf16, d_k = d_v = 128; else
  * GDN_ERR_UNSUPPORTED), and workspace is required (GDN_ERR_NULL).
  *
- * prepare reads q, k, g, beta and writes, for every 64-token chunk of every
- * head, the chunk's T diag(beta e^gamma) and T diag(beta) (T the inverse of
- * the unit-lower-triangular key Gram system, gamma the in-chunk prefix sum
- * of g: "5. Linear Attention" chapter, section "Chunk implementation of the
- * Delta Rule", stage 1) and its decayed intra-chunk attention matrix
- * lower(Q K^T * Gamma) into the workspace. All chunks are independent.
+ * prepare reads k, g, beta (q is validated but not read) and writes, for
+ * every 64-token chunk of every head, the chunk's T diag(beta) (T the
+ * inverse of the unit-lower-triangular key Gram system: "5. Linear
+ * Attention" chapter, section "Chunk implementation of the Delta Rule",
+ * stage 1) into the workspace. All chunks are independent.
  *
  * apply reads q, k, v, g and the workspace, walks each sequence's chunks in
  * order carrying the state, and writes o and final_state (stages 2-3 of the
- * same section). beta enters only through the workspace.
+ * same section, with the decayed intra-chunk attention lower(Q K^T * Gamma)
+ * formed on the way). beta enters only through the workspace.
  *
  * Splitting lets a caller overlap prepare of one batch with apply of
  * another on two streams (with two workspaces).
