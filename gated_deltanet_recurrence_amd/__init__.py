@@ -10,11 +10,11 @@ from ._binding import (GDNError, gdn_decode_mixer_step, gdn_decode_step,  # noqa
                        gdn_prefill_channel_workspace_size,
                        gdn_prefill_seqpar, gdn_prefill_seqpar_workspace_size,
                        gdn_mixer_epilogue,
-                       gdn_mixer_prologue, gdn_prefill, gdn_prefill_recurrent,
+                       gdn_mixer_prologue, gdn_prefill, gdn_prefill_noalloc, gdn_prefill_recurrent,
                        gdn_prefill_apply, gdn_prefill_prepare, gdn_prefill_workspace_size,
                        load)
 
-__all__ = ["GDNError", "gdn_prefill", "gdn_prefill_workspace_size", "gdn_prefill_prepare",
+__all__ = ["GDNError", "gdn_prefill", "gdn_prefill_noalloc", "gdn_prefill_workspace_size", "gdn_prefill_prepare",
            "gdn_prefill_apply", "gdn_prefill_recurrent", "gdn_decode_step",
            "gdn_decode_mixer_step", "gdn_prefill_channel_gated",
            "gdn_prefill_channel_workspace_size",

@@ -34,6 +34,7 @@ _SIGS = {
     "gdn_status_string": [_i],
     "gdn_check_cu_seqlens": [_vp, _i, _i],
     "gdn_prefill": [_vp] * 9 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
+    "gdn_prefill_noalloc": [_vp] * 9 + [_i] * 7 + [_f, _i, _vp],
     "gdn_prefill_workspace_size": [_i] * 8 + [_vp],
     "gdn_prefill_prepare": [_vp] * 5 + [_i] * 8 + [_vp, _sz, _vp],
     "gdn_prefill_apply": [_vp] * 8 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
@@ -167,6 +168,15 @@ def gdn_prefill(q, k, v, g, beta, initial_state=None, final_state=None, o=None,
     as given, None selects the single-pass path that needs none."""
     return _prefill("gdn_prefill", q, k, v, g, beta, initial_state, final_state, o,
                     cu_seqlens, scale, workspace)
+
+
+def gdn_prefill_noalloc(q, k, v, g, beta, initial_state=None, final_state=None, o=None,
+                        cu_seqlens=None, scale=None):
+    """gdn_prefill with the library's static scratch instead of a workspace
+    (see include/gdn.h): the C call allocates nothing. Pass ``o`` (and the
+    states) to allocate nothing here either. Returns (o, final_state)."""
+    return _prefill("gdn_prefill_noalloc", q, k, v, g, beta, initial_state, final_state, o,
+                    cu_seqlens, scale)
 
 
 def _ws(workspace):

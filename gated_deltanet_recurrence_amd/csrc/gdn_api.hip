@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "gdn.h"
 #include "common.h"
 
@@ -91,6 +93,40 @@ bool workspace_ok(const void *ws, size_t bytes, int B, int T, int H, int N,
 
 }  // namespace
 
+// ---- scratch of gdn_prefill_noalloc -----------------------------------------
+// A file-scope device array: every GPU the library runs on holds its own copy
+// (zero-initialised when the code object is loaded) until the process ends.
+// In host code `gdn_noalloc_scratch` names a host-side stand-in, not device
+// memory: its device address is looked up once per device with
+// hipGetSymbolAddress (the device current at the time) and only that address
+// is handed to kernels.
+static __device__ __attribute__((aligned(256))) unsigned char
+    gdn_noalloc_scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::atomic<void *> noalloc_addr[NOALLOC_MAX_DEVICES];
+
+// Device address of the current device's scratch (looked up on the first call
+// on that device; concurrent first calls store the same address).
+hipError_t noalloc_scratch(void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return hipErrorInvalidDevice;
+    void *p = noalloc_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(gdn_noalloc_scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        noalloc_addr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return hipSuccess;
+}
+}  // namespace
+
 extern "C" {
 
 int gdn_version(void) { return GDN_VERSION; }
@@ -105,6 +141,8 @@ const char *gdn_status_string(int status)
     case GDN_ERR_UNSUPPORTED: return "valid arguments, but this size or mode is not implemented";
     case GDN_ERR_HIP: return "the HIP runtime reported an error at launch";
     case GDN_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
+    case GDN_ERR_SCRATCH:
+        return "the sizes need more scratch than gdn_prefill_noalloc's static buffer holds";
     default: return "unknown status";
     }
 }
@@ -176,6 +214,29 @@ int gdn_prefill(const void *q, const void *k, const void *v, const float *g, con
     }
     return gdn_prefill_recurrent(q, k, v, g, beta, initial_state, final_state, o, cu_seqlens, B,
                                  T, H, H_k, d_k, d_v, N, scale, dtype, stream);
+}
+
+int gdn_prefill_noalloc(const void *q, const void *k, const void *v, const float *g,
+                        const float *beta, const float *initial_state, float *final_state,
+                        void *o, const int32_t *cu_seqlens, int B, int T, int H, int H_k,
+                        int d_k, int d_v, int N, float scale, int dtype, void *stream)
+{
+    int st = check_prefill(q, k, v, g, beta, o, cu_seqlens, B, T, H, H_k, d_k, d_v, N, dtype);
+    if (st != GDN_OK) return st;
+    if (!chunk_path(dtype, d_k, d_v))          // the token-serial path needs no scratch
+        return gdn_prefill_recurrent(q, k, v, g, beta, initial_state, final_state, o,
+                                     cu_seqlens, B, T, H, H_k, d_k, d_v, N, scale, dtype, stream);
+    if (gdn::prefill_split_workspace_bytes((long)B * T, H, N) > GDN_NOALLOC_SCRATCH_BYTES)
+        return GDN_ERR_SCRATCH;
+    void *ws = nullptr;
+    hipError_t e = noalloc_scratch(&ws);
+    if (e != hipSuccess) return GDN_ERR_HIP;
+    hipStream_t s = (hipStream_t)stream;
+    e = gdn::launch_prefill_prepare(q, k, g, beta, cu_seqlens, T, H, H_k, N, ws, s);
+    if (e == hipSuccess)
+        e = gdn::launch_prefill_apply(q, k, v, g, initial_state, final_state, o, cu_seqlens, T, H,
+                                      H_k, N, scale, ws, s);
+    return status_of(e);
 }
 
 int gdn_prefill_prepare(const void *q, const void *k, const float *g, const float *beta,

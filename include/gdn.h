@@ -71,8 +71,10 @@ typedef enum {
     GDN_ERR_DTYPE = -3,       /* dtype is not a gdn_dtype_t value                   */
     GDN_ERR_UNSUPPORTED = -4, /* valid but not implemented (e.g. head dim > 128)    */
     GDN_ERR_HIP = -5,         /* the HIP runtime reported an error at launch        */
-    GDN_ERR_WORKSPACE = -6    /* workspace smaller than gdn_prefill_workspace_size()
+    GDN_ERR_WORKSPACE = -6,   /* workspace smaller than gdn_prefill_workspace_size()
                                  or not 256-byte aligned                            */
+    GDN_ERR_SCRATCH = -7      /* gdn_prefill_noalloc: the sizes need more scratch
+                                 than GDN_NOALLOC_SCRATCH_BYTES                     */
 } gdn_status_t;
 
 /* Library version (GDN_VERSION). */
@@ -139,6 +141,36 @@ int gdn_prefill(const void *q, const void *k, const void *v,
                 int B, int T, int H, int H_k, int d_k, int d_v, int N,
                 float scale, int dtype,
                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gdn_prefill_noalloc - gdn_prefill for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation. Same arguments, result and kernels as gdn_prefill with a
+ * workspace, but no workspace argument: the scratch of the two-pass path is a
+ * static device buffer of GDN_NOALLOC_SCRATCH_BYTES inside the library (one
+ * per GPU, held from the library's first use of that GPU until the process
+ * ends). The call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine); the caller still passes every input and output.
+ *
+ * Limit: gdn_prefill_workspace_size() for the sizes must not exceed
+ * GDN_NOALLOC_SCRATCH_BYTES (32 MiB: 5461 (64-token chunk slot, head)
+ * items, e.g. B=4, T=4096, H=16), else GDN_ERR_SCRATCH and nothing is
+ * enqueued. Paths that use no scratch (fp32, head dims other than 128) run
+ * as in gdn_prefill.
+ *
+ * Every call on one GPU uses that GPU's one buffer: calls that overlap in
+ * time on one GPU (different streams, or different host threads without
+ * ordering) race and give wrong results. Order them on one stream. The
+ * buffer's contents between calls do not matter; nothing in it must start at
+ * zero.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int gdn_prefill_noalloc(const void *q, const void *k, const void *v,
+                        const float *g, const float *beta,
+                        const float *initial_state, float *final_state,
+                        void *o, const int32_t *cu_seqlens,
+                        int B, int T, int H, int H_k, int d_k, int d_v, int N,
+                        float scale, int dtype, void *stream);
 
 /*
  * gdn_prefill_workspace_size - bytes of workspace that gdn_prefill uses for

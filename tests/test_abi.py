@@ -12,6 +12,7 @@ HEADER = os.path.join(ROOT, "include", "gdn.h")
 
 GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_UNSUPPORTED = 0, -1, -2, -3, -4
 GDN_ERR_WORKSPACE = -6
+GDN_ERR_SCRATCH = -7
 
 
 def declared_functions():
@@ -43,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_version_and_status_strings(lib):
     assert lib.gdn_version() == 3
     for st in (GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_UNSUPPORTED, -5,
-               GDN_ERR_WORKSPACE, 99):
+               GDN_ERR_WORKSPACE, GDN_ERR_SCRATCH, 99):
         s = lib.gdn_status_string(st)
         assert isinstance(s, bytes) and len(s) > 0
 
@@ -221,3 +222,19 @@ def test_seqpar_validation(lib):
     b = list(a)
     b[7] = None                              # o
     assert sp(*b, 1, 4096, 16, 16, 128, 128, 8, 1.0, 1, ws, 1 << 40, None) == GDN_ERR_NULL
+
+
+def test_noalloc_validation(lib):
+    f = lib.gdn_prefill_noalloc
+
+    def call(null=None, B=1, T=8, H=1, dk=128, dv=128, N=1, dtype=1):
+        ptrs = [P] * 8
+        if null is not None:
+            ptrs[null] = None
+        return f(*ptrs, None, B, T, H, H, dk, dv, N, 1.0, dtype, None)
+    assert call(null=0) == GDN_ERR_NULL
+    assert call(dtype=3) == GDN_ERR_DTYPE
+    assert call(dk=48) == GDN_ERR_UNSUPPORTED
+    # beyond the static scratch (32 MiB = 5461 items of 6 KiB): rejected before launch
+    assert call(B=4, T=8192, H=16, N=4) == GDN_ERR_SCRATCH
+    assert call(B=1, T=64 * 5461, H=1) == GDN_ERR_SCRATCH
