@@ -108,8 +108,9 @@ constexpr int SZ_QK = C * LD_R * 2;            // 18432
 constexpr int SZ_V = C * LD_H * 2;             // 5120
 constexpr int SZ_TH = 32 * LD_H * 2;           // 2560: rows 0-31 of T_u
 constexpr int SZ_TL = 32 * LD_L * 2;           // 5120: rows 32-63 of T_u
-constexpr int SZ_SC = 3 * C * 4 + DK * 4;      // gamma, e^gamma, e^{gamma_63 - gamma};
-                                               // per-channel decay: e^{gamma_63} per channel
+constexpr int SZ_SC = 3 * C * 4 + DK * 4;      // gamma log2(e), e^gamma, e^{gamma_63 - gamma},
+                                               // then the key factors F of P (scalar gate)
+                                               // or e^{gamma_63} per channel
 constexpr int B_Q = 0;
 constexpr int B_K = B_Q + SZ_QK;
 constexpr int B_V = B_K + SZ_QK;
@@ -1269,10 +1270,20 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             const float gam = wave_inclusive_scan(rs.g);
             const float glast = __builtin_bit_cast(
                 float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gam), 63));
-            sc[lane] = gam;
             sc[C + lane] = __expf(gam);
             sc[2 * C + lane] = __expf(glast - gam);
-            if constexpr (PERCH) *reinterpret_cast<f32x2 *>(sc + 3 * C + 2 * lane) = rs.ec;
+            if constexpr (PERCH) {
+                *reinterpret_cast<f32x2 *>(sc + 3 * C + 2 * lane) = rs.ec;
+            } else {
+                // gamma log2(e), and F_j = e^{gamma_r - gamma_j} <= 1 with r the
+                // last token of j's 16-token tile (the key factor of P's
+                // off-diagonal tiles)
+                const float gl = gam * 1.4426950408889634f;
+                const float glr = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                    4 * (lane | 15), __builtin_bit_cast(int, gl)));
+                sc[lane] = gl;
+                sc[3 * C + lane] = __builtin_amdgcn_exp2f(glr - gl);
+            }
         }
     };
     const std::true_type with_t{}, with_g{}, with_v{}, with_p{};
@@ -1299,9 +1310,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         for (int hf = 0; hf < 2; ++hf) {
             const int ch = ch0 + hf;
             const int b = 1 - hf;              // ch % 2
-            int tidl = tid0;
-            asm volatile("" : "+v"(tidl));  // keep lane-derived addresses out of loop-invariant hoisting
-            const int lane = tidl & 63, m = lane & 15, qq = lane >> 4;
+            const int lane = lane0, m = lane & 15, qq = lane >> 4;
             if (ch >= 0 && ch < nchunks) {
                 const bf16 *sK = stK(b), *sV = stV(b), *sTH = stTH(b), *sTL = stTL(b);
                 // rows 16 t + m of T_u, columns 32 s + 8 q ..
@@ -1436,12 +1445,12 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                 }
 #pragma unroll
                 for (int s2 = 0; s2 < 4; ++s2) Sb[s2] = acc_pair_bf16(Sacc[2 * s2], Sacc[2 * s2 + 1]);
+                // the bf16 S copy for the output waves: Sb[s] is d_k 32 s + 8 q .. + 7
+                // of row 16 hv + m (the swizzle leaves the 16-byte piece whole)
                 bf16 *sSn = cpS(hf);           // (ch + 1) % 2
 #pragma unroll
-                for (int d = 0; d < 8; ++d) {
-                    bf16x4 x = {(bf16)Sacc[d][0], (bf16)Sacc[d][1], (bf16)Sacc[d][2], (bf16)Sacc[d][3]};
-                    *reinterpret_cast<bf16x4 *>(sSn + (16 * hv + m) * LD_R + ((32 * (d >> 1) + 8 * qq + 4 * (d & 1)) ^ swS(16 * hv + m))) = x;
-                }
+                for (int s2 = 0; s2 < 4; ++s2)
+                    *reinterpret_cast<bf16x8 *>(sSn + (16 * hv + m) * LD_R + ((32 * s2 + 8 * qq) ^ swS(16 * hv + m))) = Sb[s2];
             }
             lds_barrier();
         }
@@ -1452,12 +1461,12 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         // d_v 8 q .. 8 q + 7 of one token, stored as 16 contiguous bytes (64 per
         // token row and instruction), and the wave reads Q only for its own
         // tokens.
-        auto store_rows = [&](const f32x4 (&acc)[2], int cp, int tt, int m, int qq) {
+        auto store_rows = [&](const f32x4 (&acc)[2], int cp, int tt, int m, int qq, float sc) {
             const int tok = cp * C + 16 * tt + m;
             if (tok < len) {
                 const f32x4 a = acc[0], c = acc[1];
-                const bf16x8 x = {(bf16)(scale * a[0]), (bf16)(scale * a[1]), (bf16)(scale * a[2]), (bf16)(scale * a[3]),
-                                  (bf16)(scale * c[0]), (bf16)(scale * c[1]), (bf16)(scale * c[2]), (bf16)(scale * c[3])};
+                const bf16x8 x = {(bf16)(sc * a[0]), (bf16)(sc * a[1]), (bf16)(sc * a[2]), (bf16)(sc * a[3]),
+                                  (bf16)(sc * c[0]), (bf16)(sc * c[1]), (bf16)(sc * c[2]), (bf16)(sc * c[3])};
                 *reinterpret_cast<bf16x8 *>(o + ((size_t)bos + tok) * H * DV + (size_t)h * DV + cbase + 8 * qq) = x;
             }
         };
@@ -1496,46 +1505,69 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                             fq[x][s2] = lds8(sQ, (16 * TX[x] + m) * LD_R + 32 * s2 + 8 * qq);
                     }
                     __builtin_amdgcn_sched_barrier(0);
-                    // (Q S^T)^T = S Q^T for the wave's tokens, then e^gamma per token
+                    // (Q S^T)^T = S Q^T for the wave's tokens (the k-steps outermost, so
+                    // that the four accumulator chains interleave), then scale e^gamma
+                    // per token
 #pragma unroll
                     for (int x = 0; x < 2; ++x)
 #pragma unroll
-                        for (int u = 0; u < 2; ++u) {
-                            f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+                        for (int u = 0; u < 2; ++u) oacc[b][x][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                            for (int s2 = 0; s2 < 4; ++s2) a = mfma16(fs[u][s2], fq[x][s2], a);
-                            oacc[b][x][u] = a;
-                        }
-                    // P^T, one key tile at a time (its K fragments serve both tiles)
+                    for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+                        for (int x = 0; x < 2; ++x)
+#pragma unroll
+                            for (int u = 0; u < 2; ++u)
+                                oacc[b][x][u] = mfma16(fs[u][s2], fq[x][s2], oacc[b][x][u]);
+                    // P^T: the K fragments of every key tile first, then the products
+                    // with the k-steps outermost (independent chains interleave)
                     f32x4 pacc[2][4];
+                    {
+                        bf16x8 fk[TB + 1][4];
 #pragma unroll
-                    for (int kt = 0; kt <= TB; ++kt) {
-                        bf16x8 fk[4];
+                        for (int kt = 0; kt <= TB; ++kt)
 #pragma unroll
-                        for (int s2 = 0; s2 < 4; ++s2) fk[s2] = lds8(sK, (16 * kt + m) * LD_R + 32 * s2 + 8 * qq);
+                            for (int s2 = 0; s2 < 4; ++s2)
+                                fk[kt][s2] = lds8(sK, (16 * kt + m) * LD_R + 32 * s2 + 8 * qq);
+                        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                        for (int x = 0; x < 2; ++x) {
-                            if (kt > TX[x]) continue;
-                            f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+                        for (int x = 0; x < 2; ++x)
 #pragma unroll
-                            for (int s2 = 0; s2 < 4; ++s2) a = mfma16(fk[s2], fq[x][s2], a);
-                            pacc[x][kt] = a;
-                        }
+                            for (int kt = 0; kt <= TX[x]; ++kt) pacc[x][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+                            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                                for (int kt = 0; kt <= TX[x]; ++kt)
+                                    pacc[x][kt] = mfma16(fk[kt][s2], fq[x][s2], pacc[x][kt]);
                     }
+                    // masks and decays: e^gamma_i on S Q^T; on P^T tile (kt, TX)
+                    // element (key j, token i), j <= i: e^{gamma_i - gamma_j}
+                    // directly on the diagonal tile, e^{gamma_i - gamma_r} F_j below
+                    // it (r the last token of key tile kt; both factors <= 1)
+                    const float *sF = stSc(b) + 3 * C;
 #pragma unroll
                     for (int x = 0; x < 2; ++x) {
                         const int ti = 16 * TX[x] + m;             // this lane's token
-                        const float gi = sG[ti], e_i = sEg[ti];
+                        const float gs = sG[ti];                   // gamma_i log2(e)
+                        const float e_i = sEg[ti];
 #pragma unroll
                         for (int u = 0; u < 2; ++u) oacc[b][x][u] = oacc[b][x][u] * e_i;
 #pragma unroll
                         for (int kt = 0; kt <= TX[x]; ++kt) {
-                            const f32x4 gj = *reinterpret_cast<const f32x4 *>(sG + 16 * kt + 4 * qq);
+                            if (kt < TX[x]) {
+                                const float ek = __builtin_amdgcn_exp2f(gs - sG[16 * kt + 15]);
+                                const f32x4 fj = *reinterpret_cast<const f32x4 *>(sF + 16 * kt + 4 * qq);
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                const int j = 16 * kt + 4 * qq + r;
-                                const float e = __builtin_amdgcn_exp2f((gi - gj[r]) * 1.4426950408889634f);
-                                pacc[x][kt][r] = (kt < TX[x] || j <= ti) ? pacc[x][kt][r] * e : 0.f;
+                                for (int r = 0; r < 4; ++r) pacc[x][kt][r] = pacc[x][kt][r] * (ek * fj[r]);
+                            } else {
+                                const f32x4 gj = *reinterpret_cast<const f32x4 *>(sG + 16 * kt + 4 * qq);
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) {
+                                    const float e = __builtin_amdgcn_exp2f(gs - gj[r]);
+                                    pacc[x][kt][r] = 4 * qq + r <= m ? pacc[x][kt][r] * e : 0.f;
+                                }
                             }
                         }
 #pragma unroll
@@ -1563,7 +1595,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                             for (int u = 0; u < 2; ++u)
                                 oacc[hf][x][u] = mfma16(fd[u][s], pb[hf][x][s], oacc[hf][x][u]);
                         // oacc[x][u][r] = O[token 16 TX + m][d_v 8 qq + 4 u + r]
-                        store_rows(oacc[hf][x], cp, TX[x], m, qq);
+                        store_rows(oacc[hf][x], cp, TX[x], m, qq, scale);
                     }
                 }
                 lds_barrier();
@@ -1637,7 +1669,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
                             for (int u = 0; u < 2; ++u)
                                 oacc[hf][tt][u] = mfma16(fd[u][s2], fp[tt][s2], oacc[hf][tt][u]);
-                        store_rows(oacc[hf][tt], cp, 2 * hw + tt, m, qq);
+                        store_rows(oacc[hf][tt], cp, 2 * hw + tt, m, qq, scale);
                     }
                 }
                 lds_barrier();
