@@ -324,7 +324,7 @@ def bench_channel_gated(gdn, inputs, steps, warmup):
 def bench_seqpar(gdn, inputs, steps, warmup):
     """One long sequence (B=1, H=16, T=32768, d=128, bf16): the plain two-pass
     prefill (16 (sequence, head) pairs = 64 chain workgroups on 256 CUs)
-    against the sequence-parallel prefill with 4, 8 and 16 segments."""
+    against the sequence-parallel prefill with 3 to 16 segments."""
     import torch
     c = inputs.make_prefill(seed=92, B=1, T=32768, H=16)
     d = lambda t: t.cuda().contiguous()
@@ -340,9 +340,9 @@ def bench_seqpar(gdn, inputs, steps, warmup):
     res = dict(workload="one sequence B=1 H=16 T=32768 d=128 bf16",
                plain_ms=round(ms_plain, 4),
                plain_tokens_per_s=round(32768 / (ms_plain * 1e-3), 1))
-    for P in (4, 8, 16):
-        wsp = torch.empty(gdn.gdn_prefill_seqpar_workspace_size(1, 32768, 16, 128, 128, P,
-                                                                torch.bfloat16),
+    for P in (3, 4, 5, 8, 16):
+        wsp = torch.empty(gdn.gdn_prefill_seqpar_workspace_size(1, 32768, 16, 128, 128, 1, False,
+                                                                P, torch.bfloat16),
                           dtype=torch.uint8, device="cuda")
         ms = event_time(lambda i: gdn.gdn_prefill_seqpar(q, k, v, g, beta, P, None, fin, o,
                                                          scale=c.scale, workspace=wsp),
@@ -411,11 +411,26 @@ def bench_varlen(gdn, inputs, steps, warmup):
         gdn.gdn_prefill(q, k, v, g, beta, s0, fin, o, cu_seqlens=cu, scale=c.scale, workspace=ws)
     ms = event_time(step, max(1, steps // 4), 1)
     total = int(c.cu_seqlens[-1])
-    return dict(workload="packed prefill H=32 d=128 bf16, 8 sequences log-uniform in [512, 65536], "
-                         "non-zero initial states",
-                lengths=c.meta["lengths"], tokens_per_s=round(total / (ms * 1e-3), 1),
-                ms_per_step=round(ms, 4),
-                longest_sequence_tokens_per_s=round(max(c.meta["lengths"]) / (ms * 1e-3), 1))
+    res = dict(workload="packed prefill H=32 d=128 bf16, 8 sequences log-uniform in [512, 65536], "
+                        "non-zero initial states",
+               lengths=c.meta["lengths"], tokens_per_s=round(total / (ms * 1e-3), 1),
+               ms_per_step=round(ms, 4),
+               longest_sequence_tokens_per_s=round(max(c.meta["lengths"]) / (ms * 1e-3), 1))
+    del ws
+    # the same call through the sequence-parallel path, the longest sequence
+    # cut into P segments (P = 1: every sequence whole)
+    for P in (1, 2, 4):
+        wsp = torch.empty(gdn.gdn_prefill_seqpar_workspace_size(1, q.shape[1], q.shape[2], 128,
+                                                                128, N, True, P, torch.bfloat16),
+                          dtype=torch.uint8, device="cuda")
+        ms = event_time(lambda i: gdn.gdn_prefill_seqpar(q, k, v, g, beta, P, s0, fin, o,
+                                                         cu_seqlens=cu, scale=c.scale,
+                                                         workspace=wsp),
+                        max(1, steps // 4), 1)
+        res[f"seqpar_{P}_ms"] = round(ms, 4)
+        res[f"seqpar_{P}_tokens_per_s"] = round(total / (ms * 1e-3), 1)
+        del wsp
+    return res
 
 
 def bench_copy(steps, warmup, nbytes=1 << 30):

@@ -42,8 +42,8 @@ _SIGS = {
     "gdn_decode_step": [_vp] * 7 + [_i] * 5 + [_f, _i, _vp],
     "gdn_mixer_prologue": [_vp] * 14 + [_i] * 8 + [_vp],
     "gdn_mixer_epilogue": [_vp] * 4 + [_i] * 3 + [_f, _i, _vp],
-    "gdn_prefill_seqpar": [_vp] * 8 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
-    "gdn_prefill_seqpar_workspace_size": [_i] * 7 + [_vp],
+    "gdn_prefill_seqpar": [_vp] * 9 + [_i] * 8 + [_f, _i, _vp, _sz, _vp],
+    "gdn_prefill_seqpar_workspace_size": [_i] * 9 + [_vp],
     "gdn_prefill_channel_gated": [_vp] * 9 + [_i] * 7 + [_f, _i, _vp, _sz, _vp],
     "gdn_prefill_channel_workspace_size": [_i] * 8 + [_vp],
     "gdn_decode_step_channel_gated": [_vp] * 7 + [_i] * 5 + [_f, _i, _vp],
@@ -234,37 +234,42 @@ def gdn_prefill_recurrent(q, k, v, g, beta, initial_state=None, final_state=None
                     cu_seqlens, scale)
 
 
-def gdn_prefill_seqpar_workspace_size(B, T, H, d_k, d_v, segments, dtype) -> int:
+def gdn_prefill_seqpar_workspace_size(B, T, H, d_k, d_v, N, varlen, segments, dtype) -> int:
     code = dtype if isinstance(dtype, int) else _dtype_code(torch.empty(0, dtype=dtype))
     out = ctypes.c_size_t(0)
-    _check(load().gdn_prefill_seqpar_workspace_size(B, T, H, d_k, d_v, segments, code,
-                                                    ctypes.byref(out)))
+    _check(load().gdn_prefill_seqpar_workspace_size(B, T, H, d_k, d_v, N, int(bool(varlen)),
+                                                    segments, code, ctypes.byref(out)))
     return out.value
 
 
 def gdn_prefill_seqpar(q, k, v, g, beta, segments, initial_state=None, final_state=None, o=None,
-                       scale=None, workspace=None):
-    """Sequence-parallel chunked forward (see include/gdn.h): each of the B
-    sequences is cut into `segments` runs whose chains run side by side.
-    Returns (o, final_state). workspace: a uint8 GPU tensor, or None to
-    allocate one with torch."""
+                       cu_seqlens=None, scale=None, workspace=None):
+    """Sequence-parallel chunked forward (see include/gdn.h): the longest
+    sequence is cut into `segments` runs of whole chunks, the others into runs
+    of the same length, and the runs' chains go side by side. Packed sequences
+    as for gdn_prefill (B = 1, cu_seqlens). Returns (o, final_state).
+    workspace: a uint8 GPU tensor, or None to allocate one with torch."""
     B, T, Hk, dk = q.shape
     H, dv = v.shape[2], v.shape[3]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
     dt = q.dtype
     if o is None:
         o = torch.empty((B, T, H, dv), dtype=dt, device=q.device)
     if scale is None:
         scale = dk ** -0.5
     if workspace is None:
-        workspace = torch.empty(gdn_prefill_seqpar_workspace_size(B, T, H, dk, dv, segments, dt),
-                                dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(
+            gdn_prefill_seqpar_workspace_size(B, T, H, dk, dv, N, cu_seqlens is not None,
+                                              segments, dt),
+            dtype=torch.uint8, device=q.device)
     _check(load().gdn_prefill_seqpar(
         _dev(q, "q", dt), _dev(k, "k", dt, q.shape), _dev(v, "v", dt, (B, T, H, dv)),
         _dev(g, "g", torch.float32, (B, T, H)), _dev(beta, "beta", torch.float32, (B, T, H)),
-        _dev(initial_state, "initial_state", torch.float32, (B, H, dv, dk)),
-        _dev(final_state, "final_state", torch.float32, (B, H, dv, dk)),
+        _dev(initial_state, "initial_state", torch.float32, (N, H, dv, dk)),
+        _dev(final_state, "final_state", torch.float32, (N, H, dv, dk)),
         _dev(o, "o", dt, (B, T, H, dv)),
-        B, T, H, Hk, dk, dv, int(segments), float(scale), _dtype_code(q), *_ws(workspace),
+        _dev(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,)),
+        B, T, H, Hk, dk, dv, N, int(segments), float(scale), _dtype_code(q), *_ws(workspace),
         _stream(q.device)))
     return o, final_state
 

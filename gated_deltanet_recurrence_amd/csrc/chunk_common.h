@@ -12,6 +12,28 @@
 #include "common.h"
 
 namespace gdn {
+
+// Chain pass options: V read as zero; initial state the identity (the given
+// start state ignored); outputs written (job tables only). With the first two
+// and d_v = d_k the final state of a token range is the linear part A of its
+// state map S_end = S_start A + B.
+constexpr int CHAIN_ZERO_V = 1;
+constexpr int CHAIN_INIT_IDENTITY = 2;
+constexpr int CHAIN_OUTPUT = 4;
+
+// One (sequence, head)-pair slot of a chain pass driven by a job table (the
+// sequence-parallel prefill): walk the token range of segment `seg` of the
+// packed axis from `init`, into `fin`, with the options in `flags`. init and
+// fin point at [H][d_v][d_k] fp32 states (the head's block is added by the
+// kernel) or are NULL (zero start state; final state not kept). seg < 0:
+// nothing to do.
+struct SegJob {
+    int seg;
+    int flags;
+    const float *init;
+    float *fin;
+};
+
 namespace chunk {
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {

@@ -32,6 +32,7 @@
 // non-temporally (it is touched once); q, k, v, g and beta follow, shared by
 // the head's workgroups through the cache.
 #include "common.h"
+#include "launch.h"
 
 namespace gdn {
 

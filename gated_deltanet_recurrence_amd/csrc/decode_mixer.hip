@@ -34,6 +34,7 @@
 // before the prologue work starts, so the state stream is in flight while the
 // convolution is computed. Per-head sums of the RMSNorm run through LDS.
 #include "common.h"
+#include "launch.h"
 
 namespace gdn {
 

@@ -8,46 +8,7 @@
 
 #include "gdn.h"
 #include "common.h"
-
-namespace gdn {
-template <typename TIO>
-hipError_t launch_decode(const void *, const void *, const void *, const float *, const float *,
-                         float *, void *, int, int, int, int, int, float, bool, hipStream_t);
-template <typename TIO>
-hipError_t launch_prefill_recurrent(const void *, const void *, const void *, const float *,
-                                    const float *, const float *, float *, void *,
-                                    const int32_t *, int, int, int, int, int, int, float, bool,
-                                    hipStream_t);
-hipError_t launch_prefill_chunk(const void *, const void *, const void *, const float *,
-                                const float *, const float *, float *, void *, const int32_t *,
-                                int, int, int, int, float, hipStream_t);
-hipError_t launch_prefill_prepare(const void *, const void *, const float *, const float *,
-                                  const int32_t *, int, int, int, int, void *, hipStream_t,
-                                  bool per_channel = false);
-hipError_t launch_prefill_apply(const void *, const void *, const void *, const float *,
-                                const float *, float *, void *, const int32_t *, int, int, int,
-                                int, float, const void *, hipStream_t, int flags = 0,
-                                bool per_channel = false);
-size_t prefill_split_workspace_bytes(long tokens, int H, int N, bool per_channel = false);
-template <typename TIO>
-hipError_t launch_prologue(const void *, const void *, const void *, const void *, const void *,
-                           const void *, const float *, const float *, const int32_t *, void *,
-                           void *, void *, float *, float *, int, int, int, int, int, int, int,
-                           hipStream_t);
-template <typename TIO>
-hipError_t launch_decode_mixer(const void *, const void *, const void *, const void *, void *,
-                               const void *, const void *, const float *, const float *,
-                               const void *, const float *, float, float *, void *, int, int,
-                               int, int, int, float, hipStream_t);
-constexpr int DECODE_MIXER_MAX_ROWS = 4096;
-size_t prefill_seqpar_workspace_bytes(int B, int T, int H, int P);
-hipError_t launch_prefill_seqpar(const void *, const void *, const void *, const float *,
-                                 const float *, const float *, float *, void *, int, int, int,
-                                 int, int, float, void *, hipStream_t);
-template <typename TIO>
-hipError_t launch_epilogue(const void *, const void *, const float *, void *, long, int, float,
-                           hipStream_t);
-}  // namespace gdn
+#include "launch.h"
 
 namespace {
 
@@ -416,46 +377,54 @@ int gdn_decode_step_channel_gated(const void *q, const void *k, const void *v, c
     return status_of(e);
 }
 
-// Shared validation of the sequence-parallel prefill's sizes.
-static int check_seqpar(int B, int T, int H, int H_k, int d_k, int d_v, int segments, int dtype)
+// Shared validation of the sequence-parallel prefill's arguments: those of
+// gdn_prefill, on the MFMA chunk path only, and the segment count.
+static int check_seqpar(const void *q, const void *k, const void *v, const float *g,
+                        const float *beta, const void *o, const int32_t *cu, int B, int T, int H,
+                        int H_k, int d_k, int d_v, int N, int segments, int dtype)
 {
-    if (!valid_dtype(dtype)) return GDN_ERR_DTYPE;
-    if (B < 1 || T < 0 || segments < 1 || !heads_ok(H, H_k)) return GDN_ERR_SHAPE;
-    if ((int64_t)B * T > (int64_t)INT32_MAX) return GDN_ERR_SHAPE;
+    const int st = check_prefill(q, k, v, g, beta, o, cu, B, T, H, H_k, d_k, d_v, N, dtype);
+    if (st != GDN_OK) return st;
+    if (segments < 1) return GDN_ERR_SHAPE;
     if (!chunk_path(dtype, d_k, d_v)) return GDN_ERR_UNSUPPORTED;
-    if (H > 65535 || (int64_t)B * segments > 65535) return GDN_ERR_UNSUPPORTED;
-    if ((int64_t)H * B * segments * 4 > (int64_t)INT32_MAX) return GDN_ERR_UNSUPPORTED;
+    // segments (N * segments) index the 1-D chain grid of pass 1: 2 jobs per
+    // segment, H pairs per job, 4 workgroups per pair
+    if ((int64_t)N * segments > 65535) return GDN_ERR_UNSUPPORTED;
+    if ((int64_t)N * segments * H * 8 > (int64_t)INT32_MAX) return GDN_ERR_UNSUPPORTED;
     return GDN_OK;
 }
 
-int gdn_prefill_seqpar_workspace_size(int B, int T, int H, int d_k, int d_v, int segments,
-                                      int dtype, size_t *bytes)
+int gdn_prefill_seqpar_workspace_size(int B, int T, int H, int d_k, int d_v, int N, int varlen,
+                                      int segments, int dtype, size_t *bytes)
 {
     if (!bytes) return GDN_ERR_NULL;
     *bytes = 0;
-    const int st = check_seqpar(B, T, H, H, d_k, d_v, segments, dtype);
+    // the pointer checks of gdn_prefill_seqpar do not apply here: pass stand-ins
+    const int32_t *cu = varlen ? reinterpret_cast<const int32_t *>(bytes) : nullptr;
+    const void *p = bytes;
+    const int st = check_seqpar(p, p, p, (const float *)p, (const float *)p, p, cu, B, T, H, H,
+                                d_k, d_v, N, segments, dtype);
     if (st != GDN_OK) return st;
-    *bytes = gdn::prefill_seqpar_workspace_bytes(B, T, H, segments);
+    *bytes = gdn::prefill_seqpar_workspace_bytes((int64_t)B * T, H, N, segments);
     return GDN_OK;
 }
 
 int gdn_prefill_seqpar(const void *q, const void *k, const void *v, const float *g,
                        const float *beta, const float *initial_state, float *final_state,
-                       void *o, int B, int T, int H, int H_k, int d_k, int d_v, int segments,
-                       float scale, int dtype, void *workspace, size_t workspace_bytes,
-                       void *stream)
+                       void *o, const int32_t *cu_seqlens, int B, int T, int H, int H_k,
+                       int d_k, int d_v, int N, int segments, float scale, int dtype,
+                       void *workspace, size_t workspace_bytes, void *stream)
 {
-    const bool no_tokens = (int64_t)B * T == 0;
-    if (!no_tokens && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
-    if (!workspace) return GDN_ERR_NULL;
-    const int st = check_seqpar(B, T, H, H_k, d_k, d_v, segments, dtype);
+    const int st = check_seqpar(q, k, v, g, beta, o, cu_seqlens, B, T, H, H_k, d_k, d_v, N,
+                                segments, dtype);
     if (st != GDN_OK) return st;
+    if (!workspace) return GDN_ERR_NULL;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0 ||
-        workspace_bytes < gdn::prefill_seqpar_workspace_bytes(B, T, H, segments))
+        workspace_bytes < gdn::prefill_seqpar_workspace_bytes((int64_t)B * T, H, N, segments))
         return GDN_ERR_WORKSPACE;
     return status_of(gdn::launch_prefill_seqpar(q, k, v, g, beta, initial_state, final_state, o,
-                                                B, T, H, H_k, segments, scale, workspace,
-                                                (hipStream_t)stream));
+                                                cu_seqlens, T, H, H_k, N, segments, scale,
+                                                workspace, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -26,6 +26,7 @@
 // input element is read from HBM once (plus three tokens of history per
 // tile); the tile's loads are all issued before its first token is computed.
 #include "common.h"
+#include "launch.h"
 
 namespace gdn {
 

@@ -62,6 +62,7 @@
 // Lane l of the 32x32x16 form holds A[l%32][8(l/32)+e] and B[8(l/32)+e][l%32]
 // (e = 0..7); accumulator element r is C[8(r/4) + 4(l/32) + r%4][l%32].
 #include "chunk_common.h"
+#include "launch.h"
 
 namespace gdn {
 

@@ -31,6 +31,7 @@
 // once per block and overlaps the previous block's tokens. One barrier per
 // block.
 #include "common.h"
+#include "launch.h"
 
 namespace gdn {
 

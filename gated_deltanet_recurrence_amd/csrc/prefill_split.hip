@@ -45,6 +45,7 @@
 #include <type_traits>
 
 #include "chunk_common.h"
+#include "launch.h"
 
 namespace gdn {
 
@@ -96,11 +97,6 @@ static_assert(P_LDS_BYTES * P_WG_PER_CU <= 160 * 1024, "four prep workgroups per
 constexpr int MAX_DEVICES = 64;               // per-device launch caches
 constexpr int DVT = 32;
 constexpr int NT = 512;
-// chain_kernel flags: V read as zero; initial state the identity (s_init
-// ignored). With both and d_v = d_k the final state of a token range is the
-// linear part A of its state map S_end = S_start A + B.
-constexpr int CHAIN_ZERO_V = 1;
-constexpr int CHAIN_INIT_IDENTITY = 2;
 constexpr int LD_R = DK + 16;                  // 144: Q, K, S rows
 constexpr int LD_L = C + 16;                   // 80: rows 32-63 of T_u, P; Delta^T rows
 constexpr int LD_H = 32 + 8;                   // 40: rows 0-31 of T_u, P; V rows
@@ -1092,8 +1088,9 @@ __global__ void __launch_bounds__(NT, 1)
 chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                    const bf16 *__restrict__ v, const float *__restrict__ g,
                    const bf16 *__restrict__ ws, const float *s_init, float *s_final,
-                   bf16 *__restrict__ o, const int32_t *__restrict__ cu_seqlens, int T, int H,
-                   int Hk, int npairs, int nslots, float scale, int flags)
+                   bf16 *__restrict__ o, const int32_t *__restrict__ cu_seqlens,
+                   const SegJob *__restrict__ jobs, int T, int H, int Hk, int npairs, int nslots,
+                   float scale, int flags)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     bf16 *lds = reinterpret_cast<bf16 *>(smem);
@@ -1115,9 +1112,27 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     // packed sequences are dealt longest first (staging buffer 0 is free
     // until the loaders' first store, two barriers into the loop)
     const int h = pair % H, nsq = npairs / H;
-    const int n = (cu_seqlens && nsq <= RANK_MAX)
-        ? seq_of_rank(cu_seqlens, nsq, T, pair / H, reinterpret_cast<int *>(smem + OFF_BUF))
-        : pair / H;
+    const size_t hstate = (size_t)h * DV * DK;
+    int n;
+    const float *sin = nullptr;              // this head's start state, or NULL (zero)
+    float *sfin = nullptr;                   // ... end state, or NULL
+    bf16 *out = o;                           // NULL: no outputs
+    if (jobs) {                              // job table: one entry per pair / H
+        const SegJob jb = jobs[pair / H];
+        if (jb.seg < 0) return;              // uniform
+        n = jb.seg;
+        flags = jb.flags;
+        sin = jb.init ? jb.init + hstate : nullptr;
+        sfin = jb.fin ? jb.fin + hstate : nullptr;
+        if (!(flags & CHAIN_OUTPUT)) out = nullptr;
+    } else {
+        n = (cu_seqlens && nsq <= RANK_MAX)
+            ? seq_of_rank(cu_seqlens, nsq, T, pair / H, reinterpret_cast<int *>(smem + OFF_BUF))
+            : pair / H;
+        const size_t sbase = (size_t)n * H * DV * DK + hstate;
+        sin = s_init ? s_init + sbase : nullptr;
+        sfin = s_final ? s_final + sbase : nullptr;
+    }
     const int cbase = tile * DVT;
 
     long bos, eos;
@@ -1128,7 +1143,6 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     // the chunk's per-channel decay
     constexpr int IST = PERCH ? CH_ITEM_ELEMS : ITEM_ELEMS;
     const bf16 *wsh = ws + ((size_t)h * nslots + (size_t)((bos >> 6) + n)) * IST;
-    const size_t sbase = ((size_t)n * H + h) * DV * DK;
     const int lane0 = tid0 & 63;
 
     // ---- state: wave hv < 2 holds Sacc[d][r] = S[cbase + 16 hv + lane%16][dk(d, lane/16, r)]
@@ -1148,10 +1162,10 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     Sacc[d][r] = (32 * (d >> 1) + 8 * qq + 4 * (d & 1) + r == col) ? 1.f : 0.f;
-        } else if (s_init) {
+        } else if (sin) {
 #pragma unroll
             for (int d = 0; d < 8; ++d)
-                Sacc[d] = *reinterpret_cast<const f32x4 *>(s_init + sbase + (size_t)col * DK + 32 * (d >> 1) + 8 * qq + 4 * (d & 1));
+                Sacc[d] = *reinterpret_cast<const f32x4 *>(sin + (size_t)col * DK + 32 * (d >> 1) + 8 * qq + 4 * (d & 1));
         }
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) Sb[s2] = acc_pair_bf16(Sacc[2 * s2], Sacc[2 * s2 + 1]);
@@ -1467,7 +1481,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                 const f32x4 a = acc[0], c = acc[1];
                 const bf16x8 x = {(bf16)(sc * a[0]), (bf16)(sc * a[1]), (bf16)(sc * a[2]), (bf16)(sc * a[3]),
                                   (bf16)(sc * c[0]), (bf16)(sc * c[1]), (bf16)(sc * c[2]), (bf16)(sc * c[3])};
-                *reinterpret_cast<bf16x8 *>(o + ((size_t)bos + tok) * H * DV + (size_t)h * DV + cbase + 8 * qq) = x;
+                *reinterpret_cast<bf16x8 *>(out + ((size_t)bos + tok) * H * DV + (size_t)h * DV + cbase + 8 * qq) = x;
             }
         };
         // scalar gate: token tiles TA < TB of every chunk. P^T tile (key tile
@@ -1491,7 +1505,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                 asm volatile("" : "+v"(tidl));
                 const int lane = tidl & 63, m = lane & 15, qq = lane >> 4;
                 const int r0 = 8 * (m >> 2) + (m & 3);     // d_v row of tile row m, u = 0
-                if (o && ch >= 0 && ch < nchunks) {   // o == NULL: the states only
+                if (out && ch >= 0 && ch < nchunks) {   // o == NULL: the states only
                     const bf16 *sSc = cpS(b), *sQ = stQ(b), *sK = stK(b);
                     const float *sG = stSc(b), *sEg = stSc(b) + C;
                     bf16x8 fs[2][4], fq[2][4];
@@ -1576,7 +1590,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                                                         2 * s + 1 <= TX[x] ? pacc[x][2 * s + 1] : f32x4{0.f, 0.f, 0.f, 0.f});
                     }
                 }
-                if (o && ch >= 1 && ch <= nchunks) {
+                if (out && ch >= 1 && ch <= nchunks) {
                     // finish chunk ch - 1: O^T += Delta^T P^T, then its rows to HBM
                     const int cp = ch - 1;
                     const bf16 *sDt = cpDt(hf);
@@ -1618,7 +1632,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                 asm volatile("" : "+v"(tidl));
                 const int lane = tidl & 63, m = lane & 15, qq = lane >> 4;
                 const int r0 = 8 * (m >> 2) + (m & 3);
-                if (o && ch + 1 >= 0 && ch + 1 < nchunks) {
+                if (out && ch + 1 >= 0 && ch + 1 < nchunks) {
                     const bf16 *qp = wsh + (size_t)(ch + 1) * IST + CH_QP + 8 * lane;
 #pragma unroll
                     for (int tt = 0; tt < 2; ++tt)
@@ -1626,7 +1640,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                         for (int s2 = 0; s2 < 4; ++s2)
                             fqg[hf][tt][s2] = *reinterpret_cast<const bf16x8 *>(qp + 512 * (4 * (2 * hw + tt) + s2));
                 }
-                if (o && ch >= 0 && ch < nchunks) {
+                if (out && ch >= 0 && ch < nchunks) {
                     const bf16 *sSc = cpS(b);
                     bf16x8 fs[2][4];
 #pragma unroll
@@ -1645,7 +1659,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                             oacc[b][tt][u] = a;
                         }
                 }
-                if (o && ch >= 1 && ch <= nchunks) {
+                if (out && ch >= 1 && ch <= nchunks) {
                     const int cp = ch - 1;
                     const bf16 *sDt = cpDt(hf), *sP = cpP(hf);
                     bf16x8 fd[2][NS], fp[2][NS];
@@ -1740,9 +1754,9 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         else if constexpr (PERCH) lloop(with_t, no_g, no_v, with_p);
         else lloop(with_t, no_g, no_v, no_p);
     }
-    if (s_final && wave < 2) {
+    if (sfin && wave < 2) {
         const int m = lane0 & 15, qq = lane0 >> 4;
-        float *dst = s_final + sbase + (size_t)(cbase + 16 * wave + m) * DK + 8 * qq;
+        float *dst = sfin + (size_t)(cbase + 16 * wave + m) * DK + 8 * qq;
 #pragma unroll
         for (int d = 0; d < 8; ++d) *reinterpret_cast<f32x4 *>(dst + 32 * (d >> 1) + 4 * (d & 1)) = Sacc[d];
     }
@@ -1806,11 +1820,14 @@ hipError_t launch_prefill_prepare(const void *q, const void *k, const float *g, 
     return hipGetLastError();
 }
 
+// jobs: NULL, or a device table of njobs entries (one per pair / H) that
+// replaces the one pair per (sequence, head); N is then the number of
+// segments in cu.
 template <bool PERCH>
 static hipError_t launch_chain(const void *q, const void *k, const void *v, const float *g,
                                const float *s_init, float *s_final, void *o, const int32_t *cu,
                                int T, int H, int Hk, int N, float scale, const void *ws,
-                               hipStream_t stream, int flags)
+                               hipStream_t stream, int flags, const SegJob *jobs, int njobs)
 {
     // the dynamic LDS limit, raised once per process (thread-safe static)
     static const hipError_t attr = hipFuncSetAttribute(
@@ -1818,23 +1835,25 @@ static hipError_t launch_chain(const void *q, const void *k, const void *v, cons
     if (attr != hipSuccess) return attr;
     const long tokens = cu ? (long)T : (long)N * T;
     const long nslots = tokens / C + N + 1;
-    const int npairs = H * N;
+    const int npairs = H * (jobs ? njobs : N);
+    if (npairs == 0) return hipSuccess;
     dim3 grid(pair_grid(npairs)), block(NT);
     hipLaunchKernelGGL(chunk_chain_kernel<PERCH>, grid, block, LDS_BYTES, stream, (const bf16 *)q,
                        (const bf16 *)k, (const bf16 *)v, g, (const bf16 *)ws, s_init, s_final,
-                       (bf16 *)o, cu, T, H, Hk, npairs, (int)nslots, scale, flags);
+                       (bf16 *)o, cu, jobs, T, H, Hk, npairs, (int)nslots, scale, flags);
     return hipGetLastError();
 }
 
 hipError_t launch_prefill_apply(const void *q, const void *k, const void *v, const float *g,
                                 const float *s_init, float *s_final, void *o, const int32_t *cu,
                                 int T, int H, int Hk, int N, float scale, const void *ws,
-                                hipStream_t stream, int flags, bool per_channel)
+                                hipStream_t stream, int flags, bool per_channel,
+                                const SegJob *jobs, int njobs)
 {
     return per_channel ? launch_chain<true>(q, k, v, g, s_init, s_final, o, cu, T, H, Hk, N, scale,
-                                            ws, stream, flags)
+                                            ws, stream, flags, jobs, njobs)
                        : launch_chain<false>(q, k, v, g, s_init, s_final, o, cu, T, H, Hk, N, scale,
-                                             ws, stream, flags);
+                                             ws, stream, flags, jobs, njobs);
 }
 
 }  // namespace gdn

@@ -299,15 +299,22 @@ def make_channel_gated(seed: int = 7, B: int = 2, T: int = 300, H: int = 4, d: i
 
 def make_long_memory(seed: int = 200, B: int = 2, T: int = 1024, H: int = 2, d: int = 128,
                      gate: str = "zero", with_state: bool = False, dtype: str = "bf16",
-                     per_channel: bool = False) -> GDNCase:
+                     per_channel: bool = False, lengths: Optional[list] = None) -> GDNCase:
     """Long-memory regime: what is written survives many chunks.
 
     ``gate="zero"``: g = 0 (alpha = 1), the delta rule without forgetting;
     ``gate="near_one"``: alpha ~ U(0.99, 1), g = log(alpha) (per key channel
     when ``per_channel``, g then [B, T, H, d]). q,k unit Gaussian, v ~ N(0,1),
-    beta = sigmoid(N(0,1)), initial states N(0, 0.02) when ``with_state``."""
+    beta = sigmoid(N(0,1)), initial states N(0, 0.02) when ``with_state``.
+    ``lengths``: packed sequences of these lengths instead (B = 1, T their
+    sum, cu_seqlens set, one initial state per sequence)."""
     gen = _gen(seed)
     td = _TORCH_DTYPE[dtype]
+    cu, N = None, B
+    if lengths is not None:
+        B, T, N = 1, int(sum(lengths)), len(lengths)
+        cu = torch.zeros(N + 1, dtype=torch.int32)
+        cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
     q = unit_gaussian(gen, (B, T, H, d)).to(td)
     k = unit_gaussian(gen, (B, T, H, d)).to(td)
     v = _normal(gen, (B, T, H, d)).to(td)
@@ -319,9 +326,9 @@ def make_long_memory(seed: int = 200, B: int = 2, T: int = 1024, H: int = 2, d: 
     else:
         raise ValueError(f"unknown gate recipe {gate!r}")
     beta = _sigmoid_gaussian(gen, (B, T, H))
-    s0 = _normal(gen, (B, H, d, d), std=0.02) if with_state else None
-    return GDNCase("long_memory", q, k, v, g.contiguous(), beta, s0, None, 1.0 / math.sqrt(d),
-                   dtype, meta={"gate": gate, "per_channel": per_channel})
+    s0 = _normal(gen, (N, H, d, d), std=0.02) if with_state else None
+    return GDNCase("long_memory", q, k, v, g.contiguous(), beta, s0, cu, 1.0 / math.sqrt(d),
+                   dtype, meta={"gate": gate, "per_channel": per_channel, "lengths": lengths})
 
 
 @dataclass

@@ -220,36 +220,47 @@ int gdn_prefill_apply(const void *q, const void *k, const void *v, const float *
                       const void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * gdn_prefill_seqpar - the same forward pass as gdn_prefill for B sequences
- * of T tokens, with each sequence cut into `segments` runs of whole 64-token
- * chunks whose chains run side by side: for batches with too few (sequence,
- * head) pairs to fill the GPU (a single long sequence, few heads). A run of
- * tokens acts on the state as one affine map S_end = S_start A + B
- * ("Overwrite and Forget", section 7); the call computes B and A of every
- * segment by two chain passes (zero start state; v = 0 from the identity),
- * the segment start states in order, then a third chain pass with the true
- * start states that writes o. Three chain passes instead of one: use it when
- * B * H * 4 is well below the number of compute units. The result equals
- * gdn_prefill's up to rounding (the segment maps carry the bf16 rounding of
- * the chunk kernels once more).
+ * gdn_prefill_seqpar - the same forward pass as gdn_prefill, with long
+ * sequences cut into segments of whole 64-token chunks whose chains run side
+ * by side: for batches whose longest chains leave compute units idle (one
+ * long sequence, few heads, or a packed batch where one sequence is much
+ * longer than the rest). A run of tokens acts on the state as one affine map
+ * S_end = S_start A + B ("Overwrite and Forget", section 7). The longest
+ * sequence (M chunks) is cut into `segments` segments of L = ceil(M /
+ * segments) chunks and every other sequence into segments of L chunks (its
+ * last one shorter), so short sequences stay whole. A first chain pass runs
+ * every sequence's first segment from its initial state (writing outputs)
+ * and, side by side, computes B and A of every middle segment (zero start
+ * state; v = 0 from the identity); the start states of the later segments
+ * follow in order; a second chain pass runs those segments from their true
+ * start states and writes their outputs and the final states. Critical path:
+ * two segments' chains; extra work: two more chain walks of each middle
+ * segment. The result equals gdn_prefill's up to rounding (a map carries the
+ * bf16 rounding of the chunk kernels once more). segments = 1 runs each
+ * sequence as one segment, like gdn_prefill's two-pass path.
  *
- *   arguments     as gdn_prefill, without cu_seqlens (N = B); bf16 and
- *                 d_k = d_v = 128 only (else GDN_ERR_UNSUPPORTED)
- *   segments      >= 1 segments per sequence (B * segments <= 65535);
- *                 segments past the sequence's chunks are empty
+ *   arguments     as gdn_prefill, including cu_seqlens and N (packed
+ *                 sequences: B = 1); bf16 with d_k = d_v = 128 only (else
+ *                 GDN_ERR_UNSUPPORTED)
+ *   segments      >= 1, segments of the longest sequence; N * segments <=
+ *                 65535 (else GDN_ERR_UNSUPPORTED)
  *   workspace     required, gdn_prefill_seqpar_workspace_size() bytes,
- *                 256-byte aligned; contents on entry do not matter
+ *                 256-byte aligned, caller-owned; contents on entry do not
+ *                 matter. Calls that share a workspace must be ordered on one
+ *                 stream.
  */
 int gdn_prefill_seqpar(const void *q, const void *k, const void *v,
                        const float *g, const float *beta,
                        const float *initial_state, float *final_state, void *o,
-                       int B, int T, int H, int H_k, int d_k, int d_v, int segments,
+                       const int32_t *cu_seqlens,
+                       int B, int T, int H, int H_k, int d_k, int d_v, int N, int segments,
                        float scale, int dtype,
                        void *workspace, size_t workspace_bytes, void *stream);
 
-/* Bytes of workspace gdn_prefill_seqpar needs (H the value heads). */
-int gdn_prefill_seqpar_workspace_size(int B, int T, int H, int d_k, int d_v, int segments,
-                                      int dtype, size_t *bytes);
+/* Bytes of workspace gdn_prefill_seqpar needs (H the value heads; varlen
+ * non-zero when cu_seqlens will be given, as for gdn_prefill_workspace_size). */
+int gdn_prefill_seqpar_workspace_size(int B, int T, int H, int d_k, int d_v, int N, int varlen,
+                                      int segments, int dtype, size_t *bytes);
 
 /*
  * gdn_prefill_recurrent - the same forward pass as gdn_prefill, computed by

@@ -208,20 +208,32 @@ def test_channel_gated_validation(lib):
 def test_seqpar_validation(lib):
     out = ctypes.c_size_t(0)
     f = lib.gdn_prefill_seqpar_workspace_size
-    assert f(1, 4096, 16, 128, 128, 8, 1, ctypes.byref(out)) == GDN_OK and out.value > 0
-    assert f(1, 4096, 16, 64, 64, 8, 1, ctypes.byref(out)) == GDN_ERR_UNSUPPORTED
-    assert f(1, 4096, 16, 128, 128, 0, 1, ctypes.byref(out)) == GDN_ERR_SHAPE
-    assert f(1, 4096, 16, 128, 128, 8, 0, ctypes.byref(out)) == GDN_ERR_UNSUPPORTED
-    assert f(1, 4096, 16, 128, 128, 8, 1, None) == GDN_ERR_NULL
+    # B, T, H, d_k, d_v, N, varlen, segments, dtype
+    assert f(1, 4096, 16, 128, 128, 1, 0, 8, 1, ctypes.byref(out)) == GDN_OK and out.value > 0
+    one = out.value
+    assert f(1, 4096, 16, 128, 128, 8, 1, 8, 1, ctypes.byref(out)) == GDN_OK
+    assert out.value > one                   # packed: 8 sequences of up to 8 segments
+    assert f(1, 4096, 16, 64, 64, 1, 0, 8, 1, ctypes.byref(out)) == GDN_ERR_UNSUPPORTED
+    assert f(1, 4096, 16, 128, 128, 1, 0, 0, 1, ctypes.byref(out)) == GDN_ERR_SHAPE
+    assert f(1, 4096, 16, 128, 128, 1, 0, 8, 0, ctypes.byref(out)) == GDN_ERR_UNSUPPORTED
+    assert f(1, 4096, 16, 128, 128, 1, 0, 8, 1, None) == GDN_ERR_NULL
+    assert f(2, 4096, 16, 128, 128, 2, 1, 8, 1, ctypes.byref(out)) == GDN_ERR_SHAPE  # packed: B = 1
+    assert f(1, 4096, 16, 128, 128, 4096, 1, 16, 1, ctypes.byref(out)) == GDN_ERR_UNSUPPORTED
     sp = lib.gdn_prefill_seqpar
     ws = ctypes.c_void_p(1 << 20)            # never dereferenced: rejected before launch
-    a = [P] * 5 + [None, None, P]
-    assert sp(*a, 1, 4096, 16, 16, 128, 128, 8, 1.0, 1, None, 0, None) == GDN_ERR_NULL
-    assert sp(*a, 1, 4096, 16, 16, 128, 128, 8, 1.0, 1, ws, 10, None) == GDN_ERR_WORKSPACE
-    assert sp(*a, 1, 4096, 16, 5, 128, 128, 8, 1.0, 1, ws, 1 << 40, None) == GDN_ERR_SHAPE
+    a = [P] * 5 + [None, None, P, None]
+    dims = [1, 4096, 16, 16, 128, 128, 1, 8]  # B, T, H, H_k, d_k, d_v, N, segments
+    assert sp(*a, *dims, 1.0, 1, None, 0, None) == GDN_ERR_NULL
+    assert sp(*a, *dims, 1.0, 1, ws, 10, None) == GDN_ERR_WORKSPACE
+    bad = list(dims)
+    bad[3] = 5                               # H_k does not divide H
+    assert sp(*a, *bad, 1.0, 1, ws, 1 << 40, None) == GDN_ERR_SHAPE
+    bad = list(dims)
+    bad[6] = 3                               # N != B without offsets
+    assert sp(*a, *bad, 1.0, 1, ws, 1 << 40, None) == GDN_ERR_SHAPE
     b = list(a)
     b[7] = None                              # o
-    assert sp(*b, 1, 4096, 16, 16, 128, 128, 8, 1.0, 1, ws, 1 << 40, None) == GDN_ERR_NULL
+    assert sp(*b, *dims, 1.0, 1, ws, 1 << 40, None) == GDN_ERR_NULL
 
 
 def test_noalloc_validation(lib):

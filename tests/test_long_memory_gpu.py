@@ -17,7 +17,7 @@ import torch
 import oracle
 import gated_deltanet_recurrence_amd as gdn
 from gated_deltanet_recurrence_amd import inputs
-from parity import TOL_BF16, dev, host64, o_err, report, s_err
+from parity import TOL_BF16, dev, host64, o_err, o_err_packed, report, s_err
 
 pytestmark = pytest.mark.gpu
 
@@ -33,11 +33,12 @@ def _case(gate, T, with_state, per_channel=False, H=2):
 
 def _ref(c, per_channel=False):
     f = oracle.gdn_recurrent_channel if per_channel else oracle.gdn_recurrent
-    return f(c.q, c.k, c.v, c.g, c.beta, c.s0, None, c.scale)
+    return f(c.q, c.k, c.v, c.g, c.beta, c.s0, c.cu_seqlens, c.scale)
 
 
 def _fin(c):
     return torch.empty((c.N, c.H, c.d_v, c.d_k), dtype=torch.float32, device="cuda:0")
+
 
 
 @pytest.mark.parametrize("path", list(WS))
@@ -99,4 +100,30 @@ def test_long_memory_channel_gated_chunk(T, with_state):
     o_ref, s_ref = _ref(c, per_channel=True)
     eo, es = o_err(o, o_ref), s_err(fin, s_ref)
     report(f"long memory per-channel chunk T={T} state={with_state}", o=eo, state=es)
+    assert eo <= TOL_BF16 and es <= TOL_BF16 and eo.row <= TOL_BF16
+
+
+PACKED = [3000, 500, 0, 1200, 64]
+
+
+@pytest.mark.parametrize("segments", [2, 4, 9])
+@pytest.mark.parametrize("gate", GATES)
+def test_long_memory_seqpar_packed(gate, segments):
+    """Packed sequences of 3000, 500, 0, 1200 and 64 tokens through the
+    sequence-parallel path, with initial states: the longest (47 chunks) is
+    cut into `segments` segments and the others into segments of the same
+    length, so one call mixes sequences of one, two and several segments
+    (middle segments whose maps are far from zero with these gates). Every
+    sequence against the token recurrence."""
+    c = inputs.make_long_memory(seed=340 + 10 * GATES.index(gate), H=2, gate=gate,
+                                with_state=True, lengths=PACKED)
+    fin = _fin(c)
+    o, _ = gdn.gdn_prefill_seqpar(dev(c.q), dev(c.k), dev(c.v), dev(c.g), dev(c.beta), segments,
+                                  dev(c.s0), fin, cu_seqlens=dev(c.cu_seqlens), scale=c.scale)
+    torch.cuda.synchronize()
+    o_ref, s_ref = _ref(c)
+    cu = [int(x) for x in c.cu_seqlens.tolist()]
+    eo, es = o_err_packed(o, o_ref, cu), s_err(fin, s_ref)
+    report(f"long memory seqpar packed gate={gate} segments={segments} lengths={PACKED}",
+           o=eo, state=es)
     assert eo <= TOL_BF16 and es <= TOL_BF16 and eo.row <= TOL_BF16

@@ -593,6 +593,51 @@ def test_seqpar_long_sequence_sampled():
     assert eo <= TOL_BF16 and es <= TOL_BF16
 
 
+@pytest.mark.parametrize("segments", [1, 2, 3, 5, 40])
+def test_seqpar_packed_matches_oracle(segments):
+    """Packed sequences of 900, 64, 1, 0, 2500, 130 and 65 tokens (ragged
+    tails, an empty and a 1-token sequence), grouped heads, initial states:
+    the longest (40 chunks) cut into 1, 2, 3, 5 or 40 segments and the
+    others into segments of the same length."""
+    c = inputs.make_varlen(seed=95, H=4, Hk=2, lengths=[900, 64, 1, 0, 2500, 130, 65])
+    fin = torch.empty((7, 4, 128, 128), dtype=torch.float32, device="cuda:0")
+    o, _ = gdn.gdn_prefill_seqpar(dev(c.q), dev(c.k), dev(c.v), dev(c.g), dev(c.beta), segments,
+                                  dev(c.s0), fin, cu_seqlens=dev(c.cu_seqlens), scale=c.scale)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_prefill(c)
+    cu = [int(x) for x in c.cu_seqlens.tolist()]
+    eo, es = o_err_packed(o, o_ref, cu), s_err(fin, s_ref)
+    report(f"seqpar packed segments={segments}", o=eo, state=es)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+@pytest.mark.parametrize("segments", [2, 4])
+def test_seqpar_varlen_full_size_sampled(varlen_full, segments):
+    """The packed workload at full size (H=32, 8 sequences log-uniform in
+    [512, 65536], non-zero initial states) through the sequence-parallel
+    path: every sequence, four heads, against the oracle."""
+    c, (outs, s_ref) = varlen_full
+    fin = torch.empty((c.N, c.H, 128, 128), dtype=torch.float32, device="cuda:0")
+    o, _ = gdn.gdn_prefill_seqpar(dev(c.q), dev(c.k), dev(c.v), dev(c.g), dev(c.beta), segments,
+                                  dev(c.s0), fin, cu_seqlens=dev(c.cu_seqlens), scale=c.scale)
+    torch.cuda.synchronize()
+    cu = [int(x) for x in c.cu_seqlens.tolist()]
+    o_h = o.cpu()[:, :, VARLEN_HEADS]
+    eo = max(o_err(o_h[:, a:b], r) for (a, b), r in zip(zip(cu[:-1], cu[1:]), outs) if b > a)
+    es = s_err(fin.cpu()[:, VARLEN_HEADS], s_ref)
+    report(f"varlen seqpar segments={segments} lengths={c.meta['lengths']}", o=eo, state=es)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_seqpar_packed_zero_tokens_keeps_the_states():
+    c = inputs.make_varlen(seed=96, H=2, lengths=[0, 0, 0])
+    fin = torch.full((3, 2, 128, 128), 7.0, dtype=torch.float32, device="cuda:0")
+    gdn.gdn_prefill_seqpar(dev(c.q), dev(c.k), dev(c.v), dev(c.g), dev(c.beta), 4, dev(c.s0),
+                           fin, cu_seqlens=dev(c.cu_seqlens), scale=c.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(fin.cpu(), c.s0)
+
+
 def test_seqpar_zero_tokens_keeps_the_state():
     c = inputs.make_prefill(seed=93, B=2, T=0, H=2, with_state=True)
     fin = torch.full((2, 2, 128, 128), 7.0, dtype=torch.float32, device="cuda:0")
