@@ -162,7 +162,7 @@ int gdn_prefill(const void *q, const void *k, const void *v, const float *g, con
     hipStream_t s = (hipStream_t)stream;
     if (chunk_path(dtype, d_k, d_v)) {
         if (!workspace)
-            return status_of(gdn::launch_prefill_chunk(q, k, v, g, beta, initial_state,
+            return status_of(gdn::launch_prefill_fused(q, k, v, g, beta, initial_state,
                                                        final_state, o, cu_seqlens, T, H, H_k,
                                                        N, scale, s));
         if (!workspace_ok(workspace, workspace_bytes, B, T, H, N)) return GDN_ERR_WORKSPACE;

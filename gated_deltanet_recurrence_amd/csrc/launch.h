@@ -21,9 +21,6 @@ hipError_t launch_prefill_recurrent(const void *, const void *, const void *, co
                                     const float *, const float *, float *, void *,
                                     const int32_t *, int, int, int, int, int, int, float, bool,
                                     hipStream_t);
-hipError_t launch_prefill_chunk(const void *, const void *, const void *, const float *,
-                                const float *, const float *, float *, void *, const int32_t *,
-                                int, int, int, int, float, hipStream_t);
 
 // Two-pass chunk path (prefill_split.hip). T is the packed token count when
 // cu is given, else the tokens per sequence; N the sequences (or segments).
@@ -36,6 +33,13 @@ hipError_t launch_prefill_apply(const void *q, const void *k, const void *v, con
                                 hipStream_t stream, int flags = 0, bool per_channel = false,
                                 const SegJob *jobs = nullptr, int njobs = 0);
 size_t prefill_split_workspace_bytes(long tokens, int H, int N, bool per_channel = false);
+// One pass that also solves each chunk's triangular system on the way (scalar
+// gates); same arguments as the apply pass, no workspace.
+hipError_t launch_prefill_fused(const void *q, const void *k, const void *v, const float *g,
+                                const float *beta, const float *s_init, float *s_final, void *o,
+                                const int32_t *cu, int T, int H, int Hk, int N, float scale,
+                                hipStream_t stream, int flags = 0, const SegJob *jobs = nullptr,
+                                int njobs = 0);
 
 // Sequence-parallel prefill (seqpar.hip): N sequences (packed by cu, or N
 // rows of T tokens), the longest cut into P segments.

@@ -119,11 +119,28 @@ constexpr int SZ_P = SZ_PH + 32 * LD_L * 2;    // 7680: P rows 0-31, then 32-63
 constexpr int SZ_S = DVT * LD_R * 2;           // 9216: bf16 S [32][144]
 constexpr int SZ_DT = DVT * LD_L * 2;          // 5120: Delta^T [32][80]
 constexpr int OFF_BUF = 0;                     // two of each from here on
-constexpr int OFF_P = OFF_BUF + 2 * SZ_BUF;    // (P copies: per-channel decay only)
-constexpr int OFF_S = OFF_P + 2 * SZ_P;
-constexpr int OFF_DT = OFF_S + 2 * SZ_S;
-constexpr int LDS_BYTES = OFF_DT + 2 * SZ_DT;  // 145920
-static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+// In-chain solve (scalar gates, no workspace): each of the two solver waves
+// keeps one chunk's 16 x 16 blocks (I, J), J <= I, of A and then T, fp32
+// row-major at row stride SV_LD (conflict-free operand reads), and the
+// chunk's gamma log2(e) and beta.
+constexpr int SV_LD = 20;
+constexpr int SV_BLK = 16 * SV_LD;
+constexpr int SV_BYTES = (10 * SV_BLK + 3 * 256 + 2 * C) * 4;   // 16384: + D0^T, D1^T, D2^T
+constexpr int SV_WAVE0 = 6;                    // solver waves SV_WAVE0, + 1
+constexpr int SV_LOAD0 = 4;                    // loading waves SV_LOAD0, + 1
+constexpr int SV_PRIO = 1;                     // solver waves' issue priority
+// The copies passed between waves follow the staging buffers: P copies
+// (per-channel decay only), S, Delta^T, then the solver regions (in-chain
+// solve only).
+template <bool PERCH, bool FUSED> struct ChainLds {
+    static constexpr int P = OFF_BUF + 2 * SZ_BUF;
+    static constexpr int S = P + (PERCH ? 2 * SZ_P : 0);
+    static constexpr int DT = S + 2 * SZ_S;
+    static constexpr int SV = DT + 2 * SZ_DT;
+    static constexpr int BYTES = SV + (FUSED ? 2 * SV_BYTES : 0);
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+    static_assert(!(PERCH && FUSED), "the in-chain solve takes scalar gates");
+};
 static_assert(DV / DVT == PAIR_TILES, "one workgroup per d_v tile of a pair");
 static_assert(SZ_BUF % 16 == 0 && SZ_P % 16 == 0, "16-byte aligned tiles");
 
@@ -151,6 +168,29 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// acc += L R for 16 x 16 fp32 blocks on the bf16 matrix cores, each operand
+// split as x = hi + lo (hi = bf16(x), lo = bf16(x - hi)): the 32 k-slots of
+// one v_mfma_f32_16x16x32_bf16 hold k = 4 q + e (e < 4) twice, so that
+//   slots 8 q + e      L_hi[m][4 q + e] R_hi[4 q + e][n]
+//   slots 8 q + 4 + e  L_hi[m][4 q + e] R_lo[4 q + e][n]
+// and a second one adds L_lo R_hi: L R up to L_lo R_lo (relative 2^-17).
+// Lane 16 q + m supplies lrow = L[m][4 q .. 4 q + 3] (a row piece) and
+// rcol = R[4 q .. 4 q + 3][m] (a column piece: R's accumulator layout).
+__device__ __forceinline__ f32x4 mm16x(f32x4 acc, f32x4 lrow, f32x4 rcol) {
+    bf16x8 a1, a2, bb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const bf16 lh = (bf16)lrow[e], rh = (bf16)rcol[e];
+        a1[e] = lh;
+        a1[e + 4] = lh;
+        a2[e] = (bf16)(lrow[e] - (float)lh);
+        a2[e + 4] = (bf16)0.f;
+        bb[e] = rh;
+        bb[e + 4] = (bf16)(rcol[e] - (float)rh);
+    }
+    acc = mfma16(a1, bb, acc);
+    return mfma16(a2, bb, acc);
 }
 // Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane L
 // names 8 bytes at element offset off (its row k0 + L/4 and 4 columns of a
@@ -1083,10 +1123,11 @@ chunk_prep_channel_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k
 // Tokens past the end of a sequence are identity steps (q = k = v = 0,
 // g = 0, and T_u vanishes on them) and their outputs are not stored.
 // ---------------------------------------------------------------------------
-template <bool PERCH>
+template <bool PERCH, bool FUSED>
 __global__ void __launch_bounds__(NT, 1)
 chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                    const bf16 *__restrict__ v, const float *__restrict__ g,
+                   const float *__restrict__ beta,
                    const bf16 *__restrict__ ws, const float *s_init, float *s_final,
                    bf16 *__restrict__ o, const int32_t *__restrict__ cu_seqlens,
                    const SegJob *__restrict__ jobs, int T, int H, int Hk, int npairs, int nslots,
@@ -1101,9 +1142,10 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     auto stTH = [&](int b) { return lds + (OFF_BUF + b * SZ_BUF + B_TH) / 2; };   // [32][LD_H]
     auto stTL = [&](int b) { return lds + (OFF_BUF + b * SZ_BUF + B_TL) / 2; };   // [32][LD_L]
     auto stSc = [&](int b) { return reinterpret_cast<float *>(smem + OFF_BUF + b * SZ_BUF + B_SC); };
-    auto cpP = [&](int b) { return lds + (OFF_P + b * SZ_P) / 2; };
-    auto cpS = [&](int b) { return lds + (OFF_S + b * SZ_S) / 2; };
-    auto cpDt = [&](int b) { return lds + (OFF_DT + b * SZ_DT) / 2; };
+    using L = ChainLds<PERCH, FUSED>;
+    auto cpP = [&](int b) { return lds + (L::P + b * SZ_P) / 2; };
+    auto cpS = [&](int b) { return lds + (L::S + b * SZ_S) / 2; };
+    auto cpDt = [&](int b) { return lds + (L::DT + b * SZ_DT) / 2; };
 
     const int tid0 = (int)threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
@@ -1193,12 +1235,16 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     // workspace's K^ and K+ rows)
     const int tstride = PERCH ? DK : Hk * DK;
     const int tsv = H * DV;                    // ... and of v
-    const int wi = wave - 4;
-    const int qkmat = wi >> 1;                 // 0 Q, 1 K
-    const int qkrow = 32 * (wi & 1) + (lane0 >> 4), qkcol = 8 * (lane0 & 15);
+    // With the in-chain solve only waves 4 and 5 load: wave 4 all of Q and V
+    // row groups 0-1, wave 5 all of K, V row groups 2-3 and g.
+    const int wi = FUSED ? wave - SV_LOAD0 : wave - 4;
+    constexpr int NQK = FUSED ? 16 : 8;        // Q or K rows (of 4) per loading wave
+    const int qkmat = FUSED ? wi : wi >> 1;    // 0 Q, 1 K
+    const int qkrow0 = FUSED ? 0 : 32 * (wi & 1);
+    const int qkrow = qkrow0 + (lane0 >> 4), qkcol = 8 * (lane0 & 15);
     const int goffQK = 2 * (qkrow * tstride + qkcol);
     const int goffV = 2 * ((lane0 >> 2) * tsv + 8 * (lane0 & 3));
-    const int vr0 = 2 * (wi - 2);              // first V row group (wi 2, 3)
+    const int vr0 = FUSED ? 2 * wi : 2 * (wi - 2);   // first V row group
     // LDS element offset of workspace piece e within a staging buffer (uniform
     // per 64-piece group)
     auto tpiece_loff = [&](int e) {
@@ -1211,7 +1257,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     // Two register sets: chunk c is loaded into set c % 2 three iterations
     // before its use and stored to LDS one iteration before.
     struct Pref {
-        bf16x8 b[8], t[3], v[2];
+        bf16x8 b[NQK], t[3], v[2];
         float g;
         f32x2 ec;                              // per channel: e^{gamma_63}, channels 2 lane ..
     };
@@ -1229,7 +1275,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         const __amdgpu_buffer_rsrc_t rqk = __builtin_amdgcn_make_buffer_rsrc(
             (void *)qk_src, 0, nb, 0x00020000);
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
+        for (int r = 0; r < NQK; ++r)
             rs.b[r] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
                           rqk, goffQK, r * 4 * tstride * 2, 0));
         if constexpr (decltype(WT)::value) {
@@ -1266,9 +1312,9 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     };
     auto store = [&](const Pref &rs, int b, auto WT, auto WG, auto WV, int lane) {
         bf16 *buf = lds + (OFF_BUF + b * SZ_BUF) / 2;
-        const int lrow = (qkmat ? B_K : B_Q) / 2 + (32 * (wi & 1) + (lane >> 4)) * LD_R + 8 * (lane & 15);
+        const int lrow = (qkmat ? B_K : B_Q) / 2 + (qkrow0 + (lane >> 4)) * LD_R + 8 * (lane & 15);
 #pragma unroll
-        for (int r = 0; r < 8; ++r) *reinterpret_cast<bf16x8 *>(buf + lrow + 4 * r * LD_R) = rs.b[r];
+        for (int r = 0; r < NQK; ++r) *reinterpret_cast<bf16x8 *>(buf + lrow + 4 * r * LD_R) = rs.b[r];
         if constexpr (decltype(WT)::value) {
 #pragma unroll
             for (int r = 0; r < 3; ++r)
@@ -1749,10 +1795,228 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                 lds_barrier();
             }
         };
-        if (wave == 7) lloop(no_t, with_g, with_v, no_p);
-        else if (wave == 6) lloop(no_t, no_g, with_v, no_p);
-        else if constexpr (PERCH) lloop(with_t, no_g, no_v, with_p);
-        else lloop(with_t, no_g, no_v, no_p);
+        // ---- in-chain solve: waves 6 and 7 form T_u = (I - A)^-1 diag(beta)
+        //      of chunk c (wave 6 + c % 2) into staging buffer c % 2 over two
+        //      iterations, each phase bounded by the iteration's barrier:
+        //        iteration c - 3  load K (operand order), g, beta of chunk c
+        //        iteration c - 2  gamma; Gram tiles K K^T (bf16 MFMA); A =
+        //                         -strict_lower(diag(beta) K K^T * Gamma);
+        //                         diagonal blocks D_b = (I - A_bb)^-1 by
+        //                         forward substitution
+        //        iteration c - 1  off-diagonal blocks of T by two levels of
+        //                         2 x 2 block inversion (fp32 MFMA), T diag(beta)
+        //                         as bf16 pieces into the staging buffer (which
+        //                         the loaders fill with chunk c's tiles in the
+        //                         same iteration)
+        //      ("5. Linear Attention", chunked delta rule, stage 1; the same
+        //      arithmetic as the prep pass, by one wave per chunk) ----
+        auto sloop = [&](auto SID) {
+            constexpr int sid = decltype(SID)::value;      // chunks c with c % 2 == sid
+            __builtin_amdgcn_s_setprio(SV_PRIO);
+            float *sv = reinterpret_cast<float *>(smem + L::SV + sid * SV_BYTES);
+            float *sgl = sv + 10 * SV_BLK + 3 * 256, *sbe = sgl + C;
+            auto blk = [&](int I, int J) { return sv + (I * (I + 1) / 2 + J) * SV_BLK; };
+            auto dtr = [&](int b) { return sv + 10 * SV_BLK + 256 * b; };     // D_b^T, row stride 16
+            const bf16 *k_head = k + (size_t)bos * (Hk * DK) + (size_t)(h / (H / Hk)) * DK;
+            const float *b_head = beta + (size_t)bos * H + h;
+            bf16x8 kr[4][4];                   // K rows 16 I + lane%16, columns 32 s + 8 (lane/16) ..
+            float gv = 0.f, bv = 0.f;
+            auto sfetch = [&](int c) {
+                const int base = c * C;
+                const int nrow = len - base < C ? len - base : C;
+                const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+                    (void *)(k_head + (size_t)base * tstride), 0, (unsigned)nrow * tstride * 2, 0x00020000);
+                const unsigned off = (unsigned)(((lane0 & 15) * tstride + 8 * (lane0 >> 4)) * 2);
+#pragma unroll
+                for (int I = 0; I < 4; ++I)
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2)
+                        kr[I][s2] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                        rk, off, (unsigned)((16 * I * tstride + 32 * s2) * 2), 0));
+                const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+                    (void *)(g_head + (size_t)base * H), 0, (unsigned)nrow * H * 4, 0x00020000);
+                const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+                    (void *)(b_head + (size_t)base * H), 0, (unsigned)nrow * H * 4, 0x00020000);
+                gv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, 4 * H * lane0, 0, 0));
+                bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, 4 * H * lane0, 0, 0));
+            };
+            // acc layout (lane (q, m) holds rows 4 q + r of column m) -> row-major block
+            auto store_blk = [&](float *p, f32x4 acc, int lane) {
+                const int m = lane & 15, qq = lane >> 4;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) p[(4 * qq + r) * SV_LD + m] = acc[r];
+            };
+            auto phase1 = [&](int lane) {
+                const int m = lane & 15, qq = lane >> 4;
+                const float gam = wave_inclusive_scan(gv);
+                sgl[lane] = gam * 1.4426950408889634f;
+                sbe[lane] = bv;
+                // Gram blocks (I, J), J <= I: G[16 I + 4 q + r][16 J + m]
+                f32x4 G[10];
+#pragma unroll
+                for (int I = 0; I < 4; ++I)
+#pragma unroll
+                    for (int J = 0; J <= I; ++J) {
+                        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int s2 = 0; s2 < 4; ++s2) a = mfma16(kr[I][s2], kr[J][s2], a);
+                        G[I * (I + 1) / 2 + J] = a;
+                    }
+                wave_lds_order();
+                // A_ij = -beta_i G_ij e^{gamma_i - gamma_j} for j < i (each
+                // exponent <= 0), zero elsewhere; row-major into the blocks
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    const f32x4 gli = *reinterpret_cast<const f32x4 *>(sgl + 16 * I + 4 * qq);
+                    const f32x4 bi = *reinterpret_cast<const f32x4 *>(sbe + 16 * I + 4 * qq);
+#pragma unroll
+                    for (int J = 0; J <= I; ++J) {
+                        const float glj = sgl[16 * J + m];
+                        f32x4 a = G[I * (I + 1) / 2 + J];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float e = __builtin_amdgcn_exp2f(gli[r] - glj);
+                            a[r] = (J < I || m < 4 * qq + r) ? -(bi[r] * a[r]) * e : 0.f;
+                        }
+                        store_blk(blk(I, J), a, lane);
+                    }
+                }
+                wave_lds_order();
+                // diagonal blocks, one per 16 lanes: lane 16 b + c computes
+                // column c of D_b = (I - A_bb)^-1 row by row,
+                // D[i][c] = [i == c] + sum_{j < i} A[i][j] D[j][c]
+                // (row i + 1 read while row i is summed)
+                const int bb = lane >> 4, c = lane & 15;
+                const float *Ab = blk(bb, bb);
+                float D[16];
+                f32x4 rowv[2][4];
+                auto load_row = [&](int i, f32x4 (&dstv)[4]) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        if (4 * t < i) dstv[t] = *reinterpret_cast<const f32x4 *>(Ab + i * SV_LD + 4 * t);
+                };
+                load_row(1, rowv[1]);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    if (i + 1 < 16) load_row(i + 1, rowv[(i + 1) & 1]);
+                    float acc = i == c ? 1.f : 0.f;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (4 * t + e < i) acc += rowv[i & 1][t][e] * D[4 * t + e];
+                    D[i] = acc;
+                }
+                wave_lds_order();
+                // D_b row-major in place; D_0, D_1, D_2 also transposed (their
+                // columns are right-hand operands below)
+                float *Db = blk(bb, bb);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) Db[i * SV_LD + c] = D[i];
+                if (bb < 3) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        *reinterpret_cast<f32x4 *>(dtr(bb) + c * 16 + 4 * t) =
+                            f32x4{D[4 * t], D[4 * t + 1], D[4 * t + 2], D[4 * t + 3]};
+                }
+                wave_lds_order();
+            };
+            auto phase2 = [&](int buf, int lane) {
+                const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+                const int m = lane & 15, qq = lane >> 4;
+                // With D_b the diagonal inverses:
+                //   T10 = D1 A10 D0,  T32 = D3 A32 D2,  T21 = D2 A21 D1
+                //   T20 = D2 (A20 D0 + A21 T10)
+                //   T31 = T32 (A21 D1) + D3 (A31 D1)
+                //   T30 = T32 (A20 D0 + A21 T10) + D3 (A30 D0 + A31 T10)
+                // Left factors are row pieces of row-major blocks, right
+                // factors column pieces of D_b^T or accumulators.
+                auto piece = [&](const float *p, int ld) {
+                    return *reinterpret_cast<const f32x4 *>(p + m * ld + 4 * qq);
+                };
+                const f32x4 lA10 = piece(blk(1, 0), SV_LD), lA32 = piece(blk(3, 2), SV_LD);
+                const f32x4 lA21 = piece(blk(2, 1), SV_LD), lA20 = piece(blk(2, 0), SV_LD);
+                const f32x4 lA31 = piece(blk(3, 1), SV_LD), lA30 = piece(blk(3, 0), SV_LD);
+                const f32x4 lD1 = piece(blk(1, 1), SV_LD), lD2 = piece(blk(2, 2), SV_LD);
+                const f32x4 lD3 = piece(blk(3, 3), SV_LD);
+                const f32x4 rD0 = piece(dtr(0), 16), rD1 = piece(dtr(1), 16), rD2 = piece(dtr(2), 16);
+                const f32x4 u10 = mm16x(z4, lA10, rD0);
+                const f32x4 u32 = mm16x(z4, lA32, rD2);
+                const f32x4 X = mm16x(z4, lA21, rD1);                  // A21 D1
+                const f32x4 W0 = mm16x(z4, lA20, rD0);                 // A20 D0
+                const f32x4 Z = mm16x(z4, lA31, rD1);                  // A31 D1
+                const f32x4 V0 = mm16x(z4, lA30, rD0);                 // A30 D0
+                const f32x4 t10 = mm16x(z4, lD1, u10);
+                const f32x4 t32 = mm16x(z4, lD3, u32);
+                const f32x4 t21 = mm16x(z4, lD2, X);
+                const f32x4 W = mm16x(W0, lA21, t10);                  // + A21 T10
+                const f32x4 V = mm16x(V0, lA31, t10);                  // + A31 T10
+                const f32x4 t20 = mm16x(z4, lD2, W);
+                // T32 is a left factor next: through its block (A32 is read)
+                store_blk(blk(3, 2), t32, lane);
+                wave_lds_order();
+                const f32x4 lT32 = piece(blk(3, 2), SV_LD);
+                const f32x4 t31 = mm16x(mm16x(z4, lT32, X), lD3, Z);
+                const f32x4 t30 = mm16x(mm16x(z4, lT32, W), lD3, V);
+                store_blk(blk(1, 0), t10, lane);
+                store_blk(blk(2, 1), t21, lane);
+                store_blk(blk(2, 0), t20, lane);
+                store_blk(blk(3, 1), t31, lane);
+                store_blk(blk(3, 0), t30, lane);
+                wave_lds_order();
+                // T diag(beta) as bf16 pieces of 8 row elements: pieces
+                // 0..255 rows 32-63 (8 per row), 256..383 rows 0-31, columns
+                // 0-31 (4 per row); blocks above the diagonal are zero
+                bf16 *sb = lds + (OFF_BUF + buf * SZ_BUF) / 2;
+#pragma unroll
+                for (int u6 = 0; u6 < 6; ++u6) {
+                    const int e = lane + 64 * u6;
+                    const int i = u6 < 4 ? 32 + (e >> 3) : (e - 256) >> 2;
+                    const int gc = u6 < 4 ? e & 7 : e & 3;
+                    const int I = i >> 4, J = gc >> 1;
+                    const float *tp = blk(I, J < I ? J : I) + (i & 15) * SV_LD + 8 * (gc & 1);
+                    const f32x4 t0 = *reinterpret_cast<const f32x4 *>(tp);
+                    const f32x4 t1 = *reinterpret_cast<const f32x4 *>(tp + 4);
+                    const f32x4 b0 = *reinterpret_cast<const f32x4 *>(sbe + 8 * gc);
+                    const f32x4 b1 = *reinterpret_cast<const f32x4 *>(sbe + 8 * gc + 4);
+                    bf16x8 outp;
+#pragma unroll
+                    for (int e2 = 0; e2 < 4; ++e2) {
+                        outp[e2] = (bf16)(J <= I ? t0[e2] * b0[e2] : 0.f);
+                        outp[e2 + 4] = (bf16)(J <= I ? t1[e2] * b1[e2] : 0.f);
+                    }
+                    *reinterpret_cast<bf16x8 *>(sb + tpiece_loff(e)) = outp;
+                }
+            };
+            for (int ch0 = -3; ch0 <= nchunks; ch0 += 2)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int ch = ch0 + hf;
+                int tidl = tid0;
+                asm volatile("" : "+v"(tidl));
+                const int lane = tidl & 63;
+                if (hf == sid) {
+                    // (ch + 1) % 2 == sid: finish chunk ch + 1 into staging hf,
+                    // then load chunk ch + 3
+                    if (ch + 1 >= 0 && ch + 1 < nchunks) phase2(hf, lane);
+                    sfetch(ch + 3 < 0 ? 0 : ch + 3 < nchunks ? ch + 3 : nchunks - 1);
+                } else if (ch + 2 >= 0 && ch + 2 < nchunks) {
+                    phase1(lane);              // chunk ch + 2
+                }
+                lds_barrier();
+            }
+        };
+        if constexpr (FUSED) {
+            if (wave == SV_LOAD0 + 1) lloop(no_t, with_g, with_v, no_p);
+            else if (wave == SV_LOAD0) lloop(no_t, no_g, with_v, no_p);
+            else if (wave == SV_WAVE0) sloop(std::integral_constant<int, 0>{});
+            else sloop(std::integral_constant<int, 1>{});
+        } else {
+            if (wave == 7) lloop(no_t, with_g, with_v, no_p);
+            else if (wave == 6) lloop(no_t, no_g, with_v, no_p);
+            else if constexpr (PERCH) lloop(with_t, no_g, no_v, with_p);
+            else lloop(with_t, no_g, no_v, no_p);
+        }
     }
     if (sfin && wave < 2) {
         const int m = lane0 & 15, qq = lane0 >> 4;
@@ -1823,24 +2087,29 @@ hipError_t launch_prefill_prepare(const void *q, const void *k, const float *g, 
 // jobs: NULL, or a device table of njobs entries (one per pair / H) that
 // replaces the one pair per (sequence, head); N is then the number of
 // segments in cu.
-template <bool PERCH>
+template <bool PERCH, bool FUSED = false>
 static hipError_t launch_chain(const void *q, const void *k, const void *v, const float *g,
-                               const float *s_init, float *s_final, void *o, const int32_t *cu,
-                               int T, int H, int Hk, int N, float scale, const void *ws,
-                               hipStream_t stream, int flags, const SegJob *jobs, int njobs)
+                               const float *beta, const float *s_init, float *s_final, void *o,
+                               const int32_t *cu, int T, int H, int Hk, int N, float scale,
+                               const void *ws, hipStream_t stream, int flags, const SegJob *jobs,
+                               int njobs)
 {
+    constexpr int LDS_BYTES = ChainLds<PERCH, FUSED>::BYTES;
     // the dynamic LDS limit, raised once per process (thread-safe static)
     static const hipError_t attr = hipFuncSetAttribute(
-        (const void *)chunk_chain_kernel<PERCH>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+        (const void *)chunk_chain_kernel<PERCH, FUSED>, hipFuncAttributeMaxDynamicSharedMemorySize,
+        LDS_BYTES);
     if (attr != hipSuccess) return attr;
     const long tokens = cu ? (long)T : (long)N * T;
     const long nslots = tokens / C + N + 1;
     const int npairs = H * (jobs ? njobs : N);
     if (npairs == 0) return hipSuccess;
     dim3 grid(pair_grid(npairs)), block(NT);
-    hipLaunchKernelGGL(chunk_chain_kernel<PERCH>, grid, block, LDS_BYTES, stream, (const bf16 *)q,
-                       (const bf16 *)k, (const bf16 *)v, g, (const bf16 *)ws, s_init, s_final,
-                       (bf16 *)o, cu, jobs, T, H, Hk, npairs, (int)nslots, scale, flags);
+    auto *kern = chunk_chain_kernel<PERCH, FUSED>;
+    hipLaunchKernelGGL(kern, grid, block, LDS_BYTES, stream,
+                       (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, g, beta,
+                       (const bf16 *)ws, s_init, s_final, (bf16 *)o, cu, jobs, T, H, Hk, npairs,
+                       (int)nslots, scale, flags);
     return hipGetLastError();
 }
 
@@ -1850,10 +2119,19 @@ hipError_t launch_prefill_apply(const void *q, const void *k, const void *v, con
                                 hipStream_t stream, int flags, bool per_channel,
                                 const SegJob *jobs, int njobs)
 {
-    return per_channel ? launch_chain<true>(q, k, v, g, s_init, s_final, o, cu, T, H, Hk, N, scale,
-                                            ws, stream, flags, jobs, njobs)
-                       : launch_chain<false>(q, k, v, g, s_init, s_final, o, cu, T, H, Hk, N, scale,
-                                             ws, stream, flags, jobs, njobs);
+    return per_channel ? launch_chain<true>(q, k, v, g, nullptr, s_init, s_final, o, cu, T, H, Hk,
+                                            N, scale, ws, stream, flags, jobs, njobs)
+                       : launch_chain<false>(q, k, v, g, nullptr, s_init, s_final, o, cu, T, H, Hk,
+                                             N, scale, ws, stream, flags, jobs, njobs);
+}
+
+hipError_t launch_prefill_fused(const void *q, const void *k, const void *v, const float *g,
+                                const float *beta, const float *s_init, float *s_final, void *o,
+                                const int32_t *cu, int T, int H, int Hk, int N, float scale,
+                                hipStream_t stream, int flags, const SegJob *jobs, int njobs)
+{
+    return launch_chain<false, true>(q, k, v, g, beta, s_init, s_final, o, cu, T, H, Hk, N, scale,
+                                     nullptr, stream, flags, jobs, njobs);
 }
 
 }  // namespace gdn

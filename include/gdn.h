@@ -126,9 +126,12 @@ const char *gdn_status_string(int status);
  *                 path runs in two passes: the per-chunk triangular systems
  *                 of every chunk and head are solved in parallel first, and
  *                 only the state recurrence walks the chunks in order (the
- *                 fast path). With NULL it runs as one pass that solves each
- *                 chunk's system on the sequential path (slower, no scratch).
- *                 Both give the same result up to rounding order. Ignored by
+ *                 fast path). With NULL it runs as one pass whose
+ *                 workgroups also solve each chunk's system, two chunks ahead
+ *                 of the recurrence, on waves of their own (no scratch;
+ *                 slower, since each of a head's four 32-wide d_v tiles
+ *                 solves it again). Both give the same result up to rounding
+ *                 order. Ignored by
  *                 the token-serial path. Calls that share a workspace must be
  *                 ordered on one stream.
  *   workspace_bytes  size of workspace; GDN_ERR_WORKSPACE if workspace is
