@@ -92,7 +92,7 @@ def chain_bytes(B, T, H, dk=128, dv=128):
 
 
 def prep_bytes(B, T, H, dk=128):
-    """chunk_prep per launch as it runs: k bf16, g and beta fp32 read, the
+    """chunk_solve per launch as it runs: k bf16, g and beta fp32 read, the
     workspace written."""
     return B * T * H * (2 * dk + 4 + 4 + WS_BYTES_PER_TOKEN_HEAD)
 
@@ -509,7 +509,7 @@ def main():
         p = bench_prefill(gdn, inputs, args.steps, args.warmup)
         sec = p["ms"] * 1e-3
         chain_dominant = p["ms_chain"] >= p["ms_prep"]
-        kname = "chunk_chain_kernel" if chain_dominant else "chunk_prep_kernel"
+        kname = "chunk_chain_kernel" if chain_dominant else "chunk_solve_kernel"
         k_ms = p["ms_chain"] if chain_dominant else p["ms_prep"]
         k_med = p["med_chain"] if chain_dominant else p["med_prep"]
         # the method's bytes (1032 B per token-head plus the final states),
@@ -534,7 +534,7 @@ def main():
                          "overhead_bytes": p["ws_bytes"] + p["reread_bytes"],
                          "overhead_note": "workspace T diag(beta) written and read back (96 B "
                                           "each way per token-head) and k, g, beta read a "
-                                          "second time by the prep pass (264 B)",
+                                          "second time by the solve pass (264 B)",
                          "mfma_tflops": round(k_flops, 2),
                          "mfma_frac_of_bf16_peak": round(k_flops / BF16_PEAK_TFLOPS, 4),
                          "avg_launch_us": round(k_ms * 1e3, 2),

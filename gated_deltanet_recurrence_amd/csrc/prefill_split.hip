@@ -61,8 +61,10 @@ constexpr int WS_P = 384;                     // 16-byte pieces of P (per-channe
 constexpr int ITEM_ELEMS = 8 * WS_T;          // 3072 bf16 per (chunk, head) in the workspace
 
 // ---------------------------------------------------------------------------
-// Pass 1: chunk_prep. Workgroups of 4 waves, each looping over (chunk slot,
-// head) items.
+// Pass 1 with a per-channel decay: chunk_prep_channel, workgroups of 4 waves
+// looping over (chunk slot, head) items; the LDS layout of its triangular
+// solve (solve_store). With a scalar gate the pass is chunk_solve (one wave
+// per item, WaveSolver below).
 // ---------------------------------------------------------------------------
 constexpr int P_NT = 256;
 constexpr int P_LD_K = DK + 8;                 // bf16 row stride of K
@@ -73,15 +75,7 @@ constexpr int P_DB = 16 * 16 + 4;              // floats per diagonal 16 x 16 bl
 constexpr int P_SZ_R1 = C * P_LD_K * 2;        // 17408: K, then T
 constexpr int P_SZ_A = 48 * P_LD_A2 * 4;       // 9984: rows 16-63, columns 0-47 of A
 constexpr int P_SZ_Y = 4 * P_DB * 4;           // 4160: the diagonal blocks of A, row-major
-constexpr int P_SZ_SC = 3 * C * 4;             // gamma log2(e), beta, E
-constexpr int P_OFF_R1 = 0;
-constexpr int P_OFF_A = P_OFF_R1 + P_SZ_R1;
-constexpr int P_OFF_Y = P_OFF_A + P_SZ_A;
-constexpr int P_OFF_SC = P_OFF_Y + P_SZ_Y;
-constexpr int P_LDS_BYTES = P_OFF_SC + P_SZ_SC;   // 32320
-constexpr int P_WG_PER_CU = 4;
 static_assert(C * P_LD_A * 4 <= P_SZ_R1, "T fits where K was");
-static_assert(P_LDS_BYTES * P_WG_PER_CU <= 160 * 1024, "four prep workgroups per CU");
 
 // ---------------------------------------------------------------------------
 // Pass 2: chunk_chain. One workgroup of 8 waves per (32-wide d_v tile, head,
@@ -177,20 +171,36 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 // and a second one adds L_lo R_hi: L R up to L_lo R_lo (relative 2^-17).
 // Lane 16 q + m supplies lrow = L[m][4 q .. 4 q + 3] (a row piece) and
 // rcol = R[4 q .. 4 q + 3][m] (a column piece: R's accumulator layout).
-__device__ __forceinline__ f32x4 mm16x(f32x4 acc, f32x4 lrow, f32x4 rcol) {
-    bf16x8 a1, a2, bb;
+// The operands are split once each (lsplit, rsplit) and reused by every
+// product they enter.
+struct LSplit {
+    bf16x8 a1, a2;                             // {hi, hi}, {lo, 0}
+};
+__device__ __forceinline__ LSplit lsplit(f32x4 lrow) {
+    LSplit o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const bf16 lh = (bf16)lrow[e], rh = (bf16)rcol[e];
-        a1[e] = lh;
-        a1[e + 4] = lh;
-        a2[e] = (bf16)(lrow[e] - (float)lh);
-        a2[e + 4] = (bf16)0.f;
-        bb[e] = rh;
-        bb[e + 4] = (bf16)(rcol[e] - (float)rh);
+        const bf16 h = (bf16)lrow[e];
+        o.a1[e] = h;
+        o.a1[e + 4] = h;
+        o.a2[e] = (bf16)(lrow[e] - (float)h);
+        o.a2[e + 4] = (bf16)0.f;
     }
-    acc = mfma16(a1, bb, acc);
-    return mfma16(a2, bb, acc);
+    return o;
+}
+__device__ __forceinline__ bf16x8 rsplit(f32x4 rcol) {             // {hi, lo}
+    bf16x8 b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const bf16 h = (bf16)rcol[e];
+        b[e] = h;
+        b[e + 4] = (bf16)(rcol[e] - (float)h);
+    }
+    return b;
+}
+__device__ __forceinline__ f32x4 mm16x(f32x4 acc, const LSplit &l, bf16x8 r) {
+    acc = mfma16(l.a1, r, acc);
+    return mfma16(l.a2, r, acc);
 }
 // Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane L
 // names 8 bytes at element offset off (its row k0 + L/4 and 4 columns of a
@@ -431,180 +441,6 @@ __device__ __forceinline__ PrepItem prep_locate(const int32_t *cu, int item, int
     it.row0 = bos + c * C;
     it.nvalid = (int)(len - c * C < C ? len - c * C : C);
     return it;
-}
-
-__global__ void __launch_bounds__(P_NT, P_WG_PER_CU)
-chunk_prep_kernel(const bf16 *__restrict__ k, const float *__restrict__ g,
-                  const float *__restrict__ beta, const int32_t *__restrict__ cu_seqlens,
-                  bf16 *__restrict__ ws, int T, int H, int Hk, int N, int nslots)
-{
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    bf16 *sK = reinterpret_cast<bf16 *>(smem + P_OFF_R1);
-    float *sT = reinterpret_cast<float *>(smem + P_OFF_R1);
-    float *sA = reinterpret_cast<float *>(smem + P_OFF_A);
-    float *sY = reinterpret_cast<float *>(smem + P_OFF_Y);
-    float *sGl = reinterpret_cast<float *>(smem + P_OFF_SC);   // gamma log2(e)
-    float *sBeta = sGl + C;
-    float *sE = sBeta + C;
-
-    const int tid0 = (int)threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
-    const int nitems = nslots * H;
-    const int stride = (int)gridDim.x;
-    const int tstride = Hk * DK;               // elements between consecutive tokens of K
-
-    // K rows (tid >> 4) + 16 u, columns 8 (tid & 15) ..; g and beta of token
-    // `lane`. Buffer loads bounded by the chunk's valid tokens: rows past the
-    // end of the sequence (and every row of an empty item) read zero.
-    struct Pre {
-        bf16x8 kr[4];
-        float gv, bv;
-    };
-    auto fetch = [&](const PrepItem &it, Pre &p) {
-        const size_t tok0 = (size_t)it.row0;
-        const unsigned nb = (unsigned)it.nvalid * tstride * 2;
-        const size_t hoff = tok0 * tstride + (size_t)(it.h / (H / Hk)) * DK;   // query/key head
-        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(k + hoff), 0, nb, 0x00020000);
-        const unsigned off = (unsigned)(((tid0 >> 4) * tstride + 8 * (tid0 & 15)) * 2);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            p.kr[u] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                          rk, off, (unsigned)(16 * u * tstride * 2), 0));
-        const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(g + tok0 * H + it.h), 0, (unsigned)it.nvalid * H * 4, 0x00020000);
-        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(beta + tok0 * H + it.h), 0, (unsigned)it.nvalid * H * 4, 0x00020000);
-        p.gv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, 4 * H * (tid0 & 63), 0, 0));
-        p.bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, 4 * H * (tid0 & 63), 0, 0));
-    };
-
-    // one item: stage `p` (the current item's loads) into LDS, start the loads
-    // of `nit` into `pn` (which may be `p`), locate item `after` into `ait`,
-    // then compute and store the item
-    auto item_step = [&](const PrepItem &it, const Pre &p, const PrepItem &nit, Pre &pn,
-                         int after, PrepItem &ait) {
-        // the lane index passes through an empty asm each item, so that the
-        // compiler rebuilds the per-lane LDS addresses here instead of keeping
-        // dozens of them live across the loop
-        int tid = tid0;
-        asm volatile("" : "+v"(tid));
-        const int lane = tid & 63;
-        const int l32 = lane & 31, lh = lane >> 5;
-        auto rows4 = [&](const float *v, int i0, int qq) {
-            return *reinterpret_cast<const f32x4 *>(v + i0 + 8 * qq + 4 * lh);
-        };
-
-        if (it.nvalid > 0) {
-            const int col = 8 * (tid & 15);
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                *reinterpret_cast<bf16x8 *>(sK + ((tid >> 4) + 16 * u) * P_LD_K + col) = p.kr[u];
-            if (wave == 0) {
-                __builtin_amdgcn_s_setprio(2);     // as in the solve: the others wait for it
-                const float gam = wave_inclusive_scan(p.gv);
-                const float g32 = __builtin_bit_cast(
-                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gam), 32));
-                sGl[lane] = gam * 1.4426950408889634f;
-                sBeta[lane] = p.bv;
-                sE[lane] = __expf(lane >= 32 ? gam - g32 : g32 - gam);
-                __builtin_amdgcn_s_setprio(0);
-            }
-        }
-        fetch(nit, pn);
-        ait = prep_locate(cu_seqlens, after, nitems, T, H, N);
-        if (it.nvalid == 0) return;            // uniform over the workgroup
-        lds_barrier();
-        bf16 *dst = ws + ((size_t)it.h * nslots + it.slot) * ITEM_ELEMS;
-
-        // ---- gram tiles of A (waves 0 and 1, whose diagonal tiles take an
-        //      exponential per element, go first in issue) ----
-        if (wave < 2) __builtin_amdgcn_s_setprio(1);
-        if (wave < 3) {
-            const int ti = wave == 0 ? 0 : 1, tj = wave == 1 ? 1 : 0;
-            f32x16 at = {};
-#pragma unroll
-            for (int hk = 0; hk < 2; ++hk) {
-                bf16x8 fa[4], fb[4];
-#pragma unroll
-                for (int s2 = 0; s2 < 4; ++s2) {
-                    fa[s2] = frag32(sK, P_LD_K, 32 * ti, 64 * hk + 16 * s2, lane);
-                    fb[s2] = frag32(sK, P_LD_K, 32 * tj, 64 * hk + 16 * s2, lane);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int s2 = 0; s2 < 4; ++s2) at = mfma32(fa[s2], fb[s2], at);
-            }
-            // element r: A row i = 32 ti + acc_row(r), column j = 32 tj + l32
-            if (wave < 2) {
-                const int j = 32 * tj + l32;
-                const float glj = sGl[j];
-#pragma unroll
-                for (int qq = 0; qq < 4; ++qq) {
-                    const f32x4 gli = rows4(sGl, 32 * ti, qq), bi = rows4(sBeta, 32 * ti, qq);
-#pragma unroll
-                    for (int s2 = 0; s2 < 4; ++s2) {
-                        const int r = 4 * qq + s2, i = 32 * ti + acc_row(r, lane);
-                        const float e = __builtin_amdgcn_exp2f(gli[s2] - glj);
-                        at[r] = j < i ? -(bi[s2] * at[r]) * e : 0.f;
-                    }
-                }
-            } else {
-                const float ej = sE[l32];
-#pragma unroll
-                for (int qq = 0; qq < 4; ++qq) {
-                    const f32x4 ei = rows4(sE, 32, qq), bi = rows4(sBeta, 32, qq);
-#pragma unroll
-                    for (int s2 = 0; s2 < 4; ++s2) {
-                        const int r = 4 * qq + s2;
-                        at[r] = -(bi[s2] * at[r]) * (ei[s2] * ej);
-                    }
-                }
-            }
-            // rows 16-63, columns 0-47 of A into sA (the off-diagonal blocks are
-            // read from there); accumulator rows r < 8 of tile row 0 are rows 0-15
-            const int j = 32 * tj + l32;
-            if (j < 48) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (ti == 1 || r >= 8) sA[(32 * ti + acc_row(r, lane) - 16) * P_LD_A2 + j] = at[r];
-            }
-            if (wave < 2) {
-                // and the two diagonal 16 x 16 blocks, row-major, into sY: lanes
-                // with l32 < 16 hold rows of block 0 in accumulators 0-7, the
-                // others rows of block 1 in accumulators 8-15 (acc_row(r + 8) =
-                // acc_row(r) + 16); one select per element (the empty asm keeps
-                // the compiler from turning it into a per-lane vector index,
-                // which it would expand into a 16-way select chain)
-                const bool hi = l32 >= 16;
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    float lo_v = at[r], hi_v = at[r + 8];
-                    asm volatile("" : "+v"(lo_v), "+v"(hi_v));
-                    const float val = hi ? hi_v : lo_v;
-                    sY[(2 * wave + (hi ? 1 : 0)) * P_DB + acc_row(r, lane) * 16 + (l32 & 15)] = val;
-                }
-            }
-        }
-        lds_barrier();                         // A complete; K no longer read
-
-        __builtin_amdgcn_s_setprio(0);
-        solve_store(sA, sY, sT, sBeta, dst, tid, wave);
-        lds_barrier();                         // T and the scalars read before the next item
-    };
-
-    // one register set: each step stages it into LDS before refilling it; the
-    // item after next is located while the current one is computed
-    const int first = (int)blockIdx.x;
-    PrepItem it = prep_locate(cu_seqlens, first, nitems, T, H, N);
-    PrepItem nit = prep_locate(cu_seqlens, first + stride, nitems, T, H, N);
-    Pre pre;
-    fetch(it, pre);
-    for (int item = first; item < nitems; item += stride) {
-        PrepItem ait;
-        item_step(it, pre, nit, pre, item + 2 * stride, ait);
-        it = nit;
-        nit = ait;
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1078,6 +914,242 @@ chunk_prep_channel_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k
         item_step(it, pre, nit, pre, item + 2 * stride, ait);
         it = nit;
         nit = ait;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// One wave's solve of one (chunk, head): T_u = (I - A)^-1 diag(beta) with
+// A = -strict_lower(diag(beta) K K^T * Gamma), Gamma_ij = e^{gamma_i - gamma_j}
+// ("5. Linear Attention", chunked delta rule, stage 1), in SV_BYTES of LDS
+// that no other wave touches and no workgroup barrier:
+//   phase1  gamma = prefix sum of g; the ten Gram blocks (I, J), J <= I, of
+//           K K^T on the bf16 matrix cores (K given in operand order); A
+//           row-major into the blocks; the diagonal blocks D_b = (I - A_bb)^-1
+//           by forward substitution, in place (D_0..D_2 also transposed)
+//   phase2  the off-diagonal blocks of T by two levels of 2 x 2 block
+//           inversion on split bf16 products (mm16x), in place
+//   emit    T diag(beta) as 384 bf16 pieces of 8 row elements: pieces
+//           0..255 rows 32-63 (8 per row), 256..383 rows 0-31, columns 0-31
+//           (4 per row), handed to sink(piece, value)
+// Rows past the chunk's valid tokens have k = 0, g = 0, beta = 0 and come
+// out as identity rows of T and zero columns of T_u.
+// ---------------------------------------------------------------------------
+struct WaveSolver {
+    float *sv;
+    __device__ float *blk(int I, int J) const { return sv + (I * (I + 1) / 2 + J) * SV_BLK; }
+    __device__ float *dtr(int b) const { return sv + 10 * SV_BLK + 256 * b; }   // D_b^T, row stride 16
+    __device__ float *gl() const { return sv + 10 * SV_BLK + 3 * 256; }         // gamma log2(e)
+    __device__ float *be() const { return gl() + C; }                           // beta
+
+    // K rows 16 I + lane % 16, columns 32 s + 8 (lane / 16) .. of a chunk whose
+    // first row is `krow` (rows tstride elements apart), and g, beta of token
+    // `lane` (H floats apart); rows past `nrow` read as zero
+    __device__ static void fetch(const bf16 *krow, int tstride, const float *grow,
+                                 const float *brow, int H, int nrow, int lane,
+                                 bf16x8 (&kr)[4][4], float &gv, float &bv) {
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)krow, 0, (unsigned)nrow * tstride * 2, 0x00020000);
+        const unsigned off = (unsigned)(((lane & 15) * tstride + 8 * (lane >> 4)) * 2);
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2)
+                kr[I][s2] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                rk, off, (unsigned)((16 * I * tstride + 32 * s2) * 2), 0));
+        const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)grow, 0, (unsigned)nrow * H * 4, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)brow, 0, (unsigned)nrow * H * 4, 0x00020000);
+        gv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, 4 * H * lane, 0, 0));
+        bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, 4 * H * lane, 0, 0));
+    }
+    // accumulator layout (lane (q, m) holds rows 4 q + r of column m) -> row-major block
+    __device__ static void store_blk(float *p, f32x4 acc, int lane) {
+        const int m = lane & 15, qq = lane >> 4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[(4 * qq + r) * SV_LD + m] = acc[r];
+    }
+    __device__ void phase1(const bf16x8 (&kr)[4][4], float gv, float bv, int lane) const {
+        float *sgl = gl(), *sbe = be();
+        const int m = lane & 15, qq = lane >> 4;
+        const float gam = wave_inclusive_scan(gv);
+        sgl[lane] = gam * 1.4426950408889634f;
+        sbe[lane] = bv;
+        // Gram blocks (I, J), J <= I: G[16 I + 4 q + r][16 J + m]
+        f32x4 G[10];
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int J = 0; J <= I; ++J) {
+                f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) a = mfma16(kr[I][s2], kr[J][s2], a);
+                G[I * (I + 1) / 2 + J] = a;
+            }
+        wave_lds_order();
+        // A_ij = -beta_i G_ij e^{gamma_i - gamma_j} for j < i (each
+        // exponent <= 0), zero elsewhere; row-major into the blocks
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            const f32x4 gli = *reinterpret_cast<const f32x4 *>(sgl + 16 * I + 4 * qq);
+            const f32x4 bi = *reinterpret_cast<const f32x4 *>(sbe + 16 * I + 4 * qq);
+#pragma unroll
+            for (int J = 0; J <= I; ++J) {
+                const float glj = sgl[16 * J + m];
+                f32x4 a = G[I * (I + 1) / 2 + J];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float e = __builtin_amdgcn_exp2f(gli[r] - glj);
+                    a[r] = (J < I || m < 4 * qq + r) ? -(bi[r] * a[r]) * e : 0.f;
+                }
+                store_blk(blk(I, J), a, lane);
+            }
+        }
+        wave_lds_order();
+        // diagonal blocks, one per 16 lanes: lane 16 b + c computes
+        // column c of D_b = (I - A_bb)^-1 row by row,
+        // D[i][c] = [i == c] + sum_{j < i} A[i][j] D[j][c]
+        // (row i + 1 read while row i is summed)
+        const int bb = lane >> 4, c = lane & 15;
+        const float *Ab = blk(bb, bb);
+        float D[16];
+        f32x4 rowv[2][4];
+        auto load_row = [&](int i, f32x4 (&dstv)[4]) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                if (4 * t < i) dstv[t] = *reinterpret_cast<const f32x4 *>(Ab + i * SV_LD + 4 * t);
+        };
+        load_row(1, rowv[1]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (i + 1 < 16) load_row(i + 1, rowv[(i + 1) & 1]);
+            float acc = i == c ? 1.f : 0.f;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (4 * t + e < i) acc += rowv[i & 1][t][e] * D[4 * t + e];
+            D[i] = acc;
+        }
+        wave_lds_order();
+        // D_b row-major in place; D_0, D_1, D_2 also transposed (their
+        // columns are right-hand operands below)
+        float *Db = blk(bb, bb);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Db[i * SV_LD + c] = D[i];
+        if (bb < 3) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                *reinterpret_cast<f32x4 *>(dtr(bb) + c * 16 + 4 * t) =
+                    f32x4{D[4 * t], D[4 * t + 1], D[4 * t + 2], D[4 * t + 3]};
+        }
+        wave_lds_order();
+    }
+    __device__ void phase2(int lane) const {
+        const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+        const int m = lane & 15, qq = lane >> 4;
+        // With D_b the diagonal inverses:
+        //   T10 = D1 A10 D0,  T32 = D3 A32 D2,  T21 = D2 A21 D1
+        //   T20 = D2 (A20 D0 + A21 T10)
+        //   T31 = T32 (A21 D1) + D3 (A31 D1)
+        //   T30 = T32 (A20 D0 + A21 T10) + D3 (A30 D0 + A31 T10)
+        // Left factors are row pieces of row-major blocks, right
+        // factors column pieces of D_b^T or accumulators.
+        auto piece = [&](const float *p, int ld) {
+            return *reinterpret_cast<const f32x4 *>(p + m * ld + 4 * qq);
+        };
+        const LSplit lA10 = lsplit(piece(blk(1, 0), SV_LD)), lA32 = lsplit(piece(blk(3, 2), SV_LD));
+        const LSplit lA21 = lsplit(piece(blk(2, 1), SV_LD)), lA20 = lsplit(piece(blk(2, 0), SV_LD));
+        const LSplit lA31 = lsplit(piece(blk(3, 1), SV_LD)), lA30 = lsplit(piece(blk(3, 0), SV_LD));
+        const LSplit lD1 = lsplit(piece(blk(1, 1), SV_LD)), lD2 = lsplit(piece(blk(2, 2), SV_LD));
+        const LSplit lD3 = lsplit(piece(blk(3, 3), SV_LD));
+        const bf16x8 rD0 = rsplit(piece(dtr(0), 16)), rD1 = rsplit(piece(dtr(1), 16));
+        const bf16x8 rD2 = rsplit(piece(dtr(2), 16));
+        const f32x4 u10 = mm16x(z4, lA10, rD0);
+        const f32x4 u32 = mm16x(z4, lA32, rD2);
+        const bf16x8 X = rsplit(mm16x(z4, lA21, rD1));         // A21 D1
+        const f32x4 W0 = mm16x(z4, lA20, rD0);                 // A20 D0
+        const bf16x8 Z = rsplit(mm16x(z4, lA31, rD1));         // A31 D1
+        const f32x4 V0 = mm16x(z4, lA30, rD0);                 // A30 D0
+        const f32x4 t10 = mm16x(z4, lD1, rsplit(u10));
+        const f32x4 t32 = mm16x(z4, lD3, rsplit(u32));
+        const f32x4 t21 = mm16x(z4, lD2, X);
+        const bf16x8 rT10 = rsplit(t10);
+        const bf16x8 W = rsplit(mm16x(W0, lA21, rT10));        // + A21 T10
+        const bf16x8 V = rsplit(mm16x(V0, lA31, rT10));        // + A31 T10
+        const f32x4 t20 = mm16x(z4, lD2, W);
+        // T32 is a left factor next: through its block (A32 is read)
+        store_blk(blk(3, 2), t32, lane);
+        wave_lds_order();
+        const LSplit lT32 = lsplit(piece(blk(3, 2), SV_LD));
+        const f32x4 t31 = mm16x(mm16x(z4, lT32, X), lD3, Z);
+        const f32x4 t30 = mm16x(mm16x(z4, lT32, W), lD3, V);
+        store_blk(blk(1, 0), t10, lane);
+        store_blk(blk(2, 1), t21, lane);
+        store_blk(blk(2, 0), t20, lane);
+        store_blk(blk(3, 1), t31, lane);
+        store_blk(blk(3, 0), t30, lane);
+        wave_lds_order();
+    }
+    template <typename Sink> __device__ void emit(int lane, Sink &&sink) const {
+        const float *sbe = be();
+        // T diag(beta) as bf16 pieces of 8 row elements: pieces
+        // 0..255 rows 32-63 (8 per row), 256..383 rows 0-31, columns
+        // 0-31 (4 per row); blocks above the diagonal are zero
+#pragma unroll
+        for (int u6 = 0; u6 < 6; ++u6) {
+            const int e = lane + 64 * u6;
+            const int i = u6 < 4 ? 32 + (e >> 3) : (e - 256) >> 2;
+            const int gc = u6 < 4 ? e & 7 : e & 3;
+            const int I = i >> 4, J = gc >> 1;
+            const float *tp = blk(I, J < I ? J : I) + (i & 15) * SV_LD + 8 * (gc & 1);
+            const f32x4 t0 = *reinterpret_cast<const f32x4 *>(tp);
+            const f32x4 t1 = *reinterpret_cast<const f32x4 *>(tp + 4);
+            const f32x4 b0 = *reinterpret_cast<const f32x4 *>(sbe + 8 * gc);
+            const f32x4 b1 = *reinterpret_cast<const f32x4 *>(sbe + 8 * gc + 4);
+            bf16x8 outp;
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                outp[e2] = (bf16)(J <= I ? t0[e2] * b0[e2] : 0.f);
+                outp[e2 + 4] = (bf16)(J <= I ? t1[e2] * b1[e2] : 0.f);
+            }
+            sink(e, outp);
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// chunk_solve: the first pass of the two-pass path with a scalar gate. One
+// wave per workgroup and (chunk, head) item at a time (items blockIdx.x,
+// + gridDim.x, ...), each wave with its own SV_BYTES of LDS, so that up to
+// ten items are in flight per compute unit and none waits at a workgroup
+// barrier. Writes T_u = T diag(beta) of the item into the workspace.
+// ---------------------------------------------------------------------------
+constexpr int SOLVE_NT = 64;
+__global__ void __launch_bounds__(SOLVE_NT)
+chunk_solve_kernel(const bf16 *__restrict__ k, const float *__restrict__ g,
+                   const float *__restrict__ beta, const int32_t *__restrict__ cu_seqlens,
+                   bf16 *__restrict__ ws, int T, int H, int Hk, int N, int nslots)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const WaveSolver sol{reinterpret_cast<float *>(smem)};
+    const int lane = (int)threadIdx.x;
+    const int nitems = nslots * H;
+    const int tstride = Hk * DK;
+    for (int item = (int)blockIdx.x; item < nitems; item += (int)gridDim.x) {
+        const PrepItem it = prep_locate(cu_seqlens, item, nitems, T, H, N);
+        if (it.nvalid == 0) continue;          // uniform
+        const size_t tok0 = (size_t)it.row0;
+        bf16x8 kr[4][4];
+        float gv, bv;
+        WaveSolver::fetch(k + tok0 * tstride + (size_t)(it.h / (H / Hk)) * DK, tstride,
+                          g + tok0 * H + it.h, beta + tok0 * H + it.h, H, it.nvalid, lane, kr,
+                          gv, bv);
+        sol.phase1(kr, gv, bv, lane);
+        sol.phase2(lane);
+        bf16 *dst = ws + ((size_t)it.h * nslots + it.slot) * ITEM_ELEMS;
+        sol.emit(lane, [&](int e, bf16x8 p) { *reinterpret_cast<bf16x8 *>(dst + 8 * e) = p; });
+        wave_lds_order();                      // the blocks read before the next item writes them
     }
 }
 
@@ -1813,181 +1885,11 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         auto sloop = [&](auto SID) {
             constexpr int sid = decltype(SID)::value;      // chunks c with c % 2 == sid
             __builtin_amdgcn_s_setprio(SV_PRIO);
-            float *sv = reinterpret_cast<float *>(smem + L::SV + sid * SV_BYTES);
-            float *sgl = sv + 10 * SV_BLK + 3 * 256, *sbe = sgl + C;
-            auto blk = [&](int I, int J) { return sv + (I * (I + 1) / 2 + J) * SV_BLK; };
-            auto dtr = [&](int b) { return sv + 10 * SV_BLK + 256 * b; };     // D_b^T, row stride 16
+            const WaveSolver sol{reinterpret_cast<float *>(smem + L::SV + sid * SV_BYTES)};
             const bf16 *k_head = k + (size_t)bos * (Hk * DK) + (size_t)(h / (H / Hk)) * DK;
             const float *b_head = beta + (size_t)bos * H + h;
-            bf16x8 kr[4][4];                   // K rows 16 I + lane%16, columns 32 s + 8 (lane/16) ..
+            bf16x8 kr[4][4];
             float gv = 0.f, bv = 0.f;
-            auto sfetch = [&](int c) {
-                const int base = c * C;
-                const int nrow = len - base < C ? len - base : C;
-                const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-                    (void *)(k_head + (size_t)base * tstride), 0, (unsigned)nrow * tstride * 2, 0x00020000);
-                const unsigned off = (unsigned)(((lane0 & 15) * tstride + 8 * (lane0 >> 4)) * 2);
-#pragma unroll
-                for (int I = 0; I < 4; ++I)
-#pragma unroll
-                    for (int s2 = 0; s2 < 4; ++s2)
-                        kr[I][s2] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                        rk, off, (unsigned)((16 * I * tstride + 32 * s2) * 2), 0));
-                const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
-                    (void *)(g_head + (size_t)base * H), 0, (unsigned)nrow * H * 4, 0x00020000);
-                const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-                    (void *)(b_head + (size_t)base * H), 0, (unsigned)nrow * H * 4, 0x00020000);
-                gv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, 4 * H * lane0, 0, 0));
-                bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, 4 * H * lane0, 0, 0));
-            };
-            // acc layout (lane (q, m) holds rows 4 q + r of column m) -> row-major block
-            auto store_blk = [&](float *p, f32x4 acc, int lane) {
-                const int m = lane & 15, qq = lane >> 4;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) p[(4 * qq + r) * SV_LD + m] = acc[r];
-            };
-            auto phase1 = [&](int lane) {
-                const int m = lane & 15, qq = lane >> 4;
-                const float gam = wave_inclusive_scan(gv);
-                sgl[lane] = gam * 1.4426950408889634f;
-                sbe[lane] = bv;
-                // Gram blocks (I, J), J <= I: G[16 I + 4 q + r][16 J + m]
-                f32x4 G[10];
-#pragma unroll
-                for (int I = 0; I < 4; ++I)
-#pragma unroll
-                    for (int J = 0; J <= I; ++J) {
-                        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int s2 = 0; s2 < 4; ++s2) a = mfma16(kr[I][s2], kr[J][s2], a);
-                        G[I * (I + 1) / 2 + J] = a;
-                    }
-                wave_lds_order();
-                // A_ij = -beta_i G_ij e^{gamma_i - gamma_j} for j < i (each
-                // exponent <= 0), zero elsewhere; row-major into the blocks
-#pragma unroll
-                for (int I = 0; I < 4; ++I) {
-                    const f32x4 gli = *reinterpret_cast<const f32x4 *>(sgl + 16 * I + 4 * qq);
-                    const f32x4 bi = *reinterpret_cast<const f32x4 *>(sbe + 16 * I + 4 * qq);
-#pragma unroll
-                    for (int J = 0; J <= I; ++J) {
-                        const float glj = sgl[16 * J + m];
-                        f32x4 a = G[I * (I + 1) / 2 + J];
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const float e = __builtin_amdgcn_exp2f(gli[r] - glj);
-                            a[r] = (J < I || m < 4 * qq + r) ? -(bi[r] * a[r]) * e : 0.f;
-                        }
-                        store_blk(blk(I, J), a, lane);
-                    }
-                }
-                wave_lds_order();
-                // diagonal blocks, one per 16 lanes: lane 16 b + c computes
-                // column c of D_b = (I - A_bb)^-1 row by row,
-                // D[i][c] = [i == c] + sum_{j < i} A[i][j] D[j][c]
-                // (row i + 1 read while row i is summed)
-                const int bb = lane >> 4, c = lane & 15;
-                const float *Ab = blk(bb, bb);
-                float D[16];
-                f32x4 rowv[2][4];
-                auto load_row = [&](int i, f32x4 (&dstv)[4]) {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        if (4 * t < i) dstv[t] = *reinterpret_cast<const f32x4 *>(Ab + i * SV_LD + 4 * t);
-                };
-                load_row(1, rowv[1]);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    if (i + 1 < 16) load_row(i + 1, rowv[(i + 1) & 1]);
-                    float acc = i == c ? 1.f : 0.f;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (4 * t + e < i) acc += rowv[i & 1][t][e] * D[4 * t + e];
-                    D[i] = acc;
-                }
-                wave_lds_order();
-                // D_b row-major in place; D_0, D_1, D_2 also transposed (their
-                // columns are right-hand operands below)
-                float *Db = blk(bb, bb);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) Db[i * SV_LD + c] = D[i];
-                if (bb < 3) {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        *reinterpret_cast<f32x4 *>(dtr(bb) + c * 16 + 4 * t) =
-                            f32x4{D[4 * t], D[4 * t + 1], D[4 * t + 2], D[4 * t + 3]};
-                }
-                wave_lds_order();
-            };
-            auto phase2 = [&](int buf, int lane) {
-                const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-                const int m = lane & 15, qq = lane >> 4;
-                // With D_b the diagonal inverses:
-                //   T10 = D1 A10 D0,  T32 = D3 A32 D2,  T21 = D2 A21 D1
-                //   T20 = D2 (A20 D0 + A21 T10)
-                //   T31 = T32 (A21 D1) + D3 (A31 D1)
-                //   T30 = T32 (A20 D0 + A21 T10) + D3 (A30 D0 + A31 T10)
-                // Left factors are row pieces of row-major blocks, right
-                // factors column pieces of D_b^T or accumulators.
-                auto piece = [&](const float *p, int ld) {
-                    return *reinterpret_cast<const f32x4 *>(p + m * ld + 4 * qq);
-                };
-                const f32x4 lA10 = piece(blk(1, 0), SV_LD), lA32 = piece(blk(3, 2), SV_LD);
-                const f32x4 lA21 = piece(blk(2, 1), SV_LD), lA20 = piece(blk(2, 0), SV_LD);
-                const f32x4 lA31 = piece(blk(3, 1), SV_LD), lA30 = piece(blk(3, 0), SV_LD);
-                const f32x4 lD1 = piece(blk(1, 1), SV_LD), lD2 = piece(blk(2, 2), SV_LD);
-                const f32x4 lD3 = piece(blk(3, 3), SV_LD);
-                const f32x4 rD0 = piece(dtr(0), 16), rD1 = piece(dtr(1), 16), rD2 = piece(dtr(2), 16);
-                const f32x4 u10 = mm16x(z4, lA10, rD0);
-                const f32x4 u32 = mm16x(z4, lA32, rD2);
-                const f32x4 X = mm16x(z4, lA21, rD1);                  // A21 D1
-                const f32x4 W0 = mm16x(z4, lA20, rD0);                 // A20 D0
-                const f32x4 Z = mm16x(z4, lA31, rD1);                  // A31 D1
-                const f32x4 V0 = mm16x(z4, lA30, rD0);                 // A30 D0
-                const f32x4 t10 = mm16x(z4, lD1, u10);
-                const f32x4 t32 = mm16x(z4, lD3, u32);
-                const f32x4 t21 = mm16x(z4, lD2, X);
-                const f32x4 W = mm16x(W0, lA21, t10);                  // + A21 T10
-                const f32x4 V = mm16x(V0, lA31, t10);                  // + A31 T10
-                const f32x4 t20 = mm16x(z4, lD2, W);
-                // T32 is a left factor next: through its block (A32 is read)
-                store_blk(blk(3, 2), t32, lane);
-                wave_lds_order();
-                const f32x4 lT32 = piece(blk(3, 2), SV_LD);
-                const f32x4 t31 = mm16x(mm16x(z4, lT32, X), lD3, Z);
-                const f32x4 t30 = mm16x(mm16x(z4, lT32, W), lD3, V);
-                store_blk(blk(1, 0), t10, lane);
-                store_blk(blk(2, 1), t21, lane);
-                store_blk(blk(2, 0), t20, lane);
-                store_blk(blk(3, 1), t31, lane);
-                store_blk(blk(3, 0), t30, lane);
-                wave_lds_order();
-                // T diag(beta) as bf16 pieces of 8 row elements: pieces
-                // 0..255 rows 32-63 (8 per row), 256..383 rows 0-31, columns
-                // 0-31 (4 per row); blocks above the diagonal are zero
-                bf16 *sb = lds + (OFF_BUF + buf * SZ_BUF) / 2;
-#pragma unroll
-                for (int u6 = 0; u6 < 6; ++u6) {
-                    const int e = lane + 64 * u6;
-                    const int i = u6 < 4 ? 32 + (e >> 3) : (e - 256) >> 2;
-                    const int gc = u6 < 4 ? e & 7 : e & 3;
-                    const int I = i >> 4, J = gc >> 1;
-                    const float *tp = blk(I, J < I ? J : I) + (i & 15) * SV_LD + 8 * (gc & 1);
-                    const f32x4 t0 = *reinterpret_cast<const f32x4 *>(tp);
-                    const f32x4 t1 = *reinterpret_cast<const f32x4 *>(tp + 4);
-                    const f32x4 b0 = *reinterpret_cast<const f32x4 *>(sbe + 8 * gc);
-                    const f32x4 b1 = *reinterpret_cast<const f32x4 *>(sbe + 8 * gc + 4);
-                    bf16x8 outp;
-#pragma unroll
-                    for (int e2 = 0; e2 < 4; ++e2) {
-                        outp[e2] = (bf16)(J <= I ? t0[e2] * b0[e2] : 0.f);
-                        outp[e2 + 4] = (bf16)(J <= I ? t1[e2] * b1[e2] : 0.f);
-                    }
-                    *reinterpret_cast<bf16x8 *>(sb + tpiece_loff(e)) = outp;
-                }
-            };
             for (int ch0 = -3; ch0 <= nchunks; ch0 += 2)
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
@@ -1998,10 +1900,20 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                 if (hf == sid) {
                     // (ch + 1) % 2 == sid: finish chunk ch + 1 into staging hf,
                     // then load chunk ch + 3
-                    if (ch + 1 >= 0 && ch + 1 < nchunks) phase2(hf, lane);
-                    sfetch(ch + 3 < 0 ? 0 : ch + 3 < nchunks ? ch + 3 : nchunks - 1);
+                    if (ch + 1 >= 0 && ch + 1 < nchunks) {
+                        sol.phase2(lane);
+                        bf16 *sb = lds + (OFF_BUF + hf * SZ_BUF) / 2;
+                        sol.emit(lane, [&](int e, bf16x8 p) {
+                            *reinterpret_cast<bf16x8 *>(sb + tpiece_loff(e)) = p;
+                        });
+                    }
+                    const int cf = ch + 3 < 0 ? 0 : ch + 3 < nchunks ? ch + 3 : nchunks - 1;
+                    const int nrow = len - cf * C < C ? len - cf * C : C;
+                    WaveSolver::fetch(k_head + (size_t)cf * C * tstride, tstride,
+                                      g_head + (size_t)cf * C * H, b_head + (size_t)cf * C * H, H,
+                                      nrow, lane, kr, gv, bv);
                 } else if (ch + 2 >= 0 && ch + 2 < nchunks) {
-                    phase1(lane);              // chunk ch + 2
+                    sol.phase1(kr, gv, bv, lane);  // chunk ch + 2
                 }
                 lds_barrier();
             }
@@ -2036,7 +1948,7 @@ size_t prefill_split_workspace_bytes(long tokens, int H, int N, bool per_channel
 // Workgroups that fill every CU of the current device at the occupancy a
 // persistent prep kernel reaches (cached per device; concurrent first calls
 // compute the same value).
-static hipError_t prep_fill(const void *kern, int lds, std::atomic<long> *cache, long &fill)
+static hipError_t prep_fill(const void *kern, int nt, int lds, std::atomic<long> *cache, long &fill)
 {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -2045,7 +1957,7 @@ static hipError_t prep_fill(const void *kern, int lds, std::atomic<long> *cache,
     if (fill == 0) {
         int cus = 0, per_cu = 0;
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, P_NT, lds);
+        if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, nt, lds);
         if (e != hipSuccess) return e;
         fill = (long)(per_cu < 1 ? 1 : per_cu) * (cus < 1 ? 1 : cus);
         if (dev < MAX_DEVICES) cache[dev].store(fill, std::memory_order_relaxed);
@@ -2068,7 +1980,8 @@ hipError_t launch_prefill_prepare(const void *q, const void *k, const float *g, 
             (const void *)chunk_prep_channel_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
             CP_LDS_BYTES);
         if (attr != hipSuccess) return attr;
-        hipError_t e = prep_fill((const void *)chunk_prep_channel_kernel, CP_LDS_BYTES, fill_channel, fill);
+        hipError_t e = prep_fill((const void *)chunk_prep_channel_kernel, P_NT, CP_LDS_BYTES,
+                                 fill_channel, fill);
         if (e != hipSuccess) return e;
         dim3 grid((unsigned)(nitems < fill ? nitems : fill)), block(P_NT);
         hipLaunchKernelGGL(chunk_prep_channel_kernel, grid, block, CP_LDS_BYTES, stream,
@@ -2076,10 +1989,13 @@ hipError_t launch_prefill_prepare(const void *q, const void *k, const float *g, 
                            (int)nslots);
         return hipGetLastError();
     }
-    hipError_t e = prep_fill((const void *)chunk_prep_kernel, P_LDS_BYTES, fill_scalar, fill);
+    static const hipError_t attr = hipFuncSetAttribute(
+        (const void *)chunk_solve_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, SV_BYTES);
+    if (attr != hipSuccess) return attr;
+    hipError_t e = prep_fill((const void *)chunk_solve_kernel, SOLVE_NT, SV_BYTES, fill_scalar, fill);
     if (e != hipSuccess) return e;
-    dim3 grid((unsigned)(nitems < fill ? nitems : fill)), block(P_NT);
-    hipLaunchKernelGGL(chunk_prep_kernel, grid, block, P_LDS_BYTES, stream, (const bf16 *)k, g,
+    dim3 grid((unsigned)(nitems < fill ? nitems : fill)), block(SOLVE_NT);
+    hipLaunchKernelGGL(chunk_solve_kernel, grid, block, SV_BYTES, stream, (const bf16 *)k, g,
                        beta, cu, (bf16 *)ws, T, H, Hk, N, (int)nslots);
     return hipGetLastError();
 }
