@@ -34,3 +34,14 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    # the parity figures of every GPU test that ran (relative error per slice,
+    # per-row error, elementwise allclose violations), whatever the verbosity
+    parity = sys.modules.get("parity")
+    lines = getattr(parity, "REPORTS", []) if parity else []
+    if lines:
+        terminalreporter.section("parity figures")
+        for line in lines:
+            terminalreporter.write_line(line)

@@ -116,6 +116,11 @@ def s_err(s, s_ref):
     return slice_rel_err(s, s_ref, axes=(2, 3))
 
 
+# every report of the session, printed again in pytest's terminal summary
+# (tests/conftest.py), so that the figures reach the log even with -q
+REPORTS = []
+
+
 def report(name, **errs):
     parts = []
     for k, v in errs.items():
@@ -123,4 +128,6 @@ def report(name, **errs):
         if isinstance(v, Err):
             parts.append(f"{k}_row={v.row:.3e} {k}_row_nofloor={v.row_raw:.3e} "
                          f"{k}_allclose_viol={v.allclose:.2e}")
-    print(f"[parity] {name}: {' '.join(parts)}", flush=True)
+    line = f"[parity] {name}: {' '.join(parts)}"
+    REPORTS.append(line)
+    print(line, flush=True)
