@@ -14,10 +14,13 @@
 //   S       <- e^{gamma_63} S + Delta~^T K,  Delta~_j = e^{gamma_63 - gamma_j} Delta_j
 //
 // Everything up to T_u = T diag(beta) depends on one chunk of one head only,
-// and is the same for every d_v column. The first pass (chunk_prep)
-// computes it once per (chunk, head), fully in parallel over all chunks,
-// from k, g and beta alone; the second pass (chunk_chain) walks the chunks
-// of each sequence in order and carries the state. The chain folds the
+// and is the same for every d_v column. The first pass (chunk_solve, one
+// wave per (chunk, head)) computes it once per (chunk, head), fully in
+// parallel over all chunks, from k, g and beta alone; the second pass
+// (chunk_chain) walks the chunks of each sequence in order and carries the
+// state. Without a workspace the chain kernel instead runs the same one-wave
+// solver on two of its own waves, two chunks ahead (chunk_chain_kernel with
+// FUSED). The chain folds the
 // decay into the delta,
 //   Delta = T_u (V - diag(e^gamma) K S^T)      (T_w K S^T = T_u diag(e^gamma) K S^T)
 // so only T_u crosses between the passes, and it forms P = lower_incl_diag(
@@ -26,7 +29,7 @@
 // of a head from each repeating it; the price is the 6 KiB bf16 T_u per
 // (chunk, head) written to the caller's workspace and read back: 96 B of
 // HBM traffic each way per token-head, on top of the 1032 B of q, k, v, o,
-// g and beta (the prep pass also reads k, g and beta a second time, 264 B).
+// g and beta (the solve pass also reads k, g and beta a second time, 264 B).
 //
 // q and k may have fewer heads (H_k) than v, g, beta, o and the state (H):
 // value head h reads query/key head h / (H / H_k) (the repeat_interleave head
