@@ -299,7 +299,7 @@ def bench_channel_gated(gdn, inputs, steps, warmup):
         gdn.gdn_prefill_channel_gated(q, k, v, g, beta, None, fin, o, scale=c.scale,
                                       workspace=None)
     ms_pre = event_time(pre, steps, warmup)
-    ms_serial = event_time(pre_serial, max(1, steps // 4), 1)
+    ms_serial = event_time(pre_serial, max(5, steps // 4), 3)
     # the method's bytes: q, k, v, o bf16, one fp32 log-decay per key channel,
     # beta, and the final states
     pre_bytes = 4 * 4096 * 16 * (4 * 128 * 2 + 128 * 4 + 4) + 4 * 16 * 128 * 128 * 4
@@ -342,7 +342,7 @@ def bench_seqpar(gdn, inputs, steps, warmup):
                      dtype=torch.uint8, device="cuda")
     ms_plain = event_time(lambda i: gdn.gdn_prefill(q, k, v, g, beta, None, fin, o,
                                                     scale=c.scale, workspace=ws),
-                          max(1, steps // 4), 1)
+                          max(5, steps // 4), 3)
     res = dict(workload="one sequence B=1 H=16 T=32768 d=128 bf16",
                plain_ms=round(ms_plain, 4),
                plain_tokens_per_s=round(32768 / (ms_plain * 1e-3), 1))
@@ -352,7 +352,7 @@ def bench_seqpar(gdn, inputs, steps, warmup):
                           dtype=torch.uint8, device="cuda")
         ms = event_time(lambda i: gdn.gdn_prefill_seqpar(q, k, v, g, beta, P, None, fin, o,
                                                          scale=c.scale, workspace=wsp),
-                        max(1, steps // 4), 1)
+                        max(5, steps // 4), 3)
         res[f"segments_{P}_ms"] = round(ms, 4)
         res[f"segments_{P}_tokens_per_s"] = round(32768 / (ms * 1e-3), 1)
         del wsp
@@ -386,10 +386,10 @@ def bench_mixer(gdn, inputs, steps, warmup):
 
     def full(i):
         pro(i); core(i); epi(i)
-    ms_full = event_time(full, max(1, steps // 4), 1)
-    ms_pro = event_time(pro, max(1, steps // 4), 1)
-    ms_core = event_time(core, max(1, steps // 4), 1)
-    ms_epi = event_time(epi, max(1, steps // 4), 1)
+    ms_full = event_time(full, max(5, steps // 4), 3)
+    ms_pro = event_time(pro, max(5, steps // 4), 3)
+    ms_core = event_time(core, max(5, steps // 4), 3)
+    ms_epi = event_time(epi, max(5, steps // 4), 3)
     pro_bytes = B * T * H * (D * 2 * 3 * 2 + 2 * 2 + 4 * 2)   # q,k,v in+out, a,b in, g,beta out
     epi_bytes = B * T * H * D * 2 * 3
     return dict(workload="token mixer B=8 T=8192 H=16 d=128 bf16: conv+SiLU, L2-norm, gates -> "
@@ -415,7 +415,7 @@ def bench_varlen(gdn, inputs, steps, warmup):
 
     def step(i):
         gdn.gdn_prefill(q, k, v, g, beta, s0, fin, o, cu_seqlens=cu, scale=c.scale, workspace=ws)
-    ms = event_time(step, max(1, steps // 4), 1)
+    ms = event_time(step, max(5, steps // 4), 3)
     total = int(c.cu_seqlens[-1])
     res = dict(workload="packed prefill H=32 d=128 bf16, 8 sequences log-uniform in [512, 65536], "
                         "non-zero initial states",
@@ -432,7 +432,7 @@ def bench_varlen(gdn, inputs, steps, warmup):
         ms = event_time(lambda i: gdn.gdn_prefill_seqpar(q, k, v, g, beta, P, s0, fin, o,
                                                          cu_seqlens=cu, scale=c.scale,
                                                          workspace=wsp),
-                        max(1, steps // 4), 1)
+                        max(5, steps // 4), 3)
         res[f"seqpar_{P}_ms"] = round(ms, 4)
         res[f"seqpar_{P}_tokens_per_s"] = round(total / (ms * 1e-3), 1)
         del wsp
