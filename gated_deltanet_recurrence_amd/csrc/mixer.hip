@@ -235,7 +235,9 @@ static hipError_t launch_conv(const void *xq, const void *xk, const void *xv, co
 {
     constexpr int GPB = 256 / (D / 8);
     const long tiles = (total + PRO_TT - 1) / PRO_TT;
-    const int heads = which0 < 2 ? Hk : H;
+    // heads of the widest tensor in the launch (lane groups past a tensor's
+    // heads return at once)
+    const int heads = which0 + nwhich > 2 ? (H > Hk ? H : Hk) : Hk;
     dim3 grid((unsigned)tiles, (unsigned)((heads + GPB - 1) / GPB), (unsigned)nwhich), block(256);
     hipLaunchKernelGGL((prologue_conv_kernel<D, TIO>), grid, block, 0, stream,
                        (const TIO *)xq, (const TIO *)xk, (const TIO *)xv, (const TIO *)w,
@@ -270,7 +272,11 @@ hipError_t launch_prologue(const void *q_raw, const void *k_raw, const void *v_r
 {
     const long total = (long)B * T;
     if (total == 0) return hipSuccess;
-    // q and k share a launch (same head size); v has its own.
+    // one launch for q, k and v when their head sizes agree (no gap between
+    // two launches); else q and k share a launch and v has its own
+    if (d_k == d_v)
+        return conv_dispatch<TIO>(d_k, q_raw, k_raw, v_raw, conv_w, q, k, v, a, b, A, dt_bias,
+                                  g, beta, cu, total, (long)T, N, H, Hk, d_k, 0, 3, stream);
     hipError_t e = conv_dispatch<TIO>(d_k, q_raw, k_raw, v_raw, conv_w, q, k, v, a, b, A, dt_bias,
                                       g, beta, cu, total, (long)T, N, H, Hk, d_k, 0, 2, stream);
     if (e != hipSuccess) return e;
