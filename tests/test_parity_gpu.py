@@ -216,6 +216,49 @@ def test_packed_with_empty_and_tiny_sequences(path):
             assert torch.equal(fin[n].cpu(), c.s0[n])
 
 
+def _many_lengths(n=300, seed=57):
+    rnd = np.random.default_rng(seed)
+    lengths = [int(x) for x in rnd.integers(0, 150, size=n)]
+    lengths[7] = 700                       # one sequence of 11 chunks among short ones
+    return lengths
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_packed_more_sequences_than_ranked(path):
+    """300 packed sequences (0 to 149 tokens, one of 700): more than the 256
+    that the chain pass deals longest first, so its index-order dealing runs;
+    every sequence against the oracle, empty ones keep their state."""
+    lengths = _many_lengths()
+    c = inputs.make_varlen(seed=56, H=2, d=128, lengths=lengths)
+    o, fin = run_prefill(c, path=path)
+    o_ref, s_ref = oracle_prefill(c)
+    cu = [int(x) for x in c.cu_seqlens.tolist()]
+    eo, es = o_err_packed(o, o_ref, cu), s_err(fin, s_ref)
+    report(f"packed 300 sequences {path}", o=eo, state=es)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+    for n, L in enumerate(lengths):
+        if L == 0:
+            assert torch.equal(fin[n].cpu(), c.s0[n])
+
+
+@pytest.mark.parametrize("segments", [1, 3])
+def test_seqpar_more_sequences_than_ranked(segments):
+    """The same 300 packed sequences through the sequence-parallel path: its
+    plan deals jobs in index order above 256 sequences; with 3 segments the
+    700-token sequence has middle segments."""
+    lengths = _many_lengths()
+    c = inputs.make_varlen(seed=56, H=2, d=128, lengths=lengths)
+    fin = torch.empty((len(lengths), 2, 128, 128), dtype=torch.float32, device="cuda:0")
+    o, _ = gdn.gdn_prefill_seqpar(dev(c.q), dev(c.k), dev(c.v), dev(c.g), dev(c.beta), segments,
+                                  dev(c.s0), fin, cu_seqlens=dev(c.cu_seqlens), scale=c.scale)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_prefill(c)
+    cu = [int(x) for x in c.cu_seqlens.tolist()]
+    eo, es = o_err_packed(o, o_ref, cu), s_err(fin, s_ref)
+    report(f"seqpar packed 300 sequences segments={segments}", o=eo, state=es)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_zero_length_batch(path):
     """T = 0: nothing to compute; the final state is the initial state."""
