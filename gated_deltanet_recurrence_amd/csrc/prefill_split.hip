@@ -1948,6 +1948,20 @@ size_t prefill_split_workspace_bytes(long tokens, int H, int N, bool per_channel
     return (size_t)nslots * H * (per_channel ? CH_ITEM_ELEMS : ITEM_ELEMS) * sizeof(bf16);
 }
 
+// Raise a kernel's dynamic LDS limit on the current device, once per device
+// (the attribute belongs to the device's copy of the kernel; concurrent first
+// calls set the same value).
+static hipError_t raise_lds_limit(const void *kern, int bytes, std::atomic<int> *done)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < MAX_DEVICES && done[dev].load(std::memory_order_relaxed)) return hipSuccess;
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && dev < MAX_DEVICES) done[dev].store(1, std::memory_order_relaxed);
+    return e;
+}
+
 // Workgroups that fill every CU of the current device at the occupancy a
 // persistent prep kernel reaches (cached per device; concurrent first calls
 // compute the same value).
@@ -1977,11 +1991,11 @@ hipError_t launch_prefill_prepare(const void *q, const void *k, const float *g, 
     if (tokens == 0) return hipSuccess;        // no chunk: nothing to prepare
     const long nitems = nslots * H;
     static std::atomic<long> fill_scalar[MAX_DEVICES], fill_channel[MAX_DEVICES];
+    static std::atomic<int> lds_scalar[MAX_DEVICES], lds_channel[MAX_DEVICES];
     long fill = 0;
     if (per_channel) {
-        static const hipError_t attr = hipFuncSetAttribute(
-            (const void *)chunk_prep_channel_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-            CP_LDS_BYTES);
+        const hipError_t attr = raise_lds_limit((const void *)chunk_prep_channel_kernel,
+                                                CP_LDS_BYTES, lds_channel);
         if (attr != hipSuccess) return attr;
         hipError_t e = prep_fill((const void *)chunk_prep_channel_kernel, P_NT, CP_LDS_BYTES,
                                  fill_channel, fill);
@@ -1992,8 +2006,7 @@ hipError_t launch_prefill_prepare(const void *q, const void *k, const float *g, 
                            (int)nslots);
         return hipGetLastError();
     }
-    static const hipError_t attr = hipFuncSetAttribute(
-        (const void *)chunk_solve_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, SV_BYTES);
+    const hipError_t attr = raise_lds_limit((const void *)chunk_solve_kernel, SV_BYTES, lds_scalar);
     if (attr != hipSuccess) return attr;
     hipError_t e = prep_fill((const void *)chunk_solve_kernel, SOLVE_NT, SV_BYTES, fill_scalar, fill);
     if (e != hipSuccess) return e;
@@ -2014,10 +2027,10 @@ static hipError_t launch_chain(const void *q, const void *k, const void *v, cons
                                int njobs)
 {
     constexpr int LDS_BYTES = ChainLds<PERCH, FUSED>::BYTES;
-    // the dynamic LDS limit, raised once per process (thread-safe static)
-    static const hipError_t attr = hipFuncSetAttribute(
-        (const void *)chunk_chain_kernel<PERCH, FUSED>, hipFuncAttributeMaxDynamicSharedMemorySize,
-        LDS_BYTES);
+    // the dynamic LDS limit, raised once per device (one flag set per instantiation)
+    static std::atomic<int> lds_done[MAX_DEVICES];
+    const hipError_t attr = raise_lds_limit((const void *)chunk_chain_kernel<PERCH, FUSED>,
+                                            LDS_BYTES, lds_done);
     if (attr != hipSuccess) return attr;
     const long tokens = cu ? (long)T : (long)N * T;
     const long nslots = tokens / C + N + 1;

@@ -205,6 +205,7 @@ __global__ void state_copy_kernel(const float *src, float *dst, long n4)
 // accumulators halve the dependent chain.
 constexpr int SC_NT = 512;
 constexpr int SC_LDS_BYTES = 16 * (SP_D + 4) * 4;
+static_assert(SC_LDS_BYTES <= 65536, "within the default dynamic LDS limit");
 __global__ void __launch_bounds__(SC_NT)
 seg_compose_kernel(const float *__restrict__ Amat, const float *__restrict__ Bmat,
                    float *__restrict__ inits, const int32_t *__restrict__ seg_first,
@@ -326,15 +327,11 @@ hipError_t launch_prefill_seqpar(const void *q, const void *k, const void *v, co
     if (e == hipSuccess)          // pass 1: segment 0 of each sequence, B and A of the middle ones
         e = launch_prefill_apply(q, k, v, g, nullptr, nullptr, o, cu_seg, total, H, Hk, nsmax,
                                  scale, prep, stream, 0, false, job1, 2 * nsmax);
-    if (e == hipSuccess) {        // compose: the start states, in order
-        static const hipError_t attr = hipFuncSetAttribute(
-            (const void *)seg_compose_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, SC_LDS_BYTES);
-        e = attr;
-        if (e == hipSuccess) {
-            hipLaunchKernelGGL(seg_compose_kernel, dim3((unsigned)(N * H), SP_D / 16), dim3(SC_NT),
-                               SC_LDS_BYTES, stream, Am, Bm, In, first, count, H);
-            e = hipGetLastError();
-        }
+    if (e == hipSuccess) {        // compose: the start states, in order (8.4 KB of LDS:
+                                  // within the default dynamic limit)
+        hipLaunchKernelGGL(seg_compose_kernel, dim3((unsigned)(N * H), SP_D / 16), dim3(SC_NT),
+                           SC_LDS_BYTES, stream, Am, Bm, In, first, count, H);
+        e = hipGetLastError();
     }
     if (e == hipSuccess)          // pass 2: the other segments from their true start states
         e = launch_prefill_apply(q, k, v, g, nullptr, nullptr, o, cu_seg, total, H, Hk, nsmax,
