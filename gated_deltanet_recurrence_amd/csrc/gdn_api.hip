@@ -45,6 +45,11 @@ bool chunk_path(int dtype, int d_k, int d_v) {
     return dtype == GDN_DTYPE_BF16 && d_k == 128 && d_v == 128;
 }
 
+// the two-pass kernels index (chunk slot, head) items with 32-bit integers
+bool items_fit(int64_t tokens, int H, int64_t N) {
+    return (tokens / 64 + N + 1) * H <= (int64_t)INT32_MAX;
+}
+
 // a caller's workspace for the two-pass chunk path: 256-byte aligned, large enough
 bool workspace_ok(const void *ws, size_t bytes, int B, int T, int H, int N,
                   bool per_channel = false) {
@@ -146,8 +151,10 @@ int gdn_prefill_workspace_size(int B, int T, int H, int d_k, int d_v, int N, int
     const int st = check_prefill(p, p, p, (const float *)p, (const float *)p, p, cu, B, T, H,
                                  H, d_k, d_v, N, dtype);
     if (st != GDN_OK) return st;
-    if (chunk_path(dtype, d_k, d_v))
+    if (chunk_path(dtype, d_k, d_v)) {
+        if (!items_fit((int64_t)B * T, H, N)) return GDN_ERR_UNSUPPORTED;
         *bytes = gdn::prefill_split_workspace_bytes((long)B * T, H, N);
+    }
     return GDN_OK;
 }
 
@@ -165,6 +172,7 @@ int gdn_prefill(const void *q, const void *k, const void *v, const float *g, con
             return status_of(gdn::launch_prefill_fused(q, k, v, g, beta, initial_state,
                                                        final_state, o, cu_seqlens, T, H, H_k,
                                                        N, scale, s));
+        if (!items_fit((int64_t)B * T, H, N)) return GDN_ERR_UNSUPPORTED;
         if (!workspace_ok(workspace, workspace_bytes, B, T, H, N)) return GDN_ERR_WORKSPACE;
         hipError_t e = gdn::launch_prefill_prepare(q, k, g, beta, cu_seqlens, T, H, H_k, N,
                                                    workspace, s);
@@ -209,7 +217,8 @@ int gdn_prefill_prepare(const void *q, const void *k, const float *g, const floa
     const void *p = workspace ? workspace : (const void *)k;
     int st = check_prefill(q, k, p, g, beta, p, cu_seqlens, B, T, H, H_k, d_k, d_v, N, dtype);
     if (st != GDN_OK) return st;
-    if (!chunk_path(dtype, d_k, d_v)) return GDN_ERR_UNSUPPORTED;
+    if (!chunk_path(dtype, d_k, d_v) || !items_fit((int64_t)B * T, H, N))
+        return GDN_ERR_UNSUPPORTED;
     if (!workspace) return GDN_ERR_NULL;
     if (!workspace_ok(workspace, workspace_bytes, B, T, H, N)) return GDN_ERR_WORKSPACE;
     return status_of(gdn::launch_prefill_prepare(q, k, g, beta, cu_seqlens, T, H, H_k, N,
@@ -226,7 +235,8 @@ int gdn_prefill_apply(const void *q, const void *k, const void *v, const float *
     const float *pb = workspace ? (const float *)workspace : g;
     int st = check_prefill(q, k, v, g, pb, o, cu_seqlens, B, T, H, H_k, d_k, d_v, N, dtype);
     if (st != GDN_OK) return st;
-    if (!chunk_path(dtype, d_k, d_v)) return GDN_ERR_UNSUPPORTED;
+    if (!chunk_path(dtype, d_k, d_v) || !items_fit((int64_t)B * T, H, N))
+        return GDN_ERR_UNSUPPORTED;
     if (!workspace) return GDN_ERR_NULL;
     if (!workspace_ok(workspace, workspace_bytes, B, T, H, N)) return GDN_ERR_WORKSPACE;
     return status_of(gdn::launch_prefill_apply(q, k, v, g, initial_state, final_state, o,
@@ -326,8 +336,10 @@ int gdn_prefill_channel_workspace_size(int B, int T, int H, int d_k, int d_v, in
     const int st = check_prefill(p, p, p, (const float *)p, (const float *)p, p, cu, B, T, H,
                                  H, d_k, d_v, N, dtype);
     if (st != GDN_OK) return st;
-    if (chunk_path(dtype, d_k, d_v))
+    if (chunk_path(dtype, d_k, d_v)) {
+        if (!items_fit((int64_t)B * T, H, N)) return GDN_ERR_UNSUPPORTED;
         *bytes = gdn::prefill_split_workspace_bytes((long)B * T, H, N, true);
+    }
     return GDN_OK;
 }
 
@@ -341,6 +353,7 @@ int gdn_prefill_channel_gated(const void *q, const void *k, const void *v, const
     if (st != GDN_OK) return st;
     hipStream_t s = (hipStream_t)stream;
     if (workspace && chunk_path(dtype, d_k, d_v)) {
+        if (!items_fit((int64_t)B * T, H, N)) return GDN_ERR_UNSUPPORTED;
         if (!workspace_ok(workspace, workspace_bytes, B, T, H, N, true)) return GDN_ERR_WORKSPACE;
         hipError_t e = gdn::launch_prefill_prepare(q, k, g, beta, cu_seqlens, T, H, H_k, N,
                                                    workspace, s, true);
@@ -391,6 +404,7 @@ static int check_seqpar(const void *q, const void *k, const void *v, const float
     // segment, H pairs per job, 4 workgroups per pair
     if ((int64_t)N * segments > 65535) return GDN_ERR_UNSUPPORTED;
     if ((int64_t)N * segments * H * 8 > (int64_t)INT32_MAX) return GDN_ERR_UNSUPPORTED;
+    if (!items_fit((int64_t)B * T, H, (int64_t)N * segments)) return GDN_ERR_UNSUPPORTED;
     return GDN_OK;
 }
 

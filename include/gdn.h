@@ -135,7 +135,10 @@ const char *gdn_status_string(int status);
  *                 the token-serial path. Calls that share a workspace must be
  *                 ordered on one stream.
  *   workspace_bytes  size of workspace; GDN_ERR_WORKSPACE if workspace is
- *                 non-NULL and too small or misaligned.
+ *                 non-NULL and too small or misaligned. The two-pass path
+ *                 counts (64-token chunk slot, head) items, (B*T/64 + N + 1)
+ *                 * H, in 32 bits: above 2^31 - 1 it returns
+ *                 GDN_ERR_UNSUPPORTED (the workspace would exceed 12 TB).
  */
 int gdn_prefill(const void *q, const void *k, const void *v,
                 const float *g, const float *beta,
@@ -246,7 +249,8 @@ int gdn_prefill_apply(const void *q, const void *k, const void *v, const float *
  *                 sequences: B = 1); bf16 with d_k = d_v = 128 only (else
  *                 GDN_ERR_UNSUPPORTED)
  *   segments      >= 1, segments of the longest sequence; N * segments <=
- *                 65535 (else GDN_ERR_UNSUPPORTED)
+ *                 65535 and (B*T/64 + N * segments + 1) * H < 2^31 (else
+ *                 GDN_ERR_UNSUPPORTED)
  *   workspace     required, gdn_prefill_seqpar_workspace_size() bytes,
  *                 256-byte aligned, caller-owned; contents on entry do not
  *                 matter. Calls that share a workspace must be ordered on one

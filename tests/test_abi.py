@@ -176,6 +176,19 @@ def test_prepare_apply_validation(lib):
     b = list(a)
     b[6] = None                              # o
     assert app(*b, 1, 100, 1, 1, 128, 128, 1, 1.0, 1, ws, need, None) == GDN_ERR_NULL
+    # more (64-token slot, head) items than 32-bit indices reach: rejected
+    # before the workspace is looked at
+    big = (1, 2**31 - 1, 64, 64, 128, 128, 1)   # B, T, H, H_k, d_k, d_v, N
+    assert prep(P, P, P, P, None, *big, 1, ws, 1 << 62, None) == GDN_ERR_UNSUPPORTED
+    assert app(*a, *big, 1.0, 1, ws, 1 << 62, None) == GDN_ERR_UNSUPPORTED
+    assert lib.gdn_prefill(P, P, P, P, P, None, None, P, None, *big, 1.0, 1, ws, 1 << 62,
+                           None) == GDN_ERR_UNSUPPORTED
+    out = ctypes.c_size_t(0)
+    assert lib.gdn_prefill_workspace_size(1, 2**31 - 1, 64, 128, 128, 1, 0, 1,
+                                          ctypes.byref(out)) == GDN_ERR_UNSUPPORTED
+    # one head fewer fits
+    assert lib.gdn_prefill_workspace_size(1, 2**31 - 1, 63, 128, 128, 1, 0, 1,
+                                          ctypes.byref(out)) == GDN_OK and out.value > 0
 
 
 def test_channel_gated_validation(lib):
@@ -219,6 +232,7 @@ def test_seqpar_validation(lib):
     assert f(1, 4096, 16, 128, 128, 1, 0, 8, 1, None) == GDN_ERR_NULL
     assert f(2, 4096, 16, 128, 128, 2, 1, 8, 1, ctypes.byref(out)) == GDN_ERR_SHAPE  # packed: B = 1
     assert f(1, 4096, 16, 128, 128, 4096, 1, 16, 1, ctypes.byref(out)) == GDN_ERR_UNSUPPORTED
+    assert f(1, 2**31 - 1, 64, 128, 128, 1, 0, 1, 1, ctypes.byref(out)) == GDN_ERR_UNSUPPORTED
     sp = lib.gdn_prefill_seqpar
     ws = ctypes.c_void_p(1 << 20)            # never dereferenced: rejected before launch
     a = [P] * 5 + [None, None, P, None]
