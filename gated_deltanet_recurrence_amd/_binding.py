@@ -10,8 +10,10 @@ no fallback path.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
+import threading
 from typing import Optional
 
 import torch
@@ -82,11 +84,38 @@ def _check(status: int):
         raise GDNError(f"libgdn status {status}: {msg}")
 
 
+# The device a call runs on (that of its first tensor): every tensor of the
+# call must live there, and it is the current device while the library runs
+# (its per-device launch settings are looked up for the current device).
+_ctx = threading.local()
+
+
+@contextlib.contextmanager
+def _on(device):
+    if device.type != "cuda":                 # the tensor checks reject the call
+        yield
+        return
+    prev = getattr(_ctx, "device", None)
+    _ctx.device = device
+    try:
+        with torch.cuda.device(device):
+            yield
+    finally:
+        _ctx.device = prev
+
+
+def _same_device(t: torch.Tensor, name: str):
+    want = getattr(_ctx, "device", None)
+    if want is not None and t.device != want:
+        raise GDNError(f"{name} is on {t.device}, the call's other tensors on {want}")
+
+
 def _dev(t: Optional[torch.Tensor], name: str, dtype=None, shape=None):
     if t is None:
         return None
     if not t.is_cuda:
         raise GDNError(f"{name} must be a GPU tensor")
+    _same_device(t, name)
     if not t.is_contiguous():
         raise GDNError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
@@ -134,28 +163,30 @@ def _prefill(entry, q, k, v, g, beta, initial_state=None, final_state=None, o=No
         o = torch.empty((B, T, H, dv), dtype=dt, device=q.device)
     if scale is None:
         scale = dk ** -0.5
-    args = [
-        _dev(q, "q", dt), _dev(k, "k", dt, q.shape), _dev(v, "v", dt, (B, T, H, dv)),
-        _dev(g, "g", torch.float32,
-             (B, T, H, dk) if entry == "gdn_prefill_channel_gated" else (B, T, H)),
-        _dev(beta, "beta", torch.float32, (B, T, H)),
-        _dev(initial_state, "initial_state", torch.float32, (N, H, dv, dk)),
-        _dev(final_state, "final_state", torch.float32, (N, H, dv, dk)),
-        _dev(o, "o", dt, (B, T, H, dv)),
-        _dev(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,)),
-    ]
-    tail = [float(scale), _dtype_code(q)]
-    if entry in ("gdn_prefill", "gdn_prefill_channel_gated"):
-        if isinstance(workspace, str):
-            if workspace != "auto":
-                raise GDNError(f"workspace must be None, 'auto' or a tensor, got {workspace!r}")
-            size = (gdn_prefill_workspace_size if entry == "gdn_prefill"
-                    else gdn_prefill_channel_workspace_size)
-            nbytes = size(B, T, H, dk, dv, N, cu_seqlens is not None, _dtype_code(q))
-            workspace = (torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-                         if nbytes else None)
-        tail += list(_ws(workspace))
-    _check(getattr(load(), entry)(*args, B, T, H, Hk, dk, dv, N, *tail, _stream(q.device)))
+    with _on(q.device):
+        args = [
+            _dev(q, "q", dt), _dev(k, "k", dt, q.shape), _dev(v, "v", dt, (B, T, H, dv)),
+            _dev(g, "g", torch.float32,
+                 (B, T, H, dk) if entry == "gdn_prefill_channel_gated" else (B, T, H)),
+            _dev(beta, "beta", torch.float32, (B, T, H)),
+            _dev(initial_state, "initial_state", torch.float32, (N, H, dv, dk)),
+            _dev(final_state, "final_state", torch.float32, (N, H, dv, dk)),
+            _dev(o, "o", dt, (B, T, H, dv)),
+            _dev(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,)),
+        ]
+        tail = [float(scale), _dtype_code(q)]
+        if entry in ("gdn_prefill", "gdn_prefill_channel_gated"):
+            if isinstance(workspace, str):
+                if workspace != "auto":
+                    raise GDNError("workspace must be None, 'auto' or a tensor, "
+                                   f"got {workspace!r}")
+                size = (gdn_prefill_workspace_size if entry == "gdn_prefill"
+                        else gdn_prefill_channel_workspace_size)
+                nbytes = size(B, T, H, dk, dv, N, cu_seqlens is not None, _dtype_code(q))
+                workspace = (torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+                             if nbytes else None)
+            tail += list(_ws(workspace))
+        _check(getattr(load(), entry)(*args, B, T, H, Hk, dk, dv, N, *tail, _stream(q.device)))
     return o, final_state
 
 
@@ -184,24 +215,27 @@ def _ws(workspace):
         return None, 0
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise GDNError("workspace must be a contiguous GPU tensor")
+    _same_device(workspace, "workspace")
     return workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
 
 def gdn_prefill_prepare(q, k, g, beta, workspace, cu_seqlens=None, d_v=None):
-    """First pass of the workspace path (see include/gdn.h): T diag(beta e^gamma),
-    T diag(beta) and the decayed intra-chunk attention of every chunk into
-    `workspace`. The value heads H are those of g and beta."""
+    """First pass of the workspace path (see include/gdn.h): T diag(beta) of
+    every 64-token chunk and head into `workspace` (T the inverse of the
+    chunk's unit-lower-triangular key Gram system). The value heads H are
+    those of g and beta."""
     B, T, Hk, dk = k.shape
     H = g.shape[2]
     dv = dk if d_v is None else d_v
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
     if q.shape != k.shape or q.dtype != k.dtype:
         raise GDNError("q must match k in shape and dtype")
-    _check(load().gdn_prefill_prepare(
-        _dev(q, "q"), _dev(k, "k"), _dev(g, "g", torch.float32, (B, T, H)),
-        _dev(beta, "beta", torch.float32, (B, T, H)),
-        _dev(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,)),
-        B, T, H, Hk, dk, dv, N, _dtype_code(k), *_ws(workspace), _stream(k.device)))
+    with _on(k.device):
+        _check(load().gdn_prefill_prepare(
+            _dev(q, "q"), _dev(k, "k"), _dev(g, "g", torch.float32, (B, T, H)),
+            _dev(beta, "beta", torch.float32, (B, T, H)),
+            _dev(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,)),
+            B, T, H, Hk, dk, dv, N, _dtype_code(k), *_ws(workspace), _stream(k.device)))
 
 
 def gdn_prefill_apply(q, k, v, g, workspace, initial_state=None, final_state=None, o=None,
@@ -216,14 +250,15 @@ def gdn_prefill_apply(q, k, v, g, workspace, initial_state=None, final_state=Non
         o = torch.empty((B, T, H, dv), dtype=dt, device=q.device)
     if scale is None:
         scale = dk ** -0.5
-    _check(load().gdn_prefill_apply(
-        _dev(q, "q", dt), _dev(k, "k", dt, q.shape), _dev(v, "v", dt, (B, T, H, dv)),
-        _dev(g, "g", torch.float32, (B, T, H)),
-        _dev(initial_state, "initial_state", torch.float32, (N, H, dv, dk)),
-        _dev(final_state, "final_state", torch.float32, (N, H, dv, dk)),
-        _dev(o, "o", dt, (B, T, H, dv)), _dev(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,)),
-        B, T, H, Hk, dk, dv, N, float(scale), _dtype_code(q), *_ws(workspace),
-        _stream(q.device)))
+    with _on(q.device):
+        _check(load().gdn_prefill_apply(
+            _dev(q, "q", dt), _dev(k, "k", dt, q.shape), _dev(v, "v", dt, (B, T, H, dv)),
+            _dev(g, "g", torch.float32, (B, T, H)),
+            _dev(initial_state, "initial_state", torch.float32, (N, H, dv, dk)),
+            _dev(final_state, "final_state", torch.float32, (N, H, dv, dk)),
+            _dev(o, "o", dt, (B, T, H, dv)), _dev(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,)),
+            B, T, H, Hk, dk, dv, N, float(scale), _dtype_code(q), *_ws(workspace),
+            _stream(q.device)))
     return o, final_state
 
 
@@ -262,15 +297,16 @@ def gdn_prefill_seqpar(q, k, v, g, beta, segments, initial_state=None, final_sta
             gdn_prefill_seqpar_workspace_size(B, T, H, dk, dv, N, cu_seqlens is not None,
                                               segments, dt),
             dtype=torch.uint8, device=q.device)
-    _check(load().gdn_prefill_seqpar(
-        _dev(q, "q", dt), _dev(k, "k", dt, q.shape), _dev(v, "v", dt, (B, T, H, dv)),
-        _dev(g, "g", torch.float32, (B, T, H)), _dev(beta, "beta", torch.float32, (B, T, H)),
-        _dev(initial_state, "initial_state", torch.float32, (N, H, dv, dk)),
-        _dev(final_state, "final_state", torch.float32, (N, H, dv, dk)),
-        _dev(o, "o", dt, (B, T, H, dv)),
-        _dev(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,)),
-        B, T, H, Hk, dk, dv, N, int(segments), float(scale), _dtype_code(q), *_ws(workspace),
-        _stream(q.device)))
+    with _on(q.device):
+        _check(load().gdn_prefill_seqpar(
+            _dev(q, "q", dt), _dev(k, "k", dt, q.shape), _dev(v, "v", dt, (B, T, H, dv)),
+            _dev(g, "g", torch.float32, (B, T, H)), _dev(beta, "beta", torch.float32, (B, T, H)),
+            _dev(initial_state, "initial_state", torch.float32, (N, H, dv, dk)),
+            _dev(final_state, "final_state", torch.float32, (N, H, dv, dk)),
+            _dev(o, "o", dt, (B, T, H, dv)),
+            _dev(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,)),
+            B, T, H, Hk, dk, dv, N, int(segments), float(scale), _dtype_code(q), *_ws(workspace),
+            _stream(q.device)))
     return o, final_state
 
 
@@ -304,12 +340,13 @@ def _decode(entry, q, k, v, g, beta, state, o, scale):
         o = torch.empty((B, H, dv), dtype=dt, device=q.device)
     if scale is None:
         scale = dk ** -0.5
-    _check(getattr(load(), entry)(
-        _dev(q, "q", dt), _dev(k, "k", dt, q.shape), _dev(v, "v", dt, (B, H, dv)),
-        _dev(g, "g", torch.float32, (B, H, dk) if entry.endswith("channel_gated") else (B, H)),
-        _dev(beta, "beta", torch.float32, (B, H)),
-        _dev(state, "state", torch.float32, (B, H, dv, dk)), _dev(o, "o", dt, (B, H, dv)),
-        B, H, Hk, dk, dv, float(scale), _dtype_code(q), _stream(q.device)))
+    with _on(q.device):
+        _check(getattr(load(), entry)(
+            _dev(q, "q", dt), _dev(k, "k", dt, q.shape), _dev(v, "v", dt, (B, H, dv)),
+            _dev(g, "g", torch.float32, (B, H, dk) if entry.endswith("channel_gated") else (B, H)),
+            _dev(beta, "beta", torch.float32, (B, H)),
+            _dev(state, "state", torch.float32, (B, H, dv, dk)), _dev(o, "o", dt, (B, H, dv)),
+            B, H, Hk, dk, dv, float(scale), _dtype_code(q), _stream(q.device)))
     return o
 
 
@@ -326,17 +363,18 @@ def gdn_mixer_prologue(q_raw, k_raw, v_raw, conv_w, a, b, A, dt_bias=None, cu_se
                torch.empty((B, T, H), dtype=torch.float32, device=q_raw.device),
                torch.empty((B, T, H), dtype=torch.float32, device=q_raw.device))
     q, k, v, g, beta = out
-    _check(load().gdn_mixer_prologue(
-        _dev(q_raw, "q_raw", dt), _dev(k_raw, "k_raw", dt, q_raw.shape),
-        _dev(v_raw, "v_raw", dt, (B, T, H, dv)),
-        _dev(conv_w, "conv_w", dt, (2 * Hk * dk + H * dv, 4)),
-        _dev(a, "a", dt, (B, T, H)), _dev(b, "b", dt, (B, T, H)),
-        _dev(A, "A", torch.float32, (H,)), _dev(dt_bias, "dt_bias", torch.float32, (H,)),
-        _dev(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,)),
-        _dev(q, "q", dt, q_raw.shape), _dev(k, "k", dt, q_raw.shape),
-        _dev(v, "v", dt, (B, T, H, dv)), _dev(g, "g", torch.float32, (B, T, H)),
-        _dev(beta, "beta", torch.float32, (B, T, H)),
-        B, T, H, Hk, dk, dv, N, _dtype_code(q_raw), _stream(q_raw.device)))
+    with _on(q_raw.device):
+        _check(load().gdn_mixer_prologue(
+            _dev(q_raw, "q_raw", dt), _dev(k_raw, "k_raw", dt, q_raw.shape),
+            _dev(v_raw, "v_raw", dt, (B, T, H, dv)),
+            _dev(conv_w, "conv_w", dt, (2 * Hk * dk + H * dv, 4)),
+            _dev(a, "a", dt, (B, T, H)), _dev(b, "b", dt, (B, T, H)),
+            _dev(A, "A", torch.float32, (H,)), _dev(dt_bias, "dt_bias", torch.float32, (H,)),
+            _dev(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,)),
+            _dev(q, "q", dt, q_raw.shape), _dev(k, "k", dt, q_raw.shape),
+            _dev(v, "v", dt, (B, T, H, dv)), _dev(g, "g", torch.float32, (B, T, H)),
+            _dev(beta, "beta", torch.float32, (B, T, H)),
+            B, T, H, Hk, dk, dv, N, _dtype_code(q_raw), _stream(q_raw.device)))
     return q, k, v, g, beta
 
 
@@ -346,10 +384,12 @@ def gdn_mixer_epilogue(y, z, norm_w=None, out=None, eps=1e-6):
     dt = y.dtype
     if out is None:
         out = torch.empty_like(y)
-    _check(load().gdn_mixer_epilogue(
-        _dev(y, "y", dt), _dev(z, "z", dt, y.shape), _dev(norm_w, "norm_w", torch.float32, (dv,)),
-        _dev(out, "out", dt, y.shape), B * T, H, dv, float(eps), _dtype_code(y),
-        _stream(y.device)))
+    with _on(y.device):
+        _check(load().gdn_mixer_epilogue(
+            _dev(y, "y", dt), _dev(z, "z", dt, y.shape),
+            _dev(norm_w, "norm_w", torch.float32, (dv,)),
+            _dev(out, "out", dt, y.shape), B * T, H, dv, float(eps), _dtype_code(y),
+            _stream(y.device)))
     return out
 
 
@@ -366,13 +406,14 @@ def gdn_decode_mixer_step(q_raw, k_raw, v_raw, conv_w, conv_state, a, b, A, z, s
         out = torch.empty((B, H, dv), dtype=dt, device=q_raw.device)
     if scale is None:
         scale = dk ** -0.5
-    _check(load().gdn_decode_mixer_step(
-        _dev(q_raw, "q_raw", dt), _dev(k_raw, "k_raw", dt, q_raw.shape),
-        _dev(v_raw, "v_raw", dt, (B, H, dv)), _dev(conv_w, "conv_w", dt, (C, 4)),
-        _dev(conv_state, "conv_state", dt, (B, 3, C)),
-        _dev(a, "a", dt, (B, H)), _dev(b, "b", dt, (B, H)), _dev(A, "A", torch.float32, (H,)),
-        _dev(dt_bias, "dt_bias", torch.float32, (H,)), _dev(z, "z", dt, (B, H, dv)),
-        _dev(norm_w, "norm_w", torch.float32, (dv,)), float(eps),
-        _dev(state, "state", torch.float32, (B, H, dv, dk)), _dev(out, "out", dt, (B, H, dv)),
-        B, H, Hk, dk, dv, float(scale), _dtype_code(q_raw), _stream(q_raw.device)))
+    with _on(q_raw.device):
+        _check(load().gdn_decode_mixer_step(
+            _dev(q_raw, "q_raw", dt), _dev(k_raw, "k_raw", dt, q_raw.shape),
+            _dev(v_raw, "v_raw", dt, (B, H, dv)), _dev(conv_w, "conv_w", dt, (C, 4)),
+            _dev(conv_state, "conv_state", dt, (B, 3, C)),
+            _dev(a, "a", dt, (B, H)), _dev(b, "b", dt, (B, H)), _dev(A, "A", torch.float32, (H,)),
+            _dev(dt_bias, "dt_bias", torch.float32, (H,)), _dev(z, "z", dt, (B, H, dv)),
+            _dev(norm_w, "norm_w", torch.float32, (dv,)), float(eps),
+            _dev(state, "state", torch.float32, (B, H, dv, dk)), _dev(out, "out", dt, (B, H, dv)),
+            B, H, Hk, dk, dv, float(scale), _dtype_code(q_raw), _stream(q_raw.device)))
     return out

@@ -264,3 +264,29 @@ def test_noalloc_validation(lib):
     # beyond the static scratch (32 MiB = 5461 items of 6 KiB): rejected before launch
     assert call(B=4, T=8192, H=16, N=4) == GDN_ERR_SCRATCH
     assert call(B=1, T=64 * 5461, H=1) == GDN_ERR_SCRATCH
+
+
+def test_binding_rejects_host_tensors(lib):
+    import torch
+    from gated_deltanet_recurrence_amd import _binding
+    q = torch.zeros(1, 4, 1, 128, dtype=torch.bfloat16)
+    g = torch.zeros(1, 4, 1, dtype=torch.float32)
+    with pytest.raises(_binding.GDNError, match="GPU tensor"):
+        _binding.gdn_prefill(q, q, q, g, g, workspace=None)
+    with pytest.raises(_binding.GDNError, match="GPU tensor"):
+        _binding.gdn_decode_step(q[:, 0], q[:, 0], q[:, 0], g[:, 0], g[:, 0],
+                                 torch.zeros(1, 1, 128, 128))
+
+
+def test_binding_requires_one_device_per_call(lib):
+    # inside a call every tensor must sit on the call's device (checked before
+    # the library runs; the meta device stands in for a second GPU)
+    import torch
+    from gated_deltanet_recurrence_amd import _binding
+    _binding._ctx.device = torch.device("cuda", 0)
+    try:
+        with pytest.raises(_binding.GDNError, match="is on meta"):
+            _binding._same_device(torch.empty(0, device="meta"), "v")
+    finally:
+        _binding._ctx.device = None
+    _binding._same_device(torch.empty(0, device="meta"), "v")   # no call running: no check
