@@ -30,7 +30,7 @@
 
 namespace gdn {
 
-constexpr int PRO_TT = 16;          // tokens per lane group in the prologue
+constexpr int PRO_TT = 8;          // tokens per lane group in the prologue
 
 // Eight consecutive elements of a storage type as loaded (16 B of bf16, 32 B
 // of fp32), converted to fp32 only where they are used, so that a lane can
@@ -98,7 +98,12 @@ prologue_conv_kernel(const TIO *__restrict__ x_q, const TIO *__restrict__ x_k,
     if (h >= Ht0) return;                         // whole lane groups
     const int Ht = Ht0;                           // heads of this tensor
     const int lr = threadIdx.x % G;
-    const long t0 = (long)blockIdx.x * PRO_TT;
+    // tiles dealt so that a tile and the one before it run on the same XCD
+    // (workgroups go to the 8 XCDs in turn): the previous tile's last three
+    // tokens, this tile's convolution history, are then read from that XCD's L2
+    const long nb = (long)gridDim.x, full = nb / 8 * 8, bx = (long)blockIdx.x;
+    const long tile = bx < full ? (bx % 8) * (nb / 8) + bx / 8 : bx;
+    const long t0 = tile * PRO_TT;
     const long t1 = t0 + PRO_TT < total ? t0 + PRO_TT : total;
 
     const TIO *x = which == 0 ? x_q : (which == 1 ? x_k : x_v);
