@@ -299,7 +299,8 @@ def make_channel_gated(seed: int = 7, B: int = 2, T: int = 300, H: int = 4, d: i
 
 def make_long_memory(seed: int = 200, B: int = 2, T: int = 1024, H: int = 2, d: int = 128,
                      gate: str = "zero", with_state: bool = False, dtype: str = "bf16",
-                     per_channel: bool = False, lengths: Optional[list] = None) -> GDNCase:
+                     per_channel: bool = False, lengths: Optional[list] = None,
+                     key_norm: Optional[tuple] = None) -> GDNCase:
     """Long-memory regime: what is written survives many chunks.
 
     ``gate="zero"``: g = 0 (alpha = 1), the delta rule without forgetting;
@@ -307,7 +308,9 @@ def make_long_memory(seed: int = 200, B: int = 2, T: int = 1024, H: int = 2, d: 
     when ``per_channel``, g then [B, T, H, d]). q,k unit Gaussian, v ~ N(0,1),
     beta = sigmoid(N(0,1)), initial states N(0, 0.02) when ``with_state``.
     ``lengths``: packed sequences of these lengths instead (B = 1, T their
-    sum, cu_seqlens set, one initial state per sequence)."""
+    sum, cu_seqlens set, one initial state per sequence). ``key_norm=(lo,
+    hi)``: each key scaled to a norm ~ U(lo, hi) instead of 1 (drawn after
+    everything else, so the other tensors are those of the unit-key case)."""
     gen = _gen(seed)
     td = _TORCH_DTYPE[dtype]
     cu, N = None, B
@@ -316,7 +319,7 @@ def make_long_memory(seed: int = 200, B: int = 2, T: int = 1024, H: int = 2, d: 
         cu = torch.zeros(N + 1, dtype=torch.int32)
         cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
     q = unit_gaussian(gen, (B, T, H, d)).to(td)
-    k = unit_gaussian(gen, (B, T, H, d)).to(td)
+    k32 = unit_gaussian(gen, (B, T, H, d))
     v = _normal(gen, (B, T, H, d)).to(td)
     gshape = (B, T, H, d) if per_channel else (B, T, H)
     if gate == "zero":
@@ -327,6 +330,9 @@ def make_long_memory(seed: int = 200, B: int = 2, T: int = 1024, H: int = 2, d: 
         raise ValueError(f"unknown gate recipe {gate!r}")
     beta = _sigmoid_gaussian(gen, (B, T, H))
     s0 = _normal(gen, (N, H, d, d), std=0.02) if with_state else None
+    if key_norm is not None:
+        k32 = k32 * _uniform(gen, (B, T, H, 1), float(key_norm[0]), float(key_norm[1]))
+    k = k32.to(td)
     return GDNCase("long_memory", q, k, v, g.contiguous(), beta, s0, cu, 1.0 / math.sqrt(d),
                    dtype, meta={"gate": gate, "per_channel": per_channel, "lengths": lengths})
 
