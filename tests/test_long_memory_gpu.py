@@ -184,3 +184,44 @@ def test_full_overwrite_recalls_the_last_write(path):
     report(f"full overwrite {path}", o=eo, state=es, recall=float(rel))
     assert rel <= TOL_BF16
     assert eo <= TOL_BF16 and es <= TOL_BF16 and eo.row <= TOL_BF16
+
+
+def _random_plan(trial):
+    """Seeded packed batch: 1..40 sequences, a fifth empty, a tenth of 1..3
+    tokens, the rest 4..1500 tokens; 1..9 segments."""
+    rng = np.random.default_rng(5000 + trial)
+    n = int(rng.integers(1, 41))
+    kind = rng.random(n)
+    lengths = [0 if u < 0.2 else int(rng.integers(1, 4)) if u < 0.3 else int(rng.integers(4, 1501))
+               for u in kind]
+    return lengths, int(rng.integers(1, 10))
+
+
+@pytest.mark.parametrize("path", ["seqpar", "two_pass"])
+@pytest.mark.parametrize("trial", range(8))
+def test_random_packed_batches(trial, path):
+    """The device-side plan of the sequence-parallel path (segment length from
+    the longest sequence, each sequence cut into segments of that length,
+    job tables in longest-first order, the maps of middle segments composed
+    in order) over seeded random packed batches and segment counts, with
+    near-one gates so that every carried state and map reaches the outputs.
+    Every sequence and final state against the token recurrence; the same
+    batches through the two-pass path (longest-first dealing of packed
+    sequences in the chain pass)."""
+    lengths, segments = _random_plan(trial)
+    c = inputs.make_long_memory(seed=500 + trial, H=1, gate="near_one", with_state=True,
+                                lengths=lengths)
+    fin = _fin(c)
+    args = (dev(c.q), dev(c.k), dev(c.v), dev(c.g), dev(c.beta))
+    if path == "seqpar":
+        o, _ = gdn.gdn_prefill_seqpar(*args, segments, dev(c.s0), fin,
+                                      cu_seqlens=dev(c.cu_seqlens), scale=c.scale)
+    else:
+        o, _ = gdn.gdn_prefill(*args, dev(c.s0), fin, cu_seqlens=dev(c.cu_seqlens), scale=c.scale)
+    torch.cuda.synchronize()
+    o_ref, s_ref = _ref(c)
+    cu = [int(x) for x in c.cu_seqlens.tolist()]
+    eo, es = o_err_packed(o, o_ref, cu), s_err(fin, s_ref)
+    report(f"random packed batch {trial} {path}: {len(lengths)} sequences, {sum(lengths)} tokens"
+           + (f", {segments} segments" if path == "seqpar" else ""), o=eo, state=es)
+    assert eo <= TOL_BF16 and es <= TOL_BF16 and eo.row <= TOL_BF16
