@@ -415,7 +415,9 @@ def bench_varlen(gdn, inputs, steps, warmup):
 
     def step(i):
         gdn.gdn_prefill(q, k, v, g, beta, s0, fin, o, cu_seqlens=cu, scale=c.scale, workspace=ws)
-    ms = event_time(step, max(5, steps // 4), 3)
+    # a longer warm-up than the other workloads: the first of these 1.2 ms
+    # calls after the buffers are allocated run ~10% slower for ~20 calls
+    ms = event_time(step, max(5, steps // 4), 25)
     total = int(c.cu_seqlens[-1])
     res = dict(workload="packed prefill H=32 d=128 bf16, 8 sequences log-uniform in [512, 65536], "
                         "non-zero initial states",
@@ -432,7 +434,7 @@ def bench_varlen(gdn, inputs, steps, warmup):
         ms = event_time(lambda i: gdn.gdn_prefill_seqpar(q, k, v, g, beta, P, s0, fin, o,
                                                          cu_seqlens=cu, scale=c.scale,
                                                          workspace=wsp),
-                        max(5, steps // 4), 3)
+                        max(5, steps // 4), 10)
         res[f"seqpar_{P}_ms"] = round(ms, 4)
         res[f"seqpar_{P}_tokens_per_s"] = round(total / (ms * 1e-3), 1)
         del wsp
