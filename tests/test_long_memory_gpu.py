@@ -225,3 +225,27 @@ def test_random_packed_batches(trial, path):
     report(f"random packed batch {trial} {path}: {len(lengths)} sequences, {sum(lengths)} tokens"
            + (f", {segments} segments" if path == "seqpar" else ""), o=eo, state=es)
     assert eo <= TOL_BF16 and es <= TOL_BF16 and eo.row <= TOL_BF16
+
+
+@pytest.mark.parametrize("path", ["two_pass", "one_pass", "seqpar_8"])
+@pytest.mark.parametrize("gate", GATES)
+def test_long_memory_32k_tokens(gate, path):
+    """One sequence of 32,768 tokens (512 chunks) with no or almost no
+    forgetting: the carried fp32 state and its bf16 copy go through 512
+    chunk updates, so any rounding that accumulates along the chain shows
+    here first. One head, with an initial state."""
+    c = inputs.make_long_memory(seed=390 + GATES.index(gate), B=1, T=32768, H=1, gate=gate,
+                                with_state=True)
+    fin = _fin(c)
+    args = (dev(c.q), dev(c.k), dev(c.v), dev(c.g), dev(c.beta))
+    if path == "seqpar_8":
+        o, _ = gdn.gdn_prefill_seqpar(*args, 8, dev(c.s0), fin, scale=c.scale)
+    else:
+        o, _ = gdn.gdn_prefill(*args, dev(c.s0), fin, scale=c.scale, workspace=WS[path])
+    torch.cuda.synchronize()
+    o_ref, s_ref = _ref(c)
+    eo, es = o_err(o, o_ref), s_err(fin, s_ref)
+    # the last 4096 tokens alone: the error where the most chunks lie behind
+    el = o_err(o[:, -4096:], o_ref[:, -4096:])
+    report(f"long memory 32k gate={gate} {path}", o=eo, state=es, o_last_4k=el)
+    assert eo <= TOL_BF16 and es <= TOL_BF16 and eo.row <= TOL_BF16
