@@ -399,6 +399,8 @@ def bench_mixer(gdn, inputs, steps, warmup):
             torch.empty((B, T, H), dtype=torch.float32, device="cuda"))
     y = torch.empty_like(raw[2])
     out = torch.empty_like(y)
+    # the norm weight as a model passes it (the workload's weight is ones)
+    norm_w = torch.ones(D, dtype=torch.float32, device="cuda")
 
     def pro(i):
         gdn.gdn_mixer_prologue(*raw, A, out=outs)
@@ -410,7 +412,7 @@ def bench_mixer(gdn, inputs, steps, warmup):
         gdn.gdn_prefill(*outs, o=y, scale=c.scale, workspace=ws)
 
     def epi(i):
-        gdn.gdn_mixer_epilogue(y, z, out=out, eps=c.eps)
+        gdn.gdn_mixer_epilogue(y, z, norm_w=norm_w, out=out, eps=c.eps)
 
     def full(i):
         pro(i); core(i); epi(i)

@@ -212,14 +212,18 @@ epilogue_kernel(const TIO *y, const TIO *__restrict__ z, const float *__restrict
     constexpr int GPB = 256 / G;
     const int lr = threadIdx.x % G;
     const int c = 8 * lr;
-    float wv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) wv[e] = w ? w[c + e] : 1.0f;
     for (long r = (long)blockIdx.x * GPB + threadIdx.x / G; r < rows;
          r += (long)gridDim.x * GPB) {
-        float yv[8], zv[8], ov[8];
+        float yv[8], zv[8], ov[8], wv[8];
         load8(y + (size_t)r * D + c, yv);
         load8(z + (size_t)r * D + c, zv);
+        // the weights after the row's loads, so that their latencies overlap
+        // (a workgroup normally takes one row per lane group)
+        if (w) load8(w + c, wv);
+        else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wv[e] = 1.0f;
+        }
         float ss = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss += yv[e] * yv[e];

@@ -454,15 +454,17 @@ def test_decode_grouped_heads(dtype):
 
 def test_mixer_grouped_heads():
     """Prologue -> prefill -> epilogue with H_k = 2 query/key heads and H = 4
-    value heads: conv channels 2 H_k d + H d, gates per value head."""
+    value heads: conv channels 2 H_k d + H d, gates per value head; the
+    gated RMSNorm with a norm weight (seeded, U(0.5, 1.5) per channel)."""
     c = inputs.make_mixer(seed=66, B=2, T=150, H=4, Hk=2, d=128)
+    nw = 0.5 + torch.rand(128, generator=torch.Generator().manual_seed(67))
     q, k, v, g, beta = gdn.gdn_mixer_prologue(dev(c.q_raw), dev(c.k_raw), dev(c.v_raw),
                                               dev(c.conv_w), dev(c.a), dev(c.b), dev(c.A))
     y, _ = gdn.gdn_prefill(q, k, v, g, beta, scale=c.scale)
-    out = gdn.gdn_mixer_epilogue(y, dev(c.z), eps=c.eps)
+    out = gdn.gdn_mixer_epilogue(y, dev(c.z), norm_w=dev(nw), eps=c.eps)
     torch.cuda.synchronize()
     ref, mid = oracle.mixer(c.q_raw, c.k_raw, c.v_raw, c.z, c.a, c.b, c.conv_w, c.A,
-                            scale=c.scale, eps=c.eps, return_intermediates=True)
+                            norm_w=nw, scale=c.scale, eps=c.eps, return_intermediates=True)
     e_out, e_y = o_err(out.cpu(), ref), o_err(y.cpu(), mid["y"])
     e_q, e_k, e_v = o_err(q.cpu(), mid["q"]), o_err(k.cpu(), mid["k"]), o_err(v.cpu(), mid["v"])
     e_g = float(np.abs(host64(g.cpu()) - mid["g"]).max() / np.abs(mid["g"]).max())
