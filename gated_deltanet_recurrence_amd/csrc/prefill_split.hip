@@ -1126,9 +1126,13 @@ struct WaveSolver {
 // wave per workgroup and (chunk, head) item at a time (items blockIdx.x,
 // + gridDim.x, ...), each wave with its own SV_BYTES of LDS, so that up to
 // ten items are in flight per compute unit and none waits at a workgroup
-// barrier. Writes T_u = T diag(beta) of the item into the workspace.
+// barrier. Writes T_u = T diag(beta) of the item into the workspace. With
+// PREFETCH each item's keys are requested while the item before it is
+// solved (64 more registers: eight waves per CU instead of ten), which pays
+// when every wave has several items to walk.
 // ---------------------------------------------------------------------------
 constexpr int SOLVE_NT = 64;
+template <bool PREFETCH>
 __global__ void __launch_bounds__(SOLVE_NT)
 chunk_solve_kernel(const bf16 *__restrict__ k, const float *__restrict__ g,
                    const float *__restrict__ beta, const int32_t *__restrict__ cu_seqlens,
@@ -1139,20 +1143,63 @@ chunk_solve_kernel(const bf16 *__restrict__ k, const float *__restrict__ g,
     const int lane = (int)threadIdx.x;
     const int nitems = nslots * H;
     const int tstride = Hk * DK;
-    for (int item = (int)blockIdx.x; item < nitems; item += (int)gridDim.x) {
-        const PrepItem it = prep_locate(cu_seqlens, item, nitems, T, H, N);
-        if (it.nvalid == 0) continue;          // uniform
+    const int stride = (int)gridDim.x;
+    auto fetch_item = [&](const PrepItem &it, bf16x8 (&kr)[4][4], float &gv, float &bv) {
         const size_t tok0 = (size_t)it.row0;
-        bf16x8 kr[4][4];
-        float gv, bv;
         WaveSolver::fetch(k + tok0 * tstride + (size_t)(it.h / (H / Hk)) * DK, tstride,
                           g + tok0 * H + it.h, beta + tok0 * H + it.h, H, it.nvalid, lane, kr,
                           gv, bv);
+    };
+    auto solve_item = [&](const PrepItem &it, const bf16x8 (&kr)[4][4], float gv, float bv) {
         sol.phase1(kr, gv, bv, lane);
         sol.phase2(lane);
         bf16 *dst = ws + ((size_t)it.h * nslots + it.slot) * ITEM_ELEMS;
         sol.emit(lane, [&](int e, bf16x8 p) { *reinterpret_cast<bf16x8 *>(dst + 8 * e) = p; });
         wave_lds_order();                      // the blocks read before the next item writes them
+    };
+    if constexpr (!PREFETCH) {
+        for (int item = (int)blockIdx.x; item < nitems; item += stride) {
+            const PrepItem it = prep_locate(cu_seqlens, item, nitems, T, H, N);
+            if (it.nvalid == 0) continue;      // uniform
+            bf16x8 kr[4][4];
+            float gv, bv;
+            fetch_item(it, kr, gv, bv);
+            solve_item(it, kr, gv, bv);
+        }
+    } else {
+        // the next item with work at or after `from` (unused slots skipped)
+        auto next_item = [&](int from, PrepItem &it) {
+            int item = from;
+            while (item < nitems) {
+                it = prep_locate(cu_seqlens, item, nitems, T, H, N);
+                if (it.nvalid != 0) break;     // uniform
+                item += stride;
+            }
+            return item;
+        };
+        PrepItem it;
+        int item = next_item((int)blockIdx.x, it);
+        if (item >= nitems) return;
+        bf16x8 kr[4][4];
+        float gv, bv;
+        fetch_item(it, kr, gv, bv);
+        while (true) {
+            PrepItem itn;
+            const int nxt = next_item(item + stride, itn);
+            bf16x8 krn[4][4];
+            float gvn = 0.f, bvn = 0.f;
+            if (nxt < nitems) fetch_item(itn, krn, gvn, bvn);
+            solve_item(it, kr, gv, bv);
+            if (nxt >= nitems) break;
+            item = nxt;
+            it = itn;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) kr[i][j] = krn[i][j];
+            gv = gvn;
+            bv = bvn;
+        }
     }
 }
 
@@ -1990,8 +2037,10 @@ hipError_t launch_prefill_prepare(const void *q, const void *k, const float *g, 
     const long nslots = tokens / C + N + 1;
     if (tokens == 0) return hipSuccess;        // no chunk: nothing to prepare
     const long nitems = nslots * H;
-    static std::atomic<long> fill_scalar[MAX_DEVICES], fill_channel[MAX_DEVICES];
-    static std::atomic<int> lds_scalar[MAX_DEVICES], lds_channel[MAX_DEVICES];
+    static std::atomic<long> fill_scalar[MAX_DEVICES], fill_prefetch[MAX_DEVICES];
+    static std::atomic<long> fill_channel[MAX_DEVICES];
+    static std::atomic<int> lds_scalar[MAX_DEVICES], lds_prefetch[MAX_DEVICES];
+    static std::atomic<int> lds_channel[MAX_DEVICES];
     long fill = 0;
     if (per_channel) {
         const hipError_t attr = raise_lds_limit((const void *)chunk_prep_channel_kernel,
@@ -2006,13 +2055,27 @@ hipError_t launch_prefill_prepare(const void *q, const void *k, const float *g, 
                            (int)nslots);
         return hipGetLastError();
     }
-    const hipError_t attr = raise_lds_limit((const void *)chunk_solve_kernel, SV_BYTES, lds_scalar);
-    if (attr != hipSuccess) return attr;
-    hipError_t e = prep_fill((const void *)chunk_solve_kernel, SOLVE_NT, SV_BYTES, fill_scalar, fill);
+    // more than two items per wave of the plain kernel's grid: the kernel that
+    // fetches each item's keys during the previous item's solve
+    const void *plain = (const void *)chunk_solve_kernel<false>;
+    const void *pref = (const void *)chunk_solve_kernel<true>;
+    hipError_t e = raise_lds_limit(plain, SV_BYTES, lds_scalar);
+    if (e == hipSuccess) e = raise_lds_limit(pref, SV_BYTES, lds_prefetch);
     if (e != hipSuccess) return e;
+    e = prep_fill(plain, SOLVE_NT, SV_BYTES, fill_scalar, fill);
+    if (e != hipSuccess) return e;
+    const bool prefetch = nitems > 2 * fill;
+    if (prefetch) {
+        e = prep_fill(pref, SOLVE_NT, SV_BYTES, fill_prefetch, fill);
+        if (e != hipSuccess) return e;
+    }
     dim3 grid((unsigned)(nitems < fill ? nitems : fill)), block(SOLVE_NT);
-    hipLaunchKernelGGL(chunk_solve_kernel, grid, block, SV_BYTES, stream, (const bf16 *)k, g,
-                       beta, cu, (bf16 *)ws, T, H, Hk, N, (int)nslots);
+    if (prefetch)
+        hipLaunchKernelGGL(chunk_solve_kernel<true>, grid, block, SV_BYTES, stream,
+                           (const bf16 *)k, g, beta, cu, (bf16 *)ws, T, H, Hk, N, (int)nslots);
+    else
+        hipLaunchKernelGGL(chunk_solve_kernel<false>, grid, block, SV_BYTES, stream,
+                           (const bf16 *)k, g, beta, cu, (bf16 *)ws, T, H, Hk, N, (int)nslots);
     return hipGetLastError();
 }
 
