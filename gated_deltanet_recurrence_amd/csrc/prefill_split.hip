@@ -115,6 +115,8 @@ constexpr int SZ_PH = 32 * LD_H * 2;           // 2560: P rows 0-31
 constexpr int SZ_P = SZ_PH + 32 * LD_L * 2;    // 7680: P rows 0-31, then 32-63
 constexpr int SZ_S = DVT * LD_R * 2;           // 9216: bf16 S [32][144]
 constexpr int SZ_DT = DVT * LD_L * 2;          // 5120: Delta^T [32][80]
+constexpr int SZ_PB = 6 * 64 * 16;             // 6144: P^T of a chunk (scalar gate) as six
+                                               // B-operand registers, 1 KiB each, lane-linear
 constexpr int OFF_BUF = 0;                     // two of each from here on
 // In-chain solve (scalar gates, no workspace): each of the two solver waves
 // keeps one chunk's 16 x 16 blocks (I, J), J <= I, of A and then T, fp32
@@ -126,12 +128,14 @@ constexpr int SV_BYTES = (10 * SV_BLK + 3 * 256 + 2 * C) * 4;   // 16384: + D0^T
 constexpr int SV_WAVE0 = 6;                    // solver waves SV_WAVE0, + 1
 constexpr int SV_LOAD0 = 4;                    // loading waves SV_LOAD0, + 1
 constexpr int SV_PRIO = 1;                     // solver waves' issue priority
-// The copies passed between waves follow the staging buffers: P copies
-// (per-channel decay only), S, Delta^T, then the solver regions (in-chain
-// solve only).
+// The copies passed between waves follow the staging buffers: P copies (per
+// channel: P from the workspace; scalar gate with the two-pass layout: P^T as
+// formed by the staging waves), S, Delta^T, then the solver regions (in-chain
+// solve only, which has no room for P copies: its output waves form P^T).
 template <bool PERCH, bool FUSED> struct ChainLds {
+    static constexpr bool PST = !PERCH && !FUSED;   // P^T formed by staging waves 6-7
     static constexpr int P = OFF_BUF + 2 * SZ_BUF;
-    static constexpr int S = P + (PERCH ? 2 * SZ_P : 0);
+    static constexpr int S = P + (PERCH ? 2 * SZ_P : PST ? 2 * SZ_PB : 0);
     static constexpr int DT = S + 2 * SZ_S;
     static constexpr int SV = DT + 2 * SZ_DT;
     static constexpr int BYTES = SV + (FUSED ? 2 * SV_BYTES : 0);
@@ -156,6 +160,14 @@ __device__ __forceinline__ int swz(int lane) { return ((lane & 15) >> 2) << 3; }
 // banks (32 or 64 four-byte banks alike). Element XORs, by d_v row r < 32.
 __device__ __forceinline__ int swS(int r) { return (((r >> 3) & 1) << 3) | (((r >> 4) & 1) << 6); }
 __device__ __forceinline__ int swD(int r) { return ((r >> 3) & 3) << 3; }
+// The staged Q and K tiles (row stride LD_R) swap the two 128-byte halves of
+// rows 16-31 and 48-63 (element XOR by row bit 4). The recurrence reads K for
+// X in the row order 8 (i/4) + 4 (t%2) + i%4 (+32 (t/2)); at 288 bytes per row
+// its rows 16 apart then fall on the same banks, and measured on gfx950 these
+// reads took 1.7x the cycles of conflict-free ones; with the swap they run at
+// the conflict-free rate, and the 16-consecutive-row, transposing and staging
+// accesses keep theirs. Element XOR by row r.
+__device__ __forceinline__ int swK(int r) { return ((r >> 4) & 1) << 6; }
 __device__ __forceinline__ bf16x8 lds8(const bf16 *base, int off) {
     return *reinterpret_cast<const bf16x8 *>(base + off);
 }
@@ -1224,23 +1236,28 @@ chunk_solve_kernel(const bf16 *__restrict__ k, const float *__restrict__ g,
 // Waves 2 and 3 form the output, each for two of the chunk's four 16-token
 // tiles (wave 2 tiles 0 and 3, wave 3 tiles 1 and 2: equal work) over all 32
 // columns of the tile: O^T = (S Q^T) diag(e^gamma) + Delta^T P^T, the second
-// term one chunk later. P^T = upper_incl(K Q^T * Gamma^T) is formed by the
-// same waves from the staged K and Q tiles (its Q operand is the one S Q^T
-// reads) and held in registers until Delta arrives; the rows of S and
-// Delta^T are taken in an order that leaves 8 consecutive d_v of one token
-// in each lane, stored as 16 bytes. With a per-channel decay P comes from the
-// workspace instead (its decay is per channel) and waves 2 and 3 take tokens
-// 0-31 and 32-63. Waves 4-7 stage the next chunk.
+// term one chunk later. P^T = upper_incl(K Q^T * Gamma^T) is formed from the
+// staged K and Q tiles by staging waves 6 and 7 (the two that share SIMDs
+// with waves 2 and 3 and have the least to stage), for the token tiles of
+// wave 2 and wave 3 respectively, and passed to them as their B-operand
+// registers through a P copy; the in-chain solve (no room for the copies)
+// leaves P^T to the output waves, which then take its Q operand from S Q^T's
+// and hold it in registers until Delta arrives. The rows of S and Delta^T are
+// taken in an order that leaves 8 consecutive d_v of one token in each lane,
+// stored as 16 bytes. With a per-channel decay P comes from the workspace
+// instead (its decay is per channel) and waves 2 and 3 take tokens 0-31 and
+// 32-63. Waves 4-7 stage the next chunk.
 //
 // Iteration c (buffers b = c % 2):
 //   waves 0-1  recurrence step of chunk c: reads staging b, writes Delta^T
 //              into copy b and the new bf16 S into copy (c + 1) % 2
-//   waves 2-3  S Q^T and P^T of chunk c (S copy b, staging b); finish chunk
-//              c - 1 (Delta^T copy (c - 1) % 2) and store its output rows
-//   waves 4-5  (per-channel decay) P of chunk c, loaded in iteration c - 2,
-//              into copy b
+//   waves 2-3  S Q^T of chunk c (S copy b, staging b); finish chunk c - 1
+//              (Delta^T and P copies (c - 1) % 2) and store its output rows
 //   waves 4-7  store chunk c + 1 (in registers since iteration c - 2) into
 //              staging (c + 1) % 2, load chunk c + 3 into the registers
+//   waves 6-7  (scalar gate) then P^T of chunk c from staging b into P copy b
+//   waves 4-5  (per-channel decay) P of chunk c, loaded in iteration c - 2,
+//              into copy b
 //   barrier
 // Tokens past the end of a sequence are identity steps (q = k = v = 0,
 // g = 0, and T_u vanishes on them) and their outputs are not stored.
@@ -1268,6 +1285,13 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     auto cpP = [&](int b) { return lds + (L::P + b * SZ_P) / 2; };
     auto cpS = [&](int b) { return lds + (L::S + b * SZ_S) / 2; };
     auto cpDt = [&](int b) { return lds + (L::DT + b * SZ_DT) / 2; };
+    constexpr bool PST = L::PST;
+    // P^T register pb[x][s] of the output wave for token tiles {t, 3 - t}
+    // (x = 0: tile t, x = 1: tile 3 - t; s: key block) in P copy b: one
+    // lane-linear 1 KiB slab each, three per output wave
+    auto cpPB = [&](int b, int t, int x, int s) {
+        return lds + (L::P + b * SZ_PB) / 2 + 512 * (3 * t + (x ? 1 + s : 0));
+    };
 
     const int tid0 = (int)threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
@@ -1434,9 +1458,10 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     };
     auto store = [&](const Pref &rs, int b, auto WT, auto WG, auto WV, int lane) {
         bf16 *buf = lds + (OFF_BUF + b * SZ_BUF) / 2;
-        const int lrow = (qkmat ? B_K : B_Q) / 2 + (qkrow0 + (lane >> 4)) * LD_R + 8 * (lane & 15);
+        // row qkrow0 + lane/16 + 4 r: qkrow0 is 0 or 32, so its bit 4 is bit 2 of r
+        const int lrow = (qkmat ? B_K : B_Q) / 2 + (qkrow0 + (lane >> 4)) * LD_R, lcol = 8 * (lane & 15);
 #pragma unroll
-        for (int r = 0; r < NQK; ++r) *reinterpret_cast<bf16x8 *>(buf + lrow + 4 * r * LD_R) = rs.b[r];
+        for (int r = 0; r < NQK; ++r) *reinterpret_cast<bf16x8 *>(buf + lrow + 4 * r * LD_R + (lcol ^ swK(4 * r))) = rs.b[r];
         if constexpr (decltype(WT)::value) {
 #pragma unroll
             for (int r = 0; r < 3; ++r)
@@ -1471,6 +1496,70 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const std::true_type with_t{}, with_g{}, with_v{}, with_p{};
     const std::false_type no_t{}, no_g{}, no_v{}, no_p{};
 
+    // P^T of the chunk in staging buffer b (scalar gate) for token tiles
+    // TA < TB, from the B operands fq of those tiles' Q rows: P^T tile (key
+    // tile kt, token tile TX) = K_kt Q_TX^T, masked to keys j <= token i and
+    // scaled by e^{gamma_i - gamma_j} <= 1 elementwise (directly on the
+    // diagonal tile, as e^{gamma_i - gamma_r} F_j below it, r the last token
+    // of key tile kt; both factors <= 1). pb[x][s] is the accumulator pair of
+    // key tiles 2 s, 2 s + 1 as bf16: the B operand of Delta^T P^T over keys
+    // 32 s + 4 q + 0..3, 32 s + 16 + 4 q + 0..3, the order the recurrence
+    // writes Delta^T in. The k-steps run outermost so that the independent
+    // accumulator chains interleave.
+    auto ptiles = [&](auto TAc, auto TBc, const bf16x8 (&fq)[2][4], int b, int m, int qq,
+                      bf16x8 (&pb)[2][2]) {
+        constexpr int TA = decltype(TAc)::value, TB = decltype(TBc)::value;
+        constexpr int TX[2] = {TA, TB};
+        constexpr int NKB[2] = {TA / 2 + 1, TB / 2 + 1};
+        const bf16 *sK = stK(b);
+        const float *sG = stSc(b), *sF = stSc(b) + 3 * C;
+        f32x4 pacc[2][4];
+        {
+            bf16x8 fk[TB + 1][4];
+#pragma unroll
+            for (int kt = 0; kt <= TB; ++kt)
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2)
+                    fk[kt][s2] = lds8(sK, (16 * kt + m) * LD_R + ((32 * s2 + 8 * qq) ^ swK(16 * kt)));
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int kt = 0; kt <= TX[x]; ++kt) pacc[x][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+                for (int x = 0; x < 2; ++x)
+#pragma unroll
+                    for (int kt = 0; kt <= TX[x]; ++kt)
+                        pacc[x][kt] = mfma16(fk[kt][s2], fq[x][s2], pacc[x][kt]);
+        }
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            const int ti = 16 * TX[x] + m;
+            const float gs = sG[ti];
+#pragma unroll
+            for (int kt = 0; kt <= TX[x]; ++kt) {
+                if (kt < TX[x]) {
+                    const float ek = __builtin_amdgcn_exp2f(gs - sG[16 * kt + 15]);
+                    const f32x4 fj = *reinterpret_cast<const f32x4 *>(sF + 16 * kt + 4 * qq);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) pacc[x][kt][r] = pacc[x][kt][r] * (ek * fj[r]);
+                } else {
+                    const f32x4 gj = *reinterpret_cast<const f32x4 *>(sG + 16 * kt + 4 * qq);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float e = __builtin_amdgcn_exp2f(gs - gj[r]);
+                        pacc[x][kt][r] = 4 * qq + r <= m ? pacc[x][kt][r] * e : 0.f;
+                    }
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < NKB[x]; ++s)
+                pb[x][s] = acc_pair_bf16(pacc[x][2 * s],
+                                         2 * s + 1 <= TX[x] ? pacc[x][2 * s + 1] : f32x4{0.f, 0.f, 0.f, 0.f});
+        }
+    };
     // Each wave role runs its own loop, unrolled by two from the odd chunk -3
     // so that every buffer and register-set index is a compile-time constant:
     // in iteration c = ch0 + hf, c % 2 = 1 - hf and (c + 1) % 2 = hf. Every
@@ -1527,7 +1616,9 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                     for (int t = 0; t < 4; ++t) {
                         const int row = 32 * (t >> 1) + 8 * (m >> 2) + 4 * (t & 1) + (m & 3);
 #pragma unroll
-                        for (int s2 = 0; s2 < 4; ++s2) fk[t][s2] = lds8(sK, row * LD_R + 32 * s2 + 8 * qq);
+                        // (32 s + 8 q) ^ swK(row) as two per-lane bases with
+                        // immediate offsets
+                        for (int s2 = 0; s2 < 4; ++s2) fk[t][s2] = lds8(sK, row * LD_R + 8 * qq + (s2 < 2 ? swK(row) + 32 * s2 : 32 * s2 - swK(row)));
                     }
                     // V in X's accumulator-pair layout: tokens 32 s + 8 q + 0..7 of
                     // column 16 hv + m
@@ -1564,7 +1655,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                         const int r0 = 32 * s2 + 4 * qq + (m >> 2);
                         // per channel the update's keys are K^ (in the Q tile)
                         const bf16 *sKu = PERCH ? stQ(b) : sK;
-                        fkt[d][s2] = cat4(tr4(sKu, r0 * LD_R + c0), tr4(sKu, (r0 + 16) * LD_R + c0));
+                        fkt[d][s2] = cat4(tr4(sKu, r0 * LD_R + (c0 ^ swK(r0))), tr4(sKu, (r0 + 16) * LD_R + (c0 ^ swK(r0 + 16))));
                     }
                 __builtin_amdgcn_sched_barrier(0);
                 // R = V - diag(e^gamma) X (per channel e^gamma = 1: the decay is
@@ -1652,12 +1743,10 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                 *reinterpret_cast<bf16x8 *>(out + ((size_t)bos + tok) * H * DV + (size_t)h * DV + cbase + 8 * qq) = x;
             }
         };
-        // scalar gate: token tiles TA < TB of every chunk. P^T tile (key tile
-        // kt, token tile TX) = K_kt Q_TX^T (the Q fragments of S Q^T as B
-        // operand), masked to keys j <= token i and scaled by e^{gamma_i -
-        // gamma_j} <= 1 elementwise; the accumulator pair of key tiles 2 s,
-        // 2 s + 1 is the B operand of Delta^T P^T over keys 32 s + 4 q + 0..3,
-        // 32 s + 16 + 4 q + 0..3, the order the recurrence writes Delta^T in.
+        // scalar gate: token tiles TA < TB = 3 - TA of every chunk. P^T comes
+        // from staging wave 6 + TA through P copy (ch - 1) % 2 when the chunk
+        // is finished; with the in-chain solve this wave forms it (ptiles,
+        // its Q operand the one S Q^T reads) and holds it for one iteration.
         auto oloop_scalar = [&](auto TAc, auto TBc) {
             constexpr int TA = decltype(TAc)::value, TB = decltype(TBc)::value;
             constexpr int TX[2] = {TA, TB};
@@ -1674,8 +1763,8 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                 const int lane = tidl & 63, m = lane & 15, qq = lane >> 4;
                 const int r0 = 8 * (m >> 2) + (m & 3);     // d_v row of tile row m, u = 0
                 if (out && ch >= 0 && ch < nchunks) {   // o == NULL: the states only
-                    const bf16 *sSc = cpS(b), *sQ = stQ(b), *sK = stK(b);
-                    const float *sG = stSc(b), *sEg = stSc(b) + C;
+                    const bf16 *sSc = cpS(b), *sQ = stQ(b);
+                    const float *sEg = stSc(b) + C;
                     bf16x8 fs[2][4], fq[2][4];
 #pragma unroll
                     for (int s2 = 0; s2 < 4; ++s2) {
@@ -1684,7 +1773,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                             fs[u][s2] = lds8(sSc, (r0 + 4 * u) * LD_R + ((32 * s2 + 8 * qq) ^ swS(r0 + 4 * u)));
 #pragma unroll
                         for (int x = 0; x < 2; ++x)
-                            fq[x][s2] = lds8(sQ, (16 * TX[x] + m) * LD_R + 32 * s2 + 8 * qq);
+                            fq[x][s2] = lds8(sQ, (16 * TX[x] + m) * LD_R + ((32 * s2 + 8 * qq) ^ swK(16 * TX[x])));
                     }
                     __builtin_amdgcn_sched_barrier(0);
                     // (Q S^T)^T = S Q^T for the wave's tokens (the k-steps outermost, so
@@ -1701,61 +1790,12 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
                             for (int u = 0; u < 2; ++u)
                                 oacc[b][x][u] = mfma16(fs[u][s2], fq[x][s2], oacc[b][x][u]);
-                    // P^T: the K fragments of every key tile first, then the products
-                    // with the k-steps outermost (independent chains interleave)
-                    f32x4 pacc[2][4];
-                    {
-                        bf16x8 fk[TB + 1][4];
-#pragma unroll
-                        for (int kt = 0; kt <= TB; ++kt)
-#pragma unroll
-                            for (int s2 = 0; s2 < 4; ++s2)
-                                fk[kt][s2] = lds8(sK, (16 * kt + m) * LD_R + 32 * s2 + 8 * qq);
-                        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                        for (int x = 0; x < 2; ++x)
-#pragma unroll
-                            for (int kt = 0; kt <= TX[x]; ++kt) pacc[x][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int s2 = 0; s2 < 4; ++s2)
-#pragma unroll
-                            for (int x = 0; x < 2; ++x)
-#pragma unroll
-                                for (int kt = 0; kt <= TX[x]; ++kt)
-                                    pacc[x][kt] = mfma16(fk[kt][s2], fq[x][s2], pacc[x][kt]);
-                    }
-                    // masks and decays: e^gamma_i on S Q^T; on P^T tile (kt, TX)
-                    // element (key j, token i), j <= i: e^{gamma_i - gamma_j}
-                    // directly on the diagonal tile, e^{gamma_i - gamma_r} F_j below
-                    // it (r the last token of key tile kt; both factors <= 1)
-                    const float *sF = stSc(b) + 3 * C;
+                    if constexpr (!PST) ptiles(TAc, TBc, fq, b, m, qq, pb[b]);
 #pragma unroll
                     for (int x = 0; x < 2; ++x) {
-                        const int ti = 16 * TX[x] + m;             // this lane's token
-                        const float gs = sG[ti];                   // gamma_i log2(e)
-                        const float e_i = sEg[ti];
+                        const float e_i = sEg[16 * TX[x] + m];
 #pragma unroll
                         for (int u = 0; u < 2; ++u) oacc[b][x][u] = oacc[b][x][u] * e_i;
-#pragma unroll
-                        for (int kt = 0; kt <= TX[x]; ++kt) {
-                            if (kt < TX[x]) {
-                                const float ek = __builtin_amdgcn_exp2f(gs - sG[16 * kt + 15]);
-                                const f32x4 fj = *reinterpret_cast<const f32x4 *>(sF + 16 * kt + 4 * qq);
-#pragma unroll
-                                for (int r = 0; r < 4; ++r) pacc[x][kt][r] = pacc[x][kt][r] * (ek * fj[r]);
-                            } else {
-                                const f32x4 gj = *reinterpret_cast<const f32x4 *>(sG + 16 * kt + 4 * qq);
-#pragma unroll
-                                for (int r = 0; r < 4; ++r) {
-                                    const float e = __builtin_amdgcn_exp2f(gs - gj[r]);
-                                    pacc[x][kt][r] = 4 * qq + r <= m ? pacc[x][kt][r] * e : 0.f;
-                                }
-                            }
-                        }
-#pragma unroll
-                        for (int s = 0; s < NKB[x]; ++s)
-                            pb[b][x][s] = acc_pair_bf16(pacc[x][2 * s],
-                                                        2 * s + 1 <= TX[x] ? pacc[x][2 * s + 1] : f32x4{0.f, 0.f, 0.f, 0.f});
                     }
                 }
                 if (out && ch >= 1 && ch <= nchunks) {
@@ -1768,6 +1808,12 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
                         for (int u = 0; u < 2; ++u)
                             fd[u][s] = lds8(sDt, (r0 + 4 * u) * LD_L + ((32 * s + 8 * qq) ^ swD(r0 + 4 * u)));
+                    if constexpr (PST) {
+#pragma unroll
+                        for (int x = 0; x < 2; ++x)
+#pragma unroll
+                            for (int s = 0; s < NKB[x]; ++s) pb[hf][x][s] = lds8(cpPB(hf, TA, x, s), 8 * lane);
+                    }
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int x = 0; x < 2; ++x) {
@@ -1865,7 +1911,8 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             else oloop_scalar(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{});
         }
     } else {
-        // ============ waves 4-7: staging; waves 4-5 also stage P (per channel) ============
+        // ============ waves 4-7: staging; waves 4-5 also stage P (per channel),
+        //              waves 6-7 form P^T (scalar gate) ============
         // below the recurrence and above the output waves in issue arbitration:
         // the next chunk's tiles must be in LDS by the barrier (per channel the
         // output waves also load Q+ from memory and keep the default)
@@ -1896,7 +1943,33 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                 *reinterpret_cast<bf16x8 *>(sP + off + 8 * (grp ^ ((row & 15) >> 2))) = pr[r];
             }
         };
-        auto lloop = [&](auto WT, auto WG, auto WV, auto WP) {
+        // WPT: the token tiles {R, 3 - R} whose P^T this wave forms (scalar
+        // gate, two-pass layout: waves 6 and 7 for output waves 2 and 3), or
+        // R < 0 for none. It runs after the wave's stores and loads, which
+        // the next iteration waits for: formed before them it made the step
+        // ~10% slower.
+        auto lloop = [&](auto WT, auto WG, auto WV, auto WP, auto WPT) {
+            constexpr int R = decltype(WPT)::value;
+            auto pstage = [&](int b, int lane) {
+                if constexpr (R >= 0) {
+                    const int m = lane & 15, qq = lane >> 4;
+                    constexpr int TX[2] = {R, 3 - R};
+                    constexpr int NKB[2] = {R / 2 + 1, (3 - R) / 2 + 1};
+                    const bf16 *sQ = stQ(b);
+                    bf16x8 fq[2][4], pbv[2][2];
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+                        for (int x = 0; x < 2; ++x)
+                            fq[x][s2] = lds8(sQ, (16 * TX[x] + m) * LD_R + ((32 * s2 + 8 * qq) ^ swK(16 * TX[x])));
+                    ptiles(std::integral_constant<int, R>{}, std::integral_constant<int, 3 - R>{}, fq, b, m, qq, pbv);
+#pragma unroll
+                    for (int x = 0; x < 2; ++x)
+#pragma unroll
+                        for (int s = 0; s < NKB[x]; ++s)
+                            *reinterpret_cast<bf16x8 *>(cpPB(b, R, x, s) + 8 * lane) = pbv[x][s];
+                }
+            };
             bf16x8 pp[2][3];
             for (int ch0 = -3; ch0 <= nchunks; ch0 += 2)
 #pragma unroll
@@ -1914,6 +1987,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                 }
                 if (ch + 1 >= 0 && ch + 1 < nchunks) store(ps, hf, WT, WG, WV, lane);   // chunk ch + 1
                 fetch(ch + 3 < nchunks ? ch + 3 : nchunks - 1, ps, WT, WG, WV);
+                if (out && ch >= 0 && ch < nchunks) pstage(b, lane);
                 lds_barrier();
             }
         };
@@ -1969,15 +2043,20 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             }
         };
         if constexpr (FUSED) {
-            if (wave == SV_LOAD0 + 1) lloop(no_t, with_g, with_v, no_p);
-            else if (wave == SV_LOAD0) lloop(no_t, no_g, with_v, no_p);
+            if (wave == SV_LOAD0 + 1) lloop(no_t, with_g, with_v, no_p, std::integral_constant<int, -1>{});
+            else if (wave == SV_LOAD0) lloop(no_t, no_g, with_v, no_p, std::integral_constant<int, -1>{});
             else if (wave == SV_WAVE0) sloop(std::integral_constant<int, 0>{});
             else sloop(std::integral_constant<int, 1>{});
         } else {
-            if (wave == 7) lloop(no_t, with_g, with_v, no_p);
-            else if (wave == 6) lloop(no_t, no_g, with_v, no_p);
-            else if constexpr (PERCH) lloop(with_t, no_g, no_v, with_p);
-            else lloop(with_t, no_g, no_v, no_p);
+            // wave 6 forms P^T for output wave 2 (token tiles 0, 3), wave 7
+            // for output wave 3 (tiles 1, 2)
+            using PT0 = std::integral_constant<int, PST ? 0 : -1>;
+            using PT1 = std::integral_constant<int, PST ? 1 : -1>;
+            using PTN = std::integral_constant<int, -1>;
+            if (wave == 7) lloop(no_t, with_g, with_v, no_p, PT1{});
+            else if (wave == 6) lloop(no_t, no_g, with_v, no_p, PT0{});
+            else if constexpr (PERCH) lloop(with_t, no_g, no_v, with_p, PTN{});
+            else lloop(with_t, no_g, no_v, no_p, PTN{});
         }
     }
     if (sfin && wave < 2) {
