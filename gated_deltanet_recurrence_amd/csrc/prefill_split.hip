@@ -118,13 +118,18 @@ constexpr int SZ_DT = DVT * LD_L * 2;          // 5120: Delta^T [32][80]
 constexpr int SZ_PB = 6 * 64 * 16;             // 6144: P^T of a chunk (scalar gate) as six
                                                // B-operand registers, 1 KiB each, lane-linear
 constexpr int OFF_BUF = 0;                     // two of each from here on
-// In-chain solve (scalar gates, no workspace): each of the two solver waves
-// keeps one chunk's 16 x 16 blocks (I, J), J <= I, of A and then T, fp32
-// row-major at row stride SV_LD (conflict-free operand reads), and the
-// chunk's gamma log2(e) and beta.
+// One wave's triangular solve (WaveSolver: the solve pass, and the in-chain
+// solve with scalar gates and no workspace) keeps one chunk's 16 x 16 blocks
+// (I, J), J <= I, of A and then T, fp32 row-major at row stride SV_LD
+// (conflict-free operand reads), and the chunk's gamma log2(e) and beta. The
+// four diagonal blocks come first, SV_DIAG floats apart, so that they start
+// 64 bytes apart in the bank cycle: their forward substitutions read and
+// write row i of all four at once. Then the six off-diagonal blocks.
 constexpr int SV_LD = 20;
 constexpr int SV_BLK = 16 * SV_LD;
-constexpr int SV_BYTES = (10 * SV_BLK + 3 * 256 + 2 * C) * 4;   // 16384: + D0^T, D1^T, D2^T
+constexpr int SV_DIAG = SV_BLK + 16;
+constexpr int SV_OFF0 = 4 * SV_DIAG;
+constexpr int SV_BYTES = (SV_OFF0 + 6 * SV_BLK + 2 * C) * 4;   // 13568: twelve per CU
 constexpr int SV_WAVE0 = 6;                    // solver waves SV_WAVE0, + 1
 constexpr int SV_LOAD0 = 4;                    // loading waves SV_LOAD0, + 1
 constexpr int SV_PRIO = 1;                     // solver waves' issue priority
@@ -940,7 +945,7 @@ chunk_prep_channel_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k
 //   phase1  gamma = prefix sum of g; the ten Gram blocks (I, J), J <= I, of
 //           K K^T on the bf16 matrix cores (K given in operand order); A
 //           row-major into the blocks; the diagonal blocks D_b = (I - A_bb)^-1
-//           by forward substitution, in place (D_0..D_2 also transposed)
+//           by forward substitution, in place
 //   phase2  the off-diagonal blocks of T by two levels of 2 x 2 block
 //           inversion on split bf16 products (mm16x), in place
 //   emit    T diag(beta) as 384 bf16 pieces of 8 row elements: pieces
@@ -951,9 +956,10 @@ chunk_prep_channel_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k
 // ---------------------------------------------------------------------------
 struct WaveSolver {
     float *sv;
-    __device__ float *blk(int I, int J) const { return sv + (I * (I + 1) / 2 + J) * SV_BLK; }
-    __device__ float *dtr(int b) const { return sv + 10 * SV_BLK + 256 * b; }   // D_b^T, row stride 16
-    __device__ float *gl() const { return sv + 10 * SV_BLK + 3 * 256; }         // gamma log2(e)
+    __device__ float *blk(int I, int J) const {
+        return I == J ? sv + I * SV_DIAG : sv + SV_OFF0 + (I * (I - 1) / 2 + J) * SV_BLK;
+    }
+    __device__ float *gl() const { return sv + SV_OFF0 + 6 * SV_BLK; }          // gamma log2(e)
     __device__ float *be() const { return gl() + C; }                           // beta
 
     // K rows 16 I + lane % 16, columns 32 s + 8 (lane / 16) .. of a chunk whose
@@ -1047,17 +1053,11 @@ struct WaveSolver {
             D[i] = acc;
         }
         wave_lds_order();
-        // D_b row-major in place; D_0, D_1, D_2 also transposed (their
-        // columns are right-hand operands below)
+        // D_b row-major in place (its columns, right-hand operands below,
+        // are read as four single elements per lane)
         float *Db = blk(bb, bb);
 #pragma unroll
         for (int i = 0; i < 16; ++i) Db[i * SV_LD + c] = D[i];
-        if (bb < 3) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                *reinterpret_cast<f32x4 *>(dtr(bb) + c * 16 + 4 * t) =
-                    f32x4{D[4 * t], D[4 * t + 1], D[4 * t + 2], D[4 * t + 3]};
-        }
         wave_lds_order();
     }
     __device__ void phase2(int lane) const {
@@ -1069,17 +1069,21 @@ struct WaveSolver {
         //   T31 = T32 (A21 D1) + D3 (A31 D1)
         //   T30 = T32 (A20 D0 + A21 T10) + D3 (A30 D0 + A31 T10)
         // Left factors are row pieces of row-major blocks, right
-        // factors column pieces of D_b^T or accumulators.
+        // factors column pieces of the row-major D_b or accumulators.
         auto piece = [&](const float *p, int ld) {
             return *reinterpret_cast<const f32x4 *>(p + m * ld + 4 * qq);
+        };
+        auto colpiece = [&](const float *p) {
+            return f32x4{p[(4 * qq) * SV_LD + m], p[(4 * qq + 1) * SV_LD + m],
+                         p[(4 * qq + 2) * SV_LD + m], p[(4 * qq + 3) * SV_LD + m]};
         };
         const LSplit lA10 = lsplit(piece(blk(1, 0), SV_LD)), lA32 = lsplit(piece(blk(3, 2), SV_LD));
         const LSplit lA21 = lsplit(piece(blk(2, 1), SV_LD)), lA20 = lsplit(piece(blk(2, 0), SV_LD));
         const LSplit lA31 = lsplit(piece(blk(3, 1), SV_LD)), lA30 = lsplit(piece(blk(3, 0), SV_LD));
         const LSplit lD1 = lsplit(piece(blk(1, 1), SV_LD)), lD2 = lsplit(piece(blk(2, 2), SV_LD));
         const LSplit lD3 = lsplit(piece(blk(3, 3), SV_LD));
-        const bf16x8 rD0 = rsplit(piece(dtr(0), 16)), rD1 = rsplit(piece(dtr(1), 16));
-        const bf16x8 rD2 = rsplit(piece(dtr(2), 16));
+        const bf16x8 rD0 = rsplit(colpiece(blk(0, 0))), rD1 = rsplit(colpiece(blk(1, 1)));
+        const bf16x8 rD2 = rsplit(colpiece(blk(2, 2)));
         const f32x4 u10 = mm16x(z4, lA10, rD0);
         const f32x4 u32 = mm16x(z4, lA32, rD2);
         const bf16x8 X = rsplit(mm16x(z4, lA21, rD1));         // A21 D1
@@ -1137,15 +1141,16 @@ struct WaveSolver {
 // chunk_solve: the first pass of the two-pass path with a scalar gate. One
 // wave per workgroup and (chunk, head) item at a time (items blockIdx.x,
 // + gridDim.x, ...), each wave with its own SV_BYTES of LDS, so that up to
-// ten items are in flight per compute unit and none waits at a workgroup
-// barrier. Writes T_u = T diag(beta) of the item into the workspace. With
-// PREFETCH each item's keys are requested while the item before it is
-// solved (64 more registers: eight waves per CU instead of ten), which pays
-// when every wave has several items to walk.
+// twelve items are in flight per compute unit (three waves per SIMD, which
+// its register count is held to) and none waits at a workgroup barrier.
+// Writes T_u = T diag(beta) of the item into the workspace. With PREFETCH
+// each item's keys are requested while the item before it is solved (more
+// registers: eight waves per CU), which pays when every wave has several
+// items to walk.
 // ---------------------------------------------------------------------------
 constexpr int SOLVE_NT = 64;
 template <bool PREFETCH>
-__global__ void __launch_bounds__(SOLVE_NT)
+__global__ void __launch_bounds__(SOLVE_NT) __attribute__((amdgpu_waves_per_eu(PREFETCH ? 2 : 3)))
 chunk_solve_kernel(const bf16 *__restrict__ k, const float *__restrict__ g,
                    const float *__restrict__ beta, const int32_t *__restrict__ cu_seqlens,
                    bf16 *__restrict__ ws, int T, int H, int Hk, int N, int nslots)
