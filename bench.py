@@ -416,10 +416,14 @@ def bench_mixer(gdn, inputs, steps, warmup):
 
     def full(i):
         pro(i); core(i); epi(i)
-    ms_full = event_time(full, max(5, steps // 4), 3)
-    ms_pro = event_time(pro, max(5, steps // 4), 3)
-    ms_core = event_time(core, max(5, steps // 4), 3)
-    ms_epi = event_time(epi, max(5, steps // 4), 3)
+    # the whole step first runs for DEVICE_WARMUP_S, as for the prefill
+    # value: on fresh buffers the first calls run slow (three warm-up calls
+    # read 1.02 ms per step where the steady state is 0.87)
+    n_dev_warm = device_warmup(full)
+    ms_full = event_time(full, max(10, steps // 2), 3)
+    ms_pro = event_time(pro, max(10, steps // 2), 3)
+    ms_core = event_time(core, max(10, steps // 2), 3)
+    ms_epi = event_time(epi, max(10, steps // 2), 3)
     pro_bytes = B * T * H * (D * 2 * 3 * 2 + 2 * 2 + 4 * 2)   # q,k,v in+out, a,b in, g,beta out
     epi_bytes = B * T * H * D * 2 * 3
     return dict(workload="token mixer B=8 T=8192 H=16 d=128 bf16: conv+SiLU, L2-norm, gates -> "
@@ -428,7 +432,8 @@ def bench_mixer(gdn, inputs, steps, warmup):
                 ms_prologue=round(ms_pro, 4), ms_prefill=round(ms_core, 4),
                 ms_epilogue=round(ms_epi, 4),
                 prologue_GBps=round(pro_bytes / (ms_pro * 1e-3) / 1e9, 1),
-                epilogue_GBps=round(epi_bytes / (ms_epi * 1e-3) / 1e9, 1))
+                epilogue_GBps=round(epi_bytes / (ms_epi * 1e-3) / 1e9, 1),
+                device_warmup_steps=n_dev_warm)
 
 
 def bench_varlen(gdn, inputs, steps, warmup):
