@@ -1745,11 +1745,7 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                 const f32x4 a = acc[0], c = acc[1];
                 const bf16x8 x = {(bf16)(sc * a[0]), (bf16)(sc * a[1]), (bf16)(sc * a[2]), (bf16)(sc * a[3]),
                                   (bf16)(sc * c[0]), (bf16)(sc * c[1]), (bf16)(sc * c[2]), (bf16)(sc * c[3])};
-                // non-temporal: the rows are not read again here, and kept in
-                // L2 they would push out the q, k and workspace lines that a
-                // head's four d_v-tile workgroups share
-                __builtin_nontemporal_store(x, reinterpret_cast<bf16x8 *>(
-                    out + ((size_t)bos + tok) * H * DV + (size_t)h * DV + cbase + 8 * qq));
+                *reinterpret_cast<bf16x8 *>(out + ((size_t)bos + tok) * H * DV + (size_t)h * DV + cbase + 8 * qq) = x;
             }
         };
         // scalar gate: token tiles TA < TB = 3 - TA of every chunk. P^T comes
