@@ -1145,8 +1145,8 @@ struct WaveSolver {
 // its register count is held to) and none waits at a workgroup barrier.
 // Writes T_u = T diag(beta) of the item into the workspace. With PREFETCH
 // each item's keys are requested while the item before it is solved (more
-// registers: eight waves per CU), which pays when every wave has several
-// items to walk.
+// registers: eight waves per CU), which pays once the plain kernel's grid
+// would need a second round of items.
 // ---------------------------------------------------------------------------
 constexpr int SOLVE_NT = 64;
 template <bool PREFETCH>
@@ -2139,8 +2139,12 @@ hipError_t launch_prefill_prepare(const void *q, const void *k, const float *g, 
                            (int)nslots);
         return hipGetLastError();
     }
-    // more than two items per wave of the plain kernel's grid: the kernel that
-    // fetches each item's keys during the previous item's solve
+    // more items than the plain kernel's grid has waves: the kernel that
+    // fetches each item's keys during the previous item's solve (its second
+    // items' keys then arrive while the first ones are solved, where the plain
+    // kernel's second round waits for them; with the keys coming from HBM, as
+    // after the chain pass of the previous call, that is 1.7 us of the 4096
+    // items of B=4 T=4096 H=16)
     const void *plain = (const void *)chunk_solve_kernel<false>;
     const void *pref = (const void *)chunk_solve_kernel<true>;
     hipError_t e = raise_lds_limit(plain, SV_BYTES, lds_scalar);
@@ -2148,7 +2152,7 @@ hipError_t launch_prefill_prepare(const void *q, const void *k, const float *g, 
     if (e != hipSuccess) return e;
     e = prep_fill(plain, SOLVE_NT, SV_BYTES, fill_scalar, fill);
     if (e != hipSuccess) return e;
-    const bool prefetch = nitems > 2 * fill;
+    const bool prefetch = nitems > fill;
     if (prefetch) {
         e = prep_fill(pref, SOLVE_NT, SV_BYTES, fill_prefetch, fill);
         if (e != hipSuccess) return e;
