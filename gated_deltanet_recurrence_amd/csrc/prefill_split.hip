@@ -1836,12 +1836,27 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         };
         // per-channel decay: tokens 32 hw .. 32 hw + 31, P from the workspace
         // (staged into the P copies by waves 4-5), Q+ from the workspace in
-        // operand order, one chunk ahead
+        // operand order: chunk c into register set c % 2, two iterations ahead,
+        // by one load site per iteration that runs unconditionally (clamped to
+        // the last chunk; with no outputs its resource spans nothing), like the
+        // staging waves' prefetch: a load site under a condition let the
+        // compiler wait at the join for the loads just issued
         auto oloop_channel = [&](auto HW) {
             constexpr int hw = decltype(HW)::value;
             constexpr int NS = hw + 1;         // key blocks of 32 that tokens 32 hw .. need
             f32x4 oacc[2][2][2];               // [chunk parity][token tile 2 hw + tt][u]
             bf16x8 fqg[2][2][4];
+            auto qfetch = [&](int c, bf16x8 (&dst)[2][4], int lane) {
+                const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+                    (void *)(wsh + (size_t)c * IST + CH_QP), 0, out ? (unsigned)(C * DK * 2) : 0u,
+                    0x00020000);
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2)
+                        dst[tt][s2] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                            rq, 16 * lane, 1024 * (4 * (2 * hw + tt) + s2), 0));
+            };
             for (int ch0 = -3; ch0 <= nchunks; ch0 += 2)
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
@@ -1851,14 +1866,6 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                 asm volatile("" : "+v"(tidl));
                 const int lane = tidl & 63, m = lane & 15, qq = lane >> 4;
                 const int r0 = 8 * (m >> 2) + (m & 3);
-                if (out && ch + 1 >= 0 && ch + 1 < nchunks) {
-                    const bf16 *qp = wsh + (size_t)(ch + 1) * IST + CH_QP + 8 * lane;
-#pragma unroll
-                    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                        for (int s2 = 0; s2 < 4; ++s2)
-                            fqg[hf][tt][s2] = *reinterpret_cast<const bf16x8 *>(qp + 512 * (4 * (2 * hw + tt) + s2));
-                }
                 if (out && ch >= 0 && ch < nchunks) {
                     const bf16 *sSc = cpS(b);
                     bf16x8 fs[2][4];
@@ -1878,6 +1885,8 @@ chunk_chain_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                             oacc[b][tt][u] = a;
                         }
                 }
+                // chunk ch + 2 into the set chunk ch has just been read from
+                qfetch(ch + 2 < 0 ? 0 : ch + 2 < nchunks ? ch + 2 : nchunks - 1, fqg[b], lane);
                 if (out && ch >= 1 && ch <= nchunks) {
                     const int cp = ch - 1;
                     const bf16 *sDt = cpDt(hf), *sP = cpP(hf);
