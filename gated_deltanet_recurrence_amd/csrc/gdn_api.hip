@@ -46,8 +46,10 @@ bool chunk_path(int dtype, int d_k, int d_v) {
 }
 
 // the two-pass kernels index (chunk slot, head) items with 32-bit integers
+// the prep passes' (chunk slot, head) items, slots rounded up to groups of 8,
+// and a margin for their grid strides fit 32-bit indices
 bool items_fit(int64_t tokens, int H, int64_t N) {
-    return (tokens / 64 + N + 1) * H <= (int64_t)INT32_MAX;
+    return ((tokens / 64 + N + 1) + 7) / 8 * 8 * H + ((int64_t)1 << 20) <= (int64_t)INT32_MAX;
 }
 
 // a caller's workspace for the two-pass chunk path: 256-byte aligned, large enough

@@ -418,7 +418,7 @@ __device__ __forceinline__ void solve_store(const float *sA, const float *sY, fl
 
 // ---------------------------------------------------------------------------
 // chunk_prep: the parts of a chunk that do not depend on the state, for
-// (chunk, head) items. Item i is slot i / H of head i % H; a workgroup takes
+// (chunk, head) items (prep_locate: which slot and head an item is); a workgroup takes
 // items blockIdx.x, + gridDim.x, ... and loads the next item's K, g and beta
 // into registers while it works on the current one, so that the HBM latency
 // is paid once per workgroup.
@@ -440,12 +440,22 @@ struct PrepItem {
     int slot, h, nvalid;                       // nvalid = 0: nothing to do
     long row0;                                 // first token of the chunk
 };
+// Items and their order. Workgroup b runs on XCD b % 8, and every grid of the
+// prep passes is a multiple of 8 workgroups, so item i always runs on XCD
+// i % 8. Item i takes slot 8 (j / H) + i % 8 and head j % H, with j = i / 8:
+// the H heads of a chunk slot run on one XCD, one after the other in
+// workgroup order, and read the chunk's g and beta through one L2. Each
+// 128-byte line of g or beta holds two tokens of every head; dealt head-minor
+// over all XCDs, every XCD fetched it. The count is rounded up to whole
+// groups of 8 slots; slots past the last sequence's chunks are unused items.
+__host__ __device__ inline long prep_nitems(long nslots, int H) { return (nslots + 7) / 8 * 8 * H; }
 __device__ __forceinline__ PrepItem prep_locate(const int32_t *cu, int item, int nitems, int T,
                                                 int H, int N) {
     PrepItem it{0, 0, 0, 0};
     if (item >= nitems) return it;
-    it.slot = item / H;
-    it.h = item - it.slot * H;
+    const int j = item >> 3;
+    it.slot = 8 * (j / H) + (item & 7);
+    it.h = j % H;
     // sequence of the slot: the last n whose first slot is <= slot
     int lo = 0, hi = N - 1;
     while (lo < hi) {
@@ -552,7 +562,7 @@ chunk_prep_channel_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k
 
     const int tid0 = (int)threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
-    const int nitems = nslots * H;
+    const int nitems = (int)prep_nitems(nslots, H);
     const int stride = (int)gridDim.x;
     const int tstride = Hk * DK;
 
@@ -1158,7 +1168,7 @@ chunk_solve_kernel(const bf16 *__restrict__ k, const float *__restrict__ g,
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const WaveSolver sol{reinterpret_cast<float *>(smem)};
     const int lane = (int)threadIdx.x;
-    const int nitems = nslots * H;
+    const int nitems = (int)prep_nitems(nslots, H);
     const int tstride = Hk * DK;
     const int stride = (int)gridDim.x;
     auto fetch_item = [&](const PrepItem &it, bf16x8 (&kr)[4][4], float &gv, float &bv) {
@@ -2117,6 +2127,7 @@ static hipError_t prep_fill(const void *kern, int nt, int lds, std::atomic<long>
         if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, nt, lds);
         if (e != hipSuccess) return e;
         fill = (long)(per_cu < 1 ? 1 : per_cu) * (cus < 1 ? 1 : cus);
+        if (fill >= 8) fill = fill / 8 * 8;      // whole rounds of the 8 XCDs (prep_nitems)
         if (dev < MAX_DEVICES) cache[dev].store(fill, std::memory_order_relaxed);
     }
     return hipSuccess;
@@ -2129,7 +2140,7 @@ hipError_t launch_prefill_prepare(const void *q, const void *k, const float *g, 
     const long tokens = cu ? (long)T : (long)N * T;
     const long nslots = tokens / C + N + 1;
     if (tokens == 0) return hipSuccess;        // no chunk: nothing to prepare
-    const long nitems = nslots * H;
+    const long nitems = prep_nitems(nslots, H);
     static std::atomic<long> fill_scalar[MAX_DEVICES], fill_prefetch[MAX_DEVICES];
     static std::atomic<long> fill_channel[MAX_DEVICES];
     static std::atomic<int> lds_scalar[MAX_DEVICES], lds_prefetch[MAX_DEVICES];
